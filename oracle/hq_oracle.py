@@ -1,0 +1,285 @@
+"""CPU oracle for the rotated-and-centred quantised linear layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the library's product path may import,
+call or execute this module: it is used by ``tests/``, by the entry point's
+smoke check and by the benchmark's CPU-baseline leg, and nowhere else. It
+shares no code with the HIP path (no kernels, helpers, tables or constants).
+
+It is deliberately plain: float64 NumPy, every step in the order the pages
+give it, library matrix products as the only building block. Sources (page
+titles; equations as numbered on those pages):
+
+* HadaNorm (pith.science review of "HadaNorm: Diffusion Transformer
+  Quantization through Mean-Centered Transformations"), section "What
+  carries the argument": Eq. (1), the identity
+  XW + b = X~ W~ + b~ with X~ = X diag(1/sigma) H - mu,
+  W~ = H^T diag(sigma) W, b~ = b + mu W~, and Eq. (3), the smoothing scale
+  sigma_i = max|X_i|^alpha / max|W_i|^(1 - alpha); mu is the per-token mean
+  of the scaled-and-rotated activations.
+* "Hadamard-Domain Model Quantization for Learned Image Coding" (HaTQ):
+  Sec. III-A Eq. (3), the symmetric quantiser; Sec. III-B Eq. (4), integer
+  accumulation; Sec. III-C Eq. (7)-(8), the normalised Hadamard transform;
+  Sec. IV-B Eq. (13)-(14), double-Hadamard quantisation; Sec. IV-C Eq. (23),
+  the constant-basis component; Eq. (18), the accumulator scale s_x s_w;
+  supplement Sec. VII-A Eq. (32)-(34), the Sylvester construction.
+* "Data-free 4-bit quantization for diffusion transformers" (blog), section
+  "Hadamard rotation: the int4 improvement", steps 2-7 and "How it is applied
+  here": block-diagonal Hadamard over contiguous channel blocks, and the
+  16-bit low-rank branch fed with the smoothed, un-rotated input.
+
+Layout convention: row vectors. X is [T, d_in] (one token per row), the
+weight is passed as ``weight`` [d_out, d_in] (W = weight^T), b is [d_out].
+
+Readings taken where the pages leave a step open:
+
+* mu is one scalar per token (the mean over the d_in transformed channels).
+* sigma uses max(., 1e-5) on both maxima; X_i is input channel i over all
+  tokens, W_i is input channel i over all outputs.
+* H is the normalised Sylvester matrix in natural order, applied per
+  contiguous block of ``block`` channels.
+* Activations get one scale per token, weights one scale per output
+  channel; codes are symmetric in [-qmax, qmax], qmax = 2^(bits-1) - 1.
+* The rounding decision round(v / s) is taken in float32 as
+  rint_half_even(f32(v) * f32(qmax / f32(max|v|))): the same real number as
+  v / s, evaluated in the precision the GPU kernel uses, so both sides decide
+  each code in the same arithmetic. Scales, means and outputs stay float64.
+* A row whose maximum is 0 gets scale 0 and all-zero codes.
+* The bias correction uses c = 1^T W~ from the unquantised W~.
+* The low-rank branch sees x' = x / sigma (smoothed, not rotated, not
+  centred) and contributes (x' L1) L2, L1 [d_in, r], L2 [r, d_out].
+* Y is rounded once, half-to-even, to the output dtype.
+
+Parity status: every step below is pinned by ``tests/test_oracle.py``
+(construction and orthogonality of H, brute force on tiny inputs, the exact
+identity with quantisation off, closed forms, a hand-worked example). The
+end-to-end quantised output has no value printed on the pages; it is fixed
+only through the composition of those pinned steps.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+EPS = 1e-5
+
+
+# --------------------------------------------------------------------------
+# Hadamard matrices and the rotation
+# --------------------------------------------------------------------------
+
+def sylvester(m: int) -> np.ndarray:
+    """Unnormalised Sylvester matrix of order m (a power of two).
+
+    HaTQ supplement Sec. VII-A Eq. (34): start from [1] and double with
+    [[H, H], [H, -H]].
+    """
+    if m < 1 or (m & (m - 1)):
+        raise ValueError(f"Sylvester order must be a power of two, got {m}")
+    h = np.ones((1, 1))
+    while h.shape[0] < m:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard(m: int) -> np.ndarray:
+    """Normalised Hadamard matrix H = H~ / sqrt(m), so H H^T = I (HaTQ Eq. (7), (32)-(33))."""
+    return sylvester(m) / np.sqrt(m)
+
+
+def rotate(x: np.ndarray, block: int) -> np.ndarray:
+    """Rows of x times the block-diagonal H = diag(H_B, ..., H_B).
+
+    Each block of ``block`` contiguous channels is transformed on its own
+    (HQ-DM Sec. 2.1; blog step 7). Inside a block every output is the
+    normalised signed sum of HaTQ Eq. (8). H_B is symmetric, so x H_B equals
+    (H_B x^T)^T.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    t, d = x.shape
+    if d % block:
+        raise ValueError("block must divide the row length")
+    return (x.reshape(t, d // block, block) @ hadamard(block)).reshape(t, d)
+
+
+# --------------------------------------------------------------------------
+# Offline: smoothing scales and the weight transform
+# --------------------------------------------------------------------------
+
+def smoothing_scales(x_calib: np.ndarray, weight: np.ndarray, alpha: float,
+                     eps: float = EPS) -> np.ndarray:
+    """sigma_i = max_t |X_ti|^alpha / max_j |W_ij|^(1 - alpha) (HadaNorm Eq. (3)).
+
+    W = weight^T, so W_i (input channel i over all outputs) is column i of
+    ``weight``. Both maxima are clamped below at ``eps``.
+    """
+    ax = np.abs(np.asarray(x_calib, dtype=np.float64)).max(axis=0)
+    aw = np.abs(np.asarray(weight, dtype=np.float64)).max(axis=0)
+    return np.maximum(ax, eps) ** alpha / np.maximum(aw, eps) ** (1.0 - alpha)
+
+
+def transform_weights(weight: np.ndarray, sigma: np.ndarray, block: int):
+    """W~ = H^T diag(sigma) W (HadaNorm Eq. (1)), returned row-wise.
+
+    With W = weight^T, W~^T = weight diag(sigma) H, so row j of the result
+    is (weight_j * sigma) H. Also returns c = 1^T W~ (c_j = sum_i W~_ij), the
+    vector that turns mu into the bias correction mu W~.
+    """
+    v = np.asarray(weight, dtype=np.float64) * np.asarray(sigma, dtype=np.float64)[None, :]
+    wt = rotate(v, block)
+    c = wt.sum(axis=1)
+    return wt, c
+
+
+# --------------------------------------------------------------------------
+# Online: activation transform, centring, quantisation
+# --------------------------------------------------------------------------
+
+def transform_activations(x: np.ndarray, sigma: np.ndarray, block: int, center: bool):
+    """X~ = X diag(1/sigma) H - mu (HadaNorm Eq. (1)).
+
+    Returns (x', y, mu, x~) with x' = X / sigma, y = x' H, mu_t the mean of
+    row t of y (zero when centring is off) and x~ = y - mu.
+    """
+    xp = np.asarray(x, dtype=np.float64) / np.asarray(sigma, dtype=np.float64)[None, :]
+    y = rotate(xp, block)
+    mu = y.mean(axis=1) if center else np.zeros(y.shape[0])
+    return xp, y, mu, y - mu[:, None]
+
+
+def quantize_rows(v: np.ndarray, bits: int):
+    """Symmetric per-row quantiser of HaTQ Sec. III-A Eq. (3).
+
+    s = ||v||_inf / qmax with qmax = 2^(bits-1) - 1, and
+    q = clamp(round(v / s), -qmax, qmax). The division v / s is formed as
+    v * (qmax / ||v||_inf) in float32 and rounded half-to-even (see the module
+    header). Returns (codes int16 [rows, n], s float64 [rows]).
+    """
+    qmax = 2 ** (bits - 1) - 1
+    v = np.asarray(v, dtype=np.float64)
+    amax = np.abs(v).max(axis=1) if v.shape[1] else np.zeros(v.shape[0])
+    s = amax / qmax
+    a32 = amax.astype(np.float32)
+    nz = a32 > 0
+    r32 = np.zeros_like(a32)
+    r32[nz] = np.float32(qmax) / a32[nz]
+    t32 = v.astype(np.float32) * r32[:, None]
+    q = np.clip(np.rint(t32), -qmax, qmax).astype(np.int16)
+    return q, s
+
+
+# --------------------------------------------------------------------------
+# Integer GEMM, low-rank branch, dequantised output
+# --------------------------------------------------------------------------
+
+def int_gemm(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """acc_tj = sum_i qa_ti * qw_ji with zero points 0 (HaTQ Eq. (4)).
+
+    Evaluated as a float64 matrix product of the integer codes: every product
+    and every partial sum is an integer of magnitude below 2^53, so the
+    product is exact whatever the summation order. Returns int64.
+    """
+    qa = np.asarray(qa)
+    qw = np.asarray(qw)
+    if qa.size and qw.size:
+        bound = int(np.abs(qa).max()) * int(np.abs(qw).max()) * qa.shape[1]
+        assert bound < 2 ** 53
+    return (qa.astype(np.float64) @ qw.astype(np.float64).T).astype(np.int64)
+
+
+def low_rank(xp: np.ndarray, l1: np.ndarray, l2: np.ndarray):
+    """16-bit low-rank branch L2 (L1 x^) in row form (x' L1) L2 (blog steps 3-4, 6).
+
+    x' is the smoothed input before rotation. Returns (U = x' L1, U L2).
+    """
+    u = np.asarray(xp, dtype=np.float64) @ np.asarray(l1, dtype=np.float64)
+    return u, u @ np.asarray(l2, dtype=np.float64)
+
+
+def dequant_output(acc, s_x, s_w, bias, mu, c, lr=None) -> np.ndarray:
+    """Y_tj = s_x,t s_w,j acc_tj + b_j + mu_t c_j (+ low-rank).
+
+    s_x,t s_w,j is the accumulator scale of HaTQ Eq. (18); b + mu W~ is the
+    corrected bias of HadaNorm Eq. (1), with mu W~ = mu_t c_j.
+    """
+    y = (np.asarray(acc, dtype=np.float64) * (np.asarray(s_x, dtype=np.float64)[:, None]
+                                              * np.asarray(s_w, dtype=np.float64)[None, :]))
+    y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    y = y + np.asarray(mu, dtype=np.float64)[:, None] * np.asarray(c, dtype=np.float64)[None, :]
+    if lr is not None:
+        y = y + lr
+    return y
+
+
+def round_to_dtype(y: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values once, half-to-even, to fp32 or bf16 (returned as float64)."""
+    y = np.asarray(y, dtype=np.float64)
+    if dtype == "f32":
+        return y.astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        m, e = np.frexp(y)                      # y = m 2^e, 0.5 <= |m| < 1
+        return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)  # 8 significant bits
+    raise ValueError(dtype)
+
+
+def exact_output(x, weight, bias, xp=None, l1=None, l2=None) -> np.ndarray:
+    """The unquantised layer X W + b (+ x' L1 L2) in float64 (reference only)."""
+    y = np.asarray(x, dtype=np.float64) @ np.asarray(weight, dtype=np.float64).T
+    y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    if l1 is not None:
+        y = y + low_rank(xp, l1, l2)[1]
+    return y
+
+
+# --------------------------------------------------------------------------
+# The whole layer
+# --------------------------------------------------------------------------
+
+def prepare_weights(weight, sigma, block: int, w_bits: int):
+    """Offline half: W~, c, per-output-channel codes and scales."""
+    wt, c = transform_weights(weight, sigma, block)
+    qw, s_w = quantize_rows(wt, w_bits)
+    return {"wt": wt, "c": c, "qw": qw, "s_w": s_w}
+
+
+def quant_linear(x, prepared, bias, sigma, *, block: int, a_bits: int, center: bool,
+                 l1=None, l2=None, out_dtype: str = "f32"):
+    """Online half for the rows of ``x``: transform, centre, quantise, integer GEMM, dequantise."""
+    xp, y, mu, xt = transform_activations(x, sigma, block, center)
+    qa, s_x = quantize_rows(xt, a_bits)
+    acc = int_gemm(qa, prepared["qw"])
+    u = lr = None
+    if l1 is not None:
+        u, lr = low_rank(xp, l1, l2)
+    y_full = dequant_output(acc, s_x, prepared["s_w"], bias, mu, prepared["c"], lr)
+    return {"xp": xp, "y": y, "mu": mu, "xt": xt, "qa": qa, "s_x": s_x, "acc": acc,
+            "u": u, "lr": lr, "y_full": y_full, "y_out": round_to_dtype(y_full, out_dtype)}
+
+
+def run(x, weight, bias, *, block: int, a_bits: int, w_bits: int, center: bool,
+        sigma=None, l1=None, l2=None, out_dtype: str = "f32"):
+    """Prepare + quant_linear in one call; sigma defaults to ones."""
+    d_in = np.asarray(x).shape[1]
+    sigma = np.ones(d_in) if sigma is None else np.asarray(sigma, dtype=np.float64)
+    prep = prepare_weights(weight, sigma, block, w_bits)
+    out = quant_linear(x, prep, bias, sigma, block=block, a_bits=a_bits, center=center,
+                       l1=l1, l2=l2, out_dtype=out_dtype)
+    out.update(prep)
+    out["sigma"] = sigma
+    return out
+
+
+# --------------------------------------------------------------------------
+# Diagnostics (not parity gates)
+# --------------------------------------------------------------------------
+
+def sqnr_db(ref: np.ndarray, approx: np.ndarray) -> float:
+    """10 log10(||X||^2 / ||X - X^||^2) (HaTQ Sec. IV-A Eq. (10))."""
+    ref = np.asarray(ref, dtype=np.float64)
+    err = ref - np.asarray(approx, dtype=np.float64)
+    return float(10.0 * np.log10(np.sum(ref * ref) / np.sum(err * err)))
+
+
+def excess_kurtosis(v: np.ndarray) -> float:
+    """Empirical excess kurtosis of all entries (HaTQ Sec. IV-A Eq. (9))."""
+    v = np.asarray(v, dtype=np.float64).ravel()
+    d = v - v.mean()
+    return float(np.mean(d ** 4) / np.mean(d ** 2) ** 2 - 3.0)
