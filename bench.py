@@ -1,0 +1,178 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated-and-centred W4A4 quantised linear on one MI355X.
+
+One step = one hq_quant_linear call (activation kernel + int8 GEMM with the
+dequant epilogue) over one synthetic batch already resident in HBM. Inputs
+rotate through enough distinct X/Y buffers (> 512 MB) that a step's
+activations are not served from the 256 MB Infinity Cache left over from the
+previous visit. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dit_fc1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Hadamard-quantized linear tokens/s + effective TOPS (% int8 MFMA/HBM roofline)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dit_fc1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, x, weight, bias, sigma, l1, l2, target_s):
+    """Time the CPU oracle's online half (transform, centre, quantise, integer GEMM,
+    dequantise) on a bounded prefix of the workload's tokens; weight prep excluded."""
+    from oracle import hq_oracle as O
+    import threadpoolctl
+    sig = np.ones(w.d_in) if sigma is None else sigma.astype(np.float64)
+    prep = O.prepare_weights(weight, sig, w.block, w.w_bits)
+    rows = min(w.T, 256)
+    t0 = time.perf_counter()
+    O.quant_linear(x[:rows], prep, bias, sig, block=w.block, a_bits=w.a_bits,
+                   center=bool(w.center), l1=l1, l2=l2, out_dtype=w.out_dtype)
+    dt = time.perf_counter() - t0
+    if dt < target_s and rows < w.T:
+        rows = int(min(w.T, max(rows, rows * target_s / max(dt, 1e-3))))
+        t0 = time.perf_counter()
+        O.quant_linear(x[:rows], prep, bias, sig, block=w.block, a_bits=w.a_bits,
+                       center=bool(w.center), l1=l1, l2=l2, out_dtype=w.out_dtype)
+        dt = time.perf_counter() - t0
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] + [1])
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {rows} of {w.T} tokens of {w.name}, float64 NumPy oracle "
+                      f"(online half, prepared weights reused), {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer shards by "
+              "tokens with no communication, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import hadamard_rotated_bit_amd as hq
+    from hadamard_rotated_bit_amd import workloads as WL
+
+    w = WL.WORKLOADS[args.workload]
+    dt = hq.BF16 if w.dtype == "bf16" else hq.F32
+    desc = hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, bool(w.center),
+                   w.alpha is not None, w.rank, dt, dt, dt)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+
+    x = WL.gen_x(w)
+    weight, bias = WL.gen_weight(w), WL.gen_bias(w)
+    l1, l2 = WL.gen_lowrank(w)
+    X0 = torch.from_numpy(x).to(dev).to(tdt)
+    W = torch.from_numpy(weight).to(dev).to(tdt)
+    B = torch.from_numpy(bias).to(dev)
+    L1 = None if l1 is None else torch.from_numpy(l1).to(dev).to(tdt)
+    L2 = None if l2 is None else torch.from_numpy(l2).to(dev).to(tdt)
+    S = None
+    if w.alpha is not None:          # offline calibration on the workload's own tokens
+        S = hq.sigma(desc, hq.channel_absmax(desc, X0), W, w.alpha)
+    prep = hq.prepare(desc, W, B, S, L1, L2)
+
+    xbytes = X0.numel() * X0.element_size()
+    nbuf = max(2, math.ceil(512e6 / xbytes))
+    Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
+    Ys = [torch.empty(w.T, w.d_out, dtype=tdt, device=dev) for _ in range(nbuf)]
+    ws = torch.empty(hq.workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
+    codes = torch.empty(w.T, w.d_in, dtype=torch.int8, device=dev)
+    s_x = torch.empty(w.T, dtype=torch.float32, device=dev)
+    mu = torch.empty(w.T, dtype=torch.float32, device=dev)
+    U = torch.empty(w.T, w.rank, dtype=torch.float32, device=dev) if w.rank else None
+
+    def step(i):
+        hq.quant_linear(desc, prep, Xs[i % nbuf], out=Ys[i % nbuf], workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # Per-kernel durations: the same two kernels through the stage entry points,
+    # bracketed by events on the stream they run on.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        X = Xs[i % nbuf]
+        evs[i][0].record()
+        hq.act_quantize(desc, prep, X, out=(codes, s_x, mu, U))
+        evs[i][1].record()
+        hq.gemm_dequant(desc, prep, codes, s_x, mu, U, out=Ys[i % nbuf])
+        evs[i][2].record()
+    torch.cuda.synchronize()
+    k1 = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    k2 = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    in_b = 2 if w.dtype == "bf16" else 4
+    k1_bytes = w.T * (w.d_in * (in_b + 1) + 8 + 4 * w.rank)       # read X, write codes, s_x, mu, U
+    k2_ops = 2.0 * w.T * w.d_in * w.d_out                          # int8 multiply-adds x 2
+    k1_gbs = k1_bytes / (k1 * 1e-3) / 1e9
+    k2_tops = k2_ops / (k2 * 1e-3) / 1e12
+    tokens_s = w.T / (ms * 1e-3)
+    eff_tops = k2_ops / (ms * 1e-3) / 1e12
+    if k2 >= k1:
+        roof = {"kernel": "gemm_i8_dequant", "bound": "mfma", "achieved": round(k2_tops, 2),
+                "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "ops": "int8 multiply-add x2",
+                "frac": round(k2_tops / INT8_PEAK_TOPS, 4), "traffic": None}
+    else:
+        roof = {"kernel": "row_transform", "bound": "hbm", "achieved": round(k1_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None}
+    out = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
+                   "block": w.block, "bits": f"W{w.w_bits}A{w.a_bits}", "center": bool(w.center),
+                   "smooth_alpha": w.alpha, "rank": w.rank, "io_dtype": w.dtype},
+        "effective_tops": round(eff_tops, 2),
+        "roofline": roof,
+        "kernels": {
+            "row_transform_ms": round(k1, 5), "row_transform_GBs": round(k1_gbs, 1),
+            "row_transform_hbm_frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+            "gemm_ms": round(k2, 5), "gemm_TOPS": round(k2_tops, 2),
+            "gemm_mfma_frac": round(k2_tops / INT8_PEAK_TOPS, 4),
+        },
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        sig = None if S is None else S.cpu().numpy()
+        out["cpu_baseline"] = cpu_baseline(w, x, weight, bias, sig, l1, l2, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

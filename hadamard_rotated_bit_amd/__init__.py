@@ -1,0 +1,236 @@
+"""hadamard_rotated_bit_amd: the rotated-and-centred low-bit linear layer on MI355X.
+
+A thin Python face over libhq (include/hq.h). Every step of the layer runs in
+the library's HIP kernels; this module only checks tensors, allocates outputs
+and workspaces with torch, and passes device pointers and the current stream.
+
+    desc = Desc(d_in=1152, d_out=4608, block=128, a_bits=4, w_bits=4,
+                center=True, smooth=True, x_dtype=BF16, w_dtype=BF16, y_dtype=BF16)
+    amax = channel_absmax(desc, X_calib)
+    sig = sigma(desc, amax, weight, alpha=0.5)
+    prep = prepare(desc, weight, bias, sig)
+    Y = quant_linear(desc, prep, X)
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import HqDesc, HqError, HqLayout, check, load
+
+F32, BF16 = 0, 1
+_TORCH = {F32: torch.float32, BF16: torch.bfloat16}
+_NAME = {F32: "f32", BF16: "bf16"}
+
+
+@dataclasses.dataclass(frozen=True)
+class Desc:
+    """Layer descriptor; mirrors hq_desc."""
+    d_in: int
+    d_out: int
+    block: int
+    a_bits: int = 4
+    w_bits: int = 4
+    center: bool = True
+    smooth: bool = False
+    rank: int = 0
+    x_dtype: int = F32
+    w_dtype: int = F32
+    y_dtype: int = F32
+
+    def c(self) -> HqDesc:
+        return HqDesc(self.d_in, self.d_out, self.block, self.a_bits, self.w_bits,
+                      int(self.center), int(self.smooth), self.rank, self.x_dtype,
+                      self.w_dtype, self.y_dtype)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def validate(desc: Desc) -> None:
+    check(load().hq_validate(ctypes.byref(desc.c())))
+
+
+def prepared_bytes(desc: Desc) -> int:
+    n = load().hq_prepared_bytes(ctypes.byref(desc.c()))
+    if n == 0:
+        check(load().hq_validate(ctypes.byref(desc.c())))
+    return n
+
+
+def layout(desc: Desc) -> HqLayout:
+    out = HqLayout()
+    check(load().hq_prepared_layout_of(ctypes.byref(desc.c()), ctypes.byref(out)))
+    return out
+
+
+def workspace_bytes(desc: Desc, T: int) -> int:
+    n = load().hq_workspace_bytes(ctypes.byref(desc.c()), T)
+    if n == 0:
+        check(load().hq_validate(ctypes.byref(desc.c())))
+        if T < 0:
+            raise HqError(_lib.HQ_ERR_INVALID_ARG, "T must be >= 0")
+    return n
+
+
+def channel_absmax(desc: Desc, X: torch.Tensor) -> torch.Tensor:
+    """Per-input-channel max |X| over tokens (calibration statistic of HadaNorm Eq. (3))."""
+    T = X.shape[0]
+    _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
+    out = torch.empty(desc.d_in, dtype=torch.float32, device=X.device)
+    check(load().hq_channel_absmax(ctypes.byref(desc.c()), _ptr(X), T, _ptr(out), _stream()))
+    return out
+
+
+def sigma(desc: Desc, act_absmax: torch.Tensor, weight: torch.Tensor, alpha: float) -> torch.Tensor:
+    """Smoothing scales sigma_i = max|X_i|^alpha / max|W_i|^(1-alpha) (HadaNorm Eq. (3))."""
+    _need(act_absmax, "act_absmax", torch.float32, (desc.d_in,))
+    _need(weight, "weight", _TORCH[desc.w_dtype], (desc.d_out, desc.d_in))
+    out = torch.empty(desc.d_in, dtype=torch.float32, device=weight.device)
+    check(load().hq_sigma(ctypes.byref(desc.c()), _ptr(act_absmax), _ptr(weight),
+                          ctypes.c_float(alpha), _ptr(out), _stream()))
+    return out
+
+
+def prepare(desc: Desc, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+            sigma: Optional[torch.Tensor] = None, L1: Optional[torch.Tensor] = None,
+            L2: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Offline weight transform; returns the prepared blob (uint8 device tensor)."""
+    wdt = _TORCH[desc.w_dtype]
+    _need(weight, "weight", wdt, (desc.d_out, desc.d_in))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (desc.d_out,))
+    if sigma is not None:
+        _need(sigma, "sigma", torch.float32, (desc.d_in,))
+    if L1 is not None:
+        _need(L1, "L1", wdt, (desc.d_in, desc.rank))
+    if L2 is not None:
+        _need(L2, "L2", wdt, (desc.rank, desc.d_out))
+    blob = torch.empty(prepared_bytes(desc), dtype=torch.uint8, device=weight.device)
+    check(load().hq_prepare_weights(ctypes.byref(desc.c()), _ptr(weight), _ptr(bias),
+                                    _ptr(sigma), _ptr(L1), _ptr(L2), _ptr(blob), _stream()))
+    return blob
+
+
+def check_prepared(desc: Desc, prepared: torch.Tensor) -> None:
+    check(load().hq_check_prepared(ctypes.byref(desc.c()), _ptr(prepared), _stream()))
+
+
+def quant_linear(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
+                 out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = the quantised layer applied to X [T, d_in]."""
+    T = X.shape[0]
+    _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
+    if out is None:
+        out = torch.empty(T, desc.d_out, dtype=_TORCH[desc.y_dtype], device=X.device)
+    _need(out, "out", _TORCH[desc.y_dtype], (T, desc.d_out))
+    need = workspace_bytes(desc, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    check(load().hq_quant_linear(ctypes.byref(desc.c()), _ptr(prepared), _ptr(X), T, _ptr(out),
+                                 _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def act_quantize(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, out=None):
+    """Activation stage alone: (codes int8 [T, d_in], s_x [T], mu [T], U [T, rank] or None).
+
+    ``out`` may supply that tuple of preallocated tensors."""
+    T = X.shape[0]
+    _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
+    dev = X.device
+    if out is None:
+        codes = torch.empty(T, desc.d_in, dtype=torch.int8, device=dev)
+        s_x = torch.empty(T, dtype=torch.float32, device=dev)
+        mu = torch.empty(T, dtype=torch.float32, device=dev)
+        U = torch.empty(T, desc.rank, dtype=torch.float32, device=dev) if desc.rank else None
+    else:
+        codes, s_x, mu, U = out
+        _need(codes, "codes", torch.int8, (T, desc.d_in))
+        _need(s_x, "s_x", torch.float32, (T,))
+        _need(mu, "mu", torch.float32, (T,))
+        if desc.rank:
+            _need(U, "U", torch.float32, (T, desc.rank))
+    check(load().hq_act_quantize(ctypes.byref(desc.c()), _ptr(prepared), _ptr(X), T, _ptr(codes),
+                                 _ptr(s_x), _ptr(mu), _ptr(U), _stream()))
+    return codes, s_x, mu, U
+
+
+def act_transform(desc: Desc, prepared: torch.Tensor, X: torch.Tensor):
+    """Float X~ (normalised H, centred) and mu, before quantisation (debug export)."""
+    T = X.shape[0]
+    _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
+    xt = torch.empty(T, desc.d_in, dtype=torch.float32, device=X.device)
+    mu = torch.empty(T, dtype=torch.float32, device=X.device)
+    check(load().hq_act_transform(ctypes.byref(desc.c()), _ptr(prepared), _ptr(X), T, _ptr(xt),
+                                  _ptr(mu), _stream()))
+    return xt, mu
+
+
+def gemm_i32(desc: Desc, a_codes: torch.Tensor, w_codes: torch.Tensor) -> torch.Tensor:
+    """int32 accumulators a_codes [T, d_in] . w_codes [N, d_in]^T."""
+    T, N = a_codes.shape[0], w_codes.shape[0]
+    _need(a_codes, "a_codes", torch.int8, (T, desc.d_in))
+    _need(w_codes, "w_codes", torch.int8, (N, desc.d_in))
+    acc = torch.empty(T, N, dtype=torch.int32, device=a_codes.device)
+    check(load().hq_gemm_i32(ctypes.byref(desc.c()), _ptr(a_codes), _ptr(w_codes), T, N,
+                             _ptr(acc), _stream()))
+    return acc
+
+
+def gemm_dequant(desc: Desc, prepared: torch.Tensor, codes: torch.Tensor, s_x: torch.Tensor,
+                 mu: torch.Tensor, U: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GEMM + dequant epilogue alone, from act_quantize's outputs."""
+    T = codes.shape[0]
+    _need(codes, "codes", torch.int8, (T, desc.d_in))
+    _need(s_x, "s_x", torch.float32, (T,))
+    _need(mu, "mu", torch.float32, (T,))
+    if desc.rank:
+        _need(U, "U", torch.float32, (T, desc.rank))
+    Y = out if out is not None else torch.empty(T, desc.d_out, dtype=_TORCH[desc.y_dtype],
+                                                device=codes.device)
+    _need(Y, "out", _TORCH[desc.y_dtype], (T, desc.d_out))
+    check(load().hq_gemm_dequant(ctypes.byref(desc.c()), _ptr(prepared), _ptr(codes), _ptr(s_x),
+                                 _ptr(mu), _ptr(U), T, _ptr(Y), _stream()))
+    return Y
+
+
+def prepared_views(desc: Desc, prepared: torch.Tensor) -> dict:
+    """Views of the arrays inside a prepared blob (for inspection and tests)."""
+    L = layout(desc)
+    npad, d = L.d_out_pad, desc.d_in
+
+    def view(off, n, dtype, shape):
+        nbytes = n * torch.empty(0, dtype=dtype).element_size()
+        return prepared[off:off + nbytes].view(dtype).view(*shape)
+
+    out = {
+        "w_codes": view(L.w_codes, npad * d, torch.int8, (npad, d))[:desc.d_out],
+        "s_w": view(L.w_scale, npad, torch.float32, (npad,))[:desc.d_out],
+        "c": view(L.c, npad, torch.float32, (npad,))[:desc.d_out],
+        "bias": view(L.bias, npad, torch.float32, (npad,))[:desc.d_out],
+        "sigma_inv": view(L.sigma_inv, d, torch.float32, (d,)),
+    }
+    return out

@@ -1,0 +1,449 @@
+// C ABI of libhq: host-side validation, buffer layout and kernel dispatch.
+// Every check runs on the host before anything is enqueued; the library never
+// allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/hq.h"
+#include "hq_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(HQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr uint32_t kMagic = 0x31505148u;  // "HQP1"
+
+struct PreparedHeader {
+  uint32_t magic;
+  uint32_t version;
+  hq_desc desc;
+  int64_t d_out_pad;
+  uint64_t total;
+};
+static_assert(sizeof(PreparedHeader) <= 256, "header fits in 256 bytes");
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+inline int log2i(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+inline float qmax_of(int bits) { return float((1 << (bits - 1)) - 1); }
+
+int check_desc(const hq_desc* d) {
+  if (!d) return fail(HQ_ERR_INVALID_ARG, "desc is NULL");
+  if (d->d_in <= 0 || d->d_out <= 0)
+    return fail(HQ_ERR_INVALID_ARG, "d_in and d_out must be positive (got %d, %d)", d->d_in,
+                d->d_out);
+  if (d->x_dtype != HQ_F32 && d->x_dtype != HQ_BF16)
+    return fail(HQ_ERR_INVALID_ARG, "x_dtype %d is not an hq_dtype", d->x_dtype);
+  if (d->w_dtype != HQ_F32 && d->w_dtype != HQ_BF16)
+    return fail(HQ_ERR_INVALID_ARG, "w_dtype %d is not an hq_dtype", d->w_dtype);
+  if (d->y_dtype != HQ_F32 && d->y_dtype != HQ_BF16)
+    return fail(HQ_ERR_INVALID_ARG, "y_dtype %d is not an hq_dtype", d->y_dtype);
+  if (d->center != 0 && d->center != 1)
+    return fail(HQ_ERR_INVALID_ARG, "center must be 0 or 1 (got %d)", d->center);
+  if (d->smooth != 0 && d->smooth != 1)
+    return fail(HQ_ERR_INVALID_ARG, "smooth must be 0 or 1 (got %d)", d->smooth);
+  if (d->a_bits != 4 && d->a_bits != 8)
+    return fail(HQ_ERR_UNSUPPORTED, "a_bits must be 4 or 8 (got %d)", d->a_bits);
+  if (d->w_bits != 4 && d->w_bits != 8)
+    return fail(HQ_ERR_UNSUPPORTED, "w_bits must be 4 or 8 (got %d)", d->w_bits);
+  hq::RowGeom g;
+  if (d->d_in % 128 || !hq::row_geometry(d->d_in, &g))
+    return fail(HQ_ERR_UNSUPPORTED,
+                "d_in %d unsupported: need a multiple of 128 up to 2048, of 256 up to 4096, or "
+                "of 512 up to 8192",
+                d->d_in);
+  if (d->d_out % 8)
+    return fail(HQ_ERR_UNSUPPORTED, "d_out must be a multiple of 8 (got %d)", d->d_out);
+  if (!is_pow2(d->block) || d->d_in % d->block)
+    return fail(HQ_ERR_UNSUPPORTED, "block %d must be a power of two dividing d_in %d", d->block,
+                d->d_in);
+  if (d->rank < 0 || d->rank > 64 || d->rank % 16)
+    return fail(HQ_ERR_UNSUPPORTED, "rank must be 0, 16, 32, 48 or 64 (got %d)", d->rank);
+  return HQ_OK;
+}
+
+void layout_of(const hq_desc* d, hq_prepared_layout* L) {
+  const int64_t np = round_up(d->d_out, hq::GEMM_BN);
+  size_t off = 256;
+  L->d_out_pad = np;
+  L->w_codes = off;
+  off += align256(size_t(np) * d->d_in);
+  L->w_scale = off;
+  off += align256(4 * size_t(np));
+  L->c = off;
+  off += align256(4 * size_t(np));
+  L->bias = off;
+  off += align256(4 * size_t(np));
+  L->sigma_inv = off;
+  off += align256(4 * size_t(d->d_in));
+  L->l1_hi = off;
+  off += align256(2 * size_t(d->rank) * d->d_in);
+  L->l1_lo = off;
+  off += align256(2 * size_t(d->rank) * d->d_in);
+  L->l2_hi = off;
+  off += align256(2 * size_t(np) * d->rank);
+  L->l2_lo = off;
+  off += align256(2 * size_t(np) * d->rank);
+  L->total = off;
+}
+
+struct Workspace {
+  size_t codes, s_x, mu, U, total;
+};
+Workspace workspace_of(const hq_desc* d, int64_t T) {
+  Workspace w;
+  size_t off = 0;
+  w.codes = off;
+  off += align256(size_t(T) * d->d_in);
+  w.s_x = off;
+  off += align256(4 * size_t(T));
+  w.mu = off;
+  off += align256(4 * size_t(T));
+  w.U = off;
+  off += align256(4 * size_t(T) * d->rank);
+  w.total = off;
+  return w;
+}
+
+template <typename P>
+inline P* at(void* base, size_t off) {
+  return reinterpret_cast<P*>(static_cast<uint8_t*>(base) + off);
+}
+template <typename P>
+inline const P* at(const void* base, size_t off) {
+  return reinterpret_cast<const P*>(static_cast<const uint8_t*>(base) + off);
+}
+
+// Activation stage shared by hq_quant_linear and hq_act_quantize.
+int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, int8_t* codes,
+            float* s_x, float* mu, float* U, hipStream_t s) {
+  hq_prepared_layout L;
+  layout_of(d, &L);
+  hq::RowArgs a = {};
+  a.in = X;
+  a.in_bf16 = d->x_dtype == HQ_BF16;
+  a.rows = T;
+  a.d = d->d_in;
+  a.scale = d->smooth ? at<float>(prepared, L.sigma_inv) : nullptr;
+  a.log2b = log2i(d->block);
+  a.center = d->center;
+  a.qmax = qmax_of(d->a_bits);
+  a.codes = codes;
+  a.out_s = s_x;
+  a.out_aux = mu;
+  a.mode = hq::ROW_ACT;
+  hipError_t e = hq::launch_row_transform(a, s);
+  if (e != hipSuccess) return hip_fail(e, "activation kernel launch");
+  if (d->rank) {
+    e = hq::launch_lowrank_down(X, a.in_bf16, T, d->d_in, d->rank,
+                                at<uint16_t>(prepared, L.l1_hi), at<uint16_t>(prepared, L.l1_lo),
+                                U, s);
+    if (e != hipSuccess) return hip_fail(e, "low-rank kernel launch");
+  }
+  return HQ_OK;
+}
+
+int run_gemm_dequant(const hq_desc* d, const void* prepared, const int8_t* codes,
+                     const float* s_x, const float* mu, const float* U, int64_t T, void* Y,
+                     hipStream_t s) {
+  hq_prepared_layout L;
+  layout_of(d, &L);
+  hq::GemmEpi ep = {};
+  ep.s_x = s_x;
+  ep.mu = mu;
+  ep.s_w = at<float>(prepared, L.w_scale);
+  ep.c = at<float>(prepared, L.c);
+  ep.bias = at<float>(prepared, L.bias);
+  ep.U = U;
+  ep.l2_hi = at<uint16_t>(prepared, L.l2_hi);
+  ep.l2_lo = at<uint16_t>(prepared, L.l2_lo);
+  ep.rank = d->rank;
+  ep.Y = Y;
+  ep.y_bf16 = d->y_dtype == HQ_BF16;
+  ep.ldy = d->d_out;
+  hipError_t e = hq::launch_gemm(codes, T, at<int8_t>(prepared, L.w_codes), d->d_out, d->d_in,
+                                 nullptr, 0, &ep, s);
+  if (e != hipSuccess) return hip_fail(e, "GEMM kernel launch");
+  return HQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hq_abi_version(void) { return HQ_ABI_VERSION; }
+
+const char* hq_last_error(void) { return g_err.c_str(); }
+
+const char* hq_status_str(int status) {
+  switch (status) {
+    case HQ_OK: return "HQ_OK";
+    case HQ_ERR_INVALID_ARG: return "HQ_ERR_INVALID_ARG";
+    case HQ_ERR_UNSUPPORTED: return "HQ_ERR_UNSUPPORTED";
+    case HQ_ERR_WORKSPACE: return "HQ_ERR_WORKSPACE";
+    case HQ_ERR_BAD_PREPARED: return "HQ_ERR_BAD_PREPARED";
+    case HQ_ERR_HIP: return "HQ_ERR_HIP";
+    default: return "HQ_ERR_UNKNOWN";
+  }
+}
+
+int hq_validate(const hq_desc* desc) {
+  g_err.clear();
+  return check_desc(desc);
+}
+
+size_t hq_prepared_bytes(const hq_desc* desc) {
+  g_err.clear();
+  if (check_desc(desc) != HQ_OK) return 0;
+  hq_prepared_layout L;
+  layout_of(desc, &L);
+  return L.total;
+}
+
+int hq_prepared_layout_of(const hq_desc* desc, hq_prepared_layout* out) {
+  g_err.clear();
+  if (!out) return fail(HQ_ERR_INVALID_ARG, "out is NULL");
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  layout_of(desc, out);
+  return HQ_OK;
+}
+
+size_t hq_workspace_bytes(const hq_desc* desc, int64_t T) {
+  g_err.clear();
+  if (check_desc(desc) != HQ_OK) return 0;
+  if (T < 0) {
+    fail(HQ_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+    return 0;
+  }
+  return workspace_of(desc, T).total;
+}
+
+int hq_channel_absmax(const hq_desc* desc, const void* X, int64_t T, float* absmax,
+                      void* stream) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0");
+  if (!absmax || (T > 0 && !X)) return fail(HQ_ERR_INVALID_ARG, "X or absmax is NULL");
+  hipError_t e = hq::launch_col_absmax(X, desc->x_dtype == HQ_BF16, T, desc->d_in, absmax,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HQ_OK : hip_fail(e, "absmax kernel launch");
+}
+
+int hq_sigma(const hq_desc* desc, const float* act_absmax, const void* weight, float alpha,
+             float* sigma, void* stream) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  if (!act_absmax || !weight || !sigma)
+    return fail(HQ_ERR_INVALID_ARG, "act_absmax, weight and sigma must be non-NULL");
+  if (!(alpha >= 0.0f && alpha <= 1.0f))
+    return fail(HQ_ERR_INVALID_ARG, "alpha must lie in [0, 1] (got %g)", double(alpha));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Weight channel maxima land in `sigma`, then are turned into sigma in place.
+  hipError_t e = hq::launch_col_absmax(weight, desc->w_dtype == HQ_BF16, desc->d_out, desc->d_in,
+                                       sigma, s);
+  if (e == hipSuccess) e = hq::launch_sigma_finish(act_absmax, alpha, 1e-5f, desc->d_in, sigma, s);
+  return e == hipSuccess ? HQ_OK : hip_fail(e, "sigma kernel launch");
+}
+
+int hq_prepare_weights(const hq_desc* desc, const void* weight, const float* bias,
+                       const float* sigma, const void* L1, const void* L2, void* prepared,
+                       void* stream) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  if (!weight || !prepared) return fail(HQ_ERR_INVALID_ARG, "weight and prepared must be non-NULL");
+  if (desc->smooth && !sigma) return fail(HQ_ERR_INVALID_ARG, "smooth = 1 needs sigma");
+  if (!desc->smooth && sigma) return fail(HQ_ERR_INVALID_ARG, "smooth = 0 takes no sigma");
+  if (desc->rank && (!L1 || !L2)) return fail(HQ_ERR_INVALID_ARG, "rank > 0 needs L1 and L2");
+  if (!desc->rank && (L1 || L2)) return fail(HQ_ERR_INVALID_ARG, "rank = 0 takes no L1/L2");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hq_prepared_layout L;
+  layout_of(desc, &L);
+  const int64_t np = L.d_out_pad, dout = desc->d_out, din = desc->d_in;
+  hipError_t e = hipSuccess;
+  // Padding rows of the code matrix and of the per-channel vectors are zero.
+  if (np > dout) {
+    e = hq::launch_fill_u8(at<uint8_t>(prepared, L.w_codes + size_t(dout) * din), 0,
+                           size_t(np - dout) * din, s);
+  }
+  if (e == hipSuccess)
+    e = hq::launch_fill_u32(at<uint32_t>(prepared, L.w_scale), 0u, (L.sigma_inv - L.w_scale) / 4, s);
+  if (e == hipSuccess) {
+    if (desc->smooth)
+      e = hq::launch_reciprocal(sigma, at<float>(prepared, L.sigma_inv), int(din), s);
+    else
+      e = hq::launch_fill_u32(at<uint32_t>(prepared, L.sigma_inv), 0x3F800000u, size_t(din), s);
+  }
+  if (e == hipSuccess && bias) e = hq::launch_copy_f32(bias, at<float>(prepared, L.bias), size_t(dout), s);
+  if (e == hipSuccess) {
+    hq::RowArgs a = {};
+    a.in = weight;
+    a.in_bf16 = desc->w_dtype == HQ_BF16;
+    a.rows = dout;
+    a.d = int(din);
+    a.scale = desc->smooth ? sigma : nullptr;
+    a.log2b = log2i(desc->block);
+    a.center = 0;
+    a.qmax = qmax_of(desc->w_bits);
+    a.codes = at<int8_t>(prepared, L.w_codes);
+    a.out_s = at<float>(prepared, L.w_scale);
+    a.out_aux = at<float>(prepared, L.c);
+    a.mode = hq::ROW_WEIGHT;
+    e = hq::launch_row_transform(a, s);
+  }
+  if (e == hipSuccess && desc->rank) {
+    e = hq::launch_prep_l1(L1, desc->w_dtype == HQ_BF16,
+                           desc->smooth ? at<float>(prepared, L.sigma_inv) : nullptr, int(din),
+                           desc->rank, at<uint16_t>(prepared, L.l1_hi),
+                           at<uint16_t>(prepared, L.l1_lo), s);
+    if (e == hipSuccess)
+      e = hq::launch_prep_l2(L2, desc->w_dtype == HQ_BF16, desc->rank, int(dout), int(np),
+                             at<uint16_t>(prepared, L.l2_hi), at<uint16_t>(prepared, L.l2_lo), s);
+  }
+  if (e == hipSuccess) {
+    PreparedHeader h = {};
+    h.magic = kMagic;
+    h.version = HQ_ABI_VERSION;
+    h.desc = *desc;
+    h.d_out_pad = np;
+    h.total = L.total;
+    e = hq::launch_write_header(&h, sizeof(h), prepared, s);
+  }
+  return e == hipSuccess ? HQ_OK : hip_fail(e, "prepare kernel launch");
+}
+
+int hq_check_prepared(const hq_desc* desc, const void* prepared, void* stream) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  if (!prepared) return fail(HQ_ERR_INVALID_ARG, "prepared is NULL");
+  PreparedHeader h;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&h, prepared, sizeof(h), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the prepared header");
+  hq_prepared_layout L;
+  layout_of(desc, &L);
+  if (h.magic != kMagic) return fail(HQ_ERR_BAD_PREPARED, "prepared blob has no libhq header");
+  if (h.version != HQ_ABI_VERSION)
+    return fail(HQ_ERR_BAD_PREPARED, "prepared blob version %u != %d", h.version, HQ_ABI_VERSION);
+  if (std::memcmp(&h.desc, desc, sizeof(hq_desc)) != 0 || h.total != L.total)
+    return fail(HQ_ERR_BAD_PREPARED, "prepared blob was made for a different descriptor");
+  return HQ_OK;
+}
+
+int hq_quant_linear(const hq_desc* desc, const void* prepared, const void* X, int64_t T, void* Y,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+  if (T == 0) return HQ_OK;
+  if (!prepared || !X || !Y || !workspace)
+    return fail(HQ_ERR_INVALID_ARG, "prepared, X, Y and workspace must be non-NULL");
+  const Workspace w = workspace_of(desc, T);
+  if (workspace_bytes < w.total)
+    return fail(HQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, w.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int8_t* codes = at<int8_t>(workspace, w.codes);
+  float* s_x = at<float>(workspace, w.s_x);
+  float* mu = at<float>(workspace, w.mu);
+  float* U = desc->rank ? at<float>(workspace, w.U) : nullptr;
+  st = run_act(desc, prepared, X, T, codes, s_x, mu, U, s);
+  if (st != HQ_OK) return st;
+  return run_gemm_dequant(desc, prepared, codes, s_x, mu, U, T, Y, s);
+}
+
+int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
+                    int8_t* codes, float* s_x, float* mu, float* U, void* stream) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0");
+  if (T == 0) return HQ_OK;
+  if (!prepared || !X || !codes || !s_x || !mu || (desc->rank && !U))
+    return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  return run_act(desc, prepared, X, T, codes, s_x, mu, U, static_cast<hipStream_t>(stream));
+}
+
+int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
+                     float* Xt, float* mu, void* stream) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0");
+  if (T == 0) return HQ_OK;
+  if (!prepared || !X || !Xt || !mu) return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  hq_prepared_layout L;
+  layout_of(desc, &L);
+  hq::RowArgs a = {};
+  a.in = X;
+  a.in_bf16 = desc->x_dtype == HQ_BF16;
+  a.rows = T;
+  a.d = desc->d_in;
+  a.scale = desc->smooth ? at<float>(prepared, L.sigma_inv) : nullptr;
+  a.log2b = log2i(desc->block);
+  a.center = desc->center;
+  a.qmax = qmax_of(desc->a_bits);
+  a.out_aux = mu;
+  a.out_xt = Xt;
+  a.mode = hq::ROW_EXPORT;
+  hipError_t e = hq::launch_row_transform(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HQ_OK : hip_fail(e, "transform kernel launch");
+}
+
+int hq_gemm_i32(const hq_desc* desc, const int8_t* a_codes, const int8_t* w_codes, int64_t T,
+                int64_t N, int32_t* acc, void* stream) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  if (T < 0 || N <= 0 || N % 8) return fail(HQ_ERR_INVALID_ARG, "need T >= 0 and N a positive multiple of 8");
+  if (T == 0) return HQ_OK;
+  if (!a_codes || !w_codes || !acc) return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  hipError_t e = hq::launch_gemm(a_codes, T, w_codes, N, desc->d_in, acc, N, nullptr,
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HQ_OK : hip_fail(e, "GEMM kernel launch");
+}
+
+int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const int8_t* codes,
+                    const float* s_x, const float* mu, const float* U, int64_t T, void* Y,
+                    void* stream) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0");
+  if (T == 0) return HQ_OK;
+  if (!prepared || !codes || !s_x || !mu || !Y || (desc->rank && !U))
+    return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  return run_gemm_dequant(desc, prepared, codes, s_x, mu, U, T, Y,
+                          static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

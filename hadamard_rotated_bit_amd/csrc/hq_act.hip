@@ -1,0 +1,516 @@
+// Activation-side and offline kernels of libhq for gfx950:
+//  * the fused per-row transform (scale -> fast Walsh-Hadamard transform ->
+//    mean -> absmax -> symmetric quantise), used online for activations and
+//    offline for the weights;
+//  * per-channel absmax and the smoothing scale of HadaNorm Eq. (3);
+//  * the low-rank down projection U = x' L1 (bf16 MFMA, split operands);
+//  * small preparation helpers (fills, reciprocal, factor splitting).
+#include "hq_device.h"
+#include "hq_internal.h"
+
+namespace hq {
+
+// ---------------------------------------------------------------------------
+// Row geometry. A row of d channels is spread over G consecutive lanes of a
+// wave; lane t holds C chunks of 8 consecutive channels:
+//     channel e = c * 8G + t * 8 + j,   j in [0, 8), c in [0, C).
+// Each chunk load is one coalesced 8G-channel segment per row. The bits of e
+// split into j (3 bits, in registers), t (log2 G bits, across lanes) and c
+// (in registers), so a butterfly stage of the Walsh-Hadamard transform on
+// bit b is either an in-register add/sub pair or one cross-lane exchange.
+// The smallest G that keeps C <= 16 is chosen, which minimises cross-lane
+// stages.
+// ---------------------------------------------------------------------------
+bool row_geometry(int d, RowGeom* g) {
+  const int cands[3] = {16, 32, 64};
+  for (int i = 0; i < 3; ++i) {
+    const int G = cands[i];
+    if (d % (8 * G)) continue;
+    const int C = d / (8 * G);
+    if (C >= 1 && C <= 16) {
+      g->G = G;
+      g->C = C;
+      return true;
+    }
+  }
+  return false;
+}
+
+// One wave processes 64/G rows at once; a 256-thread block covers 4 waves.
+//
+// Per row (HadaNorm Eq. (1) activation side, HaTQ Eq. (3) quantiser):
+//   x' = x * scale                      (scale = 1/sigma; sigma for weights)
+//   y' = H~ x' per block                (unnormalised Sylvester butterflies;
+//                                        1/sqrt(B) is folded into the scales)
+//   mu' = sum(y') / d                   (if centring)
+//   amax' = max |y' - mu'|              (= max(max y' - mu', mu' - min y'))
+//   q = rint((y' - mu') * qmax / amax') (ties to even, fp32)
+//   s = amax' / (sqrt(B) qmax),  mu = mu' / sqrt(B),  c = sum(y') / sqrt(B)
+template <typename TIn, int G, int C>
+__global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv_sqrt_b) {
+  constexpr int LOG2G = (G == 16) ? 4 : (G == 32) ? 5 : 6;
+  constexpr int E = 8 * C;
+  constexpr int RPW = 64 / G;
+  const int lane = threadIdx.x & 63;
+  const int t = lane & (G - 1);
+  const int64_t row = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW + lane / G;
+  const bool valid = row < a.rows;
+  const int64_t r = valid ? row : a.rows - 1;
+  const int d = a.d;
+  const TIn* src = static_cast<const TIn*>(a.in) + r * d + t * 8;
+
+  float v[E];
+#pragma unroll
+  for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
+  if (a.scale) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      float s[8];
+      load8(a.scale + c * 8 * G + t * 8, s);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[c * 8 + j] *= s[j];
+    }
+  }
+
+  // Butterflies on channel bits 0..2 (in registers).
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    if (b < a.log2b) {
+      const int h = 1 << b;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (!(e & h)) {
+          const float x = v[e], y = v[e + h];
+          v[e] = x + y;
+          v[e + h] = x - y;
+        }
+      }
+    }
+  }
+  // Bits 3 .. 3+log2G-1 (across lanes): lower partner keeps x+y, upper x-y.
+#pragma unroll
+  for (int b = 0; b < LOG2G; ++b) {
+    if (b + 3 < a.log2b) {
+      const int m = 1 << b;
+      const float sg = (t & m) ? -1.0f : 1.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float p = xor_shfl(v[e], m);
+        v[e] = fmaf(sg, v[e], p);
+      }
+    }
+  }
+  // Remaining bits index chunks (in registers).
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int h = 1 << b;
+    if (h < C && b + 3 + LOG2G < a.log2b) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        if (!(c & h) && c + h < C) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = v[c * 8 + j], y = v[(c + h) * 8 + j];
+            v[c * 8 + j] = x + y;
+            v[(c + h) * 8 + j] = x - y;
+          }
+        }
+      }
+    }
+  }
+
+  // Row reductions: sum, max, min (bit-identical on every lane of the row).
+  float sum = 0.0f, mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    sum += v[e];
+    mx = fmaxf(mx, v[e]);
+    mn = fminf(mn, v[e]);
+  }
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) {
+    sum += xor_shfl(sum, m);
+    mx = fmaxf(mx, xor_shfl(mx, m));
+    mn = fminf(mn, xor_shfl(mn, m));
+  }
+
+  const int64_t base = row * d + t * 8;
+  if (a.mode == ROW_WEIGHT) {
+    const float amax = fmaxf(mx, -mn);
+    const float rcp = amax > 0.0f ? a.qmax / amax : 0.0f;
+    if (valid) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t p = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float q = fminf(fmaxf(v[c * 8 + h * 4 + j] * rcp, -a.qmax), a.qmax);
+            p |= rne_byte(q) << (8 * j);
+          }
+          w[h] = p;
+        }
+        *reinterpret_cast<uint2*>(a.codes + base + c * 8 * G) = make_uint2(w[0], w[1]);
+      }
+      if (t == 0) {
+        a.out_s[row] = amax * inv_sqrt_b / a.qmax;
+        a.out_aux[row] = sum * inv_sqrt_b;
+      }
+    }
+    return;
+  }
+
+  const float mu = a.center ? sum / float(d) : 0.0f;
+  if (a.mode == ROW_EXPORT) {
+    if (valid) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float* o = a.out_xt + base + c * 8 * G;
+        reinterpret_cast<float4*>(o)[0] =
+            make_float4((v[c * 8 + 0] - mu) * inv_sqrt_b, (v[c * 8 + 1] - mu) * inv_sqrt_b,
+                        (v[c * 8 + 2] - mu) * inv_sqrt_b, (v[c * 8 + 3] - mu) * inv_sqrt_b);
+        reinterpret_cast<float4*>(o)[1] =
+            make_float4((v[c * 8 + 4] - mu) * inv_sqrt_b, (v[c * 8 + 5] - mu) * inv_sqrt_b,
+                        (v[c * 8 + 6] - mu) * inv_sqrt_b, (v[c * 8 + 7] - mu) * inv_sqrt_b);
+      }
+      if (t == 0) a.out_aux[row] = mu * inv_sqrt_b;
+    }
+    return;
+  }
+
+  const float amax = fmaxf(mx - mu, mu - mn);
+  const float rcp = amax > 0.0f ? a.qmax / amax : 0.0f;
+  if (valid) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      uint32_t w[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float q = fminf(fmaxf((v[c * 8 + h * 4 + j] - mu) * rcp, -a.qmax), a.qmax);
+          p |= rne_byte(q) << (8 * j);
+        }
+        w[h] = p;
+      }
+      *reinterpret_cast<uint2*>(a.codes + base + c * 8 * G) = make_uint2(w[0], w[1]);
+    }
+    if (t == 0) {
+      a.out_s[row] = amax * inv_sqrt_b / a.qmax;
+      a.out_aux[row] = mu * inv_sqrt_b;
+    }
+  }
+}
+
+template <typename TIn, int G>
+static hipError_t launch_row_g(const RowArgs& a, int C, hipStream_t s) {
+  const int rpw = 64 / G;
+  const int64_t blocks = (a.rows + 4 * rpw - 1) / (4 * rpw);
+  const float isb = 1.0f / sqrtf(float(1 << a.log2b));
+  dim3 grid{unsigned(blocks)}, block{256};
+#define HQ_ROW_CASE(CC)                                                        \
+  case CC:                                                                     \
+    hipLaunchKernelGGL((row_transform_kernel<TIn, G, CC>), grid, block, 0, s, a, isb); \
+    break;
+  switch (C) {
+    HQ_ROW_CASE(1) HQ_ROW_CASE(2) HQ_ROW_CASE(3) HQ_ROW_CASE(4)
+    HQ_ROW_CASE(5) HQ_ROW_CASE(6) HQ_ROW_CASE(7) HQ_ROW_CASE(8)
+    HQ_ROW_CASE(9) HQ_ROW_CASE(10) HQ_ROW_CASE(11) HQ_ROW_CASE(12)
+    HQ_ROW_CASE(13) HQ_ROW_CASE(14) HQ_ROW_CASE(15) HQ_ROW_CASE(16)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef HQ_ROW_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_row_transform(const RowArgs& a, hipStream_t s) {
+  RowGeom g;
+  if (!row_geometry(a.d, &g)) return hipErrorInvalidValue;
+  if (a.rows <= 0) return hipSuccess;
+  if (a.in_bf16) {
+    if (g.G == 16) return launch_row_g<uint16_t, 16>(a, g.C, s);
+    if (g.G == 32) return launch_row_g<uint16_t, 32>(a, g.C, s);
+    return launch_row_g<uint16_t, 64>(a, g.C, s);
+  }
+  if (g.G == 16) return launch_row_g<float, 16>(a, g.C, s);
+  if (g.G == 32) return launch_row_g<float, 32>(a, g.C, s);
+  return launch_row_g<float, 64>(a, g.C, s);
+}
+
+// ---------------------------------------------------------------------------
+// Per-channel absmax over rows (calibration statistic of HadaNorm Eq. (3)).
+// Thread = 8 consecutive channels over a strip of rows; strips combine with an
+// unsigned atomic max on the float bit patterns (valid for values >= 0).
+// ---------------------------------------------------------------------------
+template <typename TIn>
+__global__ __launch_bounds__(256) void col_absmax_kernel(const TIn* __restrict__ in, int64_t rows,
+                                                         int d, int64_t strip,
+                                                         uint32_t* __restrict__ out) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= d / 8) return;
+  const int64_t r0 = int64_t(blockIdx.y) * strip;
+  const int64_t r1 = r0 + strip < rows ? r0 + strip : rows;
+  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t r = r0; r < r1; ++r) {
+    float v[8];
+    load8(in + r * d + g * 8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(v[j]));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) atomicMax(out + g * 8 + j, __float_as_uint(m[j]));
+}
+
+hipError_t launch_col_absmax(const void* in, int in_bf16, int64_t rows, int d, float* absmax,
+                             hipStream_t s) {
+  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(absmax), 0u, size_t(d), s);
+  if (e != hipSuccess || rows <= 0) return e;
+  const int64_t strip = 64;
+  const int64_t strips = (rows + strip - 1) / strip;
+  dim3 grid{unsigned((d / 8 + 255) / 256), unsigned(strips)}, block{256};
+  if (in_bf16)
+    hipLaunchKernelGGL(col_absmax_kernel<uint16_t>, grid, block, 0, s,
+                       static_cast<const uint16_t*>(in), rows, d, strip,
+                       reinterpret_cast<uint32_t*>(absmax));
+  else
+    hipLaunchKernelGGL(col_absmax_kernel<float>, grid, block, 0, s, static_cast<const float*>(in),
+                       rows, d, strip, reinterpret_cast<uint32_t*>(absmax));
+  return hipGetLastError();
+}
+
+__global__ void sigma_finish_kernel(const float* __restrict__ ax, float alpha, float eps, int d,
+                                    float* __restrict__ sigma) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= d) return;
+  const float aw = sigma[i];
+  sigma[i] = powf(fmaxf(ax[i], eps), alpha) / powf(fmaxf(aw, eps), 1.0f - alpha);
+}
+
+hipError_t launch_sigma_finish(const float* ax, float alpha, float eps, int d, float* sigma,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(sigma_finish_kernel, dim3((d + 255) / 256), dim3(256), 0, s, ax, alpha, eps, d,
+                     sigma);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Small helpers (kernels rather than hipMemset/hipMemcpy so that a caller may
+// capture them in a graph).
+// ---------------------------------------------------------------------------
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += size_t(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+__global__ void fill_u8_kernel(uint8_t* p, uint8_t v, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += size_t(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+__global__ void copy_f32_kernel(const float* src, float* dst, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += size_t(gridDim.x) * blockDim.x)
+    dst[i] = src[i];
+}
+__global__ void reciprocal_kernel(const float* src, float* dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = 1.0f / src[i];
+}
+
+static unsigned grid_for(size_t n) {
+  size_t b = (n + 255) / 256;
+  if (b > 4096) b = 4096;
+  return unsigned(b ? b : 1);
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s) {
+  if (!n) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(n)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+hipError_t launch_fill_u8(uint8_t* p, uint8_t v, size_t n, hipStream_t s) {
+  if (!n) return hipSuccess;
+  hipLaunchKernelGGL(fill_u8_kernel, dim3(grid_for(n)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s) {
+  if (!n) return hipSuccess;
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+hipError_t launch_reciprocal(const float* src, float* dst, int n, hipStream_t s) {
+  hipLaunchKernelGGL(reciprocal_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+struct Header256 {
+  uint32_t w[64];
+};
+__global__ void write_header_kernel(Header256 h, uint32_t* dst) {
+  if (threadIdx.x < 64) dst[threadIdx.x] = h.w[threadIdx.x];
+}
+hipError_t launch_write_header(const void* host_hdr, size_t bytes, void* dst, hipStream_t s) {
+  if (bytes > sizeof(Header256)) return hipErrorInvalidValue;
+  Header256 h = {};
+  const uint8_t* src = static_cast<const uint8_t*>(host_hdr);
+  uint8_t* hb = reinterpret_cast<uint8_t*>(h.w);
+  for (size_t i = 0; i < bytes; ++i) hb[i] = src[i];
+  hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, s, h, static_cast<uint32_t*>(dst));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Low-rank factor preparation: split fp32 values into bf16 hi + bf16 lo so a
+// bf16 MFMA product keeps ~16 significant bits.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void split_bf16(float v, uint16_t* hi, uint16_t* lo) {
+  const uint16_t h = f32_to_bf16(v);
+  *hi = h;
+  *lo = f32_to_bf16(v - bf16_to_f32(h));
+}
+
+template <typename TIn>
+__device__ __forceinline__ float load1(const TIn* p, int64_t i);
+template <>
+__device__ __forceinline__ float load1<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+// out[k, i] = l1[i, k] / sigma_i  (transposed to K-contiguous rows)
+template <typename TIn>
+__global__ void prep_l1_kernel(const TIn* __restrict__ l1, const float* __restrict__ sinv, int d,
+                               int r, uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(d) * r) return;
+  const int k = int(idx / d), i = int(idx % d);
+  const float v = load1(l1, int64_t(i) * r + k) * (sinv ? sinv[i] : 1.0f);
+  split_bf16(v, hi + idx, lo + idx);
+}
+// out[j, k] = l2[k, j] for j < n; zero rows up to n_pad
+template <typename TIn>
+__global__ void prep_l2_kernel(const TIn* __restrict__ l2, int r, int n, int n_pad,
+                               uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(n_pad) * r) return;
+  const int j = int(idx / r), k = int(idx % r);
+  const float v = j < n ? load1(l2, int64_t(k) * n + j) : 0.0f;
+  split_bf16(v, hi + idx, lo + idx);
+}
+
+hipError_t launch_prep_l1(const void* l1, int bf16, const float* sigma_inv, int d, int r,
+                          uint16_t* hi, uint16_t* lo, hipStream_t s) {
+  const int64_t n = int64_t(d) * r;
+  dim3 grid{unsigned((n + 255) / 256)}, block{256};
+  if (bf16)
+    hipLaunchKernelGGL(prep_l1_kernel<uint16_t>, grid, block, 0, s,
+                       static_cast<const uint16_t*>(l1), sigma_inv, d, r, hi, lo);
+  else
+    hipLaunchKernelGGL(prep_l1_kernel<float>, grid, block, 0, s, static_cast<const float*>(l1),
+                       sigma_inv, d, r, hi, lo);
+  return hipGetLastError();
+}
+hipError_t launch_prep_l2(const void* l2, int bf16, int r, int n, int n_pad, uint16_t* hi,
+                          uint16_t* lo, hipStream_t s) {
+  const int64_t tot = int64_t(n_pad) * r;
+  dim3 grid{unsigned((tot + 255) / 256)}, block{256};
+  if (bf16)
+    hipLaunchKernelGGL(prep_l2_kernel<uint16_t>, grid, block, 0, s,
+                       static_cast<const uint16_t*>(l2), r, n, n_pad, hi, lo);
+  else
+    hipLaunchKernelGGL(prep_l2_kernel<float>, grid, block, 0, s, static_cast<const float*>(l2), r,
+                       n, n_pad, hi, lo);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Low-rank down projection U = x . (l1_hi + l1_lo)^T  (blog steps 3-4: the
+// 16-bit branch sees the smoothed, un-rotated input; 1/sigma is folded into
+// l1). v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16), channels
+// 8*(l/16) .. +8 of a 32-channel step; B likewise with the rank index.
+// A 256-thread block owns 16 rows; its 4 waves split the channels into
+// quarters and add their partial 16 x R tiles through LDS.
+// fp32 inputs are split into bf16 hi + lo as well (3 products).
+// ---------------------------------------------------------------------------
+template <typename TIn, int R>
+__global__ __launch_bounds__(256) void lowrank_down_kernel(const TIn* __restrict__ x, int64_t rows,
+                                                           int d, const uint16_t* __restrict__ l1hi,
+                                                           const uint16_t* __restrict__ l1lo,
+                                                           float* __restrict__ U) {
+  constexpr int NG = R / 16;
+  __shared__ float red[4][16][R + 1];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row0 = int64_t(blockIdx.x) * 16;
+  int64_t row = row0 + (lane & 15);
+  if (row >= rows) row = rows - 1;
+  const int kq = (lane >> 4) * 8;
+  v4f acc[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) acc[g] = v4f{0, 0, 0, 0};
+  const int kbeg = w * (d / 4), kend = kbeg + d / 4;
+  for (int k0 = kbeg; k0 < kend; k0 += 32) {
+    v8bf ahi, alo;
+    if constexpr (sizeof(TIn) == 2) {
+      ahi = *reinterpret_cast<const v8bf*>(x + row * d + k0 + kq);
+    } else {
+      float f[8];
+      load8(reinterpret_cast<const float*>(x) + row * d + k0 + kq, f);
+      uint16_t h[8], l[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) split_bf16(f[j], &h[j], &l[j]);
+      ahi = *reinterpret_cast<v8bf*>(h);
+      alo = *reinterpret_cast<v8bf*>(l);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int64_t off = int64_t(g * 16 + (lane & 15)) * d + k0 + kq;
+      const v8bf bhi = *reinterpret_cast<const v8bf*>(l1hi + off);
+      const v8bf blo = *reinterpret_cast<const v8bf*>(l1lo + off);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc[g], 0, 0, 0);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, blo, acc[g], 0, 0, 0);
+      if constexpr (sizeof(TIn) == 4)
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bhi, acc[g], 0, 0, 0);
+    }
+  }
+  // 16x16 output layout: lane l, register i -> row 4*(l/16) + i, column l % 16.
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[w][4 * (lane >> 4) + i][g * 16 + (lane & 15)] = acc[g][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 16 * R; idx += 256) {
+    const int rr = idx / R, cc = idx % R;
+    const float s = red[0][rr][cc] + red[1][rr][cc] + red[2][rr][cc] + red[3][rr][cc];
+    if (row0 + rr < rows) U[(row0 + rr) * R + cc] = s;
+  }
+}
+
+hipError_t launch_lowrank_down(const void* x, int x_bf16, int64_t rows, int d, int r,
+                               const uint16_t* l1_hi, const uint16_t* l1_lo, float* U,
+                               hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid{unsigned((rows + 15) / 16)}, block{256};
+#define HQ_LR_CASE(RR)                                                                          \
+  case RR:                                                                                      \
+    if (x_bf16)                                                                                 \
+      hipLaunchKernelGGL((lowrank_down_kernel<uint16_t, RR>), grid, block, 0, s,                 \
+                         static_cast<const uint16_t*>(x), rows, d, l1_hi, l1_lo, U);            \
+    else                                                                                        \
+      hipLaunchKernelGGL((lowrank_down_kernel<float, RR>), grid, block, 0, s,                    \
+                         static_cast<const float*>(x), rows, d, l1_hi, l1_lo, U);               \
+    break;
+  switch (r) {
+    HQ_LR_CASE(16) HQ_LR_CASE(32) HQ_LR_CASE(48) HQ_LR_CASE(64)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef HQ_LR_CASE
+  return hipGetLastError();
+}
+
+}  // namespace hq

@@ -1,0 +1,88 @@
+// Internal launcher interface between the C ABI (hq_abi.cpp) and the kernels.
+// Launchers enqueue on `stream` and return the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hq {
+
+// GEMM macro tile sizes; d_out is padded to a multiple of GEMM_BN in the
+// prepared blob and T to a multiple of GEMM_BM in the workspace.
+constexpr int GEMM_BM = 256;
+constexpr int GEMM_BN = 256;
+
+// Row-transform geometry: G lanes per row, C chunks of 8*G channels per lane.
+struct RowGeom {
+  int G, C;
+};
+bool row_geometry(int d_in, RowGeom* g);
+
+enum RowMode { ROW_ACT = 0, ROW_WEIGHT = 1, ROW_EXPORT = 2 };
+
+struct RowArgs {
+  const void* in;         // [rows, d] f32 or bf16
+  int in_bf16;
+  int64_t rows;
+  int d;
+  const float* scale;     // per-channel multiplier (1/sigma or sigma); NULL = ones
+  int log2b;
+  int center;
+  float qmax;
+  int8_t* codes;          // [rows, d]             (ACT, WEIGHT)
+  float* out_s;           // [rows] dequant scale  (ACT, WEIGHT)
+  float* out_aux;         // [rows] mu (ACT, EXPORT) or c (WEIGHT)
+  float* out_xt;          // [rows, d] f32         (EXPORT)
+  int mode;
+};
+hipError_t launch_row_transform(const RowArgs& a, hipStream_t s);
+
+// absmax[i] = max over rows of |in[r, i]| ; absmax zeroed by the launcher.
+hipError_t launch_col_absmax(const void* in, int in_bf16, int64_t rows, int d, float* absmax,
+                             hipStream_t s);
+// sigma[i] = max(ax_i, eps)^alpha / max(sigma[i], eps)^(1 - alpha) in place.
+hipError_t launch_sigma_finish(const float* ax, float alpha, float eps, int d, float* sigma,
+                               hipStream_t s);
+
+// Fill n floats / bytes.
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
+hipError_t launch_fill_u8(uint8_t* p, uint8_t v, size_t n, hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s);
+hipError_t launch_reciprocal(const float* src, float* dst, int n, hipStream_t s);
+// Write a small POD header (<= 256 bytes) to device memory.
+hipError_t launch_write_header(const void* host_hdr, size_t bytes, void* dst, hipStream_t s);
+
+// Low-rank factors: l1 [d, r] -> (l1 / sigma)^T split into bf16 hi/lo [r, d];
+// l2 [r, n] -> l2^T split into bf16 hi/lo [n_pad, r] (rows >= n zero).
+hipError_t launch_prep_l1(const void* l1, int bf16, const float* sigma_inv, int d, int r,
+                          uint16_t* hi, uint16_t* lo, hipStream_t s);
+hipError_t launch_prep_l2(const void* l2, int bf16, int r, int n, int n_pad, uint16_t* hi,
+                          uint16_t* lo, hipStream_t s);
+
+// U [rows, r] = x [rows, d] . (l1_hi + l1_lo)^T  (bf16 MFMA, fp32 accumulate).
+hipError_t launch_lowrank_down(const void* x, int x_bf16, int64_t rows, int d, int r,
+                               const uint16_t* l1_hi, const uint16_t* l1_lo, float* U,
+                               hipStream_t s);
+
+struct GemmEpi {
+  const float* s_x;       // [M]
+  const float* mu;        // [M]
+  const float* s_w;       // [N]
+  const float* c;         // [N]
+  const float* bias;      // [N]
+  const float* U;         // [M, rank] or NULL
+  const uint16_t* l2_hi;  // [N, rank]
+  const uint16_t* l2_lo;
+  int rank;
+  void* Y;                // [M, ldy]
+  int y_bf16;
+  int64_t ldy;
+};
+// acc = A [M, K] . B [N, K]^T ; epilogue: int32 store to acc_out (ld = ldc) when
+// epi == NULL, else the dequant epilogue. B must have >= roundup(N, GEMM_BN)
+// readable rows unless clamp_b is set.
+hipError_t launch_gemm(const int8_t* A, int64_t M, const int8_t* B, int64_t N, int K,
+                       int32_t* acc_out, int64_t ldc, const GemmEpi* epi, hipStream_t s);
+
+}  // namespace hq

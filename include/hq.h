@@ -1,0 +1,186 @@
+/*
+ * hq.h -- C ABI of libhq: the rotated-and-centred low-bit linear layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (HadaNorm, "What carries the argument", Eq. (1)):
+ *
+ *     Y = X W + b  =  X~ W~ + b~,   X~ = X diag(1/sigma) H - mu,
+ *                                   W~ = H^T diag(sigma) W,  b~ = b + mu W~
+ *
+ * X is [T, d_in] (one token per row), W = weight^T with ``weight`` passed as
+ * [d_out, d_in] row-major (the nn.Linear layout), H the normalised Sylvester
+ * Hadamard matrix applied per contiguous block of ``block`` channels
+ * (HaTQ supplement Sec. VII-A Eq. (34); data-free int4 blog, step 7), mu the
+ * per-token mean of X diag(1/sigma) H. X~ is quantised per token and W~ per
+ * output channel with the symmetric quantiser of HaTQ Sec. III-A Eq. (3)
+ * (codes in [-(2^(b-1)-1), 2^(b-1)-1], int4 codes carried in int8 lanes),
+ * multiplied in an int8 MFMA GEMM with int32 accumulation (HaTQ Eq. (4)),
+ * and dequantised with the accumulator scale s_x s_w (HaTQ Eq. (18)) plus
+ * the bias correction:
+ *
+ *     Y_tj = s_x,t s_w,j acc_tj + b_j + mu_t c_j [+ (x'_t L1) L2_:j],
+ *     c = 1^T W~,  x' = x / sigma.
+ *
+ * The optional rank-r branch (blog steps 3-4) is kept in 16-bit and sees the
+ * smoothed, un-rotated input x'.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless the comment says (host).
+ *  - ``stream`` is a hipStream_t (NULL = the default stream). All GPU work is
+ *    enqueued asynchronously on it; no entry point synchronises the host
+ *    except where stated.
+ *  - The caller allocates and owns every buffer. The library allocates no
+ *    device memory and keeps no state besides a thread-local error string.
+ *  - All arguments are validated on the host before anything is enqueued; on
+ *    error nothing is launched, outputs are untouched, a negative hq_status
+ *    is returned and hq_last_error() describes the problem. No C++
+ *    exception crosses this interface.
+ *  - Unsupported combinations are rejected, never coerced.
+ */
+#ifndef HQ_H_
+#define HQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HQ_ABI_VERSION 1
+
+typedef enum {
+  HQ_OK = 0,
+  HQ_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad enum      */
+  HQ_ERR_UNSUPPORTED = -2,   /* valid but unsupported shape/option          */
+  HQ_ERR_WORKSPACE = -3,     /* workspace smaller than hq_workspace_bytes   */
+  HQ_ERR_BAD_PREPARED = -4,  /* prepared blob header does not match desc    */
+  HQ_ERR_HIP = -5            /* a HIP runtime call or launch failed         */
+} hq_status;
+
+typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
+
+/* Layer descriptor (plain data, passed by host pointer).
+ *  d_in    input channels: a multiple of 128 up to 2048, of 256 up to 4096,
+ *          or of 512 up to 8192.
+ *  d_out   output channels; multiple of 8, >= 8.
+ *  block   Hadamard block size: a power of two dividing d_in (1 = no rotation).
+ *  a_bits  activation code width: 4 or 8.
+ *  w_bits  weight code width: 4 or 8.
+ *  center  1: subtract the per-token mean mu (HadaNorm centring); 0: mu = 0.
+ *  smooth  1: channel smoothing with the sigma given to hq_prepare_weights;
+ *          0: sigma == 1 (no scaling pass over X).
+ *  rank    low-rank branch rank: 0 (off) or a multiple of 16 up to 64.
+ *  x_dtype dtype of X (hq_dtype).
+ *  w_dtype dtype of weight, L1 and L2 (hq_dtype).
+ *  y_dtype dtype of Y (hq_dtype).
+ * Bias, sigma and every scale are float32. */
+typedef struct {
+  int32_t d_in, d_out, block, a_bits, w_bits, center, smooth, rank;
+  int32_t x_dtype, w_dtype, y_dtype;
+} hq_desc;
+
+/* Byte offsets of the arrays inside a prepared blob (all 256-byte aligned). */
+typedef struct {
+  size_t total;        /* hq_prepared_bytes                                  */
+  size_t w_codes;      /* int8  [d_out_pad, d_in]  codes of W~^T, row j = out j */
+  size_t w_scale;      /* f32   [d_out_pad]        s_w (0 for padding rows)     */
+  size_t c;            /* f32   [d_out_pad]        c = 1^T W~                   */
+  size_t bias;         /* f32   [d_out_pad]        b (0 if none)                */
+  size_t sigma_inv;    /* f32   [d_in]             1 / sigma                    */
+  size_t l1_hi;        /* bf16  [rank, d_in]       hi part of (diag(1/sigma) L1)^T */
+  size_t l1_lo;        /* bf16  [rank, d_in]       lo part (residual)           */
+  size_t l2_hi;        /* bf16  [d_out_pad, rank]  hi part of L2^T              */
+  size_t l2_lo;        /* bf16  [d_out_pad, rank]  lo part                      */
+  int64_t d_out_pad;   /* d_out rounded up to the GEMM column tile              */
+} hq_prepared_layout;
+
+/* Library ABI version (HQ_ABI_VERSION of the build). */
+int hq_abi_version(void);
+
+/* Text of the last error on the calling thread ("" if none). Never NULL. */
+const char* hq_last_error(void);
+
+/* Static name of a status code. */
+const char* hq_status_str(int status);
+
+/* Host-only check of a descriptor (host pointer). Returns HQ_OK or the error. */
+int hq_validate(const hq_desc* desc);
+
+/* Host-only: size in bytes of the prepared-weight blob for ``desc``;
+ * 0 if the descriptor is invalid (see hq_last_error). */
+size_t hq_prepared_bytes(const hq_desc* desc);
+
+/* Host-only: layout of the prepared blob (host pointers). */
+int hq_prepared_layout_of(const hq_desc* desc, hq_prepared_layout* out);
+
+/* Host-only: workspace bytes hq_quant_linear needs for T tokens; 0 if invalid. */
+size_t hq_workspace_bytes(const hq_desc* desc, int64_t T);
+
+/* Calibration statistic for the smoothing scale (HadaNorm Eq. (3)):
+ * absmax[i] = max_t |X[t, i]| over the T rows of X [T, d_in] (x_dtype).
+ * absmax: f32 [d_in], overwritten. T = 0 writes zeros. */
+int hq_channel_absmax(const hq_desc* desc, const void* X, int64_t T, float* absmax,
+                      void* stream);
+
+/* Smoothing scales, HadaNorm Eq. (3):
+ *   sigma_i = max(act_absmax_i, 1e-5)^alpha / max(max_j |weight_ji|, 1e-5)^(1-alpha)
+ * act_absmax: f32 [d_in] (from hq_channel_absmax over calibration tokens),
+ * weight: [d_out, d_in] (w_dtype), alpha in [0, 1]. sigma: f32 [d_in]. */
+int hq_sigma(const hq_desc* desc, const float* act_absmax, const void* weight, float alpha,
+             float* sigma, void* stream);
+
+/* Offline weight transform (HadaNorm Eq. (1); HaTQ Sec. IV-D: weight-side
+ * transforms are precomputed): for each output row j,
+ *   w~_j = (weight_j * sigma) H,  c_j = sum_i w~_ji,
+ *   s_w,j = max_i |w~_ji| / qmax,  codes = clamp(round(w~_j / s_w,j), +-qmax),
+ * plus 1/sigma, the bias, and for rank > 0 the split low-rank factors.
+ *  weight  [d_out, d_in] w_dtype;  bias f32 [d_out] or NULL (zeros);
+ *  sigma   f32 [d_in], required iff desc->smooth (sigma > 0);
+ *  L1      [d_in, rank] w_dtype, L2 [rank, d_out] w_dtype (both NULL iff rank 0).
+ *  prepared  device buffer of hq_prepared_bytes(desc) bytes, fully written.
+ * The blob is immutable afterwards and may be shared by concurrent calls. */
+int hq_prepare_weights(const hq_desc* desc, const void* weight, const float* bias,
+                       const float* sigma, const void* L1, const void* L2, void* prepared,
+                       void* stream);
+
+/* Host-synchronising check that ``prepared`` was written by
+ * hq_prepare_weights for this descriptor (reads its 256-byte header). */
+int hq_check_prepared(const hq_desc* desc, const void* prepared, void* stream);
+
+/* The hot path: Y = quantised layer(X) for T tokens.
+ *  X [T, d_in] x_dtype, row-major;  Y [T, d_out] y_dtype, row-major.
+ *  workspace: device buffer of at least hq_workspace_bytes(desc, T) bytes,
+ *  not shared with a concurrent call. T = 0 is a no-op. */
+int hq_quant_linear(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
+                    void* Y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Stage entry points (the same kernels, for testing and profiling) ---- */
+
+/* Activation stage alone: codes int8 [T, d_in] (natural channel order),
+ * s_x f32 [T] (dequant scale of the normalised X~ row), mu f32 [T],
+ * U f32 [T, rank] (x' L1; ignored/NULL when rank = 0). */
+int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
+                    int8_t* codes, float* s_x, float* mu, float* U, void* stream);
+
+/* Debug export of the float transform before quantisation:
+ * Xt f32 [T, d_in] = X~ (normalised H, centred if desc->center), mu f32 [T]. */
+int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
+                     float* Xt, float* mu, void* stream);
+
+/* Integer GEMM alone: acc int32 [T, N] = a_codes [T, d_in] . w_codes [N, d_in]^T,
+ * both int8 row-major; N a multiple of 8. */
+int hq_gemm_i32(const hq_desc* desc, const int8_t* a_codes, const int8_t* w_codes, int64_t T,
+                int64_t N, int32_t* acc, void* stream);
+
+/* GEMM + dequant epilogue alone, from activation-stage outputs (layouts as in
+ * hq_act_quantize; U NULL when rank = 0). Y [T, d_out] y_dtype. */
+int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const int8_t* codes,
+                    const float* s_x, const float* mu, const float* U, int64_t T, void* Y,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQ_H_ */

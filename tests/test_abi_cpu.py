@@ -1,0 +1,109 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before touching the GPU. No kernels run."""
+import ctypes
+
+import pytest
+
+from hadamard_rotated_bit_amd import _lib
+from hadamard_rotated_bit_amd import Desc, F32, BF16
+from hadamard_rotated_bit_amd import workloads as WL
+
+lib = _lib.load()
+
+
+def _d(**kw):
+    base = dict(d_in=1152, d_out=4608, block=128, a_bits=4, w_bits=4, center=True, smooth=True,
+                rank=0, x_dtype=BF16, w_dtype=BF16, y_dtype=BF16)
+    base.update(kw)
+    return Desc(**base).c()
+
+
+def test_exports_every_declared_function():
+    names = _lib.header_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert lib.hq_abi_version() == 1
+    assert lib.hq_status_str(0) == b"HQ_OK"
+    assert lib.hq_status_str(-3) == b"HQ_ERR_WORKSPACE"
+    assert lib.hq_status_str(99) == b"HQ_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("name", WL.ORDER)
+def test_workload_descriptors_valid(name):
+    w = WL.WORKLOADS[name]
+    dt = BF16 if w.dtype == "bf16" else F32
+    d = Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, bool(w.center), w.alpha is not None,
+             w.rank, dt, dt, dt).c()
+    assert lib.hq_validate(ctypes.byref(d)) == 0
+    L = _lib.HqLayout()
+    assert lib.hq_prepared_layout_of(ctypes.byref(d), ctypes.byref(L)) == 0
+    assert L.d_out_pad % 256 == 0 and L.d_out_pad >= w.d_out
+    offs = [L.w_codes, L.w_scale, L.c, L.bias, L.sigma_inv, L.l1_hi, L.l1_lo, L.l2_hi, L.l2_lo]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    assert L.w_scale - L.w_codes >= L.d_out_pad * w.d_in
+    assert L.total == lib.hq_prepared_bytes(ctypes.byref(d))
+    ws = lib.hq_workspace_bytes(ctypes.byref(d), w.T)
+    assert ws >= w.T * w.d_in + 8 * w.T + 4 * w.T * w.rank
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_in=0), -1), (dict(d_out=-8), -1), (dict(x_dtype=3), -1), (dict(center=2), -1),
+    (dict(smooth=5), -1), (dict(a_bits=3), -2), (dict(w_bits=16), -2), (dict(d_in=1000), -2),
+    (dict(d_in=2176), -2), (dict(d_out=100), -2), (dict(block=96), -2), (dict(block=256, d_in=1152), -2),
+    (dict(rank=8), -2), (dict(rank=128), -2), (dict(d_in=16384), -2),
+])
+def test_validation_rejects(kw, status):
+    d = _d(**kw)
+    assert lib.hq_validate(ctypes.byref(d)) == status
+    assert len(lib.hq_last_error()) > 0
+    assert lib.hq_prepared_bytes(ctypes.byref(d)) == 0
+    assert lib.hq_workspace_bytes(ctypes.byref(d), 16) == 0
+
+
+@pytest.mark.parametrize("d_in", [128, 256, 384, 1152, 2048, 2560, 3072, 4096, 6144, 8192])
+def test_supported_widths(d_in):
+    assert lib.hq_validate(ctypes.byref(_d(d_in=d_in, block=128))) == 0
+
+
+def test_block_one_and_full():
+    assert lib.hq_validate(ctypes.byref(_d(block=1))) == 0
+    assert lib.hq_validate(ctypes.byref(_d(d_in=4096, block=4096))) == 0
+
+
+def test_null_desc():
+    assert lib.hq_validate(None) == -1
+    assert lib.hq_prepared_bytes(None) == 0
+
+
+def test_entry_points_reject_before_launch():
+    d = ctypes.byref(_d())
+    p = ctypes.c_void_p(0x1000)   # never dereferenced: every call fails validation first
+    assert lib.hq_quant_linear(d, None, p, 16, p, p, 1 << 30, None) == -1
+    assert lib.hq_quant_linear(d, p, p, -1, p, p, 1 << 30, None) == -1
+    assert lib.hq_quant_linear(d, p, p, 16, p, p, 10, None) == -3          # workspace too small
+    assert b"workspace" in lib.hq_last_error()
+    assert lib.hq_quant_linear(d, p, p, 0, None, None, 0, None) == 0     # T = 0 is a no-op
+    assert lib.hq_prepare_weights(d, p, None, None, None, None, p, None) == -1  # smooth needs sigma
+    d_ns = ctypes.byref(_d(smooth=False))
+    assert lib.hq_prepare_weights(d_ns, p, None, p, None, None, p, None) == -1  # sigma w/o smooth
+    d_r = ctypes.byref(_d(rank=32))
+    assert lib.hq_prepare_weights(d_r, p, None, p, None, None, p, None) == -1  # rank needs L1/L2
+    assert lib.hq_sigma(d, p, p, ctypes.c_float(1.5), p, None) == -1
+    assert lib.hq_gemm_i32(d, p, p, 16, 12, p, None) == -1                # N % 8
+    assert lib.hq_act_quantize(d_r, p, p, 4, p, p, p, None, None) == -1    # U missing
+    assert lib.hq_channel_absmax(d, None, 8, p, None) == -1
+
+
+def test_error_string_is_thread_local():
+    import threading
+    lib.hq_validate(ctypes.byref(_d(a_bits=3)))
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(lib.hq_last_error()))
+    t.start()
+    t.join()
+    assert seen == [b""]
+    assert b"a_bits" in lib.hq_last_error()
