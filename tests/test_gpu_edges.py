@@ -1,0 +1,154 @@
+"""GPU edge cases against the oracle: empty, single and ragged token counts,
+ragged output widths, degenerate rows, no / tiny / full rotation blocks, mixed
+dtypes and code widths, the low-rank branch in float32, heavy outliers, and
+determinism across launch configurations."""
+import numpy as np
+import pytest
+import torch
+
+import hadamard_rotated_bit_amd as hq
+from hadamard_rotated_bit_amd import workloads as WL
+from oracle import hq_oracle as O
+from parity import MAX_FLIP_FRAC, Y_TOL, check_codes, rel_fro, tdev, to_np
+
+pytestmark = pytest.mark.gpu
+DT = {"f32": hq.F32, "bf16": hq.BF16}
+
+
+def run_case(T, d_in, d_out, *, block, a_bits=4, w_bits=4, center=True, alpha=0.5, rank=0,
+             x_dtype="f32", w_dtype="f32", y_dtype="f32", key=100, x=None, n_outliers=4,
+             outlier=50.0):
+    print(f"\n[case] T={T} {d_in}->{d_out} block={block} A{a_bits}W{w_bits} center={center} "
+          f"alpha={alpha} rank={rank} {x_dtype}/{w_dtype}/{y_dtype}", flush=True)
+    w = WL.custom(key, T, d_in, d_out, dtype=x_dtype, block=block, alpha=alpha, center=int(center),
+                  a_bits=a_bits, w_bits=w_bits, rank=rank, n_outliers=n_outliers, outlier=outlier)
+    if x is None:
+        x = WL.gen_x(w) if T > 0 else np.zeros((0, d_in), dtype=np.float32)
+    wq = WL.Workload(**{**w.__dict__, "dtype": w_dtype})
+    weight, bias = WL.gen_weight(wq), WL.gen_bias(wq)
+    l1, l2 = WL.gen_lowrank(wq)
+    desc = hq.Desc(d_in, d_out, block, a_bits, w_bits, center, alpha is not None, rank,
+                   DT[x_dtype], DT[w_dtype], DT[y_dtype])
+    sig = None
+    if alpha is not None:
+        sig = O.smoothing_scales(x if T > 0 else np.ones((1, d_in)), weight, alpha)
+        sig = sig.astype(np.float32).astype(np.float64)
+    prep = hq.prepare(desc, tdev(weight, w_dtype), torch.from_numpy(bias).cuda(),
+                      None if sig is None else torch.from_numpy(sig.astype(np.float32)).cuda(),
+                      None if l1 is None else tdev(l1, w_dtype),
+                      None if l2 is None else tdev(l2, w_dtype))
+    X = tdev(x, x_dtype)
+    Y = hq.quant_linear(desc, prep, X)
+    codes, s_x, mu, U = hq.act_quantize(desc, prep, X)
+    ora = O.run(x, weight, bias, block=block, a_bits=a_bits, w_bits=w_bits, center=center,
+                sigma=sig, l1=l1, l2=l2, out_dtype=y_dtype)
+    return desc, prep, X, Y, codes, s_x, mu, U, ora
+
+
+def check_all(Y, codes, s_x, ora):
+    err = rel_fro(to_np(Y), ora["y_out"])
+    assert err <= Y_TOL, err
+    ratio = np.divide(ora["xt"], ora["s_x"][:, None], out=np.zeros_like(ora["xt"]),
+                      where=ora["s_x"][:, None] > 0)
+    check_codes(to_np(codes), ora["qa"], ratio, "activation codes")
+    np.testing.assert_allclose(to_np(s_x), ora["s_x"], rtol=1e-5, atol=1e-30)
+
+
+def test_empty_batch():
+    desc, prep, X, Y, codes, s_x, mu, U, ora = run_case(0, 128, 64, block=128)
+    assert Y.shape == (0, 64) and codes.shape == (0, 128)
+
+
+@pytest.mark.parametrize("T", [1, 3, 129, 257, 1000])
+def test_ragged_tokens(T):
+    r = run_case(T, 256, 264, block=64)
+    check_all(r[3], r[4], r[5], r[8])
+
+
+@pytest.mark.parametrize("T,d_out", [(600, 1032), (700, 1160), (2100, 1536)])
+def test_ragged_outputs_large_tiles(T, d_out):
+    # T > 512 and d_out > 512 take the 256x256 / 128x192 configurations
+    r = run_case(T, 512, d_out, block=512)
+    check_all(r[3], r[4], r[5], r[8])
+
+
+def test_zero_and_degenerate_rows():
+    d = 128
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, d)).astype(np.float32)
+    x[1] = 0.0                                   # all-zero row
+    x[3] = 0.0
+    x[3, 0] = 2.5                                # only channel 0: centred X~ is exactly 0
+    r = run_case(6, d, 64, block=d, alpha=None, x=x)
+    desc, prep, X, Y, codes, s_x, mu, U, ora = r
+    c = to_np(codes)
+    assert not c[1].any() and not c[3].any()
+    assert to_np(s_x)[1] == 0.0 and to_np(s_x)[3] == 0.0
+    check_all(Y, codes, s_x, ora)
+    # Y of the degenerate row is b + mu c (the whole output comes from the bias correction)
+    np.testing.assert_allclose(to_np(Y)[3], ora["y_full"][3], rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("block", [1, 2, 8, 32, 1024])
+def test_block_sizes(block):
+    r = run_case(200, 1024, 256, block=block)
+    check_all(r[3], r[4], r[5], r[8])
+
+
+@pytest.mark.parametrize("xd,wd,yd", [("f32", "bf16", "bf16"), ("bf16", "f32", "f32"),
+                                      ("bf16", "bf16", "f32")])
+def test_mixed_dtypes(xd, wd, yd):
+    r = run_case(300, 384, 512, block=128, x_dtype=xd, w_dtype=wd, y_dtype=yd)
+    check_all(r[3], r[4], r[5], r[8])
+
+
+@pytest.mark.parametrize("ab,wb", [(8, 4), (4, 8), (8, 8)])
+def test_code_widths(ab, wb):
+    r = run_case(300, 256, 256, block=256, a_bits=ab, w_bits=wb)
+    check_all(r[3], r[4], r[5], r[8])
+    assert np.abs(to_np(r[4])).max() <= 2 ** (ab - 1) - 1
+
+
+@pytest.mark.parametrize("rank,xd", [(16, "f32"), (48, "bf16"), (64, "f32")])
+def test_low_rank(rank, xd):
+    r = run_case(260, 512, 384, block=256, rank=rank, x_dtype=xd, w_dtype=xd, y_dtype=xd)
+    desc, prep, X, Y, codes, s_x, mu, U, ora = r
+    check_all(Y, codes, s_x, ora)
+    err = np.linalg.norm(to_np(U) - ora["u"], axis=1) / np.linalg.norm(ora["u"], axis=1)
+    assert err.max() <= 1e-4, err.max()
+
+
+def test_heavy_outliers_and_no_centring():
+    r = run_case(400, 2048, 512, block=2048, center=False, alpha=None, n_outliers=16,
+                 outlier=1000.0)
+    check_all(r[3], r[4], r[5], r[8])
+    assert not to_np(r[6]).any()        # mu is zero without centring
+
+
+def test_deterministic_across_launch_configs():
+    # the same 300 tokens inside a 2048-token batch (different GEMM tiling)
+    # give bit-identical accumulators and outputs
+    w = WL.custom(300, 2048, 1024, 768, dtype="bf16", block=256, alpha=None)
+    x = WL.gen_x(w)
+    desc = hq.Desc(1024, 768, 256, 4, 4, True, False, 0, hq.BF16, hq.BF16, hq.BF16)
+    prep = hq.prepare(desc, tdev(WL.gen_weight(w), "bf16"), torch.from_numpy(WL.gen_bias(w)).cuda())
+    Xb = tdev(x, "bf16")
+    Yb = hq.quant_linear(desc, prep, Xb)
+    Ys = hq.quant_linear(desc, prep, Xb[:300].contiguous())
+    assert torch.equal(Yb[:300], Ys)
+    assert torch.equal(Yb, hq.quant_linear(desc, prep, Xb))
+    v = hq.prepared_views(desc, prep)
+    codes = hq.act_quantize(desc, prep, Xb)[0]
+    a1 = hq.gemm_i32(desc, codes, v["w_codes"].contiguous())
+    a2 = hq.gemm_i32(desc, codes[:300].contiguous(), v["w_codes"].contiguous())
+    assert torch.equal(a1[:300], a2)
+
+
+def test_check_prepared_header():
+    w = WL.custom(301, 16, 256, 128, block=128)
+    desc = hq.Desc(256, 128, 128, 4, 4, True, False, 0)
+    prep = hq.prepare(desc, tdev(WL.gen_weight(w), "f32"))
+    hq.check_prepared(desc, prep)
+    other = hq.Desc(256, 128, 64, 4, 4, True, False, 0)
+    with pytest.raises(hq.HqError):
+        hq.check_prepared(other, prep)
