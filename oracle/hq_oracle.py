@@ -39,10 +39,12 @@ Readings taken where the pages leave a step open:
   contiguous block of ``block`` channels.
 * Activations get one scale per token, weights one scale per output
   channel; codes are symmetric in [-qmax, qmax], qmax = 2^(bits-1) - 1.
-* The rounding decision round(v / s) is taken in float32 as
-  rint_half_even(f32(v) * f32(qmax / f32(max|v|))): the same real number as
-  v / s, evaluated in the precision the GPU kernel uses, so both sides decide
-  each code in the same arithmetic. Scales, means and outputs stay float64.
+* The rounding decision round(v / s) is taken on float32 operands as
+  rint_half_even(f32(v) * f32(qmax / f32(max|v|))), the product formed
+  exactly and rounded once to the integer grid: the same real number as
+  v / s, rounded a single time as "round" reads, in the precision the GPU
+  kernel uses, so both sides decide each code in the same arithmetic.
+  Scales, means and outputs stay float64.
 * A row whose maximum is 0 gets scale 0 and all-zero codes.
 * The bias correction uses c = 1^T W~ from the unquantised W~.
 * The low-rank branch sees x' = x / sigma (smoothed, not rotated, not
@@ -150,8 +152,8 @@ def quantize_rows(v: np.ndarray, bits: int):
 
     s = ||v||_inf / qmax with qmax = 2^(bits-1) - 1, and
     q = clamp(round(v / s), -qmax, qmax). The division v / s is formed as
-    v * (qmax / ||v||_inf) in float32 and rounded half-to-even (see the module
-    header). Returns (codes int16 [rows, n], s float64 [rows]).
+    v * (qmax / ||v||_inf) on float32 operands and rounded once, half-to-even
+    (see the module header). Returns (codes int16 [rows, n], s float64 [rows]).
     """
     qmax = 2 ** (bits - 1) - 1
     v = np.asarray(v, dtype=np.float64)
@@ -161,8 +163,9 @@ def quantize_rows(v: np.ndarray, bits: int):
     nz = a32 > 0
     r32 = np.zeros_like(a32)
     r32[nz] = np.float32(qmax) / a32[nz]
-    t32 = v.astype(np.float32) * r32[:, None]
-    q = np.clip(np.rint(t32), -qmax, qmax).astype(np.int16)
+    # exact product of two float32 values (48 significant bits fit a float64)
+    t = v.astype(np.float32).astype(np.float64) * r32.astype(np.float64)[:, None]
+    q = np.clip(np.rint(t), -qmax, qmax).astype(np.int16)
     return q, s
 
 
