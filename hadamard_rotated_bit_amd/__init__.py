@@ -42,10 +42,15 @@ class Desc:
     w_dtype: int = F32
     y_dtype: int = F32
 
+    def __post_init__(self):
+        raw = HqDesc(self.d_in, self.d_out, self.block, self.a_bits, self.w_bits,
+                     int(self.center), int(self.smooth), self.rank, self.x_dtype,
+                     self.w_dtype, self.y_dtype)
+        object.__setattr__(self, "_raw", raw)
+        object.__setattr__(self, "_ref", ctypes.byref(raw))
+
     def c(self) -> HqDesc:
-        return HqDesc(self.d_in, self.d_out, self.block, self.a_bits, self.w_bits,
-                      int(self.center), int(self.smooth), self.rank, self.x_dtype,
-                      self.w_dtype, self.y_dtype)
+        return self._raw
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -144,11 +149,13 @@ def quant_linear(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
     _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
     if out is None:
         out = torch.empty(T, desc.d_out, dtype=_TORCH[desc.y_dtype], device=X.device)
-    _need(out, "out", _TORCH[desc.y_dtype], (T, desc.d_out))
-    need = workspace_bytes(desc, T)
+    else:
+        _need(out, "out", _TORCH[desc.y_dtype], (T, desc.d_out))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
-    check(load().hq_quant_linear(ctypes.byref(desc.c()), _ptr(prepared), _ptr(X), T, _ptr(out),
+        workspace = torch.empty(max(workspace_bytes(desc, T), 1), dtype=torch.uint8,
+                                device=X.device)
+    # the library checks the workspace size itself
+    check(load().hq_quant_linear(desc._ref, _ptr(prepared), _ptr(X), T, _ptr(out),
                                  _ptr(workspace), workspace.numel(), _stream()))
     return out
 

@@ -18,19 +18,21 @@ namespace hq {
 // split into j (3 bits, in registers), t (log2 G bits, across lanes) and c
 // (in registers), so a butterfly stage of the Walsh-Hadamard transform on
 // bit b is either an in-register add/sub pair or one cross-lane exchange.
-// The smallest G that keeps C <= 16 is chosen, which minimises cross-lane
-// stages.
+// The smallest G that keeps C <= 8 (else C <= 16) is chosen: few cross-lane
+// stages without giving up occupancy.
 // ---------------------------------------------------------------------------
 bool row_geometry(int d, RowGeom* g) {
   const int cands[3] = {16, 32, 64};
-  for (int i = 0; i < 3; ++i) {
-    const int G = cands[i];
-    if (d % (8 * G)) continue;
-    const int C = d / (8 * G);
-    if (C >= 1 && C <= 16) {
-      g->G = G;
-      g->C = C;
-      return true;
+  for (int cap : {8, 16}) {          // prefer <= 64 values per lane (occupancy)
+    for (int i = 0; i < 3; ++i) {
+      const int G = cands[i];
+      if (d % (8 * G)) continue;
+      const int C = d / (8 * G);
+      if (C >= 1 && C <= cap) {
+        g->G = G;
+        g->C = C;
+        return true;
+      }
     }
   }
   return false;
@@ -43,8 +45,9 @@ bool row_geometry(int d, RowGeom* g) {
 //   y' = H~ x' per block                (unnormalised Sylvester butterflies;
 //                                        1/sqrt(B) is folded into the scales)
 //   mu' = sum(y') / d                   (if centring)
-//   amax' = max |y' - mu'|              (= max(max y' - mu', mu' - min y'))
-//   q = rint((y' - mu') * qmax / amax') (ties to even, fp32)
+//   amax' = max |y' - mu'|
+//   q = rint((y' - mu') * (qmax / amax'))  (fp32 operands, the exact product
+//                                           rounded once, ties to even)
 //   s = amax' / (sqrt(B) qmax),  mu = mu' / sqrt(B),  c = sum(y') / sqrt(B)
 template <typename TIn, int G, int C>
 __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv_sqrt_b) {
@@ -62,43 +65,46 @@ __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv
   float v[E];
 #pragma unroll
   for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
-  if (a.scale) {
+
+  // Chunk by chunk (so work on chunk c can start as soon as its load lands):
+  // channel scaling, then the butterflies on channel bits 0..2 (in
+  // registers) and 3 .. 3+log2G-1 (across lanes, on the VALU; the lower
+  // partner keeps x+y, the upper x-y).
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
+  for (int c = 0; c < C; ++c) {
+    float* vc = &v[c * 8];
+    if (a.scale) {
       float s[8];
       load8(a.scale + c * 8 * G + t * 8, s);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[c * 8 + j] *= s[j];
+      for (int j = 0; j < 8; ++j) vc[j] *= s[j];
     }
-  }
-
-  // Butterflies on channel bits 0..2 (in registers).
 #pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    if (b < a.log2b) {
-      const int h = 1 << b;
+    for (int b = 0; b < 3; ++b) {
+      if (b < a.log2b) {
+        const int h = 1 << b;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (!(e & h)) {
-          const float x = v[e], y = v[e + h];
-          v[e] = x + y;
-          v[e + h] = x - y;
+        for (int e = 0; e < 8; ++e) {
+          if (!(e & h)) {
+            const float x = vc[e], y = vc[e + h];
+            vc[e] = x + y;
+            vc[e + h] = x - y;
+          }
         }
       }
     }
-  }
-  // Bits 3 .. 3+log2G-1 (across lanes): lower partner keeps x+y, upper x-y.
-#pragma unroll
-  for (int b = 0; b < LOG2G; ++b) {
-    if (b + 3 < a.log2b) {
-      const int m = 1 << b;
-      const float sg = (t & m) ? -1.0f : 1.0f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float p = xor_shfl(v[e], m);
-        v[e] = fmaf(sg, v[e], p);
-      }
+#define HQ_XSTAGE(BIT, M)                                                          \
+    if (BIT < LOG2G && BIT + 3 < a.log2b) {                                        \
+      const float sg = (t & M) ? -1.0f : 1.0f;                                     \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) vc[e] = butterfly<M>(vc[e], sg); \
     }
+    HQ_XSTAGE(0, 1)
+    HQ_XSTAGE(1, 2)
+    HQ_XSTAGE(2, 4)
+    HQ_XSTAGE(3, 8)
+    if constexpr (G >= 32) { HQ_XSTAGE(4, 16) }
+    if constexpr (G >= 64) { HQ_XSTAGE(5, 32) }
+#undef HQ_XSTAGE
   }
   // Remaining bits index chunks (in registers).
 #pragma unroll
@@ -119,40 +125,26 @@ __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv
     }
   }
 
-  // Row reductions: sum, max, min (bit-identical on every lane of the row).
-  float sum = 0.0f, mx = -INFINITY, mn = INFINITY;
+  // Row sum (bit-identical on every lane of the row).
+  float sum = 0.0f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    sum += v[e];
-    mx = fmaxf(mx, v[e]);
-    mn = fminf(mn, v[e]);
-  }
-#pragma unroll
-  for (int m = 1; m < G; m <<= 1) {
-    sum += xor_shfl(sum, m);
-    mx = fmaxf(mx, xor_shfl(mx, m));
-    mn = fminf(mn, xor_shfl(mn, m));
-  }
+  for (int e = 0; e < E; ++e) sum += v[e];
+  sum = group_sum<G>(sum);
 
   const int64_t base = row * d + t * 8;
   if (a.mode == ROW_WEIGHT) {
-    const float amax = fmaxf(mx, -mn);
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    amax = group_max<G>(amax);
     const float rcp = amax > 0.0f ? a.qmax / amax : 0.0f;
     if (valid) {
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        uint32_t w[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint32_t p = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float q = fminf(fmaxf(v[c * 8 + h * 4 + j] * rcp, -a.qmax), a.qmax);
-            p |= rne_byte(q) << (8 * j);
-          }
-          w[h] = p;
-        }
-        *reinterpret_cast<uint2*>(a.codes + base + c * 8 * G) = make_uint2(w[0], w[1]);
+        const float* vc = &v[c * 8];
+        *reinterpret_cast<uint2*>(a.codes + base + c * 8 * G) =
+            make_uint2(pack_codes4(vc[0], vc[1], vc[2], vc[3], rcp),
+                       pack_codes4(vc[4], vc[5], vc[6], vc[7], rcp));
       }
       if (t == 0) {
         a.out_s[row] = amax * inv_sqrt_b / a.qmax;
@@ -162,41 +154,40 @@ __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv
     return;
   }
 
+  // Centre in place; the absmax of the centred row follows.
   const float mu = a.center ? sum / float(d) : 0.0f;
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    v[e] -= mu;
+    amax = fmaxf(amax, fabsf(v[e]));
+  }
   if (a.mode == ROW_EXPORT) {
     if (valid) {
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         float* o = a.out_xt + base + c * 8 * G;
         reinterpret_cast<float4*>(o)[0] =
-            make_float4((v[c * 8 + 0] - mu) * inv_sqrt_b, (v[c * 8 + 1] - mu) * inv_sqrt_b,
-                        (v[c * 8 + 2] - mu) * inv_sqrt_b, (v[c * 8 + 3] - mu) * inv_sqrt_b);
+            make_float4(v[c * 8 + 0] * inv_sqrt_b, v[c * 8 + 1] * inv_sqrt_b,
+                        v[c * 8 + 2] * inv_sqrt_b, v[c * 8 + 3] * inv_sqrt_b);
         reinterpret_cast<float4*>(o)[1] =
-            make_float4((v[c * 8 + 4] - mu) * inv_sqrt_b, (v[c * 8 + 5] - mu) * inv_sqrt_b,
-                        (v[c * 8 + 6] - mu) * inv_sqrt_b, (v[c * 8 + 7] - mu) * inv_sqrt_b);
+            make_float4(v[c * 8 + 4] * inv_sqrt_b, v[c * 8 + 5] * inv_sqrt_b,
+                        v[c * 8 + 6] * inv_sqrt_b, v[c * 8 + 7] * inv_sqrt_b);
       }
       if (t == 0) a.out_aux[row] = mu * inv_sqrt_b;
     }
     return;
   }
 
-  const float amax = fmaxf(mx - mu, mu - mn);
+  amax = group_max<G>(amax);
   const float rcp = amax > 0.0f ? a.qmax / amax : 0.0f;
   if (valid) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      uint32_t w[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t p = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float q = fminf(fmaxf((v[c * 8 + h * 4 + j] - mu) * rcp, -a.qmax), a.qmax);
-          p |= rne_byte(q) << (8 * j);
-        }
-        w[h] = p;
-      }
-      *reinterpret_cast<uint2*>(a.codes + base + c * 8 * G) = make_uint2(w[0], w[1]);
+      const float* vc = &v[c * 8];
+      *reinterpret_cast<uint2*>(a.codes + base + c * 8 * G) =
+          make_uint2(pack_codes4(vc[0], vc[1], vc[2], vc[3], rcp),
+                     pack_codes4(vc[4], vc[5], vc[6], vc[7], rcp));
     }
     if (t == 0) {
       a.out_s[row] = amax * inv_sqrt_b / a.qmax;

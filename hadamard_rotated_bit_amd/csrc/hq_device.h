@@ -37,10 +37,18 @@ __device__ __forceinline__ void load8(const uint16_t* __restrict__ p, float v[8]
   v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xFFFF0000u);
 }
 
-// Round-half-even to an integer held in the low byte: adding 1.5 * 2^23 puts
-// rint(v) (|v| < 2^22) in the low mantissa bits, two's complement mod 2^8.
-__device__ __forceinline__ uint32_t rne_byte(float v) {
-  return __float_as_uint(v + 12582912.0f) & 0xFFu;
+// Symmetric code of v with reciprocal scale rcp = qmax / max|v|, in the low
+// byte: fma(v, rcp, 1.5 * 2^23) rounds the exact product v * rcp once, ties
+// to even, onto the integer grid of [2^23, 2^24) (|v * rcp| <= qmax (1 + 2^-24),
+// so no clamp is needed); the low byte is the code in two's complement.
+__device__ __forceinline__ uint32_t code_bits(float v, float rcp) {
+  return __float_as_uint(fmaf(v, rcp, 12582912.0f));
+}
+// Four codes -> one dword (byte k = code k).
+__device__ __forceinline__ uint32_t pack_codes4(float a, float b, float c, float d, float rcp) {
+  const uint32_t ab = __builtin_amdgcn_perm(code_bits(b, rcp), code_bits(a, rcp), 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(code_bits(d, rcp), code_bits(c, rcp), 0x0c0c0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
 // Direct global -> LDS copy of 16 bytes per lane (gfx950
@@ -54,7 +62,78 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, void* lds) {
 #endif
 }
 
-// Butterfly partner across lanes: value of lane (lane ^ mask).
-__device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
+// Cross-lane exchange on the VALU (no LDS traffic). lane_xor<M>(v) returns v
+// of lane (lane ^ M) for M in {1, 2, 4, 8} through DPP: quad_perm for 1 and
+// 2, row_ror:8 for 8, and row_half_mirror (i ^ 7) followed by
+// quad_perm[3,2,1,0] (i ^ 3) for 4.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));
+  if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));
+  if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));
+  if constexpr (M == 4) {
+    const int h = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
+    return __int_as_float(__builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, false));
+  }
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "lane_xor distance");
+  return v;
+}
+
+// (value of the lower lane, value of the upper lane) of the pair
+// {lane, lane ^ M} for M in {16, 32}: gfx950 v_permlane16/32_swap with both
+// operands equal to v leaves the lower-half value in [0] and the upper-half
+// value in [1], in both lanes of the pair.
+template <int M>
+__device__ __forceinline__ void lane_pair(float v, float* lo, float* hi) {
+  const unsigned x = __float_as_uint(v);
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    *lo = __uint_as_float(r[0]);
+    *hi = __uint_as_float(r[1]);
+  } else {
+    static_assert(M == 32, "lane_pair distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    *lo = __uint_as_float(r[0]);
+    *hi = __uint_as_float(r[1]);
+  }
+}
+
+// One Walsh-Hadamard butterfly across lanes at distance M: the lower lane of
+// each pair keeps a_lo + a_hi, the upper lane a_lo - a_hi. `sg` is +1 on
+// lower lanes and -1 on upper lanes.
+template <int M>
+__device__ __forceinline__ float butterfly(float v, float sg) {
+  if constexpr (M <= 8) {
+    return fmaf(sg, v, lane_xor<M>(v));
+  } else {
+    float lo, hi;
+    lane_pair<M>(v, &lo, &hi);
+    return fmaf(sg, hi, lo);
+  }
+}
+
+// All-reduce over aligned groups of G lanes; every lane of a group ends with
+// the bit-identical result (each pairwise step adds the same two operands).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += lane_xor<1>(v);
+  if constexpr (G >= 4) v += lane_xor<2>(v);
+  if constexpr (G >= 8) v += lane_xor<4>(v);
+  if constexpr (G >= 16) v += lane_xor<8>(v);
+  if constexpr (G >= 32) { float lo, hi; lane_pair<16>(v, &lo, &hi); v = lo + hi; }
+  if constexpr (G >= 64) { float lo, hi; lane_pair<32>(v, &lo, &hi); v = lo + hi; }
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (G >= 2) v = fmaxf(v, lane_xor<1>(v));
+  if constexpr (G >= 4) v = fmaxf(v, lane_xor<2>(v));
+  if constexpr (G >= 8) v = fmaxf(v, lane_xor<4>(v));
+  if constexpr (G >= 16) v = fmaxf(v, lane_xor<8>(v));
+  if constexpr (G >= 32) { float lo, hi; lane_pair<16>(v, &lo, &hi); v = fmaxf(lo, hi); }
+  if constexpr (G >= 64) { float lo, hi; lane_pair<32>(v, &lo, &hi); v = fmaxf(lo, hi); }
+  return v;
+}
 
 }  // namespace hq

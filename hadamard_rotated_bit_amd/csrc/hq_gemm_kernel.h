@@ -45,6 +45,108 @@ __device__ __forceinline__ v8bf pack_bf16x8(const float f[8], bool residual) {
   return __builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
+// Epilogue shared by the GEMM kernels: lane owns token
+// m = m0 + wm0 + 32 i + l % 32 and, per 32-column strip j, channels
+// n = n0 + wn0 + 32 j + 8 g + 4 (l / 32) + {0..3}, g = 0..3. `smem` must be
+// idle (no LDS reads or DMA of the main loop in flight in any wave) once
+// every wave of the block has arrived; its first 4 (3 BN + 2 BM) bytes are
+// reused for the block's per-channel and per-token vectors.
+template <int BM, int BN, int TM, int TN, int NW, bool DEQ>
+__device__ __forceinline__ void gemm_epilogue(v16i (&acc)[TM][TN], uint8_t* smem, int tid, int lane,
+                                              int64_t m0, int64_t n0, int wm0, int wn0, int64_t M,
+                                              int64_t N, int32_t* __restrict__ Cout, int64_t ldc,
+                                              const GemmEpi& ep) {
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  if constexpr (!DEQ) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + wm0 + i * 32 + lrow;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = n0 + wn0 + j * 32 + 8 * g + 4 * lhalf;
+          if (m < M && n < N) {
+            const v16i& a = acc[i][j];
+            *reinterpret_cast<int4*>(Cout + m * ldc + n) =
+                make_int4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+          }
+        }
+    }
+  } else {
+    // The block's per-channel vectors (s_w, c, b for BN channels) and
+    // per-token vectors (s_x, mu for BM tokens) are staged once in the now
+    // idle LDS; lanes then read them as broadcast LDS loads (32 lanes share
+    // each channel quadruple) instead of re-fetching them from memory.
+    float* P = reinterpret_cast<float*>(smem);
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    for (int idx = tid; idx < BN; idx += NW * 64) {
+      const int64_t nc = n0 + idx < N ? n0 + idx : N - 1;
+      P[idx] = ep.s_w[nc];
+      P[BN + idx] = ep.c[nc];
+      P[2 * BN + idx] = ep.bias[nc];
+    }
+    for (int idx = tid; idx < BM; idx += NW * 64) {
+      const int64_t mc = m0 + idx < M ? m0 + idx : M - 1;
+      P[3 * BN + idx] = ep.s_x[mc];
+      P[3 * BN + BM + idx] = ep.mu[mc];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int ml = wm0 + i * 32 + lrow;
+      const int64_t m = m0 + ml;
+      const int64_t mc = m < M ? m : M - 1;
+      const float sx = P[3 * BN + ml], mu = P[3 * BN + BM + ml];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t nb = n0 + wn0 + j * 32;
+        // Low-rank term U[m, :] . L2[:, n] on bf16 MFMA with split operands:
+        // first operand L2^T (rows = channels), second U (columns = tokens),
+        // so the fp32 result has the accumulator's layout.
+        v16f lr = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        for (int k0 = 0; k0 < ep.rank; k0 += 16) {
+          float f[8];
+          load8(ep.U + mc * ep.rank + k0 + 8 * lhalf, f);
+          const v8bf uh = pack_bf16x8(f, false), ul = pack_bf16x8(f, true);
+          const int64_t nr = nb + lrow < N ? nb + lrow : N - 1;
+          const int64_t off = nr * ep.rank + k0 + 8 * lhalf;
+          const v8bf wh = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
+          const v8bf wl = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
+          lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, uh, lr, 0, 0, 0);
+          lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, uh, lr, 0, 0, 0);
+          lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, ul, lr, 0, 0, 0);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nl = wn0 + j * 32 + 8 * g + 4 * lhalf;
+          const int64_t n = n0 + nl;
+          const float4 sw = *reinterpret_cast<const float4*>(P + nl);
+          const float4 cb = *reinterpret_cast<const float4*>(P + BN + nl);
+          const float4 bb = *reinterpret_cast<const float4*>(P + 2 * BN + nl);
+          const v16i& a = acc[i][j];
+          const float y0 = fmaf(float(a[4 * g + 0]), sx * sw.x, fmaf(mu, cb.x, bb.x)) + lr[4 * g + 0];
+          const float y1 = fmaf(float(a[4 * g + 1]), sx * sw.y, fmaf(mu, cb.y, bb.y)) + lr[4 * g + 1];
+          const float y2 = fmaf(float(a[4 * g + 2]), sx * sw.z, fmaf(mu, cb.z, bb.z)) + lr[4 * g + 2];
+          const float y3 = fmaf(float(a[4 * g + 3]), sx * sw.w, fmaf(mu, cb.w, bb.w)) + lr[4 * g + 3];
+          if (m < M && n < N) {
+            if (ep.y_bf16) {
+              const uint32_t p0 = uint32_t(f32_to_bf16(y0)) | (uint32_t(f32_to_bf16(y1)) << 16);
+              const uint32_t p1 = uint32_t(f32_to_bf16(y2)) | (uint32_t(f32_to_bf16(y3)) << 16);
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ep.Y) + m * ep.ldy + n) =
+                  make_uint2(p0, p1);
+            } else {
+              *reinterpret_cast<float4*>(static_cast<float*>(ep.Y) + m * ep.ldy + n) =
+                  make_float4(y0, y1, y2, y3);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 // Main loop
 // ---------
 // Stage loads go straight from global memory to LDS (gfx950
@@ -104,6 +206,7 @@ __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_i8_kernel(
   }
   const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
   const int KT = K / BK;
+  static_assert(4 * (3 * BN + 2 * BM) <= S * STAGE, "epilogue staging fits in LDS");
 
   // Per load instruction q: global row pointer (rows clamped into range) and
   // the 1-KB LDS block it fills.
@@ -196,76 +299,148 @@ __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_i8_kernel(
 #undef HQ_WAIT_STAGE
 #undef HQ_ISSUE_STAGE
 
-  // Epilogue: lane owns token m = m0 + wm0 + 32 i + l % 32 and, per 32-column
-  // strip j, channels n = n0 + wn0 + 32 j + 8 g + 4 (l / 32) + {0..3}, g = 0..3.
-  if constexpr (!DEQ) {
+  gemm_epilogue<BM, BN, TM, TN, NW, DEQ>(acc, smem, tid, lane, m0, n0, wm0, wn0, M, N, Cout, ldc, ep);
+}
+
+// Ping-pong variant (8 waves, 2 per SIMD)
+// ---------------------------------------
+// The block's rows are split between two groups of 4 waves (group g owns rows
+// [g BM/2, (g+1) BM/2)). Every wave alternates a memory phase for stage k
+// (issue its share of the global -> LDS copy of stage k+S-1, then read all
+// MFMA fragments of stage k into registers) and a compute phase (the MFMAs of
+// stage k). Group 1 runs one phase behind group 0 and every phase ends with a
+// block barrier, so on each SIMD one wave is always in its compute phase
+// while the other loads: the MFMA pipe is fed from alternating waves instead
+// of both waves stalling at the same stage barrier.
+//
+// Ordering (phase p = 0 .. 2 KT; wave of group g works on local phase q = p - g):
+//  * stage k is read by group 0 in phase 2k and by group 1 in phase 2k+1;
+//  * before the barrier that ends phase p every wave has completed all its
+//    LDS reads and its share of stages <= (p+1)/2, so the stage read next is
+//    whole once the barrier releases;
+//  * stage k+S-1 lands in buffer (k-1) mod S, whose last reader (group 1,
+//    phase 2k-1) finished before the barrier that ended phase 2k-1.
+template <int BM, int BN, int BK, int WM, int WN, int S, int GM, bool DEQ>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gemm_i8_pp_kernel(
+    const int8_t* __restrict__ A, int64_t M, const int8_t* __restrict__ B, int64_t N, int K,
+    int32_t* __restrict__ Cout, int64_t ldc, GemmEpi ep) {
+  constexpr int NW = 8;
+  constexpr int HM = BM / 2;
+  constexpr int WAVES_N = BN / WN;
+  static_assert((HM / WM) * (BN / WN) == 4, "4 waves per group");
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int NC = BK / 16;
+  constexpr int RPB = 64 / NC;
+  constexpr int LA = BM / (RPB * NW), LB = BN / (RPB * NW), L = LA + LB;
+  constexpr int NS = BK / 32;
+  constexpr int SH = (BK == 128) ? 1 : 2;
+  static_assert(LA * RPB * NW == BM && LB * RPB * NW == BN, "whole load instructions per wave");
+  static_assert(S >= 2 && S <= 4, "2..4 stages");
+  static_assert(BK == 64 || BK == 128, "BK");
+  constexpr int STAGE = (BM + BN) * BK;
+  static_assert(4 * (3 * BN + 2 * BM) <= S * STAGE, "epilogue staging fits in LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2, wl = wave & 3;
+  int64_t m0, n0;
+  {
+    const int tmt = int((M + BM - 1) / BM), tnt = int((N + BN - 1) / BN);
+    const int ntiles = tmt * tnt;
+    int tile = blockIdx.x;
+    if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
+    const int g = tile / (GM * tnt), r = tile - g * (GM * tnt);
+    const int rows_in = (tmt - g * GM) < GM ? (tmt - g * GM) : GM;
+    m0 = int64_t(g * GM + r % rows_in) * BM;
+    n0 = int64_t(r / rows_in) * BN;
+  }
+  const int wm0 = grp * HM + (wl / WAVES_N) * WM, wn0 = (wl % WAVES_N) * WN;
+  const int KT = K / BK;
+
+  const int8_t* gsrc[L];
+  int ldst[L];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t m = m0 + wm0 + i * 32 + lrow;
+  for (int q = 0; q < L; ++q) {
+    const bool isA = q < LA;
+    const int blk = (isA ? q : q - LA) * NW + wave;
+    const int slot = blk * 64 + lane;
+    const int row = slot / NC;
+    const int c = (slot % NC) ^ ((row >> SH) & (NC - 1));
+    int64_t gr = (isA ? m0 : n0) + row;
+    const int64_t lim = (isA ? M : N) - 1;
+    if (gr > lim) gr = lim;
+    gsrc[q] = (isA ? A : B) + gr * K + c * 16;
+    ldst[q] = (isA ? 0 : BM * BK) + blk * 1024;
+  }
+#define HQ_ISSUE_STAGE(KT_)                                                              \
+  do {                                                                                   \
+    uint8_t* base_ = smem + ((KT_) % S) * STAGE;                                         \
+    _Pragma("unroll") for (int q = 0; q < L; ++q)                                        \
+        lds_dma16(gsrc[q] + (KT_) * BK, base_ + ldst[q]);                                \
+  } while (0)
+  // Wait until at most `out_` of this wave's stages are still in flight (and
+  // every LDS read of this wave has returned).
+#define HQ_WAIT_OUT(out_)                          \
+  do {                                             \
+    if ((out_) >= 3) wait_vm_lgkm0<3 * L>();       \
+    else if ((out_) == 2) wait_vm_lgkm0<2 * L>();  \
+    else if ((out_) == 1) wait_vm_lgkm0<L>();      \
+    else wait_vm_lgkm0<0>();                       \
+  } while (0)
+
+  v16i acc[TM][TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + wn0 + j * 32 + 8 * g + 4 * lhalf;
-          if (m < M && n < N) {
-            const v16i& a = acc[i][j];
-            *reinterpret_cast<int4*>(Cout + m * ldc + n) =
-                make_int4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
-          }
+    for (int j = 0; j < TN; ++j) acc[i][j] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+  int issued = -1;  // highest stage this wave has issued
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < KT) { HQ_ISSUE_STAGE(p); issued = p; }
+  HQ_WAIT_OUT(issued);           // stage 0 complete (stages 1..issued may fly)
+  __builtin_amdgcn_s_barrier();
+
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  v4i af[NS][TM], bfr[NS][TN];
+  const int P = 2 * KT + 1;
+  for (int p = 0; p < P; ++p) {
+    const int q = p - grp;
+    if (q >= 0 && q < 2 * KT) {
+      const int k = q >> 1;
+      if (!(q & 1)) {
+        if (k + S - 1 < KT) { HQ_ISSUE_STAGE(k + S - 1); issued = k + S - 1; }
+        const uint8_t* cur = smem + (k % S) * STAGE;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int c = 2 * s + lhalf;
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            af[s][i] = *reinterpret_cast<const v4i*>(cur + swz<BK>(wm0 + i * 32 + lrow, c));
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            bfr[s][j] = *reinterpret_cast<const v4i*>(cur + BM * BK + swz<BK>(wn0 + j * 32 + lrow, c));
         }
-    }
-  } else {
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t m = m0 + wm0 + i * 32 + lrow;
-      const int64_t mc = m < M ? m : M - 1;
-      const float sx = ep.s_x[mc], mu = ep.mu[mc];
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t nb = n0 + wn0 + j * 32;
-        // Low-rank term U[m, :] . L2[:, n] on bf16 MFMA with split operands:
-        // first operand L2^T (rows = channels), second U (columns = tokens),
-        // so the fp32 result has the accumulator's layout.
-        v16f lr = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-        for (int k0 = 0; k0 < ep.rank; k0 += 16) {
-          float f[8];
-          load8(ep.U + mc * ep.rank + k0 + 8 * lhalf, f);
-          const v8bf uh = pack_bf16x8(f, false), ul = pack_bf16x8(f, true);
-          const int64_t nr = nb + lrow < N ? nb + lrow : N - 1;
-          const int64_t off = nr * ep.rank + k0 + 8 * lhalf;
-          const v8bf wh = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
-          const v8bf wl = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
-          lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, uh, lr, 0, 0, 0);
-          lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, uh, lr, 0, 0, 0);
-          lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, ul, lr, 0, 0, 0);
-        }
+          for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t n = nb + 8 * g + 4 * lhalf;
-          const int64_t nq = n < N ? n : N - 4;     // N is a multiple of 8
-          const float4 sw = *reinterpret_cast<const float4*>(ep.s_w + nq);
-          const float4 cb = *reinterpret_cast<const float4*>(ep.c + nq);
-          const float4 bb = *reinterpret_cast<const float4*>(ep.bias + nq);
-          const v16i& a = acc[i][j];
-          const float y0 = fmaf(float(a[4 * g + 0]), sx * sw.x, fmaf(mu, cb.x, bb.x)) + lr[4 * g + 0];
-          const float y1 = fmaf(float(a[4 * g + 1]), sx * sw.y, fmaf(mu, cb.y, bb.y)) + lr[4 * g + 1];
-          const float y2 = fmaf(float(a[4 * g + 2]), sx * sw.z, fmaf(mu, cb.z, bb.z)) + lr[4 * g + 2];
-          const float y3 = fmaf(float(a[4 * g + 3]), sx * sw.w, fmaf(mu, cb.w, bb.w)) + lr[4 * g + 3];
-          if (m < M && n < N) {
-            if (ep.y_bf16) {
-              const uint32_t p0 = uint32_t(f32_to_bf16(y0)) | (uint32_t(f32_to_bf16(y1)) << 16);
-              const uint32_t p1 = uint32_t(f32_to_bf16(y2)) | (uint32_t(f32_to_bf16(y3)) << 16);
-              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ep.Y) + m * ep.ldy + n) =
-                  make_uint2(p0, p1);
-            } else {
-              *reinterpret_cast<float4*>(static_cast<float*>(ep.Y) + m * ep.ldy + n) =
-                  make_float4(y0, y1, y2, y3);
-            }
-          }
-        }
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bfr[s][j], af[s][i], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    const int need = (p + 1) >> 1;
+    const int out = issued - need;
+    HQ_WAIT_OUT(out < 0 ? 0 : out);
+    __builtin_amdgcn_s_barrier();
   }
+#undef HQ_ISSUE_STAGE
+#undef HQ_WAIT_OUT
+  gemm_epilogue<BM, BN, TM, TN, NW, DEQ>(acc, smem, tid, lane, m0, n0, wm0, wn0, M, N, Cout, ldc, ep);
 }
 
 }  // namespace hq
