@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Hadamard-quantized linear tokens/s + effective TOPS (% int8 MFMA/HBM roofline)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
+FP6_PEAK_TOPS = 10100.0        # MI355X dense fp6 / fp4 MFMA (10.1 PFLOP/s)
 
 
 def parse():
@@ -100,7 +101,8 @@ def main():
     Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
     Ys = [torch.empty(w.T, w.d_out, dtype=tdt, device=dev) for _ in range(nbuf)]
     ws = torch.empty(hq.workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
-    codes = torch.empty(w.T, w.d_in, dtype=torch.int8, device=dev)
+    codes = torch.empty(hq.code_bytes(desc, w.T), dtype=torch.uint8, device=dev)
+    fp6 = hq.code_format(desc) == hq.HQ_CODES_E2M3
     s_x = torch.empty(w.T, dtype=torch.float32, device=dev)
     mu = torch.empty(w.T, dtype=torch.float32, device=dev)
     U = torch.empty(w.T, w.rank, dtype=torch.float32, device=dev) if w.rank else None
@@ -136,16 +138,19 @@ def main():
     k2 = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
     in_b = 2 if w.dtype == "bf16" else 4
-    k1_bytes = w.T * (w.d_in * (in_b + 1) + 8 + 4 * w.rank)       # read X, write codes, s_x, mu, U
-    k2_ops = 2.0 * w.T * w.d_in * w.d_out                          # int8 multiply-adds x 2
+    # read X, write codes, s_x, mu, U
+    k1_bytes = w.T * (w.d_in * in_b + 8 + 4 * w.rank) + hq.code_bytes(desc, w.T)
+    k2_ops = 2.0 * w.T * w.d_in * w.d_out                          # code multiply-adds x 2
+    peak = FP6_PEAK_TOPS if fp6 else INT8_PEAK_TOPS
     k1_gbs = k1_bytes / (k1 * 1e-3) / 1e9
     k2_tops = k2_ops / (k2 * 1e-3) / 1e12
     tokens_s = w.T / (ms * 1e-3)
     eff_tops = k2_ops / (ms * 1e-3) / 1e12
     if k2 >= k1:
-        roof = {"kernel": "gemm_i8_dequant", "bound": "mfma", "achieved": round(k2_tops, 2),
-                "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "ops": "int8 multiply-add x2",
-                "frac": round(k2_tops / INT8_PEAK_TOPS, 4), "traffic": None}
+        roof = {"kernel": "gemm_f6_dequant" if fp6 else "gemm_i8_dequant", "bound": "mfma",
+                "achieved": round(k2_tops, 2), "peak": peak, "unit": "TFLOP/s",
+                "ops": ("e2m3" if fp6 else "int8") + " multiply-add x2",
+                "frac": round(k2_tops / peak, 4), "traffic": None}
     else:
         roof = {"kernel": "row_transform", "bound": "hbm", "achieved": round(k1_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
@@ -153,7 +158,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e2m3" if fp6 else "int8",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
                    "block": w.block, "bits": f"W{w.w_bits}A{w.a_bits}", "center": bool(w.center),
@@ -164,7 +170,7 @@ def main():
             "row_transform_ms": round(k1, 5), "row_transform_GBs": round(k1_gbs, 1),
             "row_transform_hbm_frac": round(k1_gbs / HBM_PEAK_GBS, 4),
             "gemm_ms": round(k2, 5), "gemm_TOPS": round(k2_tops, 2),
-            "gemm_mfma_frac": round(k2_tops / INT8_PEAK_TOPS, 4),
+            "gemm_mfma_frac": round(k2_tops / peak, 4),
         },
         "wall_s_timed": round(wall, 4),
     }

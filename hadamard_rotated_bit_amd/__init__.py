@@ -20,7 +20,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import HqDesc, HqError, HqLayout, check, load
+from ._lib import HQ_CODES_E2M3, HQ_CODES_I8, HqDesc, HqError, HqLayout, check, load
 
 F32, BF16 = 0, 1
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16}
@@ -73,29 +73,57 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
 
 
 def validate(desc: Desc) -> None:
-    check(load().hq_validate(ctypes.byref(desc.c())))
+    check(load().hq_validate(desc._ref))
 
 
 def prepared_bytes(desc: Desc) -> int:
-    n = load().hq_prepared_bytes(ctypes.byref(desc.c()))
+    n = load().hq_prepared_bytes(desc._ref)
     if n == 0:
-        check(load().hq_validate(ctypes.byref(desc.c())))
+        check(load().hq_validate(desc._ref))
     return n
 
 
 def layout(desc: Desc) -> HqLayout:
     out = HqLayout()
-    check(load().hq_prepared_layout_of(ctypes.byref(desc.c()), ctypes.byref(out)))
+    check(load().hq_prepared_layout_of(desc._ref, ctypes.byref(out)))
     return out
 
 
 def workspace_bytes(desc: Desc, T: int) -> int:
-    n = load().hq_workspace_bytes(ctypes.byref(desc.c()), T)
+    n = load().hq_workspace_bytes(desc._ref, T)
     if n == 0:
-        check(load().hq_validate(ctypes.byref(desc.c())))
+        check(load().hq_validate(desc._ref))
         if T < 0:
             raise HqError(_lib.HQ_ERR_INVALID_ARG, "T must be >= 0")
     return n
+
+
+def code_format(desc: Desc) -> int:
+    """HQ_CODES_I8 or HQ_CODES_E2M3 (see the code formats in include/hq.h)."""
+    f = load().hq_code_format(desc._ref)
+    if f < 0:
+        check(f)
+    return f
+
+
+def code_bytes(desc: Desc, rows: int) -> int:
+    """Bytes of a code matrix of `rows` rows in the descriptor's code format."""
+    if rows < 0:
+        raise HqError(_lib.HQ_ERR_INVALID_ARG, "rows must be >= 0")
+    n = load().hq_code_bytes(desc._ref, rows)
+    if n == 0 and rows > 0:
+        check(load().hq_validate(desc._ref))
+    return n
+
+
+def _need_codes(t: torch.Tensor, name: str, desc: Desc, rows: int) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in (torch.uint8, torch.int8) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous uint8/int8 code buffer")
+    need = code_bytes(desc, rows)
+    if t.numel() < need:
+        raise ValueError(f"{name} holds {t.numel()} bytes, {need} needed for {rows} rows")
 
 
 def channel_absmax(desc: Desc, X: torch.Tensor) -> torch.Tensor:
@@ -103,7 +131,7 @@ def channel_absmax(desc: Desc, X: torch.Tensor) -> torch.Tensor:
     T = X.shape[0]
     _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
     out = torch.empty(desc.d_in, dtype=torch.float32, device=X.device)
-    check(load().hq_channel_absmax(ctypes.byref(desc.c()), _ptr(X), T, _ptr(out), _stream()))
+    check(load().hq_channel_absmax(desc._ref, _ptr(X), T, _ptr(out), _stream()))
     return out
 
 
@@ -112,7 +140,7 @@ def sigma(desc: Desc, act_absmax: torch.Tensor, weight: torch.Tensor, alpha: flo
     _need(act_absmax, "act_absmax", torch.float32, (desc.d_in,))
     _need(weight, "weight", _TORCH[desc.w_dtype], (desc.d_out, desc.d_in))
     out = torch.empty(desc.d_in, dtype=torch.float32, device=weight.device)
-    check(load().hq_sigma(ctypes.byref(desc.c()), _ptr(act_absmax), _ptr(weight),
+    check(load().hq_sigma(desc._ref, _ptr(act_absmax), _ptr(weight),
                           ctypes.c_float(alpha), _ptr(out), _stream()))
     return out
 
@@ -132,13 +160,13 @@ def prepare(desc: Desc, weight: torch.Tensor, bias: Optional[torch.Tensor] = Non
     if L2 is not None:
         _need(L2, "L2", wdt, (desc.rank, desc.d_out))
     blob = torch.empty(prepared_bytes(desc), dtype=torch.uint8, device=weight.device)
-    check(load().hq_prepare_weights(ctypes.byref(desc.c()), _ptr(weight), _ptr(bias),
+    check(load().hq_prepare_weights(desc._ref, _ptr(weight), _ptr(bias),
                                     _ptr(sigma), _ptr(L1), _ptr(L2), _ptr(blob), _stream()))
     return blob
 
 
 def check_prepared(desc: Desc, prepared: torch.Tensor) -> None:
-    check(load().hq_check_prepared(ctypes.byref(desc.c()), _ptr(prepared), _stream()))
+    check(load().hq_check_prepared(desc._ref, _ptr(prepared), _stream()))
 
 
 def quant_linear(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
@@ -161,25 +189,26 @@ def quant_linear(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
 
 
 def act_quantize(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, out=None):
-    """Activation stage alone: (codes int8 [T, d_in], s_x [T], mu [T], U [T, rank] or None).
+    """Activation stage alone: (codes, s_x [T], mu [T], U [T, rank] or None).
 
-    ``out`` may supply that tuple of preallocated tensors."""
+    ``codes`` is a uint8 buffer of code_bytes(desc, T) bytes in the
+    descriptor's code format. ``out`` may supply that tuple preallocated."""
     T = X.shape[0]
     _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
     dev = X.device
     if out is None:
-        codes = torch.empty(T, desc.d_in, dtype=torch.int8, device=dev)
+        codes = torch.empty(max(code_bytes(desc, T), 1), dtype=torch.uint8, device=dev)
         s_x = torch.empty(T, dtype=torch.float32, device=dev)
         mu = torch.empty(T, dtype=torch.float32, device=dev)
         U = torch.empty(T, desc.rank, dtype=torch.float32, device=dev) if desc.rank else None
     else:
         codes, s_x, mu, U = out
-        _need(codes, "codes", torch.int8, (T, desc.d_in))
+        _need_codes(codes, "codes", desc, T)
         _need(s_x, "s_x", torch.float32, (T,))
         _need(mu, "mu", torch.float32, (T,))
         if desc.rank:
             _need(U, "U", torch.float32, (T, desc.rank))
-    check(load().hq_act_quantize(ctypes.byref(desc.c()), _ptr(prepared), _ptr(X), T, _ptr(codes),
+    check(load().hq_act_quantize(desc._ref, _ptr(prepared), _ptr(X), T, _ptr(codes),
                                  _ptr(s_x), _ptr(mu), _ptr(U), _stream()))
     return codes, s_x, mu, U
 
@@ -190,28 +219,29 @@ def act_transform(desc: Desc, prepared: torch.Tensor, X: torch.Tensor):
     _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
     xt = torch.empty(T, desc.d_in, dtype=torch.float32, device=X.device)
     mu = torch.empty(T, dtype=torch.float32, device=X.device)
-    check(load().hq_act_transform(ctypes.byref(desc.c()), _ptr(prepared), _ptr(X), T, _ptr(xt),
+    check(load().hq_act_transform(desc._ref, _ptr(prepared), _ptr(X), T, _ptr(xt),
                                   _ptr(mu), _stream()))
     return xt, mu
 
 
-def gemm_i32(desc: Desc, a_codes: torch.Tensor, w_codes: torch.Tensor) -> torch.Tensor:
-    """int32 accumulators a_codes [T, d_in] . w_codes [N, d_in]^T."""
-    T, N = a_codes.shape[0], w_codes.shape[0]
-    _need(a_codes, "a_codes", torch.int8, (T, desc.d_in))
-    _need(w_codes, "w_codes", torch.int8, (N, desc.d_in))
+def gemm_i32(desc: Desc, a_codes: torch.Tensor, w_codes: torch.Tensor, T: int,
+             N: int) -> torch.Tensor:
+    """int32 accumulators [T, N] of a_codes (T rows) . w_codes (N rows)^T, both
+    code buffers in the descriptor's code format."""
+    _need_codes(a_codes, "a_codes", desc, T)
+    _need_codes(w_codes, "w_codes", desc, N)
     acc = torch.empty(T, N, dtype=torch.int32, device=a_codes.device)
-    check(load().hq_gemm_i32(ctypes.byref(desc.c()), _ptr(a_codes), _ptr(w_codes), T, N,
-                             _ptr(acc), _stream()))
+    check(load().hq_gemm_i32(desc._ref, _ptr(a_codes), _ptr(w_codes), T, N, _ptr(acc),
+                             _stream()))
     return acc
 
 
 def gemm_dequant(desc: Desc, prepared: torch.Tensor, codes: torch.Tensor, s_x: torch.Tensor,
                  mu: torch.Tensor, U: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """GEMM + dequant epilogue alone, from act_quantize's outputs."""
-    T = codes.shape[0]
-    _need(codes, "codes", torch.int8, (T, desc.d_in))
+    """GEMM + dequant epilogue alone, from act_quantize's outputs (T = len(s_x))."""
+    T = s_x.shape[0]
+    _need_codes(codes, "codes", desc, T)
     _need(s_x, "s_x", torch.float32, (T,))
     _need(mu, "mu", torch.float32, (T,))
     if desc.rank:
@@ -219,13 +249,14 @@ def gemm_dequant(desc: Desc, prepared: torch.Tensor, codes: torch.Tensor, s_x: t
     Y = out if out is not None else torch.empty(T, desc.d_out, dtype=_TORCH[desc.y_dtype],
                                                 device=codes.device)
     _need(Y, "out", _TORCH[desc.y_dtype], (T, desc.d_out))
-    check(load().hq_gemm_dequant(ctypes.byref(desc.c()), _ptr(prepared), _ptr(codes), _ptr(s_x),
+    check(load().hq_gemm_dequant(desc._ref, _ptr(prepared), _ptr(codes), _ptr(s_x),
                                  _ptr(mu), _ptr(U), T, _ptr(Y), _stream()))
     return Y
 
 
 def prepared_views(desc: Desc, prepared: torch.Tensor) -> dict:
-    """Views of the arrays inside a prepared blob (for inspection and tests)."""
+    """Views of the arrays inside a prepared blob (for inspection and tests);
+    w_codes is the raw code buffer of the d_out weight rows."""
     L = layout(desc)
     npad, d = L.d_out_pad, desc.d_in
 
@@ -234,7 +265,7 @@ def prepared_views(desc: Desc, prepared: torch.Tensor) -> dict:
         return prepared[off:off + nbytes].view(dtype).view(*shape)
 
     out = {
-        "w_codes": view(L.w_codes, npad * d, torch.int8, (npad, d))[:desc.d_out],
+        "w_codes": prepared[L.w_codes:L.w_codes + code_bytes(desc, desc.d_out)],
         "s_w": view(L.w_scale, npad, torch.float32, (npad,))[:desc.d_out],
         "c": view(L.c, npad, torch.float32, (npad,))[:desc.d_out],
         "bias": view(L.bias, npad, torch.float32, (npad,))[:desc.d_out],

@@ -23,6 +23,8 @@ class HqLayout(ctypes.Structure):
                  "l2_hi", "l2_lo"]] + [("d_out_pad", ctypes.c_int64)]
 
 
+HQ_CODES_I8, HQ_CODES_E2M3 = 0, 1
+
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_BAD_PREPARED, \
     HQ_ERR_HIP = 0, -1, -2, -3, -4, -5
 
@@ -37,6 +39,8 @@ _SIGS = {
     "hq_prepared_bytes": (ctypes.c_size_t, [_D]),
     "hq_prepared_layout_of": (ctypes.c_int, [_D, ctypes.POINTER(HqLayout)]),
     "hq_workspace_bytes": (ctypes.c_size_t, [_D, _I64]),
+    "hq_code_format": (ctypes.c_int, [_D]),
+    "hq_code_bytes": (ctypes.c_size_t, [_D, _I64]),
     "hq_channel_absmax": (ctypes.c_int, [_D, _P, _I64, _P, _P]),
     "hq_sigma": (ctypes.c_int, [_D, _P, _P, ctypes.c_float, _P, _P]),
     "hq_prepare_weights": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P]),

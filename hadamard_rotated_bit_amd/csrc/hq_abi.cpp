@@ -86,12 +86,18 @@ int check_desc(const hq_desc* d) {
   return HQ_OK;
 }
 
+// Both operands use E2M3 (FP6 MFMA) when both code widths are 4 bits, else
+// int8 bytes (int8 MFMA).
+int code_fmt_of(const hq_desc* d) {
+  return (d->a_bits == 4 && d->w_bits == 4) ? hq::CODES_E2M3 : hq::CODES_I8;
+}
+
 void layout_of(const hq_desc* d, hq_prepared_layout* L) {
   const int64_t np = round_up(d->d_out, hq::GEMM_BN);
   size_t off = 256;
   L->d_out_pad = np;
   L->w_codes = off;
-  off += align256(size_t(np) * d->d_in);
+  off += align256(hq::code_bytes(code_fmt_of(d), np, d->d_in));
   L->w_scale = off;
   off += align256(4 * size_t(np));
   L->c = off;
@@ -118,7 +124,7 @@ Workspace workspace_of(const hq_desc* d, int64_t T) {
   Workspace w;
   size_t off = 0;
   w.codes = off;
-  off += align256(size_t(T) * d->d_in);
+  off += align256(hq::code_bytes(code_fmt_of(d), T, d->d_in));
   w.s_x = off;
   off += align256(4 * size_t(T));
   w.mu = off;
@@ -139,7 +145,7 @@ inline const P* at(const void* base, size_t off) {
 }
 
 // Activation stage shared by hq_quant_linear and hq_act_quantize.
-int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, int8_t* codes,
+int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, void* codes,
             float* s_x, float* mu, float* U, hipStream_t s) {
   hq_prepared_layout L;
   layout_of(d, &L);
@@ -152,7 +158,8 @@ int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, in
   a.log2b = log2i(d->block);
   a.center = d->center;
   a.qmax = qmax_of(d->a_bits);
-  a.codes = codes;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.code_fmt = code_fmt_of(d);
   a.out_s = s_x;
   a.out_aux = mu;
   a.mode = hq::ROW_ACT;
@@ -167,7 +174,18 @@ int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, in
   return HQ_OK;
 }
 
-int run_gemm_dequant(const hq_desc* d, const void* prepared, const int8_t* codes,
+// Integer GEMM on the descriptor's code format.
+hipError_t launch_codes_gemm(const hq_desc* d, const void* a_codes, int64_t T, const void* w_codes,
+                             int64_t N, int32_t* acc, int64_t ldc, const hq::GemmEpi* ep,
+                             hipStream_t s) {
+  if (code_fmt_of(d) == hq::CODES_E2M3)
+    return hq::launch_gemm_f6(static_cast<const uint8_t*>(a_codes), T,
+                              static_cast<const uint8_t*>(w_codes), N, d->d_in, acc, ldc, ep, s);
+  return hq::launch_gemm(static_cast<const int8_t*>(a_codes), T,
+                         static_cast<const int8_t*>(w_codes), N, d->d_in, acc, ldc, ep, s);
+}
+
+int run_gemm_dequant(const hq_desc* d, const void* prepared, const void* codes,
                      const float* s_x, const float* mu, const float* U, int64_t T, void* Y,
                      hipStream_t s) {
   hq_prepared_layout L;
@@ -185,8 +203,8 @@ int run_gemm_dequant(const hq_desc* d, const void* prepared, const int8_t* codes
   ep.Y = Y;
   ep.y_bf16 = d->y_dtype == HQ_BF16;
   ep.ldy = d->d_out;
-  hipError_t e = hq::launch_gemm(codes, T, at<int8_t>(prepared, L.w_codes), d->d_out, d->d_in,
-                                 nullptr, 0, &ep, s);
+  hipError_t e = launch_codes_gemm(d, codes, T, at<uint8_t>(prepared, L.w_codes), d->d_out,
+                                   nullptr, 0, &ep, s);
   if (e != hipSuccess) return hip_fail(e, "GEMM kernel launch");
   return HQ_OK;
 }
@@ -243,6 +261,23 @@ size_t hq_workspace_bytes(const hq_desc* desc, int64_t T) {
   return workspace_of(desc, T).total;
 }
 
+int hq_code_format(const hq_desc* desc) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  return code_fmt_of(desc);
+}
+
+size_t hq_code_bytes(const hq_desc* desc, int64_t rows) {
+  g_err.clear();
+  if (check_desc(desc) != HQ_OK) return 0;
+  if (rows < 0) {
+    fail(HQ_ERR_INVALID_ARG, "rows must be >= 0 (got %lld)", (long long)rows);
+    return 0;
+  }
+  return hq::code_bytes(code_fmt_of(desc), rows, desc->d_in);
+}
+
 int hq_channel_absmax(const hq_desc* desc, const void* X, int64_t T, float* absmax,
                       void* stream) {
   g_err.clear();
@@ -288,10 +323,13 @@ int hq_prepare_weights(const hq_desc* desc, const void* weight, const float* bia
   layout_of(desc, &L);
   const int64_t np = L.d_out_pad, dout = desc->d_out, din = desc->d_in;
   hipError_t e = hipSuccess;
-  // Padding rows of the code matrix and of the per-channel vectors are zero.
+  // Padding rows of the code matrix and of the per-channel vectors are zero
+  // (d_out is a multiple of 8, so E2M3 row groups are never split).
+  const int fmt = code_fmt_of(desc);
   if (np > dout) {
-    e = hq::launch_fill_u8(at<uint8_t>(prepared, L.w_codes + size_t(dout) * din), 0,
-                           size_t(np - dout) * din, s);
+    const size_t used = hq::code_bytes(fmt, dout, int(din));
+    e = hq::launch_fill_u8(at<uint8_t>(prepared, L.w_codes + used), 0,
+                           hq::code_bytes(fmt, np, int(din)) - used, s);
   }
   if (e == hipSuccess)
     e = hq::launch_fill_u32(at<uint32_t>(prepared, L.w_scale), 0u, (L.sigma_inv - L.w_scale) / 4, s);
@@ -312,7 +350,8 @@ int hq_prepare_weights(const hq_desc* desc, const void* weight, const float* bia
     a.log2b = log2i(desc->block);
     a.center = 0;
     a.qmax = qmax_of(desc->w_bits);
-    a.codes = at<int8_t>(prepared, L.w_codes);
+    a.codes = at<uint8_t>(prepared, L.w_codes);
+    a.code_fmt = fmt;
     a.out_s = at<float>(prepared, L.w_scale);
     a.out_aux = at<float>(prepared, L.c);
     a.mode = hq::ROW_WEIGHT;
@@ -372,7 +411,7 @@ int hq_quant_linear(const hq_desc* desc, const void* prepared, const void* X, in
   if (workspace_bytes < w.total)
     return fail(HQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, w.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int8_t* codes = at<int8_t>(workspace, w.codes);
+  void* codes = at<uint8_t>(workspace, w.codes);
   float* s_x = at<float>(workspace, w.s_x);
   float* mu = at<float>(workspace, w.mu);
   float* U = desc->rank ? at<float>(workspace, w.U) : nullptr;
@@ -382,7 +421,7 @@ int hq_quant_linear(const hq_desc* desc, const void* prepared, const void* X, in
 }
 
 int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
-                    int8_t* codes, float* s_x, float* mu, float* U, void* stream) {
+                    void* codes, float* s_x, float* mu, float* U, void* stream) {
   g_err.clear();
   int st = check_desc(desc);
   if (st != HQ_OK) return st;
@@ -419,7 +458,7 @@ int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, i
   return e == hipSuccess ? HQ_OK : hip_fail(e, "transform kernel launch");
 }
 
-int hq_gemm_i32(const hq_desc* desc, const int8_t* a_codes, const int8_t* w_codes, int64_t T,
+int hq_gemm_i32(const hq_desc* desc, const void* a_codes, const void* w_codes, int64_t T,
                 int64_t N, int32_t* acc, void* stream) {
   g_err.clear();
   int st = check_desc(desc);
@@ -427,12 +466,12 @@ int hq_gemm_i32(const hq_desc* desc, const int8_t* a_codes, const int8_t* w_code
   if (T < 0 || N <= 0 || N % 8) return fail(HQ_ERR_INVALID_ARG, "need T >= 0 and N a positive multiple of 8");
   if (T == 0) return HQ_OK;
   if (!a_codes || !w_codes || !acc) return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
-  hipError_t e = hq::launch_gemm(a_codes, T, w_codes, N, desc->d_in, acc, N, nullptr,
-                                 static_cast<hipStream_t>(stream));
+  hipError_t e = launch_codes_gemm(desc, a_codes, T, w_codes, N, acc, N, nullptr,
+                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? HQ_OK : hip_fail(e, "GEMM kernel launch");
 }
 
-int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const int8_t* codes,
+int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes,
                     const float* s_x, const float* mu, const float* U, int64_t T, void* Y,
                     void* stream) {
   g_err.clear();

@@ -38,6 +38,26 @@ bool row_geometry(int d, RowGeom* g) {
   return false;
 }
 
+// Writes the lane's C chunks of codes (chunk c = channels c 8G + 8t .. +7) in
+// the launch's code format: int8 bytes at row * d + channel, or E2M3 pieces
+// in the 4-row-group layout.
+template <int G, int C>
+__device__ __forceinline__ void store_codes(const RowArgs& a, int64_t row, int64_t base, int t,
+                                            const float* v, float rcp) {
+  if (a.code_fmt == CODES_E2M3) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) store_e2m3x8(a.codes, row, a.d, c * 8 * G + t * 8, &v[c * 8], rcp);
+  } else {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const float* vc = &v[c * 8];
+      *reinterpret_cast<uint2*>(a.codes + base + c * 8 * G) =
+          make_uint2(pack_codes4(vc[0], vc[1], vc[2], vc[3], rcp),
+                     pack_codes4(vc[4], vc[5], vc[6], vc[7], rcp));
+    }
+  }
+}
+
 // One wave processes 64/G rows at once; a 256-thread block covers 4 waves.
 //
 // Per row (HadaNorm Eq. (1) activation side, HaTQ Eq. (3) quantiser):
@@ -139,13 +159,7 @@ __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv
     amax = group_max<G>(amax);
     const float rcp = amax > 0.0f ? a.qmax / amax : 0.0f;
     if (valid) {
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const float* vc = &v[c * 8];
-        *reinterpret_cast<uint2*>(a.codes + base + c * 8 * G) =
-            make_uint2(pack_codes4(vc[0], vc[1], vc[2], vc[3], rcp),
-                       pack_codes4(vc[4], vc[5], vc[6], vc[7], rcp));
-      }
+      store_codes<G, C>(a, row, base, t, v, rcp);
       if (t == 0) {
         a.out_s[row] = amax * inv_sqrt_b / a.qmax;
         a.out_aux[row] = sum * inv_sqrt_b;
@@ -182,13 +196,7 @@ __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv
   amax = group_max<G>(amax);
   const float rcp = amax > 0.0f ? a.qmax / amax : 0.0f;
   if (valid) {
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const float* vc = &v[c * 8];
-      *reinterpret_cast<uint2*>(a.codes + base + c * 8 * G) =
-          make_uint2(pack_codes4(vc[0], vc[1], vc[2], vc[3], rcp),
-                     pack_codes4(vc[4], vc[5], vc[6], vc[7], rcp));
-    }
+    store_codes<G, C>(a, row, base, t, v, rcp);
     if (t == 0) {
       a.out_s[row] = amax * inv_sqrt_b / a.qmax;
       a.out_aux[row] = mu * inv_sqrt_b;

@@ -15,11 +15,9 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 // bf16 is carried as raw uint16_t bit patterns on the device side.
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// float -> bf16, round to nearest even (inputs here are finite).
+// float -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Load 8 consecutive elements as float.
@@ -49,6 +47,39 @@ __device__ __forceinline__ uint32_t pack_codes4(float a, float b, float c, float
   const uint32_t ab = __builtin_amdgcn_perm(code_bits(b, rcp), code_bits(a, rcp), 0x0c0c0400u);
   const uint32_t cd = __builtin_amdgcn_perm(code_bits(d, rcp), code_bits(c, rcp), 0x0c0c0400u);
   return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// Four codes as E2M3 bytes (byte k = code of the k-th value): the magnitude
+// |q| = rint(|v| rcp) in 0..7 indexes the table of E2M3 encodings
+// {0, 8, 16, 20, 24, 26, 28, 30} with one byte permute; the sign bit (bit 5)
+// is set for negative v with q != 0, so that q = 0 is always +0.
+__device__ __forceinline__ uint32_t e2m3_codes4(float a, float b, float c, float d, float rcp) {
+  const uint32_t mag = pack_codes4(fabsf(a), fabsf(b), fabsf(c), fabsf(d), rcp);
+  const uint32_t t = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, mag);
+  const uint32_t s01 = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0703u);
+  const uint32_t s23 = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x07030c0cu);
+  const uint32_t nz = (t + 0x7F7F7F7Fu) & 0x80808080u;  // bit 7 of byte k: code k != 0
+  return t | (((s01 | s23) & nz) >> 2);
+}
+// Four 6-bit values in the bytes of x -> one 24-bit little-endian string.
+__device__ __forceinline__ uint32_t pack6x4(uint32_t x) {
+  const uint32_t y = (x & 0x003F003Fu) | ((x >> 2) & 0x0FC00FC0u);
+  return (y & 0xFFFu) | ((y >> 4) & 0xFFF000u);
+}
+// Stores the E2M3 codes of the 8 values v (channels e0 .. e0+7 of `row`,
+// e0 a multiple of 8) in the 4-row-group layout of a d-channel code matrix:
+// a 6-byte piece at (row/4) 3d + (e0/128) 384 + (row%4) 96 + 6 ((e0%128)/8),
+// written as a dword and a short at their natural alignment.
+__device__ __forceinline__ void store_e2m3x8(uint8_t* __restrict__ codes, int64_t row, int d,
+                                             int e0, const float* v, float rcp) {
+  const uint32_t p0 = pack6x4(e2m3_codes4(v[0], v[1], v[2], v[3], rcp));
+  const uint32_t p1 = pack6x4(e2m3_codes4(v[4], v[5], v[6], v[7], rcp));
+  const uint32_t w0 = p0 | (p1 << 24), w1 = p1 >> 8;  // 48-bit piece
+  uint8_t* p = codes + (row >> 2) * 3 * int64_t(d) + (e0 >> 7) * 384 + (row & 3) * 96 +
+               6 * ((e0 & 127) >> 3);
+  const bool odd = e0 & 8;  // odd pieces start 2 bytes past a dword boundary
+  *reinterpret_cast<uint32_t*>(p + (odd ? 2 : 0)) = odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0;
+  *reinterpret_cast<uint16_t*>(p + (odd ? 0 : 4)) = uint16_t(odd ? w0 : w1);
 }
 
 // Direct global -> LDS copy of 16 bytes per lane (gfx950

@@ -45,14 +45,15 @@ __device__ __forceinline__ v8bf pack_bf16x8(const float f[8], bool residual) {
   return __builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-// Epilogue shared by the GEMM kernels: lane owns token
+// Epilogue shared by the GEMM kernels (int32 or exact-integer float
+// accumulators): lane owns token
 // m = m0 + wm0 + 32 i + l % 32 and, per 32-column strip j, channels
 // n = n0 + wn0 + 32 j + 8 g + 4 (l / 32) + {0..3}, g = 0..3. `smem` must be
 // idle (no LDS reads or DMA of the main loop in flight in any wave) once
 // every wave of the block has arrived; its first 4 (3 BN + 2 BM) bytes are
 // reused for the block's per-channel and per-token vectors.
-template <int BM, int BN, int TM, int TN, int NW, bool DEQ>
-__device__ __forceinline__ void gemm_epilogue(v16i (&acc)[TM][TN], uint8_t* smem, int tid, int lane,
+template <int BM, int BN, int TM, int TN, int NW, bool DEQ, typename AccT>
+__device__ __forceinline__ void gemm_epilogue(AccT (&acc)[TM][TN], uint8_t* smem, int tid, int lane,
                                               int64_t m0, int64_t n0, int wm0, int wn0, int64_t M,
                                               int64_t N, int32_t* __restrict__ Cout, int64_t ldc,
                                               const GemmEpi& ep) {
@@ -67,9 +68,9 @@ __device__ __forceinline__ void gemm_epilogue(v16i (&acc)[TM][TN], uint8_t* smem
         for (int g = 0; g < 4; ++g) {
           const int64_t n = n0 + wn0 + j * 32 + 8 * g + 4 * lhalf;
           if (m < M && n < N) {
-            const v16i& a = acc[i][j];
+            const AccT& a = acc[i][j];
             *reinterpret_cast<int4*>(Cout + m * ldc + n) =
-                make_int4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+                make_int4(int(a[4 * g]), int(a[4 * g + 1]), int(a[4 * g + 2]), int(a[4 * g + 3]));
           }
         }
     }
@@ -125,7 +126,7 @@ __device__ __forceinline__ void gemm_epilogue(v16i (&acc)[TM][TN], uint8_t* smem
           const float4 sw = *reinterpret_cast<const float4*>(P + nl);
           const float4 cb = *reinterpret_cast<const float4*>(P + BN + nl);
           const float4 bb = *reinterpret_cast<const float4*>(P + 2 * BN + nl);
-          const v16i& a = acc[i][j];
+          const AccT& a = acc[i][j];
           const float y0 = fmaf(float(a[4 * g + 0]), sx * sw.x, fmaf(mu, cb.x, bb.x)) + lr[4 * g + 0];
           const float y1 = fmaf(float(a[4 * g + 1]), sx * sw.y, fmaf(mu, cb.y, bb.y)) + lr[4 * g + 1];
           const float y2 = fmaf(float(a[4 * g + 2]), sx * sw.z, fmaf(mu, cb.z, bb.z)) + lr[4 * g + 2];

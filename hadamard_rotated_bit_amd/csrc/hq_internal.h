@@ -21,6 +21,16 @@ bool row_geometry(int d_in, RowGeom* g);
 
 enum RowMode { ROW_ACT = 0, ROW_WEIGHT = 1, ROW_EXPORT = 2 };
 
+// Code storage (the C ABI's hq_code_format_t): int8 bytes, or E2M3 fp6 in
+// 4-row groups (group g of rows at 3 d g bytes; 128-code slice s of row
+// 4g + i at byte 384 s + 96 i inside it; code k of the slice at bits 6k).
+enum CodeFmt { CODES_I8 = 0, CODES_E2M3 = 1 };
+constexpr int F6_GROUP = 4;
+inline size_t code_bytes(int fmt, int64_t rows, int d) {
+  if (fmt == CODES_E2M3) return size_t((rows + F6_GROUP - 1) / F6_GROUP) * 3 * size_t(d);
+  return size_t(rows) * size_t(d);
+}
+
 struct RowArgs {
   const void* in;         // [rows, d] f32 or bf16
   int in_bf16;
@@ -30,7 +40,8 @@ struct RowArgs {
   int log2b;
   int center;
   float qmax;
-  int8_t* codes;          // [rows, d]             (ACT, WEIGHT)
+  uint8_t* codes;         // rows x d codes in code_fmt (ACT, WEIGHT)
+  int code_fmt;           // CodeFmt
   float* out_s;           // [rows] dequant scale  (ACT, WEIGHT)
   float* out_aux;         // [rows] mu (ACT, EXPORT) or c (WEIGHT)
   float* out_xt;          // [rows, d] f32         (EXPORT)
@@ -80,9 +91,14 @@ struct GemmEpi {
   int64_t ldy;
 };
 // acc = A [M, K] . B [N, K]^T ; epilogue: int32 store to acc_out (ld = ldc) when
-// epi == NULL, else the dequant epilogue. B must have >= roundup(N, GEMM_BN)
-// readable rows unless clamp_b is set.
+// epi == NULL, else the dequant epilogue. Loads of rows past M / N are
+// clamped to the last row.
 hipError_t launch_gemm(const int8_t* A, int64_t M, const int8_t* B, int64_t N, int K,
                        int32_t* acc_out, int64_t ldc, const GemmEpi* epi, hipStream_t s);
+// The same product on E2M3 codes (CODES_E2M3 layout, M and N rows; K a
+// multiple of 128) with the FP6 MFMA; rows past M / N in their last 4-row
+// group must be readable (their results are discarded).
+hipError_t launch_gemm_f6(const uint8_t* A, int64_t M, const uint8_t* B, int64_t N, int K,
+                          int32_t* acc_out, int64_t ldc, const GemmEpi* epi, hipStream_t s);
 
 }  // namespace hq

@@ -13,10 +13,9 @@
  * (HaTQ supplement Sec. VII-A Eq. (34); data-free int4 blog, step 7), mu the
  * per-token mean of X diag(1/sigma) H. X~ is quantised per token and W~ per
  * output channel with the symmetric quantiser of HaTQ Sec. III-A Eq. (3)
- * (codes in [-(2^(b-1)-1), 2^(b-1)-1], int4 codes carried in int8 lanes),
- * multiplied in an int8 MFMA GEMM with int32 accumulation (HaTQ Eq. (4)),
- * and dequantised with the accumulator scale s_x s_w (HaTQ Eq. (18)) plus
- * the bias correction:
+ * (codes in [-(2^(b-1)-1), 2^(b-1)-1]), multiplied in an integer-exact MFMA
+ * GEMM (HaTQ Eq. (4); see "Code formats" below) and dequantised with the
+ * accumulator scale s_x s_w (HaTQ Eq. (18)) plus the bias correction:
  *
  *     Y_tj = s_x,t s_w,j acc_tj + b_j + mu_t c_j [+ (x'_t L1) L2_:j],
  *     c = 1^T W~,  x' = x / sigma.
@@ -36,6 +35,24 @@
  *    is returned and hq_last_error() describes the problem. No C++
  *    exception crosses this interface.
  *  - Unsupported combinations are rejected, never coerced.
+ *
+ * Code formats (hq_code_format). Activation and weight codes of one layer
+ * share a format, fixed by the descriptor:
+ *  HQ_CODES_I8    (a_bits = 8 or w_bits = 8): int8, row-major [rows, d_in],
+ *                 one byte per code; int32 accumulation on the int8 MFMA.
+ *  HQ_CODES_E2M3  (a_bits = w_bits = 4): each code q in [-7, 7] is stored as
+ *                 the 6-bit float E2M3 of the same value (bit 5 sign, bits
+ *                 4-3 exponent with bias 1, bits 2-0 mantissa; |q| = 0..7 ->
+ *                 0, 8, 16, 20, 24, 26, 28, 30; q = 0 is stored as +0). E2M3
+ *                 holds every integer up to 7 exactly, so the FP6 MFMA with
+ *                 fp32 accumulation returns the exact integer dot products
+ *                 (|acc| <= 49 d_in < 2^24). Rows are grouped by 4: group g
+ *                 (rows 4g .. 4g+3) occupies bytes [3 d_in g, 3 d_in (g+1));
+ *                 inside it, 128-code slice s of row 4g+i is the 96-byte
+ *                 little-endian bit string at byte 384 s + 96 i, code
+ *                 128 s + k at bits [6k, 6k+6). A matrix of R rows takes
+ *                 hq_code_bytes(desc, R) = ceil(R/4) * 3 d_in bytes; bytes of
+ *                 rows past R in the last group are never read as results.
  */
 #ifndef HQ_H_
 #define HQ_H_
@@ -47,7 +64,7 @@
 extern "C" {
 #endif
 
-#define HQ_ABI_VERSION 1
+#define HQ_ABI_VERSION 2
 
 typedef enum {
   HQ_OK = 0,
@@ -59,6 +76,8 @@ typedef enum {
 } hq_status;
 
 typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
+
+typedef enum { HQ_CODES_I8 = 0, HQ_CODES_E2M3 = 1 } hq_code_format_t;
 
 /* Layer descriptor (plain data, passed by host pointer).
  *  d_in    input channels: a multiple of 128 up to 2048, of 256 up to 4096,
@@ -83,7 +102,8 @@ typedef struct {
 /* Byte offsets of the arrays inside a prepared blob (all 256-byte aligned). */
 typedef struct {
   size_t total;        /* hq_prepared_bytes                                  */
-  size_t w_codes;      /* int8  [d_out_pad, d_in]  codes of W~^T, row j = out j */
+  size_t w_codes;      /* codes of W~^T, d_out_pad rows (row j = out j), in
+                          the descriptor's code format                      */
   size_t w_scale;      /* f32   [d_out_pad]        s_w (0 for padding rows)     */
   size_t c;            /* f32   [d_out_pad]        c = 1^T W~                   */
   size_t bias;         /* f32   [d_out_pad]        b (0 if none)                */
@@ -116,6 +136,14 @@ int hq_prepared_layout_of(const hq_desc* desc, hq_prepared_layout* out);
 
 /* Host-only: workspace bytes hq_quant_linear needs for T tokens; 0 if invalid. */
 size_t hq_workspace_bytes(const hq_desc* desc, int64_t T);
+
+/* Host-only: the code format of ``desc`` (hq_code_format_t), or a negative
+ * hq_status if the descriptor is invalid. */
+int hq_code_format(const hq_desc* desc);
+
+/* Host-only: bytes of a code matrix of ``rows`` rows for ``desc`` (see Code
+ * formats); 0 if the descriptor is invalid or rows < 0. */
+size_t hq_code_bytes(const hq_desc* desc, int64_t rows);
 
 /* Calibration statistic for the smoothing scale (HadaNorm Eq. (3)):
  * absmax[i] = max_t |X[t, i]| over the T rows of X [T, d_in] (x_dtype).
@@ -157,11 +185,12 @@ int hq_quant_linear(const hq_desc* desc, const void* prepared, const void* X, in
 
 /* ---- Stage entry points (the same kernels, for testing and profiling) ---- */
 
-/* Activation stage alone: codes int8 [T, d_in] (natural channel order),
- * s_x f32 [T] (dequant scale of the normalised X~ row), mu f32 [T],
- * U f32 [T, rank] (x' L1; ignored/NULL when rank = 0). */
+/* Activation stage alone: codes of T rows in the descriptor's code format
+ * (hq_code_bytes(desc, T) bytes, natural channel order), s_x f32 [T]
+ * (dequant scale of the normalised X~ row), mu f32 [T], U f32 [T, rank]
+ * (x' L1; ignored/NULL when rank = 0). */
 int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
-                    int8_t* codes, float* s_x, float* mu, float* U, void* stream);
+                    void* codes, float* s_x, float* mu, float* U, void* stream);
 
 /* Debug export of the float transform before quantisation:
  * Xt f32 [T, d_in] = X~ (normalised H, centred if desc->center), mu f32 [T]. */
@@ -169,13 +198,13 @@ int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, i
                      float* Xt, float* mu, void* stream);
 
 /* Integer GEMM alone: acc int32 [T, N] = a_codes [T, d_in] . w_codes [N, d_in]^T,
- * both int8 row-major; N a multiple of 8. */
-int hq_gemm_i32(const hq_desc* desc, const int8_t* a_codes, const int8_t* w_codes, int64_t T,
+ * both in the descriptor's code format (T and N rows); N a multiple of 8. */
+int hq_gemm_i32(const hq_desc* desc, const void* a_codes, const void* w_codes, int64_t T,
                 int64_t N, int32_t* acc, void* stream);
 
 /* GEMM + dequant epilogue alone, from activation-stage outputs (layouts as in
  * hq_act_quantize; U NULL when rank = 0). Y [T, d_out] y_dtype. */
-int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const int8_t* codes,
+int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes,
                     const float* s_x, const float* mu, const float* U, int64_t T, void* Y,
                     void* stream);
 

@@ -21,6 +21,7 @@ import torch
 from oracle import hq_oracle as O
 from hadamard_rotated_bit_amd import workloads as WL
 import hadamard_rotated_bit_amd as hq
+import codefmt
 
 TIE_WINDOW = 2e-3
 MAX_FLIP_FRAC = 1e-4
@@ -93,6 +94,21 @@ def check_codes(gpu_codes, ora_codes, ora_v, what: str):
         dist = np.abs(av - np.floor(av) - 0.5)
         assert dist.max() <= TIE_WINDOW, f"{what}: flip not at a tie (distance {dist.max():.3e})"
     return int(bad.sum())
+
+
+def codes_np(desc: hq.Desc, buf: torch.Tensor, rows: int, idx=None) -> np.ndarray:
+    """Integer codes [rows, d_in] (or rows `idx`) of a device code buffer of
+    `rows` rows, read on the host from the format's definition (codefmt.py)."""
+    fmt = codefmt.fmt_of(desc.a_bits, desc.w_bits)
+    assert hq.code_format(desc) == fmt
+    assert hq.code_bytes(desc, rows) == codefmt.nbytes(fmt, rows, desc.d_in)
+    return codefmt.decode(fmt, buf.detach().cpu().numpy(), rows, desc.d_in, idx)
+
+
+def codes_dev(desc: hq.Desc, codes: np.ndarray) -> torch.Tensor:
+    """Device code buffer holding integer codes [rows, d_in]."""
+    fmt = codefmt.fmt_of(desc.a_bits, desc.w_bits)
+    return torch.from_numpy(codefmt.encode(fmt, codes)).cuda()
 
 
 def rel_fro(a, b) -> float:

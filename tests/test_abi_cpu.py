@@ -7,6 +7,7 @@ import pytest
 from hadamard_rotated_bit_amd import _lib
 from hadamard_rotated_bit_amd import Desc, F32, BF16
 from hadamard_rotated_bit_amd import workloads as WL
+import codefmt
 
 lib = _lib.load()
 
@@ -26,7 +27,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lib.hq_abi_version() == 1
+    assert lib.hq_abi_version() == 2
     assert lib.hq_status_str(0) == b"HQ_OK"
     assert lib.hq_status_str(-3) == b"HQ_ERR_WORKSPACE"
     assert lib.hq_status_str(99) == b"HQ_ERR_UNKNOWN"
@@ -44,10 +45,12 @@ def test_workload_descriptors_valid(name):
     assert L.d_out_pad % 256 == 0 and L.d_out_pad >= w.d_out
     offs = [L.w_codes, L.w_scale, L.c, L.bias, L.sigma_inv, L.l1_hi, L.l1_lo, L.l2_hi, L.l2_lo]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
-    assert L.w_scale - L.w_codes >= L.d_out_pad * w.d_in
+    fmt = codefmt.fmt_of(w.a_bits, w.w_bits)
+    assert lib.hq_code_format(ctypes.byref(d)) == fmt
+    assert L.w_scale - L.w_codes >= codefmt.nbytes(fmt, L.d_out_pad, w.d_in)
     assert L.total == lib.hq_prepared_bytes(ctypes.byref(d))
     ws = lib.hq_workspace_bytes(ctypes.byref(d), w.T)
-    assert ws >= w.T * w.d_in + 8 * w.T + 4 * w.T * w.rank
+    assert ws >= codefmt.nbytes(fmt, w.T, w.d_in) + 8 * w.T + 4 * w.T * w.rank
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -74,6 +77,33 @@ def test_block_one_and_full():
     assert lib.hq_validate(ctypes.byref(_d(d_in=4096, block=4096))) == 0
 
 
+@pytest.mark.parametrize("a_bits,w_bits,fmt", [(4, 4, 1), (8, 4, 0), (4, 8, 0), (8, 8, 0)])
+def test_code_format_and_bytes(a_bits, w_bits, fmt):
+    d = ctypes.byref(_d(a_bits=a_bits, w_bits=w_bits))
+    assert lib.hq_code_format(d) == fmt
+    for rows in [0, 1, 3, 4, 5, 8192]:
+        assert lib.hq_code_bytes(d, rows) == codefmt.nbytes(fmt, rows, 1152)
+    assert lib.hq_code_bytes(d, -1) == 0
+    assert lib.hq_code_format(ctypes.byref(_d(a_bits=5))) == -2
+
+
+def test_e2m3_table_matches_format_definition():
+    # codes 0..7 and their negatives against the E2M3 definition (sign, two
+    # exponent bits with bias 1, three mantissa bits), and the sample of the
+    # format text: |q| = 0..7 -> 0, 8, 16, 20, 24, 26, 28, 30
+    import numpy as np
+    pats = codefmt.e2m3_bits(np.arange(-7, 8))
+    assert list(pats[7:]) == [0, 8, 16, 20, 24, 26, 28, 30]
+    assert list(codefmt.e2m3_value(pats)) == list(range(-7, 8))
+    assert codefmt.e2m3_value(np.array([0b000100]))[0] == 0.5      # subnormal m/8
+    assert codefmt.e2m3_value(np.array([0b011111]))[0] == 7.5      # largest
+    # a hand-packed 128-code slice: code 0 = 1, code 1 = -7
+    q = np.zeros((1, 128), dtype=np.int64)
+    q[0, 0], q[0, 1] = 1, -7
+    buf = codefmt.encode(codefmt.E2M3, q)
+    assert buf.size == 384 and buf[0] == 0x88 and buf[1] == 0x0F and not buf[2:].any()
+
+
 def test_null_desc():
     assert lib.hq_validate(None) == -1
     assert lib.hq_prepared_bytes(None) == 0
@@ -94,6 +124,7 @@ def test_entry_points_reject_before_launch():
     assert lib.hq_prepare_weights(d_r, p, None, p, None, None, p, None) == -1  # rank needs L1/L2
     assert lib.hq_sigma(d, p, p, ctypes.c_float(1.5), p, None) == -1
     assert lib.hq_gemm_i32(d, p, p, 16, 12, p, None) == -1                # N % 8
+    assert lib.hq_gemm_i32(d, p, None, 16, 16, p, None) == -1             # NULL codes
     assert lib.hq_act_quantize(d_r, p, p, 4, p, p, p, None, None) == -1    # U missing
     assert lib.hq_channel_absmax(d, None, 8, p, None) == -1
 

@@ -9,7 +9,7 @@ import torch
 import hadamard_rotated_bit_amd as hq
 from hadamard_rotated_bit_amd import workloads as WL
 from oracle import hq_oracle as O
-from parity import MAX_FLIP_FRAC, Y_TOL, check_codes, rel_fro, tdev, to_np
+from parity import MAX_FLIP_FRAC, Y_TOL, check_codes, codes_np, rel_fro, tdev, to_np
 
 pytestmark = pytest.mark.gpu
 DT = {"f32": hq.F32, "bf16": hq.BF16}
@@ -45,31 +45,31 @@ def run_case(T, d_in, d_out, *, block, a_bits=4, w_bits=4, center=True, alpha=0.
     return desc, prep, X, Y, codes, s_x, mu, U, ora
 
 
-def check_all(Y, codes, s_x, ora):
+def check_all(Y, codes, s_x, ora, desc):
     err = rel_fro(to_np(Y), ora["y_out"])
     assert err <= Y_TOL, err
     ratio = np.divide(ora["xt"], ora["s_x"][:, None], out=np.zeros_like(ora["xt"]),
                       where=ora["s_x"][:, None] > 0)
-    check_codes(to_np(codes), ora["qa"], ratio, "activation codes")
+    check_codes(codes_np(desc, codes, Y.shape[0]), ora["qa"], ratio, "activation codes")
     np.testing.assert_allclose(to_np(s_x), ora["s_x"], rtol=1e-5, atol=1e-30)
 
 
 def test_empty_batch():
     desc, prep, X, Y, codes, s_x, mu, U, ora = run_case(0, 128, 64, block=128)
-    assert Y.shape == (0, 64) and codes.shape == (0, 128)
+    assert Y.shape == (0, 64) and hq.code_bytes(desc, 0) == 0
 
 
 @pytest.mark.parametrize("T", [1, 3, 129, 257, 1000])
 def test_ragged_tokens(T):
     r = run_case(T, 256, 264, block=64)
-    check_all(r[3], r[4], r[5], r[8])
+    check_all(r[3], r[4], r[5], r[8], r[0])
 
 
 @pytest.mark.parametrize("T,d_out", [(600, 1032), (700, 1160), (2100, 1536)])
 def test_ragged_outputs_large_tiles(T, d_out):
     # T > 512 and d_out > 512 take the 256x256 / 128x192 configurations
     r = run_case(T, 512, d_out, block=512)
-    check_all(r[3], r[4], r[5], r[8])
+    check_all(r[3], r[4], r[5], r[8], r[0])
 
 
 def test_zero_and_degenerate_rows():
@@ -81,10 +81,10 @@ def test_zero_and_degenerate_rows():
     x[3, 0] = 2.5                                # only channel 0: centred X~ is exactly 0
     r = run_case(6, d, 64, block=d, alpha=None, x=x)
     desc, prep, X, Y, codes, s_x, mu, U, ora = r
-    c = to_np(codes)
+    c = codes_np(desc, codes, 6)
     assert not c[1].any() and not c[3].any()
     assert to_np(s_x)[1] == 0.0 and to_np(s_x)[3] == 0.0
-    check_all(Y, codes, s_x, ora)
+    check_all(Y, codes, s_x, ora, desc)
     # Y of the degenerate row is b + mu c (the whole output comes from the bias correction)
     np.testing.assert_allclose(to_np(Y)[3], ora["y_full"][3], rtol=1e-5, atol=1e-6)
 
@@ -92,28 +92,28 @@ def test_zero_and_degenerate_rows():
 @pytest.mark.parametrize("block", [1, 2, 8, 32, 1024])
 def test_block_sizes(block):
     r = run_case(200, 1024, 256, block=block)
-    check_all(r[3], r[4], r[5], r[8])
+    check_all(r[3], r[4], r[5], r[8], r[0])
 
 
 @pytest.mark.parametrize("xd,wd,yd", [("f32", "bf16", "bf16"), ("bf16", "f32", "f32"),
                                       ("bf16", "bf16", "f32")])
 def test_mixed_dtypes(xd, wd, yd):
     r = run_case(300, 384, 512, block=128, x_dtype=xd, w_dtype=wd, y_dtype=yd)
-    check_all(r[3], r[4], r[5], r[8])
+    check_all(r[3], r[4], r[5], r[8], r[0])
 
 
 @pytest.mark.parametrize("ab,wb", [(8, 4), (4, 8), (8, 8)])
 def test_code_widths(ab, wb):
     r = run_case(300, 256, 256, block=256, a_bits=ab, w_bits=wb)
-    check_all(r[3], r[4], r[5], r[8])
-    assert np.abs(to_np(r[4])).max() <= 2 ** (ab - 1) - 1
+    check_all(r[3], r[4], r[5], r[8], r[0])
+    assert np.abs(codes_np(r[0], r[4], 300)).max() <= 2 ** (ab - 1) - 1
 
 
 @pytest.mark.parametrize("rank,xd", [(16, "f32"), (48, "bf16"), (64, "f32")])
 def test_low_rank(rank, xd):
     r = run_case(260, 512, 384, block=256, rank=rank, x_dtype=xd, w_dtype=xd, y_dtype=xd)
     desc, prep, X, Y, codes, s_x, mu, U, ora = r
-    check_all(Y, codes, s_x, ora)
+    check_all(Y, codes, s_x, ora, desc)
     err = np.linalg.norm(to_np(U) - ora["u"], axis=1) / np.linalg.norm(ora["u"], axis=1)
     assert err.max() <= 1e-4, err.max()
 
@@ -121,7 +121,7 @@ def test_low_rank(rank, xd):
 def test_heavy_outliers_and_no_centring():
     r = run_case(400, 2048, 512, block=2048, center=False, alpha=None, n_outliers=16,
                  outlier=1000.0)
-    check_all(r[3], r[4], r[5], r[8])
+    check_all(r[3], r[4], r[5], r[8], r[0])
     assert not to_np(r[6]).any()        # mu is zero without centring
 
 
@@ -139,8 +139,8 @@ def test_deterministic_across_launch_configs():
     assert torch.equal(Yb, hq.quant_linear(desc, prep, Xb))
     v = hq.prepared_views(desc, prep)
     codes = hq.act_quantize(desc, prep, Xb)[0]
-    a1 = hq.gemm_i32(desc, codes, v["w_codes"].contiguous())
-    a2 = hq.gemm_i32(desc, codes[:300].contiguous(), v["w_codes"].contiguous())
+    a1 = hq.gemm_i32(desc, codes, v["w_codes"], 2048, 768)
+    a2 = hq.gemm_i32(desc, codes[:hq.code_bytes(desc, 300)].clone(), v["w_codes"], 300, 768)
     assert torch.equal(a1[:300], a2)
 
 

@@ -13,7 +13,7 @@ import torch
 import hadamard_rotated_bit_amd as hq
 from hadamard_rotated_bit_amd import workloads as WL
 from oracle import hq_oracle as O
-from parity import Y_TOL, check_codes, desc_for, rel_fro, tdev, to_np
+from parity import Y_TOL, check_codes, codes_dev, codes_np, desc_for, rel_fro, tdev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def test_full_size_sampled(name):
     torch.cuda.synchronize()
     rows = sample_rows(w.T)
     idx = torch.from_numpy(rows).cuda()
-    y_s, c_s = to_np(Y[idx]), to_np(codes[idx])
+    y_s, c_s = to_np(Y[idx]), codes_np(desc, codes, w.T, rows)
     sx_s, mu_s = to_np(s_x[idx]), to_np(mu[idx])
     del Y, codes, X
 
@@ -71,7 +71,7 @@ def test_full_size_gemm_bit_exact(name):
     rng = np.random.default_rng(1234 + w.key)
     a = rng.integers(-qmax, qmax + 1, (w.T, w.d_in), dtype=np.int8)
     b = rng.integers(-qmax, qmax + 1, (w.d_out, w.d_in), dtype=np.int8)
-    acc = hq.gemm_i32(desc, torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda())
+    acc = hq.gemm_i32(desc, codes_dev(desc, a), codes_dev(desc, b), w.T, w.d_out)
     rows = sample_rows(w.T)
     got = to_np(acc[torch.from_numpy(rows).cuda()]).astype(np.int64)
     np.testing.assert_array_equal(got, O.int_gemm(a[rows], b))

@@ -11,8 +11,8 @@ import torch
 import hadamard_rotated_bit_amd as hq
 from hadamard_rotated_bit_amd import workloads as WL
 from oracle import hq_oracle as O
-from parity import (MAX_FLIP_FRAC, XT_TOL, Y_TOL, check_codes, rel_fro, small_case, tdev,
-                    to_np)
+from parity import (MAX_FLIP_FRAC, XT_TOL, Y_TOL, check_codes, codes_dev, codes_np, rel_fro,
+                    small_case, tdev, to_np)
 
 pytestmark = pytest.mark.gpu
 NAMES = WL.ORDER
@@ -36,8 +36,9 @@ def test_weight_prepare(name):
     qmax = 2 ** (c.w.w_bits - 1) - 1
     ratio = np.divide(o["wt"], o["s_w"][:, None], out=np.zeros_like(o["wt"]),
                       where=o["s_w"][:, None] > 0)
-    check_codes(to_np(v["w_codes"]), o["qw"], ratio, "weight codes")
-    assert np.abs(to_np(v["w_codes"])).max() <= qmax
+    wc = codes_np(c.desc, v["w_codes"], c.desc.d_out)
+    check_codes(wc, o["qw"], ratio, "weight codes")
+    assert np.abs(wc).max() <= qmax
     np.testing.assert_allclose(to_np(v["s_w"]), o["s_w"], rtol=1e-5)
     cerr = np.abs(to_np(v["c"]) - o["c"]) / np.abs(o["wt"]).sum(axis=1)
     assert cerr.max() <= 1e-5, cerr.max()
@@ -69,8 +70,8 @@ def test_activation_codes(name):
     o = c.ora
     ratio = np.divide(o["xt"], o["s_x"][:, None], out=np.zeros_like(o["xt"]),
                       where=o["s_x"][:, None] > 0)
-    flips = check_codes(to_np(codes), o["qa"], ratio, "activation codes")
-    print(f"{name}: {flips} activation code flips of {codes.numel()}")
+    flips = check_codes(codes_np(c.desc, codes, c.T), o["qa"], ratio, "activation codes")
+    print(f"{name}: {flips} activation code flips of {o['qa'].size}")
     np.testing.assert_allclose(to_np(s_x), o["s_x"], rtol=1e-5)
     rms = np.sqrt(np.mean(o["y"] ** 2, axis=1))
     assert np.all(np.abs(to_np(mu) - o["mu"]) <= XT_TOL * rms)
@@ -84,9 +85,9 @@ def test_activation_codes(name):
 def test_gemm_bit_exact(name):
     c = small_case(name)
     o = c.ora
-    a = torch.from_numpy(o["qa"].astype(np.int8)).cuda()
-    w = torch.from_numpy(o["qw"].astype(np.int8)).cuda()
-    acc = hq.gemm_i32(c.desc, a, w)
+    a = codes_dev(c.desc, o["qa"])
+    w = codes_dev(c.desc, o["qw"])
+    acc = hq.gemm_i32(c.desc, a, w, c.T, c.desc.d_out)
     np.testing.assert_array_equal(to_np(acc).astype(np.int64), o["acc"])
 
 
@@ -111,13 +112,13 @@ def test_output_with_oracle_codes_is_tight(name):
     # + dequant epilogue reproduces the oracle's output up to float32 epilogue rounding.
     c = small_case(name)
     o = c.ora
-    codes = torch.from_numpy(o["qa"].astype(np.int8)).cuda()
+    codes = codes_dev(c.desc, o["qa"])
     s_x = torch.from_numpy(o["s_x"].astype(np.float32)).cuda()
     mu = torch.from_numpy(o["mu"].astype(np.float32)).cuda()
     U = None if o["u"] is None else torch.from_numpy(o["u"].astype(np.float32)).cuda()
     # substitute the oracle's weight codes too, so only the epilogue differs
     v = hq.prepared_views(c.desc, c.prep)
-    if not np.array_equal(to_np(v["w_codes"]), o["qw"]):
+    if not np.array_equal(codes_np(c.desc, v["w_codes"], c.desc.d_out), o["qw"]):
         pytest.skip("weight codes differ at a tie; the end-to-end test covers this case")
     Y = hq.gemm_dequant(c.desc, c.prep, codes, s_x, mu, U)
     y_ref = o["y_full"]
