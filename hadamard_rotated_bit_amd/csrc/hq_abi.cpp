@@ -86,6 +86,8 @@ int check_desc(const hq_desc* d) {
   return HQ_OK;
 }
 
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
 // Both operands use E2M3 (FP6 MFMA) when both code widths are 4 bits, else
 // int8 bytes (int8 MFMA).
 int code_fmt_of(const hq_desc* d) {
@@ -407,6 +409,8 @@ int hq_quant_linear(const hq_desc* desc, const void* prepared, const void* X, in
   if (T == 0) return HQ_OK;
   if (!prepared || !X || !Y || !workspace)
     return fail(HQ_ERR_INVALID_ARG, "prepared, X, Y and workspace must be non-NULL");
+  if (misaligned(X) || misaligned(Y) || misaligned(workspace) || misaligned(prepared))
+    return fail(HQ_ERR_INVALID_ARG, "X, Y, workspace and prepared must be 16-byte aligned");
   const Workspace w = workspace_of(desc, T);
   if (workspace_bytes < w.total)
     return fail(HQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, w.total);
@@ -481,6 +485,8 @@ int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes
   if (T == 0) return HQ_OK;
   if (!prepared || !codes || !s_x || !mu || !Y || (desc->rank && !U))
     return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (misaligned(Y) || misaligned(codes) || misaligned(prepared))
+    return fail(HQ_ERR_INVALID_ARG, "Y, codes and prepared must be 16-byte aligned");
   return run_gemm_dequant(desc, prepared, codes, s_x, mu, U, T, Y,
                           static_cast<hipStream_t>(stream));
 }

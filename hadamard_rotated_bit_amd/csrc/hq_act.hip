@@ -230,6 +230,8 @@ hipError_t launch_row_transform(const RowArgs& a, hipStream_t s) {
   RowGeom g;
   if (!row_geometry(a.d, &g)) return hipErrorInvalidValue;
   if (a.rows <= 0) return hipSuccess;
+  const hipError_t fe = launch_row_fast(a, g, s);
+  if (fe != hipErrorNotSupported) return fe;
   if (a.in_bf16) {
     if (g.G == 16) return launch_row_g<uint16_t, 16>(a, g.C, s);
     if (g.G == 32) return launch_row_g<uint16_t, 32>(a, g.C, s);

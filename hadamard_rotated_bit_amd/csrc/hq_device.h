@@ -20,6 +20,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two floats -> packed bf16 pair (low half = a), one v_cvt_pk_bf16_f32.
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+
 // Load 8 consecutive elements as float.
 __device__ __forceinline__ void load8(const float* __restrict__ p, float v[8]) {
   const float4 a = reinterpret_cast<const float4*>(p)[0];

@@ -148,6 +148,99 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[TM][TN], uint8_t* smem
   }
 }
 
+// Dequant epilogue with bf16 output staged through LDS (same values as
+// gemm_epilogue), with the block's parameters already in LDS at P (laid out
+// as in gemm_epilogue, outside the first BM (2 BN + 8) bytes): each lane writes its 4-channel runs (8 bytes) into a
+// block-sized bf16 tile in LDS with a row pitch of 2 BN + 8 bytes (the 32
+// rows written by one ds_write_b64 phase then fall on 32 distinct bank
+// pairs), and the block copies the tile out row by row in 16-byte pieces, so
+// every global store instruction writes whole contiguous row segments.
+// Loops run channel quadruple outermost, so the per-channel parameters are
+// read from LDS once per quadruple and reused for the lane's TM tokens; LR
+// selects the low-rank term at compile time. The main loop's LDS must be
+// idle.
+template <int BM, int BN, int TM, int TN, int NW, bool LR, typename AccT>
+__device__ __forceinline__ void gemm_epilogue_bf16_staged(AccT (&acc)[TM][TN], uint8_t* smem,
+                                                          const float* P, int tid, int lane,
+                                                          int64_t m0, int64_t n0, int wm0, int wn0,
+                                                          int64_t M, int64_t N, const GemmEpi& ep) {
+  constexpr int PITCH = 2 * BN + 8;
+  static_assert((((PITCH / 4) % 64) & 3) == 2, "pitch = 2 x odd dwords mod 64 banks");
+  uint8_t* tile = smem;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  float sx[TM], mu[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    sx[i] = P[3 * BN + wm0 + i * 32 + lrow];
+    mu[i] = P[3 * BN + BM + wm0 + i * 32 + lrow];
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    v16f lr[LR ? TM : 1];
+    if constexpr (LR) {
+      const int64_t nb = n0 + wn0 + j * 32;
+      const int64_t nr = nb + lrow < N ? nb + lrow : N - 1;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int64_t m = m0 + wm0 + i * 32 + lrow;
+        const int64_t mc = m < M ? m : M - 1;
+        lr[i] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        for (int k0 = 0; k0 < ep.rank; k0 += 16) {
+          float f[8];
+          load8(ep.U + mc * ep.rank + k0 + 8 * lhalf, f);
+          const v8bf uh = pack_bf16x8(f, false), ul = pack_bf16x8(f, true);
+          const int64_t off = nr * ep.rank + k0 + 8 * lhalf;
+          const v8bf wh = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
+          const v8bf wl = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
+          lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, uh, lr[i], 0, 0, 0);
+          lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, uh, lr[i], 0, 0, 0);
+          lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, ul, lr[i], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int nl = wn0 + j * 32 + 8 * g + 4 * lhalf;
+      const float4 sw = *reinterpret_cast<const float4*>(P + nl);
+      const float4 cb = *reinterpret_cast<const float4*>(P + BN + nl);
+      const float4 bb = *reinterpret_cast<const float4*>(P + 2 * BN + nl);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const AccT& a = acc[i][j];
+        float y0 = fmaf(float(a[4 * g + 0]), sx[i] * sw.x, fmaf(mu[i], cb.x, bb.x));
+        float y1 = fmaf(float(a[4 * g + 1]), sx[i] * sw.y, fmaf(mu[i], cb.y, bb.y));
+        float y2 = fmaf(float(a[4 * g + 2]), sx[i] * sw.z, fmaf(mu[i], cb.z, bb.z));
+        float y3 = fmaf(float(a[4 * g + 3]), sx[i] * sw.w, fmaf(mu[i], cb.w, bb.w));
+        if constexpr (LR) {
+          y0 += lr[i][4 * g + 0];
+          y1 += lr[i][4 * g + 1];
+          y2 += lr[i][4 * g + 2];
+          y3 += lr[i][4 * g + 3];
+        }
+        const int ml = wm0 + i * 32 + lrow;
+        *reinterpret_cast<uint2*>(tile + ml * PITCH + nl * 2) =
+            make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = BN / 8;  // 16-byte pieces per tile row
+  uint16_t* Y = static_cast<uint16_t*>(ep.Y);
+#pragma unroll 8
+  for (int q = tid; q < BM * CPR; q += NW * 64) {
+    const int row = q / CPR, ch = q - row * CPR;
+    const int64_t m = m0 + row, n = n0 + ch * 8;
+    if (m < M && n < N) {
+      const uint8_t* src = tile + row * PITCH + ch * 16;
+      const uint2 lo = *reinterpret_cast<const uint2*>(src);
+      const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+      *reinterpret_cast<uint4*>(Y + m * ep.ldy + n) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  }
+}
+
 // Main loop
 // ---------
 // Stage loads go straight from global memory to LDS (gfx950

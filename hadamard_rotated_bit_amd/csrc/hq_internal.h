@@ -48,6 +48,9 @@ struct RowArgs {
   int mode;
 };
 hipError_t launch_row_transform(const RowArgs& a, hipStream_t s);
+// The fast kernel for blocks of at least 8 G channels; hipErrorNotSupported
+// when the geometry has no instance (the general kernel then runs).
+hipError_t launch_row_fast(const RowArgs& a, const RowGeom& g, hipStream_t s);
 
 // absmax[i] = max over rows of |in[r, i]| ; absmax zeroed by the launcher.
 hipError_t launch_col_absmax(const void* in, int in_bf16, int64_t rows, int d, float* absmax,

@@ -1,0 +1,298 @@
+// Fast row transform of libhq for the common geometry: the Hadamard block
+// covers at least the 8 G channels spread over a row's lanes, so every
+// butterfly stage on the register and lane bits is taken, and the NX stages
+// on chunk-index bits are a compile-time count. (Smaller blocks use the
+// general kernel in hq_act.hip.)
+//
+// Same arithmetic per row as the general kernel (HadaNorm Eq. (1) activation
+// side, HaTQ Sec. III-A Eq. (3) quantiser), with three differences in how the
+// lanes carry it out:
+//  * Cross-lane butterflies at lane distance 1, 2 and 8 are one
+//    v_fmac_f32_dpp each (v += g * v[lane ^ M], g = +1 on the lower and -1
+//    on the upper lane of a pair); distance 4 and 16 use ds_swizzle plus one
+//    fma. The upper lane then holds the negated difference, so after all
+//    stages lane t stores sigma_t times the transformed value, with
+//    sigma_t = (-1)^popcount(t & NEG) a per-lane sign (NEG = the lane bits
+//    done this way). Sums are taken as sigma_t * (lane sum), the mean is
+//    subtracted as sigma_t * mu, and the quantiser uses sigma_t * (qmax /
+//    absmax): every code, scale and mean is the same as with unsigned
+//    storage, bit for bit.
+//  * E2M3 codes come from v_cvt_scalef32_2xpk16_fp6_f32 on the integer codes
+//    rint(x * qmax / absmax) (formed as fma(x, r, 1.5 2^23) - 1.5 2^23, one
+//    rounding of the exact product), 32 codes per instruction; the
+//    instruction interleaves its two 16-value halves (field 2i holds x[i],
+//    field 2i+1 holds y[i]), so four chunks of 8 channels are fed in that
+//    order and come out as four 48-bit pieces.
+//  * No runtime stage tests, so the butterflies run in place.
+#include "hq_device.h"
+#include "hq_internal.h"
+
+namespace hq {
+
+typedef unsigned v6u __attribute__((ext_vector_type(6)));
+
+// v[i] += v[lane ^ M][i] * g for the 8 registers of a chunk, one DPP fma
+// each. The leading s_nop covers the DPP read-after-VALU-write hazard for
+// the first instruction; the others read registers written before the block.
+#define HQ_DPP_FMAC8(CTRL)                                                         \
+  asm("s_nop 1\n\t"                                                                \
+      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"          \
+      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"          \
+      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"          \
+      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"          \
+      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"          \
+      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"          \
+      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"          \
+      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"              \
+      : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),   \
+        "+v"(v[6]), "+v"(v[7])                                                     \
+      : "v"(g))
+
+// One cross-lane butterfly stage at lane distance M on a chunk of 8 values.
+// M = 1, 2, 4, 8, 16: negating form v + g v[lane ^ M]; M = 32: true form
+// lo + g hi from the permlane32 swap.
+template <int M>
+__device__ __forceinline__ void xstage8(float* v, float g) {
+  if constexpr (M == 1) {
+    HQ_DPP_FMAC8("quad_perm:[1,0,3,2]");
+  } else if constexpr (M == 2) {
+    HQ_DPP_FMAC8("quad_perm:[2,3,0,1]");
+  } else if constexpr (M == 8) {
+    HQ_DPP_FMAC8("row_ror:8");
+  } else if constexpr (M == 4 || M == 16) {
+    // ds_swizzle bitmask mode on 32-lane groups: lane reads lane ^ M.
+    constexpr int pat = 0x1F | (M << 10);
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      p[j] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[j]), pat));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = fmaf(p[j], g, v[j]);
+  } else {
+    static_assert(M == 32, "lane distance");
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float lo, hi;
+      lane_pair<32>(v[j], &lo, &hi);
+      v[j] = fmaf(g, hi, lo);
+    }
+  }
+}
+#undef HQ_DPP_FMAC8
+
+// One 48-bit piece (w0 = bits 0..31, w1 = bits 32..47) at p; p is 4-byte
+// aligned (odd = false) or 2 bytes past (odd = true).
+__device__ __forceinline__ void store_piece48(uint8_t* p, uint32_t w0, uint32_t w1, bool odd) {
+  *reinterpret_cast<uint32_t*>(p + (odd ? 2 : 0)) = odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0;
+  *reinterpret_cast<uint16_t*>(p + (odd ? 0 : 4)) = uint16_t(odd ? w0 : w1);
+}
+
+template <typename TIn, int G, int C, int NX>
+__global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt_b) {
+  constexpr int LOG2G = (G == 16) ? 4 : (G == 32) ? 5 : 6;
+  constexpr int E = 8 * C;
+  constexpr int RPW = 64 / G;
+  constexpr int NEG = (G >= 32) ? 31 : 15;  // lane bits done in negating form
+  static_assert((C >> NX) << NX == C, "chunk stages pair whole chunks");
+  const int lane = threadIdx.x & 63;
+  const int t = lane & (G - 1);
+  const int64_t row = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW + lane / G;
+  const bool valid = row < a.rows;
+  const int64_t r = valid ? row : a.rows - 1;
+  const int d = a.d;
+  const TIn* src = static_cast<const TIn*>(a.in) + r * d + t * 8;
+
+  float v[E];
+#pragma unroll
+  for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
+
+  const float g1 = (t & 1) ? -1.0f : 1.0f, g2 = (t & 2) ? -1.0f : 1.0f;
+  const float g4 = (t & 4) ? -1.0f : 1.0f, g8 = (t & 8) ? -1.0f : 1.0f;
+  const float g16 = (t & 16) ? -1.0f : 1.0f, g32 = (t & 32) ? -1.0f : 1.0f;
+  const float sgn = (__builtin_popcount(t & NEG) & 1) ? -1.0f : 1.0f;
+
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    float* vc = &v[c * 8];
+    if (a.scale) {
+      float s[8];
+      load8(a.scale + c * 8 * G + t * 8, s);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vc[j] *= s[j];
+    }
+    // channel bits 0..2, in registers
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (!(e & h)) {
+          const float x = vc[e], y = vc[e + h];
+          vc[e] = x + y;
+          vc[e + h] = x - y;
+        }
+      }
+    }
+    // channel bits 3 .. 3 + log2 G - 1, across lanes
+    xstage8<1>(vc, g1);
+    xstage8<2>(vc, g2);
+    xstage8<4>(vc, g4);
+    xstage8<8>(vc, g8);
+    if constexpr (G >= 32) xstage8<16>(vc, g16);
+    if constexpr (G >= 64) xstage8<32>(vc, g32);
+  }
+  // channel bits above: chunk index bits 0 .. NX-1, in registers
+#pragma unroll
+  for (int b = 0; b < NX; ++b) {
+    const int h = 1 << b;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      if (!(c & h)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = v[c * 8 + j], y = v[(c + h) * 8 + j];
+          v[c * 8 + j] = x + y;
+          v[(c + h) * 8 + j] = x - y;
+        }
+      }
+    }
+  }
+
+  float sum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) sum += v[e];
+  sum = group_sum<G>(sgn * sum);
+
+  const bool weight = a.mode == ROW_WEIGHT;
+  const float mu = (!weight && a.center) ? sum / float(d) : 0.0f;
+  const float smu = sgn * mu;
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    v[e] -= smu;
+    amax = fmaxf(amax, fabsf(v[e]));
+  }
+  if (a.mode == ROW_EXPORT) {
+    if (valid) {
+      const float sc = sgn * inv_sqrt_b;
+      float* o = a.out_xt + row * d + t * 8;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const float* vc = &v[c * 8];
+        reinterpret_cast<float4*>(o + c * 8 * G)[0] =
+            make_float4(vc[0] * sc, vc[1] * sc, vc[2] * sc, vc[3] * sc);
+        reinterpret_cast<float4*>(o + c * 8 * G)[1] =
+            make_float4(vc[4] * sc, vc[5] * sc, vc[6] * sc, vc[7] * sc);
+      }
+      if (t == 0) a.out_aux[row] = mu * inv_sqrt_b;
+    }
+    return;
+  }
+  amax = group_max<G>(amax);
+  const float rs = sgn * (amax > 0.0f ? a.qmax / amax : 0.0f);
+  if (!valid) return;
+  if (a.code_fmt == CODES_E2M3) {
+    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+    const bool odd = t & 1;
+    uint8_t* rb = a.codes + (row >> 2) * 3 * int64_t(d) + (row & 3) * 96;
+#pragma unroll
+    for (int c0 = 0; c0 < C; c0 += 4) {
+      v16f x, y;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float q = (c0 + m < C) ? fmaf(v[(c0 + m) * 8 + j], rs, MAGIC) - MAGIC : 0.0f;
+          if (j & 1) y[4 * m + j / 2] = q; else x[4 * m + j / 2] = q;
+        }
+      const v6u p = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(x, y, 1.0f);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (c0 + m >= C) break;
+        const int e0 = (c0 + m) * 8 * G + t * 8;
+        uint8_t* dst = rb + (e0 >> 7) * 384 + 6 * ((e0 & 127) >> 3);
+        uint32_t w0, w1;
+        if (m == 0) { w0 = p[0]; w1 = p[1] & 0xFFFFu; }
+        else if (m == 1) { w0 = __builtin_amdgcn_alignbit(p[2], p[1], 16); w1 = p[2] >> 16; }
+        else if (m == 2) { w0 = p[3]; w1 = p[4] & 0xFFFFu; }
+        else { w0 = __builtin_amdgcn_alignbit(p[5], p[4], 16); w1 = p[5] >> 16; }
+        store_piece48(dst, w0, w1, odd);
+      }
+    }
+  } else {
+    const int64_t base = row * d + t * 8;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const float* vc = &v[c * 8];
+      *reinterpret_cast<uint2*>(a.codes + base + c * 8 * G) =
+          make_uint2(pack_codes4(vc[0], vc[1], vc[2], vc[3], rs),
+                     pack_codes4(vc[4], vc[5], vc[6], vc[7], rs));
+    }
+  }
+  if (t == 0) {
+    a.out_s[row] = amax * inv_sqrt_b / a.qmax;
+    a.out_aux[row] = (weight ? sum : mu) * inv_sqrt_b;
+  }
+}
+
+// Instantiated geometries: the (G, C) pairs row_geometry picks for the
+// supported widths, each with every chunk-stage count its block sizes need.
+template <typename TIn, int G, int C>
+static hipError_t launch_fast_gc(const RowArgs& a, int nx, dim3 grid, float isb, hipStream_t s) {
+  switch (nx) {
+#define HQ_NX(N)                                                                          \
+  case N:                                                                                 \
+    if constexpr (((C >> N) << N) == C) {                                                 \
+      hipLaunchKernelGGL((row_fast_kernel<TIn, G, C, N>), grid, dim3(256), 0, s, a, isb); \
+      return hipGetLastError();                                                           \
+    }                                                                                     \
+    break;
+    HQ_NX(0) HQ_NX(1) HQ_NX(2) HQ_NX(3) HQ_NX(4)
+#undef HQ_NX
+    default:
+      break;
+  }
+  return hipErrorNotSupported;
+}
+
+// (G, C) pairs that row_geometry can return for a supported d_in.
+template <int G, int C>
+constexpr bool reachable() {
+  if (G == 16) return C <= 8 || (C % 2 == 1);
+  if (G == 32) return (C >= 5 && C <= 8) || (C >= 9 && C % 2 == 1);
+  return C >= 5;
+}
+
+template <typename TIn, int G>
+static hipError_t launch_fast_g(const RowArgs& a, int C, int nx, hipStream_t s) {
+  const int rpw = 64 / G;
+  const int64_t blocks = (a.rows + 4 * rpw - 1) / (4 * rpw);
+  const float isb = 1.0f / sqrtf(float(1 << a.log2b));
+  const dim3 grid{unsigned(blocks)};
+  switch (C) {
+#define HQ_C(CC)                                                  \
+  case CC:                                                        \
+    if constexpr (reachable<G, CC>()) return launch_fast_gc<TIn, G, CC>(a, nx, grid, isb, s); \
+    return hipErrorNotSupported;
+    HQ_C(1) HQ_C(2) HQ_C(3) HQ_C(4) HQ_C(5) HQ_C(6) HQ_C(7) HQ_C(8)
+    HQ_C(9) HQ_C(10) HQ_C(11) HQ_C(12) HQ_C(13) HQ_C(14) HQ_C(15) HQ_C(16)
+#undef HQ_C
+    default:
+      return hipErrorNotSupported;
+  }
+}
+
+hipError_t launch_row_fast(const RowArgs& a, const RowGeom& g, hipStream_t s) {
+  const int log2g = g.G == 16 ? 4 : g.G == 32 ? 5 : 6;
+  const int nx = a.log2b - 3 - log2g;
+  if (nx < 0 || (1 << nx) > g.C) return hipErrorNotSupported;
+  if (a.in_bf16) {
+    if (g.G == 16) return launch_fast_g<uint16_t, 16>(a, g.C, nx, s);
+    if (g.G == 32) return launch_fast_g<uint16_t, 32>(a, g.C, nx, s);
+    return launch_fast_g<uint16_t, 64>(a, g.C, nx, s);
+  }
+  if (g.G == 16) return launch_fast_g<float, 16>(a, g.C, nx, s);
+  if (g.G == 32) return launch_fast_g<float, 32>(a, g.C, nx, s);
+  return launch_fast_g<float, 64>(a, g.C, nx, s);
+}
+
+}  // namespace hq

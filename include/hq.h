@@ -30,6 +30,8 @@
  *    except where stated.
  *  - The caller allocates and owns every buffer. The library allocates no
  *    device memory and keeps no state besides a thread-local error string.
+ *  - X, Y, prepared, workspace and code buffers must be 16-byte aligned
+ *    (checked; any allocator's base pointer is).
  *  - All arguments are validated on the host before anything is enqueued; on
  *    error nothing is launched, outputs are untouched, a negative hq_status
  *    is returned and hq_last_error() describes the problem. No C++
