@@ -105,9 +105,9 @@ __device__ __forceinline__ void lds_dma4_buf(__amdgpu_buffer_rsrc_t r, uint32_t 
 __host__ __device__ constexpr int64_t f6_row_bytes(int64_t K) { return K / 4 * 3; }
 
 // Origin of tile `tile` of an M x N output in BM x BN tiles: tiles are
-// renumbered so that the blocks of one XCD (block b runs on XCD b mod 8, and
-// a persistent block keeps its residue) own a contiguous range, walked in
-// column-major order inside bands of GM tile rows.
+// renumbered so that the blocks of one XCD (block b runs on XCD b mod 8) own
+// a contiguous range, walked in column-major order inside bands of GM tile
+// rows.
 template <int BM, int BN, int GM>
 __device__ __forceinline__ void f6_tile_origin(int tile, int64_t M, int64_t N, int64_t* m0,
                                                int64_t* n0) {
@@ -118,100 +118,6 @@ __device__ __forceinline__ void f6_tile_origin(int tile, int64_t M, int64_t N, i
   const int rows_in = (tmt - g * GM) < GM ? (tmt - g * GM) : GM;
   *m0 = int64_t(g * GM + r % rows_in) * BM;
   *n0 = int64_t(r / rows_in) * BN;
-}
-
-// Epilogue without staging: the lane's outputs go straight to memory (4
-// consecutive channels per store), parameters come from the block's LDS copy
-// P = [s_w | c | b] (BN each) then [s_x | mu] (BM each). Loops run channel
-// quadruple outermost so the per-channel parameters are read once per
-// quadruple; LR selects the low-rank term at compile time.
-template <int BM, int BN, int TM, int TN, bool DEQ, bool LR, typename AccT>
-__device__ __forceinline__ void gemm_epilogue_direct(AccT (&acc)[TM][TN], const float* P, int lane,
-                                                     int64_t m0, int64_t n0, int wm0, int wn0,
-                                                     int64_t M, int64_t N,
-                                                     int32_t* __restrict__ Cout, int64_t ldc,
-                                                     const GemmEpi& ep) {
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  if constexpr (!DEQ) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t m = m0 + wm0 + i * 32 + lrow;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + wn0 + j * 32 + 8 * g + 4 * lhalf;
-          if (m < M && n < N) {
-            const AccT& a = acc[i][j];
-            *reinterpret_cast<int4*>(Cout + m * ldc + n) =
-                make_int4(int(a[4 * g]), int(a[4 * g + 1]), int(a[4 * g + 2]), int(a[4 * g + 3]));
-          }
-        }
-    }
-  } else {
-    float sx[TM], mu[TM];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      sx[i] = P[3 * BN + wm0 + i * 32 + lrow];
-      mu[i] = P[3 * BN + BM + wm0 + i * 32 + lrow];
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      v16f lr[LR ? TM : 1];
-      if constexpr (LR) {
-        const int64_t nb = n0 + wn0 + j * 32;
-        const int64_t nr = nb + lrow < N ? nb + lrow : N - 1;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int64_t m = m0 + wm0 + i * 32 + lrow;
-          const int64_t mc = m < M ? m : M - 1;
-          lr[i] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-          for (int k0 = 0; k0 < ep.rank; k0 += 16) {
-            float f[8];
-            load8(ep.U + mc * ep.rank + k0 + 8 * lhalf, f);
-            const v8bf uh = pack_bf16x8(f, false), ul = pack_bf16x8(f, true);
-            const int64_t off = nr * ep.rank + k0 + 8 * lhalf;
-            const v8bf wh = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
-            const v8bf wl = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
-            lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, uh, lr[i], 0, 0, 0);
-            lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, uh, lr[i], 0, 0, 0);
-            lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, ul, lr[i], 0, 0, 0);
-          }
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = wn0 + j * 32 + 8 * g + 4 * lhalf;
-        const int64_t n = n0 + nl;
-        const float4 sw = *reinterpret_cast<const float4*>(P + nl);
-        const float4 cb = *reinterpret_cast<const float4*>(P + BN + nl);
-        const float4 bb = *reinterpret_cast<const float4*>(P + 2 * BN + nl);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const AccT& a = acc[i][j];
-          float y0 = fmaf(float(a[4 * g + 0]), sx[i] * sw.x, fmaf(mu[i], cb.x, bb.x));
-          float y1 = fmaf(float(a[4 * g + 1]), sx[i] * sw.y, fmaf(mu[i], cb.y, bb.y));
-          float y2 = fmaf(float(a[4 * g + 2]), sx[i] * sw.z, fmaf(mu[i], cb.z, bb.z));
-          float y3 = fmaf(float(a[4 * g + 3]), sx[i] * sw.w, fmaf(mu[i], cb.w, bb.w));
-          if constexpr (LR) {
-            y0 += lr[i][4 * g + 0];
-            y1 += lr[i][4 * g + 1];
-            y2 += lr[i][4 * g + 2];
-            y3 += lr[i][4 * g + 3];
-          }
-          const int64_t m = m0 + wm0 + i * 32 + lrow;
-          if (m < M && n < N) {
-            if (ep.y_bf16)
-              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ep.Y) + m * ep.ldy + n) =
-                  make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
-            else
-              *reinterpret_cast<float4*>(static_cast<float*>(ep.Y) + m * ep.ldy + n) =
-                  make_float4(y0, y1, y2, y3);
-          }
-        }
-      }
-    }
-  }
 }
 
 // DMA copy of a tile's epilogue parameters into LDS P = [s_w | c | b] (BN
@@ -276,16 +182,7 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int64_t m0, n0;
-  {
-    const int tmt = int((M + BM - 1) / BM), tnt = int((N + BN - 1) / BN);
-    const int ntiles = tmt * tnt;
-    int tile = blockIdx.x;
-    if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
-    const int g = tile / (GM * tnt), r = tile - g * (GM * tnt);
-    const int rows_in = (tmt - g * GM) < GM ? (tmt - g * GM) : GM;
-    m0 = int64_t(g * GM + r % rows_in) * BM;
-    n0 = int64_t(r / rows_in) * BN;
-  }
+  f6_tile_origin<BM, BN, GM>(int(blockIdx.x), M, N, &m0, &n0);
   const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
   const int KT = K / 128;
   const int64_t lda = f6_row_bytes(K);
@@ -414,198 +311,6 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_kernel(
     }
   }
   gemm_epilogue<BM, BN, TM, TN, NW, DEQ>(acc, smem, tid, lane, m0, n0, wm0, wn0, M, N, Cout, ldc, ep);
-}
-
-}  // namespace hq
-
-namespace hq {
-
-// Persistent form of gemm_f6_kernel: one block per CU walks the tiles
-// blockIdx.x, blockIdx.x + gridDim.x, ... and the three-buffer stage
-// pipeline runs on across tile boundaries (stage g of the block = stage
-// g mod KT of its tile g / KT): the last three iterations of a tile already
-// load the first three stages of the next one, so the next tile's data
-// arrives while the epilogue runs, and the epilogue's stores drain while the
-// next tile's MFMAs run. The epilogue's per-tile parameters are copied to LDS
-// by DMA at the start of the tile. Every wave runs the same number of tiles
-// and leaves the loop together.
-template <int BM, int BN, int WM, int WN, int GM, bool DEQ, bool LR, int RG>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
-    const uint8_t* __restrict__ A, int64_t M, const uint8_t* __restrict__ B, int64_t N, int K,
-    int32_t* __restrict__ Cout, int64_t ldc, GemmEpi ep) {
-  constexpr int S = 3;
-  constexpr int NW = (BM / WM) * (BN / WN);
-  constexpr int WAVES_N = BN / WN;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int STAGE = 96 * (BM + BN);
-  constexpr int UA = 3 * BM / 32;
-  constexpr int UNITS = 3 * (BM + BN) / 32;
-  constexpr int LPW = (UNITS + NW - 1) / NW;
-  constexpr int QA = UA / NW;
-  constexpr int NP = DEQ ? 3 * BN + 2 * BM : 0;  // epilogue parameters (floats)
-  constexpr int PU = NP / 64;                    // 256-byte DMA units for them
-  constexpr int PPW = (PU + NW - 1) / NW;
-  static_assert(UA % NW == 0, "A units split evenly over the waves");
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "whole DMA units");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + 4 * NP];
-  float* P = reinterpret_cast<float*>(smem + S * STAGE);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
-  const int tmt = int((M + BM - 1) / BM), tnt = int((N + BN - 1) / BN);
-  const int ntiles = tmt * tnt;
-  const int nmine = (ntiles - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
-  const int KT = K / 128;
-  const int64_t lda = f6_row_bytes(K);
-
-  // Tile-relative DMA offsets (as in gemm_f6_kernel).
-  uint32_t voff[LPW];
-  int ldst[LPW];
-#pragma unroll
-  for (int q = 0; q < LPW; ++q) {
-    int u = q * NW + wv;
-    if (u > UNITS - 1) u = UNITS - 1;
-    const bool isA = q < QA;
-    const int ul = isA ? u : u - UA;
-    const int c = 64 * ul + lane;
-    const int row = c / 6, slot = c - 6 * (c / 6);
-    const int h = (slot >= 3 ? 1 : 0) ^ ((row >> 3) & 1);
-    voff[q] = uint32_t((row / RG) * RG * lda + (row % RG) * 96 + 48 * h +
-                       16 * (slot - 3 * (slot >= 3 ? 1 : 0)));
-    ldst[q] = u * 1024;
-  }
-
-  // Issue cursor: the next stage to load (tile it_i, stage kt_i, buffer b_i).
-  int it_i = 0, kt_i = 0, b_i = 0;
-  const uint8_t *ia = A, *ib = B;
-  int na = 0, nb = 0;
-  auto cursor_tile = [&]() {
-    if (it_i < nmine) {
-      int64_t m0, n0;
-      f6_tile_origin<BM, BN, GM>(int(blockIdx.x) + it_i * int(gridDim.x), M, N, &m0, &n0);
-      const int64_t ra = (M - m0) < BM ? (M - m0) : BM, rb = (N - n0) < BN ? (N - n0) : BN;
-      ia = A + m0 * lda;
-      ib = B + n0 * lda;
-      na = int((ra + RG - 1) / RG * RG * lda);
-      nb = int((rb + RG - 1) / RG * RG * lda);
-    } else {
-      na = nb = 0;  // past the last tile: empty loads
-    }
-  };
-  cursor_tile();
-#define HQ6P_ISSUE()                                                                      \
-  do {                                                                                    \
-    uint8_t* base_ = smem + b_i * STAGE;                                                  \
-    const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(ia, na);                                 \
-    const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(ib, nb);                                 \
-    _Pragma("unroll") for (int q = 0; q < LPW; ++q)                                       \
-        lds_dma16_buf(q < QA ? ra_ : rb_, voff[q], uint32_t(kt_i) * (96u * RG), base_ + ldst[q]); \
-    b_i = b_i == S - 1 ? 0 : b_i + 1;                                                     \
-    if (++kt_i == KT) {                                                                   \
-      kt_i = 0;                                                                           \
-      ++it_i;                                                                             \
-      cursor_tile();                                                                      \
-    }                                                                                     \
-  } while (0)
-
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  const int loff = lrow * 96 + 48 * (lhalf ^ ((lrow >> 3) & 1));
-  int b_r = 0;  // buffer of the stage whose MFMAs run next
-#define HQ6P_READ(SET_, BUF_)                                                             \
-  do {                                                                                    \
-    const uint8_t* cur_ = smem + (BUF_) * STAGE + loff;                                   \
-    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                        \
-      _Pragma("unroll") for (int p = 0; p < 3; ++p) af[SET_][i].c[p] =                    \
-          *reinterpret_cast<const v4i*>(cur_ + (wm0 + 32 * i) * 96 + 16 * p);             \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
-      _Pragma("unroll") for (int p = 0; p < 3; ++p) bf[SET_][j].c[p] =                    \
-          *reinterpret_cast<const v4i*>(cur_ + (BM + wn0 + 32 * j) * 96 + 16 * p);        \
-  } while (0)
-#define HQ6P_MFMA(SET_)                                                                   \
-  do {                                                                                    \
-    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                        \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                    \
-        acc[i][j] = mfma_f6(f6_op0(bf[SET_][j]), f6_op0(af[SET_][i]), acc[i][j]);         \
-        acc[i][j] = mfma_f6(f6_op1(bf[SET_][j]), f6_op1(af[SET_][i]), acc[i][j]);         \
-      }                                                                                   \
-  } while (0)
-  // One iteration on the stage in buffer b_r (fragments in set SET_): wait for
-  // the next stage (WAITN_ more may stay in flight) and join the block, refill
-  // b_r, prefetch the next stage's fragments, run the MFMAs.
-#define HQ6P_ITER(SET_, WAITN_, EXTRA_, READ_)                                            \
-  do {                                                                                    \
-    wait_vm_lgkm0<WAITN_>();                                                              \
-    __builtin_amdgcn_s_barrier();                                                         \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    EXTRA_;                                                                               \
-    HQ6P_ISSUE();                                                                         \
-    {                                                                                     \
-      const int nb_ = b_r == S - 1 ? 0 : b_r + 1;                                         \
-      if (READ_) HQ6P_READ(1 - (SET_), nb_);                                              \
-      b_r = nb_;                                                                          \
-    }                                                                                     \
-    HQ6P_MFMA(SET_);                                                                      \
-    mfma_interleave<0, 2 * TM * TN, 3 * (TM + TN), LPW>();                                \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-  } while (0)
-#define HQ6P_PARAMS(M0_, N0_) \
-  do { if constexpr (DEQ) params_dma<BM, BN, NW>(smem + S * STAGE, wv, lane, M0_, N0_, M, N, ep); } while (0)
-
-  Frag6 af[2][TM], bf[2][TN];
-  v16f acc[TM][TN];
-
-  HQ6P_ISSUE();
-  HQ6P_ISSUE();
-  HQ6P_ISSUE();
-
-  for (int it = 0; it < nmine; ++it) {
-    int64_t m0, n0;
-    f6_tile_origin<BM, BN, GM>(int(blockIdx.x) + it * int(gridDim.x), M, N, &m0, &n0);
-    // The tile's first stage: its loads were issued two or more iterations
-    // (or the previous epilogue) ago; wait for them and everything before,
-    // including the previous epilogue's stores, then read its fragments.
-    wait_vm_lgkm0<2 * LPW>();
-    __builtin_amdgcn_s_barrier();
-    HQ6P_READ(0, b_r);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    // the P refill is issued after the barrier that ends the previous
-    // epilogue's reads of P
-    int kt = 0;
-    if (KT == 1) {
-      HQ6P_ITER(0, 0, HQ6P_PARAMS(m0, n0), false);
-    } else {
-      HQ6P_ITER(0, LPW, HQ6P_PARAMS(m0, n0), true);
-      kt = 1;
-      for (; kt + 2 < KT; kt += 2) {
-        HQ6P_ITER(1, LPW, (void)0, true);
-        HQ6P_ITER(0, LPW, (void)0, true);
-      }
-      // one or two stages left; the last one prefetches no fragments
-      if (kt + 1 < KT) {
-        HQ6P_ITER(1, LPW, (void)0, true);
-        HQ6P_ITER(0, LPW, (void)0, false);
-      } else {
-        HQ6P_ITER(1, LPW, (void)0, false);
-      }
-    }
-    // P (issued before the last LPW loads) has landed in every wave
-    wait_vm_lgkm0<LPW>();
-    __builtin_amdgcn_s_barrier();
-    gemm_epilogue_direct<BM, BN, TM, TN, DEQ, LR>(acc, P, lane, m0, n0, wm0, wn0, M, N, Cout, ldc,
-                                                 ep);
-  }
-  wait_vm_lgkm0<0>();  // no LDS write may land after the block ends
-#undef HQ6P_PARAMS
-#undef HQ6P_ITER
-#undef HQ6P_MFMA
-#undef HQ6P_READ
-#undef HQ6P_ISSUE
 }
 
 }  // namespace hq
