@@ -1,8 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the rotated-and-centred W4A4 quantised linear on one MI355X.
 
-One step = one hq_quant_linear call (activation kernel + int8 GEMM with the
-dequant epilogue) over one synthetic batch already resident in HBM. Inputs
+One step = one hq_quant_linear call (activation kernel + integer-exact GEMM
+with the dequant epilogue; E2M3 / FP6 MFMA for 4-bit codes, the same layer on
+the int8 MFMA engine is reported alongside) over one synthetic batch already
+resident in HBM. Inputs
 rotate through enough distinct X/Y buffers (> 512 MB) that a step's
 activations are not served from the 256 MB Infinity Cache left over from the
 previous visit. Prints one JSON line.
@@ -12,6 +14,7 @@ previous visit. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -66,11 +69,83 @@ def cpu_baseline(w, x, weight, bias, sigma, l1, l2, target_s):
                       f"(online half, prepared weights reused), {dt:.2f} s"}
 
 
+def measure(hq, torch, desc, w, Xs, Ys, S, W, B, L1, L2, steps, warmup, dev):
+    """Times `steps` quant_linear calls after `warmup`, then each of the two
+    kernels alone (stage entry points, captured back to back in a HIP graph
+    so the per-kernel time carries no host launch gaps)."""
+    nbuf = len(Xs)
+    tdt = Xs[0].dtype
+    prep = hq.prepare(desc, W, B, S, L1, L2)
+    ws = torch.empty(hq.workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
+    codes = torch.empty(hq.code_bytes(desc, w.T), dtype=torch.uint8, device=dev)
+    s_x = torch.empty(w.T, dtype=torch.float32, device=dev)
+    mu = torch.empty(w.T, dtype=torch.float32, device=dev)
+    U = torch.empty(w.T, w.rank, dtype=torch.float32, device=dev) if w.rank else None
+
+    def step(i):
+        hq.quant_linear(desc, prep, Xs[i % nbuf], out=Ys[i % nbuf], workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        step(warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+
+    # Per-kernel durations on the stream the kernels run on.
+    n = min(steps, 20)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        hq.act_quantize(desc, prep, Xs[0], out=(codes, s_x, mu, U))      # warm
+        hq.gemm_dequant(desc, prep, codes, s_x, mu, U, out=Ys[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g1):
+        for i in range(n):
+            hq.act_quantize(desc, prep, Xs[i % nbuf], out=(codes, s_x, mu, U))
+    with torch.cuda.graph(g2):
+        for i in range(n):
+            hq.gemm_dequant(desc, prep, codes, s_x, mu, U, out=Ys[i % nbuf])
+    times = []
+    for g in (g1, g2):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / n)
+    del g1, g2
+    return {"ms": ms, "wall": wall, "k1": times[0], "k2": times[1], "prep": prep}
+
+
+def kernel_report(hq, desc, w, r):
+    in_b = 2 if w.dtype == "bf16" else 4
+    fp6 = hq.code_format(desc) == hq.HQ_CODES_E2M3
+    # read X, write codes, s_x, mu, U
+    k1_bytes = w.T * (w.d_in * in_b + 8 + 4 * w.rank) + hq.code_bytes(desc, w.T)
+    k2_ops = 2.0 * w.T * w.d_in * w.d_out                          # code multiply-adds x 2
+    peak = FP6_PEAK_TOPS if fp6 else INT8_PEAK_TOPS
+    k1_gbs = k1_bytes / (r["k1"] * 1e-3) / 1e9
+    k2_tops = k2_ops / (r["k2"] * 1e-3) / 1e12
+    return fp6, peak, k1_gbs, k2_tops, k2_ops
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer shards by "
-              "tokens with no communication, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs on a "
+              "single GPU; across GPUs the layer would shard by tokens with no communication",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import hadamard_rotated_bit_amd as hq
@@ -94,59 +169,18 @@ def main():
     S = None
     if w.alpha is not None:          # offline calibration on the workload's own tokens
         S = hq.sigma(desc, hq.channel_absmax(desc, X0), W, w.alpha)
-    prep = hq.prepare(desc, W, B, S, L1, L2)
 
     xbytes = X0.numel() * X0.element_size()
     nbuf = max(2, math.ceil(512e6 / xbytes))
     Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
     Ys = [torch.empty(w.T, w.d_out, dtype=tdt, device=dev) for _ in range(nbuf)]
-    ws = torch.empty(hq.workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
-    codes = torch.empty(hq.code_bytes(desc, w.T), dtype=torch.uint8, device=dev)
-    fp6 = hq.code_format(desc) == hq.HQ_CODES_E2M3
-    s_x = torch.empty(w.T, dtype=torch.float32, device=dev)
-    mu = torch.empty(w.T, dtype=torch.float32, device=dev)
-    U = torch.empty(w.T, w.rank, dtype=torch.float32, device=dev) if w.rank else None
 
-    def step(i):
-        hq.quant_linear(desc, prep, Xs[i % nbuf], out=Ys[i % nbuf], workspace=ws)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
-
-    # Per-kernel durations: the same two kernels through the stage entry points,
-    # bracketed by events on the stream they run on.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        X = Xs[i % nbuf]
-        evs[i][0].record()
-        hq.act_quantize(desc, prep, X, out=(codes, s_x, mu, U))
-        evs[i][1].record()
-        hq.gemm_dequant(desc, prep, codes, s_x, mu, U, out=Ys[i % nbuf])
-        evs[i][2].record()
-    torch.cuda.synchronize()
-    k1 = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    k2 = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-
-    in_b = 2 if w.dtype == "bf16" else 4
-    # read X, write codes, s_x, mu, U
-    k1_bytes = w.T * (w.d_in * in_b + 8 + 4 * w.rank) + hq.code_bytes(desc, w.T)
-    k2_ops = 2.0 * w.T * w.d_in * w.d_out                          # code multiply-adds x 2
-    peak = FP6_PEAK_TOPS if fp6 else INT8_PEAK_TOPS
-    k1_gbs = k1_bytes / (k1 * 1e-3) / 1e9
-    k2_tops = k2_ops / (k2 * 1e-3) / 1e12
+    r = measure(hq, torch, desc, w, Xs, Ys, S, W, B, L1, L2, args.steps, args.warmup, dev)
+    fp6, peak, k1_gbs, k2_tops, k2_ops = kernel_report(hq, desc, w, r)
+    ms = r["ms"]
     tokens_s = w.T / (ms * 1e-3)
     eff_tops = k2_ops / (ms * 1e-3) / 1e12
-    if k2 >= k1:
+    if r["k2"] >= r["k1"]:
         roof = {"kernel": "gemm_f6_dequant" if fp6 else "gemm_i8_dequant", "bound": "mfma",
                 "achieved": round(k2_tops, 2), "peak": peak, "unit": "TFLOP/s",
                 "ops": ("e2m3" if fp6 else "int8") + " multiply-add x2",
@@ -163,17 +197,29 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
                    "block": w.block, "bits": f"W{w.w_bits}A{w.a_bits}", "center": bool(w.center),
-                   "smooth_alpha": w.alpha, "rank": w.rank, "io_dtype": w.dtype},
+                   "smooth_alpha": w.alpha, "rank": w.rank, "io_dtype": w.dtype,
+                   "gemm": "e2m3 fp6 mfma" if fp6 else "int8 mfma"},
         "effective_tops": round(eff_tops, 2),
         "roofline": roof,
         "kernels": {
-            "row_transform_ms": round(k1, 5), "row_transform_GBs": round(k1_gbs, 1),
+            "row_transform_ms": round(r["k1"], 5), "row_transform_GBs": round(k1_gbs, 1),
             "row_transform_hbm_frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-            "gemm_ms": round(k2, 5), "gemm_TOPS": round(k2_tops, 2),
+            "gemm_ms": round(r["k2"], 5), "gemm_TOPS": round(k2_tops, 2),
             "gemm_mfma_frac": round(k2_tops / peak, 4),
         },
-        "wall_s_timed": round(wall, 4),
+        "wall_s_timed": round(r["wall"], 4),
     }
+    if fp6:
+        # the same layer on the int8 engine (int4 codes in int8 lanes, int32
+        # accumulation): identical accumulators, measured against the int8 peak
+        d8 = dataclasses.replace(desc, gemm=hq.HQ_GEMM_I8)
+        r8 = measure(hq, torch, d8, w, Xs, Ys, S, W, B, L1, L2, args.steps, args.warmup, dev)
+        _, p8, g8, t8, _ = kernel_report(hq, d8, w, r8)
+        out["int8_engine"] = {
+            "value": round(w.T / (r8["ms"] * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(r8["ms"], 5), "row_transform_ms": round(r8["k1"], 5),
+            "row_transform_GBs": round(g8, 1), "gemm_ms": round(r8["k2"], 5),
+            "gemm_TOPS": round(t8, 2), "gemm_mfma_frac": round(t8 / p8, 4), "peak": p8}
     if not args.no_cpu_baseline:
         sig = None if S is None else S.cpu().numpy()
         out["cpu_baseline"] = cpu_baseline(w, x, weight, bias, sig, l1, l2, args.cpu_seconds)

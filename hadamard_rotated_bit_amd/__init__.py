@@ -20,7 +20,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import HQ_CODES_E2M3, HQ_CODES_I8, HqDesc, HqError, HqLayout, check, load
+from ._lib import (HQ_CODES_E2M3, HQ_CODES_I8, HQ_GEMM_AUTO, HQ_GEMM_I8, HqDesc, HqError,
+                   HqLayout, check, load)
 
 F32, BF16 = 0, 1
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16}
@@ -41,11 +42,12 @@ class Desc:
     x_dtype: int = F32
     w_dtype: int = F32
     y_dtype: int = F32
+    gemm: int = HQ_GEMM_AUTO
 
     def __post_init__(self):
         raw = HqDesc(self.d_in, self.d_out, self.block, self.a_bits, self.w_bits,
                      int(self.center), int(self.smooth), self.rank, self.x_dtype,
-                     self.w_dtype, self.y_dtype)
+                     self.w_dtype, self.y_dtype, self.gemm)
         object.__setattr__(self, "_raw", raw)
         object.__setattr__(self, "_ref", ctypes.byref(raw))
 

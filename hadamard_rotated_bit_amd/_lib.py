@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(HERE, "libhq.so")
 HEADER = os.path.join(HERE, "..", "include", "hq.h")
 
 DESC_FIELDS = ["d_in", "d_out", "block", "a_bits", "w_bits", "center", "smooth", "rank",
-               "x_dtype", "w_dtype", "y_dtype"]
+               "x_dtype", "w_dtype", "y_dtype", "gemm"]
 
 
 class HqDesc(ctypes.Structure):
@@ -24,6 +24,7 @@ class HqLayout(ctypes.Structure):
 
 
 HQ_CODES_I8, HQ_CODES_E2M3 = 0, 1
+HQ_GEMM_AUTO, HQ_GEMM_I8 = 0, 1
 
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_BAD_PREPARED, \
     HQ_ERR_HIP = 0, -1, -2, -3, -4, -5

@@ -62,6 +62,8 @@ int check_desc(const hq_desc* d) {
     return fail(HQ_ERR_INVALID_ARG, "w_dtype %d is not an hq_dtype", d->w_dtype);
   if (d->y_dtype != HQ_F32 && d->y_dtype != HQ_BF16)
     return fail(HQ_ERR_INVALID_ARG, "y_dtype %d is not an hq_dtype", d->y_dtype);
+  if (d->gemm != HQ_GEMM_AUTO && d->gemm != HQ_GEMM_I8)
+    return fail(HQ_ERR_INVALID_ARG, "gemm %d is not an hq_gemm_engine", d->gemm);
   if (d->center != 0 && d->center != 1)
     return fail(HQ_ERR_INVALID_ARG, "center must be 0 or 1 (got %d)", d->center);
   if (d->smooth != 0 && d->smooth != 1)
@@ -88,10 +90,11 @@ int check_desc(const hq_desc* d) {
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
 
-// Both operands use E2M3 (FP6 MFMA) when both code widths are 4 bits, else
-// int8 bytes (int8 MFMA).
+// Both operands use E2M3 (FP6 MFMA) when both code widths are 4 bits and the
+// engine is automatic, else int8 bytes (int8 MFMA).
 int code_fmt_of(const hq_desc* d) {
-  return (d->a_bits == 4 && d->w_bits == 4) ? hq::CODES_E2M3 : hq::CODES_I8;
+  return (d->gemm == HQ_GEMM_AUTO && d->a_bits == 4 && d->w_bits == 4) ? hq::CODES_E2M3
+                                                                         : hq::CODES_I8;
 }
 
 void layout_of(const hq_desc* d, hq_prepared_layout* L) {

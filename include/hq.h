@@ -40,9 +40,10 @@
  *
  * Code formats (hq_code_format). Activation and weight codes of one layer
  * share a format, fixed by the descriptor:
- *  HQ_CODES_I8    (a_bits = 8 or w_bits = 8): int8, row-major [rows, d_in],
- *                 one byte per code; int32 accumulation on the int8 MFMA.
- *  HQ_CODES_E2M3  (a_bits = w_bits = 4): each code q in [-7, 7] is stored as
+ *  HQ_CODES_I8    (a_bits = 8, w_bits = 8 or gemm = HQ_GEMM_I8): int8,
+ *                 row-major [rows, d_in], one byte per code; int32
+ *                 accumulation on the int8 MFMA.
+ *  HQ_CODES_E2M3  (a_bits = w_bits = 4, gemm = HQ_GEMM_AUTO): each code q in [-7, 7] is stored as
  *                 the 6-bit float E2M3 of the same value (bit 5 sign, bits
  *                 4-3 exponent with bias 1, bits 2-0 mantissa; |q| = 0..7 ->
  *                 0, 8, 16, 20, 24, 26, 28, 30; q = 0 is stored as +0). E2M3
@@ -66,7 +67,7 @@
 extern "C" {
 #endif
 
-#define HQ_ABI_VERSION 2
+#define HQ_ABI_VERSION 3
 
 typedef enum {
   HQ_OK = 0,
@@ -80,6 +81,12 @@ typedef enum {
 typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
 
 typedef enum { HQ_CODES_I8 = 0, HQ_CODES_E2M3 = 1 } hq_code_format_t;
+
+/* GEMM engine: HQ_GEMM_AUTO takes the E2M3 / FP6 MFMA when both code widths
+ * are 4 bits and the int8 MFMA otherwise; HQ_GEMM_I8 always uses int8 lanes
+ * (int4 codes held losslessly in int8) on the int8 MFMA with int32
+ * accumulation. Both return identical accumulators. */
+typedef enum { HQ_GEMM_AUTO = 0, HQ_GEMM_I8 = 1 } hq_gemm_engine;
 
 /* Layer descriptor (plain data, passed by host pointer).
  *  d_in    input channels: a multiple of 128 up to 2048, of 256 up to 4096,
@@ -95,10 +102,11 @@ typedef enum { HQ_CODES_I8 = 0, HQ_CODES_E2M3 = 1 } hq_code_format_t;
  *  x_dtype dtype of X (hq_dtype).
  *  w_dtype dtype of weight, L1 and L2 (hq_dtype).
  *  y_dtype dtype of Y (hq_dtype).
+ *  gemm    GEMM engine (hq_gemm_engine); it also fixes the code format.
  * Bias, sigma and every scale are float32. */
 typedef struct {
   int32_t d_in, d_out, block, a_bits, w_bits, center, smooth, rank;
-  int32_t x_dtype, w_dtype, y_dtype;
+  int32_t x_dtype, w_dtype, y_dtype, gemm;
 } hq_desc;
 
 /* Byte offsets of the arrays inside a prepared blob (all 256-byte aligned). */

@@ -16,8 +16,8 @@ import numpy as np
 I8, E2M3 = 0, 1
 
 
-def fmt_of(a_bits: int, w_bits: int) -> int:
-    return E2M3 if (a_bits == 4 and w_bits == 4) else I8
+def fmt_of(a_bits: int, w_bits: int, gemm: int = 0) -> int:
+    return E2M3 if (a_bits == 4 and w_bits == 4 and gemm == 0) else I8
 
 
 def nbytes(fmt: int, rows: int, d: int) -> int:

@@ -29,10 +29,21 @@ Y_TOL = 1e-3
 XT_TOL = 1e-5
 
 
-def desc_for(w: WL.Workload) -> hq.Desc:
+def desc_for(w: WL.Workload, gemm: int = hq.HQ_GEMM_AUTO) -> hq.Desc:
     dt = hq.BF16 if w.dtype == "bf16" else hq.F32
     return hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, bool(w.center),
-                   w.alpha is not None, w.rank, dt, dt, dt)
+                   w.alpha is not None, w.rank, dt, dt, dt, gemm)
+
+
+# (workload, GEMM engine) pairs the parity tests run: every workload on the
+# automatic engine, and the 4-bit ones also on the int8 engine.
+ENGINE_CASES = [(n, hq.HQ_GEMM_AUTO) for n in WL.ORDER] + [
+    (n, hq.HQ_GEMM_I8) for n in WL.ORDER
+    if WL.WORKLOADS[n].a_bits == 4 and WL.WORKLOADS[n].w_bits == 4]
+
+
+def case_id(c) -> str:
+    return f"{c[0]}-{'i8' if c[1] == hq.HQ_GEMM_I8 else 'auto'}"
 
 
 def tdev(a: np.ndarray, dtype: str) -> torch.Tensor:
@@ -45,10 +56,10 @@ def tdev(a: np.ndarray, dtype: str) -> torch.Tensor:
 class Case:
     """Inputs of a workload (first T rows), the oracle's results, the GPU prepared blob."""
 
-    def __init__(self, w: WL.Workload, T: int, x=None):
+    def __init__(self, w: WL.Workload, T: int, x=None, gemm: int = hq.HQ_GEMM_AUTO):
         self.w = w
         self.T = T
-        self.desc = desc_for(w)
+        self.desc = desc_for(w, gemm)
         self.x = WL.gen_x(w, T=T) if x is None else x
         self.weight = WL.gen_weight(w)
         self.bias = WL.gen_bias(w)
@@ -74,9 +85,9 @@ class Case:
 
 
 @functools.lru_cache(maxsize=None)
-def small_case(name: str, T: int = 300) -> Case:
-    print(f"\n[case] {name} T={T}", flush=True)
-    return Case(WL.WORKLOADS[name], T)
+def small_case(name: str, T: int = 300, gemm: int = hq.HQ_GEMM_AUTO) -> Case:
+    print(f"\n[case] {name} T={T} gemm={gemm}", flush=True)
+    return Case(WL.WORKLOADS[name], T, gemm=gemm)
 
 
 def check_codes(gpu_codes, ora_codes, ora_v, what: str):
@@ -99,7 +110,7 @@ def check_codes(gpu_codes, ora_codes, ora_v, what: str):
 def codes_np(desc: hq.Desc, buf: torch.Tensor, rows: int, idx=None) -> np.ndarray:
     """Integer codes [rows, d_in] (or rows `idx`) of a device code buffer of
     `rows` rows, read on the host from the format's definition (codefmt.py)."""
-    fmt = codefmt.fmt_of(desc.a_bits, desc.w_bits)
+    fmt = codefmt.fmt_of(desc.a_bits, desc.w_bits, desc.gemm)
     assert hq.code_format(desc) == fmt
     assert hq.code_bytes(desc, rows) == codefmt.nbytes(fmt, rows, desc.d_in)
     return codefmt.decode(fmt, buf.detach().cpu().numpy(), rows, desc.d_in, idx)
@@ -107,7 +118,7 @@ def codes_np(desc: hq.Desc, buf: torch.Tensor, rows: int, idx=None) -> np.ndarra
 
 def codes_dev(desc: hq.Desc, codes: np.ndarray) -> torch.Tensor:
     """Device code buffer holding integer codes [rows, d_in]."""
-    fmt = codefmt.fmt_of(desc.a_bits, desc.w_bits)
+    fmt = codefmt.fmt_of(desc.a_bits, desc.w_bits, desc.gemm)
     return torch.from_numpy(codefmt.encode(fmt, codes)).cuda()
 
 

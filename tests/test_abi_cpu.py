@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lib.hq_abi_version() == 2
+    assert lib.hq_abi_version() == 3
     assert lib.hq_status_str(0) == b"HQ_OK"
     assert lib.hq_status_str(-3) == b"HQ_ERR_WORKSPACE"
     assert lib.hq_status_str(99) == b"HQ_ERR_UNKNOWN"
@@ -57,7 +57,8 @@ def test_workload_descriptors_valid(name):
     (dict(d_in=0), -1), (dict(d_out=-8), -1), (dict(x_dtype=3), -1), (dict(center=2), -1),
     (dict(smooth=5), -1), (dict(a_bits=3), -2), (dict(w_bits=16), -2), (dict(d_in=1000), -2),
     (dict(d_in=2176), -2), (dict(d_out=100), -2), (dict(block=96), -2), (dict(block=256, d_in=1152), -2),
-    (dict(rank=8), -2), (dict(rank=128), -2), (dict(d_in=16384), -2),
+    (dict(rank=8), -2), (dict(rank=128), -2), (dict(d_in=16384), -2), (dict(gemm=2), -1),
+    (dict(gemm=-1), -1),
 ])
 def test_validation_rejects(kw, status):
     d = _d(**kw)
@@ -77,9 +78,10 @@ def test_block_one_and_full():
     assert lib.hq_validate(ctypes.byref(_d(d_in=4096, block=4096))) == 0
 
 
-@pytest.mark.parametrize("a_bits,w_bits,fmt", [(4, 4, 1), (8, 4, 0), (4, 8, 0), (8, 8, 0)])
-def test_code_format_and_bytes(a_bits, w_bits, fmt):
-    d = ctypes.byref(_d(a_bits=a_bits, w_bits=w_bits))
+@pytest.mark.parametrize("a_bits,w_bits,gemm,fmt", [(4, 4, 0, 1), (8, 4, 0, 0), (4, 8, 0, 0),
+                                                    (8, 8, 0, 0), (4, 4, 1, 0), (8, 8, 1, 0)])
+def test_code_format_and_bytes(a_bits, w_bits, gemm, fmt):
+    d = ctypes.byref(_d(a_bits=a_bits, w_bits=w_bits, gemm=gemm))
     assert lib.hq_code_format(d) == fmt
     for rows in [0, 1, 3, 4, 5, 8192]:
         assert lib.hq_code_bytes(d, rows) == codefmt.nbytes(fmt, rows, 1152)

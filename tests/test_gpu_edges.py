@@ -17,9 +17,9 @@ DT = {"f32": hq.F32, "bf16": hq.BF16}
 
 def run_case(T, d_in, d_out, *, block, a_bits=4, w_bits=4, center=True, alpha=0.5, rank=0,
              x_dtype="f32", w_dtype="f32", y_dtype="f32", key=100, x=None, n_outliers=4,
-             outlier=50.0):
+             outlier=50.0, gemm=hq.HQ_GEMM_AUTO):
     print(f"\n[case] T={T} {d_in}->{d_out} block={block} A{a_bits}W{w_bits} center={center} "
-          f"alpha={alpha} rank={rank} {x_dtype}/{w_dtype}/{y_dtype}", flush=True)
+          f"alpha={alpha} rank={rank} {x_dtype}/{w_dtype}/{y_dtype} gemm={gemm}", flush=True)
     w = WL.custom(key, T, d_in, d_out, dtype=x_dtype, block=block, alpha=alpha, center=int(center),
                   a_bits=a_bits, w_bits=w_bits, rank=rank, n_outliers=n_outliers, outlier=outlier)
     if x is None:
@@ -28,7 +28,7 @@ def run_case(T, d_in, d_out, *, block, a_bits=4, w_bits=4, center=True, alpha=0.
     weight, bias = WL.gen_weight(wq), WL.gen_bias(wq)
     l1, l2 = WL.gen_lowrank(wq)
     desc = hq.Desc(d_in, d_out, block, a_bits, w_bits, center, alpha is not None, rank,
-                   DT[x_dtype], DT[w_dtype], DT[y_dtype])
+                   DT[x_dtype], DT[w_dtype], DT[y_dtype], gemm)
     sig = None
     if alpha is not None:
         sig = O.smoothing_scales(x if T > 0 else np.ones((1, d_in)), weight, alpha)
@@ -59,16 +59,21 @@ def test_empty_batch():
     assert Y.shape == (0, 64) and hq.code_bytes(desc, 0) == 0
 
 
+ENGINES = [hq.HQ_GEMM_AUTO, hq.HQ_GEMM_I8]
+
+
+@pytest.mark.parametrize("gemm", ENGINES)
 @pytest.mark.parametrize("T", [1, 3, 129, 257, 1000])
-def test_ragged_tokens(T):
-    r = run_case(T, 256, 264, block=64)
+def test_ragged_tokens(T, gemm):
+    r = run_case(T, 256, 264, block=64, gemm=gemm)
     check_all(r[3], r[4], r[5], r[8], r[0])
 
 
+@pytest.mark.parametrize("gemm", ENGINES)
 @pytest.mark.parametrize("T,d_out", [(600, 1032), (700, 1160), (2100, 1536)])
-def test_ragged_outputs_large_tiles(T, d_out):
-    # T > 512 and d_out > 512 take the 256x256 / 128x192 configurations
-    r = run_case(T, 512, d_out, block=512)
+def test_ragged_outputs_large_tiles(T, d_out, gemm):
+    # T > 512 and d_out > 512 take the large tile shapes of both engines
+    r = run_case(T, 512, d_out, block=512, gemm=gemm)
     check_all(r[3], r[4], r[5], r[8], r[0])
 
 
@@ -109,9 +114,11 @@ def test_code_widths(ab, wb):
     assert np.abs(codes_np(r[0], r[4], 300)).max() <= 2 ** (ab - 1) - 1
 
 
+@pytest.mark.parametrize("gemm", ENGINES)
 @pytest.mark.parametrize("rank,xd", [(16, "f32"), (48, "bf16"), (64, "f32")])
-def test_low_rank(rank, xd):
-    r = run_case(260, 512, 384, block=256, rank=rank, x_dtype=xd, w_dtype=xd, y_dtype=xd)
+def test_low_rank(rank, xd, gemm):
+    r = run_case(260, 512, 384, block=256, rank=rank, x_dtype=xd, w_dtype=xd, y_dtype=xd,
+                 gemm=gemm)
     desc, prep, X, Y, codes, s_x, mu, U, ora = r
     check_all(Y, codes, s_x, ora, desc)
     err = np.linalg.norm(to_np(U) - ora["u"], axis=1) / np.linalg.norm(ora["u"], axis=1)

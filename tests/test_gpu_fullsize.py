@@ -13,7 +13,8 @@ import torch
 import hadamard_rotated_bit_amd as hq
 from hadamard_rotated_bit_amd import workloads as WL
 from oracle import hq_oracle as O
-from parity import Y_TOL, check_codes, codes_dev, codes_np, desc_for, rel_fro, tdev, to_np
+from parity import (ENGINE_CASES, Y_TOL, case_id, check_codes, codes_dev, codes_np, desc_for, rel_fro,
+                    tdev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,11 +63,12 @@ def test_full_size_sampled(name):
     assert np.all(np.abs(mu_s - ora["mu"]) <= 1e-5 * rms)
 
 
-@pytest.mark.parametrize("name", WL.ORDER)
-def test_full_size_gemm_bit_exact(name):
+@pytest.mark.parametrize("ec", ENGINE_CASES, ids=case_id)
+def test_full_size_gemm_bit_exact(ec):
+    name = ec[0]
     w = WL.WORKLOADS[name]
-    print(f"\n[case] full-size GEMM {name} {w.T}x{w.d_out}x{w.d_in}", flush=True)
-    desc = desc_for(w)
+    print(f"\n[case] full-size GEMM {name} {w.T}x{w.d_out}x{w.d_in} gemm={ec[1]}", flush=True)
+    desc = desc_for(w, ec[1])
     qmax = 2 ** (w.a_bits - 1) - 1
     rng = np.random.default_rng(1234 + w.key)
     a = rng.integers(-qmax, qmax + 1, (w.T, w.d_in), dtype=np.int8)

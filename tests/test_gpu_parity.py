@@ -11,8 +11,8 @@ import torch
 import hadamard_rotated_bit_amd as hq
 from hadamard_rotated_bit_amd import workloads as WL
 from oracle import hq_oracle as O
-from parity import (MAX_FLIP_FRAC, XT_TOL, Y_TOL, check_codes, codes_dev, codes_np, rel_fro,
-                    small_case, tdev, to_np)
+from parity import (ENGINE_CASES, MAX_FLIP_FRAC, XT_TOL, Y_TOL, case_id, check_codes, codes_dev,
+                    codes_np, rel_fro, small_case, tdev, to_np)
 
 pytestmark = pytest.mark.gpu
 NAMES = WL.ORDER
@@ -28,9 +28,10 @@ def test_sigma(name):
     assert err <= 1e-6, err
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_weight_prepare(name):
-    c = small_case(name)
+@pytest.mark.parametrize("ec", ENGINE_CASES, ids=case_id)
+def test_weight_prepare(ec):
+    name = ec[0]
+    c = small_case(name, gemm=ec[1])
     v = hq.prepared_views(c.desc, c.prep)
     o = c.ora
     qmax = 2 ** (c.w.w_bits - 1) - 1
@@ -63,9 +64,10 @@ def test_activation_transform(name):
                       <= 1e-5 * np.abs(o["xt"]).sum(axis=1))
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_activation_codes(name):
-    c = small_case(name)
+@pytest.mark.parametrize("ec", ENGINE_CASES, ids=case_id)
+def test_activation_codes(ec):
+    name = ec[0]
+    c = small_case(name, gemm=ec[1])
     codes, s_x, mu, U = hq.act_quantize(c.desc, c.prep, c.X)
     o = c.ora
     ratio = np.divide(o["xt"], o["s_x"][:, None], out=np.zeros_like(o["xt"]),
@@ -81,9 +83,10 @@ def test_activation_codes(name):
         assert err.max() <= 1e-4, err.max()
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_gemm_bit_exact(name):
-    c = small_case(name)
+@pytest.mark.parametrize("ec", ENGINE_CASES, ids=case_id)
+def test_gemm_bit_exact(ec):
+    name = ec[0]
+    c = small_case(name, gemm=ec[1])
     o = c.ora
     a = codes_dev(c.desc, o["qa"])
     w = codes_dev(c.desc, o["qw"])
@@ -91,9 +94,10 @@ def test_gemm_bit_exact(name):
     np.testing.assert_array_equal(to_np(acc).astype(np.int64), o["acc"])
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_output(name):
-    c = small_case(name)
+@pytest.mark.parametrize("ec", ENGINE_CASES, ids=case_id)
+def test_output(ec):
+    name = ec[0]
+    c = small_case(name, gemm=ec[1])
     Y = hq.quant_linear(c.desc, c.prep, c.X)
     err = rel_fro(to_np(Y), c.ora["y_out"])
     print(f"{name}: rel Frobenius error {err:.3e}")
@@ -106,11 +110,11 @@ def test_output(name):
     assert torch.equal(Y, hq.quant_linear(c.desc, c.prep, c.X))
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_output_with_oracle_codes_is_tight(name):
+@pytest.mark.parametrize("ec", ENGINE_CASES, ids=case_id)
+def test_output_with_oracle_codes_is_tight(ec):
     # Epilogue check: feeding the oracle's own codes/scales/mu (and U) through the GEMM
     # + dequant epilogue reproduces the oracle's output up to float32 epilogue rounding.
-    c = small_case(name)
+    c = small_case(ec[0], gemm=ec[1])
     o = c.ora
     codes = codes_dev(c.desc, o["qa"])
     s_x = torch.from_numpy(o["s_x"].astype(np.float32)).cuda()
