@@ -128,6 +128,25 @@ def measure(hq, torch, desc, w, Xs, Ys, S, W, B, L1, L2, steps, warmup, dev):
     return {"ms": ms, "wall": wall, "k1": times[0], "k2": times[1], "prep": prep}
 
 
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary of this kernel and
+    workload (profiles/<kernel>_<workload>_traffic.json), or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel.replace('_dequant', '')}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["sources_sha256"] or rec["kernel"] != kernel:
+        return None
+    return int(round(rec["traffic_bytes_per_launch"]))
+
+
 def kernel_report(hq, desc, w, r):
     in_b = 2 if w.dtype == "bf16" else 4
     fp6 = hq.code_format(desc) == hq.HQ_CODES_E2M3
@@ -181,10 +200,12 @@ def main():
     tokens_s = w.T / (ms * 1e-3)
     eff_tops = k2_ops / (ms * 1e-3) / 1e12
     if r["k2"] >= r["k1"]:
-        roof = {"kernel": "gemm_f6_dequant" if fp6 else "gemm_i8_dequant", "bound": "mfma",
+        kname = "gemm_f6_dequant" if fp6 else "gemm_i8_dequant"
+        roof = {"kernel": kname, "bound": "mfma",
                 "achieved": round(k2_tops, 2), "peak": peak, "unit": "TFLOP/s",
                 "ops": ("e2m3" if fp6 else "int8") + " multiply-add x2",
-                "frac": round(k2_tops / peak, 4), "traffic": None}
+                "frac": round(k2_tops / peak, 4), "traffic": measured_traffic(kname, w.name),
+                "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)"}
     else:
         roof = {"kernel": "row_transform", "bound": "hbm", "achieved": round(k1_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
