@@ -23,6 +23,19 @@ static hipError_t launch_f6_cfg(const uint8_t* A, int64_t M, const uint8_t* B, i
   return hipGetLastError();
 }
 
+// Persistent 256 x 192 kernel for bf16 outputs (K >= 384): one block per CU
+// (at most one per tile) walks its tiles with the stage pipeline running
+// across tile boundaries.
+template <bool LR>
+static hipError_t launch_f6_persist(const uint8_t* A, int64_t M, const uint8_t* B, int64_t N,
+                                    int K, const GemmEpi& ep, int cus, hipStream_t s) {
+  const int64_t ntiles = ((M + 255) / 256) * ((N + 191) / 192);
+  const unsigned grid = unsigned(ntiles < cus ? ntiles : cus);
+  hipLaunchKernelGGL((gemm_f6_persist<256, 192, 128, 96, 4, F6_GROUP, LR>), dim3(grid), dim3(256),
+                     0, s, A, M, B, N, K, ep);
+  return hipGetLastError();
+}
+
 // Tile choice: 256 x 256 or 256 x 192 (one block of 4 waves per CU), whichever
 // needs less work per CU once the tiles are dealt in rounds of one per CU
 // (rounds x tile width): e.g. 8192 x 4608 takes 3 rounds of 256 x 192 tiles
@@ -42,6 +55,9 @@ hipError_t launch_gemm_f6(const uint8_t* A, int64_t M, const uint8_t* B, int64_t
     }
     if (cu_cache[dev] > 0) cus = cu_cache[dev];
   }
+  if (epi && epi->y_bf16 && K >= 384)
+    return epi->rank ? launch_f6_persist<true>(A, M, B, N, K, *epi, cus, s)
+                     : launch_f6_persist<false>(A, M, B, N, K, *epi, cus, s);
   const int64_t tm = (M + 255) / 256;
   const int64_t rounds256 = (tm * ((N + 255) / 256) + cus - 1) / cus;
   const int64_t rounds192 = (tm * ((N + 191) / 192) + cus - 1) / cus;

@@ -159,9 +159,33 @@ __device__ __forceinline__ void params_dma(uint8_t* P, int wv, int lane, int64_t
   }
 }
 
-template <int BM, int BN, int WM, int WN, int S, int GM, bool DEQ, int RG = 1>
+// The same parameters with a fixed unit per wave and array: wave w copies
+// unit min(w, units - 1) of each of the five vectors (64 floats per unit;
+// repeated units write the same bytes), five loads per wave with no
+// wave-dependent control flow.
+template <int BM, int BN, int NW>
+__device__ __forceinline__ void params_dma_fixed(uint8_t* P, int wv, int lane, int64_t m0,
+                                                 int64_t n0, int64_t M, int64_t N,
+                                                 const GemmEpi& ep) {
+  constexpr int UN = BN / 64, UM = BM / 64;
+  static_assert(BN % 64 == 0 && BM % 64 == 0 && UN <= NW && UM <= NW, "one unit per wave");
+  const int un = wv < UN ? wv : UN - 1;
+  const int um = wv < UM ? wv : UM - 1;
+  const int64_t cn = n0 + 64 * un, rm = m0 + 64 * um;
+  const int64_t ln = N - cn, lm = M - rm;
+  const int bn = int((ln < 64 ? (ln > 0 ? ln : 0) : 64) * 4);
+  const int bm = int((lm < 64 ? (lm > 0 ? lm : 0) : 64) * 4);
+  const uint32_t vo = uint32_t(lane) * 4u;
+  lds_dma4_buf(make_rsrc(ep.s_w + cn, bn), vo, 0u, P + 4 * (64 * un));
+  lds_dma4_buf(make_rsrc(ep.c + cn, bn), vo, 0u, P + 4 * (BN + 64 * un));
+  lds_dma4_buf(make_rsrc(ep.bias + cn, bn), vo, 0u, P + 4 * (2 * BN + 64 * un));
+  lds_dma4_buf(make_rsrc(ep.s_x + rm, bm), vo, 0u, P + 4 * (3 * BN + 64 * um));
+  lds_dma4_buf(make_rsrc(ep.mu + rm, bm), vo, 0u, P + 4 * (3 * BN + BM + 64 * um));
+}
+
+template <int BM, int BN, int WM, int WN, int S, int GM, bool DEQ, int RG = 1, int OCC = 1>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_kernel(
+__attribute__((amdgpu_waves_per_eu(OCC))) void gemm_f6_kernel(
     const uint8_t* __restrict__ A, int64_t M, const uint8_t* __restrict__ B, int64_t N, int K,
     int32_t* __restrict__ Cout, int64_t ldc, GemmEpi ep) {
   constexpr int NW = (BM / WM) * (BN / WN);
@@ -173,7 +197,7 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_kernel(
   constexpr int LPW = (UNITS + NW - 1) / NW;  // DMA instructions per wave and stage
   constexpr int QA = UA / NW;                 // the first QA of them load A
   static_assert(UA % NW == 0, "A units split evenly over the waves");
-  static_assert(S == 3, "three-buffer pipeline");
+  static_assert(S == 2 || S == 3, "two or three stage buffers");
   static_assert(BM % 32 == 0 && BN % 32 == 0, "whole 1-KB units per tile");
   static_assert(4 * (3 * BN + 2 * BM) <= S * STAGE, "epilogue staging fits in LDS");
   static_assert(BM * (2 * BN + 8) <= S * STAGE, "bf16 tile fits in the stage buffers");
@@ -259,10 +283,10 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_kernel(
   // so every iteration is the same straight sequence.
 #define HQ6_FULL(SET_, KT_)                                                               \
   do {                                                                                    \
-    wait_vm_lgkm0<LPW>();                                                                 \
+    wait_vm_lgkm0<(S - 2) * LPW>();                                                       \
     __builtin_amdgcn_s_barrier();                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                    \
-    HQ6_ISSUE((KT_) + 3);                                                                 \
+    HQ6_ISSUE((KT_) + S);                                                                 \
     HQ6_READ(1 - (SET_), (KT_) + 1);                                                      \
     HQ6_MFMA(SET_);                                                                       \
     mfma_interleave<0, 2 * TM * TN, 3 * (TM + TN), LPW>();                                \
@@ -281,8 +305,8 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_kernel(
   if constexpr (DEQ) params_dma<BM, BN, NW>(smem + S * STAGE, wv, lane, m0, n0, M, N, ep);
   HQ6_ISSUE(0);
   HQ6_ISSUE(1);
-  HQ6_ISSUE(2);
-  wait_vm_lgkm0<2 * LPW>();
+  if constexpr (S == 3) HQ6_ISSUE(2);
+  wait_vm_lgkm0<(S - 1) * LPW>();
   __builtin_amdgcn_s_barrier();
   HQ6_READ(0, 0);
   int kt = 0;
@@ -311,6 +335,343 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_kernel(
     }
   }
   gemm_epilogue<BM, BN, TM, TN, NW, DEQ>(acc, smem, tid, lane, m0, n0, wm0, wn0, M, N, Cout, ldc, ep);
+}
+
+// Persistent variant for bf16 outputs (one block of 4 waves per CU, grid at
+// most one block per CU): the block walks the tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ... with a single stage pipeline across tile
+// boundaries. Global stage g (tile g / KT, k-step g % KT) lives in buffer
+// g mod 3, so the last iterations of a tile already load the first three
+// stages of the next one and those loads overlap the epilogue.
+//
+// The epilogue does not touch the stage buffers: each wave stages its
+// 32-row slices in a private LDS area and writes them back with 16-byte
+// buffer stores that always issue (rows past M fall outside the descriptor,
+// columns past N get an out-of-range offset); then the next tile's epilogue
+// parameters are loaded into the other of two parameter buffers. Every wave
+// thus issues, per tile, KT stage loads of LPW instructions, NST stores and
+// PPW parameter loads, in a fixed order, and the waits count them (vector
+// memory operations retire in issue order): k-steps 0 and 1 may leave the
+// previous epilogue's stores and parameter loads in flight
+// (LPW + NST + PPW outstanding), later k-steps only the stage loaded one
+// iteration earlier (LPW). The prologue issues NST stores that move no
+// memory so that the first tile has the same sequence. A tile's parameters
+// are retired by its k-step 2 (K >= 384: three stages per tile).
+template <int BM, int BN, int WM, int WN, int GM, int RG, bool LR>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
+    const uint8_t* __restrict__ A, int64_t M, const uint8_t* __restrict__ B, int64_t N, int K,
+    GemmEpi ep) {
+  constexpr int S = 3;
+  constexpr int NW = (BM / WM) * (BN / WN);
+  constexpr int WAVES_N = BN / WN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int STAGE = 96 * (BM + BN);
+  constexpr int UA = 3 * BM / 32;
+  constexpr int UNITS = 3 * (BM + BN) / 32;
+  constexpr int LPW = (UNITS + NW - 1) / NW;
+  constexpr int QA = UA / NW;
+  constexpr int NP = 3 * BN + 2 * BM;          // floats per parameter buffer
+  constexpr int PPW = 5;                       // loads per params_dma_fixed
+  constexpr int CPR = WN / 8;                  // 16-byte pieces per slice row
+  constexpr int SP = 2 * WN + 8;               // staging pitch (bytes)
+  constexpr int SPS = 32 * CPR / 64;           // stores per slice
+  constexpr int NST = TM * SPS;                // stores per wave and tile
+  constexpr int WBIG = LPW + NST + PPW;
+  static_assert(UA % NW == 0 && BM % 32 == 0 && BN % 32 == 0, "whole 1-KB units per tile");
+  static_assert((32 * CPR) % 64 == 0, "whole store instructions per slice");
+  static_assert(2 * LPW + NST + PPW <= 63, "outstanding count fits vmcnt");
+  static_assert((((SP / 4) % 64) & 3) == 2, "staging pitch = 2 x odd dwords mod 64 banks");
+  // LDS: two parameter buffers, the waves' staging areas, the stage buffers
+  // (the epilogue's accesses keep small constant offsets).
+  constexpr int SB = 2 * 4 * NP + NW * 32 * SP;
+  static_assert(SB % 256 == 0, "stage buffers start on a bank line");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[SB + S * STAGE];
+  uint8_t* const smem = lds + SB;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint8_t* const stg = lds + 2 * 4 * NP + wv * 32 * SP;
+  const int wm0 = (wv / WAVES_N) * WM, wn0 = (wv % WAVES_N) * WN;
+  const int KT = K / 128;
+  const int64_t lda = f6_row_bytes(K);
+  const int ntiles = int((M + BM - 1) / BM) * int((N + BN - 1) / BN);
+  const int G = int(gridDim.x);
+
+  // Three 1-KB units cover 32 rows exactly (192 chunks of 16 B), so the
+  // global offset of unit 3t + r is that of unit r plus 32 t rows: each
+  // lane keeps the offsets of units 0, 1 and 2 only.
+  static_assert(UA % 3 == 0 && 32 % RG == 0, "unit triples are whole row groups");
+  uint32_t vb[3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    const int c = 64 * r + lane;
+    const int row = c / 6, slot = c - 6 * (c / 6);
+    const int h = (slot >= 3 ? 1 : 0) ^ ((row >> 3) & 1);
+    vb[r] = uint32_t((row / RG) * RG * lda + (row % RG) * 96 + 48 * h +
+                     16 * (slot - 3 * (slot >= 3 ? 1 : 0)));
+  }
+
+  // Source rows of a tile: base pointers and descriptor sizes (0 past the end).
+  struct Src {
+    const uint8_t* a;
+    const uint8_t* b;
+    int na, nb;
+    int64_t m0, n0;
+  };
+  auto tile_src = [&](int t) {
+    Src r{A, B, 0, 0, 0, 0};
+    if (t < ntiles) {
+      f6_tile_origin<BM, BN, GM>(t, M, N, &r.m0, &r.n0);
+      const int64_t ra = (M - r.m0) < BM ? (M - r.m0) : BM;
+      const int64_t rb = (N - r.n0) < BN ? (N - r.n0) : BN;
+      r.a = A + r.m0 * lda;
+      r.b = B + r.n0 * lda;
+      r.na = int((ra + RG - 1) / RG * RG * lda);
+      r.nb = int((rb + RG - 1) / RG * RG * lda);
+    }
+    return r;
+  };
+
+  int tile = int(blockIdx.x);
+  Src cur = tile_src(tile), nxt = tile_src(tile + G);
+  int bufc = 0;  // buffer of the current global stage
+  int pb = 0;    // parameter buffer of the current tile
+
+  // Load of k-step KS_ of the current tile (past its end: of the next tile).
+#define HP_ISSUE(KS_, BUF_)                                                               \
+  do {                                                                                    \
+    const int k3_ = (KS_);                                                                \
+    const bool nx_ = k3_ >= KT;                                                           \
+    const int ks_ = nx_ ? k3_ - KT : k3_;                                                 \
+    const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(nx_ ? nxt.a : cur.a, nx_ ? nxt.na : cur.na); \
+    const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(nx_ ? nxt.b : cur.b, nx_ ? nxt.nb : cur.nb); \
+    uint8_t* base_ = smem + (BUF_) * STAGE;                                               \
+    _Pragma("unroll") for (int q = 0; q < LPW; ++q) {                                     \
+      int u_ = q * NW + wv;                                                               \
+      if (u_ > UNITS - 1) u_ = UNITS - 1;                                                 \
+      const int ul_ = q < QA ? u_ : u_ - UA;                                              \
+      const int t_ = ul_ / 3, r_ = ul_ - 3 * t_;                                          \
+      const uint32_t vo_ = (r_ == 0 ? vb[0] : (r_ == 1 ? vb[1] : vb[2])) +                \
+                           uint32_t(t_) * uint32_t(32 * lda);                             \
+      lds_dma16_buf(q < QA ? ra_ : rb_, vo_, uint32_t(ks_) * (96u * RG), base_ + u_ * 1024); \
+    }                                                                                     \
+  } while (0)
+
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int loff = lrow * 96 + 48 * (lhalf ^ ((lrow >> 3) & 1));
+#define HP_READ(SET_, BUF_)                                                               \
+  do {                                                                                    \
+    const uint8_t* cur_ = smem + (BUF_) * STAGE + loff;                                   \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                        \
+      _Pragma("unroll") for (int p = 0; p < 3; ++p) af[SET_][i].c[p] =                    \
+          *reinterpret_cast<const v4i*>(cur_ + (wm0 + 32 * i) * 96 + 16 * p);             \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
+      _Pragma("unroll") for (int p = 0; p < 3; ++p) bf[SET_][j].c[p] =                    \
+          *reinterpret_cast<const v4i*>(cur_ + (BM + wn0 + 32 * j) * 96 + 16 * p);        \
+  } while (0)
+#define HP_MFMA(SET_)                                                                     \
+  do {                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                        \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                    \
+        acc[i][j] = mfma_f6(f6_op0(bf[SET_][j]), f6_op0(af[SET_][i]), acc[i][j]);         \
+        acc[i][j] = mfma_f6(f6_op1(bf[SET_][j]), f6_op1(af[SET_][i]), acc[i][j]);         \
+      }                                                                                   \
+  } while (0)
+  // One iteration on k-step KT_ of the current tile (fragments in SET_):
+  // wait for the next global stage, join the block, refill the current
+  // buffer with the stage three ahead, prefetch the fragments of the next
+  // global stage (at the tile's last k-step: the next tile's first), run the
+  // MFMAs.
+#define HP_STEP(SET_, KT_)                                                                \
+  do {                                                                                    \
+    if ((KT_) < 2) wait_vm_lgkm0<WBIG>(); else wait_vm_lgkm0<LPW>();                      \
+    __builtin_amdgcn_s_barrier();                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    const int bn_ = bufc == S - 1 ? 0 : bufc + 1;                                         \
+    HP_ISSUE((KT_) + 3, bufc);                                                            \
+    HP_READ(1 - (SET_), bn_);                                                             \
+    HP_MFMA(SET_);                                                                        \
+    mfma_interleave<0, 2 * TM * TN, 3 * (TM + TN), LPW>();                                \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    bufc = bn_;                                                                           \
+  } while (0)
+
+  v16f acc[TM][TN];
+  Frag6 af[2][TM], bf[2][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      acc[i][j] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+  HP_ISSUE(0, 0);
+  HP_ISSUE(1, 1);
+  HP_ISSUE(2, 2);
+  {
+    const __amdgpu_buffer_rsrc_t none = make_rsrc(ep.Y, 0);
+    const v4i z = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int q = 0; q < NST; ++q) __builtin_amdgcn_raw_buffer_store_b128(z, none, 16 * q, 0, 0);
+  }
+  params_dma_fixed<BM, BN, NW>(lds, wv, lane, cur.m0, cur.n0, M, N, ep);
+  wait_vm_lgkm0<2 * LPW + NST + PPW>();
+  __builtin_amdgcn_s_barrier();
+  HP_READ(0, 0);
+  for (;;) {
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+      HP_STEP(0, kt);
+      HP_STEP(1, kt + 1);
+    }
+    if (kt < KT) {
+      HP_STEP(0, kt);
+      // odd KT: the next tile's first fragments went to set 1
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[0][i] = af[1][i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[0][j] = bf[1][j];
+    }
+
+    // Epilogue: Y = acc s_x s_w + mu c + b (+ U L2), per 32-row slice of the
+    // wave's sub-tile, staged in the wave's LDS area.
+    {
+      // The lane index is passed through an empty asm statement so that the
+      // lane-dependent addresses below are formed per tile instead of being
+      // hoisted out of the tile loop (and held in registers across it).
+      int el = lane;
+      asm volatile("" : "+v"(el));
+      const int erow = el & 31, ehalf = el >> 5;
+      const float* const Pf = reinterpret_cast<const float*>(lds + pb * 4 * NP);
+      const int64_t mw = cur.m0 + wm0;
+      const int64_t rem = M - mw;
+      const int rows_v = rem <= 0 ? 0 : (rem < WM ? int(rem) : WM);
+      const int64_t cl = N - (cur.n0 + wn0);
+      const int ncols = cl <= 0 ? 0 : (cl < WN ? int(cl) : WN);  // valid columns of the wave
+      uint16_t* const ybase = static_cast<uint16_t*>(ep.Y) + mw * ep.ldy + (cur.n0 + wn0);
+      const __amdgpu_buffer_rsrc_t yr = make_rsrc(ybase, int(rows_v * ep.ldy * 2));
+      const int ypitch = int(ep.ldy * 2);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const float sx = Pf[3 * BN + wm0 + 32 * i + erow];
+        const float mu = Pf[3 * BN + BM + wm0 + 32 * i + erow];
+        // Low-rank term of slice i (all strips): one 32-rank chunk of U and
+        // L2 operands loaded before any product (see the tiled epilogue).
+        v16f lr[LR ? TN : 1];
+        if constexpr (LR) {
+          const int64_t m = mw + i * 32 + erow;
+          const int64_t mc = m < M ? m : M - 1;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) lr[j] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+          for (int kc = 0; kc < ep.rank; kc += 32) {
+            const bool two = kc + 16 < ep.rank;
+            float uf[2][8];
+            v8bf wh[TN][2], wl[TN][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int k0 = (h == 0 || two) ? kc + 16 * h : kc;
+              load8(ep.U + mc * ep.rank + k0 + 8 * ehalf, uf[h]);
+#pragma unroll
+              for (int j = 0; j < TN; ++j) {
+                const int64_t nb = cur.n0 + wn0 + j * 32;
+                const int64_t nr = nb + erow < N ? nb + erow : N - 1;
+                const int64_t off = nr * ep.rank + k0 + 8 * ehalf;
+                wh[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
+                wl[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
+              }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              if (h == 1 && !two) break;
+              const v8bf uh = pack_bf16x8(uf[h], false), ul = pack_bf16x8(uf[h], true);
+#pragma unroll
+              for (int j = 0; j < TN; ++j) {
+                lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[j][h], uh, lr[j], 0, 0, 0);
+                lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl[j][h], uh, lr[j], 0, 0, 0);
+                lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[j][h], ul, lr[j], 0, 0, 0);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          // Parameters are re-read from LDS per slice and column group (a
+          // compiler barrier keeps them from being held across the slices).
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int nl = wn0 + j * 32 + 8 * g + 4 * ehalf;
+            const float4 sw = make_float4(Pf[nl], Pf[nl+1], Pf[nl+2], Pf[nl+3]);
+            const float4 cb = make_float4(Pf[BN+nl], Pf[BN+nl+1], Pf[BN+nl+2], Pf[BN+nl+3]);
+            const float4 bb = make_float4(Pf[2*BN+nl], Pf[2*BN+nl+1], Pf[2*BN+nl+2], Pf[2*BN+nl+3]);
+            const v16f& a = acc[i][j];
+            float y0 = fmaf(a[4 * g + 0], sx * sw.x, fmaf(mu, cb.x, bb.x));
+            float y1 = fmaf(a[4 * g + 1], sx * sw.y, fmaf(mu, cb.y, bb.y));
+            float y2 = fmaf(a[4 * g + 2], sx * sw.z, fmaf(mu, cb.z, bb.z));
+            float y3 = fmaf(a[4 * g + 3], sx * sw.w, fmaf(mu, cb.w, bb.w));
+            if constexpr (LR) {
+              y0 += lr[j][4 * g + 0];
+              y1 += lr[j][4 * g + 1];
+              y2 += lr[j][4 * g + 2];
+              y3 += lr[j][4 * g + 3];
+            }
+            {
+              const uint32_t la = uint32_t(reinterpret_cast<uintptr_t>(stg + erow * SP + (j * 32 + 8 * g + 4 * ehalf) * 2));
+              const uint2 dv = make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+              asm volatile("ds_write_b64 %0, %1" :: "v"(la), "v"(dv) : "memory");
+            }
+          }
+        }
+        static_assert(SPS == 6, "six pieces per lane and slice");
+        uint32_t la[SPS];
+        uint32_t off[SPS];
+#pragma unroll
+        for (int s = 0; s < SPS; ++s) {
+          const int q = el + 64 * s, r = q / CPR, ch = q - r * CPR;
+          la[s] = uint32_t(reinterpret_cast<uintptr_t>(stg + r * SP + ch * 16));
+          const bool ok = ch * 8 < ncols;
+          off[s] = ok ? uint32_t((32 * i + r) * ypitch + ch * 16) : 0x80000000u;
+        }
+        v4i d0, d1, d2, d3, d4, d5;
+        asm volatile(
+            "ds_read2_b64 %0, %6 offset1:1\n"
+            "ds_read2_b64 %1, %7 offset1:1\n"
+            "ds_read2_b64 %2, %8 offset1:1\n"
+            "ds_read2_b64 %3, %9 offset1:1\n"
+            "ds_read2_b64 %4, %10 offset1:1\n"
+            "ds_read2_b64 %5, %11 offset1:1\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "=&v"(d4), "=&v"(d5)
+            : "v"(la[0]), "v"(la[1]), "v"(la[2]), "v"(la[3]), "v"(la[4]), "v"(la[5])
+            : "memory");
+        __builtin_amdgcn_raw_buffer_store_b128(d0, yr, off[0], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(d1, yr, off[1], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(d2, yr, off[2], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(d3, yr, off[3], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(d4, yr, off[4], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(d5, yr, off[5], 0, 0);
+      }
+    }
+    // The next tile's parameters go to the other buffer (nobody reads it:
+    // its last reader was the epilogue two tiles back).
+    pb ^= 1;
+    params_dma_fixed<BM, BN, NW>(lds + pb * 4 * NP, wv, lane, nxt.m0, nxt.n0, M, N, ep);
+
+    tile += G;
+    if (tile >= ntiles) break;
+    cur = nxt;
+    nxt = tile_src(tile + G);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  wait_vm_lgkm0<0>();  // no LDS write may land after the block ends
+#undef HP_STEP
+#undef HP_MFMA
+#undef HP_READ
+#undef HP_ISSUE
 }
 
 }  // namespace hq

@@ -180,23 +180,42 @@ __device__ __forceinline__ void gemm_epilogue_bf16_staged(AccT (&acc)[TM][TN], u
   for (int j = 0; j < TN; ++j) {
     v16f lr[LR ? TM : 1];
     if constexpr (LR) {
+      // Low-rank term of strip j for the wave's TM row slices, 32 ranks at a
+      // time: every U and L2 operand of a 32-rank chunk is loaded before the
+      // first is used (one memory round trip per chunk; the U loads do not
+      // depend on j). A missing second half (rank 16) reloads the first and
+      // skips its products.
       const int64_t nb = n0 + wn0 + j * 32;
       const int64_t nr = nb + lrow < N ? nb + lrow : N - 1;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int64_t m = m0 + wm0 + i * 32 + lrow;
-        const int64_t mc = m < M ? m : M - 1;
-        lr[i] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-        for (int k0 = 0; k0 < ep.rank; k0 += 16) {
-          float f[8];
-          load8(ep.U + mc * ep.rank + k0 + 8 * lhalf, f);
-          const v8bf uh = pack_bf16x8(f, false), ul = pack_bf16x8(f, true);
+      for (int i = 0; i < TM; ++i) lr[i] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      for (int kc = 0; kc < ep.rank; kc += 32) {
+        const bool two = kc + 16 < ep.rank;
+        float uf[TM][2][8];
+        v8bf wh[2], wl[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k0 = (h == 0 || two) ? kc + 16 * h : kc;
           const int64_t off = nr * ep.rank + k0 + 8 * lhalf;
-          const v8bf wh = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
-          const v8bf wl = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
-          lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, uh, lr[i], 0, 0, 0);
-          lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, uh, lr[i], 0, 0, 0);
-          lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, ul, lr[i], 0, 0, 0);
+          wh[h] = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
+          wl[h] = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const int64_t m = m0 + wm0 + i * 32 + lrow;
+            const int64_t mc = m < M ? m : M - 1;
+            load8(ep.U + mc * ep.rank + k0 + 8 * lhalf, uf[i][h]);
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 1 && !two) break;
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const v8bf uh = pack_bf16x8(uf[i][h], false), ul = pack_bf16x8(uf[i][h], true);
+            lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[h], uh, lr[i], 0, 0, 0);
+            lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl[h], uh, lr[i], 0, 0, 0);
+            lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[h], ul, lr[i], 0, 0, 0);
+          }
         }
       }
     }
