@@ -32,7 +32,12 @@ weight is passed as ``weight`` [d_out, d_in] (W = weight^T), b is [d_out].
 
 Readings taken where the pages leave a step open:
 
-* mu is one scalar per token (the mean over the d_in transformed channels).
+* mu is one scalar per token (the mean over the d_in transformed channels):
+  ``center`` 1 (or True). ``center`` 2 takes the other reading of the same
+  equation: mu is one vector over the channels, the mean over the T tokens of
+  the call of each transformed channel (HadaNorm Fig. 2 caption, "mu, sigma
+  in R^d"; "one added token"), and b~ = b + mu W~ is then a single corrected
+  bias for every token. ``center`` 0 (or False) leaves mu = 0.
 * sigma uses max(., 1e-5) on both maxima; X_i is input channel i over all
   tokens, W_i is input channel i over all outputs.
 * H is the normalised Sylvester matrix in natural order, applied per
@@ -62,6 +67,7 @@ from __future__ import annotations
 import numpy as np
 
 EPS = 1e-5
+CENTER_NONE, CENTER_TOKEN, CENTER_CHANNEL = 0, 1, 2
 
 
 # --------------------------------------------------------------------------
@@ -135,15 +141,24 @@ def transform_weights(weight: np.ndarray, sigma: np.ndarray, block: int):
 # Online: activation transform, centring, quantisation
 # --------------------------------------------------------------------------
 
-def transform_activations(x: np.ndarray, sigma: np.ndarray, block: int, center: bool):
+def transform_activations(x: np.ndarray, sigma: np.ndarray, block: int, center):
     """X~ = X diag(1/sigma) H - mu (HadaNorm Eq. (1)).
 
-    Returns (x', y, mu, x~) with x' = X / sigma, y = x' H, mu_t the mean of
-    row t of y (zero when centring is off) and x~ = y - mu.
+    Returns (x', y, mu, x~) with x' = X / sigma and y = x' H. ``center`` 1 /
+    True: mu_t is the mean of row t of y (one value per token) and
+    x~ = y - mu[:, None]; ``center`` 2: mu_i is the mean of column i of y
+    over the tokens (one value per channel) and x~ = y - mu[None, :];
+    ``center`` 0 / False: mu = 0 per token and x~ = y.
     """
     xp = np.asarray(x, dtype=np.float64) / np.asarray(sigma, dtype=np.float64)[None, :]
     y = rotate(xp, block)
-    mu = y.mean(axis=1) if center else np.zeros(y.shape[0])
+    mode = int(center)
+    if mode == CENTER_CHANNEL:
+        mu = y.mean(axis=0) if y.shape[0] else np.zeros(y.shape[1])
+        return xp, y, mu, y - mu[None, :]
+    if mode not in (CENTER_NONE, CENTER_TOKEN):
+        raise ValueError(f"center must be 0, 1 or 2, got {center}")
+    mu = y.mean(axis=1) if mode == CENTER_TOKEN else np.zeros(y.shape[0])
     return xp, y, mu, y - mu[:, None]
 
 
@@ -243,7 +258,14 @@ def prepare_weights(weight, sigma, block: int, w_bits: int):
     return {"wt": wt, "c": c, "qw": qw, "s_w": s_w}
 
 
-def quant_linear(x, prepared, bias, sigma, *, block: int, a_bits: int, center: bool,
+def channel_bias(bias, wt, mu_c) -> np.ndarray:
+    """b~ = b + mu W~ for a per-channel mu (HadaNorm Eq. (1), center = 2): W~ = wt^T,
+    so mu W~ is wt @ mu, one corrected bias shared by every token."""
+    return np.asarray(bias, dtype=np.float64) + np.asarray(wt, dtype=np.float64) @ np.asarray(
+        mu_c, dtype=np.float64)
+
+
+def quant_linear(x, prepared, bias, sigma, *, block: int, a_bits: int, center,
                  l1=None, l2=None, out_dtype: str = "f32"):
     """Online half for the rows of ``x``: transform, centre, quantise, integer GEMM, dequantise."""
     xp, y, mu, xt = transform_activations(x, sigma, block, center)
@@ -252,12 +274,19 @@ def quant_linear(x, prepared, bias, sigma, *, block: int, a_bits: int, center: b
     u = lr = None
     if l1 is not None:
         u, lr = low_rank(xp, l1, l2)
-    y_full = dequant_output(acc, s_x, prepared["s_w"], bias, mu, prepared["c"], lr)
+    if int(center) == CENTER_CHANNEL:
+        bias_eff = channel_bias(bias, prepared["wt"], mu)
+        y_full = dequant_output(acc, s_x, prepared["s_w"], bias_eff, np.zeros(len(xt)),
+                                prepared["c"], lr)
+    else:
+        bias_eff = np.asarray(bias, dtype=np.float64)
+        y_full = dequant_output(acc, s_x, prepared["s_w"], bias, mu, prepared["c"], lr)
     return {"xp": xp, "y": y, "mu": mu, "xt": xt, "qa": qa, "s_x": s_x, "acc": acc,
-            "u": u, "lr": lr, "y_full": y_full, "y_out": round_to_dtype(y_full, out_dtype)}
+            "u": u, "lr": lr, "bias_eff": bias_eff, "y_full": y_full,
+            "y_out": round_to_dtype(y_full, out_dtype)}
 
 
-def run(x, weight, bias, *, block: int, a_bits: int, w_bits: int, center: bool,
+def run(x, weight, bias, *, block: int, a_bits: int, w_bits: int, center,
         sigma=None, l1=None, l2=None, out_dtype: str = "f32"):
     """Prepare + quant_linear in one call; sigma defaults to ones."""
     d_in = np.asarray(x).shape[1]

@@ -197,6 +197,78 @@ def test_full_rotation_mu_c_is_channel_zero_product():
     np.testing.assert_allclose(mu[:, None] * c[None, :], np.outer(x[:, 0], weight[:, 0]), rtol=1e-11)
 
 
+# ---------------------------------------------------------------- per-channel centring (center = 2)
+
+@pytest.mark.parametrize("name", ["dit_fc1", "square4k", "lic_dh", "flux_proj"])
+def test_channel_centring_columns_sum_to_zero(name):
+    # mu is the per-channel mean over the tokens, so every column of X~ sums to 0
+    w, x, weight, bias, l1, l2, sigma = _sample_inputs(name, rows=64)
+    xp, y, mu, xt = O.transform_activations(x, sigma, w.block, O.CENTER_CHANNEL)
+    assert mu.shape == (w.d_in,)
+    assert np.all(np.abs(xt.sum(axis=0)) <= 1e-12 * (np.abs(y).sum(axis=0) + 1e-300))
+
+
+@pytest.mark.parametrize("name", ["dit_fc1", "square4k"])
+def test_channel_mean_is_rotated_input_mean(name):
+    # linearity of Eq. (1): mean_t(X' H) = (mean_t X') H, built from the plain column
+    # mean and a dense block-diagonal H (scipy) rather than the oracle's rotate
+    w, x, weight, bias, l1, l2, sigma = _sample_inputs(name, rows=48)
+    xp, y, mu, xt = O.transform_activations(x, sigma, w.block, O.CENTER_CHANNEL)
+    m = (np.asarray(x, np.float64) / sigma).mean(axis=0)
+    hb = scipy.linalg.hadamard(w.block).astype(np.float64) / np.sqrt(w.block)
+    dense = (m.reshape(-1, w.block) @ hb).reshape(-1)
+    np.testing.assert_allclose(mu, dense, rtol=1e-10, atol=1e-13 * np.abs(dense).max())
+
+
+@pytest.mark.parametrize("name", WL.ORDER)
+def test_channel_identity_float64(name):
+    # HadaNorm Eq. (1) with a per-channel mu: X~ W~ + b + mu W~ = X W + b exactly
+    w, x, weight, bias, l1, l2, sigma = _sample_inputs(name, rows=16)
+    xp, y, mu, xt = O.transform_activations(x, sigma, w.block, O.CENTER_CHANNEL)
+    wt, c = O.transform_weights(weight, sigma, w.block)
+    got = xt @ wt.T + O.channel_bias(bias, wt, mu)[None, :]
+    if l1 is not None:
+        got = got + O.low_rank(xp, l1, l2)[1]
+    ref = O.exact_output(x, weight, bias, xp, l1, l2)
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert err <= 1e-12, err
+
+
+@pytest.mark.parametrize("name", ["dit_fc1", "square4k", "lic_dh"])
+def test_channel_bias_is_mean_token_through_weight(name):
+    # mu W~ = m_X W (H H^T = I, diag(sigma) diag(1/sigma) = I): the correction is the
+    # original layer applied to the mean token -- the "one added token"
+    w, x, weight, bias, l1, l2, sigma = _sample_inputs(name, rows=32)
+    xp, y, mu, xt = O.transform_activations(x, sigma, w.block, O.CENTER_CHANNEL)
+    wt, c = O.transform_weights(weight, sigma, w.block)
+    ref = np.asarray(weight, np.float64) @ np.asarray(x, np.float64).mean(axis=0)
+    np.testing.assert_allclose(O.channel_bias(bias, wt, mu) - bias, ref, rtol=1e-10,
+                               atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_channel_centring_equal_tokens(T):
+    # identical tokens centre to zero: every code and scale is 0 and the output is
+    # the unquantised layer b + x W itself (T a power of two, so the float64 mean
+    # of T equal values is that value exactly)
+    rng = np.random.default_rng(17)
+    row = rng.standard_normal(256) * rng.uniform(0.1, 20, 256)
+    x = np.tile(row, (T, 1))
+    weight = rng.standard_normal((24, 256))
+    bias = rng.standard_normal(24)
+    sigma = rng.uniform(0.5, 2.0, 256)
+    out = O.run(x, weight, bias, block=64, a_bits=4, w_bits=4, center=O.CENTER_CHANNEL,
+                sigma=sigma)
+    assert not out["qa"].any() and not out["s_x"].any()
+    np.testing.assert_allclose(out["y_full"], O.exact_output(x, weight, bias), rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_center_mode_rejected():
+    with pytest.raises(ValueError):
+        O.transform_activations(np.ones((2, 8)), np.ones(8), 8, 3)
+
+
 # ---------------------------------------------------------------- quantiser
 
 @pytest.mark.parametrize("bits", [4, 8])
