@@ -20,8 +20,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (HQ_CODES_E2M3, HQ_CODES_I8, HQ_GEMM_AUTO, HQ_GEMM_I8, HqDesc, HqError,
-                   HqLayout, check, load)
+from ._lib import (HQ_CENTER_CHANNEL, HQ_CENTER_NONE, HQ_CENTER_TOKEN, HQ_CODES_E2M3,
+                   HQ_CODES_I8, HQ_GEMM_AUTO, HQ_GEMM_I8, HqDesc, HqError, HqLayout, check, load)
 
 F32, BF16 = 0, 1
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16}
@@ -30,13 +30,14 @@ _NAME = {F32: "f32", BF16: "bf16"}
 
 @dataclasses.dataclass(frozen=True)
 class Desc:
-    """Layer descriptor; mirrors hq_desc."""
+    """Layer descriptor; mirrors hq_desc. ``center``: 0 / False none, 1 / True
+    per-token mean, 2 per-channel mean over the call's tokens (HQ_CENTER_*)."""
     d_in: int
     d_out: int
     block: int
     a_bits: int = 4
     w_bits: int = 4
-    center: bool = True
+    center: int = HQ_CENTER_TOKEN
     smooth: bool = False
     rank: int = 0
     x_dtype: int = F32
@@ -190,37 +191,70 @@ def quant_linear(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
     return out
 
 
-def act_quantize(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, out=None):
+def _channel(desc: Desc) -> bool:
+    return int(desc.center) == HQ_CENTER_CHANNEL
+
+
+def channel_center(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
+                   workspace: Optional[torch.Tensor] = None):
+    """Per-channel centring statistics of X (center = 2): (mean [d_in] =
+    mean_t(X), bias_eff [d_out_pad] = b + mean_t(X) W)."""
+    T = X.shape[0]
+    _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
+    mean = torch.empty(desc.d_in, dtype=torch.float32, device=X.device)
+    bias_eff = torch.empty(layout(desc).d_out_pad, dtype=torch.float32, device=X.device)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(desc, T), 1), dtype=torch.uint8,
+                                device=X.device)
+    check(load().hq_channel_center(desc._ref, _ptr(prepared), _ptr(X), T, _ptr(mean),
+                                   _ptr(bias_eff), _ptr(workspace), workspace.numel(),
+                                   _stream()))
+    return mean, bias_eff
+
+
+def act_quantize(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, out=None, mean=None):
     """Activation stage alone: (codes, s_x [T], mu [T], U [T, rank] or None).
 
     ``codes`` is a uint8 buffer of code_bytes(desc, T) bytes in the
-    descriptor's code format. ``out`` may supply that tuple preallocated."""
+    descriptor's code format. ``out`` may supply that tuple preallocated.
+    For center = 2 the third entry is the per-channel mean [d_in] that was
+    subtracted (``mean`` if given, else channel_center's)."""
     T = X.shape[0]
     _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
     dev = X.device
+    chan = _channel(desc)
+    if chan and mean is None:
+        mean = channel_center(desc, prepared, X)[0]
     if out is None:
         codes = torch.empty(max(code_bytes(desc, T), 1), dtype=torch.uint8, device=dev)
         s_x = torch.empty(T, dtype=torch.float32, device=dev)
-        mu = torch.empty(T, dtype=torch.float32, device=dev)
+        mu = mean if chan else torch.empty(T, dtype=torch.float32, device=dev)
         U = torch.empty(T, desc.rank, dtype=torch.float32, device=dev) if desc.rank else None
     else:
         codes, s_x, mu, U = out
+        if chan:
+            mu = mean
         _need_codes(codes, "codes", desc, T)
         _need(s_x, "s_x", torch.float32, (T,))
-        _need(mu, "mu", torch.float32, (T,))
         if desc.rank:
             _need(U, "U", torch.float32, (T, desc.rank))
+    _need(mu, "mu", torch.float32, (desc.d_in,) if chan else (T,))
     check(load().hq_act_quantize(desc._ref, _ptr(prepared), _ptr(X), T, _ptr(codes),
                                  _ptr(s_x), _ptr(mu), _ptr(U), _stream()))
     return codes, s_x, mu, U
 
 
-def act_transform(desc: Desc, prepared: torch.Tensor, X: torch.Tensor):
-    """Float X~ (normalised H, centred) and mu, before quantisation (debug export)."""
+def act_transform(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, mean=None):
+    """Float X~ (normalised H, centred) and mu, before quantisation (debug export).
+    For center = 2 the second entry is the per-channel mean that was subtracted."""
     T = X.shape[0]
     _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
     xt = torch.empty(T, desc.d_in, dtype=torch.float32, device=X.device)
-    mu = torch.empty(T, dtype=torch.float32, device=X.device)
+    if _channel(desc):
+        mu = mean if mean is not None else channel_center(desc, prepared, X)[0]
+        _need(mu, "mean", torch.float32, (desc.d_in,))
+    else:
+        mu = torch.empty(T, dtype=torch.float32, device=X.device)
     check(load().hq_act_transform(desc._ref, _ptr(prepared), _ptr(X), T, _ptr(xt),
                                   _ptr(mu), _stream()))
     return xt, mu
@@ -241,11 +275,12 @@ def gemm_i32(desc: Desc, a_codes: torch.Tensor, w_codes: torch.Tensor, T: int,
 def gemm_dequant(desc: Desc, prepared: torch.Tensor, codes: torch.Tensor, s_x: torch.Tensor,
                  mu: torch.Tensor, U: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """GEMM + dequant epilogue alone, from act_quantize's outputs (T = len(s_x))."""
+    """GEMM + dequant epilogue alone, from act_quantize's outputs (T = len(s_x)).
+    For center = 2, ``mu`` is channel_center's bias_eff [d_out_pad]."""
     T = s_x.shape[0]
     _need_codes(codes, "codes", desc, T)
     _need(s_x, "s_x", torch.float32, (T,))
-    _need(mu, "mu", torch.float32, (T,))
+    _need(mu, "mu", torch.float32, (layout(desc).d_out_pad,) if _channel(desc) else (T,))
     if desc.rank:
         _need(U, "U", torch.float32, (T, desc.rank))
     Y = out if out is not None else torch.empty(T, desc.d_out, dtype=_TORCH[desc.y_dtype],
@@ -273,4 +308,6 @@ def prepared_views(desc: Desc, prepared: torch.Tensor) -> dict:
         "bias": view(L.bias, npad, torch.float32, (npad,))[:desc.d_out],
         "sigma_inv": view(L.sigma_inv, d, torch.float32, (d,)),
     }
+    if _channel(desc):
+        out["weight"] = view(L.weight, desc.d_out * d, _TORCH[desc.w_dtype], (desc.d_out, d))
     return out

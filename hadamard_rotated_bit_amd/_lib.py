@@ -20,11 +20,12 @@ class HqDesc(ctypes.Structure):
 class HqLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ["total", "w_codes", "w_scale", "c", "bias", "sigma_inv", "l1_hi", "l1_lo",
-                 "l2_hi", "l2_lo"]] + [("d_out_pad", ctypes.c_int64)]
+                 "l2_hi", "l2_lo", "weight"]] + [("d_out_pad", ctypes.c_int64)]
 
 
 HQ_CODES_I8, HQ_CODES_E2M3 = 0, 1
 HQ_GEMM_AUTO, HQ_GEMM_I8 = 0, 1
+HQ_CENTER_NONE, HQ_CENTER_TOKEN, HQ_CENTER_CHANNEL = 0, 1, 2
 
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_BAD_PREPARED, \
     HQ_ERR_HIP = 0, -1, -2, -3, -4, -5
@@ -47,6 +48,7 @@ _SIGS = {
     "hq_prepare_weights": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P]),
     "hq_check_prepared": (ctypes.c_int, [_D, _P, _P]),
     "hq_quant_linear": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "hq_channel_center": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "hq_act_quantize": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, _P, _P, _P]),
     "hq_act_transform": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, _P]),
     "hq_gemm_i32": (ctypes.c_int, [_D, _P, _P, _I64, _I64, _P, _P]),

@@ -64,8 +64,8 @@ int check_desc(const hq_desc* d) {
     return fail(HQ_ERR_INVALID_ARG, "y_dtype %d is not an hq_dtype", d->y_dtype);
   if (d->gemm != HQ_GEMM_AUTO && d->gemm != HQ_GEMM_I8)
     return fail(HQ_ERR_INVALID_ARG, "gemm %d is not an hq_gemm_engine", d->gemm);
-  if (d->center != 0 && d->center != 1)
-    return fail(HQ_ERR_INVALID_ARG, "center must be 0 or 1 (got %d)", d->center);
+  if (d->center != HQ_CENTER_NONE && d->center != HQ_CENTER_TOKEN && d->center != HQ_CENTER_CHANNEL)
+    return fail(HQ_ERR_INVALID_ARG, "center must be 0, 1 or 2 (got %d)", d->center);
   if (d->smooth != 0 && d->smooth != 1)
     return fail(HQ_ERR_INVALID_ARG, "smooth must be 0 or 1 (got %d)", d->smooth);
   if (d->a_bits != 4 && d->a_bits != 8)
@@ -119,14 +119,21 @@ void layout_of(const hq_desc* d, hq_prepared_layout* L) {
   off += align256(2 * size_t(np) * d->rank);
   L->l2_lo = off;
   off += align256(2 * size_t(np) * d->rank);
+  L->weight = 0;
+  if (d->center == HQ_CENTER_CHANNEL) {
+    L->weight = off;
+    off += align256(size_t(d->w_dtype == HQ_BF16 ? 2 : 4) * size_t(d->d_out) * d->d_in);
+  }
   L->total = off;
 }
 
 struct Workspace {
-  size_t codes, s_x, mu, U, total;
+  size_t codes, s_x, mu, U;
+  size_t partial, mean, bias_eff;  // center = 2 only
+  size_t total;
 };
 Workspace workspace_of(const hq_desc* d, int64_t T) {
-  Workspace w;
+  Workspace w = {};
   size_t off = 0;
   w.codes = off;
   off += align256(hq::code_bytes(code_fmt_of(d), T, d->d_in));
@@ -136,6 +143,14 @@ Workspace workspace_of(const hq_desc* d, int64_t T) {
   off += align256(4 * size_t(T));
   w.U = off;
   off += align256(4 * size_t(T) * d->rank);
+  if (d->center == HQ_CENTER_CHANNEL) {
+    w.partial = off;
+    off += align256(4 * size_t(hq::center_chunks(T > 0 ? T : 1)) * d->d_in);
+    w.mean = off;
+    off += align256(4 * size_t(d->d_in));
+    w.bias_eff = off;
+    off += align256(4 * size_t(round_up(d->d_out, hq::GEMM_BN)));
+  }
   w.total = off;
   return w;
 }
@@ -149,9 +164,26 @@ inline const P* at(const void* base, size_t off) {
   return reinterpret_cast<const P*>(static_cast<const uint8_t*>(base) + off);
 }
 
-// Activation stage shared by hq_quant_linear and hq_act_quantize.
+// Per-channel centring statistics of the T rows of X (center = 2): mean
+// [d_in] = mean_t X, subtracted by the row transform, and bias_eff
+// [d_out_pad] = b + weight . mean, the corrected bias of the GEMM epilogue.
+int run_center(const hq_desc* d, const void* prepared, const void* X, int64_t T, float* partial,
+               float* mean, float* bias_eff, hipStream_t s) {
+  hq_prepared_layout L;
+  layout_of(d, &L);
+  hipError_t e = hq::launch_channel_mean(X, d->x_dtype == HQ_BF16, T, d->d_in, partial, mean, s);
+  if (e == hipSuccess)
+    e = hq::launch_bias_gemv(at<uint8_t>(prepared, L.weight), d->w_dtype == HQ_BF16, mean,
+                             at<float>(prepared, L.bias), d->d_out, int(L.d_out_pad), d->d_in,
+                             bias_eff, s);
+  return e == hipSuccess ? HQ_OK : hip_fail(e, "centring kernel launch");
+}
+
+// Activation stage shared by hq_quant_linear and hq_act_quantize. For
+// center = 2, `cmean` is the per-channel mean and `mu` (per-token) is NULL;
+// otherwise cmean is NULL and mu gets the per-token means.
 int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, void* codes,
-            float* s_x, float* mu, float* U, hipStream_t s) {
+            float* s_x, float* mu, const float* cmean, float* U, hipStream_t s) {
   hq_prepared_layout L;
   layout_of(d, &L);
   hq::RowArgs a = {};
@@ -160,8 +192,9 @@ int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, vo
   a.rows = T;
   a.d = d->d_in;
   a.scale = d->smooth ? at<float>(prepared, L.sigma_inv) : nullptr;
+  a.chan_mean = cmean;
   a.log2b = log2i(d->block);
-  a.center = d->center;
+  a.center = d->center == HQ_CENTER_TOKEN;
   a.qmax = qmax_of(d->a_bits);
   a.codes = static_cast<uint8_t*>(codes);
   a.code_fmt = code_fmt_of(d);
@@ -190,17 +223,21 @@ hipError_t launch_codes_gemm(const hq_desc* d, const void* a_codes, int64_t T, c
                          static_cast<const int8_t*>(w_codes), N, d->d_in, acc, ldc, ep, s);
 }
 
+// GEMM + epilogue. For center = 2 `mu` is the corrected bias [d_out_pad]
+// (b + weight . mean) and replaces b; the prepared c is zero in that mode, so
+// the per-token term vanishes (s_x stands in for the per-token vector).
 int run_gemm_dequant(const hq_desc* d, const void* prepared, const void* codes,
                      const float* s_x, const float* mu, const float* U, int64_t T, void* Y,
                      hipStream_t s) {
   hq_prepared_layout L;
   layout_of(d, &L);
+  const bool chan = d->center == HQ_CENTER_CHANNEL;
   hq::GemmEpi ep = {};
   ep.s_x = s_x;
-  ep.mu = mu;
+  ep.mu = chan ? s_x : mu;
   ep.s_w = at<float>(prepared, L.w_scale);
   ep.c = at<float>(prepared, L.c);
-  ep.bias = at<float>(prepared, L.bias);
+  ep.bias = chan ? mu : at<float>(prepared, L.bias);
   ep.U = U;
   ep.l2_hi = at<uint16_t>(prepared, L.l2_hi);
   ep.l2_lo = at<uint16_t>(prepared, L.l2_lo);
@@ -358,10 +395,15 @@ int hq_prepare_weights(const hq_desc* desc, const void* weight, const float* bia
     a.codes = at<uint8_t>(prepared, L.w_codes);
     a.code_fmt = fmt;
     a.out_s = at<float>(prepared, L.w_scale);
-    a.out_aux = at<float>(prepared, L.c);
+    // c = 1^T W~ (the per-token correction); zero under per-channel centring,
+    // whose correction is the per-call bias instead.
+    a.out_aux = desc->center != HQ_CENTER_CHANNEL ? at<float>(prepared, L.c) : nullptr;
     a.mode = hq::ROW_WEIGHT;
     e = hq::launch_row_transform(a, s);
   }
+  if (e == hipSuccess && desc->center == HQ_CENTER_CHANNEL)
+    e = hq::launch_copy_f32(static_cast<const float*>(weight), at<float>(prepared, L.weight),
+                            size_t(desc->w_dtype == HQ_BF16 ? 2 : 4) * size_t(dout) * din / 4, s);
   if (e == hipSuccess && desc->rank) {
     e = hq::launch_prep_l1(L1, desc->w_dtype == HQ_BF16,
                            desc->smooth ? at<float>(prepared, L.sigma_inv) : nullptr, int(din),
@@ -422,9 +464,37 @@ int hq_quant_linear(const hq_desc* desc, const void* prepared, const void* X, in
   float* s_x = at<float>(workspace, w.s_x);
   float* mu = at<float>(workspace, w.mu);
   float* U = desc->rank ? at<float>(workspace, w.U) : nullptr;
-  st = run_act(desc, prepared, X, T, codes, s_x, mu, U, s);
+  if (desc->center == HQ_CENTER_CHANNEL) {
+    float* cmean = at<float>(workspace, w.mean);
+    float* bias_eff = at<float>(workspace, w.bias_eff);
+    st = run_center(desc, prepared, X, T, at<float>(workspace, w.partial), cmean, bias_eff, s);
+    if (st == HQ_OK) st = run_act(desc, prepared, X, T, codes, s_x, nullptr, cmean, U, s);
+    if (st != HQ_OK) return st;
+    return run_gemm_dequant(desc, prepared, codes, s_x, bias_eff, U, T, Y, s);
+  }
+  st = run_act(desc, prepared, X, T, codes, s_x, mu, nullptr, U, s);
   if (st != HQ_OK) return st;
   return run_gemm_dequant(desc, prepared, codes, s_x, mu, U, T, Y, s);
+}
+
+int hq_channel_center(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
+                      float* mean, float* bias_eff, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  if (desc->center != HQ_CENTER_CHANNEL)
+    return fail(HQ_ERR_INVALID_ARG, "hq_channel_center needs center = 2 (got %d)", desc->center);
+  if (T <= 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 1 (got %lld)", (long long)T);
+  if (!prepared || !X || !mean || !bias_eff || !workspace)
+    return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (misaligned(X) || misaligned(workspace) || misaligned(prepared))
+    return fail(HQ_ERR_INVALID_ARG, "X, workspace and prepared must be 16-byte aligned");
+  const Workspace w = workspace_of(desc, T);
+  if (workspace_bytes < w.total)
+    return fail(HQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, w.total);
+  return run_center(desc, prepared, X, T, at<float>(workspace, w.partial), mean, bias_eff,
+                    static_cast<hipStream_t>(stream));
 }
 
 int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
@@ -436,7 +506,9 @@ int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, in
   if (T == 0) return HQ_OK;
   if (!prepared || !X || !codes || !s_x || !mu || (desc->rank && !U))
     return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
-  return run_act(desc, prepared, X, T, codes, s_x, mu, U, static_cast<hipStream_t>(stream));
+  const bool chan = desc->center == HQ_CENTER_CHANNEL;
+  return run_act(desc, prepared, X, T, codes, s_x, chan ? nullptr : mu, chan ? mu : nullptr, U,
+                 static_cast<hipStream_t>(stream));
 }
 
 int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
@@ -456,9 +528,11 @@ int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, i
   a.d = desc->d_in;
   a.scale = desc->smooth ? at<float>(prepared, L.sigma_inv) : nullptr;
   a.log2b = log2i(desc->block);
-  a.center = desc->center;
+  const bool chan = desc->center == HQ_CENTER_CHANNEL;
+  a.chan_mean = chan ? mu : nullptr;
+  a.center = desc->center == HQ_CENTER_TOKEN;
   a.qmax = qmax_of(desc->a_bits);
-  a.out_aux = mu;
+  a.out_aux = chan ? nullptr : mu;
   a.out_xt = Xt;
   a.mode = hq::ROW_EXPORT;
   hipError_t e = hq::launch_row_transform(a, static_cast<hipStream_t>(stream));

@@ -82,22 +82,35 @@ __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv
   const int d = a.d;
   const TIn* src = static_cast<const TIn*>(a.in) + r * d + t * 8;
 
+  // Per-channel multiplier and mean first: loads retire in issue order, so
+  // issuing them after the row would make the first chunk wait for all of it.
+  float sc[E], sh[E];
+  if (a.scale) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) load8(a.scale + c * 8 * G + t * 8, &sc[c * 8]);
+  }
+  if (a.chan_mean) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) load8(a.chan_mean + c * 8 * G + t * 8, &sh[c * 8]);
+  }
   float v[E];
 #pragma unroll
   for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
 
   // Chunk by chunk (so work on chunk c can start as soon as its load lands):
-  // channel scaling, then the butterflies on channel bits 0..2 (in
-  // registers) and 3 .. 3+log2G-1 (across lanes, on the VALU; the lower
+  // per-channel centring and scaling, then the butterflies on channel bits 0..2
+  // (in registers) and 3 .. 3+log2G-1 (across lanes, on the VALU; the lower
   // partner keeps x+y, the upper x-y).
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     float* vc = &v[c * 8];
-    if (a.scale) {
-      float s[8];
-      load8(a.scale + c * 8 * G + t * 8, s);
+    if (a.chan_mean) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vc[j] *= s[j];
+      for (int j = 0; j < 8; ++j) vc[j] -= sh[c * 8 + j];
+    }
+    if (a.scale) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vc[j] *= sc[c * 8 + j];
     }
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
@@ -162,7 +175,7 @@ __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv
       store_codes<G, C>(a, row, base, t, v, rcp);
       if (t == 0) {
         a.out_s[row] = amax * inv_sqrt_b / a.qmax;
-        a.out_aux[row] = sum * inv_sqrt_b;
+        if (a.out_aux) a.out_aux[row] = sum * inv_sqrt_b;
       }
     }
     return;
@@ -188,7 +201,7 @@ __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv
             make_float4(v[c * 8 + 4] * inv_sqrt_b, v[c * 8 + 5] * inv_sqrt_b,
                         v[c * 8 + 6] * inv_sqrt_b, v[c * 8 + 7] * inv_sqrt_b);
       }
-      if (t == 0) a.out_aux[row] = mu * inv_sqrt_b;
+      if (t == 0 && a.out_aux) a.out_aux[row] = mu * inv_sqrt_b;
     }
     return;
   }
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv
     store_codes<G, C>(a, row, base, t, v, rcp);
     if (t == 0) {
       a.out_s[row] = amax * inv_sqrt_b / a.qmax;
-      a.out_aux[row] = mu * inv_sqrt_b;
+      if (a.out_aux) a.out_aux[row] = mu * inv_sqrt_b;
     }
   }
 }

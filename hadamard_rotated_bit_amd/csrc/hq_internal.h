@@ -37,13 +37,15 @@ struct RowArgs {
   int64_t rows;
   int d;
   const float* scale;     // per-channel multiplier (1/sigma or sigma); NULL = ones
+  const float* chan_mean; // per-channel value subtracted before the multiplier
+                          // (per-channel centring); NULL = none
   int log2b;
   int center;
   float qmax;
   uint8_t* codes;         // rows x d codes in code_fmt (ACT, WEIGHT)
   int code_fmt;           // CodeFmt
   float* out_s;           // [rows] dequant scale  (ACT, WEIGHT)
-  float* out_aux;         // [rows] mu (ACT, EXPORT) or c (WEIGHT)
+  float* out_aux;         // [rows] mu (ACT, EXPORT) or c (WEIGHT); NULL = not written
   float* out_xt;          // [rows, d] f32         (EXPORT)
   int mode;
 };
@@ -78,6 +80,16 @@ hipError_t launch_prep_l2(const void* l2, int bf16, int r, int n, int n_pad, uin
 hipError_t launch_lowrank_down(const void* x, int x_bf16, int64_t rows, int d, int r,
                                const uint16_t* l1_hi, const uint16_t* l1_lo, float* U,
                                hipStream_t s);
+
+// Per-channel centring (center = 2): partial column sums over chunks of
+// CENTER_RPC rows, then mean [d]; partial holds center_chunks(rows) x d floats.
+constexpr int CENTER_RPC = 64;
+int center_chunks(int64_t rows);
+hipError_t launch_channel_mean(const void* x, int x_bf16, int64_t rows, int d, float* partial,
+                               float* mean, hipStream_t s);
+// out [n_pad] = bias + weight [n, d] . mean (rows n..n_pad-1: bias).
+hipError_t launch_bias_gemv(const void* weight, int w_bf16, const float* mean, const float* bias,
+                            int n, int n_pad, int d, float* out, hipStream_t s);
 
 struct GemmEpi {
   const float* s_x;       // [M]

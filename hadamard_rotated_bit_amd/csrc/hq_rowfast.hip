@@ -102,6 +102,18 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
   const int d = a.d;
   const TIn* src = static_cast<const TIn*>(a.in) + r * d + t * 8;
 
+  // The channel multipliers (and means) go first: loads retire in issue
+  // order, so issued after the row they would make the first chunk wait for
+  // the whole row.
+  float sc[E], sh[E];
+  if (a.scale) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) load8(a.scale + c * 8 * G + t * 8, &sc[c * 8]);
+  }
+  if (a.chan_mean) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) load8(a.chan_mean + c * 8 * G + t * 8, &sh[c * 8]);
+  }
   float v[E];
 #pragma unroll
   for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
@@ -114,11 +126,13 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     float* vc = &v[c * 8];
-    if (a.scale) {
-      float s[8];
-      load8(a.scale + c * 8 * G + t * 8, s);
+    if (a.chan_mean) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vc[j] *= s[j];
+      for (int j = 0; j < 8; ++j) vc[j] -= sh[c * 8 + j];
+    }
+    if (a.scale) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vc[j] *= sc[c * 8 + j];
     }
     // channel bits 0..2, in registers
 #pragma unroll
@@ -183,7 +197,7 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
         reinterpret_cast<float4*>(o + c * 8 * G)[1] =
             make_float4(vc[4] * sc, vc[5] * sc, vc[6] * sc, vc[7] * sc);
       }
-      if (t == 0) a.out_aux[row] = mu * inv_sqrt_b;
+      if (t == 0 && a.out_aux) a.out_aux[row] = mu * inv_sqrt_b;
     }
     return;
   }
@@ -230,7 +244,7 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
   }
   if (t == 0) {
     a.out_s[row] = amax * inv_sqrt_b / a.qmax;
-    a.out_aux[row] = (weight ? sum : mu) * inv_sqrt_b;
+    if (a.out_aux) a.out_aux[row] = (weight ? sum : mu) * inv_sqrt_b;
   }
 }
 

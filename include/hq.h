@@ -23,6 +23,18 @@
  * The optional rank-r branch (blog steps 3-4) is kept in 16-bit and sees the
  * smoothed, un-rotated input x'.
  *
+ * Centring modes (hq_desc.center). HQ_CENTER_TOKEN reads mu as above, one
+ * mean per token. HQ_CENTER_CHANNEL takes the other reading of the same
+ * identity (HadaNorm Fig. 2 caption: "mu, sigma in R^d"; "one added token"):
+ * mu is the mean over the T tokens of one call of each channel of
+ * X diag(1/sigma) H, i.e. (mean_t X) diag(1/sigma) H, and the correction
+ * mu W~ = (mean_t X) W is a single vector, so
+ *
+ *     Y_tj = s_x,t s_w,j acc_tj + b~_j,   b~ = b + (mean_t X) W
+ *
+ * (c is zero in this mode). The mean is taken over the rows of each call, so
+ * a token's codes depend on the other tokens of the same call.
+ *
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers unless the comment says (host).
  *  - ``stream`` is a hipStream_t (NULL = the default stream). All GPU work is
@@ -67,7 +79,7 @@
 extern "C" {
 #endif
 
-#define HQ_ABI_VERSION 3
+#define HQ_ABI_VERSION 4
 
 typedef enum {
   HQ_OK = 0,
@@ -88,6 +100,9 @@ typedef enum { HQ_CODES_I8 = 0, HQ_CODES_E2M3 = 1 } hq_code_format_t;
  * accumulation. Both return identical accumulators. */
 typedef enum { HQ_GEMM_AUTO = 0, HQ_GEMM_I8 = 1 } hq_gemm_engine;
 
+/* Centring of X~ (see "Centring modes" above). */
+typedef enum { HQ_CENTER_NONE = 0, HQ_CENTER_TOKEN = 1, HQ_CENTER_CHANNEL = 2 } hq_center_mode;
+
 /* Layer descriptor (plain data, passed by host pointer).
  *  d_in    input channels: a multiple of 128 up to 2048, of 256 up to 4096,
  *          or of 512 up to 8192.
@@ -95,7 +110,9 @@ typedef enum { HQ_GEMM_AUTO = 0, HQ_GEMM_I8 = 1 } hq_gemm_engine;
  *  block   Hadamard block size: a power of two dividing d_in (1 = no rotation).
  *  a_bits  activation code width: 4 or 8.
  *  w_bits  weight code width: 4 or 8.
- *  center  1: subtract the per-token mean mu (HadaNorm centring); 0: mu = 0.
+ *  center  hq_center_mode: 1 subtract the per-token mean mu (HadaNorm
+ *          centring); 2 subtract the per-channel mean over the call's
+ *          tokens; 0 mu = 0.
  *  smooth  1: channel smoothing with the sigma given to hq_prepare_weights;
  *          0: sigma == 1 (no scaling pass over X).
  *  rank    low-rank branch rank: 0 (off) or a multiple of 16 up to 64.
@@ -122,6 +139,8 @@ typedef struct {
   size_t l1_lo;        /* bf16  [rank, d_in]       lo part (residual)           */
   size_t l2_hi;        /* bf16  [d_out_pad, rank]  hi part of L2^T              */
   size_t l2_lo;        /* bf16  [d_out_pad, rank]  lo part                      */
+  size_t weight;       /* w_dtype [d_out, d_in]    copy of weight (center = 2
+                          only, for b~ = b + (mean_t X) W; 0 otherwise)     */
   int64_t d_out_pad;   /* d_out rounded up to the GEMM column tile              */
 } hq_prepared_layout;
 
@@ -195,15 +214,27 @@ int hq_quant_linear(const hq_desc* desc, const void* prepared, const void* X, in
 
 /* ---- Stage entry points (the same kernels, for testing and profiling) ---- */
 
+/* Per-channel centring statistics (center = 2 only; T >= 1): over the T rows
+ * of X, mean f32 [d_in] = mean_t X (the activation stage subtracts it from
+ * every token before the channel scaling and the rotation, which yields the
+ * same X~ as subtracting mu after them) and bias_eff f32 [d_out_pad] =
+ * b + (mean_t X) W (the corrected bias; padding entries 0). Both are summed in
+ * a fixed order. workspace: at least hq_workspace_bytes(desc, T) bytes. */
+int hq_channel_center(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
+                      float* mean, float* bias_eff, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 /* Activation stage alone: codes of T rows in the descriptor's code format
  * (hq_code_bytes(desc, T) bytes, natural channel order), s_x f32 [T]
  * (dequant scale of the normalised X~ row), mu f32 [T], U f32 [T, rank]
- * (x' L1; ignored/NULL when rank = 0). */
+ * (x' L1; ignored/NULL when rank = 0). For center = 2, mu is instead an
+ * INPUT: the mean [d_in] of hq_channel_center. */
 int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
                     void* codes, float* s_x, float* mu, float* U, void* stream);
 
 /* Debug export of the float transform before quantisation:
- * Xt f32 [T, d_in] = X~ (normalised H, centred if desc->center), mu f32 [T]. */
+ * Xt f32 [T, d_in] = X~ (normalised H, centred if desc->center), mu f32 [T].
+ * For center = 2, mu is an INPUT: the mean [d_in] of hq_channel_center. */
 int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
                      float* Xt, float* mu, void* stream);
 
@@ -213,7 +244,8 @@ int hq_gemm_i32(const hq_desc* desc, const void* a_codes, const void* w_codes, i
                 int64_t N, int32_t* acc, void* stream);
 
 /* GEMM + dequant epilogue alone, from activation-stage outputs (layouts as in
- * hq_act_quantize; U NULL when rank = 0). Y [T, d_out] y_dtype. */
+ * hq_act_quantize; U NULL when rank = 0). Y [T, d_out] y_dtype. For
+ * center = 2, mu is the bias_eff [d_out_pad] of hq_channel_center. */
 int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes,
                     const float* s_x, const float* mu, const float* U, int64_t T, void* Y,
                     void* stream);

@@ -31,7 +31,7 @@ XT_TOL = 1e-5
 
 def desc_for(w: WL.Workload, gemm: int = hq.HQ_GEMM_AUTO) -> hq.Desc:
     dt = hq.BF16 if w.dtype == "bf16" else hq.F32
-    return hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, bool(w.center),
+    return hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, int(w.center),
                    w.alpha is not None, w.rank, dt, dt, dt, gemm)
 
 
@@ -72,7 +72,7 @@ class Case:
             self.sigma32 = None
         sig = None if self.sigma32 is None else self.sigma32.astype(np.float64)
         self.ora = O.run(self.x, self.weight, self.bias, block=w.block, a_bits=w.a_bits,
-                         w_bits=w.w_bits, center=bool(w.center), sigma=sig, l1=self.l1,
+                         w_bits=w.w_bits, center=int(w.center), sigma=sig, l1=self.l1,
                          l2=self.l2, out_dtype=w.out_dtype)
         # device tensors
         self.X = tdev(self.x, w.dtype)

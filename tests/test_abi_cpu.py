@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lib.hq_abi_version() == 3
+    assert lib.hq_abi_version() == 4
     assert lib.hq_status_str(0) == b"HQ_OK"
     assert lib.hq_status_str(-3) == b"HQ_ERR_WORKSPACE"
     assert lib.hq_status_str(99) == b"HQ_ERR_UNKNOWN"
@@ -54,7 +54,7 @@ def test_workload_descriptors_valid(name):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(d_in=0), -1), (dict(d_out=-8), -1), (dict(x_dtype=3), -1), (dict(center=2), -1),
+    (dict(d_in=0), -1), (dict(d_out=-8), -1), (dict(x_dtype=3), -1), (dict(center=3), -1), (dict(center=-1), -1),
     (dict(smooth=5), -1), (dict(a_bits=3), -2), (dict(w_bits=16), -2), (dict(d_in=1000), -2),
     (dict(d_in=2176), -2), (dict(d_out=100), -2), (dict(block=96), -2), (dict(block=256, d_in=1152), -2),
     (dict(rank=8), -2), (dict(rank=128), -2), (dict(d_in=16384), -2), (dict(gemm=2), -1),
@@ -104,6 +104,35 @@ def test_e2m3_table_matches_format_definition():
     q[0, 0], q[0, 1] = 1, -7
     buf = codefmt.encode(codefmt.E2M3, q)
     assert buf.size == 384 and buf[0] == 0x88 and buf[1] == 0x0F and not buf[2:].any()
+
+
+@pytest.mark.parametrize("w_dtype,esize", [(BF16, 2), (F32, 4)])
+def test_channel_centring_layout(w_dtype, esize):
+    # center = 2 keeps a copy of the weight in the blob and needs partial sums,
+    # the channel mean and the corrected bias in the workspace
+    tok = _d(w_dtype=w_dtype)
+    chan = _d(center=2, w_dtype=w_dtype)
+    assert lib.hq_validate(ctypes.byref(chan)) == 0
+    Lt, Lc = _lib.HqLayout(), _lib.HqLayout()
+    assert lib.hq_prepared_layout_of(ctypes.byref(tok), ctypes.byref(Lt)) == 0
+    assert lib.hq_prepared_layout_of(ctypes.byref(chan), ctypes.byref(Lc)) == 0
+    assert Lt.weight == 0 and Lc.weight % 256 == 0 and Lc.weight >= Lc.l2_lo
+    assert Lc.total - Lc.weight >= esize * 4608 * 1152
+    for T in [1, 64, 65, 8192]:
+        extra = lib.hq_workspace_bytes(ctypes.byref(chan), T) - \
+            lib.hq_workspace_bytes(ctypes.byref(tok), T)
+        chunks = (T + 63) // 64
+        assert extra >= 4 * (chunks * 1152 + 1152 + Lc.d_out_pad)
+
+
+def test_channel_center_rejects_other_modes():
+    d = _d(center=1)
+    z = ctypes.c_void_p(16)
+    assert lib.hq_channel_center(ctypes.byref(d), z, z, 4, z, z, z, 1 << 20, None) == -1
+    assert b"center = 2" in lib.hq_last_error()
+    c = _d(center=2)
+    assert lib.hq_channel_center(ctypes.byref(c), z, z, 0, z, z, z, 1 << 20, None) == -1
+    assert lib.hq_channel_center(ctypes.byref(c), z, z, 4, z, z, z, 16, None) == -3
 
 
 def test_null_desc():

@@ -51,7 +51,7 @@ def test_full_size_sampled(name):
     del Y, codes, X
 
     ora = O.run(x[rows], weight, bias, block=w.block, a_bits=w.a_bits, w_bits=w.w_bits,
-                center=bool(w.center), sigma=sig, l1=l1, l2=l2, out_dtype=w.out_dtype)
+                center=int(w.center), sigma=sig, l1=l1, l2=l2, out_dtype=w.out_dtype)
     err = rel_fro(y_s, ora["y_out"])
     print(f"{name}: sampled rel Frobenius error {err:.3e}")
     assert err <= Y_TOL, err
