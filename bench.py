@@ -54,13 +54,13 @@ def cpu_baseline(w, x, weight, bias, sigma, l1, l2, target_s):
     rows = min(w.T, 256)
     t0 = time.perf_counter()
     O.quant_linear(x[:rows], prep, bias, sig, block=w.block, a_bits=w.a_bits,
-                   center=bool(w.center), l1=l1, l2=l2, out_dtype=w.out_dtype)
+                   center=int(w.center), l1=l1, l2=l2, out_dtype=w.out_dtype)
     dt = time.perf_counter() - t0
     if dt < target_s and rows < w.T:
         rows = int(min(w.T, max(rows, rows * target_s / max(dt, 1e-3))))
         t0 = time.perf_counter()
         O.quant_linear(x[:rows], prep, bias, sig, block=w.block, a_bits=w.a_bits,
-                       center=bool(w.center), l1=l1, l2=l2, out_dtype=w.out_dtype)
+                       center=int(w.center), l1=l1, l2=l2, out_dtype=w.out_dtype)
         dt = time.perf_counter() - t0
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info] + [1])
@@ -159,6 +159,44 @@ def kernel_report(hq, desc, w, r):
     return fp6, peak, k1_gbs, k2_tops, k2_ops
 
 
+def centring_modes(hq, torch, WL, steps, warmup, dev):
+    """square4k (channels with different means) under per-token and per-channel
+    centring: time per quant_linear call and the output SQNR against the
+    float32 layer X W + b (HaTQ Sec. IV-A Eq. (10))."""
+    w = WL.WORKLOADS["square4k"]
+    x = WL.gen_x(w)
+    X0 = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    W = torch.from_numpy(WL.gen_weight(w)).to(dev).to(torch.bfloat16)
+    B = torch.from_numpy(WL.gen_bias(w)).to(dev)
+    nbuf = max(2, math.ceil(512e6 / (X0.numel() * 2)))
+    Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
+    Y = torch.empty(w.T, w.d_out, dtype=torch.bfloat16, device=dev)
+    ref = torch.addmm(B, X0.float(), W.float().t())
+    out = {"workload": "square4k", "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
+           "block": w.block, "bits": "W4A4", "io_dtype": "bf16"}
+    for mode, key in ((hq.HQ_CENTER_TOKEN, "per_token"), (hq.HQ_CENTER_CHANNEL, "per_channel")):
+        desc = hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, mode, False, 0,
+                       hq.BF16, hq.BF16, hq.BF16)
+        prep = hq.prepare(desc, W, B)
+        ws = torch.empty(hq.workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
+        for i in range(warmup):
+            hq.quant_linear(desc, prep, Xs[i % nbuf], out=Y, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            hq.quant_linear(desc, prep, Xs[(warmup + i) % nbuf], out=Y, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        hq.quant_linear(desc, prep, X0, out=Y, workspace=ws)
+        err = (Y.float() - ref).pow(2).sum().item()
+        sqnr = 10.0 * math.log10(ref.pow(2).sum().item() / max(err, 1e-300))
+        out[key] = {"value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s",
+                    "ms_per_step": round(ms, 5), "sqnr_db": round(sqnr, 2)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -172,7 +210,7 @@ def main():
 
     w = WL.WORKLOADS[args.workload]
     dt = hq.BF16 if w.dtype == "bf16" else hq.F32
-    desc = hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, bool(w.center),
+    desc = hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, int(w.center),
                    w.alpha is not None, w.rank, dt, dt, dt)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
@@ -217,7 +255,7 @@ def main():
         "dtype": "e2m3" if fp6 else "int8",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
-                   "block": w.block, "bits": f"W{w.w_bits}A{w.a_bits}", "center": bool(w.center),
+                   "block": w.block, "bits": f"W{w.w_bits}A{w.a_bits}", "center": int(w.center),
                    "smooth_alpha": w.alpha, "rank": w.rank, "io_dtype": w.dtype,
                    "gemm": "e2m3 fp6 mfma" if fp6 else "int8 mfma"},
         "effective_tops": round(eff_tops, 2),
@@ -241,6 +279,9 @@ def main():
             "ms_per_step": round(r8["ms"], 5), "row_transform_ms": round(r8["k1"], 5),
             "row_transform_GBs": round(g8, 1), "gemm_ms": round(r8["k2"], 5),
             "gemm_TOPS": round(t8, 2), "gemm_mfma_frac": round(t8 / p8, 4), "peak": p8}
+    del Xs, Ys
+    out["centring_modes"] = centring_modes(hq, torch, WL, min(args.steps, 20),
+                                           min(args.warmup, 5), dev)
     if not args.no_cpu_baseline:
         sig = None if S is None else S.cpu().numpy()
         out["cpu_baseline"] = cpu_baseline(w, x, weight, bias, sig, l1, l2, args.cpu_seconds)

@@ -47,14 +47,31 @@ __global__ __launch_bounds__(256) void col_partial_kernel(const TIn* __restrict_
   }
 }
 
-// mean[i] = (sum of the chunk partials in chunk order) / rows.
-__global__ void mean_finish_kernel(const float* __restrict__ partial, int chunks, int64_t rows,
-                                   int d, float* __restrict__ mean) {
-  const int i = int(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= d) return;
+// mean[i] = (sum of the chunk partials) / rows. Block: 64 columns x 4 chunk
+// lanes; lane g sums chunks g, g + 4, ... eight loads at a time (issued
+// together, added as a fixed tree), and the 4 lane sums are combined in lane
+// order, so the result does not depend on timing.
+__global__ __launch_bounds__(256) void mean_finish_kernel(const float* __restrict__ partial,
+                                                          int chunks, int64_t rows, int d,
+                                                          float* __restrict__ mean) {
+  const int ci = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int i = int(blockIdx.x) * 64 + ci;
   float s = 0.0f;
-  for (int c = 0; c < chunks; ++c) s += partial[int64_t(c) * d + i];
-  mean[i] = s / float(rows);
+  if (i < d) {
+    int c = g;
+    for (; c + 28 < chunks; c += 32) {
+      float p[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[k] = partial[int64_t(c + 4 * k) * d + i];
+      s += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    }
+    for (; c < chunks; c += 4) s += partial[int64_t(c) * d + i];
+  }
+  __shared__ float red[4][64];
+  red[g][ci] = s;
+  __syncthreads();
+  if (g == 0 && i < d)
+    mean[i] = (((red[0][ci] + red[1][ci]) + red[2][ci]) + red[3][ci]) / float(rows);
 }
 
 // out[j] = bias[j] + sum_i weight[j, i] mean[i] for j < n (the corrected bias
@@ -98,7 +115,7 @@ hipError_t launch_channel_mean(const void* x, int x_bf16, int64_t rows, int d, f
                        static_cast<const float*>(x), rows, d, int64_t(CENTER_RPC), partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mean_finish_kernel, dim3((d + 255) / 256), dim3(256), 0, s, partial, chunks,
+  hipLaunchKernelGGL(mean_finish_kernel, dim3((d + 63) / 64), dim3(256), 0, s, partial, chunks,
                      rows, d, mean);
   return hipGetLastError();
 }
