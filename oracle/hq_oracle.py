@@ -54,6 +54,12 @@ Readings taken where the pages leave a step open:
 * The bias correction uses c = 1^T W~ from the unquantised W~.
 * The low-rank branch sees x' = x / sigma (smoothed, not rotated, not
   centred) and contributes (x' L1) L2, L1 [d_in, r], L2 [r, d_out].
+* ``group`` = 64 (the data-free int4 blog's recipe, "Hadamard rotation: the
+  int4 improvement", step 7 and "How it is applied here"): one scale per row
+  and group of 64 consecutive channels instead of one per row, for both
+  activations and weights; the integer products are summed per group and
+  each group's sum is scaled by s_x[t, g] s_w[j, g]. ``group`` = 0 keeps one
+  scale per row.
 * Y is rounded once, half-to-even, to the output dtype.
 
 Parity status: every step below is pinned by ``tests/test_oracle.py``
@@ -184,6 +190,20 @@ def quantize_rows(v: np.ndarray, bits: int):
     return q, s
 
 
+def quantize_groups(v: np.ndarray, bits: int, group: int):
+    """The quantiser of quantize_rows with one scale per row and group of
+    ``group`` consecutive channels (blog, "Hadamard rotation: the int4
+    improvement": each group of 64 input channels shares one scale): every
+    group is quantised on its own. Returns (codes [rows, n], s [rows, n / group])."""
+    v = np.asarray(v, dtype=np.float64)
+    rows, n = v.shape
+    if group <= 0 or n % group:
+        raise ValueError("group must divide the row length")
+    g = n // group
+    q, sc = quantize_rows(v.reshape(rows * g, group), bits)
+    return q.reshape(rows, n), sc.reshape(rows, g)
+
+
 # --------------------------------------------------------------------------
 # Integer GEMM, low-rank branch, dequantised output
 # --------------------------------------------------------------------------
@@ -201,6 +221,20 @@ def int_gemm(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
         bound = int(np.abs(qa).max()) * int(np.abs(qw).max()) * qa.shape[1]
         assert bound < 2 ** 53
     return (qa.astype(np.float64) @ qw.astype(np.float64).T).astype(np.int64)
+
+
+def group_product(qa, s_x, qw, s_w, group: int) -> np.ndarray:
+    """sum_g s_x[t, g] s_w[j, g] (sum_{k in g} qa_tk qw_jk): the integer product
+    of each channel group (exact, int_gemm) scaled by its two group scales."""
+    qa = np.asarray(qa)
+    qw = np.asarray(qw)
+    y = np.zeros((qa.shape[0], qw.shape[0]))
+    for g in range(qa.shape[1] // group):
+        k = slice(g * group, (g + 1) * group)
+        y += int_gemm(qa[:, k], qw[:, k]).astype(np.float64) * (
+            np.asarray(s_x, dtype=np.float64)[:, g][:, None]
+            * np.asarray(s_w, dtype=np.float64)[:, g][None, :])
+    return y
 
 
 def low_rank(xp: np.ndarray, l1: np.ndarray, l2: np.ndarray):
@@ -251,11 +285,11 @@ def exact_output(x, weight, bias, xp=None, l1=None, l2=None) -> np.ndarray:
 # The whole layer
 # --------------------------------------------------------------------------
 
-def prepare_weights(weight, sigma, block: int, w_bits: int):
-    """Offline half: W~, c, per-output-channel codes and scales."""
+def prepare_weights(weight, sigma, block: int, w_bits: int, group: int = 0):
+    """Offline half: W~, c, per-output-channel (or per channel and group) codes and scales."""
     wt, c = transform_weights(weight, sigma, block)
-    qw, s_w = quantize_rows(wt, w_bits)
-    return {"wt": wt, "c": c, "qw": qw, "s_w": s_w}
+    qw, s_w = quantize_groups(wt, w_bits, group) if group else quantize_rows(wt, w_bits)
+    return {"wt": wt, "c": c, "qw": qw, "s_w": s_w, "group": group}
 
 
 def channel_bias(bias, wt, mu_c) -> np.ndarray:
@@ -269,29 +303,38 @@ def quant_linear(x, prepared, bias, sigma, *, block: int, a_bits: int, center,
                  l1=None, l2=None, out_dtype: str = "f32"):
     """Online half for the rows of ``x``: transform, centre, quantise, integer GEMM, dequantise."""
     xp, y, mu, xt = transform_activations(x, sigma, block, center)
-    qa, s_x = quantize_rows(xt, a_bits)
-    acc = int_gemm(qa, prepared["qw"])
+    group = prepared.get("group", 0)
+    if group:
+        qa, s_x = quantize_groups(xt, a_bits, group)
+        acc = None
+        # per-group scaled products; the rest of the epilogue as below with unit scales
+        acc_in = group_product(qa, s_x, prepared["qw"], prepared["s_w"], group)
+        sx_in, sw_in = np.ones(len(xt)), np.ones(len(prepared["qw"]))
+    else:
+        qa, s_x = quantize_rows(xt, a_bits)
+        acc = acc_in = int_gemm(qa, prepared["qw"])
+        sx_in, sw_in = s_x, prepared["s_w"]
     u = lr = None
     if l1 is not None:
         u, lr = low_rank(xp, l1, l2)
     if int(center) == CENTER_CHANNEL:
         bias_eff = channel_bias(bias, prepared["wt"], mu)
-        y_full = dequant_output(acc, s_x, prepared["s_w"], bias_eff, np.zeros(len(xt)),
+        y_full = dequant_output(acc_in, sx_in, sw_in, bias_eff, np.zeros(len(xt)),
                                 prepared["c"], lr)
     else:
         bias_eff = np.asarray(bias, dtype=np.float64)
-        y_full = dequant_output(acc, s_x, prepared["s_w"], bias, mu, prepared["c"], lr)
+        y_full = dequant_output(acc_in, sx_in, sw_in, bias, mu, prepared["c"], lr)
     return {"xp": xp, "y": y, "mu": mu, "xt": xt, "qa": qa, "s_x": s_x, "acc": acc,
             "u": u, "lr": lr, "bias_eff": bias_eff, "y_full": y_full,
             "y_out": round_to_dtype(y_full, out_dtype)}
 
 
 def run(x, weight, bias, *, block: int, a_bits: int, w_bits: int, center,
-        sigma=None, l1=None, l2=None, out_dtype: str = "f32"):
+        sigma=None, l1=None, l2=None, out_dtype: str = "f32", group: int = 0):
     """Prepare + quant_linear in one call; sigma defaults to ones."""
     d_in = np.asarray(x).shape[1]
     sigma = np.ones(d_in) if sigma is None else np.asarray(sigma, dtype=np.float64)
-    prep = prepare_weights(weight, sigma, block, w_bits)
+    prep = prepare_weights(weight, sigma, block, w_bits, group)
     out = quant_linear(x, prep, bias, sigma, block=block, a_bits=a_bits, center=center,
                        l1=l1, l2=l2, out_dtype=out_dtype)
     out.update(prep)

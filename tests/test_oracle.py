@@ -264,6 +264,76 @@ def test_channel_centring_equal_tokens(T):
                                atol=1e-12)
 
 
+# ---------------------------------------------------------------- group-wise quantisation (group = 64)
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_groups_of_full_width_are_the_row_quantiser(bits):
+    rng = np.random.default_rng(21)
+    v = rng.standard_normal((9, 128)) * rng.uniform(0.1, 30, (9, 1))
+    q1, s1 = O.quantize_rows(v, bits)
+    q2, s2 = O.quantize_groups(v, bits, 128)
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(s1, s2[:, 0])
+
+
+def test_group_scales_are_per_group_and_independent():
+    # each group's scale is its own max|v| / qmax; rescaling one group by a power
+    # of two scales only that group's scale and leaves every code unchanged
+    rng = np.random.default_rng(22)
+    v = rng.standard_normal((5, 256))
+    v[:, 70] *= 40.0                                   # an outlier in group 1
+    q, sc = O.quantize_groups(v, 4, 64)
+    np.testing.assert_allclose(sc, np.abs(v.reshape(5, 4, 64)).max(axis=2) / 7, rtol=1e-15)
+    w = v.copy()
+    w[:, 128:192] *= 4.0
+    q2, sc2 = O.quantize_groups(w, 4, 64)
+    np.testing.assert_array_equal(q2, q)
+    np.testing.assert_allclose(sc2[:, 2], 4 * sc[:, 2], rtol=1e-15)
+    np.testing.assert_array_equal(np.delete(sc2, 2, axis=1), np.delete(sc, 2, axis=1))
+    # half-step bound inside every group
+    err = np.abs(v - q * np.repeat(sc, 64, axis=1))
+    assert np.all(err <= np.repeat(sc, 64, axis=1) / 2 * (1 + 1e-12))
+
+
+def test_group_product_brute_force():
+    rng = np.random.default_rng(23)
+    qa = rng.integers(-7, 8, (3, 128))
+    qw = rng.integers(-7, 8, (4, 128))
+    sa = rng.uniform(0.1, 2, (3, 2))
+    sw = rng.uniform(0.1, 2, (4, 2))
+    got = O.group_product(qa, sa, qw, sw, 64)
+    for t in range(3):
+        for j in range(4):
+            ref = 0.0
+            for g in range(2):
+                ref += sa[t, g] * sw[j, g] * sum(int(qa[t, k]) * int(qw[j, k])
+                                                 for k in range(64 * g, 64 * g + 64))
+            assert abs(got[t, j] - ref) <= 1e-12 * abs(ref) + 1e-12
+
+
+def test_group_product_one_group_is_scaled_int_gemm():
+    rng = np.random.default_rng(24)
+    qa = rng.integers(-7, 8, (5, 64))
+    qw = rng.integers(-7, 8, (6, 64))
+    sa, sw = rng.uniform(0.1, 2, (5, 1)), rng.uniform(0.1, 2, (6, 1))
+    np.testing.assert_allclose(O.group_product(qa, sa, qw, sw, 64),
+                               O.int_gemm(qa, qw) * sa * sw.T, rtol=1e-14)
+
+
+def test_group_quantised_layer_beats_row_scales_on_outliers():
+    # diagnostic of the blog's motivation: with a few large channels, 64-channel
+    # groups quantise W4A4 more accurately than one scale per row (block 64)
+    rng = np.random.default_rng(25)
+    x = rng.standard_normal((64, 512))
+    x[:, [5, 300]] *= 60.0
+    weight = rng.standard_normal((96, 512)) * 0.02
+    bias = np.zeros(96)
+    ref = O.exact_output(x, weight, bias)
+    row = O.run(x, weight, bias, block=64, a_bits=4, w_bits=4, center=False)
+    grp = O.run(x, weight, bias, block=64, a_bits=4, w_bits=4, center=False, group=64)
+    assert O.sqnr_db(ref, grp["y_full"]) > O.sqnr_db(ref, row["y_full"]) + 1.0
+
+
 def test_center_mode_rejected():
     with pytest.raises(ValueError):
         O.transform_activations(np.ones((2, 8)), np.ones(8), 8, 3)
