@@ -30,6 +30,10 @@ METRIC = "Hadamard-quantized linear tokens/s + effective TOPS (% int8 MFMA/HBM r
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
 FP6_PEAK_TOPS = 10100.0        # MI355X dense fp6 / fp4 MFMA (10.1 PFLOP/s)
+# Non-packed fp32 VALU lane operations per second: 256 CUs x 4 SIMDs x 16
+# lanes x 2.4 GHz (a wave64 instruction issues over 4 cycles); the 157.3
+# TFLOP/s vector figure counts packed fp32 fma, which this build does not emit.
+VALU_F32_LANE_OPS = 256 * 4 * 16 * 2.4e9
 
 
 def parse():
@@ -78,7 +82,7 @@ def measure(hq, torch, desc, w, Xs, Ys, S, W, B, L1, L2, steps, warmup, dev):
     prep = hq.prepare(desc, W, B, S, L1, L2)
     ws = torch.empty(hq.workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
     codes = torch.empty(hq.code_bytes(desc, w.T), dtype=torch.uint8, device=dev)
-    s_x = torch.empty(w.T, dtype=torch.float32, device=dev)
+    s_x = torch.empty(desc.sx_shape(w.T), dtype=torch.float32, device=dev)
     mu = torch.empty(w.T, dtype=torch.float32, device=dev)
     U = torch.empty(w.T, w.rank, dtype=torch.float32, device=dev) if w.rank else None
 
@@ -197,6 +201,50 @@ def centring_modes(hq, torch, WL, steps, warmup, dev):
     return out
 
 
+def group_wise(hq, torch, WL, steps, warmup, dev):
+    """flux_g64 (group-wise scales, 64-point blocks, rank 32): time per call and
+    per kernel, and the output SQNR against the float32 layer
+    X W + b + (X L1) L2 with group-wise and with per-row scales on the same
+    rotation. The group GEMM rescales every 64-channel partial product on the
+    VALU (one multiply and one fma per output element and group); its floor is
+    that work at the chip's non-packed fp32 rate."""
+    w = WL.WORKLOADS["flux_g64"]
+    x = WL.gen_x(w)
+    l1, l2 = WL.gen_lowrank(w)
+    X0 = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    W = torch.from_numpy(WL.gen_weight(w)).to(dev).to(torch.bfloat16)
+    B = torch.from_numpy(WL.gen_bias(w)).to(dev)
+    L1 = torch.from_numpy(l1).to(dev).to(torch.bfloat16)
+    L2 = torch.from_numpy(l2).to(dev).to(torch.bfloat16)
+    nbuf = max(2, math.ceil(512e6 / (X0.numel() * 2)))
+    Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
+    Ys = [torch.empty(w.T, w.d_out, dtype=torch.bfloat16, device=dev) for _ in range(nbuf)]
+    desc = hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, int(w.center), False, w.rank,
+                   hq.BF16, hq.BF16, hq.BF16, group=w.group)
+    r = measure(hq, torch, desc, w, Xs, Ys, None, W, B, L1, L2, steps, warmup, dev)
+    del Xs, Ys
+    ops = 2.0 * w.T * w.d_in * w.d_out
+    valu_lane_ops = 2.0 * w.T * w.d_out * (w.d_in // w.group)
+    valu_floor_ms = valu_lane_ops / VALU_F32_LANE_OPS * 1e3
+    ref = torch.addmm(B, X0.float(), W.float().t()) + (X0.float() @ L1.float()) @ L2.float()
+    sq = {}
+    for key, g in (("group64", w.group), ("per_row", 0)):
+        d = dataclasses.replace(desc, group=g)
+        Y = hq.quant_linear(d, r["prep"] if g else hq.prepare(d, W, B, None, L1, L2), X0)
+        err = (Y.float() - ref).pow(2).sum().item()
+        sq[key] = round(10.0 * math.log10(ref.pow(2).sum().item() / max(err, 1e-300)), 2)
+        del Y
+    return {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
+            "block": w.block, "group": w.group, "rank": w.rank, "bits": "W4A4",
+            "io_dtype": "bf16", "value": round(w.T / (r["ms"] * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(r["ms"], 5), "row_transform_ms": round(r["k1"], 5),
+            "gemm_ms": round(r["k2"], 5), "gemm_TOPS": round(ops / (r["k2"] * 1e-3) / 1e12, 2),
+            "gemm_mfma_frac": round(ops / (r["k2"] * 1e-3) / 1e12 / FP6_PEAK_TOPS, 4),
+            "gemm_valu_floor_ms": round(valu_floor_ms, 5),
+            "gemm_valu_frac": round(valu_floor_ms / r["k2"], 4),
+            "sqnr_db": sq}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -280,6 +328,7 @@ def main():
             "row_transform_GBs": round(g8, 1), "gemm_ms": round(r8["k2"], 5),
             "gemm_TOPS": round(t8, 2), "gemm_mfma_frac": round(t8 / p8, 4), "peak": p8}
     del Xs, Ys
+    out["group_wise"] = group_wise(hq, torch, WL, min(args.steps, 20), min(args.warmup, 5), dev)
     out["centring_modes"] = centring_modes(hq, torch, WL, min(args.steps, 20),
                                            min(args.warmup, 5), dev)
     if not args.no_cpu_baseline:

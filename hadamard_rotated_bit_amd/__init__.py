@@ -31,7 +31,8 @@ _NAME = {F32: "f32", BF16: "bf16"}
 @dataclasses.dataclass(frozen=True)
 class Desc:
     """Layer descriptor; mirrors hq_desc. ``center``: 0 / False none, 1 / True
-    per-token mean, 2 per-channel mean over the call's tokens (HQ_CENTER_*)."""
+    per-token mean, 2 per-channel mean over the call's tokens (HQ_CENTER_*).
+    ``group``: 0 one scale per row, 64 one per row and 64-channel group."""
     d_in: int
     d_out: int
     block: int
@@ -44,16 +45,22 @@ class Desc:
     w_dtype: int = F32
     y_dtype: int = F32
     gemm: int = HQ_GEMM_AUTO
+    group: int = 0
 
     def __post_init__(self):
         raw = HqDesc(self.d_in, self.d_out, self.block, self.a_bits, self.w_bits,
                      int(self.center), int(self.smooth), self.rank, self.x_dtype,
-                     self.w_dtype, self.y_dtype, self.gemm)
+                     self.w_dtype, self.y_dtype, self.gemm, self.group)
         object.__setattr__(self, "_raw", raw)
         object.__setattr__(self, "_ref", ctypes.byref(raw))
 
     def c(self) -> HqDesc:
         return self._raw
+
+    def sx_shape(self, T: int) -> tuple:
+        """Shape of the activation scales of T tokens: (T,), or (d_in / 64, T)
+        with group-wise scales (group-major)."""
+        return (self.d_in // self.group, T) if self.group else (T,)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -213,7 +220,8 @@ def channel_center(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
 
 
 def act_quantize(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, out=None, mean=None):
-    """Activation stage alone: (codes, s_x [T], mu [T], U [T, rank] or None).
+    """Activation stage alone: (codes, s_x, mu [T], U [T, rank] or None); s_x
+    has desc.sx_shape(T) ([T], or [d_in / 64, T] with group-wise scales).
 
     ``codes`` is a uint8 buffer of code_bytes(desc, T) bytes in the
     descriptor's code format. ``out`` may supply that tuple preallocated.
@@ -227,7 +235,7 @@ def act_quantize(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, out=None, 
         mean = channel_center(desc, prepared, X)[0]
     if out is None:
         codes = torch.empty(max(code_bytes(desc, T), 1), dtype=torch.uint8, device=dev)
-        s_x = torch.empty(T, dtype=torch.float32, device=dev)
+        s_x = torch.empty(desc.sx_shape(T), dtype=torch.float32, device=dev)
         mu = mean if chan else torch.empty(T, dtype=torch.float32, device=dev)
         U = torch.empty(T, desc.rank, dtype=torch.float32, device=dev) if desc.rank else None
     else:
@@ -235,7 +243,7 @@ def act_quantize(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, out=None, 
         if chan:
             mu = mean
         _need_codes(codes, "codes", desc, T)
-        _need(s_x, "s_x", torch.float32, (T,))
+        _need(s_x, "s_x", torch.float32, desc.sx_shape(T))
         if desc.rank:
             _need(U, "U", torch.float32, (T, desc.rank))
     _need(mu, "mu", torch.float32, (desc.d_in,) if chan else (T,))
@@ -275,11 +283,11 @@ def gemm_i32(desc: Desc, a_codes: torch.Tensor, w_codes: torch.Tensor, T: int,
 def gemm_dequant(desc: Desc, prepared: torch.Tensor, codes: torch.Tensor, s_x: torch.Tensor,
                  mu: torch.Tensor, U: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """GEMM + dequant epilogue alone, from act_quantize's outputs (T = len(s_x)).
-    For center = 2, ``mu`` is channel_center's bias_eff [d_out_pad]."""
-    T = s_x.shape[0]
+    """GEMM + dequant epilogue alone, from act_quantize's outputs (T = the last
+    dimension of s_x). For center = 2, ``mu`` is channel_center's bias_eff [d_out_pad]."""
+    T = s_x.shape[-1]
     _need_codes(codes, "codes", desc, T)
-    _need(s_x, "s_x", torch.float32, (T,))
+    _need(s_x, "s_x", torch.float32, desc.sx_shape(T))
     _need(mu, "mu", torch.float32, (layout(desc).d_out_pad,) if _channel(desc) else (T,))
     if desc.rank:
         _need(U, "U", torch.float32, (T, desc.rank))
@@ -303,7 +311,9 @@ def prepared_views(desc: Desc, prepared: torch.Tensor) -> dict:
 
     out = {
         "w_codes": prepared[L.w_codes:L.w_codes + code_bytes(desc, desc.d_out)],
-        "s_w": view(L.w_scale, npad, torch.float32, (npad,))[:desc.d_out],
+        "s_w": (view(L.w_scale, npad * (d // desc.group), torch.float32,
+                     (d // desc.group, npad))[:, :desc.d_out] if desc.group
+                else view(L.w_scale, npad, torch.float32, (npad,))[:desc.d_out]),
         "c": view(L.c, npad, torch.float32, (npad,))[:desc.d_out],
         "bias": view(L.bias, npad, torch.float32, (npad,))[:desc.d_out],
         "sigma_inv": view(L.sigma_inv, d, torch.float32, (d,)),

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(HERE, "libhq.so")
 HEADER = os.path.join(HERE, "..", "include", "hq.h")
 
 DESC_FIELDS = ["d_in", "d_out", "block", "a_bits", "w_bits", "center", "smooth", "rank",
-               "x_dtype", "w_dtype", "y_dtype", "gemm"]
+               "x_dtype", "w_dtype", "y_dtype", "gemm", "group"]
 
 
 class HqDesc(ctypes.Structure):

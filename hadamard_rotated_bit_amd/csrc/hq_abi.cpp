@@ -50,6 +50,8 @@ inline int log2i(int v) {
   return l;
 }
 inline float qmax_of(int bits) { return float((1 << (bits - 1)) - 1); }
+// Scales per row: 1, or one per 64-channel group.
+inline int64_t scales_per_row(const hq_desc* d) { return d->group ? d->d_in / d->group : 1; }
 
 int check_desc(const hq_desc* d) {
   if (!d) return fail(HQ_ERR_INVALID_ARG, "desc is NULL");
@@ -85,6 +87,11 @@ int check_desc(const hq_desc* d) {
                 d->d_in);
   if (d->rank < 0 || d->rank > 64 || d->rank % 16)
     return fail(HQ_ERR_UNSUPPORTED, "rank must be 0, 16, 32, 48 or 64 (got %d)", d->rank);
+  if (d->group != 0 && d->group != 64)
+    return fail(HQ_ERR_UNSUPPORTED, "group must be 0 or 64 (got %d)", d->group);
+  if (d->group && (d->a_bits != 4 || d->w_bits != 4 || d->gemm != HQ_GEMM_AUTO))
+    return fail(HQ_ERR_UNSUPPORTED,
+                "group = 64 needs a_bits = w_bits = 4 and gemm = HQ_GEMM_AUTO (FP6 engine)");
   return HQ_OK;
 }
 
@@ -104,7 +111,7 @@ void layout_of(const hq_desc* d, hq_prepared_layout* L) {
   L->w_codes = off;
   off += align256(hq::code_bytes(code_fmt_of(d), np, d->d_in));
   L->w_scale = off;
-  off += align256(4 * size_t(np));
+  off += align256(4 * size_t(np) * scales_per_row(d));
   L->c = off;
   off += align256(4 * size_t(np));
   L->bias = off;
@@ -138,7 +145,7 @@ Workspace workspace_of(const hq_desc* d, int64_t T) {
   w.codes = off;
   off += align256(hq::code_bytes(code_fmt_of(d), T, d->d_in));
   w.s_x = off;
-  off += align256(4 * size_t(T));
+  off += align256(4 * size_t(T) * scales_per_row(d));
   w.mu = off;
   off += align256(4 * size_t(T));
   w.U = off;
@@ -199,6 +206,8 @@ int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, vo
   a.codes = static_cast<uint8_t*>(codes);
   a.code_fmt = code_fmt_of(d);
   a.out_s = s_x;
+  a.group = d->group;
+  a.s_ld = T;
   a.out_aux = mu;
   a.mode = hq::ROW_ACT;
   hipError_t e = hq::launch_row_transform(a, s);
@@ -245,7 +254,11 @@ int run_gemm_dequant(const hq_desc* d, const void* prepared, const void* codes,
   ep.Y = Y;
   ep.y_bf16 = d->y_dtype == HQ_BF16;
   ep.ldy = d->d_out;
-  hipError_t e = launch_codes_gemm(d, codes, T, at<uint8_t>(prepared, L.w_codes), d->d_out,
+  hipError_t e =
+      d->group ? hq::launch_gemm_f6g(static_cast<const uint8_t*>(codes), T,
+                                     at<uint8_t>(prepared, L.w_codes), d->d_out, d->d_in, s_x, T,
+                                     ep.s_w, L.d_out_pad, &ep, s)
+               : launch_codes_gemm(d, codes, T, at<uint8_t>(prepared, L.w_codes), d->d_out,
                                    nullptr, 0, &ep, s);
   if (e != hipSuccess) return hip_fail(e, "GEMM kernel launch");
   return HQ_OK;
@@ -395,6 +408,8 @@ int hq_prepare_weights(const hq_desc* desc, const void* weight, const float* bia
     a.codes = at<uint8_t>(prepared, L.w_codes);
     a.code_fmt = fmt;
     a.out_s = at<float>(prepared, L.w_scale);
+    a.group = desc->group;
+    a.s_ld = np;
     // c = 1^T W~ (the per-token correction); zero under per-channel centring,
     // whose correction is the per-call bias instead.
     a.out_aux = desc->center != HQ_CENTER_CHANNEL ? at<float>(prepared, L.c) : nullptr;

@@ -69,6 +69,42 @@ __device__ __forceinline__ void store_codes(const RowArgs& a, int64_t row, int64
 //   q = rint((y' - mu') * (qmax / amax'))  (fp32 operands, the exact product
 //                                           rounded once, ties to even)
 //   s = amax' / (sqrt(B) qmax),  mu = mu' / sqrt(B),  c = sum(y') / sqrt(B)
+// Group-wise variant of store_codes (a.group = 64): chunk c of lane t lies in
+// channel group c G/8 + t/8, shared by the 8 lanes t & ~7; each group is
+// quantised with its own max |v| (a group maximum over those 8 lanes) and its
+// scale written by the group's first lane to out_s[g * s_ld + row]. Every
+// lane of the wave runs the cross-lane maxima; only valid rows store.
+template <int G, int C>
+__device__ __forceinline__ void store_group_codes(const RowArgs& a, int64_t row, int64_t base,
+                                                  int t, const float* v, bool valid,
+                                                  float inv_sqrt_b) {
+  static_assert(G % 8 == 0, "8 lanes per 64-channel group");
+  float rc[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[c * 8 + j]));
+    m = group_max<8>(m);
+    rc[c] = m > 0.0f ? a.qmax / m : 0.0f;
+    if (valid && (t & 7) == 0)
+      a.out_s[int64_t(c * (G / 8) + t / 8) * a.s_ld + row] = m * inv_sqrt_b / a.qmax;
+  }
+  if (!valid) return;
+  if (a.code_fmt == CODES_E2M3) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) store_e2m3x8(a.codes, row, a.d, c * 8 * G + t * 8, &v[c * 8], rc[c]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const float* vc = &v[c * 8];
+      *reinterpret_cast<uint2*>(a.codes + base + c * 8 * G) =
+          make_uint2(pack_codes4(vc[0], vc[1], vc[2], vc[3], rc[c]),
+                     pack_codes4(vc[4], vc[5], vc[6], vc[7], rc[c]));
+    }
+  }
+}
+
 template <typename TIn, int G, int C>
 __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv_sqrt_b) {
   constexpr int LOG2G = (G == 16) ? 4 : (G == 32) ? 5 : 6;
@@ -165,6 +201,11 @@ __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv
   sum = group_sum<G>(sum);
 
   const int64_t base = row * d + t * 8;
+  if (a.mode == ROW_WEIGHT && a.group) {
+    store_group_codes<G, C>(a, row, base, t, v, valid, inv_sqrt_b);
+    if (valid && t == 0 && a.out_aux) a.out_aux[row] = sum * inv_sqrt_b;
+    return;
+  }
   if (a.mode == ROW_WEIGHT) {
     float amax = 0.0f;
 #pragma unroll
@@ -206,6 +247,11 @@ __global__ __launch_bounds__(256) void row_transform_kernel(RowArgs a, float inv
     return;
   }
 
+  if (a.group) {
+    store_group_codes<G, C>(a, row, base, t, v, valid, inv_sqrt_b);
+    if (valid && t == 0 && a.out_aux) a.out_aux[row] = mu * inv_sqrt_b;
+    return;
+  }
   amax = group_max<G>(amax);
   const float rcp = amax > 0.0f ? a.qmax / amax : 0.0f;
   if (valid) {

@@ -40,6 +40,7 @@
 namespace hq {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 struct Frag6 {
   v4i c[3];

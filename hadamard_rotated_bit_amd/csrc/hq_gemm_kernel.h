@@ -82,15 +82,16 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[TM][TN], uint8_t* smem
     float* P = reinterpret_cast<float*>(smem);
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
+    // (prescaled accumulators: unit scales, so y = acc + b + mu c exactly)
     for (int idx = tid; idx < BN; idx += NW * 64) {
       const int64_t nc = n0 + idx < N ? n0 + idx : N - 1;
-      P[idx] = ep.s_w[nc];
+      P[idx] = ep.prescaled ? 1.0f : ep.s_w[nc];
       P[BN + idx] = ep.c[nc];
       P[2 * BN + idx] = ep.bias[nc];
     }
     for (int idx = tid; idx < BM; idx += NW * 64) {
       const int64_t mc = m0 + idx < M ? m0 + idx : M - 1;
-      P[3 * BN + idx] = ep.s_x[mc];
+      P[3 * BN + idx] = ep.prescaled ? 1.0f : ep.s_x[mc];
       P[3 * BN + BM + idx] = ep.mu[mc];
     }
     __syncthreads();

@@ -44,7 +44,10 @@ struct RowArgs {
   float qmax;
   uint8_t* codes;         // rows x d codes in code_fmt (ACT, WEIGHT)
   int code_fmt;           // CodeFmt
-  float* out_s;           // [rows] dequant scale  (ACT, WEIGHT)
+  float* out_s;           // [rows] dequant scale  (ACT, WEIGHT); with group > 0
+                          // [d / group, s_ld], one scale per row and group
+  int group;              // 0: one scale per row; 64: one per 64-channel group
+  int64_t s_ld;           // row stride of out_s between groups (group > 0)
   float* out_aux;         // [rows] mu (ACT, EXPORT) or c (WEIGHT); NULL = not written
   float* out_xt;          // [rows, d] f32         (EXPORT)
   int mode;
@@ -104,6 +107,7 @@ struct GemmEpi {
   void* Y;                // [M, ldy]
   int y_bf16;
   int64_t ldy;
+  int prescaled;          // accumulators already carry s_x s_w (group-wise GEMM)
 };
 // acc = A [M, K] . B [N, K]^T ; epilogue: int32 store to acc_out (ld = ldc) when
 // epi == NULL, else the dequant epilogue. Loads of rows past M / N are
@@ -113,6 +117,12 @@ hipError_t launch_gemm(const int8_t* A, int64_t M, const int8_t* B, int64_t N, i
 // The same product on E2M3 codes (CODES_E2M3 layout, M and N rows; K a
 // multiple of 128) with the FP6 MFMA; rows past M / N in their last 4-row
 // group must be readable (their results are discarded).
+// Group-wise FP6 GEMM with the dequant epilogue: 64-code groups, s_xg [K/64,
+// ld_sx] and s_wg [K/64, ld_sw] one scale per row / column and group; the
+// epilogue adds b + mu c (+ low rank) to the group-scaled sums. K % 128 == 0.
+hipError_t launch_gemm_f6g(const uint8_t* A, int64_t M, const uint8_t* B, int64_t N, int K,
+                           const float* s_xg, int64_t ld_sx, const float* s_wg, int64_t ld_sw,
+                           const GemmEpi* epi, hipStream_t s);
 hipError_t launch_gemm_f6(const uint8_t* A, int64_t M, const uint8_t* B, int64_t N, int K,
                           int32_t* acc_out, int64_t ldc, const GemmEpi* epi, hipStream_t s);
 

@@ -296,6 +296,7 @@ static hipError_t launch_fast_g(const RowArgs& a, int C, int nx, hipStream_t s) 
 }
 
 hipError_t launch_row_fast(const RowArgs& a, const RowGeom& g, hipStream_t s) {
+  if (a.group) return hipErrorNotSupported;  // group-wise scales: general kernel
   const int log2g = g.G == 16 ? 4 : g.G == 32 ? 5 : 6;
   const int nx = a.log2b - 3 - log2g;
   if (nx < 0 || (1 << nx) > g.C) return hipErrorNotSupported;

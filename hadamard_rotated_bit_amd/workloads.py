@@ -31,6 +31,13 @@ not available here:
                    projection (4096 image + 512 text tokens); 0.5 % outlier
                    channels x50; three 1024-point blocks; rank-32 bf16
                    low-rank branch.
+
+One more workload exercises group-wise scales (not one of the five above):
+
+* ``flux_g64``  -- flux_proj's shape and value distribution with the data-free
+                   int4 blog's recipe: 64-point Hadamard blocks, one scale per
+                   row and 64-channel group, rank-32 branch, no smoothing, no
+                   centring.
 """
 from __future__ import annotations
 
@@ -66,6 +73,7 @@ class Workload:
     b_std: float = 0.01
     lr_std: float = 0.02
     mean_std: float = 0.0  # per-channel mean std (student_t3_means only)
+    group: int = 0         # 0: one scale per row; 64: one per row and 64-channel group
 
     @property
     def out_dtype(self) -> str:
@@ -83,8 +91,11 @@ WORKLOADS = {
                        "laplace", 8, 30.0, 30.0, 0.05),
     "flux_proj": Workload(5, "flux_proj", 4608, 3072, 12288, "bf16", 1024, 0.5, 1, 4, 4, 32,
                           "normal", 15, 50.0, 50.0, 0.02),
+    "flux_g64": Workload(6, "flux_g64", 4608, 3072, 12288, "bf16", 64, None, 0, 4, 4, 32,
+                         "normal", 15, 50.0, 50.0, 0.02, group=64),
 }
 ORDER = ["tiny", "dit_fc1", "square4k", "lic_dh", "flux_proj"]
+GROUP_ORDER = ["flux_g64"]
 
 
 def rng(key: int, stream: int) -> np.random.Generator:
@@ -169,10 +180,11 @@ def gen_lowrank(w: Workload):
 def custom(key: int, T: int, d_in: int, d_out: int, *, dtype: str = "f32", block: int = 0,
            alpha: Optional[float] = 0.5, center: int = 1, a_bits: int = 4, w_bits: int = 4,
            rank: int = 0, x_dist: str = "normal", n_outliers: int = 0,
-           outlier: float = 50.0, w_std: float = 0.02) -> Workload:
+           outlier: float = 50.0, w_std: float = 0.02, group: int = 0) -> Workload:
     """An ad-hoc workload for edge-case and ragged-shape tests."""
     return Workload(key, f"custom{key}", T, d_in, d_out, dtype, block or d_in, alpha, center,
-                    a_bits, w_bits, rank, x_dist, n_outliers, outlier, outlier, w_std)
+                    a_bits, w_bits, rank, x_dist, n_outliers, outlier, outlier, w_std,
+                    group=group)
 
 
 def generate(w: Workload, T: Optional[int] = None):

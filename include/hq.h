@@ -23,6 +23,18 @@
  * The optional rank-r branch (blog steps 3-4) is kept in 16-bit and sees the
  * smoothed, un-rotated input x'.
  *
+ * Group-wise scales (hq_desc.group = 64; data-free int4 blog, "Hadamard
+ * rotation: the int4 improvement" and "How it is applied here": one scale per
+ * group of 64 consecutive input channels). X~ gets one scale per token and
+ * group, W~ one per output channel and group, and the accumulator is the sum
+ * of the per-group integer products, each scaled by its two group scales:
+ *
+ *     Y_tj = sum_g s_x[g, t] s_w[g, j] acc_tj^(g) + b_j + mu_t c_j [+ ...],
+ *     acc^(g) = the integer product over channels [64 g, 64 g + 64).
+ *
+ * Scales of G = d_in / 64 groups are stored group-major: s_x as [G, T]
+ * (activation stage) and s_w as [G, d_out_pad] (prepared blob).
+ *
  * Centring modes (hq_desc.center). HQ_CENTER_TOKEN reads mu as above, one
  * mean per token. HQ_CENTER_CHANNEL takes the other reading of the same
  * identity (HadaNorm Fig. 2 caption: "mu, sigma in R^d"; "one added token"):
@@ -79,7 +91,7 @@
 extern "C" {
 #endif
 
-#define HQ_ABI_VERSION 4
+#define HQ_ABI_VERSION 5
 
 typedef enum {
   HQ_OK = 0,
@@ -120,10 +132,12 @@ typedef enum { HQ_CENTER_NONE = 0, HQ_CENTER_TOKEN = 1, HQ_CENTER_CHANNEL = 2 } 
  *  w_dtype dtype of weight, L1 and L2 (hq_dtype).
  *  y_dtype dtype of Y (hq_dtype).
  *  gemm    GEMM engine (hq_gemm_engine); it also fixes the code format.
+ *  group   0: one scale per row; 64: one scale per row and 64-channel group
+ *          (needs a_bits = w_bits = 4 and gemm = HQ_GEMM_AUTO).
  * Bias, sigma and every scale are float32. */
 typedef struct {
   int32_t d_in, d_out, block, a_bits, w_bits, center, smooth, rank;
-  int32_t x_dtype, w_dtype, y_dtype, gemm;
+  int32_t x_dtype, w_dtype, y_dtype, gemm, group;
 } hq_desc;
 
 /* Byte offsets of the arrays inside a prepared blob (all 256-byte aligned). */
@@ -131,7 +145,8 @@ typedef struct {
   size_t total;        /* hq_prepared_bytes                                  */
   size_t w_codes;      /* codes of W~^T, d_out_pad rows (row j = out j), in
                           the descriptor's code format                      */
-  size_t w_scale;      /* f32   [d_out_pad]        s_w (0 for padding rows)     */
+  size_t w_scale;      /* f32   [d_out_pad]        s_w (0 for padding rows);
+                          [d_in / 64, d_out_pad] with group = 64           */
   size_t c;            /* f32   [d_out_pad]        c = 1^T W~                   */
   size_t bias;         /* f32   [d_out_pad]        b (0 if none)                */
   size_t sigma_inv;    /* f32   [d_in]             1 / sigma                    */
@@ -190,7 +205,8 @@ int hq_sigma(const hq_desc* desc, const float* act_absmax, const void* weight, f
 /* Offline weight transform (HadaNorm Eq. (1); HaTQ Sec. IV-D: weight-side
  * transforms are precomputed): for each output row j,
  *   w~_j = (weight_j * sigma) H,  c_j = sum_i w~_ji,
- *   s_w,j = max_i |w~_ji| / qmax,  codes = clamp(round(w~_j / s_w,j), +-qmax),
+ *   s_w,j = max_i |w~_ji| / qmax,  codes = clamp(round(w~_j / s_w,j), +-qmax)
+ *   (with group = 64 the maximum and the scale are taken per 64-channel group),
  * plus 1/sigma, the bias, and for rank > 0 the split low-rank factors.
  *  weight  [d_out, d_in] w_dtype;  bias f32 [d_out] or NULL (zeros);
  *  sigma   f32 [d_in], required iff desc->smooth (sigma > 0);
@@ -226,7 +242,8 @@ int hq_channel_center(const hq_desc* desc, const void* prepared, const void* X, 
 
 /* Activation stage alone: codes of T rows in the descriptor's code format
  * (hq_code_bytes(desc, T) bytes, natural channel order), s_x f32 [T]
- * (dequant scale of the normalised X~ row), mu f32 [T], U f32 [T, rank]
+ * (dequant scale of the normalised X~ row; [d_in / 64, T] with group = 64,
+ * one per token and group), mu f32 [T], U f32 [T, rank]
  * (x' L1; ignored/NULL when rank = 0). For center = 2, mu is instead an
  * INPUT: the mean [d_in] of hq_channel_center. */
 int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
@@ -239,7 +256,9 @@ int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, i
                      float* Xt, float* mu, void* stream);
 
 /* Integer GEMM alone: acc int32 [T, N] = a_codes [T, d_in] . w_codes [N, d_in]^T,
- * both in the descriptor's code format (T and N rows); N a multiple of 8. */
+ * both in the descriptor's code format (T and N rows); N a multiple of 8.
+ * With group = 64 this is still the product over all d_in channels (the sum
+ * of the unscaled per-group products). */
 int hq_gemm_i32(const hq_desc* desc, const void* a_codes, const void* w_codes, int64_t T,
                 int64_t N, int32_t* acc, void* stream);
 

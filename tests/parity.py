@@ -32,7 +32,7 @@ XT_TOL = 1e-5
 def desc_for(w: WL.Workload, gemm: int = hq.HQ_GEMM_AUTO) -> hq.Desc:
     dt = hq.BF16 if w.dtype == "bf16" else hq.F32
     return hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, int(w.center),
-                   w.alpha is not None, w.rank, dt, dt, dt, gemm)
+                   w.alpha is not None, w.rank, dt, dt, dt, gemm, w.group)
 
 
 # (workload, GEMM engine) pairs the parity tests run: every workload on the
@@ -73,7 +73,7 @@ class Case:
         sig = None if self.sigma32 is None else self.sigma32.astype(np.float64)
         self.ora = O.run(self.x, self.weight, self.bias, block=w.block, a_bits=w.a_bits,
                          w_bits=w.w_bits, center=int(w.center), sigma=sig, l1=self.l1,
-                         l2=self.l2, out_dtype=w.out_dtype)
+                         l2=self.l2, out_dtype=w.out_dtype, group=w.group)
         # device tensors
         self.X = tdev(self.x, w.dtype)
         self.W = tdev(self.weight, w.dtype)

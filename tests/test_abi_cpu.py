@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lib.hq_abi_version() == 4
+    assert lib.hq_abi_version() == 5
     assert lib.hq_status_str(0) == b"HQ_OK"
     assert lib.hq_status_str(-3) == b"HQ_ERR_WORKSPACE"
     assert lib.hq_status_str(99) == b"HQ_ERR_UNKNOWN"
@@ -58,7 +58,8 @@ def test_workload_descriptors_valid(name):
     (dict(smooth=5), -1), (dict(a_bits=3), -2), (dict(w_bits=16), -2), (dict(d_in=1000), -2),
     (dict(d_in=2176), -2), (dict(d_out=100), -2), (dict(block=96), -2), (dict(block=256, d_in=1152), -2),
     (dict(rank=8), -2), (dict(rank=128), -2), (dict(d_in=16384), -2), (dict(gemm=2), -1),
-    (dict(gemm=-1), -1),
+    (dict(gemm=-1), -1), (dict(group=32), -2), (dict(group=128), -2), (dict(group=-64), -2),
+    (dict(group=64, a_bits=8), -2), (dict(group=64, w_bits=8), -2), (dict(group=64, gemm=1), -2),
 ])
 def test_validation_rejects(kw, status):
     d = _d(**kw)
@@ -123,6 +124,35 @@ def test_channel_centring_layout(w_dtype, esize):
             lib.hq_workspace_bytes(ctypes.byref(tok), T)
         chunks = (T + 63) // 64
         assert extra >= 4 * (chunks * 1152 + 1152 + Lc.d_out_pad)
+
+
+@pytest.mark.parametrize("center", [0, 1, 2])
+def test_group_layout(center):
+    # group = 64: one weight scale per output channel and group in the blob
+    # ([d_in / 64, d_out_pad], group-major) and one activation scale per token
+    # and group in the workspace
+    row = _d(center=center, d_in=3072, block=64)
+    grp = _d(center=center, d_in=3072, block=64, group=64)
+    assert lib.hq_validate(ctypes.byref(grp)) == 0
+    assert lib.hq_code_format(ctypes.byref(grp)) == _lib.HQ_CODES_E2M3
+    Lr, Lg = _lib.HqLayout(), _lib.HqLayout()
+    assert lib.hq_prepared_layout_of(ctypes.byref(row), ctypes.byref(Lr)) == 0
+    assert lib.hq_prepared_layout_of(ctypes.byref(grp), ctypes.byref(Lg)) == 0
+    G = 3072 // 64
+    assert Lg.c - Lg.w_scale >= 4 * G * Lg.d_out_pad
+    assert Lg.total - Lr.total == (Lg.c - Lg.w_scale) - (Lr.c - Lr.w_scale)
+    for T in [1, 64, 65, 4608]:
+        extra = lib.hq_workspace_bytes(ctypes.byref(grp), T) - \
+            lib.hq_workspace_bytes(ctypes.byref(row), T)
+        a256 = lambda n: (n + 255) // 256 * 256
+        assert extra == a256(4 * G * T) - a256(4 * T)
+
+
+def test_group_desc_python_mirror():
+    d = Desc(3072, 12288, 64, group=64)
+    assert d.c().group == 64
+    assert d.sx_shape(10) == (48, 10)
+    assert Desc(3072, 12288, 64).sx_shape(10) == (10,)
 
 
 def test_channel_center_rejects_other_modes():
