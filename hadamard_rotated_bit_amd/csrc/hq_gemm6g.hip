@@ -27,6 +27,76 @@
 
 namespace hq {
 
+// A fragment from its six 8-byte pieces (two 24-byte operands).
+__device__ __forceinline__ void frag_from_pieces(Frag6& f, const v2i* q) {
+  f.c[0] = v4i{q[0].x, q[0].y, q[1].x, q[1].y};
+  f.c[1] = v4i{q[2].x, q[2].y, q[3].x, q[3].y};
+  f.c[2] = v4i{q[4].x, q[4].y, q[5].x, q[5].y};
+}
+
+// MFMA of tile n of a stage (two groups, TM x TN 32 x 32 tiles per group):
+// group n / (TM TN), column strip (n / TM) % TN, row strip n % TM, into a
+// zeroed temporary.
+template <int TM, int TN, int N>
+__device__ __forceinline__ v16f group_tile_mfma(const Frag6 (&af)[TM], const Frag6 (&bf)[TN]) {
+  constexpr int g = N / (TM * TN), j = (N / TM) % TN, i = N % TM;
+  const v16f zero = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  if constexpr (g == 0) return mfma_f6(f6_op0(bf[j]), f6_op0(af[i]), zero);
+  else return mfma_f6(f6_op1(bf[j]), f6_op1(af[i]), zero);
+}
+
+// Accumulator register r of a lane in half h holds column 8 (r / 4) + 4 h + r % 4
+// of its 32-column strip. Lane l holds the scale of column
+// 8 ((l % 16) / 4) + 4 (l / 32) + l % 4: the 16 lanes of a row hold the 16
+// columns of their half, lane r of the row the one of register r, so DPP
+// row_newbcast:r (every lane of a 16-lane row reads lane r of that row) hands
+// each lane its register-r scale inside the multiply. Written as one asm
+// block (the compiler does not fold the broadcast into a multiply whose
+// operand is shared); the leading s_nop covers the two wait states a DPP
+// read needs after a VALU write of its source.
+__device__ __forceinline__ void scale_products(float (&p)[16], float sw, float sx) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mul_f32_dpp %0, %16, %17 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %1, %16, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %2, %16, %17 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %3, %16, %17 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %4, %16, %17 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %5, %16, %17 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %6, %16, %17 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %7, %16, %17 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %8, %16, %17 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %9, %16, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %10, %16, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %11, %16, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %12, %16, %17 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %13, %16, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %14, %16, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %15, %16, %17 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+      : "=&v"(p[0]), "=&v"(p[1]), "=&v"(p[2]), "=&v"(p[3]), "=&v"(p[4]), "=&v"(p[5]),
+        "=&v"(p[6]), "=&v"(p[7]), "=&v"(p[8]), "=&v"(p[9]), "=&v"(p[10]), "=&v"(p[11]),
+        "=&v"(p[12]), "=&v"(p[13]), "=&v"(p[14]), "=&v"(p[15])
+      : "v"(sw), "v"(sx));
+}
+
+// The MFMAs and rescales of one stage: per tile, the MFMA, the tile's 16
+// scale products (independent of it, so they issue while it runs), then
+// acc += t * s_x * s_w.
+template <int TM, int TN, int N>
+__device__ __forceinline__ void group_tiles(v16f (&acc)[TM][TN], const Frag6 (&af)[TM],
+                                           const Frag6 (&bf)[TN], const float (&sx)[2][TM],
+                                           const float (&sw)[2][TN]) {
+  if constexpr (N < 2 * TM * TN) {
+    constexpr int g = N / (TM * TN), j = (N / TM) % TN, i = N % TM;
+    const v16f t = group_tile_mfma<TM, TN, N>(af, bf);
+    float p[16];
+    scale_products(p, sw[g][j], sx[g][i]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(t[r], p[r], acc[i][j][r]);
+    group_tiles<TM, TN, N + 1>(acc, af, bf, sx, sw);
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int GM, int RG>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(2))) void gemm_f6g_kernel(
@@ -104,7 +174,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_f6g_kernel(
 
   // Fragment of a row: dwords 0-5 = logical bytes [24h, 24h+24) (group 0),
   // dwords 6-11 = [48+24h, 72+24h) (group 1); rows with bit 3 set hold their
-  // 48-byte halves swapped. The LDS reads are written as inline asm that
+  // 48-byte halves swapped. Scales: s_x of the lane's rows wm0 + lrow +
+  // {0, 32}; s_w of column 8 ((l % 16) / 4) + 4 (l / 32) + l % 4 of each
+  // 32-column strip (see scale_products). The LDS reads are written as inline asm that
   // waits for its own results: the compiler would otherwise wait for every
   // stage load in flight (it cannot tell that they fill other buffers).
   static_assert(TM == 2 && TN == 2, "fragment reads are written for 64 x 64 waves");
@@ -116,7 +188,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_f6g_kernel(
   const uint32_t pb0 = pa0 + uint32_t((BM + wn0 - wm0) * 96);
   const uint32_t pb1 = pa1 + uint32_t((BM + wn0 - wm0) * 96);
   const uint32_t psx = lds0 + uint32_t(CODEB + 4 * (wm0 + lrow));
-  const uint32_t psw = lds0 + uint32_t(CODEB + 4 * (2 * BM + wn0 + 4 * lhalf));
+  const uint32_t psw =
+      lds0 + uint32_t(CODEB + 4 * (2 * BM + wn0 + 8 * ((lane & 15) >> 2) + 4 * lhalf + (lane & 3)));
 #define HG_READ(BUF_)                                                                      \
   do {                                                                                     \
     const uint32_t o_ = uint32_t(BUF_) * STAGE;                                            \
@@ -140,48 +213,34 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_f6g_kernel(
           "=&v"(r_[20]), "=&v"(r_[21]), "=&v"(r_[22]), "=&v"(r_[23])                       \
         : "v"(pa0 + o_), "v"(pa1 + o_), "v"(pb0 + o_), "v"(pb1 + o_)                       \
         : "memory");                                                                       \
-    _Pragma("unroll") for (int f_ = 0; f_ < 4; ++f_) {                                     \
-      Frag6& F_ = f_ < 2 ? af[f_] : bf[f_ - 2];                                            \
-      const v2i* q_ = r_ + 6 * f_;                                                         \
-      F_.c[0] = v4i{q_[0].x, q_[0].y, q_[1].x, q_[1].y};                                   \
-      F_.c[1] = v4i{q_[2].x, q_[2].y, q_[3].x, q_[3].y};                                   \
-      F_.c[2] = v4i{q_[4].x, q_[4].y, q_[5].x, q_[5].y};                                   \
-    }                                                                                      \
+    frag_from_pieces(af[0], r_ + 0);                                                       \
+    frag_from_pieces(af[1], r_ + 6);                                                       \
+    frag_from_pieces(bf[0], r_ + 12);                                                      \
+    frag_from_pieces(bf[1], r_ + 18);                                                      \
   } while (0)
   // Both groups of the stage in buffer BUF_: MFMA into a zeroed temporary,
   // then acc += temp * s_x[row] * s_w[col]. Group GI_'s scales: s_x of the
   // lane's rows wm0 + lrow + {0, 32}, s_w of its 16 columns.
-#define HG_SCALES(BUF_, GI_)                                                               \
+#define HG_SCALES(BUF_)                                                                    \
   do {                                                                                     \
-    const uint32_t o_ = uint32_t(BUF_) * STAGE + uint32_t(GI_) * (4 * BM);                 \
+    const uint32_t o_ = uint32_t(BUF_) * STAGE;                                            \
     asm volatile(                                                                          \
-        "ds_read_b32 %0, %10\n ds_read_b32 %1, %10 offset:128\n"                          \
-        "ds_read_b128 %2, %11\n ds_read_b128 %3, %11 offset:32\n"                         \
-        "ds_read_b128 %4, %11 offset:64\n ds_read_b128 %5, %11 offset:96\n"               \
-        "ds_read_b128 %6, %11 offset:128\n ds_read_b128 %7, %11 offset:160\n"             \
-        "ds_read_b128 %8, %11 offset:192\n ds_read_b128 %9, %11 offset:224\n"             \
+        "ds_read_b32 %0, %8\n ds_read_b32 %1, %8 offset:128\n"                            \
+        "ds_read_b32 %2, %8 offset:512\n ds_read_b32 %3, %8 offset:640\n"                 \
+        "ds_read_b32 %4, %9\n ds_read_b32 %5, %9 offset:128\n"                            \
+        "ds_read_b32 %6, %9 offset:512\n ds_read_b32 %7, %9 offset:640\n"                 \
         "s_waitcnt lgkmcnt(0)"                                                             \
-        : "=&v"(sx_[0]), "=&v"(sx_[1]), "=&v"(sw_[0][0]), "=&v"(sw_[0][1]),                \
-          "=&v"(sw_[0][2]), "=&v"(sw_[0][3]), "=&v"(sw_[1][0]), "=&v"(sw_[1][1]),          \
-          "=&v"(sw_[1][2]), "=&v"(sw_[1][3])                                               \
+        : "=&v"(sx_[0][0]), "=&v"(sx_[0][1]), "=&v"(sx_[1][0]), "=&v"(sx_[1][1]),          \
+          "=&v"(sw_[0][0]), "=&v"(sw_[0][1]), "=&v"(sw_[1][0]), "=&v"(sw_[1][1])           \
         : "v"(psx + o_), "v"(psw + o_)                                                     \
         : "memory");                                                                       \
   } while (0)
 #define HG_MATH(BUF_)                                                                      \
   do {                                                                                     \
-    _Pragma("unroll") for (int gi = 0; gi < 2; ++gi) {                                     \
-      float sx_[TM];                                                                       \
-      v4f sw_[TN][4];                                                                      \
-      HG_SCALES(BUF_, gi);                                                                 \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                     \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                   \
-          const v16f t_ = mfma_f6(gi ? f6_op1(bf[j]) : f6_op0(bf[j]),                      \
-                                  gi ? f6_op1(af[i]) : f6_op0(af[i]), zero);               \
-          _Pragma("unroll") for (int r = 0; r < 16; ++r)                                   \
-            acc[i][j][r] = fmaf(t_[r], sx_[i] * sw_[j][r >> 2][r & 3], acc[i][j][r]);      \
-        }                                                                                  \
-      }                                                                                    \
-    }                                                                                      \
+    float sx_[2][TM];                                                                      \
+    float sw_[2][TN];                                                                      \
+    HG_SCALES(BUF_);                                                                       \
+    group_tiles<TM, TN, 0>(acc, af, bf, sx_, sw_);                                         \
   } while (0)
 #define HG_STEP(KT_)                                                                       \
   do {                                                                                     \
@@ -208,9 +267,39 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_f6g_kernel(
 #undef HG_STEP
 #undef HG_MATH
 #undef HG_SCALES
+#undef HG_SCALES
 #undef HG_READ
 #undef HG_ISSUE
 
+  if (ep.y_bf16) {
+    // bf16 output staged through LDS (whole row segments per store). The
+    // accumulators already carry both scales, so the staged parameter block
+    // holds unit s_w and s_x next to c, b and mu; it sits in the last stage
+    // buffer, clear of the output tile.
+    static_assert(BM * (2 * BN + 8) <= 2 * STAGE && 4 * (3 * BN + 2 * BM) <= STAGE,
+                  "output tile and parameters fit");
+    float* P = reinterpret_cast<float*>(smem + 2 * STAGE);
+    __builtin_amdgcn_s_barrier();   // every wave is past its last stage read
+    for (int idx = tid; idx < BN; idx += NW * 64) {
+      const int64_t nc = n0 + idx < N ? n0 + idx : N - 1;
+      P[idx] = 1.0f;
+      P[BN + idx] = ep.c[nc];
+      P[2 * BN + idx] = ep.bias[nc];
+    }
+    for (int idx = tid; idx < BM; idx += NW * 64) {
+      const int64_t mc = m0 + idx < M ? m0 + idx : M - 1;
+      P[3 * BN + idx] = 1.0f;
+      P[3 * BN + BM + idx] = ep.mu[mc];
+    }
+    __syncthreads();
+    if (ep.rank)
+      gemm_epilogue_bf16_staged<BM, BN, TM, TN, NW, true>(acc, smem, P, tid, lane, m0, n0, wm0,
+                                                          wn0, M, N, ep);
+    else
+      gemm_epilogue_bf16_staged<BM, BN, TM, TN, NW, false>(acc, smem, P, tid, lane, m0, n0, wm0,
+                                                           wn0, M, N, ep);
+    return;
+  }
   gemm_epilogue<BM, BN, TM, TN, NW, true>(acc, smem, tid, lane, m0, n0, wm0, wn0, M, N, nullptr,
                                          0, ep);
 }
