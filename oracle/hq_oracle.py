@@ -21,7 +21,9 @@ titles; equations as numbered on those pages):
   accumulation; Sec. III-C Eq. (7)-(8), the normalised Hadamard transform;
   Sec. IV-B Eq. (13)-(14), double-Hadamard quantisation; Sec. IV-C Eq. (23),
   the constant-basis component; Eq. (18), the accumulator scale s_x s_w;
-  supplement Sec. VII-A Eq. (32)-(34), the Sylvester construction.
+  supplement Sec. VII-A Eq. (32)-(34), the Sylvester construction; Sec. IV-B
+  Eq. (15)-(22) with supplement Eq. (40)-(44), the weight-only Hadamard layer
+  and its integer requantisation (section "Weight-only Hadamard layer" below).
 * "Data-free 4-bit quantization for diffusion transformers" (blog), section
   "Hadamard rotation: the int4 improvement", steps 2-7 and "How it is applied
   here": block-diagonal Hadamard over contiguous channel blocks, and the
@@ -344,6 +346,119 @@ def run(x, weight, bias, *, block: int, a_bits: int, w_bits: int, center,
 
 # --------------------------------------------------------------------------
 # Diagnostics (not parity gates)
+# --------------------------------------------------------------------------
+# Weight-only Hadamard layer with integer requantisation
+# --------------------------------------------------------------------------
+#
+# HaTQ Sec. IV-B: the weight is transformed along its output channels,
+# W-bar = H_out W (supplement Eq. (40), T_out = H_out symmetric, so
+# (T_out)^T W = H_out W and b-bar = b H_out), the activation stays in its
+# original basis with one static per-tensor scale, and the int8 product is
+# mapped back to the original basis and onto the next layer's int8 grid with
+# integers only (Eq. (19)-(22) with the identity activation, a WH layer
+# followed by a WH layer: H_out before phi, no input transform after it,
+# gamma = sqrt(m_out)). Readings taken where the pages leave a step open:
+# * H_out is the normalised Sylvester matrix of order m (a power of two
+#   dividing d_out), block-diagonal over d_out / m blocks of output channels;
+#   m = d_out is the pages' full transform.
+# * M_c = round(2^n rho_c) with one shared shift n: the largest n in [0, 48]
+#   for which every M_c fits a positive 16-bit integer (<= 32767), the
+#   multiplier-precision constraint of Eq. (19); n = 0 when every rho_c is 0.
+# * round() is round half to even throughout, on exact rationals.
+# * Codes are symmetric in [-qmax, qmax] (qmax = 127 for 8 bits).
+
+RQ_MULT_MAX = 32767
+RQ_SHIFT_MAX = 48
+
+
+def round_half_even_shift(v, n: int) -> np.ndarray:
+    """round(v / 2^n), ties to even, for integer v (exact; numpy int64)."""
+    v = np.asarray(v, dtype=np.int64)
+    if n == 0:
+        return v.copy()
+    q = v >> n                      # floor division (arithmetic shift)
+    r = v - (q << n)                # 0 <= r < 2^n
+    half = np.int64(1) << (n - 1)
+    up = (r > half) | ((r == half) & ((q & 1) == 1))
+    return q + up.astype(np.int64)
+
+
+def requant_shift(rho) -> int:
+    """The shared right shift n of Eq. (19) (see the reading above)."""
+    rho = np.asarray(rho, dtype=np.float64)
+    top = float(rho.max()) if rho.size else 0.0
+    if top <= 0.0:
+        return 0
+    n = 0
+    while n < RQ_SHIFT_MAX and np.rint(top * 2.0 ** (n + 1)) <= RQ_MULT_MAX:
+        n += 1
+    return n
+
+
+def unnormalised_transform(u, block: int) -> np.ndarray:
+    """The integer transform of Eq. (20): each block of ``block`` channels of
+    every row multiplied by the +-1 Sylvester matrix (additions and
+    subtractions only; exact in int64)."""
+    u = np.asarray(u, dtype=np.int64)
+    t, d = u.shape
+    h = sylvester(block).astype(np.int64)
+    return (u.reshape(t, d // block, block) @ h).reshape(t, d)
+
+
+def wh_prepare(weight, bias, s_x: float, s_y: float, block: int, w_bits: int = 8):
+    """Offline half of a WH layer (HaTQ Eq. (15)-(19), supplement Eq. (40)-(44)).
+
+    weight [d_out, d_in] (row c = output channel c), bias [d_out], s_x the
+    static scale of the int8 input, s_y the scale of the int8 output (the
+    next layer's input scale), block = m, the order of H_out.
+    Returns W-bar, b-bar, the weight codes and scales, the bias codes
+    b_int = round(b-bar / (s_x s_w)), rho, the shift n and the multipliers M."""
+    weight = np.asarray(weight, dtype=np.float64)
+    d_out = weight.shape[0]
+    if d_out % block:
+        raise ValueError("block must divide d_out")
+    # H_out acts on the output-channel index: column-wise on weight, row-wise on b
+    wbar = rotate(weight.T, block).T
+    bbar = rotate(np.asarray(bias, dtype=np.float64)[None, :], block)[0]
+    qw, s_w = quantize_rows(wbar, w_bits)
+    s_a = float(s_x) * s_w
+    b_int = np.zeros(d_out, dtype=np.int64)
+    nz = s_a > 0
+    b_int[nz] = np.rint(bbar[nz] / s_a[nz]).astype(np.int64)
+    rho = s_a / (np.sqrt(block) * float(s_y))
+    n = requant_shift(rho)
+    m_c = np.rint(rho * 2.0 ** n).astype(np.int64)
+    return {"wbar": wbar, "bbar": bbar, "qw": qw, "s_w": s_w, "b_int": b_int, "rho": rho,
+            "shift": n, "mult": m_c, "block": block, "s_x": float(s_x), "s_y": float(s_y)}
+
+
+def wh_forward_int(x_int, prep, bits: int = 8) -> dict:
+    """Online integer path of a WH layer: a = x_int w-bar_int^T + b_int (Eq. (4)),
+    v = H~_out (M . a) (Eq. (20)), y_int = clamp(round(v / 2^n), +-qmax) (Eq. (22)
+    with the identity activation and no input-side transform)."""
+    qmax = 2 ** (bits - 1) - 1
+    a = int_gemm(x_int, prep["qw"]) + prep["b_int"][None, :]
+    u = a * prep["mult"][None, :]
+    v = unnormalised_transform(u, prep["block"])
+    y = np.clip(round_half_even_shift(v, prep["shift"]), -qmax, qmax)
+    return {"acc": a, "u": u, "v": v, "y_int": y.astype(np.int16)}
+
+
+def wh_dequant_reference(x_int, prep) -> np.ndarray:
+    """The dequantised WH output of Eq. (17) with the bias codes, in the
+    original basis and in units of s_y: (s_A . a) H_out / s_y (float64)."""
+    a = int_gemm(x_int, prep["qw"]) + prep["b_int"][None, :]
+    ya = a.astype(np.float64) * (prep["s_x"] * prep["s_w"])[None, :]
+    return rotate(ya, prep["block"]) / prep["s_y"]
+
+
+def quantize_static(x, s: float, bits: int = 8) -> np.ndarray:
+    """Per-tensor symmetric quantisation with a fixed scale (the int8 operand
+    of Sec. III-B): clamp(round(x / s), +-qmax), ties to even."""
+    qmax = 2 ** (bits - 1) - 1
+    return np.clip(np.rint(np.asarray(x, dtype=np.float64) / s), -qmax, qmax).astype(np.int16)
+
+
 # --------------------------------------------------------------------------
 
 def sqnr_db(ref: np.ndarray, approx: np.ndarray) -> float:

@@ -1,7 +1,8 @@
 """Pins for the CPU oracle: each checks it against something other than itself.
 
-Sources: HadaNorm Eq. (1) and (3); HaTQ Eq. (3), (4), (7), (8), (13), (23),
-(32)-(34); the data-free int4 blog's H_64 Kronecker form (step 7). Pins are
+Sources: HadaNorm Eq. (1) and (3); HaTQ Eq. (3), (4), (7), (8), (13), (15)-(22),
+(23), (32)-(34), supplement Eq. (40)-(44); the data-free int4 blog's H_64
+Kronecker form (step 7). Pins are
 closed forms, independent constructions (popcount formula, Kronecker power,
 scipy's Hadamard routine), brute force on tiny inputs, invariants, and the
 hand-worked fixtures under tests/golden/.
@@ -468,3 +469,121 @@ def test_quantised_layer_converges_and_rotation_helps():
     r0 = O.run(x, weight, bias, block=1, a_bits=4, w_bits=4, center=False)
     assert s4 > O.sqnr_db(exact, r0["y_full"]) + 3
     assert O.excess_kurtosis(r4["xt"]) < O.excess_kurtosis(x)
+
+
+# ------------------------------------- weight-only Hadamard + integer requantisation
+
+def _block_h(d: int, m: int) -> np.ndarray:
+    """Block-diagonal normalised Hadamard of order m over d channels, built
+    with scipy (independent of the oracle's Sylvester recursion)."""
+    return np.kron(np.eye(d // m), scipy.linalg.hadamard(m) / np.sqrt(m))
+
+
+def _wh_inputs(seed=3, T=40, d_in=96, d_out=64):
+    rng = np.random.default_rng(seed)
+    x = rng.laplace(0.0, 1.0, (T, d_in))
+    x[:, 5] *= 20.0
+    weight = rng.normal(0.0, 0.05, (d_out, d_in))
+    bias = rng.normal(0.0, 0.05, d_out)
+    y = x @ weight.T + bias
+    return x, weight, bias, np.abs(x).max() / 127, np.abs(y).max() / 127
+
+
+@pytest.mark.parametrize("m", [1, 2, 16, 64])
+def test_wh_weight_transform_and_identity(m):
+    # W-bar = H_out W and b-bar = b H_out (supplement Eq. (40)) from a
+    # scipy-built H; the float WH identity Eq. (41): (X W-bar^T + b-bar) H_out^T = X W^T + b
+    x, weight, bias, s_x, s_y = _wh_inputs()
+    p = O.wh_prepare(weight, bias, s_x, s_y, m)
+    h = _block_h(weight.shape[0], m)
+    np.testing.assert_allclose(p["wbar"], h @ weight, atol=1e-14)
+    np.testing.assert_allclose(p["bbar"], bias @ h, atol=1e-14)
+    np.testing.assert_allclose((x @ p["wbar"].T + p["bbar"]) @ h.T, x @ weight.T + bias,
+                               atol=1e-12)
+
+
+def test_round_half_even_shift_brute_force():
+    from fractions import Fraction
+    v = np.arange(-70, 71, dtype=np.int64)
+    for n in [0, 1, 2, 3, 5]:
+        got = O.round_half_even_shift(v, n)
+        ref = [round(Fraction(int(a), 2 ** n)) for a in v]   # Python rounds halves to even
+        assert got.tolist() == ref
+    big = np.array([(1 << 45) + (1 << 19), -(1 << 45) - 3 * (1 << 19)], dtype=np.int64)
+    assert O.round_half_even_shift(big, 20).tolist() == [(1 << 25), -(1 << 25) - 2]
+
+
+def test_requant_shift_is_maximal():
+    rng = np.random.default_rng(4)
+    for top in [1e-7, 3.3e-5, 0.25, 0.5, 1.0, 700.0, 32767.0]:
+        rho = rng.uniform(0, top, 50)
+        rho[7] = top
+        n = O.requant_shift(rho)
+        assert np.rint(top * 2.0 ** n) <= O.RQ_MULT_MAX
+        assert n == O.RQ_SHIFT_MAX or np.rint(top * 2.0 ** (n + 1)) > O.RQ_MULT_MAX
+    assert O.requant_shift(np.zeros(4)) == 0
+
+
+@pytest.mark.parametrize("m", [2, 8, 64])
+def test_unnormalised_transform_twice_is_m_identity(m):
+    # H~ H~ = m I for a Sylvester matrix (Eq. (7)); exact in integers
+    rng = np.random.default_rng(5)
+    u = rng.integers(-2 ** 40, 2 ** 40, (6, 128), dtype=np.int64)
+    twice = O.unnormalised_transform(O.unnormalised_transform(u, m), m)
+    assert np.array_equal(twice, m * u)
+    h = scipy.linalg.hadamard(m).astype(np.int64)
+    np.testing.assert_array_equal(O.unnormalised_transform(u, m)[:, :m], u[:, :m] @ h)
+
+
+@pytest.mark.parametrize("m", [1, 4, 64])
+def test_wh_integer_path_within_its_rounding_bound(m):
+    # y_int = clamp(round(H~(M . a) / 2^n)) against the dequantised Eq. (17)
+    # output in units of s_y, H~(rho . a): they differ by the final rounding
+    # (1/2) plus the multiplier rounding |M - 2^n rho| <= 1/2 on each channel.
+    x, weight, bias, s_x, s_y = _wh_inputs()
+    p = O.wh_prepare(weight, bias, s_x, s_y, m)
+    xi = O.quantize_static(x, s_x)
+    r = O.wh_forward_int(xi, p)
+    ref = O.wh_dequant_reference(xi, p)
+    a = np.abs(r["acc"]).astype(np.float64)
+    bound = 0.5 + 0.5 * (a.reshape(a.shape[0], -1, m).sum(axis=2).repeat(m, axis=1)) / 2.0 ** p["shift"]
+    assert np.all(np.abs(r["y_int"] - np.clip(ref, -127, 127)) <= bound + 1e-9)
+    # and the layer is reproduced to int8 accuracy
+    assert O.sqnr_db((x @ weight.T + bias) / s_y, r["y_int"].astype(np.float64)) > 25
+
+
+def test_wh_bias_only_passes_back_to_original_basis():
+    # x = 0: a = b_int, and the restored output is b / s_y up to the bias and
+    # multiplier roundings (the bias is transformed with the weight, Eq. (40),
+    # and H_out brings it back)
+    x, weight, bias, s_x, s_y = _wh_inputs()
+    m = 16
+    p = O.wh_prepare(weight, bias, s_x, s_y, m)
+    r = O.wh_forward_int(np.zeros((1, weight.shape[1]), dtype=np.int16), p)
+    err_b = np.abs(p["b_int"] - p["bbar"] / (s_x * p["s_w"]))          # <= 1/2 each
+    assert err_b.max() <= 0.5 + 1e-9
+    # H~(rho . b-bar / s_A) = H b-bar / s_y = b / s_y; the bias rounding adds at most
+    # (1/2) sum rho over the block, the multiplier rounding (1/2) sum |b_int| / 2^n
+    bound = 0.5 + (0.5 * p["rho"].reshape(-1, m).sum(axis=1).repeat(m)
+                   + 0.5 * np.abs(p["b_int"]).reshape(-1, m).sum(axis=1).repeat(m) / 2.0 ** p["shift"])
+    assert np.all(np.abs(r["y_int"][0] - np.clip(bias / s_y, -127, 127)) <= bound + 1e-9)
+
+
+def test_wh_hand_example():
+    g = load_golden("wh_requant_example.txt")
+    weight = g["weight"].reshape(2, 1)
+    p = O.wh_prepare(weight, g["bias"], g["s_x"].item(), g["s_y"].item(), int(g["block"].item()))
+    assert p["qw"].ravel().tolist() == g["codes"].ravel().tolist()
+    assert p["shift"] == int(g["shift"].item())
+    assert p["mult"].tolist() == g["mult"].astype(int).tolist()
+    r = O.wh_forward_int(np.array([[int(g["x_int"].item())]]), p)
+    assert r["v"][0].tolist() == g["v"].astype(int).tolist()
+    assert r["y_int"][0].tolist() == g["y_int"].astype(int).tolist()
+
+
+def test_wh_rejects_bad_block():
+    x, weight, bias, s_x, s_y = _wh_inputs()
+    with pytest.raises(ValueError):
+        O.wh_prepare(weight, bias, s_x, s_y, 3)
+    with pytest.raises(ValueError):
+        O.wh_prepare(weight, bias, s_x, s_y, 128)
