@@ -321,3 +321,95 @@ def prepared_views(desc: Desc, prepared: torch.Tensor) -> dict:
     if _channel(desc):
         out["weight"] = view(L.weight, desc.d_out * d, _TORCH[desc.w_dtype], (desc.d_out, d))
     return out
+
+
+# ---- weight-only Hadamard layer with integer requantisation ----------------
+
+@dataclasses.dataclass(frozen=True)
+class WhDesc:
+    """Descriptor of a weight-only Hadamard layer; mirrors hq_wh_desc
+    (block = m, the order of the output-side Hadamard transform)."""
+    d_in: int
+    d_out: int
+    block: int
+    w_dtype: int = F32
+
+    def __post_init__(self):
+        raw = _lib.HqWhDesc(self.d_in, self.d_out, self.block, self.w_dtype)
+        object.__setattr__(self, "_raw", raw)
+        object.__setattr__(self, "_ref", ctypes.byref(raw))
+
+
+def wh_layout(desc: WhDesc) -> "_lib.HqWhLayout":
+    out = _lib.HqWhLayout()
+    check(load().hq_wh_prepared_layout_of(desc._ref, ctypes.byref(out)))
+    return out
+
+
+def wh_workspace_bytes(desc: WhDesc, T: int) -> int:
+    if T < 0:
+        raise HqError(_lib.HQ_ERR_INVALID_ARG, "T must be >= 0")
+    n = load().hq_wh_workspace_bytes(desc._ref, T)
+    if n == 0:
+        check(load().hq_wh_validate(desc._ref))
+    return n
+
+
+def wh_prepare(desc: WhDesc, weight: torch.Tensor, bias: Optional[torch.Tensor], s_x: float,
+               s_y: float) -> torch.Tensor:
+    """Offline WH weight transform; returns the prepared blob (uint8 device tensor)."""
+    _need(weight, "weight", _TORCH[desc.w_dtype], (desc.d_out, desc.d_in))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (desc.d_out,))
+    n = load().hq_wh_prepared_bytes(desc._ref)
+    if n == 0:
+        check(load().hq_wh_validate(desc._ref))
+    blob = torch.empty(n, dtype=torch.uint8, device=weight.device)
+    check(load().hq_wh_prepare(desc._ref, _ptr(weight), _ptr(bias), ctypes.c_float(s_x),
+                               ctypes.c_float(s_y), _ptr(blob), _stream()))
+    return blob
+
+
+def wh_linear(desc: WhDesc, prepared: torch.Tensor, x_codes: torch.Tensor,
+              out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int8 output codes [T, d_out] of the WH layer for int8 input codes [T, d_in]."""
+    T = x_codes.shape[0]
+    _need(x_codes, "x_codes", torch.int8, (T, desc.d_in))
+    y = out if out is not None else torch.empty(T, desc.d_out, dtype=torch.int8,
+                                                 device=x_codes.device)
+    _need(y, "out", torch.int8, (T, desc.d_out))
+    nws = wh_workspace_bytes(desc, T)
+    ws = workspace if workspace is not None else torch.empty(
+        max(nws, 1), dtype=torch.uint8, device=x_codes.device)
+    check(load().hq_wh_linear(desc._ref, _ptr(prepared), _ptr(x_codes), T, _ptr(y), _ptr(ws),
+                              ws.numel(), _stream()))
+    return y
+
+
+def wh_requant(desc: WhDesc, prepared: torch.Tensor, acc: torch.Tensor) -> torch.Tensor:
+    """Requantisation alone: int8 [T, d_out] from int32 products [T, d_out] (no bias)."""
+    T = acc.shape[0]
+    _need(acc, "acc", torch.int32, (T, desc.d_out))
+    y = torch.empty(T, desc.d_out, dtype=torch.int8, device=acc.device)
+    check(load().hq_wh_requant(desc._ref, _ptr(prepared), _ptr(acc), T, _ptr(y), _stream()))
+    return y
+
+
+def wh_views(desc: WhDesc, prepared: torch.Tensor) -> dict:
+    """Views of the arrays inside a WH prepared blob (for inspection and tests)."""
+    L = wh_layout(desc)
+    npad, d = L.d_out_pad, desc.d_in
+
+    def view(off, n, dtype, shape):
+        nbytes = n * torch.empty(0, dtype=dtype).element_size()
+        return prepared[off:off + nbytes].view(dtype).view(*shape)
+
+    return {
+        "w_codes": view(L.w_codes, npad * d, torch.int8, (npad, d))[:desc.d_out],
+        "s_w": view(L.w_scale, npad, torch.float32, (npad,))[:desc.d_out],
+        "b_int": view(L.b_int, npad, torch.int32, (npad,))[:desc.d_out],
+        "mult": view(L.mult, npad, torch.int32, (npad,))[:desc.d_out],
+        "shift": view(L.shift, 1, torch.int32, (1,)),
+        "wbar": view(L.wbar, desc.d_out * d, torch.float32, (desc.d_out, d)),
+    }

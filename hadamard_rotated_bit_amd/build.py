@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhq.so")
-SOURCES = ["hq_act.hip", "hq_rowfast.hip", "hq_center.hip", "hq_gemm.hip", "hq_gemm6.hip", "hq_gemm6g.hip", "hq_abi.cpp"]
+SOURCES = ["hq_act.hip", "hq_rowfast.hip", "hq_center.hip", "hq_gemm.hip", "hq_gemm6.hip", "hq_gemm6g.hip", "hq_wh.hip",
+           "hq_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU forms.

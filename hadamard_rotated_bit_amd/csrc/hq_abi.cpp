@@ -264,6 +264,71 @@ int run_gemm_dequant(const hq_desc* d, const void* prepared, const void* codes,
   return HQ_OK;
 }
 
+// ---- weight-only Hadamard layer --------------------------------------------
+
+constexpr uint32_t kMagicWH = 0x31575148u;  // "HQW1"
+
+struct WhHeader {
+  uint32_t magic;
+  uint32_t version;
+  hq_wh_desc desc;
+  int64_t d_out_pad;
+  uint64_t total;
+  float s_x, s_y;
+};
+static_assert(sizeof(WhHeader) <= 256, "header fits in 256 bytes");
+
+int check_wh_desc(const hq_wh_desc* d) {
+  if (!d) return fail(HQ_ERR_INVALID_ARG, "desc is NULL");
+  if (d->d_in <= 0 || d->d_out <= 0)
+    return fail(HQ_ERR_INVALID_ARG, "d_in and d_out must be positive (got %d, %d)", d->d_in,
+                d->d_out);
+  if (d->w_dtype != HQ_F32 && d->w_dtype != HQ_BF16)
+    return fail(HQ_ERR_INVALID_ARG, "w_dtype %d is not an hq_dtype", d->w_dtype);
+  hq::RowGeom g;
+  if (d->d_in % 128 || !hq::row_geometry(d->d_in, &g))
+    return fail(HQ_ERR_UNSUPPORTED,
+                "d_in %d unsupported: need a multiple of 128 up to 2048, of 256 up to 4096, or "
+                "of 512 up to 8192",
+                d->d_in);
+  if (d->d_out % 8)
+    return fail(HQ_ERR_UNSUPPORTED, "d_out must be a multiple of 8 (got %d)", d->d_out);
+  if (!is_pow2(d->block) || d->block > hq::WH_MAX_BLOCK || d->d_out % d->block)
+    return fail(HQ_ERR_UNSUPPORTED, "block %d must be a power of two <= %d dividing d_out %d",
+                d->block, hq::WH_MAX_BLOCK, d->d_out);
+  return HQ_OK;
+}
+
+void wh_layout_of(const hq_wh_desc* d, hq_wh_layout* L) {
+  const int64_t np = round_up(d->d_out, hq::GEMM_BN);
+  size_t off = 256;
+  L->d_out_pad = np;
+  L->w_codes = off;
+  off += align256(size_t(np) * d->d_in);
+  L->w_scale = off;
+  off += align256(4 * size_t(np));
+  L->b_int = off;
+  off += align256(4 * size_t(np));
+  L->mult = off;
+  off += align256(4 * size_t(np));
+  L->shift = off;
+  off += 256;
+  L->wbar = off;
+  off += align256(4 * size_t(d->d_out) * d->d_in);
+  L->total = off;
+}
+
+int run_wh_requant(const hq_wh_desc* d, const void* prepared, const int32_t* acc, int64_t T,
+                   int8_t* y, hipStream_t s) {
+  hq_wh_layout L;
+  wh_layout_of(d, &L);
+  hipError_t e = hq::launch_wh_requant(acc, d->d_out, T, d->d_out, d->block,
+                                       at<int32_t>(prepared, L.b_int),
+                                       at<int32_t>(prepared, L.mult),
+                                       at<int32_t>(prepared, L.shift), y, d->d_out, s);
+  return e == hipSuccess ? HQ_OK : hip_fail(e, "requantisation kernel launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -581,6 +646,132 @@ int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes
     return fail(HQ_ERR_INVALID_ARG, "Y, codes and prepared must be 16-byte aligned");
   return run_gemm_dequant(desc, prepared, codes, s_x, mu, U, T, Y,
                           static_cast<hipStream_t>(stream));
+}
+
+int hq_wh_validate(const hq_wh_desc* desc) {
+  g_err.clear();
+  return check_wh_desc(desc);
+}
+
+size_t hq_wh_prepared_bytes(const hq_wh_desc* desc) {
+  g_err.clear();
+  if (check_wh_desc(desc) != HQ_OK) return 0;
+  hq_wh_layout L;
+  wh_layout_of(desc, &L);
+  return L.total;
+}
+
+int hq_wh_prepared_layout_of(const hq_wh_desc* desc, hq_wh_layout* out) {
+  g_err.clear();
+  if (!out) return fail(HQ_ERR_INVALID_ARG, "out is NULL");
+  int st = check_wh_desc(desc);
+  if (st != HQ_OK) return st;
+  wh_layout_of(desc, out);
+  return HQ_OK;
+}
+
+size_t hq_wh_workspace_bytes(const hq_wh_desc* desc, int64_t T) {
+  g_err.clear();
+  if (check_wh_desc(desc) != HQ_OK) return 0;
+  if (T < 0) {
+    fail(HQ_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+    return 0;
+  }
+  return align256(4 * size_t(T) * desc->d_out);
+}
+
+int hq_wh_prepare(const hq_wh_desc* desc, const void* weight, const float* bias, float s_x,
+                  float s_y, void* prepared, void* stream) {
+  g_err.clear();
+  int st = check_wh_desc(desc);
+  if (st != HQ_OK) return st;
+  if (!weight || !prepared) return fail(HQ_ERR_INVALID_ARG, "weight and prepared must be non-NULL");
+  if (!(s_x > 0.0f) || !(s_y > 0.0f) || !std::isfinite(s_x) || !std::isfinite(s_y))
+    return fail(HQ_ERR_INVALID_ARG, "s_x and s_y must be positive and finite (got %g, %g)",
+                double(s_x), double(s_y));
+  if (misaligned(prepared)) return fail(HQ_ERR_INVALID_ARG, "prepared must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hq_wh_layout L;
+  wh_layout_of(desc, &L);
+  const int64_t np = L.d_out_pad, dout = desc->d_out, din = desc->d_in;
+  hipError_t e = hipSuccess;
+  if (np > dout)
+    e = hq::launch_fill_u8(at<uint8_t>(prepared, L.w_codes + size_t(dout) * din), 0,
+                           size_t(np - dout) * din, s);
+  if (e == hipSuccess)
+    e = hq::launch_fill_u32(at<uint32_t>(prepared, L.w_scale), 0u, size_t(np), s);
+  if (e == hipSuccess)
+    e = hq::launch_wh_weight(weight, desc->w_dtype == HQ_BF16, int(dout), int(din), desc->block,
+                             at<float>(prepared, L.wbar), s);
+  if (e == hipSuccess) {
+    // per-output-channel 8-bit codes of W-bar (no further rotation)
+    hq::RowArgs a = {};
+    a.in = at<float>(prepared, L.wbar);
+    a.in_bf16 = 0;
+    a.rows = dout;
+    a.d = int(din);
+    a.log2b = 0;
+    a.qmax = 127.0f;
+    a.codes = at<uint8_t>(prepared, L.w_codes);
+    a.code_fmt = hq::CODES_I8;
+    a.out_s = at<float>(prepared, L.w_scale);
+    a.mode = hq::ROW_WEIGHT;
+    e = hq::launch_row_transform(a, s);
+  }
+  if (e == hipSuccess)
+    e = hq::launch_wh_constants(bias, at<float>(prepared, L.w_scale), int(dout), int(np),
+                                desc->block, s_x, s_y, at<int32_t>(prepared, L.b_int),
+                                at<int32_t>(prepared, L.mult), at<int32_t>(prepared, L.shift), s);
+  if (e == hipSuccess) {
+    WhHeader h = {};
+    h.magic = kMagicWH;
+    h.version = HQ_ABI_VERSION;
+    h.desc = *desc;
+    h.d_out_pad = np;
+    h.total = L.total;
+    h.s_x = s_x;
+    h.s_y = s_y;
+    e = hq::launch_write_header(&h, sizeof(h), prepared, s);
+  }
+  return e == hipSuccess ? HQ_OK : hip_fail(e, "WH prepare kernel launch");
+}
+
+int hq_wh_linear(const hq_wh_desc* desc, const void* prepared, const int8_t* x_codes, int64_t T,
+                 int8_t* y_codes, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int st = check_wh_desc(desc);
+  if (st != HQ_OK) return st;
+  if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+  if (T == 0) return HQ_OK;
+  if (!prepared || !x_codes || !y_codes || !workspace)
+    return fail(HQ_ERR_INVALID_ARG, "prepared, x_codes, y_codes and workspace must be non-NULL");
+  if (misaligned(x_codes) || misaligned(y_codes) || misaligned(workspace) || misaligned(prepared))
+    return fail(HQ_ERR_INVALID_ARG, "x_codes, y_codes, workspace and prepared must be 16-byte aligned");
+  const size_t need = align256(4 * size_t(T) * desc->d_out);
+  if (workspace_bytes < need)
+    return fail(HQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hq_wh_layout L;
+  wh_layout_of(desc, &L);
+  int32_t* acc = static_cast<int32_t*>(workspace);
+  hipError_t e = hq::launch_gemm(x_codes, T, at<int8_t>(prepared, L.w_codes), desc->d_out,
+                                 desc->d_in, acc, desc->d_out, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "GEMM kernel launch");
+  return run_wh_requant(desc, prepared, acc, T, y_codes, s);
+}
+
+int hq_wh_requant(const hq_wh_desc* desc, const void* prepared, const int32_t* acc, int64_t T,
+                  int8_t* y_codes, void* stream) {
+  g_err.clear();
+  int st = check_wh_desc(desc);
+  if (st != HQ_OK) return st;
+  if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+  if (T == 0) return HQ_OK;
+  if (!prepared || !acc || !y_codes)
+    return fail(HQ_ERR_INVALID_ARG, "prepared, acc and y_codes must be non-NULL");
+  if (misaligned(acc) || misaligned(y_codes) || misaligned(prepared))
+    return fail(HQ_ERR_INVALID_ARG, "acc, y_codes and prepared must be 16-byte aligned");
+  return run_wh_requant(desc, prepared, acc, T, y_codes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

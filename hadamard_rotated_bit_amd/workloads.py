@@ -32,12 +32,16 @@ not available here:
                    channels x50; three 1024-point blocks; rank-32 bf16
                    low-rank branch.
 
-One more workload exercises group-wise scales (not one of the five above):
+Two more workloads exercise the next rows (not among the five above):
 
 * ``flux_g64``  -- flux_proj's shape and value distribution with the data-free
                    int4 blog's recipe: 64-point Hadamard blocks, one scale per
                    row and 64-channel group, rank-32 branch, no smoothing, no
                    centring.
+* ``lic_wh``    -- lic_dh's shape and value distribution as a weight-only
+                   Hadamard layer with integer requantisation: int8 input
+                   codes with one per-tensor scale, H_256 on the output
+                   channels, int8 output codes.
 """
 from __future__ import annotations
 
@@ -93,9 +97,12 @@ WORKLOADS = {
                           "normal", 15, 50.0, 50.0, 0.02),
     "flux_g64": Workload(6, "flux_g64", 4608, 3072, 12288, "bf16", 64, None, 0, 4, 4, 32,
                          "normal", 15, 50.0, 50.0, 0.02, group=64),
+    "lic_wh": Workload(7, "lic_wh", 12288, 256, 256, "f32", 256, None, 0, 8, 8, 0,
+                       "laplace", 8, 30.0, 30.0, 0.05),
 }
 ORDER = ["tiny", "dit_fc1", "square4k", "lic_dh", "flux_proj"]
 GROUP_ORDER = ["flux_g64"]
+WH_ORDER = ["lic_wh"]
 
 
 def rng(key: int, stream: int) -> np.random.Generator:

@@ -364,11 +364,13 @@ def run(x, weight, bias, *, block: int, a_bits: int, w_bits: int, center,
 # * M_c = round(2^n rho_c) with one shared shift n: the largest n in [0, 48]
 #   for which every M_c fits a positive 16-bit integer (<= 32767), the
 #   multiplier-precision constraint of Eq. (19); n = 0 when every rho_c is 0.
+# * Bias codes saturate at +-2^30 (so that a + b_int stays a 32-bit integer).
 # * round() is round half to even throughout, on exact rationals.
 # * Codes are symmetric in [-qmax, qmax] (qmax = 127 for 8 bits).
 
 RQ_MULT_MAX = 32767
 RQ_SHIFT_MAX = 48
+RQ_BIAS_MAX = 2 ** 30
 
 
 def round_half_even_shift(v, n: int) -> np.ndarray:
@@ -424,7 +426,7 @@ def wh_prepare(weight, bias, s_x: float, s_y: float, block: int, w_bits: int = 8
     s_a = float(s_x) * s_w
     b_int = np.zeros(d_out, dtype=np.int64)
     nz = s_a > 0
-    b_int[nz] = np.rint(bbar[nz] / s_a[nz]).astype(np.int64)
+    b_int[nz] = np.clip(np.rint(bbar[nz] / s_a[nz]), -RQ_BIAS_MAX, RQ_BIAS_MAX).astype(np.int64)
     rho = s_a / (np.sqrt(block) * float(s_y))
     n = requant_shift(rho)
     m_c = np.rint(rho * 2.0 ** n).astype(np.int64)
