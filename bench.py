@@ -245,6 +245,47 @@ def group_wise(hq, torch, WL, steps, warmup, dev):
             "sqnr_db": sq}
 
 
+def weight_only_hadamard(hq, torch, WL, steps, warmup, dev):
+    """lic_wh: the weight-only Hadamard layer with integer requantisation
+    (int8 codes in, int8 codes out; H_256 on the output channels). Time per
+    call and per kernel (int8 GEMM into int32, then the requantisation), and
+    the output SQNR of the int8 codes against the float32 layer. The input
+    codes are the workload's X on a per-tensor grid (synthetic input)."""
+    w = WL.WORKLOADS["lic_wh"]
+    X = torch.from_numpy(WL.gen_x(w)).to(dev)
+    W = torch.from_numpy(WL.gen_weight(w)).to(dev)
+    B = torch.from_numpy(WL.gen_bias(w)).to(dev)
+    ref = torch.addmm(B, X, W.t())
+    s_x = float(X.abs().max().item() / 127.0)
+    s_y = float(ref.abs().max().item() / 127.0)
+    X0 = torch.clamp(torch.round(X / s_x), -127, 127).to(torch.int8)
+    desc = hq.WhDesc(w.d_in, w.d_out, w.block, hq.F32)
+    prep = hq.wh_prepare(desc, W, B, s_x, s_y)
+    nbuf = max(2, math.ceil(512e6 / X0.numel()))
+    Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
+    Ys = [torch.empty(w.T, w.d_out, dtype=torch.int8, device=dev) for _ in range(nbuf)]
+    ws = torch.empty(hq.wh_workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
+    for i in range(warmup):
+        hq.wh_linear(desc, prep, Xs[i % nbuf], out=Ys[i % nbuf], workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        hq.wh_linear(desc, prep, Xs[(warmup + i) % nbuf], out=Ys[(warmup + i) % nbuf], workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    y = Ys[(warmup + steps - 1) % nbuf].float() * s_y
+    sq = 10.0 * math.log10(ref.pow(2).sum().item() / max((y - ref).pow(2).sum().item(), 1e-300))
+    del Xs, Ys
+    # bytes that must move: int8 codes in and out, weight codes, constants
+    algo = w.T * (w.d_in + w.d_out) + w.d_out * (w.d_in + 12)
+    return {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
+            "block": w.block, "bits": "W8A8 int8 -> int8", "value": round(w.T / (ms * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_step": round(ms, 5),
+            "algorithmic_GBs": round(algo / (ms * 1e-3) / 1e9, 1), "sqnr_db": round(sq, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -329,6 +370,8 @@ def main():
             "gemm_TOPS": round(t8, 2), "gemm_mfma_frac": round(t8 / p8, 4), "peak": p8}
     del Xs, Ys
     out["group_wise"] = group_wise(hq, torch, WL, min(args.steps, 20), min(args.warmup, 5), dev)
+    out["weight_only_hadamard"] = weight_only_hadamard(hq, torch, WL, min(args.steps, 20),
+                                                       min(args.warmup, 5), dev)
     out["centring_modes"] = centring_modes(hq, torch, WL, min(args.steps, 20),
                                            min(args.warmup, 5), dev)
     if not args.no_cpu_baseline:
