@@ -43,8 +43,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dit_fc1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="measure the headline workload only, on both engines (no group-wise, "
+                         "weight-only Hadamard or centring objects), e.g. for clean profiles")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="host only: turn the FETCH_SIZE / WRITE_SIZE counter runs in DIR "
+                         "(rocprofv3 -o fetch / -o write, csv) into the committed traffic record "
+                         "of the dit_fc1 GEMM, then exit")
     return ap.parse_args()
 
 
@@ -149,6 +156,65 @@ def measured_traffic(kernel, workload):
     if h.hexdigest() != rec["sources_sha256"] or rec["kernel"] != kernel:
         return None
     return int(round(rec["traffic_bytes_per_launch"]))
+
+
+TRAFFIC_SOURCES = ["hadamard_rotated_bit_amd/csrc/hq_gemm6_kernel.h",
+                   "hadamard_rotated_bit_amd/csrc/hq_gemm_kernel.h",
+                   "hadamard_rotated_bit_amd/csrc/hq_gemm6.hip",
+                   "hadamard_rotated_bit_amd/csrc/hq_device.h",
+                   "hadamard_rotated_bit_amd/csrc/hq_internal.h"]
+COPY_BYTES = 18874368   # one clone of dit_fc1's X (8192 x 1152 bf16): the plain copy kernel
+
+
+def write_traffic(d):
+    """Per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of the FP6 GEMM from two
+    counter runs of this benchmark, each scaled by what the counter reads for
+    the run's plain copy kernel of known size, into
+    profiles/gemm_f6_dit_fc1_traffic.json with the hash of the GEMM sources."""
+    import csv
+    import hashlib
+    from collections import defaultdict
+
+    def per_kernel(f, counter):
+        acc = defaultdict(list)
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return acc
+
+    def pick(acc, key):
+        v = [x for k in acc if key in k for x in acc[k]]
+        if not v:
+            raise SystemExit(f"no dispatch of {key} in the counter files")
+        return sum(v) / len(v), len(v)
+
+    fe = per_kernel(os.path.join(d, "fetch_counter_collection.csv"), "FETCH_SIZE")
+    wr = per_kernel(os.path.join(d, "write_counter_collection.csv"), "WRITE_SIZE")
+    cf, _ = pick(fe, "__amd_rocclr_copyBuffer")
+    cw, _ = pick(wr, "__amd_rocclr_copyBuffer")
+    fs, ws = COPY_BYTES / 1024 / cf, COPY_BYTES / 1024 / cw
+    print(f"copy kernel: FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB -> scales {fs:.4f}, {ws:.4f}")
+    for key in ["gemm_f6_persist", "gemm_i8_kernel", "row_fast_kernel"]:
+        f, n = pick(fe, key)
+        w, n2 = pick(wr, key)
+        print(f"| `{key}` | {f:.1f} | {w:.1f} | {f * fs * 1024 / 1e6:.1f} MB | "
+              f"{w * ws * 1024 / 1e6:.1f} MB | {(f * fs + w * ws) * 1024 / 1e6:.1f} MB | {n}, {n2} dispatches")
+    f, _ = pick(fe, "gemm_f6_persist")
+    w, _ = pick(wr, "gemm_f6_persist")
+    h = hashlib.sha256()
+    for src in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as fh:
+            h.update(fh.read())
+    rec = {"kernel": "gemm_f6_dequant", "workload": "dit_fc1", "sources": TRAFFIC_SOURCES,
+           "sources_sha256": h.hexdigest(), "fetch_kib_per_dispatch": f,
+           "write_kib_per_dispatch": w,
+           "copy_kernel": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                           "fetch_scale": fs, "write_scale": ws},
+           "traffic_bytes_per_launch": (f * fs + w * ws) * 1024}
+    with open(os.path.join(ROOT, "profiles", "gemm_f6_dit_fc1_traffic.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(f"traffic per launch: {rec['traffic_bytes_per_launch'] / 1e6:.1f} MB")
 
 
 def kernel_report(hq, desc, w, r):
@@ -288,6 +354,9 @@ def weight_only_hadamard(hq, torch, WL, steps, warmup, dev):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs on a "
               "single GPU; across GPUs the layer would shard by tokens with no communication",
@@ -369,11 +438,13 @@ def main():
             "row_transform_GBs": round(g8, 1), "gemm_ms": round(r8["k2"], 5),
             "gemm_TOPS": round(t8, 2), "gemm_mfma_frac": round(t8 / p8, 4), "peak": p8}
     del Xs, Ys
-    out["group_wise"] = group_wise(hq, torch, WL, min(args.steps, 20), min(args.warmup, 5), dev)
-    out["weight_only_hadamard"] = weight_only_hadamard(hq, torch, WL, min(args.steps, 20),
-                                                       min(args.warmup, 5), dev)
-    out["centring_modes"] = centring_modes(hq, torch, WL, min(args.steps, 20),
-                                           min(args.warmup, 5), dev)
+    if not args.no_extras:
+        out["group_wise"] = group_wise(hq, torch, WL, min(args.steps, 20), min(args.warmup, 5),
+                                       dev)
+        out["weight_only_hadamard"] = weight_only_hadamard(hq, torch, WL, min(args.steps, 20),
+                                                           min(args.warmup, 5), dev)
+        out["centring_modes"] = centring_modes(hq, torch, WL, min(args.steps, 20),
+                                               min(args.warmup, 5), dev)
     if not args.no_cpu_baseline:
         sig = None if S is None else S.cpu().numpy()
         out["cpu_baseline"] = cpu_baseline(w, x, weight, bias, sig, l1, l2, args.cpu_seconds)
