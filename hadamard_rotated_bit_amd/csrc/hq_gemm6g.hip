@@ -14,15 +14,17 @@
 // its 16 values per lane are added to the accumulators scaled by
 // s_x[g, row] s_w[g, col] (fp32 VALU; exact integers times the scales).
 //
-// Tiles 128 x 128, 4 waves of 64 x 64, two blocks per CU. Stage buffer =
-// A and B codes plus the stage's four scale vectors (s_x and s_w of both
-// groups), all by buffer_load ... lds against per-tile descriptors (rows past
-// M / N and stages past K move nothing). Three buffers: iteration kt waits
-// for stage kt (stage kt+1 may stay in flight), joins the block (every wave
-// is done with stage kt-1), refills stage kt-1's buffer with stage kt+2,
-// then reads stage kt's fragments and scales and runs its two groups. Each
-// load has two iterations to land; the other block on the CU covers the
-// fragment reads.
+// Tiles 128 x 128, 4 waves of 64 x 64. Stage buffer = A and B codes plus the
+// stage's four scale vectors (s_x and s_w of both groups), all by
+// buffer_load ... lds against per-tile descriptors (rows past M / N and stages
+// past K move nothing). With S buffers, iteration kt waits for stage kt
+// (S = 3: stage kt+1 may stay in flight), joins the block (every wave is done
+// with stage kt-1), refills stage kt-1's buffer with stage kt+S-1, then reads
+// stage kt's fragments and scales and runs its two groups. The launch uses
+// S = 2 and three blocks per CU (168 VGPRs, 3 x 53 KB of LDS): the rescale
+// keeps the VALU busy, and three independent blocks per SIMD hide each
+// other's loads, barriers and epilogues better than two blocks with a deeper
+// pipeline (measured on flux_g64: 242 vs 303 us).
 #include "hq_gemm6_kernel.h"
 
 namespace hq {
@@ -82,7 +84,7 @@ __device__ __forceinline__ void scale_products(float (&p)[16], float sw, float s
 // The MFMAs and rescales of one stage: per tile, the MFMA, the tile's 16
 // scale products (independent of it, so they issue while it runs), then
 // acc += t * s_x * s_w.
-template <int TM, int TN, int N>
+template <int TM, int TN, int N, bool PIN>
 __device__ __forceinline__ void group_tiles(v16f (&acc)[TM][TN], const Frag6 (&af)[TM],
                                            const Frag6 (&bf)[TN], const float (&sx)[2][TM],
                                            const float (&sw)[2][TN]) {
@@ -93,17 +95,17 @@ __device__ __forceinline__ void group_tiles(v16f (&acc)[TM][TN], const Frag6 (&a
     scale_products(p, sw[g][j], sx[g][i]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(t[r], p[r], acc[i][j][r]);
-    group_tiles<TM, TN, N + 1>(acc, af, bf, sx, sw);
+    if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
+    group_tiles<TM, TN, N + 1, PIN>(acc, af, bf, sx, sw);
   }
 }
 
-template <int BM, int BN, int WM, int WN, int GM, int RG>
+template <int BM, int BN, int WM, int WN, int GM, int RG, int S = 3, int OCC = 2>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(2))) void gemm_f6g_kernel(
+__attribute__((amdgpu_waves_per_eu(OCC))) void gemm_f6g_kernel(
     const uint8_t* __restrict__ A, int64_t M, const uint8_t* __restrict__ B, int64_t N, int K,
     GemmEpi ep, const float* __restrict__ sxg, int64_t ldsx, const float* __restrict__ swg,
     int64_t ldsw) {
-  constexpr int S = 3;
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int WAVES_N = BN / WN;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -117,8 +119,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_f6g_kernel(
   constexpr int SPW = 4 * UV / NW;               // scale units per wave and stage
   static_assert(BM == BN && BM % 64 == 0, "square tiles of whole scale units");
   static_assert(UNITS % NW == 0 && UA % NW == 0 && (4 * UV) % NW == 0, "even DMA split");
-  static_assert(BM * (2 * BN + 8) <= S * STAGE && 4 * (3 * BN + 2 * BM) <= S * STAGE,
-                "epilogue fits in the stage buffers");
+  static_assert(S == 2 || S == 3, "two or three stage buffers");
+  static_assert(BM * (2 * BN + 8) + 4 * (3 * BN + 2 * BM) <= S * STAGE,
+                "epilogue tile and parameters fit in the stage buffers");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -240,14 +243,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_f6g_kernel(
     float sx_[2][TM];                                                                      \
     float sw_[2][TN];                                                                      \
     HG_SCALES(BUF_);                                                                       \
-    group_tiles<TM, TN, 0>(acc, af, bf, sx_, sw_);                                         \
+    group_tiles<TM, TN, 0, (OCC > 2)>(acc, af, bf, sx_, sw_);                              \
   } while (0)
 #define HG_STEP(KT_)                                                                       \
   do {                                                                                     \
-    wait_vm_lgkm0<LPW + SPW>();                                                            \
+    wait_vm_lgkm0<(S - 2) * (LPW + SPW)>();                                                \
     __builtin_amdgcn_s_barrier();                                                          \
     const int cb_ = (KT_) % S;                                                             \
-    HG_ISSUE((KT_) + 2, cb_ == 0 ? 2 : cb_ - 1);                                           \
+    HG_ISSUE((KT_) + S - 1, cb_ == 0 ? S - 1 : cb_ - 1);                                   \
     HG_READ(cb_);                                                                          \
     HG_MATH(cb_);                                                                          \
   } while (0)
@@ -261,7 +264,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_f6g_kernel(
   Frag6 af[TM], bf[TN];
 
   HG_ISSUE(0, 0);
-  HG_ISSUE(1, 1);
+  if constexpr (S == 3) HG_ISSUE(1, 1);
   for (int kt = 0; kt < KT; ++kt) HG_STEP(kt);
   wait_vm_lgkm0<0>();   // no LDS write may land after the block ends
 #undef HG_STEP
@@ -274,11 +277,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_f6g_kernel(
   if (ep.y_bf16) {
     // bf16 output staged through LDS (whole row segments per store). The
     // accumulators already carry both scales, so the staged parameter block
-    // holds unit s_w and s_x next to c, b and mu; it sits in the last stage
-    // buffer, clear of the output tile.
-    static_assert(BM * (2 * BN + 8) <= 2 * STAGE && 4 * (3 * BN + 2 * BM) <= STAGE,
-                  "output tile and parameters fit");
-    float* P = reinterpret_cast<float*>(smem + 2 * STAGE);
+    // holds unit s_w and s_x next to c, b and mu, right after the output tile.
+    float* P = reinterpret_cast<float*>(smem + BM * (2 * BN + 8));
     __builtin_amdgcn_s_barrier();   // every wave is past its last stage read
     for (int idx = tid; idx < BN; idx += NW * 64) {
       const int64_t nc = n0 + idx < N ? n0 + idx : N - 1;
@@ -313,7 +313,7 @@ hipError_t launch_gemm_f6g(const uint8_t* A, int64_t M, const uint8_t* B, int64_
   const int64_t ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   GemmEpi ep = *epi;
   ep.prescaled = 1;
-  hipLaunchKernelGGL((gemm_f6g_kernel<BM, BN, 64, 64, 4, F6_GROUP>), dim3(unsigned(ntiles)),
+  hipLaunchKernelGGL((gemm_f6g_kernel<BM, BN, 64, 64, 4, F6_GROUP, 2, 3>), dim3(unsigned(ntiles)),
                      dim3(256), 0, s, A, M, B, N, K, ep, s_xg, ld_sx, s_wg, ld_sw);
   return hipGetLastError();
 }
