@@ -130,7 +130,7 @@ hipError_t launch_gemm_f6(const uint8_t* A, int64_t M, const uint8_t* B, int64_t
 constexpr int WH_MAX_BLOCK = 256;       // largest output-side Hadamard order
 constexpr int WH_SHIFT_MAX = 48;        // largest shared requantisation shift
 constexpr int WH_MULT_MAX = 32767;      // multipliers fit a positive 16-bit integer
-constexpr int WH_BIAS_MAX = 1 << 30;    // bias codes saturate here (a + b_int fits int32)
+constexpr int WH_BIAS_MAX = 1 << 27;    // bias codes saturate here (exact float64 requant)
 // wbar [d_out, d_in] f32 = H_m (blocks of m output channels) . weight.
 hipError_t launch_wh_weight(const void* w, int w_bf16, int d_out, int d_in, int m, float* wbar,
                             hipStream_t s);

@@ -49,8 +49,8 @@ __global__ __launch_bounds__(256) void wh_weight_kernel(const TW* __restrict__ w
 }
 
 // Offline constants (one block, float64): b-bar = b H_m, s_A = s_x s_w,
-// b_int = round(b-bar / s_A) (saturated at +-2^30 so that a + b_int fits an
-// int32), rho = s_A / (sqrt(m) s_y), the shared shift n (largest n <= 48 with
+// b_int = round(b-bar / s_A) (saturated at +-2^27, see the requantisation
+// kernel), rho = s_A / (sqrt(m) s_y), the shared shift n (largest n <= 48 with
 // every round(2^n rho) <= 32767) and M = round(2^n rho). Rows past d_out get
 // zeros.
 __global__ __launch_bounds__(256) void wh_constants_kernel(const float* __restrict__ bias,
@@ -104,65 +104,116 @@ __global__ __launch_bounds__(256) void wh_constants_kernel(const float* __restri
   }
 }
 
-// round(v / 2^n), ties to even, for n >= 1.
-__device__ __forceinline__ int64_t rne_shift(int64_t v, int n) {
-  const int64_t q = v >> n;
-  const int64_t r = v - (q << n);
-  const int64_t half = int64_t(1) << (n - 1);
-  return q + ((r > half || (r == half && (q & 1))) ? 1 : 0);
+// The requantisation carries its integers in float64 registers: with
+// |a + b_int| < 2^28 (|a| <= 127^2 d_in <= 2^27, |b_int| <= 2^27), M < 2^15
+// and at most 256 terms per butterfly output, every intermediate is an
+// integer below 2^51 in magnitude, so float64 additions, products, the scaling
+// by 2^-n and round-to-nearest-even are exact and give the integer results
+// bit for bit, at a quarter of the instructions 64-bit integer arithmetic
+// needs on the VALU.
+
+// Value of x held by lane l ^ D of the same 16-lane row (D = 1, 2, 4, 8):
+// DPP quad permutes for 1 and 2, a DPP row rotation by 8 (its direction does
+// not matter), and for 4 the swizzle's xor mode.
+template <int D>
+__device__ __forceinline__ int lane_xor16(int x) {
+  static_assert(D == 1 || D == 2 || D == 4 || D == 8, "lane distance");
+  if constexpr (D == 1) return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
+  if constexpr (D == 2) return __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+  if constexpr (D == 8) return __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);
+  return __builtin_amdgcn_ds_swizzle(x, 0x1F | (4 << 10));
 }
 
-// Requantisation of int32 products acc [T, ldc] (without bias): one wave per
-// (token, 256-channel chunk), lane l holding channels 4 l .. 4 l + 3 of the
-// chunk. u = M (acc + b_int) in int64, the unnormalised Sylvester butterflies
-// over blocks of m channels (channel bits 0-1 inside the lane, bits 2.. across
-// lanes), then round(u / 2^n) with ties to even and clamping to +-127.
+template <int D>
+__device__ __forceinline__ double lane_xor16_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const int lo = lane_xor16<D>(int(uint32_t(b)));
+  const int hi = lane_xor16<D>(int(uint32_t(b >> 32)));
+  return __builtin_bit_cast(double, (uint64_t(uint32_t(hi)) << 32) | uint64_t(uint32_t(lo)));
+}
+
+// One butterfly stage over channel bit 4 + log2(D) (lane distance D): the
+// lane with bit D clear keeps u + partner, the other partner - u.
+template <int D>
+__device__ __forceinline__ void wh_xstage(double (&u)[16], int lane, int m) {
+  if (16 * D >= m) return;
+  const double g = (lane & D) ? -1.0 : 1.0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) u[k] = fma(u[k], g, lane_xor16_f64<D>(u[k]));
+}
+
+// Requantisation of int32 products acc [T, ldc] (without bias). Each group of
+// 16 lanes takes one (token, 256-channel chunk) unit, lane l of the group
+// holding channels 16 l .. 16 l + 15 of the chunk. u = M (acc + b_int), the
+// unnormalised Sylvester butterflies over blocks of m channels (channel bits
+// 0-3 inside the lane, bits 4-7 across the group's lanes), then
+// round(u / 2^n) with ties to even and clamping to +-127. Every lane of a
+// group runs the butterflies (invalid channels hold 0; blocks never mix valid
+// and invalid channels, m dividing d_out).
 __global__ __launch_bounds__(256) void wh_requant_kernel(
     const int32_t* __restrict__ acc, int64_t ldc, int64_t T, int d_out, int chunks, int m,
     const int32_t* __restrict__ b_int, const int32_t* __restrict__ mult,
     const int32_t* __restrict__ shift, int8_t* __restrict__ y, int64_t ldy) {
-  const int lane = threadIdx.x & 63;
-  const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (unit >= T * chunks) return;   // whole waves leave together
-  const int64_t row = unit / chunks;
-  const int c = int(unit - row * chunks) * 256 + 4 * lane;
-  const bool valid = c < d_out;     // d_out % 8 == 0: a lane is all in or all out
-  int64_t u[4] = {0, 0, 0, 0};
-  if (valid) {
-    const int4 a = *reinterpret_cast<const int4*>(acc + row * ldc + c);
-    const int4 b = *reinterpret_cast<const int4*>(b_int + c);
-    const int4 mm = *reinterpret_cast<const int4*>(mult + c);
-    u[0] = int64_t(mm.x) * int64_t(a.x + b.x);
-    u[1] = int64_t(mm.y) * int64_t(a.y + b.y);
-    u[2] = int64_t(mm.z) * int64_t(a.z + b.z);
-    u[3] = int64_t(mm.w) * int64_t(a.w + b.w);
-  }
-  if (m >= 2) {
-    const int64_t p0 = u[0] + u[1], q0 = u[0] - u[1], p1 = u[2] + u[3], q1 = u[2] - u[3];
-    u[0] = p0; u[1] = q0; u[2] = p1; u[3] = q1;
-  }
-  if (m >= 4) {
-    const int64_t p0 = u[0] + u[2], q0 = u[0] - u[2], p1 = u[1] + u[3], q1 = u[1] - u[3];
-    u[0] = p0; u[2] = q0; u[1] = p1; u[3] = q1;
-  }
-  for (int dl = 1; 4 * dl < m; dl <<= 1) {
-    const bool upper = (lane & dl) != 0;
+  const int lane = threadIdx.x & 15;
+  const int64_t unit = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const bool live = unit < T * chunks;
+  const int64_t uu = live ? unit : T * chunks - 1;
+  const int64_t row = uu / chunks;
+  const int c0 = int(uu - row * chunks) * 256 + 16 * lane;
+  double u[16];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t o = __shfl_xor(u[k], dl);
-      u[k] = upper ? o - u[k] : u[k] + o;
+  for (int q = 0; q < 4; ++q) {
+    const int c = c0 + 4 * q;
+    if (c < d_out) {   // d_out % 8 == 0: whole runs of 4 are in or out
+      const int4 a = *reinterpret_cast<const int4*>(acc + row * ldc + c);
+      const int4 b = *reinterpret_cast<const int4*>(b_int + c);
+      const int4 mm = *reinterpret_cast<const int4*>(mult + c);
+      u[4 * q + 0] = double(a.x + b.x) * double(mm.x);
+      u[4 * q + 1] = double(a.y + b.y) * double(mm.y);
+      u[4 * q + 2] = double(a.z + b.z) * double(mm.z);
+      u[4 * q + 3] = double(a.w + b.w) * double(mm.w);
+    } else {
+      u[4 * q + 0] = u[4 * q + 1] = u[4 * q + 2] = u[4 * q + 3] = 0.0;
     }
   }
-  if (!valid) return;
-  const int n = *shift;
-  uint32_t packed = 0;
+  // channel bits 0-3, in the lane
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    int64_t q = n > 0 ? rne_shift(u[k], n) : u[k];
-    q = q > 127 ? 127 : (q < -127 ? -127 : q);
-    packed |= (uint32_t(q) & 0xFFu) << (8 * k);
+  for (int h = 1; h < 16; h <<= 1) {
+    if (h < m) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (!(k & h)) {
+          const double x = u[k], z = u[k + h];
+          u[k] = x + z;
+          u[k + h] = x - z;
+        }
+      }
+    }
   }
-  *reinterpret_cast<uint32_t*>(y + row * ldy + c) = packed;
+  // channel bits 4-7, across the 16 lanes of the group
+  wh_xstage<1>(u, lane, m);
+  wh_xstage<2>(u, lane, m);
+  wh_xstage<4>(u, lane, m);
+  wh_xstage<8>(u, lane, m);
+  if (!live || c0 >= d_out) return;
+  const double scale = ldexp(1.0, -*shift);
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const double v = fmin(fmax(rint(u[4 * q + k] * scale), -127.0), 127.0);
+      packed |= (uint32_t(int(v)) & 0xFFu) << (8 * k);
+    }
+    w[q] = packed;
+  }
+  int8_t* dst = y + row * ldy + c0;
+  if (c0 + 16 <= d_out) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {   // the last 8 channels of d_out
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  }
 }
 
 hipError_t launch_wh_weight(const void* w, int w_bf16, int d_out, int d_in, int m, float* wbar,
@@ -194,9 +245,9 @@ hipError_t launch_wh_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_o
   if (m < 1 || m > WH_MAX_BLOCK || (m & (m - 1)) || d_out % m || d_out % 8)
     return hipErrorInvalidValue;
   const int chunks = (d_out + 255) / 256;
-  const int64_t waves = T * chunks;
-  hipLaunchKernelGGL(wh_requant_kernel, dim3(unsigned((waves + 3) / 4)), dim3(256), 0, s, acc, ldc,
-                     T, d_out, chunks, m, b_int, mult, shift, y, ldy);
+  const int64_t units = T * chunks;   // 16 lanes each, 16 per block
+  hipLaunchKernelGGL(wh_requant_kernel, dim3(unsigned((units + 15) / 16)), dim3(256), 0, s, acc,
+                     ldc, T, d_out, chunks, m, b_int, mult, shift, y, ldy);
   return hipGetLastError();
 }
 

@@ -288,8 +288,10 @@ int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes
  * form (additions and subtractions only). s_w,c: per-output-channel scale of
  * W-bar (8-bit symmetric codes); s_y: the scale of the output codes (the next
  * layer's input scale). n: the largest shift <= 48 with every M_c <= 32767.
- * round() is round half to even; bias codes saturate at +-2^30. Every online
- * step is exact integer arithmetic (int32 products, int64 after M).
+ * round() is round half to even; bias codes saturate at +-2^27, so every
+ * intermediate stays below 2^51 in magnitude. Every online step is exact
+ * integer arithmetic (int32 products; after M the kernel carries the
+ * integers in float64 registers, exact in that range).
  */
 typedef struct {
   int32_t d_in;     /* input channels: same rule as hq_desc.d_in                */
@@ -332,7 +334,8 @@ int hq_wh_linear(const hq_wh_desc* desc, const void* prepared, const int8_t* x_c
 
 /* Requantisation alone: y_codes int8 [T, d_out] from the int32 products
  * acc [T, d_out] (x_int . w-bar_int^T, WITHOUT the bias codes, which this
- * stage adds). */
+ * stage adds). |acc| <= 2^27 (as every product of int8 codes over d_in <= 8192
+ * is); larger values are outside the exact range of the kernel. */
 int hq_wh_requant(const hq_wh_desc* desc, const void* prepared, const int32_t* acc, int64_t T,
                   int8_t* y_codes, void* stream);
 

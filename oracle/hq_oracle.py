@@ -364,13 +364,14 @@ def run(x, weight, bias, *, block: int, a_bits: int, w_bits: int, center,
 # * M_c = round(2^n rho_c) with one shared shift n: the largest n in [0, 48]
 #   for which every M_c fits a positive 16-bit integer (<= 32767), the
 #   multiplier-precision constraint of Eq. (19); n = 0 when every rho_c is 0.
-# * Bias codes saturate at +-2^30 (so that a + b_int stays a 32-bit integer).
+# * Bias codes saturate at +-2^27: with |a| <= 127^2 d_in <= 2^27 and M <= 32767,
+#   every intermediate of the requantisation then stays below 2^51 in magnitude.
 # * round() is round half to even throughout, on exact rationals.
 # * Codes are symmetric in [-qmax, qmax] (qmax = 127 for 8 bits).
 
 RQ_MULT_MAX = 32767
 RQ_SHIFT_MAX = 48
-RQ_BIAS_MAX = 2 ** 30
+RQ_BIAS_MAX = 2 ** 27
 
 
 def round_half_even_shift(v, n: int) -> np.ndarray:
