@@ -493,17 +493,36 @@ hipError_t launch_prep_l2(const void* l2, int bf16, int r, int n, int n_pad, uin
 // 16-bit branch sees the smoothed, un-rotated input; 1/sigma is folded into
 // l1). v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16), channels
 // 8*(l/16) .. +8 of a 32-channel step; B likewise with the rank index.
-// A 256-thread block owns 16 rows; its 4 waves split the channels into
-// quarters and add their partial 16 x R tiles through LDS.
+// A block of W waves owns 16 rows; the waves split the channels into W
+// contiguous parts and add their partial 16 x R tiles through LDS. Each wave
+// loads the operands of U steps before their products, so U memory round
+// trips overlap instead of one per step.
 // fp32 inputs are split into bf16 hi + lo as well (3 products).
 // ---------------------------------------------------------------------------
 template <typename TIn, int R>
-__global__ __launch_bounds__(256) void lowrank_down_kernel(const TIn* __restrict__ x, int64_t rows,
-                                                           int d, const uint16_t* __restrict__ l1hi,
-                                                           const uint16_t* __restrict__ l1lo,
-                                                           float* __restrict__ U) {
-  constexpr int NG = R / 16;
-  __shared__ float red[4][16][R + 1];
+__device__ __forceinline__ void lowrank_load_a(const TIn* __restrict__ x, int64_t off, v8bf* hi,
+                                               v8bf* lo) {
+  if constexpr (sizeof(TIn) == 2) {
+    *hi = *reinterpret_cast<const v8bf*>(x + off);
+  } else {
+    float f[8];
+    load8(reinterpret_cast<const float*>(x) + off, f);
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) split_bf16(f[j], &h[j], &l[j]);
+    *hi = *reinterpret_cast<v8bf*>(h);
+    *lo = *reinterpret_cast<v8bf*>(l);
+  }
+}
+
+template <typename TIn, int R, int W>
+__global__ __launch_bounds__(W * 64) void lowrank_down_kernel(const TIn* __restrict__ x,
+                                                              int64_t rows, int d,
+                                                              const uint16_t* __restrict__ l1hi,
+                                                              const uint16_t* __restrict__ l1lo,
+                                                              float* __restrict__ U) {
+  constexpr int NG = R / 16, UN = 4;
+  __shared__ float red[W][16][R + 1];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t row0 = int64_t(blockIdx.x) * 16;
   int64_t row = row0 + (lane & 15);
@@ -512,30 +531,43 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const TIn* __restrict
   v4f acc[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) acc[g] = v4f{0, 0, 0, 0};
-  const int kbeg = w * (d / 4), kend = kbeg + d / 4;
-  for (int k0 = kbeg; k0 < kend; k0 += 32) {
-    v8bf ahi, alo;
-    if constexpr (sizeof(TIn) == 2) {
-      ahi = *reinterpret_cast<const v8bf*>(x + row * d + k0 + kq);
-    } else {
-      float f[8];
-      load8(reinterpret_cast<const float*>(x) + row * d + k0 + kq, f);
-      uint16_t h[8], l[8];
+  const int kbeg = w * (d / W), kend = kbeg + d / W;
+  auto step = [&](const v8bf& ahi, const v8bf& alo, const v8bf (&bhi)[NG], const v8bf (&blo)[NG]) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) split_bf16(f[j], &h[j], &l[j]);
-      ahi = *reinterpret_cast<v8bf*>(h);
-      alo = *reinterpret_cast<v8bf*>(l);
+    for (int g = 0; g < NG; ++g) {
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi[g], acc[g], 0, 0, 0);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, blo[g], acc[g], 0, 0, 0);
+      if constexpr (sizeof(TIn) == 4)
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bhi[g], acc[g], 0, 0, 0);
     }
+  };
+  int k0 = kbeg;
+  for (; k0 + 32 * UN <= kend; k0 += 32 * UN) {
+    v8bf ahi[UN], alo[UN], bhi[UN][NG], blo[UN][NG];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      lowrank_load_a<TIn, R>(x, row * d + k0 + 32 * u + kq, &ahi[u], &alo[u]);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int64_t off = int64_t(g * 16 + (lane & 15)) * d + k0 + 32 * u + kq;
+        bhi[u][g] = *reinterpret_cast<const v8bf*>(l1hi + off);
+        blo[u][g] = *reinterpret_cast<const v8bf*>(l1lo + off);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the group issues before the products
+#pragma unroll
+    for (int u = 0; u < UN; ++u) step(ahi[u], alo[u], bhi[u], blo[u]);
+  }
+  for (; k0 < kend; k0 += 32) {
+    v8bf ahi, alo, bhi[NG], blo[NG];
+    lowrank_load_a<TIn, R>(x, row * d + k0 + kq, &ahi, &alo);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const int64_t off = int64_t(g * 16 + (lane & 15)) * d + k0 + kq;
-      const v8bf bhi = *reinterpret_cast<const v8bf*>(l1hi + off);
-      const v8bf blo = *reinterpret_cast<const v8bf*>(l1lo + off);
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc[g], 0, 0, 0);
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, blo, acc[g], 0, 0, 0);
-      if constexpr (sizeof(TIn) == 4)
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bhi, acc[g], 0, 0, 0);
+      bhi[g] = *reinterpret_cast<const v8bf*>(l1hi + off);
+      blo[g] = *reinterpret_cast<const v8bf*>(l1lo + off);
     }
+    step(ahi, alo, bhi, blo);
   }
   // 16x16 output layout: lane l, register i -> row 4*(l/16) + i, column l % 16.
 #pragma unroll
@@ -543,10 +575,12 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const TIn* __restrict
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[w][4 * (lane >> 4) + i][g * 16 + (lane & 15)] = acc[g][i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 16 * R; idx += 256) {
+  for (int idx = threadIdx.x; idx < 16 * R; idx += W * 64) {
     const int rr = idx / R, cc = idx % R;
-    const float s = red[0][rr][cc] + red[1][rr][cc] + red[2][rr][cc] + red[3][rr][cc];
-    if (row0 + rr < rows) U[(row0 + rr) * R + cc] = s;
+    float sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < W; ++q) sum += red[q][rr][cc];
+    if (row0 + rr < rows) U[(row0 + rr) * R + cc] = sum;
   }
 }
 
@@ -554,15 +588,20 @@ hipError_t launch_lowrank_down(const void* x, int x_bf16, int64_t rows, int d, i
                                const uint16_t* l1_hi, const uint16_t* l1_lo, float* U,
                                hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  dim3 grid{unsigned((rows + 15) / 16)}, block{256};
+  if (d % 128) return hipErrorInvalidValue;
+  // eight waves per 16 rows when every wave still gets whole 32-channel steps
+  const bool wide = d % 256 == 0 && d >= 1024;
+  dim3 grid{unsigned((rows + 15) / 16)};
+#define HQ_LR_LAUNCH(RR, WW)                                                                    \
+  if (x_bf16)                                                                                   \
+    hipLaunchKernelGGL((lowrank_down_kernel<uint16_t, RR, WW>), grid, dim3(WW * 64), 0, s,       \
+                       static_cast<const uint16_t*>(x), rows, d, l1_hi, l1_lo, U);              \
+  else                                                                                          \
+    hipLaunchKernelGGL((lowrank_down_kernel<float, RR, WW>), grid, dim3(WW * 64), 0, s,          \
+                       static_cast<const float*>(x), rows, d, l1_hi, l1_lo, U);
 #define HQ_LR_CASE(RR)                                                                          \
   case RR:                                                                                      \
-    if (x_bf16)                                                                                 \
-      hipLaunchKernelGGL((lowrank_down_kernel<uint16_t, RR>), grid, block, 0, s,                 \
-                         static_cast<const uint16_t*>(x), rows, d, l1_hi, l1_lo, U);            \
-    else                                                                                        \
-      hipLaunchKernelGGL((lowrank_down_kernel<float, RR>), grid, block, 0, s,                    \
-                         static_cast<const float*>(x), rows, d, l1_hi, l1_lo, U);               \
+    if (wide) { HQ_LR_LAUNCH(RR, 8) } else { HQ_LR_LAUNCH(RR, 4) }                              \
     break;
   switch (r) {
     HQ_LR_CASE(16) HQ_LR_CASE(32) HQ_LR_CASE(48) HQ_LR_CASE(64)
@@ -570,6 +609,7 @@ hipError_t launch_lowrank_down(const void* x, int x_bf16, int64_t rows, int d, i
       return hipErrorInvalidValue;
   }
 #undef HQ_LR_CASE
+#undef HQ_LR_LAUNCH
   return hipGetLastError();
 }
 
