@@ -162,7 +162,7 @@ TRAFFIC_SOURCES = ["hadamard_rotated_bit_amd/csrc/hq_gemm6_kernel.h",
                    "hadamard_rotated_bit_amd/csrc/hq_gemm_kernel.h",
                    "hadamard_rotated_bit_amd/csrc/hq_gemm6.hip",
                    "hadamard_rotated_bit_amd/csrc/hq_device.h",
-                   "hadamard_rotated_bit_amd/csrc/hq_internal.h"]
+                   "hadamard_rotated_bit_amd/csrc/hq_gemm_types.h"]
 COPY_BYTES = 18874368   # one clone of dit_fc1's X (8192 x 1152 bf16): the plain copy kernel
 
 

@@ -16,6 +16,7 @@
 //                                       the 192-wide tiles fill whole waves of CUs;
 //   128 x 128 (4 waves)                 narrow outputs (d_out <= 512).
 #include "hq_gemm_kernel.h"
+#include "hq_internal.h"
 
 namespace hq {
 

@@ -2,6 +2,7 @@
 // epilogue as the int8 path (hq_gemm.hip), on v_mfma_f32_32x32x64_f8f6f4.
 // Kernel structure in hq_gemm6_kernel.h.
 #include "hq_gemm6_kernel.h"
+#include "hq_internal.h"
 
 namespace hq {
 

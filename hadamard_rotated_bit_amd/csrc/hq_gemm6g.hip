@@ -26,6 +26,7 @@
 // other's loads, barriers and epilogues better than two blocks with a deeper
 // pipeline (measured on flux_g64: 242 vs 303 us).
 #include "hq_gemm6_kernel.h"
+#include "hq_internal.h"
 
 namespace hq {
 

@@ -3,7 +3,7 @@
 #pragma once
 
 #include "hq_device.h"
-#include "hq_internal.h"
+#include "hq_gemm_types.h"
 
 namespace hq {
 

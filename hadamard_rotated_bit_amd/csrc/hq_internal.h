@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "hq_gemm_types.h"
+
 namespace hq {
 
 // GEMM macro tile sizes; d_out is padded to a multiple of GEMM_BN in the
@@ -25,7 +27,6 @@ enum RowMode { ROW_ACT = 0, ROW_WEIGHT = 1, ROW_EXPORT = 2 };
 // 4-row groups (group g of rows at 3 d g bytes; 128-code slice s of row
 // 4g + i at byte 384 s + 96 i inside it; code k of the slice at bits 6k).
 enum CodeFmt { CODES_I8 = 0, CODES_E2M3 = 1 };
-constexpr int F6_GROUP = 4;
 inline size_t code_bytes(int fmt, int64_t rows, int d) {
   if (fmt == CODES_E2M3) return size_t((rows + F6_GROUP - 1) / F6_GROUP) * 3 * size_t(d);
   return size_t(rows) * size_t(d);
@@ -94,21 +95,7 @@ hipError_t launch_channel_mean(const void* x, int x_bf16, int64_t rows, int d, f
 hipError_t launch_bias_gemv(const void* weight, int w_bf16, const float* mean, const float* bias,
                             int n, int n_pad, int d, float* out, hipStream_t s);
 
-struct GemmEpi {
-  const float* s_x;       // [M]
-  const float* mu;        // [M]
-  const float* s_w;       // [N]
-  const float* c;         // [N]
-  const float* bias;      // [N]
-  const float* U;         // [M, rank] or NULL
-  const uint16_t* l2_hi;  // [N, rank]
-  const uint16_t* l2_lo;
-  int rank;
-  void* Y;                // [M, ldy]
-  int y_bf16;
-  int64_t ldy;
-  int prescaled;          // accumulators already carry s_x s_w (group-wise GEMM)
-};
+
 // acc = A [M, K] . B [N, K]^T ; epilogue: int32 store to acc_out (ld = ldc) when
 // epi == NULL, else the dequant epilogue. Loads of rows past M / N are
 // clamped to the last row.

@@ -13,10 +13,9 @@
 //    fma. The upper lane then holds the negated difference, so after all
 //    stages lane t stores sigma_t times the transformed value, with
 //    sigma_t = (-1)^popcount(t & NEG) a per-lane sign (NEG = the lane bits
-//    done this way). Sums are taken as sigma_t * (lane sum), the mean is
-//    subtracted as sigma_t * mu, and the quantiser uses sigma_t * (qmax /
-//    absmax): every code, scale and mean is the same as with unsigned
-//    storage, bit for bit.
+//    done this way). The mean is subtracted as sigma_t * mu and the
+//    quantiser uses sigma_t * (qmax / absmax): every code and scale is the
+//    same as with unsigned storage, bit for bit.
 //  * E2M3 codes come from v_cvt_scalef32_2xpk16_fp6_f32 on the integer codes
 //    rint(x * qmax / absmax) (formed as fma(x, r, 1.5 2^23) - 1.5 2^23, one
 //    rounding of the exact product), 32 codes per instruction; the
@@ -24,6 +23,9 @@
 //    field 2i+1 holds y[i]), so four chunks of 8 channels are fed in that
 //    order and come out as four 48-bit pieces.
 //  * No runtime stage tests, so the butterflies run in place.
+//  * The row sum (for the mean, and c for weights) is taken from the closed
+//    form B * sum of the blocks' first inputs instead of summing every
+//    output.
 #include "hq_device.h"
 #include "hq_internal.h"
 
@@ -123,6 +125,11 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
   const float g16 = (t & 16) ? -1.0f : 1.0f, g32 = (t & 32) ? -1.0f : 1.0f;
   const float sgn = (__builtin_popcount(t & NEG) & 1) ? -1.0f : 1.0f;
 
+  // Row sum of the unnormalised transform: every row of a Sylvester H~_B
+  // but the first sums to zero, so the sum over a block's outputs is B times
+  // its first input; lane 0 of a row holds the first input of the blocks
+  // starting at its chunks c = 0 mod 2^NX.
+  float s0 = 0.0f;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     float* vc = &v[c * 8];
@@ -134,6 +141,7 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
 #pragma unroll
       for (int j = 0; j < 8; ++j) vc[j] *= sc[c * 8 + j];
     }
+    if ((c & ((1 << NX) - 1)) == 0) s0 += vc[0];
     // channel bits 0..2, in registers
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
@@ -171,10 +179,7 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
     }
   }
 
-  float sum = 0.0f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) sum += v[e];
-  sum = group_sum<G>(sgn * sum);
+  const float sum = float(1 << a.log2b) * group_sum<G>(t == 0 ? s0 : 0.0f);
 
   const bool weight = a.mode == ROW_WEIGHT;
   const float mu = (!weight && a.center) ? sum / float(d) : 0.0f;
