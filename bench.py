@@ -311,33 +311,47 @@ def group_wise(hq, torch, WL, steps, warmup, dev):
             "sqnr_db": sq}
 
 
-def weight_only_hadamard(hq, torch, WL, steps, warmup, dev):
-    """lic_wh: the weight-only Hadamard layer with integer requantisation
-    (int8 codes in, int8 codes out; H_256 on the output channels). Time per
-    call and per kernel (int8 GEMM into int32, then the requantisation), and
-    the output SQNR of the int8 codes against the float32 layer. The input
-    codes are the workload's X on a per-tensor grid (synthetic input)."""
+def integer_layer(hq, torch, WL, steps, warmup, dev, side):
+    """lic_wh as an integer-only layer with integer requantisation (int8
+    codes in, int8 codes out): the weight-only Hadamard layer (H_256 on the
+    output channels, output in the original basis) or the double-Hadamard
+    layer (input in the H_256 basis of the previous DH layer, output moved to
+    the next one's H_256 basis). Time per call (int8 GEMM into int32, then the
+    requantisation) and the output SQNR of the int8 codes against the float32
+    layer in the same basis. The input codes are the workload's X (rotated for
+    DH) on a per-tensor grid (synthetic input)."""
     w = WL.WORKLOADS["lic_wh"]
     X = torch.from_numpy(WL.gen_x(w)).to(dev)
     W = torch.from_numpy(WL.gen_weight(w)).to(dev)
     B = torch.from_numpy(WL.gen_bias(w)).to(dev)
     ref = torch.addmm(B, X, W.t())
+    wh = side == hq.HQ_INT_WH
+    if not wh:
+        # orthonormal Sylvester H_256: the DH input and output bases
+        H = torch.ones(1, 1, dtype=torch.float64)
+        while H.shape[0] < w.block:
+            H = torch.cat([torch.cat([H, H], 1), torch.cat([H, -H], 1)], 0)
+        H = (H / math.sqrt(w.block)).to(dev)
+        def rot(a):
+            return (a.double().reshape(a.shape[0], -1, w.block) @ H).reshape(a.shape).float()
+        X, ref = rot(X), rot(ref)
     s_x = float(X.abs().max().item() / 127.0)
     s_y = float(ref.abs().max().item() / 127.0)
     X0 = torch.clamp(torch.round(X / s_x), -127, 127).to(torch.int8)
-    desc = hq.WhDesc(w.d_in, w.d_out, w.block, hq.F32)
-    prep = hq.wh_prepare(desc, W, B, s_x, s_y)
+    desc = hq.IntDesc(w.d_in, w.d_out, w.block, hq.F32, side, 1 if wh else w.block)
+    prep = hq.int_prepare(desc, W, B, s_x, s_y)
     nbuf = max(2, math.ceil(512e6 / X0.numel()))
     Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
     Ys = [torch.empty(w.T, w.d_out, dtype=torch.int8, device=dev) for _ in range(nbuf)]
-    ws = torch.empty(hq.wh_workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
+    ws = torch.empty(hq.int_workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
     for i in range(warmup):
-        hq.wh_linear(desc, prep, Xs[i % nbuf], out=Ys[i % nbuf], workspace=ws)
+        hq.int_linear(desc, prep, Xs[i % nbuf], out=Ys[i % nbuf], workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
-        hq.wh_linear(desc, prep, Xs[(warmup + i) % nbuf], out=Ys[(warmup + i) % nbuf], workspace=ws)
+        hq.int_linear(desc, prep, Xs[(warmup + i) % nbuf], out=Ys[(warmup + i) % nbuf],
+                      workspace=ws)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -346,10 +360,11 @@ def weight_only_hadamard(hq, torch, WL, steps, warmup, dev):
     del Xs, Ys
     # bytes that must move: int8 codes in and out, weight codes, constants
     algo = w.T * (w.d_in + w.d_out) + w.d_out * (w.d_in + 12)
-    return {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
-            "block": w.block, "bits": "W8A8 int8 -> int8", "value": round(w.T / (ms * 1e-3), 1),
-            "unit": "tokens/s", "ms_per_step": round(ms, 5),
-            "algorithmic_GBs": round(algo / (ms * 1e-3) / 1e9, 1), "sqnr_db": round(sq, 2)}
+    return {"workload": w.name, "layer": "WH" if wh else "DH-to-DH", "tokens": w.T,
+            "d_in": w.d_in, "d_out": w.d_out, "block": w.block, "bits": "W8A8 int8 -> int8",
+            "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 5), "algorithmic_GBs": round(algo / (ms * 1e-3) / 1e9, 1),
+            "sqnr_db": round(sq, 2)}
 
 
 def main():
@@ -441,8 +456,9 @@ def main():
     if not args.no_extras:
         out["group_wise"] = group_wise(hq, torch, WL, min(args.steps, 20), min(args.warmup, 5),
                                        dev)
-        out["weight_only_hadamard"] = weight_only_hadamard(hq, torch, WL, min(args.steps, 20),
-                                                           min(args.warmup, 5), dev)
+        out["integer_layers"] = [
+            integer_layer(hq, torch, WL, min(args.steps, 20), min(args.warmup, 5), dev, side)
+            for side in (hq.HQ_INT_WH, hq.HQ_INT_DH)]
         out["centring_modes"] = centring_modes(hq, torch, WL, min(args.steps, 20),
                                                min(args.warmup, 5), dev)
     if not args.no_cpu_baseline:

@@ -21,7 +21,8 @@ import torch
 
 from . import _lib
 from ._lib import (HQ_CENTER_CHANNEL, HQ_CENTER_NONE, HQ_CENTER_TOKEN, HQ_CODES_E2M3,
-                   HQ_CODES_I8, HQ_GEMM_AUTO, HQ_GEMM_I8, HqDesc, HqError, HqLayout, check, load)
+                   HQ_CODES_I8, HQ_GEMM_AUTO, HQ_GEMM_I8, HQ_INT_DH, HQ_INT_WH, HqDesc, HqError,
+                   HqLayout, check, load)
 
 F32, BF16 = 0, 1
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16}
@@ -323,82 +324,87 @@ def prepared_views(desc: Desc, prepared: torch.Tensor) -> dict:
     return out
 
 
-# ---- weight-only Hadamard layer with integer requantisation ----------------
+# ---- integer-only DH / WH layers with integer requantisation ---------------
 
 @dataclasses.dataclass(frozen=True)
-class WhDesc:
-    """Descriptor of a weight-only Hadamard layer; mirrors hq_wh_desc
-    (block = m, the order of the output-side Hadamard transform)."""
+class IntDesc:
+    """Descriptor of an integer-only layer; mirrors hq_int_desc. ``side``
+    HQ_INT_WH (weight transformed along its outputs by H of order ``block``)
+    or HQ_INT_DH (along its inputs by H of order ``in_block``); ``block`` is
+    the order of the output-side integer transform."""
     d_in: int
     d_out: int
     block: int
     w_dtype: int = F32
+    side: int = _lib.HQ_INT_WH
+    in_block: int = 1
 
     def __post_init__(self):
-        raw = _lib.HqWhDesc(self.d_in, self.d_out, self.block, self.w_dtype)
+        raw = _lib.HqIntDesc(self.d_in, self.d_out, self.block, self.w_dtype, self.side,
+                             self.in_block)
         object.__setattr__(self, "_raw", raw)
         object.__setattr__(self, "_ref", ctypes.byref(raw))
 
 
-def wh_layout(desc: WhDesc) -> "_lib.HqWhLayout":
-    out = _lib.HqWhLayout()
-    check(load().hq_wh_prepared_layout_of(desc._ref, ctypes.byref(out)))
+def int_layout(desc: IntDesc) -> "_lib.HqIntLayout":
+    out = _lib.HqIntLayout()
+    check(load().hq_int_prepared_layout_of(desc._ref, ctypes.byref(out)))
     return out
 
 
-def wh_workspace_bytes(desc: WhDesc, T: int) -> int:
+def int_workspace_bytes(desc: IntDesc, T: int) -> int:
     if T < 0:
         raise HqError(_lib.HQ_ERR_INVALID_ARG, "T must be >= 0")
-    n = load().hq_wh_workspace_bytes(desc._ref, T)
+    n = load().hq_int_workspace_bytes(desc._ref, T)
     if n == 0:
-        check(load().hq_wh_validate(desc._ref))
+        check(load().hq_int_validate(desc._ref))
     return n
 
 
-def wh_prepare(desc: WhDesc, weight: torch.Tensor, bias: Optional[torch.Tensor], s_x: float,
-               s_y: float) -> torch.Tensor:
-    """Offline WH weight transform; returns the prepared blob (uint8 device tensor)."""
+def int_prepare(desc: IntDesc, weight: torch.Tensor, bias: Optional[torch.Tensor], s_x: float,
+                s_y: float) -> torch.Tensor:
+    """Offline transform of an integer-only layer; returns the prepared blob."""
     _need(weight, "weight", _TORCH[desc.w_dtype], (desc.d_out, desc.d_in))
     if bias is not None:
         _need(bias, "bias", torch.float32, (desc.d_out,))
-    n = load().hq_wh_prepared_bytes(desc._ref)
+    n = load().hq_int_prepared_bytes(desc._ref)
     if n == 0:
-        check(load().hq_wh_validate(desc._ref))
+        check(load().hq_int_validate(desc._ref))
     blob = torch.empty(n, dtype=torch.uint8, device=weight.device)
-    check(load().hq_wh_prepare(desc._ref, _ptr(weight), _ptr(bias), ctypes.c_float(s_x),
-                               ctypes.c_float(s_y), _ptr(blob), _stream()))
+    check(load().hq_int_prepare(desc._ref, _ptr(weight), _ptr(bias), ctypes.c_float(s_x),
+                                ctypes.c_float(s_y), _ptr(blob), _stream()))
     return blob
 
 
-def wh_linear(desc: WhDesc, prepared: torch.Tensor, x_codes: torch.Tensor,
-              out: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """int8 output codes [T, d_out] of the WH layer for int8 input codes [T, d_in]."""
+def int_linear(desc: IntDesc, prepared: torch.Tensor, x_codes: torch.Tensor,
+               out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int8 output codes [T, d_out] of the layer for int8 input codes [T, d_in]."""
     T = x_codes.shape[0]
     _need(x_codes, "x_codes", torch.int8, (T, desc.d_in))
     y = out if out is not None else torch.empty(T, desc.d_out, dtype=torch.int8,
-                                                 device=x_codes.device)
+                                                device=x_codes.device)
     _need(y, "out", torch.int8, (T, desc.d_out))
-    nws = wh_workspace_bytes(desc, T)
+    nws = int_workspace_bytes(desc, T)
     ws = workspace if workspace is not None else torch.empty(
         max(nws, 1), dtype=torch.uint8, device=x_codes.device)
-    check(load().hq_wh_linear(desc._ref, _ptr(prepared), _ptr(x_codes), T, _ptr(y), _ptr(ws),
-                              ws.numel(), _stream()))
+    check(load().hq_int_linear(desc._ref, _ptr(prepared), _ptr(x_codes), T, _ptr(y), _ptr(ws),
+                               ws.numel(), _stream()))
     return y
 
 
-def wh_requant(desc: WhDesc, prepared: torch.Tensor, acc: torch.Tensor) -> torch.Tensor:
+def int_requant(desc: IntDesc, prepared: torch.Tensor, acc: torch.Tensor) -> torch.Tensor:
     """Requantisation alone: int8 [T, d_out] from int32 products [T, d_out] (no bias)."""
     T = acc.shape[0]
     _need(acc, "acc", torch.int32, (T, desc.d_out))
     y = torch.empty(T, desc.d_out, dtype=torch.int8, device=acc.device)
-    check(load().hq_wh_requant(desc._ref, _ptr(prepared), _ptr(acc), T, _ptr(y), _stream()))
+    check(load().hq_int_requant(desc._ref, _ptr(prepared), _ptr(acc), T, _ptr(y), _stream()))
     return y
 
 
-def wh_views(desc: WhDesc, prepared: torch.Tensor) -> dict:
-    """Views of the arrays inside a WH prepared blob (for inspection and tests)."""
-    L = wh_layout(desc)
+def int_views(desc: IntDesc, prepared: torch.Tensor) -> dict:
+    """Views of the arrays inside an integer-layer prepared blob (for tests)."""
+    L = int_layout(desc)
     npad, d = L.d_out_pad, desc.d_in
 
     def view(off, n, dtype, shape):

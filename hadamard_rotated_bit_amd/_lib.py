@@ -23,11 +23,12 @@ class HqLayout(ctypes.Structure):
                  "l2_hi", "l2_lo", "weight"]] + [("d_out_pad", ctypes.c_int64)]
 
 
-class HqWhDesc(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ["d_in", "d_out", "block", "w_dtype"]]
+class HqIntDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ["d_in", "d_out", "block", "w_dtype", "side", "in_block"]]
 
 
-class HqWhLayout(ctypes.Structure):
+class HqIntLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ["total", "w_codes", "w_scale", "b_int", "mult", "shift", "wbar"]] + [
         ("d_out_pad", ctypes.c_int64)]
@@ -36,13 +37,14 @@ class HqWhLayout(ctypes.Structure):
 HQ_CODES_I8, HQ_CODES_E2M3 = 0, 1
 HQ_GEMM_AUTO, HQ_GEMM_I8 = 0, 1
 HQ_CENTER_NONE, HQ_CENTER_TOKEN, HQ_CENTER_CHANNEL = 0, 1, 2
+HQ_INT_WH, HQ_INT_DH = 0, 1
 
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_BAD_PREPARED, \
     HQ_ERR_HIP = 0, -1, -2, -3, -4, -5
 
 _P = ctypes.c_void_p
 _D = ctypes.POINTER(HqDesc)
-_W = ctypes.POINTER(HqWhDesc)
+_W = ctypes.POINTER(HqIntDesc)
 _I64 = ctypes.c_int64
 _SIGS = {
     "hq_abi_version": (ctypes.c_int, []),
@@ -64,13 +66,13 @@ _SIGS = {
     "hq_act_transform": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, _P]),
     "hq_gemm_i32": (ctypes.c_int, [_D, _P, _P, _I64, _I64, _P, _P]),
     "hq_gemm_dequant": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _I64, _P, _P]),
-    "hq_wh_validate": (ctypes.c_int, [_W]),
-    "hq_wh_prepared_bytes": (ctypes.c_size_t, [_W]),
-    "hq_wh_prepared_layout_of": (ctypes.c_int, [_W, ctypes.POINTER(HqWhLayout)]),
-    "hq_wh_workspace_bytes": (ctypes.c_size_t, [_W, _I64]),
-    "hq_wh_prepare": (ctypes.c_int, [_W, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P]),
-    "hq_wh_linear": (ctypes.c_int, [_W, _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
-    "hq_wh_requant": (ctypes.c_int, [_W, _P, _P, _I64, _P, _P]),
+    "hq_int_validate": (ctypes.c_int, [_W]),
+    "hq_int_prepared_bytes": (ctypes.c_size_t, [_W]),
+    "hq_int_prepared_layout_of": (ctypes.c_int, [_W, ctypes.POINTER(HqIntLayout)]),
+    "hq_int_workspace_bytes": (ctypes.c_size_t, [_W, _I64]),
+    "hq_int_prepare": (ctypes.c_int, [_W, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P]),
+    "hq_int_linear": (ctypes.c_int, [_W, _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "hq_int_requant": (ctypes.c_int, [_W, _P, _P, _I64, _P, _P]),
 }
 
 _lib = None

@@ -264,27 +264,29 @@ int run_gemm_dequant(const hq_desc* d, const void* prepared, const void* codes,
   return HQ_OK;
 }
 
-// ---- weight-only Hadamard layer --------------------------------------------
+// ---- integer-only DH / WH layers ---------------------------------------------
 
-constexpr uint32_t kMagicWH = 0x31575148u;  // "HQW1"
+constexpr uint32_t kMagicInt = 0x31495148u;  // "HQI1"
 
-struct WhHeader {
+struct IntHeader {
   uint32_t magic;
   uint32_t version;
-  hq_wh_desc desc;
+  hq_int_desc desc;
   int64_t d_out_pad;
   uint64_t total;
   float s_x, s_y;
 };
-static_assert(sizeof(WhHeader) <= 256, "header fits in 256 bytes");
+static_assert(sizeof(IntHeader) <= 256, "header fits in 256 bytes");
 
-int check_wh_desc(const hq_wh_desc* d) {
+int check_int_desc(const hq_int_desc* d) {
   if (!d) return fail(HQ_ERR_INVALID_ARG, "desc is NULL");
   if (d->d_in <= 0 || d->d_out <= 0)
     return fail(HQ_ERR_INVALID_ARG, "d_in and d_out must be positive (got %d, %d)", d->d_in,
                 d->d_out);
   if (d->w_dtype != HQ_F32 && d->w_dtype != HQ_BF16)
     return fail(HQ_ERR_INVALID_ARG, "w_dtype %d is not an hq_dtype", d->w_dtype);
+  if (d->side != HQ_INT_WH && d->side != HQ_INT_DH)
+    return fail(HQ_ERR_INVALID_ARG, "side must be HQ_INT_WH or HQ_INT_DH (got %d)", d->side);
   hq::RowGeom g;
   if (d->d_in % 128 || !hq::row_geometry(d->d_in, &g))
     return fail(HQ_ERR_UNSUPPORTED,
@@ -296,10 +298,15 @@ int check_wh_desc(const hq_wh_desc* d) {
   if (!is_pow2(d->block) || d->block > hq::WH_MAX_BLOCK || d->d_out % d->block)
     return fail(HQ_ERR_UNSUPPORTED, "block %d must be a power of two <= %d dividing d_out %d",
                 d->block, hq::WH_MAX_BLOCK, d->d_out);
+  if (d->side == HQ_INT_WH && d->in_block != 1)
+    return fail(HQ_ERR_UNSUPPORTED, "a WH layer takes in_block = 1 (got %d)", d->in_block);
+  if (d->side == HQ_INT_DH && (!is_pow2(d->in_block) || d->d_in % d->in_block))
+    return fail(HQ_ERR_UNSUPPORTED, "in_block %d must be a power of two dividing d_in %d",
+                d->in_block, d->d_in);
   return HQ_OK;
 }
 
-void wh_layout_of(const hq_wh_desc* d, hq_wh_layout* L) {
+void int_layout_of(const hq_int_desc* d, hq_int_layout* L) {
   const int64_t np = round_up(d->d_out, hq::GEMM_BN);
   size_t off = 256;
   L->d_out_pad = np;
@@ -318,14 +325,14 @@ void wh_layout_of(const hq_wh_desc* d, hq_wh_layout* L) {
   L->total = off;
 }
 
-int run_wh_requant(const hq_wh_desc* d, const void* prepared, const int32_t* acc, int64_t T,
-                   int8_t* y, hipStream_t s) {
-  hq_wh_layout L;
-  wh_layout_of(d, &L);
-  hipError_t e = hq::launch_wh_requant(acc, d->d_out, T, d->d_out, d->block,
-                                       at<int32_t>(prepared, L.b_int),
-                                       at<int32_t>(prepared, L.mult),
-                                       at<int32_t>(prepared, L.shift), y, d->d_out, s);
+int run_int_requant(const hq_int_desc* d, const void* prepared, const int32_t* acc, int64_t T,
+                    int8_t* y, hipStream_t s) {
+  hq_int_layout L;
+  int_layout_of(d, &L);
+  hipError_t e = hq::launch_int_requant(acc, d->d_out, T, d->d_out, d->block,
+                                        at<int32_t>(prepared, L.b_int),
+                                        at<int32_t>(prepared, L.mult),
+                                        at<int32_t>(prepared, L.shift), y, d->d_out, s);
   return e == hipSuccess ? HQ_OK : hip_fail(e, "requantisation kernel launch");
 }
 
@@ -648,31 +655,31 @@ int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes
                           static_cast<hipStream_t>(stream));
 }
 
-int hq_wh_validate(const hq_wh_desc* desc) {
+int hq_int_validate(const hq_int_desc* desc) {
   g_err.clear();
-  return check_wh_desc(desc);
+  return check_int_desc(desc);
 }
 
-size_t hq_wh_prepared_bytes(const hq_wh_desc* desc) {
+size_t hq_int_prepared_bytes(const hq_int_desc* desc) {
   g_err.clear();
-  if (check_wh_desc(desc) != HQ_OK) return 0;
-  hq_wh_layout L;
-  wh_layout_of(desc, &L);
+  if (check_int_desc(desc) != HQ_OK) return 0;
+  hq_int_layout L;
+  int_layout_of(desc, &L);
   return L.total;
 }
 
-int hq_wh_prepared_layout_of(const hq_wh_desc* desc, hq_wh_layout* out) {
+int hq_int_prepared_layout_of(const hq_int_desc* desc, hq_int_layout* out) {
   g_err.clear();
   if (!out) return fail(HQ_ERR_INVALID_ARG, "out is NULL");
-  int st = check_wh_desc(desc);
+  int st = check_int_desc(desc);
   if (st != HQ_OK) return st;
-  wh_layout_of(desc, out);
+  int_layout_of(desc, out);
   return HQ_OK;
 }
 
-size_t hq_wh_workspace_bytes(const hq_wh_desc* desc, int64_t T) {
+size_t hq_int_workspace_bytes(const hq_int_desc* desc, int64_t T) {
   g_err.clear();
-  if (check_wh_desc(desc) != HQ_OK) return 0;
+  if (check_int_desc(desc) != HQ_OK) return 0;
   if (T < 0) {
     fail(HQ_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
     return 0;
@@ -680,10 +687,10 @@ size_t hq_wh_workspace_bytes(const hq_wh_desc* desc, int64_t T) {
   return align256(4 * size_t(T) * desc->d_out);
 }
 
-int hq_wh_prepare(const hq_wh_desc* desc, const void* weight, const float* bias, float s_x,
-                  float s_y, void* prepared, void* stream) {
+int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bias, float s_x,
+                   float s_y, void* prepared, void* stream) {
   g_err.clear();
-  int st = check_wh_desc(desc);
+  int st = check_int_desc(desc);
   if (st != HQ_OK) return st;
   if (!weight || !prepared) return fail(HQ_ERR_INVALID_ARG, "weight and prepared must be non-NULL");
   if (!(s_x > 0.0f) || !(s_y > 0.0f) || !std::isfinite(s_x) || !std::isfinite(s_y))
@@ -691,18 +698,35 @@ int hq_wh_prepare(const hq_wh_desc* desc, const void* weight, const float* bias,
                 double(s_x), double(s_y));
   if (misaligned(prepared)) return fail(HQ_ERR_INVALID_ARG, "prepared must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hq_wh_layout L;
-  wh_layout_of(desc, &L);
+  hq_int_layout L;
+  int_layout_of(desc, &L);
   const int64_t np = L.d_out_pad, dout = desc->d_out, din = desc->d_in;
+  const bool wh = desc->side == HQ_INT_WH;
   hipError_t e = hipSuccess;
   if (np > dout)
     e = hq::launch_fill_u8(at<uint8_t>(prepared, L.w_codes + size_t(dout) * din), 0,
                            size_t(np - dout) * din, s);
   if (e == hipSuccess)
     e = hq::launch_fill_u32(at<uint32_t>(prepared, L.w_scale), 0u, size_t(np), s);
-  if (e == hipSuccess)
-    e = hq::launch_wh_weight(weight, desc->w_dtype == HQ_BF16, int(dout), int(din), desc->block,
-                             at<float>(prepared, L.wbar), s);
+  if (e == hipSuccess) {
+    if (wh) {
+      // W-bar = H_out W: butterflies over the output-channel index
+      e = hq::launch_wh_weight(weight, desc->w_dtype == HQ_BF16, int(dout), int(din),
+                               desc->block, at<float>(prepared, L.wbar), s);
+    } else {
+      // W-bar = W H_in: the row transform along d_in, exported as float
+      hq::RowArgs a = {};
+      a.in = weight;
+      a.in_bf16 = desc->w_dtype == HQ_BF16;
+      a.rows = dout;
+      a.d = int(din);
+      a.log2b = log2i(desc->in_block);
+      a.qmax = 127.0f;
+      a.out_xt = at<float>(prepared, L.wbar);
+      a.mode = hq::ROW_EXPORT;
+      e = hq::launch_row_transform(a, s);
+    }
+  }
   if (e == hipSuccess) {
     // per-output-channel 8-bit codes of W-bar (no further rotation)
     hq::RowArgs a = {};
@@ -719,12 +743,13 @@ int hq_wh_prepare(const hq_wh_desc* desc, const void* weight, const float* bias,
     e = hq::launch_row_transform(a, s);
   }
   if (e == hipSuccess)
-    e = hq::launch_wh_constants(bias, at<float>(prepared, L.w_scale), int(dout), int(np),
-                                desc->block, s_x, s_y, at<int32_t>(prepared, L.b_int),
-                                at<int32_t>(prepared, L.mult), at<int32_t>(prepared, L.shift), s);
+    e = hq::launch_int_constants(bias, at<float>(prepared, L.w_scale), int(dout), int(np),
+                                 desc->block, wh ? desc->block : 1, s_x, s_y,
+                                 at<int32_t>(prepared, L.b_int), at<int32_t>(prepared, L.mult),
+                                 at<int32_t>(prepared, L.shift), s);
   if (e == hipSuccess) {
-    WhHeader h = {};
-    h.magic = kMagicWH;
+    IntHeader h = {};
+    h.magic = kMagicInt;
     h.version = HQ_ABI_VERSION;
     h.desc = *desc;
     h.d_out_pad = np;
@@ -733,13 +758,14 @@ int hq_wh_prepare(const hq_wh_desc* desc, const void* weight, const float* bias,
     h.s_y = s_y;
     e = hq::launch_write_header(&h, sizeof(h), prepared, s);
   }
-  return e == hipSuccess ? HQ_OK : hip_fail(e, "WH prepare kernel launch");
+  return e == hipSuccess ? HQ_OK : hip_fail(e, "integer-layer prepare kernel launch");
 }
 
-int hq_wh_linear(const hq_wh_desc* desc, const void* prepared, const int8_t* x_codes, int64_t T,
-                 int8_t* y_codes, void* workspace, size_t workspace_bytes, void* stream) {
+int hq_int_linear(const hq_int_desc* desc, const void* prepared, const int8_t* x_codes,
+                  int64_t T, int8_t* y_codes, void* workspace, size_t workspace_bytes,
+                  void* stream) {
   g_err.clear();
-  int st = check_wh_desc(desc);
+  int st = check_int_desc(desc);
   if (st != HQ_OK) return st;
   if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
   if (T == 0) return HQ_OK;
@@ -751,19 +777,19 @@ int hq_wh_linear(const hq_wh_desc* desc, const void* prepared, const int8_t* x_c
   if (workspace_bytes < need)
     return fail(HQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hq_wh_layout L;
-  wh_layout_of(desc, &L);
+  hq_int_layout L;
+  int_layout_of(desc, &L);
   int32_t* acc = static_cast<int32_t*>(workspace);
   hipError_t e = hq::launch_gemm(x_codes, T, at<int8_t>(prepared, L.w_codes), desc->d_out,
                                  desc->d_in, acc, desc->d_out, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "GEMM kernel launch");
-  return run_wh_requant(desc, prepared, acc, T, y_codes, s);
+  return run_int_requant(desc, prepared, acc, T, y_codes, s);
 }
 
-int hq_wh_requant(const hq_wh_desc* desc, const void* prepared, const int32_t* acc, int64_t T,
-                  int8_t* y_codes, void* stream) {
+int hq_int_requant(const hq_int_desc* desc, const void* prepared, const int32_t* acc, int64_t T,
+                   int8_t* y_codes, void* stream) {
   g_err.clear();
-  int st = check_wh_desc(desc);
+  int st = check_int_desc(desc);
   if (st != HQ_OK) return st;
   if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
   if (T == 0) return HQ_OK;
@@ -771,7 +797,7 @@ int hq_wh_requant(const hq_wh_desc* desc, const void* prepared, const int32_t* a
     return fail(HQ_ERR_INVALID_ARG, "prepared, acc and y_codes must be non-NULL");
   if (misaligned(acc) || misaligned(y_codes) || misaligned(prepared))
     return fail(HQ_ERR_INVALID_ARG, "acc, y_codes and prepared must be 16-byte aligned");
-  return run_wh_requant(desc, prepared, acc, T, y_codes, static_cast<hipStream_t>(stream));
+  return run_int_requant(desc, prepared, acc, T, y_codes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

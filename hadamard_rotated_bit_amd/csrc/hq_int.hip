@@ -1,11 +1,16 @@
-// Weight-only Hadamard (WH) layer with integer requantisation ("Hadamard-Domain
-// Model Quantization for Learned Image Coding", Sec. IV-B Eq. (15)-(22) and
-// supplement Eq. (40)-(44)): the weight is transformed along its output
-// channels, W-bar = H_out W, b-bar = b H_out; the int8 activation stays in its
-// original basis; the int32 product a = x w-bar^T + b_int is mapped back to
-// the original basis and onto the next layer's int8 grid with integers only:
+// Integer-only layers with integer requantisation ("Hadamard-Domain Model
+// Quantization for Learned Image Coding", Sec. IV-B Eq. (13)-(22) and
+// supplement Eq. (40)-(44)). A weight-only Hadamard (WH) layer transforms the
+// weight along its output channels, W-bar = H_out W, b-bar = b H_out, and
+// takes its int8 activation in the original basis; a double-Hadamard (DH)
+// layer transforms it along its input channels, W-bar = W H_in, b-bar = b,
+// and takes its activation in the H_in basis. The int32 product
+// a = x w-bar^T + b_int goes onto the next layer's int8 grid with integers
+// only, through one unnormalised transform of order m over the channels
+// (WH: restoring the original basis; DH: the next layer's H_in basis; m = 1:
+// none):
 //
-//   y = clamp(round(H~_out (M . a) / 2^n), -127, 127)
+//   y = clamp(round(H~_m (M . a) / 2^n), -127, 127)
 //
 // with per-channel 16-bit multipliers M and one shared shift n (the Hadamard
 // normalisation 1/sqrt(m) folded into M).
@@ -48,15 +53,16 @@ __global__ __launch_bounds__(256) void wh_weight_kernel(const TW* __restrict__ w
     for (int r = tr; r < m; r += 8) wbar[(row0 + r) * d_in + col] = tile[r * LD + tc] * inv_sqrt_m;
 }
 
-// Offline constants (one block, float64): b-bar = b H_m, s_A = s_x s_w,
+// Offline constants (one block, float64): b-bar = b H_bb (bb = m for WH, 1
+// for DH), s_A = s_x s_w,
 // b_int = round(b-bar / s_A) (saturated at +-2^27, see the requantisation
 // kernel), rho = s_A / (sqrt(m) s_y), the shared shift n (largest n <= 48 with
 // every round(2^n rho) <= 32767) and M = round(2^n rho). Rows past d_out get
 // zeros.
-__global__ __launch_bounds__(256) void wh_constants_kernel(const float* __restrict__ bias,
+__global__ __launch_bounds__(256) void int_constants_kernel(const float* __restrict__ bias,
                                                            const float* __restrict__ s_w,
                                                            int d_out, int d_out_pad, int m,
-                                                           double s_x, double s_y,
+                                                           int bb_order, double s_x, double s_y,
                                                            int32_t* __restrict__ b_int,
                                                            int32_t* __restrict__ mult,
                                                            int32_t* __restrict__ shift) {
@@ -87,13 +93,13 @@ __global__ __launch_bounds__(256) void wh_constants_kernel(const float* __restri
       const double rho = s_a / (sqm * s_y);
       mc = int32_t(rint(ldexp(rho, n)));
       if (bias && s_a > 0.0) {
-        const int base = (c / m) * m, ci = c - base;
+        const int base = (c / bb_order) * bb_order, ci = c - base;
         double bb = 0.0;
-        for (int k = 0; k < m; ++k) {
+        for (int k = 0; k < bb_order; ++k) {
           const double v = double(bias[base + k]);
           bb += (__popc(ci & k) & 1) ? -v : v;
         }
-        double q = rint((bb / sqm) / s_a);
+        double q = rint((bb / sqrt(double(bb_order))) / s_a);
         q = q > double(WH_BIAS_MAX) ? double(WH_BIAS_MAX) : q;
         q = q < -double(WH_BIAS_MAX) ? -double(WH_BIAS_MAX) : q;
         bi = int32_t(q);
@@ -135,7 +141,7 @@ __device__ __forceinline__ double lane_xor16_f64(double v) {
 // One butterfly stage over channel bit 4 + log2(D) (lane distance D): the
 // lane with bit D clear keeps u + partner, the other partner - u.
 template <int D>
-__device__ __forceinline__ void wh_xstage(double (&u)[16], int lane, int m) {
+__device__ __forceinline__ void int_xstage(double (&u)[16], int lane, int m) {
   if (16 * D >= m) return;
   const double g = (lane & D) ? -1.0 : 1.0;
 #pragma unroll
@@ -150,7 +156,7 @@ __device__ __forceinline__ void wh_xstage(double (&u)[16], int lane, int m) {
 // round(u / 2^n) with ties to even and clamping to +-127. Every lane of a
 // group runs the butterflies (invalid channels hold 0; blocks never mix valid
 // and invalid channels, m dividing d_out).
-__global__ __launch_bounds__(256) void wh_requant_kernel(
+__global__ __launch_bounds__(256) void int_requant_kernel(
     const int32_t* __restrict__ acc, int64_t ldc, int64_t T, int d_out, int chunks, int m,
     const int32_t* __restrict__ b_int, const int32_t* __restrict__ mult,
     const int32_t* __restrict__ shift, int8_t* __restrict__ y, int64_t ldy) {
@@ -191,10 +197,10 @@ __global__ __launch_bounds__(256) void wh_requant_kernel(
     }
   }
   // channel bits 4-7, across the 16 lanes of the group
-  wh_xstage<1>(u, lane, m);
-  wh_xstage<2>(u, lane, m);
-  wh_xstage<4>(u, lane, m);
-  wh_xstage<8>(u, lane, m);
+  int_xstage<1>(u, lane, m);
+  int_xstage<2>(u, lane, m);
+  int_xstage<4>(u, lane, m);
+  int_xstage<8>(u, lane, m);
   if (!live || c0 >= d_out) return;
   const double scale = ldexp(1.0, -*shift);
   uint32_t w[4];
@@ -230,15 +236,17 @@ hipError_t launch_wh_weight(const void* w, int w_bf16, int d_out, int d_in, int 
   return hipGetLastError();
 }
 
-hipError_t launch_wh_constants(const float* bias, const float* s_w, int d_out, int d_out_pad,
-                               int m, float s_x, float s_y, int32_t* b_int, int32_t* mult,
-                               int32_t* shift, hipStream_t s) {
-  hipLaunchKernelGGL(wh_constants_kernel, dim3(1), dim3(256), 0, s, bias, s_w, d_out, d_out_pad,
-                     m, double(s_x), double(s_y), b_int, mult, shift);
+hipError_t launch_int_constants(const float* bias, const float* s_w, int d_out, int d_out_pad,
+                                int m, int bias_block, float s_x, float s_y, int32_t* b_int,
+                                int32_t* mult, int32_t* shift, hipStream_t s) {
+  if (bias_block < 1 || (bias_block & (bias_block - 1)) || d_out % bias_block)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(int_constants_kernel, dim3(1), dim3(256), 0, s, bias, s_w, d_out, d_out_pad,
+                     m, bias_block, double(s_x), double(s_y), b_int, mult, shift);
   return hipGetLastError();
 }
 
-hipError_t launch_wh_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_out, int m,
+hipError_t launch_int_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_out, int m,
                              const int32_t* b_int, const int32_t* mult, const int32_t* shift,
                              int8_t* y, int64_t ldy, hipStream_t s) {
   if (T <= 0) return hipSuccess;
@@ -246,7 +254,7 @@ hipError_t launch_wh_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_o
     return hipErrorInvalidValue;
   const int chunks = (d_out + 255) / 256;
   const int64_t units = T * chunks;   // 16 lanes each, 16 per block
-  hipLaunchKernelGGL(wh_requant_kernel, dim3(unsigned((units + 15) / 16)), dim3(256), 0, s, acc,
+  hipLaunchKernelGGL(int_requant_kernel, dim3(unsigned((units + 15) / 16)), dim3(256), 0, s, acc,
                      ldc, T, d_out, chunks, m, b_int, mult, shift, y, ldy);
   return hipGetLastError();
 }

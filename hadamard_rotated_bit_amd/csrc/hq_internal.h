@@ -113,7 +113,7 @@ hipError_t launch_gemm_f6g(const uint8_t* A, int64_t M, const uint8_t* B, int64_
 hipError_t launch_gemm_f6(const uint8_t* A, int64_t M, const uint8_t* B, int64_t N, int K,
                           int32_t* acc_out, int64_t ldc, const GemmEpi* epi, hipStream_t s);
 
-// Weight-only Hadamard layer with integer requantisation.
+// Integer-only DH / WH layers with integer requantisation.
 constexpr int WH_MAX_BLOCK = 256;       // largest output-side Hadamard order
 constexpr int WH_SHIFT_MAX = 48;        // largest shared requantisation shift
 constexpr int WH_MULT_MAX = 32767;      // multipliers fit a positive 16-bit integer
@@ -121,13 +121,14 @@ constexpr int WH_BIAS_MAX = 1 << 27;    // bias codes saturate here (exact float
 // wbar [d_out, d_in] f32 = H_m (blocks of m output channels) . weight.
 hipError_t launch_wh_weight(const void* w, int w_bf16, int d_out, int d_in, int m, float* wbar,
                             hipStream_t s);
-// b_int, mult [d_out_pad] and shift [1] from bias [d_out] (or NULL), s_w [d_out].
-hipError_t launch_wh_constants(const float* bias, const float* s_w, int d_out, int d_out_pad,
-                               int m, float s_x, float s_y, int32_t* b_int, int32_t* mult,
-                               int32_t* shift, hipStream_t s);
+// b_int, mult [d_out_pad] and shift [1] from bias [d_out] (or NULL; b-bar =
+// b H over blocks of bias_block channels) and s_w [d_out]; rho uses sqrt(m).
+hipError_t launch_int_constants(const float* bias, const float* s_w, int d_out, int d_out_pad,
+                                int m, int bias_block, float s_x, float s_y, int32_t* b_int,
+                                int32_t* mult, int32_t* shift, hipStream_t s);
 // y [T, ldy] int8 = clamp(round(H~_m (mult . (acc + b_int)) / 2^shift), +-127).
-hipError_t launch_wh_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_out, int m,
-                             const int32_t* b_int, const int32_t* mult, const int32_t* shift,
-                             int8_t* y, int64_t ldy, hipStream_t s);
+hipError_t launch_int_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_out, int m,
+                              const int32_t* b_int, const int32_t* mult, const int32_t* shift,
+                              int8_t* y, int64_t ldy, hipStream_t s);
 
 }  // namespace hq

@@ -91,7 +91,7 @@
 extern "C" {
 #endif
 
-#define HQ_ABI_VERSION 6
+#define HQ_ABI_VERSION 7
 
 typedef enum {
   HQ_OK = 0,
@@ -269,38 +269,49 @@ int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes
                     const float* s_x, const float* mu, const float* U, int64_t T, void* Y,
                     void* stream);
 
-/* ---- Weight-only Hadamard (WH) layer with integer requantisation ----------
+/* ---- Integer-only layers: double-Hadamard (DH) and weight-only Hadamard (WH) ----
  *
  * "Hadamard-Domain Model Quantization for Learned Image Coding" (HaTQ),
- * Sec. IV-B Eq. (15)-(17): the weight is transformed along its OUTPUT
- * channels, W-bar = H_out W, and the bias with it, b-bar = b H_out (supplement
- * Eq. (40)); the activation stays in its original basis as int8 codes with one
- * static per-tensor scale s_x. Integer-only inference (Sec. III-B, Eq. (4)-(6),
- * (18)-(22), supplement Eq. (44)), for a WH layer whose output feeds another
- * WH layer through the identity activation:
+ * Sec. IV-B Eq. (13)-(17) and supplement Eq. (40): a WH layer transforms its
+ * weight along the OUTPUT channels, W-bar = H_out W, and the bias with it,
+ * b-bar = b H_out, and takes its int8 activation in the original basis; a DH
+ * layer transforms its weight along the INPUT channels, W-bar = W H_in,
+ * keeps b-bar = b, and takes its int8 activation already in the H_in basis.
+ * The activation has one static per-tensor scale s_x. Integer-only inference
+ * (Sec. III-B Eq. (4)-(6), Eq. (18)-(22), supplement Eq. (44)) with the
+ * identity activation:
  *
  *     a   = x_int . w-bar_int^T + b_int,   b_int = round(b-bar / (s_x s_w))
- *     y   = clamp(round(H~_out (M . a) / 2^n), -127, 127)
+ *     y   = clamp(round(H~_m (M . a) / 2^n), -127, 127)
  *     M_c = round(2^n rho_c),  rho_c = s_x s_w,c / (sqrt(m) s_y)
  *
- * H_out: normalised Sylvester matrix of order m, block-diagonal over d_out / m
- * blocks of output channels (m = d_out is the full transform); H~_out its +-1
- * form (additions and subtractions only). s_w,c: per-output-channel scale of
- * W-bar (8-bit symmetric codes); s_y: the scale of the output codes (the next
- * layer's input scale). n: the largest shift <= 48 with every M_c <= 32767.
- * round() is round half to even; bias codes saturate at +-2^27, so every
- * intermediate stays below 2^51 in magnitude. Every online step is exact
- * integer arithmetic (int32 products; after M the kernel carries the
- * integers in float64 registers, exact in that range).
+ * H~_m: the +-1 Sylvester matrix of order m, block-diagonal over d_out / m
+ * blocks of output channels (additions and subtractions only). It is Table
+ * I's output-side conversion: for a WH layer followed by a WH layer it
+ * restores the original basis (m = the layer's H_out order); for a DH layer
+ * followed by a DH layer it produces the next layer's H_in basis (m = that
+ * layer's H_in order); m = 1 is no transform (DH followed by WH). H (H_in,
+ * H_out) is the normalised Sylvester matrix over contiguous blocks. s_w,c:
+ * per-output-channel scale of W-bar (8-bit symmetric codes); s_y: the scale
+ * of the output codes (the next layer's input scale). n: the largest shift
+ * <= 48 with every M_c <= 32767. round() is round half to even; bias codes
+ * saturate at +-2^27, so every intermediate stays below 2^51 in magnitude.
+ * Every online step is exact integer arithmetic (int32 products; after M the
+ * kernel carries the integers in float64 registers, exact in that range).
  */
-typedef struct {
-  int32_t d_in;     /* input channels: same rule as hq_desc.d_in                */
-  int32_t d_out;    /* output channels: multiple of 8                           */
-  int32_t block;    /* m: power of two <= 256 dividing d_out                    */
-  int32_t w_dtype;  /* hq_dtype of weight                                       */
-} hq_wh_desc;
+typedef enum { HQ_INT_WH = 0, HQ_INT_DH = 1 } hq_int_side;
 
-/* Byte offsets of the arrays in a WH prepared blob (256-byte aligned). */
+typedef struct {
+  int32_t d_in;     /* input channels: same rule as hq_desc.d_in                  */
+  int32_t d_out;    /* output channels: multiple of 8                             */
+  int32_t block;    /* m: output-side transform order, power of two <= 256
+                       dividing d_out (for WH also the order of H_out)            */
+  int32_t w_dtype;  /* hq_dtype of weight                                         */
+  int32_t side;     /* hq_int_side                                                */
+  int32_t in_block; /* DH: order of H_in, a power of two dividing d_in; WH: 1     */
+} hq_int_desc;
+
+/* Byte offsets of the arrays in an integer-layer prepared blob (256-byte aligned). */
 typedef struct {
   size_t total;
   size_t w_codes;   /* int8  [d_out_pad, d_in]  codes of W-bar (padding rows 0)  */
@@ -310,34 +321,35 @@ typedef struct {
   size_t shift;     /* int32 [1]                shared shift n                  */
   size_t wbar;      /* f32   [d_out, d_in]      W-bar (written by the prepare)  */
   int64_t d_out_pad;
-} hq_wh_layout;
+} hq_int_layout;
 
-/* Host-only: validation, blob size and layout, workspace of hq_wh_linear
+/* Host-only: validation, blob size and layout, workspace of hq_int_linear
  * (int32 products [T, d_out]). */
-int hq_wh_validate(const hq_wh_desc* desc);
-size_t hq_wh_prepared_bytes(const hq_wh_desc* desc);
-int hq_wh_prepared_layout_of(const hq_wh_desc* desc, hq_wh_layout* out);
-size_t hq_wh_workspace_bytes(const hq_wh_desc* desc, int64_t T);
+int hq_int_validate(const hq_int_desc* desc);
+size_t hq_int_prepared_bytes(const hq_int_desc* desc);
+int hq_int_prepared_layout_of(const hq_int_desc* desc, hq_int_layout* out);
+size_t hq_int_workspace_bytes(const hq_int_desc* desc, int64_t T);
 
 /* Offline: weight [d_out, d_in] (w_dtype) and bias f32 [d_out] (or NULL) into
- * the blob (hq_wh_prepared_bytes): W-bar, its int8 codes and scales, the bias
+ * the blob (hq_int_prepared_bytes): W-bar, its int8 codes and scales, the bias
  * codes, the multipliers and the shift. s_x > 0 is the scale of the int8
  * input, s_y > 0 that of the int8 output. */
-int hq_wh_prepare(const hq_wh_desc* desc, const void* weight, const float* bias, float s_x,
-                  float s_y, void* prepared, void* stream);
+int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bias, float s_x,
+                   float s_y, void* prepared, void* stream);
 
-/* The WH hot path: y_codes int8 [T, d_out] from x_codes int8 [T, d_in]
- * (codes in [-127, 127]; row-major): the int8 MFMA product into the
- * workspace, then hq_wh_requant's kernel. T = 0 is a no-op. */
-int hq_wh_linear(const hq_wh_desc* desc, const void* prepared, const int8_t* x_codes, int64_t T,
-                 int8_t* y_codes, void* workspace, size_t workspace_bytes, void* stream);
+/* The hot path: y_codes int8 [T, d_out] from x_codes int8 [T, d_in] (codes in
+ * [-127, 127], row-major, in the layer's input basis): the int8 MFMA product
+ * into the workspace, then hq_int_requant's kernel. T = 0 is a no-op. */
+int hq_int_linear(const hq_int_desc* desc, const void* prepared, const int8_t* x_codes,
+                  int64_t T, int8_t* y_codes, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /* Requantisation alone: y_codes int8 [T, d_out] from the int32 products
  * acc [T, d_out] (x_int . w-bar_int^T, WITHOUT the bias codes, which this
  * stage adds). |acc| <= 2^27 (as every product of int8 codes over d_in <= 8192
  * is); larger values are outside the exact range of the kernel. */
-int hq_wh_requant(const hq_wh_desc* desc, const void* prepared, const int32_t* acc, int64_t T,
-                  int8_t* y_codes, void* stream);
+int hq_int_requant(const hq_int_desc* desc, const void* prepared, const int32_t* acc, int64_t T,
+                   int8_t* y_codes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -347,20 +347,27 @@ def run(x, weight, bias, *, block: int, a_bits: int, w_bits: int, center,
 # --------------------------------------------------------------------------
 # Diagnostics (not parity gates)
 # --------------------------------------------------------------------------
-# Weight-only Hadamard layer with integer requantisation
+# Integer-only DH and WH layers with integer requantisation
 # --------------------------------------------------------------------------
 #
-# HaTQ Sec. IV-B: the weight is transformed along its output channels,
-# W-bar = H_out W (supplement Eq. (40), T_out = H_out symmetric, so
-# (T_out)^T W = H_out W and b-bar = b H_out), the activation stays in its
-# original basis with one static per-tensor scale, and the int8 product is
-# mapped back to the original basis and onto the next layer's int8 grid with
-# integers only (Eq. (19)-(22) with the identity activation, a WH layer
-# followed by a WH layer: H_out before phi, no input transform after it,
-# gamma = sqrt(m_out)). Readings taken where the pages leave a step open:
-# * H_out is the normalised Sylvester matrix of order m (a power of two
-#   dividing d_out), block-diagonal over d_out / m blocks of output channels;
-#   m = d_out is the pages' full transform.
+# HaTQ Sec. IV-B. A weight-only Hadamard (WH) layer transforms the weight
+# along its output channels, W-bar = H_out W (supplement Eq. (40): T_out =
+# H_out is symmetric, so (T_out)^T W = H_out W, and b-bar = b H_out); its
+# activation stays in the original basis. A double-Hadamard (DH) layer
+# transforms the weight along its input channels, W-bar = W H_in (Eq. (13)),
+# keeps b-bar = b (supplement Sec. VIII-B), and receives its activation
+# already in the H_in basis. Either way the int8 product is moved onto the
+# next layer's int8 grid with integers only (Eq. (19)-(22) with the identity
+# activation): one unnormalised transform of order m over the output
+# channels with gamma = sqrt(m), which for a WH layer followed by a WH layer
+# restores the original basis (Table I, WH-to-WH), for a DH layer followed by
+# a DH layer produces the next layer's H_in basis (DH-to-DH), and with m = 1
+# is no transform (DH-to-WH). Readings taken where the pages leave a step
+# open:
+# * H is the normalised Sylvester matrix of the stated order (a power of two
+#   dividing the channel count), block-diagonal over contiguous blocks; the
+#   full order is the pages' transform. WH-to-DH (two transforms around the
+#   activation) and padded or Paley orders are not built.
 # * M_c = round(2^n rho_c) with one shared shift n: the largest n in [0, 48]
 #   for which every M_c fits a positive 16-bit integer (<= 32767), the
 #   multiplier-precision constraint of Eq. (19); n = 0 when every rho_c is 0.
@@ -408,21 +415,37 @@ def unnormalised_transform(u, block: int) -> np.ndarray:
     return (u.reshape(t, d // block, block) @ h).reshape(t, d)
 
 
-def wh_prepare(weight, bias, s_x: float, s_y: float, block: int, w_bits: int = 8):
-    """Offline half of a WH layer (HaTQ Eq. (15)-(19), supplement Eq. (40)-(44)).
+SIDE_WH, SIDE_DH = 0, 1
+
+
+def int_prepare(weight, bias, s_x: float, s_y: float, block: int, side: int = SIDE_WH,
+                in_block: int = 1, w_bits: int = 8):
+    """Offline half of an integer-only layer (HaTQ Eq. (13)-(19), supplement
+    Eq. (40)-(44)).
 
     weight [d_out, d_in] (row c = output channel c), bias [d_out], s_x the
     static scale of the int8 input, s_y the scale of the int8 output (the
-    next layer's input scale), block = m, the order of H_out.
+    next layer's input scale), block = m, the order of the output-side
+    integer transform (for WH also the order of H_out on the weight), side
+    SIDE_WH or SIDE_DH, in_block the order of H_in on a DH weight.
     Returns W-bar, b-bar, the weight codes and scales, the bias codes
     b_int = round(b-bar / (s_x s_w)), rho, the shift n and the multipliers M."""
     weight = np.asarray(weight, dtype=np.float64)
-    d_out = weight.shape[0]
+    d_out, d_in = weight.shape
     if d_out % block:
         raise ValueError("block must divide d_out")
-    # H_out acts on the output-channel index: column-wise on weight, row-wise on b
-    wbar = rotate(weight.T, block).T
-    bbar = rotate(np.asarray(bias, dtype=np.float64)[None, :], block)[0]
+    bias = np.asarray(bias, dtype=np.float64)
+    if side == SIDE_WH:
+        # H_out acts on the output-channel index: column-wise on weight, row-wise on b
+        wbar = rotate(weight.T, block).T
+        bbar = rotate(bias[None, :], block)[0]
+    elif side == SIDE_DH:
+        if d_in % in_block:
+            raise ValueError("in_block must divide d_in")
+        wbar = rotate(weight, in_block)
+        bbar = bias.copy()
+    else:
+        raise ValueError(f"side must be SIDE_WH or SIDE_DH, got {side}")
     qw, s_w = quantize_rows(wbar, w_bits)
     s_a = float(s_x) * s_w
     b_int = np.zeros(d_out, dtype=np.int64)
@@ -432,13 +455,16 @@ def wh_prepare(weight, bias, s_x: float, s_y: float, block: int, w_bits: int = 8
     n = requant_shift(rho)
     m_c = np.rint(rho * 2.0 ** n).astype(np.int64)
     return {"wbar": wbar, "bbar": bbar, "qw": qw, "s_w": s_w, "b_int": b_int, "rho": rho,
-            "shift": n, "mult": m_c, "block": block, "s_x": float(s_x), "s_y": float(s_y)}
+            "shift": n, "mult": m_c, "block": block, "side": side, "in_block": in_block,
+            "s_x": float(s_x), "s_y": float(s_y)}
 
 
-def wh_forward_int(x_int, prep, bits: int = 8) -> dict:
-    """Online integer path of a WH layer: a = x_int w-bar_int^T + b_int (Eq. (4)),
-    v = H~_out (M . a) (Eq. (20)), y_int = clamp(round(v / 2^n), +-qmax) (Eq. (22)
-    with the identity activation and no input-side transform)."""
+def int_forward(x_int, prep, bits: int = 8) -> dict:
+    """Online integer path: a = x_int w-bar_int^T + b_int (Eq. (4)),
+    v = H~_m (M . a) (Eq. (20), Eq. (22)'s transform for DH-to-DH),
+    y_int = clamp(round(v / 2^n), +-qmax) (Eq. (22), identity activation).
+    x_int is the int8 input in the layer's own basis (the original one for
+    WH, the H_in basis for DH)."""
     qmax = 2 ** (bits - 1) - 1
     a = int_gemm(x_int, prep["qw"]) + prep["b_int"][None, :]
     u = a * prep["mult"][None, :]
@@ -447,9 +473,11 @@ def wh_forward_int(x_int, prep, bits: int = 8) -> dict:
     return {"acc": a, "u": u, "v": v, "y_int": y.astype(np.int16)}
 
 
-def wh_dequant_reference(x_int, prep) -> np.ndarray:
-    """The dequantised WH output of Eq. (17) with the bias codes, in the
-    original basis and in units of s_y: (s_A . a) H_out / s_y (float64)."""
+def int_dequant_reference(x_int, prep) -> np.ndarray:
+    """The dequantised output with the bias codes, moved by the normalised
+    output-side transform and in units of s_y: (s_A . a) H_m / s_y (float64).
+    For WH this is Eq. (17) in the original basis; for DH the output of
+    Eq. (14) in the next layer's H_in basis."""
     a = int_gemm(x_int, prep["qw"]) + prep["b_int"][None, :]
     ya = a.astype(np.float64) * (prep["s_x"] * prep["s_w"])[None, :]
     return rotate(ya, prep["block"]) / prep["s_y"]

@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lib.hq_abi_version() == 6
+    assert lib.hq_abi_version() == 7
     assert lib.hq_status_str(0) == b"HQ_OK"
     assert lib.hq_status_str(-3) == b"HQ_ERR_WORKSPACE"
     assert lib.hq_status_str(99) == b"HQ_ERR_UNKNOWN"
@@ -201,53 +201,61 @@ def test_error_string_is_thread_local():
     assert b"a_bits" in lib.hq_last_error()
 
 
-# ---- weight-only Hadamard layer (host-side checks only)
+# ---- integer-only DH / WH layers (host-side checks only)
 
-def _wh(**kw):
-    from hadamard_rotated_bit_amd import WhDesc
+def _il(**kw):
+    from hadamard_rotated_bit_amd import IntDesc
     base = dict(d_in=256, d_out=256, block=256, w_dtype=F32)
     base.update(kw)
-    return WhDesc(**base)
+    return IntDesc(**base)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(d_in=0), -1), (dict(d_out=-8), -1), (dict(w_dtype=4), -1), (dict(d_in=100), -2),
     (dict(d_out=260), -2), (dict(block=3), -2), (dict(block=512, d_out=512), -2),
-    (dict(block=128, d_out=200), -2), (dict(block=0), -2),
+    (dict(block=128, d_out=200), -2), (dict(block=0), -2), (dict(side=2), -1),
+    (dict(side=-1), -1), (dict(in_block=2), -2), (dict(side=1, in_block=3), -2),
+    (dict(side=1, in_block=512), -2), (dict(side=1, in_block=0), -2),
 ])
-def test_wh_validation_rejects(kw, status):
-    d = _wh(**kw)
-    assert lib.hq_wh_validate(d._ref) == status
+def test_int_validation_rejects(kw, status):
+    d = _il(**kw)
+    assert lib.hq_int_validate(d._ref) == status
     assert len(lib.hq_last_error()) > 0
-    assert lib.hq_wh_prepared_bytes(d._ref) == 0
-    assert lib.hq_wh_workspace_bytes(d._ref, 16) == 0
+    assert lib.hq_int_prepared_bytes(d._ref) == 0
+    assert lib.hq_int_workspace_bytes(d._ref, 16) == 0
 
 
-def test_wh_layout_and_workspace():
-    d = _wh(d_in=384, d_out=136, block=8)
-    assert lib.hq_wh_validate(d._ref) == 0
-    L = _lib.HqWhLayout()
-    assert lib.hq_wh_prepared_layout_of(d._ref, ctypes.byref(L)) == 0
+@pytest.mark.parametrize("kw", [dict(), dict(side=1, in_block=256), dict(side=1, in_block=1, block=1),
+                                dict(side=1, in_block=32, block=8, d_out=136)])
+def test_int_validation_accepts(kw):
+    assert lib.hq_int_validate(_il(**kw)._ref) == 0
+
+
+def test_int_layout_and_workspace():
+    d = _il(d_in=384, d_out=136, block=8)
+    assert lib.hq_int_validate(d._ref) == 0
+    L = _lib.HqIntLayout()
+    assert lib.hq_int_prepared_layout_of(d._ref, ctypes.byref(L)) == 0
     assert L.d_out_pad == 256
     offs = [L.w_codes, L.w_scale, L.b_int, L.mult, L.shift, L.wbar, L.total]
     assert all(o % 256 == 0 for o in offs[:-1]) and offs == sorted(offs)
     assert L.w_scale - L.w_codes >= 256 * 384 and L.total - L.wbar >= 4 * 136 * 384
     assert L.b_int - L.w_scale >= 4 * 256 and L.mult - L.b_int >= 4 * 256
-    assert lib.hq_wh_prepared_bytes(d._ref) == L.total
-    assert lib.hq_wh_workspace_bytes(d._ref, 1000) == 4 * 1000 * 136
-    assert lib.hq_wh_workspace_bytes(d._ref, -1) == 0
+    assert lib.hq_int_prepared_bytes(d._ref) == L.total
+    assert lib.hq_int_workspace_bytes(d._ref, 1000) == 4 * 1000 * 136
+    assert lib.hq_int_workspace_bytes(d._ref, -1) == 0
 
 
-def test_wh_entry_points_reject_before_launch():
-    d = _wh()._ref
+def test_int_entry_points_reject_before_launch():
+    d = _il()._ref
     p = ctypes.c_void_p(0x1000)   # never dereferenced: every call fails validation first
-    assert lib.hq_wh_prepare(d, None, None, ctypes.c_float(1.0), ctypes.c_float(1.0), p, None) == -1
-    assert lib.hq_wh_prepare(d, p, None, ctypes.c_float(0.0), ctypes.c_float(1.0), p, None) == -1
-    assert lib.hq_wh_prepare(d, p, None, ctypes.c_float(1.0), ctypes.c_float(float("nan")), p,
-                             None) == -1
-    assert lib.hq_wh_linear(d, p, p, -1, p, p, 1 << 30, None) == -1
-    assert lib.hq_wh_linear(d, p, p, 16, p, p, 10, None) == -3
-    assert lib.hq_wh_linear(d, p, p, 0, None, None, 0, None) == 0
-    assert lib.hq_wh_linear(d, None, p, 16, p, p, 1 << 30, None) == -1
-    assert lib.hq_wh_requant(d, p, None, 16, p, None) == -1
-    assert lib.hq_wh_requant(d, p, ctypes.c_void_p(0x1001), 16, p, None) == -1   # misaligned
+    assert lib.hq_int_prepare(d, None, None, ctypes.c_float(1.0), ctypes.c_float(1.0), p, None) == -1
+    assert lib.hq_int_prepare(d, p, None, ctypes.c_float(0.0), ctypes.c_float(1.0), p, None) == -1
+    assert lib.hq_int_prepare(d, p, None, ctypes.c_float(1.0), ctypes.c_float(float("nan")), p,
+                              None) == -1
+    assert lib.hq_int_linear(d, p, p, -1, p, p, 1 << 30, None) == -1
+    assert lib.hq_int_linear(d, p, p, 16, p, p, 10, None) == -3
+    assert lib.hq_int_linear(d, p, p, 0, None, None, 0, None) == 0
+    assert lib.hq_int_linear(d, None, p, 16, p, p, 1 << 30, None) == -1
+    assert lib.hq_int_requant(d, p, None, 16, p, None) == -1
+    assert lib.hq_int_requant(d, p, ctypes.c_void_p(0x1001), 16, p, None) == -1   # misaligned

@@ -494,7 +494,7 @@ def test_wh_weight_transform_and_identity(m):
     # W-bar = H_out W and b-bar = b H_out (supplement Eq. (40)) from a
     # scipy-built H; the float WH identity Eq. (41): (X W-bar^T + b-bar) H_out^T = X W^T + b
     x, weight, bias, s_x, s_y = _wh_inputs()
-    p = O.wh_prepare(weight, bias, s_x, s_y, m)
+    p = O.int_prepare(weight, bias, s_x, s_y, m)
     h = _block_h(weight.shape[0], m)
     np.testing.assert_allclose(p["wbar"], h @ weight, atol=1e-14)
     np.testing.assert_allclose(p["bbar"], bias @ h, atol=1e-14)
@@ -541,10 +541,10 @@ def test_wh_integer_path_within_its_rounding_bound(m):
     # output in units of s_y, H~(rho . a): they differ by the final rounding
     # (1/2) plus the multiplier rounding |M - 2^n rho| <= 1/2 on each channel.
     x, weight, bias, s_x, s_y = _wh_inputs()
-    p = O.wh_prepare(weight, bias, s_x, s_y, m)
+    p = O.int_prepare(weight, bias, s_x, s_y, m)
     xi = O.quantize_static(x, s_x)
-    r = O.wh_forward_int(xi, p)
-    ref = O.wh_dequant_reference(xi, p)
+    r = O.int_forward(xi, p)
+    ref = O.int_dequant_reference(xi, p)
     a = np.abs(r["acc"]).astype(np.float64)
     bound = 0.5 + 0.5 * (a.reshape(a.shape[0], -1, m).sum(axis=2).repeat(m, axis=1)) / 2.0 ** p["shift"]
     assert np.all(np.abs(r["y_int"] - np.clip(ref, -127, 127)) <= bound + 1e-9)
@@ -558,8 +558,8 @@ def test_wh_bias_only_passes_back_to_original_basis():
     # and H_out brings it back)
     x, weight, bias, s_x, s_y = _wh_inputs()
     m = 16
-    p = O.wh_prepare(weight, bias, s_x, s_y, m)
-    r = O.wh_forward_int(np.zeros((1, weight.shape[1]), dtype=np.int16), p)
+    p = O.int_prepare(weight, bias, s_x, s_y, m)
+    r = O.int_forward(np.zeros((1, weight.shape[1]), dtype=np.int16), p)
     err_b = np.abs(p["b_int"] - p["bbar"] / (s_x * p["s_w"]))          # <= 1/2 each
     assert err_b.max() <= 0.5 + 1e-9
     # H~(rho . b-bar / s_A) = H b-bar / s_y = b / s_y; the bias rounding adds at most
@@ -572,11 +572,11 @@ def test_wh_bias_only_passes_back_to_original_basis():
 def test_wh_hand_example():
     g = load_golden("wh_requant_example.txt")
     weight = g["weight"].reshape(2, 1)
-    p = O.wh_prepare(weight, g["bias"], g["s_x"].item(), g["s_y"].item(), int(g["block"].item()))
+    p = O.int_prepare(weight, g["bias"], g["s_x"].item(), g["s_y"].item(), int(g["block"].item()))
     assert p["qw"].ravel().tolist() == g["codes"].ravel().tolist()
     assert p["shift"] == int(g["shift"].item())
     assert p["mult"].tolist() == g["mult"].astype(int).tolist()
-    r = O.wh_forward_int(np.array([[int(g["x_int"].item())]]), p)
+    r = O.int_forward(np.array([[int(g["x_int"].item())]]), p)
     assert r["v"][0].tolist() == g["v"].astype(int).tolist()
     assert r["y_int"][0].tolist() == g["y_int"].astype(int).tolist()
 
@@ -584,6 +584,87 @@ def test_wh_hand_example():
 def test_wh_rejects_bad_block():
     x, weight, bias, s_x, s_y = _wh_inputs()
     with pytest.raises(ValueError):
-        O.wh_prepare(weight, bias, s_x, s_y, 3)
+        O.int_prepare(weight, bias, s_x, s_y, 3)
     with pytest.raises(ValueError):
-        O.wh_prepare(weight, bias, s_x, s_y, 128)
+        O.int_prepare(weight, bias, s_x, s_y, 128)
+
+
+@pytest.mark.parametrize("k", [1, 4, 32])
+def test_dh_weight_transform_and_identity(k):
+    # DH: W-bar = W H_in over blocks of k input channels (scipy-built H), b-bar = b,
+    # and the float identity of Eq. (13): (X H_in)(W H_in)^T + b = X W^T + b
+    x, weight, bias, s_x, s_y = _wh_inputs()
+    p = O.int_prepare(weight, bias, s_x, s_y, 1, side=O.SIDE_DH, in_block=k)
+    h = _block_h(weight.shape[1], k)
+    np.testing.assert_allclose(p["wbar"], weight @ h, atol=1e-14)
+    np.testing.assert_array_equal(p["bbar"], bias)
+    np.testing.assert_allclose((x @ h) @ p["wbar"].T + p["bbar"], x @ weight.T + bias, atol=1e-12)
+
+
+@pytest.mark.parametrize("k,m", [(1, 1), (32, 1), (32, 16), (4, 64)])
+def test_dh_integer_path_within_its_rounding_bound(k, m):
+    # the DH layer's input arrives in its H_in basis; its output is moved into
+    # the next layer's basis by the order-m transform (DH-to-DH; m = 1: DH-to-WH)
+    x, weight, bias, _, _ = _wh_inputs()
+    xh = O.rotate(x, k)
+    s_x = np.abs(xh).max() / 127
+    yh = O.rotate(x @ weight.T + bias, m)
+    s_y = np.abs(yh).max() / 127
+    p = O.int_prepare(weight, bias, s_x, s_y, m, side=O.SIDE_DH, in_block=k)
+    xi = O.quantize_static(xh, s_x)
+    r = O.int_forward(xi, p)
+    ref = O.int_dequant_reference(xi, p)
+    a = np.abs(r["acc"]).astype(np.float64)
+    bound = 0.5 + 0.5 * (a.reshape(a.shape[0], -1, m).sum(axis=2).repeat(m, axis=1)) / 2.0 ** p["shift"]
+    assert np.all(np.abs(r["y_int"] - np.clip(ref, -127, 127)) <= bound + 1e-9)
+    # the codes stand for the float layer's output in the next layer's basis
+    assert O.sqnr_db(yh / s_y, r["y_int"].astype(np.float64)) > 25
+
+
+def _two_layers(seed=9, T=48, d0=64, d1=128, d2=64):
+    rng = np.random.default_rng(seed)
+    x = rng.laplace(0.0, 1.0, (T, d0))
+    w1, b1 = rng.normal(0, 0.1, (d1, d0)), rng.normal(0, 0.05, d1)
+    w2, b2 = rng.normal(0, 0.1, (d2, d1)), rng.normal(0, 0.05, d2)
+    y1 = x @ w1.T + b1
+    y2 = y1 @ w2.T + b2
+    return x, w1, b1, w2, b2, y1, y2
+
+
+def test_two_wh_layers_chain():
+    # WH -> WH with the identity activation (Table I, WH-to-WH): each layer's
+    # int8 output is the next one's input, in the original basis
+    x, w1, b1, w2, b2, y1, y2 = _two_layers()
+    s0, s1, s2 = (np.abs(v).max() / 127 for v in (x, y1, y2))
+    p1 = O.int_prepare(w1, b1, s0, s1, 128, side=O.SIDE_WH)
+    p2 = O.int_prepare(w2, b2, s1, s2, 64, side=O.SIDE_WH)
+    q1 = O.int_forward(O.quantize_static(x, s0), p1)["y_int"]
+    q2 = O.int_forward(q1, p2)["y_int"]
+    assert O.sqnr_db(y1 / s1, q1.astype(np.float64)) > 25
+    assert O.sqnr_db(y2 / s2, q2.astype(np.float64)) > 22
+
+
+def test_two_dh_layers_chain():
+    # DH -> DH -> (WH): layer 1 takes x in its H_32 basis and hands its output
+    # over in layer 2's H_128 basis (Table I, DH-to-DH: the input-side transform
+    # of the next layer, gamma = sqrt(128)); layer 2 ends in the original basis
+    # (m = 1, DH-to-WH)
+    x, w1, b1, w2, b2, y1, y2 = _two_layers()
+    xh = O.rotate(x, 32)
+    s0 = np.abs(xh).max() / 127
+    s1 = np.abs(O.rotate(y1, 128)).max() / 127
+    s2 = np.abs(y2).max() / 127
+    p1 = O.int_prepare(w1, b1, s0, s1, 128, side=O.SIDE_DH, in_block=32)
+    p2 = O.int_prepare(w2, b2, s1, s2, 1, side=O.SIDE_DH, in_block=128)
+    q1 = O.int_forward(O.quantize_static(xh, s0), p1)["y_int"]
+    q2 = O.int_forward(q1, p2)["y_int"]
+    assert O.sqnr_db(O.rotate(y1, 128) / s1, q1.astype(np.float64)) > 25
+    assert O.sqnr_db(y2 / s2, q2.astype(np.float64)) > 22
+
+
+def test_int_prepare_rejects_bad_side_and_block():
+    x, weight, bias, s_x, s_y = _wh_inputs()
+    with pytest.raises(ValueError):
+        O.int_prepare(weight, bias, s_x, s_y, 1, side=2)
+    with pytest.raises(ValueError):
+        O.int_prepare(weight, bias, s_x, s_y, 1, side=O.SIDE_DH, in_block=64)   # 96 % 64
