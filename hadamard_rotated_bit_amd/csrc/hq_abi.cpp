@@ -450,11 +450,12 @@ int hq_prepare_weights(const hq_desc* desc, const void* weight, const float* bia
   layout_of(desc, &L);
   const int64_t np = L.d_out_pad, dout = desc->d_out, din = desc->d_in;
   hipError_t e = hipSuccess;
-  // Padding rows of the code matrix and of the per-channel vectors are zero
-  // (d_out is a multiple of 8, so E2M3 row groups are never split).
+  // Padding rows of the code matrix and of the per-channel vectors are zero.
+  // E2M3 rows past d_out can share a row group with real rows (their bytes
+  // interleave slice by slice), so the whole code matrix is cleared first.
   const int fmt = code_fmt_of(desc);
   if (np > dout) {
-    const size_t used = hq::code_bytes(fmt, dout, int(din));
+    const size_t used = fmt == hq::CODES_E2M3 ? 0 : hq::code_bytes(fmt, dout, int(din));
     e = hq::launch_fill_u8(at<uint8_t>(prepared, L.w_codes + used), 0,
                            hq::code_bytes(fmt, np, int(din)) - used, s);
   }

@@ -40,13 +40,13 @@ bool row_geometry(int d, RowGeom* g) {
 
 // Writes the lane's C chunks of codes (chunk c = channels c 8G + 8t .. +7) in
 // the launch's code format: int8 bytes at row * d + channel, or E2M3 pieces
-// in the 4-row-group layout.
+// in the row-group layout.
 template <int G, int C>
 __device__ __forceinline__ void store_codes(const RowArgs& a, int64_t row, int64_t base, int t,
                                             const float* v, float rcp) {
   if (a.code_fmt == CODES_E2M3) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) store_e2m3x8(a.codes, row, a.d, c * 8 * G + t * 8, &v[c * 8], rcp);
+    for (int c = 0; c < C; ++c) store_e2m3x8<F6_GROUP>(a.codes, row, a.d, c * 8 * G + t * 8, &v[c * 8], rcp);
   } else {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -93,7 +93,7 @@ __device__ __forceinline__ void store_group_codes(const RowArgs& a, int64_t row,
   if (!valid) return;
   if (a.code_fmt == CODES_E2M3) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) store_e2m3x8(a.codes, row, a.d, c * 8 * G + t * 8, &v[c * 8], rc[c]);
+    for (int c = 0; c < C; ++c) store_e2m3x8<F6_GROUP>(a.codes, row, a.d, c * 8 * G + t * 8, &v[c * 8], rc[c]);
   } else {
 #pragma unroll
     for (int c = 0; c < C; ++c) {

@@ -73,17 +73,26 @@ __device__ __forceinline__ uint32_t pack6x4(uint32_t x) {
   const uint32_t y = (x & 0x003F003Fu) | ((x >> 2) & 0x0FC00FC0u);
   return (y & 0xFFFu) | ((y >> 4) & 0xFFF000u);
 }
+// Byte offset of the 6-byte piece holding channels e0 .. e0+7 (e0 a
+// multiple of 8) of `row` in the E2M3 layout of a d-channel code matrix with
+// R-row groups: (row / R) 3 R d / 4 + (e0 / 128) 96 R + (row % R) 96 +
+// 6 ((e0 % 128) / 8).
+template <int R>
+__device__ __forceinline__ int64_t e2m3_piece_offset(int64_t row, int d, int e0) {
+  return (row / R) * (int64_t(R) * 3 / 4) * int64_t(d) + (e0 >> 7) * (96 * R) + (row % R) * 96 +
+         6 * ((e0 & 127) >> 3);
+}
+
 // Stores the E2M3 codes of the 8 values v (channels e0 .. e0+7 of `row`,
-// e0 a multiple of 8) in the 4-row-group layout of a d-channel code matrix:
-// a 6-byte piece at (row/4) 3d + (e0/128) 384 + (row%4) 96 + 6 ((e0%128)/8),
-// written as a dword and a short at their natural alignment.
+// e0 a multiple of 8) at their piece of the R-row-group layout, written as a
+// dword and a short at their natural alignment.
+template <int R>
 __device__ __forceinline__ void store_e2m3x8(uint8_t* __restrict__ codes, int64_t row, int d,
                                              int e0, const float* v, float rcp) {
   const uint32_t p0 = pack6x4(e2m3_codes4(v[0], v[1], v[2], v[3], rcp));
   const uint32_t p1 = pack6x4(e2m3_codes4(v[4], v[5], v[6], v[7], rcp));
   const uint32_t w0 = p0 | (p1 << 24), w1 = p1 >> 8;  // 48-bit piece
-  uint8_t* p = codes + (row >> 2) * 3 * int64_t(d) + (e0 >> 7) * 384 + (row & 3) * 96 +
-               6 * ((e0 & 127) >> 3);
+  uint8_t* p = codes + e2m3_piece_offset<R>(row, d, e0);
   const bool odd = e0 & 8;  // odd pieces start 2 bytes past a dword boundary
   *reinterpret_cast<uint32_t*>(p + (odd ? 2 : 0)) = odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0;
   *reinterpret_cast<uint16_t*>(p + (odd ? 0 : 4)) = uint16_t(odd ? w0 : w1);

@@ -7,6 +7,8 @@
 namespace hq {
 
 // Rows per group of the E2M3 code layout (see CodeFmt in hq_internal.h).
+// 32-row groups (each 1-KB stage load of the FP6 GEMM reading one contiguous
+// range) measured no faster than 4-row groups.
 constexpr int F6_GROUP = 4;
 
 // Dequant epilogue of the GEMMs: y = s_x s_w acc + b + mu c (+ U L2), stored

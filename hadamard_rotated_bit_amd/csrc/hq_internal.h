@@ -24,11 +24,13 @@ bool row_geometry(int d_in, RowGeom* g);
 enum RowMode { ROW_ACT = 0, ROW_WEIGHT = 1, ROW_EXPORT = 2 };
 
 // Code storage (the C ABI's hq_code_format_t): int8 bytes, or E2M3 fp6 in
-// 4-row groups (group g of rows at 3 d g bytes; 128-code slice s of row
-// 4g + i at byte 384 s + 96 i inside it; code k of the slice at bits 6k).
+// groups of R = F6_GROUP rows (group g of rows at 3 R d g / 4 bytes; 128-code
+// slice s of row R g + i at byte 96 R s + 96 i inside it; code k of the
+// slice at bits 6k).
 enum CodeFmt { CODES_I8 = 0, CODES_E2M3 = 1 };
 inline size_t code_bytes(int fmt, int64_t rows, int d) {
-  if (fmt == CODES_E2M3) return size_t((rows + F6_GROUP - 1) / F6_GROUP) * 3 * size_t(d);
+  if (fmt == CODES_E2M3)
+    return size_t((rows + F6_GROUP - 1) / F6_GROUP) * (size_t(F6_GROUP) * 3 / 4) * size_t(d);
   return size_t(rows) * size_t(d);
 }
 
@@ -102,7 +104,7 @@ hipError_t launch_bias_gemv(const void* weight, int w_bf16, const float* mean, c
 hipError_t launch_gemm(const int8_t* A, int64_t M, const int8_t* B, int64_t N, int K,
                        int32_t* acc_out, int64_t ldc, const GemmEpi* epi, hipStream_t s);
 // The same product on E2M3 codes (CODES_E2M3 layout, M and N rows; K a
-// multiple of 128) with the FP6 MFMA; rows past M / N in their last 4-row
+// multiple of 128) with the FP6 MFMA; rows past M / N in their last row
 // group must be readable (their results are discarded).
 // Group-wise FP6 GEMM with the dequant epilogue: 64-code groups, s_xg [K/64,
 // ld_sx] and s_wg [K/64, ld_sw] one scale per row / column and group; the

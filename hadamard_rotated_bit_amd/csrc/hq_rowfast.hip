@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
   if (a.code_fmt == CODES_E2M3) {
     constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
     const bool odd = t & 1;
-    uint8_t* rb = a.codes + (row >> 2) * 3 * int64_t(d) + (row & 3) * 96;
+    uint8_t* rb = a.codes + e2m3_piece_offset<F6_GROUP>(row, d, 0);
 #pragma unroll
     for (int c0 = 0; c0 < C; c0 += 4) {
       v16f x, y;
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
       for (int m = 0; m < 4; ++m) {
         if (c0 + m >= C) break;
         const int e0 = (c0 + m) * 8 * G + t * 8;
-        uint8_t* dst = rb + (e0 >> 7) * 384 + 6 * ((e0 & 127) >> 3);
+        uint8_t* dst = rb + (e0 >> 7) * (96 * F6_GROUP) + 6 * ((e0 & 127) >> 3);
         uint32_t w0, w1;
         if (m == 0) { w0 = p[0]; w1 = p[1] & 0xFFFFu; }
         else if (m == 1) { w0 = __builtin_amdgcn_alignbit(p[2], p[1], 16); w1 = p[2] >> 16; }

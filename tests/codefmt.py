@@ -14,6 +14,7 @@ is an integer in [-7, 7]; it shares nothing with the library's encoder.
 import numpy as np
 
 I8, E2M3 = 0, 1
+RG = 4            # rows per E2M3 row group
 
 
 def fmt_of(a_bits: int, w_bits: int, gemm: int = 0) -> int:
@@ -22,7 +23,7 @@ def fmt_of(a_bits: int, w_bits: int, gemm: int = 0) -> int:
 
 def nbytes(fmt: int, rows: int, d: int) -> int:
     if fmt == E2M3:
-        return (rows + 3) // 4 * 3 * d
+        return (rows + RG - 1) // RG * (RG * 3 // 4) * d
     return rows * d
 
 
@@ -56,7 +57,8 @@ def decode(fmt: int, buf, rows: int, d: int, idx=None) -> np.ndarray:
     if fmt == I8:
         return raw[:rows * d].view(np.int8).reshape(rows, d)[idx].astype(np.int64)
     S = d // 128
-    base = (idx // 4)[:, None] * (3 * d) + np.arange(S)[None, :] * 384 + (idx % 4)[:, None] * 96
+    base = ((idx // RG)[:, None] * (RG * 3 // 4 * d) + np.arange(S)[None, :] * (96 * RG)
+            + (idx % RG)[:, None] * 96)
     seg = raw[base[..., None] + np.arange(96)]                        # [n, S, 96]
     bits = np.unpackbits(seg, axis=-1, bitorder="little").reshape(idx.size, S, 128, 6)
     pat = (bits.astype(np.int64) << np.arange(6)).sum(axis=-1)       # [n, S, 128]
@@ -72,16 +74,17 @@ def encode(fmt: int, codes: np.ndarray) -> np.ndarray:
     rows, d = codes.shape
     if fmt == I8:
         return codes.astype(np.int8).view(np.uint8).reshape(-1).copy()
-    groups = (rows + 3) // 4
-    out = np.empty(groups * 3 * d, dtype=np.uint8)
+    groups = (rows + RG - 1) // RG
+    gb = RG * 3 // 4 * d                             # bytes per group
+    out = np.empty(groups * gb, dtype=np.uint8)
     step = 256                                       # groups per chunk (bounded memory)
     for g0 in range(0, groups, step):
         g1 = min(groups, g0 + step)
-        full = np.zeros(((g1 - g0) * 4, d), dtype=np.int64)
-        part = codes[g0 * 4:min(rows, g1 * 4)]
+        full = np.zeros(((g1 - g0) * RG, d), dtype=np.int64)
+        part = codes[g0 * RG:min(rows, g1 * RG)]
         full[:part.shape[0]] = part
-        pat = e2m3_bits(full).reshape(g1 - g0, 4, d // 128, 128).transpose(0, 2, 1, 3)
+        pat = e2m3_bits(full).reshape(g1 - g0, RG, d // 128, 128).transpose(0, 2, 1, 3)
         bits = ((pat[..., None] >> np.arange(6)) & 1).astype(np.uint8)
-        seg = np.packbits(bits.reshape(g1 - g0, d // 128, 4, 768), axis=-1, bitorder="little")
-        out[g0 * 3 * d:g1 * 3 * d] = seg.reshape(-1)
+        seg = np.packbits(bits.reshape(g1 - g0, d // 128, RG, 768), axis=-1, bitorder="little")
+        out[g0 * gb:g1 * gb] = seg.reshape(-1)
     return out

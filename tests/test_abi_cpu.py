@@ -107,6 +107,25 @@ def test_e2m3_table_matches_format_definition():
     assert buf.size == 384 and buf[0] == 0x88 and buf[1] == 0x0F and not buf[2:].any()
 
 
+def test_e2m3_row_group_placement():
+    # the layout text's offsets, element by element: code k of row 4g + i sits
+    # in slice s = k // 128 at byte 3 d g + 384 s + 96 i, bits 6 (k % 128) up
+    import numpy as np
+    d, rows = 256, 70
+    q = np.zeros((rows, d), dtype=np.int64)
+    for r, k, v in [(0, 0, 3), (37, 130, -5), (69, 255, 7), (31, 127, -1)]:
+        q[r, k] = v
+    buf = codefmt.encode(codefmt.E2M3, q)
+    assert buf.size == 18 * 3 * d
+    pat = codefmt.e2m3_bits(np.array([3, -5, 7, -1]))
+    for (r, k), p in zip([(0, 0), (37, 130), (69, 255), (31, 127)], pat):
+        g, i, s, kk = r // 4, r % 4, k // 128, k % 128
+        bit = 8 * (3 * d * g + 384 * s + 96 * i) + 6 * kk
+        got = sum(((int(buf[(bit + j) // 8]) >> ((bit + j) % 8)) & 1) << j for j in range(6))
+        assert got == p
+    np.testing.assert_array_equal(codefmt.decode(codefmt.E2M3, buf, rows, d), q)
+
+
 @pytest.mark.parametrize("w_dtype,esize", [(BF16, 2), (F32, 4)])
 def test_channel_centring_layout(w_dtype, esize):
     # center = 2 keeps a copy of the weight in the blob and needs partial sums,
