@@ -198,7 +198,10 @@ int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, vo
   a.in_bf16 = d->x_dtype == HQ_BF16;
   a.rows = T;
   a.d = d->d_in;
-  a.scale = d->smooth ? at<float>(prepared, L.sigma_inv) : nullptr;
+  // with per-channel centring the multipliers are always passed (the blob
+  // holds ones without smoothing): the fast row kernel takes means only
+  // together with multipliers
+  a.scale = (d->smooth || cmean) ? at<float>(prepared, L.sigma_inv) : nullptr;
   a.chan_mean = cmean;
   a.log2b = log2i(d->block);
   a.center = d->center == HQ_CENTER_TOKEN;
@@ -614,9 +617,9 @@ int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, i
   a.in_bf16 = desc->x_dtype == HQ_BF16;
   a.rows = T;
   a.d = desc->d_in;
-  a.scale = desc->smooth ? at<float>(prepared, L.sigma_inv) : nullptr;
-  a.log2b = log2i(desc->block);
   const bool chan = desc->center == HQ_CENTER_CHANNEL;
+  a.scale = (desc->smooth || chan) ? at<float>(prepared, L.sigma_inv) : nullptr;
+  a.log2b = log2i(desc->block);
   a.chan_mean = chan ? mu : nullptr;
   a.center = desc->center == HQ_CENTER_TOKEN;
   a.qmax = qmax_of(desc->a_bits);

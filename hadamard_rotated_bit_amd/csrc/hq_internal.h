@@ -41,7 +41,8 @@ struct RowArgs {
   int d;
   const float* scale;     // per-channel multiplier (1/sigma or sigma); NULL = ones
   const float* chan_mean; // per-channel value subtracted before the multiplier
-                          // (per-channel centring); NULL = none
+                          // (per-channel centring); NULL = none. Needs scale
+                          // (ones for no smoothing).
   int log2b;
   int center;
   float qmax;

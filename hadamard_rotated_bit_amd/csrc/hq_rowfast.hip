@@ -89,7 +89,7 @@ __device__ __forceinline__ void store_piece48(uint8_t* p, uint32_t w0, uint32_t 
   *reinterpret_cast<uint16_t*>(p + (odd ? 0 : 4)) = uint16_t(odd ? w0 : w1);
 }
 
-template <typename TIn, int G, int C, int NX>
+template <typename TIn, int G, int C, int NX, int P>
 __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt_b) {
   constexpr int LOG2G = (G == 16) ? 4 : (G == 32) ? 5 : 6;
   constexpr int E = 8 * C;
@@ -104,21 +104,38 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
   const int d = a.d;
   const TIn* src = static_cast<const TIn*>(a.in) + r * d + t * 8;
 
-  // The channel multipliers (and means) go first: loads retire in issue
-  // order, so issued after the row they would make the first chunk wait for
-  // the whole row.
-  float sc[E], sh[E];
-  if (a.scale) {
-#pragma unroll
-    for (int c = 0; c < C; ++c) load8(a.scale + c * 8 * G + t * 8, &sc[c * 8]);
-  }
-  if (a.chan_mean) {
-#pragma unroll
-    for (int c = 0; c < C; ++c) load8(a.chan_mean + c * 8 * G + t * 8, &sh[c * 8]);
-  }
+  // The channel multipliers (P >= 1) and means (P = 2) are the same for
+  // every row: the block stages them once in LDS and each lane reads its 8
+  // per chunk there, so they hold no per-lane registers across the row and
+  // take no slots in the vector memory queue behind the row. Their loads go
+  // first (loads retire in issue order, so issued after the row they would
+  // wait for the whole row); lanes past the end repeat the last float4, so
+  // no load or store is conditional.
+  constexpr int NV4 = 2 * C * G;                // float4 per vector (d / 4)
+  constexpr int PV = (NV4 + 255) / 256;         // per thread
+  constexpr int NP = P == 2 ? 2 : 1;
+  __shared__ float4 lpar[P == 0 ? 1 : NP * PV * 256];
   float v[E];
+  if constexpr (P > 0) {
+    const int tid = threadIdx.x;
+    float4 pv[NP][PV];
 #pragma unroll
-  for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
+    for (int k = 0; k < PV; ++k) {
+      const int i = k * 256 + tid < NV4 ? k * 256 + tid : NV4 - 1;
+      pv[0][k] = reinterpret_cast<const float4*>(a.scale)[i];
+      if constexpr (P == 2) pv[1][k] = reinterpret_cast<const float4*>(a.chan_mean)[i];
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int k = 0; k < PV; ++k) lpar[q * PV * 256 + k * 256 + tid] = pv[q][k];
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
+  }
 
   const float g1 = (t & 1) ? -1.0f : 1.0f, g2 = (t & 2) ? -1.0f : 1.0f;
   const float g4 = (t & 4) ? -1.0f : 1.0f, g8 = (t & 8) ? -1.0f : 1.0f;
@@ -133,13 +150,15 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     float* vc = &v[c * 8];
-    if (a.chan_mean) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vc[j] -= sh[c * 8 + j];
+    if constexpr (P == 2) {
+      const float4 m0 = lpar[PV * 256 + c * 2 * G + 2 * t], m1 = lpar[PV * 256 + c * 2 * G + 2 * t + 1];
+      vc[0] -= m0.x; vc[1] -= m0.y; vc[2] -= m0.z; vc[3] -= m0.w;
+      vc[4] -= m1.x; vc[5] -= m1.y; vc[6] -= m1.z; vc[7] -= m1.w;
     }
-    if (a.scale) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vc[j] *= sc[c * 8 + j];
+    if constexpr (P > 0) {
+      const float4 s0_ = lpar[c * 2 * G + 2 * t], s1_ = lpar[c * 2 * G + 2 * t + 1];
+      vc[0] *= s0_.x; vc[1] *= s0_.y; vc[2] *= s0_.z; vc[3] *= s0_.w;
+      vc[4] *= s1_.x; vc[5] *= s1_.y; vc[6] *= s1_.z; vc[7] *= s1_.w;
     }
     if ((c & ((1 << NX) - 1)) == 0) s0 += vc[0];
     // channel bits 0..2, in registers
@@ -261,7 +280,12 @@ static hipError_t launch_fast_gc(const RowArgs& a, int nx, dim3 grid, float isb,
 #define HQ_NX(N)                                                                          \
   case N:                                                                                 \
     if constexpr (((C >> N) << N) == C) {                                                 \
-      hipLaunchKernelGGL((row_fast_kernel<TIn, G, C, N>), grid, dim3(256), 0, s, a, isb); \
+      if (a.chan_mean)                                                                    \
+        hipLaunchKernelGGL((row_fast_kernel<TIn, G, C, N, 2>), grid, dim3(256), 0, s, a, isb); \
+      else if (a.scale)                                                                   \
+        hipLaunchKernelGGL((row_fast_kernel<TIn, G, C, N, 1>), grid, dim3(256), 0, s, a, isb); \
+      else                                                                                \
+        hipLaunchKernelGGL((row_fast_kernel<TIn, G, C, N, 0>), grid, dim3(256), 0, s, a, isb); \
       return hipGetLastError();                                                           \
     }                                                                                     \
     break;
@@ -301,6 +325,7 @@ static hipError_t launch_fast_g(const RowArgs& a, int C, int nx, hipStream_t s) 
 }
 
 hipError_t launch_row_fast(const RowArgs& a, const RowGeom& g, hipStream_t s) {
+  if (a.chan_mean && !a.scale) return hipErrorInvalidValue;
   if (a.group) return hipErrorNotSupported;  // group-wise scales: general kernel
   const int log2g = g.G == 16 ? 4 : g.G == 32 ? 5 : 6;
   const int nx = a.log2b - 3 - log2g;
