@@ -136,6 +136,7 @@ void layout_of(const hq_desc* d, hq_prepared_layout* L) {
 
 struct Workspace {
   size_t codes, s_x, mu, U;
+  size_t lr_part;                  // rank > 0 with the split down projection
   size_t partial, mean, bias_eff;  // center = 2 only
   size_t total;
 };
@@ -150,6 +151,9 @@ Workspace workspace_of(const hq_desc* d, int64_t T) {
   off += align256(4 * size_t(T));
   w.U = off;
   off += align256(4 * size_t(T) * d->rank);
+  const int ks = d->rank ? hq::lowrank_slices(d->d_in, d->rank) : 0;
+  w.lr_part = ks ? off : 0;
+  off += align256(4 * size_t(ks) * size_t(T) * d->rank);
   if (d->center == HQ_CENTER_CHANNEL) {
     w.partial = off;
     off += align256(4 * size_t(hq::center_chunks(T > 0 ? T : 1)) * d->d_in);
@@ -190,7 +194,8 @@ int run_center(const hq_desc* d, const void* prepared, const void* X, int64_t T,
 // center = 2, `cmean` is the per-channel mean and `mu` (per-token) is NULL;
 // otherwise cmean is NULL and mu gets the per-token means.
 int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, void* codes,
-            float* s_x, float* mu, const float* cmean, float* U, hipStream_t s) {
+            float* s_x, float* mu, const float* cmean, float* U, hipStream_t s,
+            float* lr_part = nullptr) {
   hq_prepared_layout L;
   layout_of(d, &L);
   hq::RowArgs a = {};
@@ -216,9 +221,15 @@ int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, vo
   hipError_t e = hq::launch_row_transform(a, s);
   if (e != hipSuccess) return hip_fail(e, "activation kernel launch");
   if (d->rank) {
-    e = hq::launch_lowrank_down(X, a.in_bf16, T, d->d_in, d->rank,
-                                at<uint16_t>(prepared, L.l1_hi), at<uint16_t>(prepared, L.l1_lo),
-                                U, s);
+    // with a workspace for the slice products: the split form (same U bits)
+    if (lr_part)
+      e = hq::launch_lowrank_split(X, a.in_bf16, T, d->d_in, d->rank,
+                                   at<uint16_t>(prepared, L.l1_hi),
+                                   at<uint16_t>(prepared, L.l1_lo), lr_part, U, s);
+    else
+      e = hq::launch_lowrank_down(X, a.in_bf16, T, d->d_in, d->rank,
+                                  at<uint16_t>(prepared, L.l1_hi),
+                                  at<uint16_t>(prepared, L.l1_lo), U, s);
     if (e != hipSuccess) return hip_fail(e, "low-rank kernel launch");
   }
   return HQ_OK;
@@ -555,15 +566,17 @@ int hq_quant_linear(const hq_desc* desc, const void* prepared, const void* X, in
   float* s_x = at<float>(workspace, w.s_x);
   float* mu = at<float>(workspace, w.mu);
   float* U = desc->rank ? at<float>(workspace, w.U) : nullptr;
+  float* lr_part = w.lr_part ? at<float>(workspace, w.lr_part) : nullptr;
   if (desc->center == HQ_CENTER_CHANNEL) {
     float* cmean = at<float>(workspace, w.mean);
     float* bias_eff = at<float>(workspace, w.bias_eff);
     st = run_center(desc, prepared, X, T, at<float>(workspace, w.partial), cmean, bias_eff, s);
-    if (st == HQ_OK) st = run_act(desc, prepared, X, T, codes, s_x, nullptr, cmean, U, s);
+    if (st == HQ_OK)
+      st = run_act(desc, prepared, X, T, codes, s_x, nullptr, cmean, U, s, lr_part);
     if (st != HQ_OK) return st;
     return run_gemm_dequant(desc, prepared, codes, s_x, bias_eff, U, T, Y, s);
   }
-  st = run_act(desc, prepared, X, T, codes, s_x, mu, nullptr, U, s);
+  st = run_act(desc, prepared, X, T, codes, s_x, mu, nullptr, U, s, lr_part);
   if (st != HQ_OK) return st;
   return run_gemm_dequant(desc, prepared, codes, s_x, mu, U, T, Y, s);
 }

@@ -584,13 +584,142 @@ __global__ __launch_bounds__(W * 64) void lowrank_down_kernel(const TIn* __restr
   }
 }
 
+// Split form of the down projection: block (bx, q) takes rows 128 bx ..
+// 128 bx + 127 (16 per wave) over slice q of d (kw = d / KS channels). The
+// block stages the slice of l1 (hi and lo, R rows) in LDS with a pitch of
+// kw / 8 + 1 chunks of 16 B (the 16 rows one read phase touches land on 16
+// distinct bank groups); every load of the block (the row's kw channels and
+// the slice) issues before the first wait, so a wave makes one round trip.
+// Each wave runs the one-pass kernel's MFMA sequence for its slice and
+// writes its 16 x R products to part[q].
+constexpr int LR_MAX_STEPS = 16;   // kw <= 512
+constexpr int LR_FILL = 8;         // 16-B chunks of the slice per thread
+template <typename TIn, int R>
+__global__ __launch_bounds__(512) void lowrank_part_kernel(const TIn* __restrict__ x,
+                                                           int64_t rows, int d, int kw,
+                                                           const uint16_t* __restrict__ l1hi,
+                                                           const uint16_t* __restrict__ l1lo,
+                                                           float* __restrict__ part) {
+  constexpr int NG = R / 16;
+  extern __shared__ __attribute__((aligned(16))) uint4 lsl[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int q = blockIdx.y, kbeg = q * kw, cpr = kw / 8, pitch = cpr + 1;
+  const int nch = R * cpr;           // chunks per array
+  // the slice: chunk i of array a (row i / cpr, chunk i % cpr), clamped
+  // repeats past the end (same value to the same place)
+  uint4 fv[LR_FILL];
+  int fpos[LR_FILL];
+#pragma unroll
+  for (int j = 0; j < LR_FILL; ++j) {
+    int i = j * 512 + tid;
+    if (i > 2 * nch - 1) i = 2 * nch - 1;
+    const int a = i >= nch ? 1 : 0, ii = i - a * nch, r = ii / cpr, c = ii - r * cpr;
+    const uint16_t* src = (a ? l1lo : l1hi) + int64_t(r) * d + kbeg + 8 * c;
+    fv[j] = *reinterpret_cast<const uint4*>(src);
+    fpos[j] = a * R * pitch + r * pitch + c;
+  }
+  const int64_t row0 = int64_t(blockIdx.x) * 128 + 16 * w;
+  int64_t row = row0 + (lane & 15);
+  if (row >= rows) row = rows - 1;
+  const int kq = (lane >> 4) * 8;
+  const int steps = kw / 32;
+  v8bf ahi[LR_MAX_STEPS], alo[LR_MAX_STEPS];
+#pragma unroll
+  for (int st = 0; st < LR_MAX_STEPS; ++st)
+    if (st < steps) lowrank_load_a<TIn, R>(x, row * d + kbeg + 32 * st + kq, &ahi[st], &alo[st]);
+#pragma unroll
+  for (int j = 0; j < LR_FILL; ++j) lsl[fpos[j]] = fv[j];
+  __syncthreads();
+  v4f acc[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) acc[g] = v4f{0, 0, 0, 0};
+#pragma unroll
+  for (int st = 0; st < LR_MAX_STEPS; ++st) {
+    if (st < steps) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int p = (g * 16 + (lane & 15)) * pitch + 4 * st + (lane >> 4);
+        const v8bf bhi = *reinterpret_cast<const v8bf*>(&lsl[p]);
+        const v8bf blo = *reinterpret_cast<const v8bf*>(&lsl[R * pitch + p]);
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[st], bhi, acc[g], 0, 0, 0);
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[st], blo, acc[g], 0, 0, 0);
+        if constexpr (sizeof(TIn) == 4)
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[st], bhi, acc[g], 0, 0, 0);
+      }
+    }
+  }
+  // 16x16 output layout: lane l, register i -> row 4 (l / 16) + i, column l % 16.
+  float* pq = part + int64_t(q) * rows * R;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t rr = row0 + 4 * (lane >> 4) + i;
+    if (rr < rows) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) pq[rr * R + g * 16 + (lane & 15)] = acc[g][i];
+    }
+  }
+}
+
+// U = sum over the slices in order, from 0 (the one-pass kernel's order).
+__global__ void lowrank_sum_kernel(const float* __restrict__ part, int64_t n, int ks,
+                                   float* __restrict__ U) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int q = 0; q < ks; ++q) s += part[q * n + i];
+  U[i] = s;
+}
+
+// Waves (one-pass kernel) = slices (split form) per width d.
+static int lowrank_waves(int d) { return d % 256 == 0 && d >= 1024 ? 8 : 4; }
+
+int lowrank_slices(int d, int r) {
+  if (d % 128 || (r != 16 && r != 32 && r != 48 && r != 64)) return 0;
+  const int ks = lowrank_waves(d), kw = d / ks;
+  if (kw / 32 > LR_MAX_STEPS || 2 * r * (kw / 8) > LR_FILL * 512) return 0;
+  if (2 * r * (kw / 8 + 1) * 16 > 65536) return 0;   // the slice in at most 64 KB of LDS
+  return ks;
+}
+
+hipError_t launch_lowrank_split(const void* x, int x_bf16, int64_t rows, int d, int r,
+                                const uint16_t* l1_hi, const uint16_t* l1_lo, float* part,
+                                float* U, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int ks = lowrank_slices(d, r);
+  if (!ks) return hipErrorInvalidValue;
+  const int kw = d / ks;
+  const size_t lds = size_t(2) * r * (kw / 8 + 1) * 16;
+  dim3 grid{unsigned((rows + 127) / 128), unsigned(ks)};
+#define HQ_LRS(RR)                                                                              \
+  case RR:                                                                                      \
+    if (x_bf16)                                                                                 \
+      hipLaunchKernelGGL((lowrank_part_kernel<uint16_t, RR>), grid, dim3(512), lds, s,          \
+                         static_cast<const uint16_t*>(x), rows, d, kw, l1_hi, l1_lo, part);     \
+    else                                                                                        \
+      hipLaunchKernelGGL((lowrank_part_kernel<float, RR>), grid, dim3(512), lds, s,             \
+                         static_cast<const float*>(x), rows, d, kw, l1_hi, l1_lo, part);        \
+    break;
+  switch (r) {
+    HQ_LRS(16) HQ_LRS(32) HQ_LRS(48) HQ_LRS(64)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef HQ_LRS
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = rows * r;
+  hipLaunchKernelGGL(lowrank_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, part,
+                     n, ks, U);
+  return hipGetLastError();
+}
+
 hipError_t launch_lowrank_down(const void* x, int x_bf16, int64_t rows, int d, int r,
                                const uint16_t* l1_hi, const uint16_t* l1_lo, float* U,
                                hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (d % 128) return hipErrorInvalidValue;
   // eight waves per 16 rows when every wave still gets whole 32-channel steps
-  const bool wide = d % 256 == 0 && d >= 1024;
+  const bool wide = lowrank_waves(d) == 8;
   dim3 grid{unsigned((rows + 15) / 16)};
 #define HQ_LR_LAUNCH(RR, WW)                                                                    \
   if (x_bf16)                                                                                   \

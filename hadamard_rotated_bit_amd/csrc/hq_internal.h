@@ -87,6 +87,15 @@ hipError_t launch_prep_l2(const void* l2, int bf16, int r, int n, int n_pad, uin
 hipError_t launch_lowrank_down(const void* x, int x_bf16, int64_t rows, int d, int r,
                                const uint16_t* l1_hi, const uint16_t* l1_lo, float* U,
                                hipStream_t s);
+// The same U in two passes: per slice of d, products for 128 rows per block
+// with the slice of l1 shared in LDS, into part [slices, rows, r]; then the
+// slices summed in order. lowrank_slices(d, r) is the slice count (the
+// partition the one-pass kernel gives its waves, so U is bit-identical), or
+// 0 where the split form does not apply.
+int lowrank_slices(int d, int r);
+hipError_t launch_lowrank_split(const void* x, int x_bf16, int64_t rows, int d, int r,
+                                const uint16_t* l1_hi, const uint16_t* l1_lo, float* part,
+                                float* U, hipStream_t s);
 
 // Per-channel centring (center = 2): partial column sums over chunks of
 // CENTER_RPC rows, then mean [d]; partial holds center_chunks(rows) x d floats.

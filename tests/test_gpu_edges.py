@@ -125,6 +125,22 @@ def test_low_rank(rank, xd, gemm):
     assert err.max() <= 1e-4, err.max()
 
 
+@pytest.mark.parametrize("T,d_in,rank,xd", [(130, 2048, 32, "bf16"), (300, 3072, 32, "bf16"),
+                                         (77, 1152, 16, "f32"), (129, 1024, 64, "f32"),
+                                         (1, 512, 48, "bf16")])
+def test_low_rank_split_matches_one_pass(T, d_in, rank, xd):
+    # quant_linear forms U in two passes over slices of d_in (workspace for the
+    # slice products); act_quantize has no workspace and runs the one-pass
+    # kernel. The slices are the one-pass kernel's wave partition summed in
+    # the same order, so U and therefore Y are bit-identical.
+    r = run_case(T, d_in, 264, block=128, rank=rank, x_dtype=xd, w_dtype=xd, y_dtype=xd)
+    desc, prep, X, Y, codes, s_x, mu, U, ora = r
+    check_all(Y, codes, s_x, ora, desc)
+    err = np.linalg.norm(to_np(U) - ora["u"], axis=1) / np.linalg.norm(ora["u"], axis=1)
+    assert err.max() <= 1e-4, err.max()
+    assert torch.equal(Y, hq.gemm_dequant(desc, prep, codes, s_x, mu, U))
+
+
 def test_heavy_outliers_and_no_centring():
     r = run_case(400, 2048, 512, block=2048, center=False, alpha=None, n_outliers=16,
                  outlier=1000.0)
