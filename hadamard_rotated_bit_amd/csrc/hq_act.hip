@@ -660,13 +660,19 @@ __global__ __launch_bounds__(512) void lowrank_part_kernel(const TIn* __restrict
   }
 }
 
-// U = sum over the slices in order, from 0 (the one-pass kernel's order).
-__global__ void lowrank_sum_kernel(const float* __restrict__ part, int64_t n, int ks,
+// U = sum over the KS slices in order, from 0 (the one-pass kernel's
+// order); the KS loads of an element issue together.
+template <int KS>
+__global__ void lowrank_sum_kernel(const float* __restrict__ part, int64_t n,
                                    float* __restrict__ U) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
+  float p[KS];
+#pragma unroll
+  for (int q = 0; q < KS; ++q) p[q] = part[q * n + i];
   float s = 0.0f;
-  for (int q = 0; q < ks; ++q) s += part[q * n + i];
+#pragma unroll
+  for (int q = 0; q < KS; ++q) s += p[q];
   U[i] = s;
 }
 
@@ -708,8 +714,11 @@ hipError_t launch_lowrank_split(const void* x, int x_bf16, int64_t rows, int d, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = rows * r;
-  hipLaunchKernelGGL(lowrank_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, part,
-                     n, ks, U);
+  const dim3 sg{unsigned((n + 255) / 256)};
+  if (ks == 8)
+    hipLaunchKernelGGL(lowrank_sum_kernel<8>, sg, dim3(256), 0, s, part, n, U);
+  else
+    hipLaunchKernelGGL(lowrank_sum_kernel<4>, sg, dim3(256), 0, s, part, n, U);
   return hipGetLastError();
 }
 
