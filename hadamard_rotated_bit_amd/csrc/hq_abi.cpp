@@ -796,6 +796,15 @@ int hq_int_linear(const hq_int_desc* desc, const void* prepared, const int8_t* x
   hipStream_t s = static_cast<hipStream_t>(stream);
   hq_int_layout L;
   int_layout_of(desc, &L);
+  if (desc->d_out % 256 == 0) {
+    // whole 256-channel units: GEMM and requantisation in one kernel (the
+    // same integers as the two-kernel path below)
+    const hipError_t e = hq::launch_int_fused(
+        x_codes, T, desc->d_in, at<int8_t>(prepared, L.w_codes), desc->d_out, desc->block,
+        at<int32_t>(prepared, L.b_int), at<int32_t>(prepared, L.mult),
+        at<int32_t>(prepared, L.shift), y_codes, s);
+    return e == hipSuccess ? HQ_OK : hip_fail(e, "integer-layer kernel launch");
+  }
   int32_t* acc = static_cast<int32_t*>(workspace);
   hipError_t e = hq::launch_gemm(x_codes, T, at<int8_t>(prepared, L.w_codes), desc->d_out,
                                  desc->d_in, acc, desc->d_out, nullptr, s);

@@ -148,6 +148,44 @@ __device__ __forceinline__ void int_xstage(double (&u)[16], int lane, int m) {
   for (int k = 0; k < 16; ++k) u[k] = fma(u[k], g, lane_xor16_f64<D>(u[k]));
 }
 
+// Butterflies of one 16-lane group's 256-channel unit (channel bits 0-3 in
+// the lane, bits 4-7 across the group), for blocks of m channels.
+__device__ __forceinline__ void int_unit_transform(double (&u)[16], int lane, int m) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+    if (h < m) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (!(k & h)) {
+          const double x = u[k], z = u[k + h];
+          u[k] = x + z;
+          u[k + h] = x - z;
+        }
+      }
+    }
+  }
+  int_xstage<1>(u, lane, m);
+  int_xstage<2>(u, lane, m);
+  int_xstage<4>(u, lane, m);
+  int_xstage<8>(u, lane, m);
+}
+
+// round(u 2^-n) with ties to even, clamped to +-127, as 16 int8 codes.
+__device__ __forceinline__ uint4 int_unit_codes(const double (&u)[16], double scale) {
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const double v = fmin(fmax(rint(u[4 * q + k] * scale), -127.0), 127.0);
+      packed |= (uint32_t(int(v)) & 0xFFu) << (8 * k);
+    }
+    w[q] = packed;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Requantisation of int32 products acc [T, ldc] (without bias). Each group of
 // 16 lanes takes one (token, 256-channel chunk) unit, lane l of the group
 // holding channels 16 l .. 16 l + 15 of the chunk. u = M (acc + b_int), the
@@ -182,43 +220,95 @@ __global__ __launch_bounds__(256) void int_requant_kernel(
       u[4 * q + 0] = u[4 * q + 1] = u[4 * q + 2] = u[4 * q + 3] = 0.0;
     }
   }
-  // channel bits 0-3, in the lane
+  int_unit_transform(u, lane, m);
+  if (!live || c0 >= d_out) return;
+  const uint4 w = int_unit_codes(u, ldexp(1.0, -*shift));
+  int8_t* dst = y + row * ldy + c0;
+  if (c0 + 16 <= d_out) {
+    *reinterpret_cast<uint4*>(dst) = w;
+  } else {   // the last 8 channels of d_out
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w.x, w.y);
+  }
+}
+
+// The whole integer layer in one kernel for d_out a multiple of 256: block
+// (bx, by) takes tokens 32 bx .. 32 bx + 31 and channels 256 by .. + 255.
+// Each of the 4 waves forms its 32 x 64 part of a = x w-bar^T with
+// v_mfma_i32_32x32x32_i8 (operands straight from memory: 8 k-steps of both
+// operands in flight per round trip), the exact int32 tile goes to LDS, and
+// the block then requantises it unit by unit as above (16 tokens per pass),
+// so the products never leave the chip.
+typedef int iv4 __attribute__((ext_vector_type(4)));
+typedef int iv16 __attribute__((ext_vector_type(16)));
+constexpr int IF_ROWS = 32;
+constexpr int IF_PITCH = 256 + 4;   // int32 per LDS row (16-B aligned, rows 4 banks apart)
+__global__ __launch_bounds__(256) void int_fused_kernel(
+    const int8_t* __restrict__ x, int64_t T, int d_in, const int8_t* __restrict__ w, int d_out,
+    int m, const int32_t* __restrict__ b_int, const int32_t* __restrict__ mult,
+    const int32_t* __restrict__ shift, int8_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) int32_t tile[IF_ROWS * IF_PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t row0 = int64_t(blockIdx.x) * IF_ROWS;
+  const int c_blk = int(blockIdx.y) * 256;
+  int64_t xr = row0 + (lane & 31);
+  if (xr >= T) xr = T - 1;
+  // MFMA operands: lane l feeds row l % 32 and k-bytes 16 (l / 32) .. + 15 of
+  // each 32-byte k-step
+  const int kh = 16 * (lane >> 5);
+  const int8_t* xa = x + xr * d_in + kh;
+  const int8_t* wb = w + int64_t(c_blk + 64 * wv + (lane & 31)) * d_in + kh;
+  const int64_t w32 = int64_t(32) * d_in;
+  iv16 acc0 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  iv16 acc1 = acc0;
+  for (int k0 = 0; k0 < d_in; k0 += 256) {
+    iv4 a[8], b0[8], b1[8];
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
-    if (h < m) {
+    for (int st = 0; st < 8; ++st) {
+      if (k0 + 32 * st < d_in) {
+        a[st] = *reinterpret_cast<const iv4*>(xa + k0 + 32 * st);
+        b0[st] = *reinterpret_cast<const iv4*>(wb + k0 + 32 * st);
+        b1[st] = *reinterpret_cast<const iv4*>(wb + w32 + k0 + 32 * st);
+      }
+    }
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        if (!(k & h)) {
-          const double x = u[k], z = u[k + h];
-          u[k] = x + z;
-          u[k + h] = x - z;
-        }
+    for (int st = 0; st < 8; ++st) {
+      if (k0 + 32 * st < d_in) {
+        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[st], a[st], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[st], a[st], acc1, 0, 0, 0);
       }
     }
   }
-  // channel bits 4-7, across the 16 lanes of the group
-  int_xstage<1>(u, lane, m);
-  int_xstage<2>(u, lane, m);
-  int_xstage<4>(u, lane, m);
-  int_xstage<8>(u, lane, m);
-  if (!live || c0 >= d_out) return;
-  const double scale = ldexp(1.0, -*shift);
-  uint32_t w[4];
+  // lane l, register r: token l % 32, channel (of the wave's 32-wide tile)
+  // 8 (r / 4) + 4 (l / 32) + r % 4
+  int32_t* trow = tile + (lane & 31) * IF_PITCH + 64 * wv + 4 * (lane >> 5);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    uint32_t packed = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const double v = fmin(fmax(rint(u[4 * q + k] * scale), -127.0), 127.0);
-      packed |= (uint32_t(int(v)) & 0xFFu) << (8 * k);
-    }
-    w[q] = packed;
+    *reinterpret_cast<iv4*>(trow + 8 * q) =
+        iv4{acc0[4 * q], acc0[4 * q + 1], acc0[4 * q + 2], acc0[4 * q + 3]};
+    *reinterpret_cast<iv4*>(trow + 32 + 8 * q) =
+        iv4{acc1[4 * q], acc1[4 * q + 1], acc1[4 * q + 2], acc1[4 * q + 3]};
   }
-  int8_t* dst = y + row * ldy + c0;
-  if (c0 + 16 <= d_out) {
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {   // the last 8 channels of d_out
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  __syncthreads();
+  const int l16 = tid & 15, cl = 16 * l16;
+  const double scale = ldexp(1.0, -*shift);
+#pragma unroll
+  for (int pass = 0; pass < IF_ROWS / 16; ++pass) {
+    const int r = pass * 16 + (tid >> 4);
+    double u[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = c_blk + cl + 4 * q;
+      const int4 av = *reinterpret_cast<const int4*>(tile + r * IF_PITCH + cl + 4 * q);
+      const int4 bv = *reinterpret_cast<const int4*>(b_int + c);
+      const int4 mv = *reinterpret_cast<const int4*>(mult + c);
+      u[4 * q + 0] = double(av.x + bv.x) * double(mv.x);
+      u[4 * q + 1] = double(av.y + bv.y) * double(mv.y);
+      u[4 * q + 2] = double(av.z + bv.z) * double(mv.z);
+      u[4 * q + 3] = double(av.w + bv.w) * double(mv.w);
+    }
+    int_unit_transform(u, l16, m);
+    if (row0 + r < T)
+      *reinterpret_cast<uint4*>(y + (row0 + r) * d_out + c_blk + cl) = int_unit_codes(u, scale);
   }
 }
 
@@ -243,6 +333,18 @@ hipError_t launch_int_constants(const float* bias, const float* s_w, int d_out, 
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(int_constants_kernel, dim3(1), dim3(256), 0, s, bias, s_w, d_out, d_out_pad,
                      m, bias_block, double(s_x), double(s_y), b_int, mult, shift);
+  return hipGetLastError();
+}
+
+hipError_t launch_int_fused(const int8_t* x, int64_t T, int d_in, const int8_t* w, int d_out,
+                            int m, const int32_t* b_int, const int32_t* mult,
+                            const int32_t* shift, int8_t* y, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (d_out % 256 || d_in % 32 || m < 1 || m > WH_MAX_BLOCK || (m & (m - 1)))
+    return hipErrorInvalidValue;
+  const dim3 grid{unsigned((T + IF_ROWS - 1) / IF_ROWS), unsigned(d_out / 256)};
+  hipLaunchKernelGGL(int_fused_kernel, grid, dim3(256), 0, s, x, T, d_in, w, d_out, m, b_int,
+                     mult, shift, y);
   return hipGetLastError();
 }
 

@@ -138,6 +138,12 @@ hipError_t launch_wh_weight(const void* w, int w_bf16, int d_out, int d_in, int 
 hipError_t launch_int_constants(const float* bias, const float* s_w, int d_out, int d_out_pad,
                                 int m, int bias_block, float s_x, float s_y, int32_t* b_int,
                                 int32_t* mult, int32_t* shift, hipStream_t s);
+// The integer GEMM and that requantisation in one kernel (d_out % 256 == 0):
+// y [T, d_out] from x [T, d_in] int8 and w [>= d_out, d_in] int8; the int32
+// products stay on the chip.
+hipError_t launch_int_fused(const int8_t* x, int64_t T, int d_in, const int8_t* w, int d_out,
+                            int m, const int32_t* b_int, const int32_t* mult,
+                            const int32_t* shift, int8_t* y, hipStream_t s);
 // y [T, ldy] int8 = clamp(round(H~_m (mult . (acc + b_int)) / 2^shift), +-127).
 hipError_t launch_int_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_out, int m,
                               const int32_t* b_int, const int32_t* mult, const int32_t* shift,
