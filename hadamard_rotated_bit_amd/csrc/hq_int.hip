@@ -233,16 +233,16 @@ __global__ __launch_bounds__(256) void int_requant_kernel(
 
 // The whole integer layer in one kernel for d_out a multiple of 256: block
 // (bx, by) takes tokens 32 bx .. 32 bx + 31 and channels 256 by .. + 255.
-// Each of the 4 waves forms its 32 x 64 part of a = x w-bar^T with
+// Each of the 8 waves forms its 32 x 32 part of a = x w-bar^T with
 // v_mfma_i32_32x32x32_i8 (operands straight from memory: 8 k-steps of both
 // operands in flight per round trip), the exact int32 tile goes to LDS, and
-// the block then requantises it unit by unit as above (16 tokens per pass),
-// so the products never leave the chip.
+// the block then requantises it unit by unit as above (32 units, one per 16
+// lanes), so the products never leave the chip.
 typedef int iv4 __attribute__((ext_vector_type(4)));
 typedef int iv16 __attribute__((ext_vector_type(16)));
 constexpr int IF_ROWS = 32;
 constexpr int IF_PITCH = 256 + 4;   // int32 per LDS row (16-B aligned, rows 4 banks apart)
-__global__ __launch_bounds__(256) void int_fused_kernel(
+__global__ __launch_bounds__(512) void int_fused_kernel(
     const int8_t* __restrict__ x, int64_t T, int d_in, const int8_t* __restrict__ w, int d_out,
     int m, const int32_t* __restrict__ b_int, const int32_t* __restrict__ mult,
     const int32_t* __restrict__ shift, int8_t* __restrict__ y) {
@@ -256,44 +256,33 @@ __global__ __launch_bounds__(256) void int_fused_kernel(
   // each 32-byte k-step
   const int kh = 16 * (lane >> 5);
   const int8_t* xa = x + xr * d_in + kh;
-  const int8_t* wb = w + int64_t(c_blk + 64 * wv + (lane & 31)) * d_in + kh;
-  const int64_t w32 = int64_t(32) * d_in;
-  iv16 acc0 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-  iv16 acc1 = acc0;
+  const int8_t* wb = w + int64_t(c_blk + 32 * wv + (lane & 31)) * d_in + kh;
+  iv16 acc = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   for (int k0 = 0; k0 < d_in; k0 += 256) {
-    iv4 a[8], b0[8], b1[8];
+    iv4 a[8], b[8];
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       if (k0 + 32 * st < d_in) {
         a[st] = *reinterpret_cast<const iv4*>(xa + k0 + 32 * st);
-        b0[st] = *reinterpret_cast<const iv4*>(wb + k0 + 32 * st);
-        b1[st] = *reinterpret_cast<const iv4*>(wb + w32 + k0 + 32 * st);
+        b[st] = *reinterpret_cast<const iv4*>(wb + k0 + 32 * st);
       }
     }
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (k0 + 32 * st < d_in) {
-        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[st], a[st], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[st], a[st], acc1, 0, 0, 0);
-      }
-    }
+    for (int st = 0; st < 8; ++st)
+      if (k0 + 32 * st < d_in) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[st], a[st], acc, 0, 0, 0);
   }
   // lane l, register r: token l % 32, channel (of the wave's 32-wide tile)
   // 8 (r / 4) + 4 (l / 32) + r % 4
-  int32_t* trow = tile + (lane & 31) * IF_PITCH + 64 * wv + 4 * (lane >> 5);
+  int32_t* trow = tile + (lane & 31) * IF_PITCH + 32 * wv + 4 * (lane >> 5);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < 4; ++q)
     *reinterpret_cast<iv4*>(trow + 8 * q) =
-        iv4{acc0[4 * q], acc0[4 * q + 1], acc0[4 * q + 2], acc0[4 * q + 3]};
-    *reinterpret_cast<iv4*>(trow + 32 + 8 * q) =
-        iv4{acc1[4 * q], acc1[4 * q + 1], acc1[4 * q + 2], acc1[4 * q + 3]};
-  }
+        iv4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
   __syncthreads();
   const int l16 = tid & 15, cl = 16 * l16;
   const double scale = ldexp(1.0, -*shift);
-#pragma unroll
-  for (int pass = 0; pass < IF_ROWS / 16; ++pass) {
-    const int r = pass * 16 + (tid >> 4);
+  {
+    const int r = tid >> 4;   // 32 units, one per 16 lanes
     double u[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -343,7 +332,7 @@ hipError_t launch_int_fused(const int8_t* x, int64_t T, int d_in, const int8_t* 
   if (d_out % 256 || d_in % 32 || m < 1 || m > WH_MAX_BLOCK || (m & (m - 1)))
     return hipErrorInvalidValue;
   const dim3 grid{unsigned((T + IF_ROWS - 1) / IF_ROWS), unsigned(d_out / 256)};
-  hipLaunchKernelGGL(int_fused_kernel, grid, dim3(256), 0, s, x, T, d_in, w, d_out, m, b_int,
+  hipLaunchKernelGGL(int_fused_kernel, grid, dim3(512), 0, s, x, T, d_in, w, d_out, m, b_int,
                      mult, shift, y);
   return hipGetLastError();
 }

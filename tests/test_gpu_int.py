@@ -246,3 +246,18 @@ def test_dh_wh_two_layer_chain():
     q2 = O.int_forward(q1, g2)["y_int"].astype(np.int64)
     assert np.array_equal(y2, q2)
     assert O.sqnr_db(y2f / s2, y2.astype(np.float64)) > 15
+
+
+@pytest.mark.parametrize("side,k,T,d_out", [(hq.HQ_INT_WH, 1, 77, 512), (hq.HQ_INT_DH, 256, 300, 256)])
+def test_fused_layer_equals_requant_stage(side, k, T, d_out):
+    # d_out a multiple of 256: int_linear runs GEMM and requantisation in one
+    # kernel. The standalone requantisation stage fed the exact int32 products
+    # (formed here on the host) gives the same codes.
+    w = WL.custom(800 + T, T, 256, d_out, dtype="f32", x_dist="laplace", n_outliers=3,
+                  outlier=20.0, w_std=0.05)
+    c = IntCase(w, T, 256, side=side, in_block=k)
+    y = to_np(hq.int_linear(c.desc, c.prep, c.X)).astype(np.int64)
+    g = c.gpu_constants()
+    acc = c.xi.astype(np.int64) @ g["qw"][:d_out].T
+    ys = to_np(hq.int_requant(c.desc, c.prep, torch.from_numpy(acc.astype(np.int32)).cuda()))
+    assert np.array_equal(y, ys.astype(np.int64))
