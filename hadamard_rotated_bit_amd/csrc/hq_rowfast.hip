@@ -7,15 +7,22 @@
 // Same arithmetic per row as the general kernel (HadaNorm Eq. (1) activation
 // side, HaTQ Sec. III-A Eq. (3) quantiser), with three differences in how the
 // lanes carry it out:
-//  * Cross-lane butterflies at lane distance 1, 2 and 8 are one
-//    v_fmac_f32_dpp each (v += g * v[lane ^ M], g = +1 on the lower and -1
-//    on the upper lane of a pair); distance 4 and 16 use ds_swizzle plus one
-//    fma. The upper lane then holds the negated difference, so after all
-//    stages lane t stores sigma_t times the transformed value, with
-//    sigma_t = (-1)^popcount(t & NEG) a per-lane sign (NEG = the lane bits
-//    done this way). The mean is subtracted as sigma_t * mu and the
-//    quantiser uses sigma_t * (qmax / absmax): every code and scale is the
-//    same as with unsigned storage, bit for bit.
+//  * Cross-lane butterflies are one v_fmac_f32_dpp each where a DPP pattern
+//    reaches the partner (v += g * v[partner], g = +1 on the lower and -1 on
+//    the upper lane of a pair): lane ^ 1 and lane ^ 2 (quad permutes),
+//    lane ^ 8 (row rotation by 8) and lane ^ 7 (half-row mirror); distance
+//    16 uses ds_swizzle plus one fma, distance 32 v_permlane32_swap. The
+//    xor-7 stage runs first, on channel bit 5 (lane bit 2): butterflies over
+//    the masks 7, 1, 2 (then 8, 16, 32) give the Sylvester transform with its
+//    outputs permuted, lane t holding channel pi(t) = t with bit 2 flipped
+//    when bits 0 and 1 differ, so results are stored at pi(t). The upper lane
+//    of a pair holds the negated difference: after all stages lane t stores
+//    sigma_t times the transformed value, with sigma_t = (-1)^popcount(t &
+//    NEG) (NEG = the lane bits done in this form), negated again on lanes
+//    with t mod 8 = 5 or 6 (the xor-7 stage's pairing). The mean is
+//    subtracted as sigma_t * mu and the quantiser uses sigma_t * (qmax /
+//    absmax): every code and scale is the same as with unsigned storage, bit
+//    for bit.
 //  * E2M3 codes come from v_cvt_scalef32_2xpk16_fp6_f32 on the integer codes
 //    rint(x * qmax / absmax) (formed as fma(x, r, 1.5 2^23) - 1.5 2^23, one
 //    rounding of the exact product), 32 codes per instruction; the
@@ -61,6 +68,8 @@ __device__ __forceinline__ void xstage8(float* v, float g) {
     HQ_DPP_FMAC8("quad_perm:[2,3,0,1]");
   } else if constexpr (M == 8) {
     HQ_DPP_FMAC8("row_ror:8");
+  } else if constexpr (M == 7) {
+    HQ_DPP_FMAC8("row_half_mirror");   // lane ^ 7 inside each 8-lane half row
   } else if constexpr (M == 4 || M == 16) {
     // ds_swizzle bitmask mode on 32-lane groups: lane reads lane ^ M.
     constexpr int pat = 0x1F | (M << 10);
@@ -140,7 +149,10 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
   const float g1 = (t & 1) ? -1.0f : 1.0f, g2 = (t & 2) ? -1.0f : 1.0f;
   const float g4 = (t & 4) ? -1.0f : 1.0f, g8 = (t & 8) ? -1.0f : 1.0f;
   const float g16 = (t & 16) ? -1.0f : 1.0f, g32 = (t & 32) ? -1.0f : 1.0f;
-  const float sgn = (__builtin_popcount(t & NEG) & 1) ? -1.0f : 1.0f;
+  const float sgn = ((__builtin_popcount(t & NEG) & 1) ? -1.0f : 1.0f) *
+                    (((t & 7) == 5 || (t & 7) == 6) ? -1.0f : 1.0f);
+  // channel position of the lane's transformed values (see the file comment)
+  const int pt = t ^ (((t ^ (t >> 1)) & 1) << 2);
 
   // Row sum of the unnormalised transform: every row of a Sylvester H~_B
   // but the first sums to zero, so the sum over a block's outputs is B times
@@ -174,9 +186,9 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
       }
     }
     // channel bits 3 .. 3 + log2 G - 1, across lanes
+    xstage8<7>(vc, g4);
     xstage8<1>(vc, g1);
     xstage8<2>(vc, g2);
-    xstage8<4>(vc, g4);
     xstage8<8>(vc, g8);
     if constexpr (G >= 32) xstage8<16>(vc, g16);
     if constexpr (G >= 64) xstage8<32>(vc, g32);
@@ -212,7 +224,7 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
   if (a.mode == ROW_EXPORT) {
     if (valid) {
       const float sc = sgn * inv_sqrt_b;
-      float* o = a.out_xt + row * d + t * 8;
+      float* o = a.out_xt + row * d + pt * 8;
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         const float* vc = &v[c * 8];
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
   if (!valid) return;
   if (a.code_fmt == CODES_E2M3) {
     constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
-    const bool odd = t & 1;
+    const bool odd = pt & 1;
     uint8_t* rb = a.codes + e2m3_piece_offset<F6_GROUP>(row, d, 0);
 #pragma unroll
     for (int c0 = 0; c0 < C; c0 += 4) {
@@ -246,7 +258,7 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         if (c0 + m >= C) break;
-        const int e0 = (c0 + m) * 8 * G + t * 8;
+        const int e0 = (c0 + m) * 8 * G + pt * 8;
         uint8_t* dst = rb + (e0 >> 7) * (96 * F6_GROUP) + 6 * ((e0 & 127) >> 3);
         uint32_t w0, w1;
         if (m == 0) { w0 = p[0]; w1 = p[1] & 0xFFFFu; }
@@ -257,7 +269,7 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
       }
     }
   } else {
-    const int64_t base = row * d + t * 8;
+    const int64_t base = row * d + pt * 8;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const float* vc = &v[c * 8];
