@@ -552,6 +552,39 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
       uint16_t* const ybase = static_cast<uint16_t*>(ep.Y) + mw * ep.ldy + (cur.n0 + wn0);
       const __amdgpu_buffer_rsrc_t yr = make_rsrc(ybase, int(rows_v * ep.ldy * 2));
       const int ypitch = int(ep.ldy * 2);
+      // Rank <= 32 (one 32-rank chunk): the wave's L2 operands are the same
+      // for every slice, so they are loaded once per tile, and U of slice
+      // i + 1 is loaded while slice i is computed.
+      const bool lr_one = LR && ep.rank <= 32;
+      const bool lr_two = LR && ep.rank > 16;
+      v8bf wh1[LR ? TN : 1][2], wl1[LR ? TN : 1][2];
+      float un[2][8];
+      auto load_u = [&](int i_, float (&dst)[2][8]) {
+        const int64_t m = mw + i_ * 32 + erow;
+        const int64_t mc = m < M ? m : M - 1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k0 = (h == 0 || lr_two) ? 16 * h : 0;
+          load8(ep.U + mc * ep.rank + k0 + 8 * ehalf, dst[h]);
+        }
+      };
+      if constexpr (LR) {
+        if (lr_one) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int k0 = (h == 0 || lr_two) ? 16 * h : 0;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const int64_t nb = cur.n0 + wn0 + j * 32;
+              const int64_t nr = nb + erow < N ? nb + erow : N - 1;
+              const int64_t off = nr * ep.rank + k0 + 8 * ehalf;
+              wh1[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
+              wl1[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
+            }
+          }
+          load_u(0, un);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const float sx = Pf[3 * BN + wm0 + 32 * i + erow];
@@ -564,7 +597,26 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
           const int64_t mc = m < M ? m : M - 1;
 #pragma unroll
           for (int j = 0; j < TN; ++j) lr[j] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-          for (int kc = 0; kc < ep.rank; kc += 32) {
+          if (lr_one) {
+            float uf[2][8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) uf[h][e] = un[h][e];
+            if (i + 1 < TM) load_u(i + 1, un);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              if (h == 1 && !lr_two) break;
+              const v8bf uh = pack_bf16x8(uf[h], false), ul = pack_bf16x8(uf[h], true);
+#pragma unroll
+              for (int j = 0; j < TN; ++j) {
+                lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh1[j][h], uh, lr[j], 0, 0, 0);
+                lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl1[j][h], uh, lr[j], 0, 0, 0);
+                lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh1[j][h], ul, lr[j], 0, 0, 0);
+              }
+            }
+          }
+          for (int kc = 0; !lr_one && kc < ep.rank; kc += 32) {
             const bool two = kc + 16 < ep.rank;
             float uf[2][8];
             v8bf wh[TN][2], wl[TN][2];
