@@ -127,7 +127,7 @@ def test_low_rank(rank, xd, gemm):
 
 @pytest.mark.parametrize("T,d_in,rank,xd", [(130, 2048, 32, "bf16"), (300, 3072, 32, "bf16"),
                                          (77, 1152, 16, "f32"), (129, 1024, 64, "f32"),
-                                         (1, 512, 48, "bf16")])
+                                         (1, 512, 48, "bf16"), (200, 1024, 16, "bf16")])
 def test_low_rank_split_matches_one_pass(T, d_in, rank, xd):
     # quant_linear forms U in two passes over slices of d_in (workspace for the
     # slice products); act_quantize has no workspace and runs the one-pass
