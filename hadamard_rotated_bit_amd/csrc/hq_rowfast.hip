@@ -5,8 +5,8 @@
 // general kernel in hq_act.hip.)
 //
 // Same arithmetic per row as the general kernel (HadaNorm Eq. (1) activation
-// side, HaTQ Sec. III-A Eq. (3) quantiser), with three differences in how the
-// lanes carry it out:
+// side, HaTQ Sec. III-A Eq. (3) quantiser), with these differences in how
+// the lanes carry it out:
 //  * Cross-lane butterflies are one v_fmac_f32_dpp each where a DPP pattern
 //    reaches the partner (v += g * v[partner], g = +1 on the lower and -1 on
 //    the upper lane of a pair): lane ^ 1 and lane ^ 2 (quad permutes),
@@ -33,6 +33,8 @@
 //  * The row sum (for the mean, and c for weights) is taken from the closed
 //    form B * sum of the blocks' first inputs instead of summing every
 //    output.
+//  * The per-channel multipliers and means are staged once per block in LDS
+//    (template mode P: none, multipliers, multipliers and means).
 #include "hq_device.h"
 #include "hq_internal.h"
 
