@@ -120,11 +120,15 @@ def test_output_with_oracle_codes_is_tight(ec):
     s_x = torch.from_numpy(o["s_x"].astype(np.float32)).cuda()
     mu = torch.from_numpy(o["mu"].astype(np.float32)).cuda()
     U = None if o["u"] is None else torch.from_numpy(o["u"].astype(np.float32)).cuda()
-    # substitute the oracle's weight codes too, so only the epilogue differs
-    v = hq.prepared_views(c.desc, c.prep)
-    if not np.array_equal(codes_np(c.desc, v["w_codes"], c.desc.d_out), o["qw"]):
-        pytest.skip("weight codes differ at a tie; the end-to-end test covers this case")
-    Y = hq.gemm_dequant(c.desc, c.prep, codes, s_x, mu, U)
+    # substitute the oracle's weight codes too (in a copy of the blob), so
+    # only the epilogue differs even where a weight code sits at a tie
+    prep = c.prep.clone()
+    L = hq.layout(c.desc)
+    wc = codes_dev(c.desc, o["qw"])
+    prep[L.w_codes:L.w_codes + wc.numel()].copy_(wc)
+    assert np.array_equal(codes_np(c.desc, hq.prepared_views(c.desc, prep)["w_codes"],
+                                   c.desc.d_out), o["qw"])
+    Y = hq.gemm_dequant(c.desc, prep, codes, s_x, mu, U)
     y_ref = o["y_full"]
     tol = 2e-6 if c.w.out_dtype == "f32" else 8e-3
     err = np.abs(to_np(Y) - y_ref).max() / np.abs(y_ref).max()
