@@ -1,20 +1,28 @@
 #!/usr/bin/env python3
-"""Benchmark of the rotated-and-centred W4A4 quantised linear on one MI355X.
+"""Benchmark of the rotated-and-centred low-bit linear layer on one MI355X.
 
-One step = one hq_quant_linear call (activation kernel + integer-exact GEMM
-with the dequant epilogue; E2M3 / FP6 MFMA for 4-bit codes, the same layer on
-the int8 MFMA engine is reported alongside) over one synthetic batch already
-resident in HBM. Inputs
-rotate through enough distinct X/Y buffers (> 512 MB) that a step's
+One step = one hq_quant_linear call (the activation kernel, then the
+integer-exact GEMM with the dequant epilogue; E2M3 / FP6 MFMA for 4-bit
+codes, int8 MFMA for 8-bit codes) over one synthetic batch already resident
+in HBM. The headline is the FLUX-scale joint-attention projection (4608 x
+3072 -> 12288 bf16, three 1024-point blocks, per-token centring, W4A4 with
+the rank-32 branch); the other workloads (the toy layer, the DiT MLP fc1,
+the square 4096 projection with centring on and off, the learned-image-coding
+double-Hadamard W8A8 layer) get one object each in the same JSON line.
+
+Inputs rotate through enough distinct X / Y buffers (> 512 MB) that a step's
 activations are not served from the 256 MB Infinity Cache left over from the
-previous visit. Prints one JSON line.
+previous visit. Per-kernel times come from HIP events around back-to-back
+launches of each stage entry point (captured in a HIP graph, replayed on the
+stream the events are recorded on). Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dit_fc1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flux_proj]
 """
 from __future__ import annotations
 
 import argparse
 import dataclasses
+import hashlib
 import json
 import math
 import os
@@ -34,6 +42,7 @@ FP6_PEAK_TOPS = 10100.0        # MI355X dense fp6 / fp4 MFMA (10.1 PFLOP/s)
 # lanes x 2.4 GHz (a wave64 instruction issues over 4 cycles); the 157.3
 # TFLOP/s vector figure counts packed fp32 fma, which this build does not emit.
 VALU_F32_LANE_OPS = 256 * 4 * 16 * 2.4e9
+CONFIG_ORDER = ["tiny", "dit_fc1", "square4k", "lic_dh", "flux_proj"]
 
 
 def parse():
@@ -41,139 +50,418 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dit_fc1")
+    ap.add_argument("--workload", default="flux_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="measure the headline workload only, on both engines (no group-wise, "
-                         "weight-only Hadamard or centring objects), e.g. for clean profiles")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="measure the headline workload only (both engines), e.g. for clean "
+                         "profiles: no other configs, group-wise, integer-layer or centring objects")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="host only: turn the FETCH_SIZE / WRITE_SIZE counter runs in DIR "
-                         "(rocprofv3 -o fetch / -o write, csv) into the committed traffic record "
-                         "of the dit_fc1 GEMM, then exit")
+                         "(rocprofv3 -o fetch / -o write, csv) of the --workload run into the "
+                         "committed traffic record of its GEMM, then exit")
     return ap.parse_args()
 
 
-def cpu_baseline(w, x, weight, bias, sigma, l1, l2, target_s):
-    """Time the CPU oracle's online half (transform, centre, quantise, integer GEMM,
-    dequantise) on a bounded prefix of the workload's tokens; weight prep excluded."""
+def host_cores() -> int:
+    return len(os.sched_getaffinity(0))
+
+
+def sha256_arrays(**arrays) -> dict:
+    out = {}
+    for k, a in arrays.items():
+        if a is not None:
+            out[k] = hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+    return out
+
+
+def cpu_baseline(w, x, weight, bias, sigma, l1, l2, Y_gpu, target_s):
+    """The CPU oracle's online half (transform, centre, quantise, integer GEMM,
+    dequantise; weight preparation done once beforehand and not timed) on a
+    bounded prefix of the workload's tokens, with NumPy's BLAS on every host
+    core. The same rows of the GPU output are compared with the oracle's
+    (relative Frobenius error) as the run's parity statistic."""
     from oracle import hq_oracle as O
     import threadpoolctl
-    sig = np.ones(w.d_in) if sigma is None else sigma.astype(np.float64)
-    prep = O.prepare_weights(weight, sig, w.block, w.w_bits)
-    rows = min(w.T, 256)
-    t0 = time.perf_counter()
-    O.quant_linear(x[:rows], prep, bias, sig, block=w.block, a_bits=w.a_bits,
-                   center=int(w.center), l1=l1, l2=l2, out_dtype=w.out_dtype)
-    dt = time.perf_counter() - t0
-    if dt < target_s and rows < w.T:
-        rows = int(min(w.T, max(rows, rows * target_s / max(dt, 1e-3))))
-        t0 = time.perf_counter()
-        O.quant_linear(x[:rows], prep, bias, sig, block=w.block, a_bits=w.a_bits,
-                       center=int(w.center), l1=l1, l2=l2, out_dtype=w.out_dtype)
-        dt = time.perf_counter() - t0
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info] + [1])
+    cores = host_cores()
+    with threadpoolctl.threadpool_limits(limits=cores):
+        sig = np.ones(w.d_in) if sigma is None else sigma.astype(np.float64)
+        prep = O.prepare_weights(weight, sig, w.block, w.w_bits)
+        rows = min(w.T, 128)
+
+        def run(n):
+            t0 = time.perf_counter()
+            r = O.quant_linear(x[:n], prep, bias, sig, block=w.block, a_bits=w.a_bits,
+                               center=int(w.center), l1=None if l1 is None else l1,
+                               l2=l2, out_dtype=w.out_dtype)
+            return r, time.perf_counter() - t0
+
+        r, dt = run(rows)
+        if dt < target_s and rows < w.T:
+            rows = int(min(w.T, max(rows, rows * target_s / max(dt, 1e-3))))
+            r, dt = run(rows)
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
+    y = Y_gpu[:rows].float().cpu().numpy().astype(np.float64)
+    ref = r["y_out"]
+    err = float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
     return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "blas_threads": int(threads),
             "sample": f"first {rows} of {w.T} tokens of {w.name}, float64 NumPy oracle "
-                      f"(online half, prepared weights reused), {dt:.2f} s"}
+                      f"(online half, prepared weights reused), {dt:.2f} s",
+            "parity_rel_fro_vs_gpu": err, "parity_rows": rows}
 
 
-def measure(hq, torch, desc, w, Xs, Ys, S, W, B, L1, L2, steps, warmup, dev):
-    """Times `steps` quant_linear calls after `warmup`, then each of the two
-    kernels alone (stage entry points, captured back to back in a HIP graph
-    so the per-kernel time carries no host launch gaps)."""
-    nbuf = len(Xs)
-    tdt = Xs[0].dtype
-    prep = hq.prepare(desc, W, B, S, L1, L2)
+def timed_steps(torch, fn, nbuf, steps, warmup):
+    for i in range(warmup):
+        fn(i % nbuf)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        fn((warmup + i) % nbuf)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+
+
+def graph_time(torch, fn, n):
+    """Average time of fn(i), i < n, captured back to back in one HIP graph
+    and replayed on the current stream, timed with HIP events on that stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / n
+
+
+class Layer:
+    """One workload on the GPU: inputs, the prepared blob, rotating buffers."""
+
+    def __init__(self, hq, torch, WL, w, dev, gemm=None, center=None):
+        self.w = w
+        dt = hq.BF16 if w.dtype == "bf16" else hq.F32
+        self.tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.x = WL.gen_x(w)
+        self.weight, self.bias = WL.gen_weight(w), WL.gen_bias(w)
+        self.l1, self.l2 = WL.gen_lowrank(w)
+        self.X0 = torch.from_numpy(self.x).to(dev).to(self.tdt)
+        self.W = torch.from_numpy(self.weight).to(dev).to(self.tdt)
+        self.B = torch.from_numpy(self.bias).to(dev)
+        self.L1 = None if self.l1 is None else torch.from_numpy(self.l1).to(dev).to(self.tdt)
+        self.L2 = None if self.l2 is None else torch.from_numpy(self.l2).to(dev).to(self.tdt)
+        self.desc = hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits,
+                            int(w.center if center is None else center), w.alpha is not None,
+                            w.rank, dt, dt, dt, hq.HQ_GEMM_AUTO if gemm is None else gemm)
+        self.S = None
+        if w.alpha is not None:   # offline calibration on the workload's own tokens
+            self.S = hq.sigma(self.desc, hq.channel_absmax(self.desc, self.X0), self.W, w.alpha)
+        xbytes = self.X0.numel() * self.X0.element_size()
+        self.nbuf = max(2, math.ceil(512e6 / xbytes))
+        self.Xs = [self.X0] + [self.X0.clone() for _ in range(self.nbuf - 1)]
+        self.Ys = [torch.empty(w.T, w.d_out, dtype=self.tdt, device=dev)
+                   for _ in range(self.nbuf)]
+        self.dev = dev
+
+    def sha(self):
+        return sha256_arrays(x=self.x, weight=self.weight, bias=self.bias, l1=self.l1, l2=self.l2)
+
+    def free(self):
+        del self.Xs, self.Ys
+
+
+def measure(hq, torch, L, desc, steps, warmup):
+    """Times `steps` quant_linear calls after `warmup` (the step), then each
+    stage kernel alone: the activation stage (hq_act_quantize with the same
+    kernels quant_linear runs) and the GEMM + epilogue (hq_gemm_dequant)."""
+    w, dev = L.w, L.dev
+    prep = hq.prepare(desc, L.W, L.B, L.S, L.L1, L.L2)
     ws = torch.empty(hq.workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
     codes = torch.empty(hq.code_bytes(desc, w.T), dtype=torch.uint8, device=dev)
     s_x = torch.empty(desc.sx_shape(w.T), dtype=torch.float32, device=dev)
     mu = torch.empty(w.T, dtype=torch.float32, device=dev)
     U = torch.empty(w.T, w.rank, dtype=torch.float32, device=dev) if w.rank else None
+    nbuf = L.nbuf
 
     def step(i):
-        hq.quant_linear(desc, prep, Xs[i % nbuf], out=Ys[i % nbuf], workspace=ws)
+        hq.quant_linear(desc, prep, L.Xs[i], out=L.Ys[i], workspace=ws)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for i in range(steps):
-        step(warmup + i)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / steps
+    ms, wall = timed_steps(torch, step, nbuf, steps, warmup)
+    n = max(1, min(steps, 20))
+    if int(desc.center) == hq.HQ_CENTER_CHANNEL:
+        # per-channel centring: the statistics stage (column means and the
+        # corrected bias) is timed with the activation stage
+        mean, bias_eff = hq.channel_center(desc, prep, L.Xs[0], workspace=ws)
 
-    # Per-kernel durations on the stream the kernels run on.
-    n = min(steps, 20)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        hq.act_quantize(desc, prep, Xs[0], out=(codes, s_x, mu, U))      # warm
-        hq.gemm_dequant(desc, prep, codes, s_x, mu, U, out=Ys[0])
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g1):
-        for i in range(n):
-            hq.act_quantize(desc, prep, Xs[i % nbuf], out=(codes, s_x, mu, U))
-    with torch.cuda.graph(g2):
-        for i in range(n):
-            hq.gemm_dequant(desc, prep, codes, s_x, mu, U, out=Ys[i % nbuf])
-    times = []
-    for g in (g1, g2):
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / n)
-    del g1, g2
-    return {"ms": ms, "wall": wall, "k1": times[0], "k2": times[1], "prep": prep}
+        def act(i):
+            hq.channel_center_into(desc, prep, L.Xs[i % nbuf], mean, bias_eff, ws)
+            hq.act_quantize(desc, prep, L.Xs[i % nbuf], out=(codes, s_x, mu, U), mean=mean)
+        k1 = graph_time(torch, act, n)
+        k2 = graph_time(torch, lambda i: hq.gemm_dequant(desc, prep, codes, s_x, bias_eff, U,
+                                                         out=L.Ys[i % nbuf]), n)
+    else:
+        k1 = graph_time(torch, lambda i: hq.act_quantize(desc, prep, L.Xs[i % nbuf],
+                                                         out=(codes, s_x, mu, U)), n)
+        k2 = graph_time(torch, lambda i: hq.gemm_dequant(desc, prep, codes, s_x, mu, U,
+                                                         out=L.Ys[i % nbuf]), n)
+    return {"ms": ms, "wall": wall, "k1": k1, "k2": k2, "prep": prep}
+
+
+def kernel_figures(hq, desc, w, r):
+    """Algorithmic work of each kernel and the rates it reached.
+
+    K1 (activation stage) bytes per call: read X, write the codes in the
+    descriptor's format, s_x and mu (4 B per token each) and U (4 r B per
+    token), read 1/sigma and (rank > 0) the two bf16 halves of L1 once; the
+    4-bit minimum (0.5 B per code) is reported beside it. K2 (GEMM +
+    epilogue) ops = 2 T d_in d_out code multiply-adds; bytes = both code
+    matrices, the per-row and per-column vectors, U and L2 (rank > 0) and Y."""
+    in_b = 2 if w.dtype == "bf16" else 4
+    out_b = in_b
+    fp6 = hq.code_format(desc) == hq.HQ_CODES_E2M3
+    code_b = hq.code_bytes(desc, w.T)
+    k1_bytes = (w.T * (w.d_in * in_b + 8 + 4 * w.rank) + code_b + 4 * w.d_in
+                + 4 * w.rank * w.d_in)
+    k1_min = w.T * (w.d_in * in_b + 8 + 4 * w.rank) + w.T * w.d_in * w.a_bits // 8
+    k2_ops = 2.0 * w.T * w.d_in * w.d_out
+    k2_bytes = (code_b + hq.code_bytes(desc, w.d_out) + 8 * w.T + 12 * w.d_out
+                + 4 * w.rank * w.T + 4 * w.rank * w.d_out + out_b * w.T * w.d_out)
+    peak = FP6_PEAK_TOPS if fp6 else INT8_PEAK_TOPS
+    k1_gbs = k1_bytes / (r["k1"] * 1e-3) / 1e9
+    k2_tops = k2_ops / (r["k2"] * 1e-3) / 1e12
+    k2_gbs = k2_bytes / (r["k2"] * 1e-3) / 1e9
+    return {
+        "engine": "e2m3 fp6 mfma" if fp6 else "int8 mfma",
+        "value": round(w.T / (r["ms"] * 1e-3), 1), "unit": "tokens/s",
+        "ms_per_step": round(r["ms"], 5),
+        "effective_TOPS_step": round(k2_ops / (r["ms"] * 1e-3) / 1e12, 2),
+        "k1": {"ms": round(r["k1"], 5), "bytes": int(k1_bytes), "GBs": round(k1_gbs, 1),
+               "hbm_frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+               "bytes_4bit_min": int(k1_min),
+               "hbm_frac_4bit_min": round(k1_min / (r["k1"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "k2": {"ms": round(r["k2"], 5), "ops": k2_ops, "TOPS": round(k2_tops, 2),
+               "peak_TOPS": peak, "mfma_frac": round(k2_tops / peak, 4),
+               "bytes": int(k2_bytes), "GBs": round(k2_gbs, 1),
+               "hbm_frac": round(k2_gbs / HBM_PEAK_GBS, 4)},
+    }
+
+
+def diagnostics(hq, torch, L, desc, prep):
+    """Not gates: output SQNR (HaTQ Sec. IV-A Eq. (10)) of the method and of
+    the same quantiser without any transform (sigma = 1, no rotation, no
+    centring) against the unquantised layer in float32, and the excess
+    kurtosis (Eq. (9)) of X and of X~ over all entries."""
+    w = L.w
+    X = L.X0
+    ref = torch.addmm(L.B, X.float(), L.W.float().t())
+    if L.L1 is not None:
+        xs = X.float() if L.S is None else X.float() / L.S
+        ref = ref + (xs @ L.L1.float()) @ L.L2.float()
+
+    def sqnr(Y):
+        e = (Y.float() - ref).pow(2).sum().item()
+        return round(10.0 * math.log10(ref.pow(2).sum().item() / max(e, 1e-300)), 2)
+
+    Y = hq.quant_linear(desc, prep, X)
+    # the same quantiser on X W + b alone: no smoothing, no rotation, no
+    # centring and no low-rank branch (its reference leaves the branch out)
+    plain = dataclasses.replace(desc, block=1, smooth=False, center=hq.HQ_CENTER_NONE, rank=0)
+    pp = hq.prepare(plain, L.W, L.B)
+    Y0 = hq.quant_linear(plain, pp, X)
+    ref0 = torch.addmm(L.B, X.float(), L.W.float().t())
+    e0 = (Y0.float() - ref0).pow(2).sum().item()
+    sq = {"method": sqnr(Y),
+          "no_transform": round(10.0 * math.log10(ref0.pow(2).sum().item() / max(e0, 1e-300)), 2)}
+    del pp, Y0, ref0
+
+    def kurt(v):
+        v = v.double().flatten()
+        d = v - v.mean()
+        return round((d.pow(4).mean() / d.pow(2).mean().pow(2) - 3.0).item(), 3)
+
+    xt, _ = hq.act_transform(desc, prep, X)
+    k = {"x": kurt(X.float()), "x_tilde": kurt(xt)}
+    del xt
+    return Y, sq, k
+
+
+def config_object(hq, torch, WL, name, steps, warmup, dev, both_engines=True):
+    """Every figure for one workload; returns (object, Layer, measurement)."""
+    w = WL.WORKLOADS[name]
+    L = Layer(hq, torch, WL, w, dev)
+    r = measure(hq, torch, L, L.desc, steps, warmup)
+    obj = {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
+           "block": w.block, "bits": f"W{w.w_bits}A{w.a_bits}", "center": int(w.center),
+           "smooth_alpha": w.alpha, "rank": w.rank, "io_dtype": w.dtype}
+    obj.update(kernel_figures(hq, L.desc, w, r))
+    Y, obj["sqnr_db"], obj["kurtosis"] = diagnostics(hq, torch, L, L.desc, r["prep"])
+    obj["input_sha256"] = L.sha()
+    if both_engines and hq.code_format(L.desc) == hq.HQ_CODES_E2M3:
+        # the same layer on the int8 engine (int4 codes in int8 lanes, int32
+        # accumulation): identical accumulators, measured against the int8 peak
+        d8 = dataclasses.replace(L.desc, gemm=hq.HQ_GEMM_I8)
+        r8 = measure(hq, torch, L, d8, steps, warmup)
+        obj["int8_engine"] = kernel_figures(hq, d8, w, r8)
+        del r8
+    return obj, L, r, Y
+
+
+def centring_off(hq, torch, L, r_on, steps, warmup):
+    """The square projection run again with centring off (HadaNorm's centring
+    is the difference), and the centring overhead per kernel and per step."""
+    d0 = dataclasses.replace(L.desc, center=hq.HQ_CENTER_NONE)
+    r0 = measure(hq, torch, L, d0, steps, warmup)
+    obj = kernel_figures(hq, d0, L.w, r0)
+    Y, obj["sqnr_db"], obj["kurtosis"] = diagnostics(hq, torch, L, d0, r0["prep"])
+    del Y
+    over = {"k1_ms": round(r_on["k1"] - r0["k1"], 5), "k2_ms": round(r_on["k2"] - r0["k2"], 5),
+            "step_ms": round(r_on["ms"] - r0["ms"], 5)}
+    return obj, over
+
+
+def centring_modes(hq, torch, L, steps, warmup):
+    """square4k under per-channel centring (mu one vector over channels, b~
+    one corrected bias): time per call and output SQNR."""
+    d2 = dataclasses.replace(L.desc, center=hq.HQ_CENTER_CHANNEL)
+    r2 = measure(hq, torch, L, d2, steps, warmup)
+    Y, sq, k = diagnostics(hq, torch, L, d2, r2["prep"])
+    del Y
+    return {"value": round(L.w.T / (r2["ms"] * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(r2["ms"], 5), "sqnr_db": sq}
+
+
+def group_wise(hq, torch, WL, steps, warmup, dev):
+    """flux_g64 (group-wise scales, 64-point blocks, rank 32): time per call and
+    per kernel, and the output SQNR with group-wise and with per-row scales on
+    the same rotation. The group GEMM rescales every 64-channel partial product
+    on the VALU (one multiply and one fma per output element and group); its
+    floor is that work at the chip's non-packed fp32 rate."""
+    w = WL.WORKLOADS["flux_g64"]
+    L = Layer(hq, torch, WL, w, dev)
+    desc = dataclasses.replace(L.desc, group=w.group)
+    r = measure(hq, torch, L, desc, steps, warmup)
+    ops = 2.0 * w.T * w.d_in * w.d_out
+    valu_floor_ms = 2.0 * w.T * w.d_out * (w.d_in // w.group) / VALU_F32_LANE_OPS * 1e3
+    sq = {}
+    _, sq["group64"], _ = diagnostics(hq, torch, L, desc, r["prep"])
+    d0 = dataclasses.replace(desc, group=0)
+    _, sq["per_row"], _ = diagnostics(hq, torch, L, d0, hq.prepare(d0, L.W, L.B, None, L.L1, L.L2))
+    L.free()
+    return {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
+            "block": w.block, "group": w.group, "rank": w.rank, "bits": "W4A4",
+            "io_dtype": "bf16", "value": round(w.T / (r["ms"] * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(r["ms"], 5), "row_transform_ms": round(r["k1"], 5),
+            "gemm_ms": round(r["k2"], 5), "gemm_TOPS": round(ops / (r["k2"] * 1e-3) / 1e12, 2),
+            "gemm_mfma_frac": round(ops / (r["k2"] * 1e-3) / 1e12 / FP6_PEAK_TOPS, 4),
+            "gemm_valu_floor_ms": round(valu_floor_ms, 5),
+            "gemm_valu_frac": round(valu_floor_ms / r["k2"], 4),
+            "sqnr_db": {k: v["method"] for k, v in sq.items()}}
+
+
+def integer_layer(hq, torch, WL, steps, warmup, dev, side):
+    """lic_wh as an integer-only layer with integer requantisation (int8
+    codes in, int8 codes out): the weight-only Hadamard layer (H_256 on the
+    output channels, output in the original basis) or the double-Hadamard
+    layer (input in the H_256 basis of the previous DH layer, output moved to
+    the next one's H_256 basis). Time per call and the output SQNR of the int8
+    codes against the float32 layer in the same basis. The input codes are
+    the workload's X (rotated for DH) on a per-tensor grid (synthetic input)."""
+    w = WL.WORKLOADS["lic_wh"]
+    X = torch.from_numpy(WL.gen_x(w)).to(dev)
+    W = torch.from_numpy(WL.gen_weight(w)).to(dev)
+    B = torch.from_numpy(WL.gen_bias(w)).to(dev)
+    ref = torch.addmm(B, X, W.t())
+    wh = side == hq.HQ_INT_WH
+    if not wh:
+        # orthonormal Sylvester H_256: the DH input and output bases
+        H = torch.ones(1, 1, dtype=torch.float64)
+        while H.shape[0] < w.block:
+            H = torch.cat([torch.cat([H, H], 1), torch.cat([H, -H], 1)], 0)
+        H = (H / math.sqrt(w.block)).to(dev)
+
+        def rot(a):
+            return (a.double().reshape(a.shape[0], -1, w.block) @ H).reshape(a.shape).float()
+        X, ref = rot(X), rot(ref)
+    s_x = float(X.abs().max().item() / 127.0)
+    s_y = float(ref.abs().max().item() / 127.0)
+    X0 = torch.clamp(torch.round(X / s_x), -127, 127).to(torch.int8)
+    desc = hq.IntDesc(w.d_in, w.d_out, w.block, hq.F32, side, 1 if wh else w.block)
+    prep = hq.int_prepare(desc, W, B, s_x, s_y)
+    nbuf = max(2, math.ceil(512e6 / X0.numel()))
+    Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
+    Ys = [torch.empty(w.T, w.d_out, dtype=torch.int8, device=dev) for _ in range(nbuf)]
+    ws = torch.empty(hq.int_workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
+    ms, _ = timed_steps(torch, lambda i: hq.int_linear(desc, prep, Xs[i], out=Ys[i], workspace=ws),
+                        nbuf, steps, warmup)
+    y = Ys[(warmup + steps - 1) % nbuf].float() * s_y
+    sq = 10.0 * math.log10(ref.pow(2).sum().item() / max((y - ref).pow(2).sum().item(), 1e-300))
+    del Xs, Ys
+    # bytes that must move: int8 codes in and out, weight codes, constants
+    algo = w.T * (w.d_in + w.d_out) + w.d_out * (w.d_in + 12)
+    return {"workload": w.name, "layer": "WH" if wh else "DH-to-DH", "tokens": w.T,
+            "d_in": w.d_in, "d_out": w.d_out, "block": w.block, "bits": "W8A8 int8 -> int8",
+            "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 5), "algorithmic_GBs": round(algo / (ms * 1e-3) / 1e9, 1),
+            "sqnr_db": round(sq, 2)}
+
+
+# ---- traffic records (rocprofv3 FETCH_SIZE / WRITE_SIZE) -------------------
+
+GEMM_SOURCES = ["hadamard_rotated_bit_amd/csrc/hq_gemm6_kernel.h",
+                "hadamard_rotated_bit_amd/csrc/hq_gemm_kernel.h",
+                "hadamard_rotated_bit_amd/csrc/hq_gemm6.hip",
+                "hadamard_rotated_bit_amd/csrc/hq_gemm.hip",
+                "hadamard_rotated_bit_amd/csrc/hq_device.h",
+                "hadamard_rotated_bit_amd/csrc/hq_gemm_types.h"]
+
+
+def sources_sha(srcs) -> str:
+    h = hashlib.sha256()
+    for src in srcs:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed counter summary of this kernel and
-    workload (profiles/<kernel>_<workload>_traffic.json), or None when there is
-    none or the kernel sources changed since the counters were taken."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel.replace('_dequant', '')}_{workload}_traffic.json")
+    """HBM bytes per launch from the committed counter record of this kernel
+    and workload (profiles/<kernel>_<workload>_traffic.json), or None when
+    there is none or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    h = hashlib.sha256()
-    for src in rec["sources"]:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            h.update(f.read())
-    if h.hexdigest() != rec["sources_sha256"] or rec["kernel"] != kernel:
+    if rec.get("kernel") != kernel or sources_sha(rec["sources"]) != rec["sources_sha256"]:
         return None
     return int(round(rec["traffic_bytes_per_launch"]))
 
 
-TRAFFIC_SOURCES = ["hadamard_rotated_bit_amd/csrc/hq_gemm6_kernel.h",
-                   "hadamard_rotated_bit_amd/csrc/hq_gemm_kernel.h",
-                   "hadamard_rotated_bit_amd/csrc/hq_gemm6.hip",
-                   "hadamard_rotated_bit_amd/csrc/hq_device.h",
-                   "hadamard_rotated_bit_amd/csrc/hq_gemm_types.h"]
-COPY_BYTES = 18874368   # one clone of dit_fc1's X (8192 x 1152 bf16): the plain copy kernel
-
-
-def write_traffic(d):
-    """Per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of the FP6 GEMM from two
-    counter runs of this benchmark, each scaled by what the counter reads for
-    the run's plain copy kernel of known size, into
-    profiles/gemm_f6_dit_fc1_traffic.json with the hash of the GEMM sources."""
+def write_traffic(d, workload):
+    """Per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of the GEMM from two counter
+    runs of this benchmark on `workload`, each scaled by what the counter reads
+    for the run's plain copy kernel of known size (a clone of X), into
+    profiles/gemm_f6_<workload>_traffic.json with the hash of the GEMM sources."""
     import csv
-    import hashlib
     from collections import defaultdict
+    from hadamard_rotated_bit_amd import workloads as WL
+    w = WL.WORKLOADS[workload]
+    copy_bytes = w.T * w.d_in * (2 if w.dtype == "bf16" else 4)
 
     def per_kernel(f, counter):
         acc = defaultdict(list)
@@ -193,184 +481,34 @@ def write_traffic(d):
     wr = per_kernel(os.path.join(d, "write_counter_collection.csv"), "WRITE_SIZE")
     cf, _ = pick(fe, "__amd_rocclr_copyBuffer")
     cw, _ = pick(wr, "__amd_rocclr_copyBuffer")
-    fs, ws = COPY_BYTES / 1024 / cf, COPY_BYTES / 1024 / cw
-    print(f"copy kernel: FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB -> scales {fs:.4f}, {ws:.4f}")
-    for key in ["gemm_f6_persist", "gemm_i8_kernel", "row_fast_kernel"]:
+    fs, ws = copy_bytes / 1024 / cf, copy_bytes / 1024 / cw
+    print(f"copy kernel ({copy_bytes} bytes): FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB "
+          f"-> scales {fs:.4f}, {ws:.4f}")
+    names = sorted({k for k in fe if "copyBuffer" not in k})
+    for key in names:
         f, n = pick(fe, key)
-        w, n2 = pick(wr, key)
-        print(f"| `{key}` | {f:.1f} | {w:.1f} | {f * fs * 1024 / 1e6:.1f} MB | "
-              f"{w * ws * 1024 / 1e6:.1f} MB | {(f * fs + w * ws) * 1024 / 1e6:.1f} MB | {n}, {n2} dispatches")
+        wv, n2 = pick(wr, key)
+        print(f"| `{key[:60]}` | {f:.1f} | {wv:.1f} | {f * fs * 1024 / 1e6:.1f} MB | "
+              f"{wv * ws * 1024 / 1e6:.1f} MB | {(f * fs + wv * ws) * 1024 / 1e6:.1f} MB | "
+              f"{n}, {n2} dispatches")
     f, _ = pick(fe, "gemm_f6_persist")
-    w, _ = pick(wr, "gemm_f6_persist")
-    h = hashlib.sha256()
-    for src in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, src), "rb") as fh:
-            h.update(fh.read())
-    rec = {"kernel": "gemm_f6_dequant", "workload": "dit_fc1", "sources": TRAFFIC_SOURCES,
-           "sources_sha256": h.hexdigest(), "fetch_kib_per_dispatch": f,
-           "write_kib_per_dispatch": w,
-           "copy_kernel": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+    wv, _ = pick(wr, "gemm_f6_persist")
+    rec = {"kernel": "gemm_f6_dequant", "workload": workload, "sources": GEMM_SOURCES,
+           "sources_sha256": sources_sha(GEMM_SOURCES), "fetch_kib_per_dispatch": f,
+           "write_kib_per_dispatch": wv,
+           "copy_kernel": {"bytes": copy_bytes, "fetch_kib": cf, "write_kib": cw,
                            "fetch_scale": fs, "write_scale": ws},
-           "traffic_bytes_per_launch": (f * fs + w * ws) * 1024}
-    with open(os.path.join(ROOT, "profiles", "gemm_f6_dit_fc1_traffic.json"), "w") as fh:
+           "traffic_bytes_per_launch": (f * fs + wv * ws) * 1024}
+    out = os.path.join(ROOT, "profiles", f"gemm_f6_dequant_{workload}_traffic.json")
+    with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
-    print(f"traffic per launch: {rec['traffic_bytes_per_launch'] / 1e6:.1f} MB")
-
-
-def kernel_report(hq, desc, w, r):
-    in_b = 2 if w.dtype == "bf16" else 4
-    fp6 = hq.code_format(desc) == hq.HQ_CODES_E2M3
-    # read X, write codes, s_x, mu, U
-    k1_bytes = w.T * (w.d_in * in_b + 8 + 4 * w.rank) + hq.code_bytes(desc, w.T)
-    k2_ops = 2.0 * w.T * w.d_in * w.d_out                          # code multiply-adds x 2
-    peak = FP6_PEAK_TOPS if fp6 else INT8_PEAK_TOPS
-    k1_gbs = k1_bytes / (r["k1"] * 1e-3) / 1e9
-    k2_tops = k2_ops / (r["k2"] * 1e-3) / 1e12
-    return fp6, peak, k1_gbs, k2_tops, k2_ops
-
-
-def centring_modes(hq, torch, WL, steps, warmup, dev):
-    """square4k (channels with different means) under per-token and per-channel
-    centring: time per quant_linear call and the output SQNR against the
-    float32 layer X W + b (HaTQ Sec. IV-A Eq. (10))."""
-    w = WL.WORKLOADS["square4k"]
-    x = WL.gen_x(w)
-    X0 = torch.from_numpy(x).to(dev).to(torch.bfloat16)
-    W = torch.from_numpy(WL.gen_weight(w)).to(dev).to(torch.bfloat16)
-    B = torch.from_numpy(WL.gen_bias(w)).to(dev)
-    nbuf = max(2, math.ceil(512e6 / (X0.numel() * 2)))
-    Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
-    Y = torch.empty(w.T, w.d_out, dtype=torch.bfloat16, device=dev)
-    ref = torch.addmm(B, X0.float(), W.float().t())
-    out = {"workload": "square4k", "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
-           "block": w.block, "bits": "W4A4", "io_dtype": "bf16"}
-    for mode, key in ((hq.HQ_CENTER_TOKEN, "per_token"), (hq.HQ_CENTER_CHANNEL, "per_channel")):
-        desc = hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, mode, False, 0,
-                       hq.BF16, hq.BF16, hq.BF16)
-        prep = hq.prepare(desc, W, B)
-        ws = torch.empty(hq.workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
-        for i in range(warmup):
-            hq.quant_linear(desc, prep, Xs[i % nbuf], out=Y, workspace=ws)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(steps):
-            hq.quant_linear(desc, prep, Xs[(warmup + i) % nbuf], out=Y, workspace=ws)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        hq.quant_linear(desc, prep, X0, out=Y, workspace=ws)
-        err = (Y.float() - ref).pow(2).sum().item()
-        sqnr = 10.0 * math.log10(ref.pow(2).sum().item() / max(err, 1e-300))
-        out[key] = {"value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s",
-                    "ms_per_step": round(ms, 5), "sqnr_db": round(sqnr, 2)}
-    return out
-
-
-def group_wise(hq, torch, WL, steps, warmup, dev):
-    """flux_g64 (group-wise scales, 64-point blocks, rank 32): time per call and
-    per kernel, and the output SQNR against the float32 layer
-    X W + b + (X L1) L2 with group-wise and with per-row scales on the same
-    rotation. The group GEMM rescales every 64-channel partial product on the
-    VALU (one multiply and one fma per output element and group); its floor is
-    that work at the chip's non-packed fp32 rate."""
-    w = WL.WORKLOADS["flux_g64"]
-    x = WL.gen_x(w)
-    l1, l2 = WL.gen_lowrank(w)
-    X0 = torch.from_numpy(x).to(dev).to(torch.bfloat16)
-    W = torch.from_numpy(WL.gen_weight(w)).to(dev).to(torch.bfloat16)
-    B = torch.from_numpy(WL.gen_bias(w)).to(dev)
-    L1 = torch.from_numpy(l1).to(dev).to(torch.bfloat16)
-    L2 = torch.from_numpy(l2).to(dev).to(torch.bfloat16)
-    nbuf = max(2, math.ceil(512e6 / (X0.numel() * 2)))
-    Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
-    Ys = [torch.empty(w.T, w.d_out, dtype=torch.bfloat16, device=dev) for _ in range(nbuf)]
-    desc = hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, int(w.center), False, w.rank,
-                   hq.BF16, hq.BF16, hq.BF16, group=w.group)
-    r = measure(hq, torch, desc, w, Xs, Ys, None, W, B, L1, L2, steps, warmup, dev)
-    del Xs, Ys
-    ops = 2.0 * w.T * w.d_in * w.d_out
-    valu_lane_ops = 2.0 * w.T * w.d_out * (w.d_in // w.group)
-    valu_floor_ms = valu_lane_ops / VALU_F32_LANE_OPS * 1e3
-    ref = torch.addmm(B, X0.float(), W.float().t()) + (X0.float() @ L1.float()) @ L2.float()
-    sq = {}
-    for key, g in (("group64", w.group), ("per_row", 0)):
-        d = dataclasses.replace(desc, group=g)
-        Y = hq.quant_linear(d, r["prep"] if g else hq.prepare(d, W, B, None, L1, L2), X0)
-        err = (Y.float() - ref).pow(2).sum().item()
-        sq[key] = round(10.0 * math.log10(ref.pow(2).sum().item() / max(err, 1e-300)), 2)
-        del Y
-    return {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
-            "block": w.block, "group": w.group, "rank": w.rank, "bits": "W4A4",
-            "io_dtype": "bf16", "value": round(w.T / (r["ms"] * 1e-3), 1), "unit": "tokens/s",
-            "ms_per_step": round(r["ms"], 5), "row_transform_ms": round(r["k1"], 5),
-            "gemm_ms": round(r["k2"], 5), "gemm_TOPS": round(ops / (r["k2"] * 1e-3) / 1e12, 2),
-            "gemm_mfma_frac": round(ops / (r["k2"] * 1e-3) / 1e12 / FP6_PEAK_TOPS, 4),
-            "gemm_valu_floor_ms": round(valu_floor_ms, 5),
-            "gemm_valu_frac": round(valu_floor_ms / r["k2"], 4),
-            "sqnr_db": sq}
-
-
-def integer_layer(hq, torch, WL, steps, warmup, dev, side):
-    """lic_wh as an integer-only layer with integer requantisation (int8
-    codes in, int8 codes out): the weight-only Hadamard layer (H_256 on the
-    output channels, output in the original basis) or the double-Hadamard
-    layer (input in the H_256 basis of the previous DH layer, output moved to
-    the next one's H_256 basis). Time per call (int8 GEMM into int32, then the
-    requantisation) and the output SQNR of the int8 codes against the float32
-    layer in the same basis. The input codes are the workload's X (rotated for
-    DH) on a per-tensor grid (synthetic input)."""
-    w = WL.WORKLOADS["lic_wh"]
-    X = torch.from_numpy(WL.gen_x(w)).to(dev)
-    W = torch.from_numpy(WL.gen_weight(w)).to(dev)
-    B = torch.from_numpy(WL.gen_bias(w)).to(dev)
-    ref = torch.addmm(B, X, W.t())
-    wh = side == hq.HQ_INT_WH
-    if not wh:
-        # orthonormal Sylvester H_256: the DH input and output bases
-        H = torch.ones(1, 1, dtype=torch.float64)
-        while H.shape[0] < w.block:
-            H = torch.cat([torch.cat([H, H], 1), torch.cat([H, -H], 1)], 0)
-        H = (H / math.sqrt(w.block)).to(dev)
-        def rot(a):
-            return (a.double().reshape(a.shape[0], -1, w.block) @ H).reshape(a.shape).float()
-        X, ref = rot(X), rot(ref)
-    s_x = float(X.abs().max().item() / 127.0)
-    s_y = float(ref.abs().max().item() / 127.0)
-    X0 = torch.clamp(torch.round(X / s_x), -127, 127).to(torch.int8)
-    desc = hq.IntDesc(w.d_in, w.d_out, w.block, hq.F32, side, 1 if wh else w.block)
-    prep = hq.int_prepare(desc, W, B, s_x, s_y)
-    nbuf = max(2, math.ceil(512e6 / X0.numel()))
-    Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
-    Ys = [torch.empty(w.T, w.d_out, dtype=torch.int8, device=dev) for _ in range(nbuf)]
-    ws = torch.empty(hq.int_workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
-    for i in range(warmup):
-        hq.int_linear(desc, prep, Xs[i % nbuf], out=Ys[i % nbuf], workspace=ws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        hq.int_linear(desc, prep, Xs[(warmup + i) % nbuf], out=Ys[(warmup + i) % nbuf],
-                      workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    y = Ys[(warmup + steps - 1) % nbuf].float() * s_y
-    sq = 10.0 * math.log10(ref.pow(2).sum().item() / max((y - ref).pow(2).sum().item(), 1e-300))
-    del Xs, Ys
-    # bytes that must move: int8 codes in and out, weight codes, constants
-    algo = w.T * (w.d_in + w.d_out) + w.d_out * (w.d_in + 12)
-    return {"workload": w.name, "layer": "WH" if wh else "DH-to-DH", "tokens": w.T,
-            "d_in": w.d_in, "d_out": w.d_out, "block": w.block, "bits": "W8A8 int8 -> int8",
-            "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s",
-            "ms_per_step": round(ms, 5), "algorithmic_GBs": round(algo / (ms * 1e-3) / 1e9, 1),
-            "sqnr_db": round(sq, 2)}
+    print(f"traffic per launch: {rec['traffic_bytes_per_launch'] / 1e6:.1f} MB -> {out}")
 
 
 def main():
     args = parse()
     if args.write_traffic:
-        write_traffic(args.write_traffic)
+        write_traffic(args.write_traffic, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs on a "
@@ -381,89 +519,61 @@ def main():
     import hadamard_rotated_bit_amd as hq
     from hadamard_rotated_bit_amd import workloads as WL
 
-    w = WL.WORKLOADS[args.workload]
-    dt = hq.BF16 if w.dtype == "bf16" else hq.F32
-    desc = hq.Desc(w.d_in, w.d_out, w.block, w.a_bits, w.w_bits, int(w.center),
-                   w.alpha is not None, w.rank, dt, dt, dt)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
-
-    x = WL.gen_x(w)
-    weight, bias = WL.gen_weight(w), WL.gen_bias(w)
-    l1, l2 = WL.gen_lowrank(w)
-    X0 = torch.from_numpy(x).to(dev).to(tdt)
-    W = torch.from_numpy(weight).to(dev).to(tdt)
-    B = torch.from_numpy(bias).to(dev)
-    L1 = None if l1 is None else torch.from_numpy(l1).to(dev).to(tdt)
-    L2 = None if l2 is None else torch.from_numpy(l2).to(dev).to(tdt)
-    S = None
-    if w.alpha is not None:          # offline calibration on the workload's own tokens
-        S = hq.sigma(desc, hq.channel_absmax(desc, X0), W, w.alpha)
-
-    xbytes = X0.numel() * X0.element_size()
-    nbuf = max(2, math.ceil(512e6 / xbytes))
-    Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
-    Ys = [torch.empty(w.T, w.d_out, dtype=tdt, device=dev) for _ in range(nbuf)]
-
-    r = measure(hq, torch, desc, w, Xs, Ys, S, W, B, L1, L2, args.steps, args.warmup, dev)
-    fp6, peak, k1_gbs, k2_tops, k2_ops = kernel_report(hq, desc, w, r)
-    ms = r["ms"]
-    tokens_s = w.T / (ms * 1e-3)
-    eff_tops = k2_ops / (ms * 1e-3) / 1e12
-    if r["k2"] >= r["k1"]:
+    steps, warmup = args.steps, args.warmup
+    head, L, r, Y = config_object(hq, torch, WL, args.workload, steps, warmup, dev)
+    w = L.w
+    fp6 = head["engine"].startswith("e2m3")
+    k1, k2 = head["k1"], head["k2"]
+    if k2["ms"] >= k1["ms"]:
         kname = "gemm_f6_dequant" if fp6 else "gemm_i8_dequant"
-        roof = {"kernel": kname, "bound": "mfma",
-                "achieved": round(k2_tops, 2), "peak": peak, "unit": "TFLOP/s",
-                "ops": ("e2m3" if fp6 else "int8") + " multiply-add x2",
-                "frac": round(k2_tops / peak, 4), "traffic": measured_traffic(kname, w.name),
-                "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)"}
+        roof = {"kernel": kname, "bound": "mfma", "achieved": k2["TOPS"], "peak": k2["peak_TOPS"],
+                "unit": "TFLOP/s", "ops": ("e2m3" if fp6 else "int8") + " multiply-add x2",
+                "frac": k2["mfma_frac"], "traffic": measured_traffic(kname, w.name),
+                "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
+                "algorithmic_bytes": k2["bytes"]}
     else:
-        roof = {"kernel": "row_transform", "bound": "hbm", "achieved": round(k1_gbs, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-                "traffic": None}
+        roof = {"kernel": "act_stage", "bound": "hbm", "achieved": k1["GBs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": k1["hbm_frac"], "traffic": None}
     out = {
-        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "e2m3" if fp6 else "int8",
-        "data": "synthetic",
+        "dtype": "e2m3" if fp6 else "int8", "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
                    "block": w.block, "bits": f"W{w.w_bits}A{w.a_bits}", "center": int(w.center),
                    "smooth_alpha": w.alpha, "rank": w.rank, "io_dtype": w.dtype,
-                   "gemm": "e2m3 fp6 mfma" if fp6 else "int8 mfma"},
-        "effective_tops": round(eff_tops, 2),
+                   "gemm": head["engine"]},
+        "effective_tops": head["effective_TOPS_step"],
         "roofline": roof,
-        "kernels": {
-            "row_transform_ms": round(r["k1"], 5), "row_transform_GBs": round(k1_gbs, 1),
-            "row_transform_hbm_frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-            "gemm_ms": round(r["k2"], 5), "gemm_TOPS": round(k2_tops, 2),
-            "gemm_mfma_frac": round(k2_tops / peak, 4),
-        },
         "wall_s_timed": round(r["wall"], 4),
+        "host_cores": host_cores(),
+        "headline": head,
     }
-    if fp6:
-        # the same layer on the int8 engine (int4 codes in int8 lanes, int32
-        # accumulation): identical accumulators, measured against the int8 peak
-        d8 = dataclasses.replace(desc, gemm=hq.HQ_GEMM_I8)
-        r8 = measure(hq, torch, d8, w, Xs, Ys, S, W, B, L1, L2, args.steps, args.warmup, dev)
-        _, p8, g8, t8, _ = kernel_report(hq, d8, w, r8)
-        out["int8_engine"] = {
-            "value": round(w.T / (r8["ms"] * 1e-3), 1), "unit": "tokens/s",
-            "ms_per_step": round(r8["ms"], 5), "row_transform_ms": round(r8["k1"], 5),
-            "row_transform_GBs": round(g8, 1), "gemm_ms": round(r8["k2"], 5),
-            "gemm_TOPS": round(t8, 2), "gemm_mfma_frac": round(t8 / p8, 4), "peak": p8}
-    del Xs, Ys
-    if not args.no_extras:
-        out["group_wise"] = group_wise(hq, torch, WL, min(args.steps, 20), min(args.warmup, 5),
-                                       dev)
-        out["integer_layers"] = [
-            integer_layer(hq, torch, WL, min(args.steps, 20), min(args.warmup, 5), dev, side)
-            for side in (hq.HQ_INT_WH, hq.HQ_INT_DH)]
-        out["centring_modes"] = centring_modes(hq, torch, WL, min(args.steps, 20),
-                                               min(args.warmup, 5), dev)
     if not args.no_cpu_baseline:
-        sig = None if S is None else S.cpu().numpy()
-        out["cpu_baseline"] = cpu_baseline(w, x, weight, bias, sig, l1, l2, args.cpu_seconds)
+        sig = None if L.S is None else L.S.cpu().numpy()
+        out["cpu_baseline"] = cpu_baseline(w, L.x, L.weight, L.bias, sig, L.l1, L.l2, Y,
+                                           args.cpu_seconds)
+    L.free()
+    del L, r, Y
+    if not args.no_extras:
+        es, ew = min(steps, 20), min(warmup, 5)
+        cfgs = {}
+        for name in CONFIG_ORDER:
+            if name == args.workload:
+                continue
+            obj, Lc, rc, Yc = config_object(hq, torch, WL, name, es, ew, dev)
+            if name == "square4k":
+                obj["center_off"], obj["centring_overhead"] = centring_off(hq, torch, Lc, rc,
+                                                                          es, ew)
+                obj["per_channel_centring"] = centring_modes(hq, torch, Lc, es, ew)
+            Lc.free()
+            del Lc, rc, Yc
+            cfgs[name] = obj
+        out["configs"] = cfgs
+        out["group_wise"] = group_wise(hq, torch, WL, es, ew, dev)
+        out["integer_layers"] = [integer_layer(hq, torch, WL, es, ew, dev, side)
+                                 for side in (hq.HQ_INT_WH, hq.HQ_INT_DH)]
     print(json.dumps(out), flush=True)
 
 

@@ -220,6 +220,20 @@ def channel_center(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
     return mean, bias_eff
 
 
+def channel_center_into(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
+                        mean: torch.Tensor, bias_eff: torch.Tensor,
+                        workspace: torch.Tensor) -> None:
+    """channel_center writing into preallocated ``mean`` [d_in] and
+    ``bias_eff`` [d_out_pad] (no allocation; e.g. under graph capture)."""
+    T = X.shape[0]
+    _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
+    _need(mean, "mean", torch.float32, (desc.d_in,))
+    _need(bias_eff, "bias_eff", torch.float32, (layout(desc).d_out_pad,))
+    check(load().hq_channel_center(desc._ref, _ptr(prepared), _ptr(X), T, _ptr(mean),
+                                   _ptr(bias_eff), _ptr(workspace), workspace.numel(),
+                                   _stream()))
+
+
 def act_quantize(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, out=None, mean=None):
     """Activation stage alone: (codes, s_x, mu [T], U [T, rank] or None); s_x
     has desc.sx_shape(T) ([T], or [d_in / 64, T] with group-wise scales).

@@ -426,6 +426,8 @@ int hq_channel_absmax(const hq_desc* desc, const void* X, int64_t T, float* absm
   if (st != HQ_OK) return st;
   if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0");
   if (!absmax || (T > 0 && !X)) return fail(HQ_ERR_INVALID_ARG, "X or absmax is NULL");
+  if (misaligned(X) || misaligned(absmax))
+    return fail(HQ_ERR_INVALID_ARG, "X and absmax must be 16-byte aligned");
   hipError_t e = hq::launch_col_absmax(X, desc->x_dtype == HQ_BF16, T, desc->d_in, absmax,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? HQ_OK : hip_fail(e, "absmax kernel launch");
@@ -438,6 +440,8 @@ int hq_sigma(const hq_desc* desc, const float* act_absmax, const void* weight, f
   if (st != HQ_OK) return st;
   if (!act_absmax || !weight || !sigma)
     return fail(HQ_ERR_INVALID_ARG, "act_absmax, weight and sigma must be non-NULL");
+  if (misaligned(act_absmax) || misaligned(weight) || misaligned(sigma))
+    return fail(HQ_ERR_INVALID_ARG, "act_absmax, weight and sigma must be 16-byte aligned");
   if (!(alpha >= 0.0f && alpha <= 1.0f))
     return fail(HQ_ERR_INVALID_ARG, "alpha must lie in [0, 1] (got %g)", double(alpha));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -459,6 +463,10 @@ int hq_prepare_weights(const hq_desc* desc, const void* weight, const float* bia
   if (!desc->smooth && sigma) return fail(HQ_ERR_INVALID_ARG, "smooth = 0 takes no sigma");
   if (desc->rank && (!L1 || !L2)) return fail(HQ_ERR_INVALID_ARG, "rank > 0 needs L1 and L2");
   if (!desc->rank && (L1 || L2)) return fail(HQ_ERR_INVALID_ARG, "rank = 0 takes no L1/L2");
+  if (misaligned(weight) || misaligned(prepared) || misaligned(bias) || misaligned(sigma) ||
+      misaligned(L1) || misaligned(L2))
+    return fail(HQ_ERR_INVALID_ARG,
+                "weight, bias, sigma, L1, L2 and prepared must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hq_prepared_layout L;
   layout_of(desc, &L);
@@ -592,8 +600,10 @@ int hq_channel_center(const hq_desc* desc, const void* prepared, const void* X, 
   if (T <= 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 1 (got %lld)", (long long)T);
   if (!prepared || !X || !mean || !bias_eff || !workspace)
     return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (misaligned(X) || misaligned(workspace) || misaligned(prepared))
-    return fail(HQ_ERR_INVALID_ARG, "X, workspace and prepared must be 16-byte aligned");
+  if (misaligned(X) || misaligned(workspace) || misaligned(prepared) || misaligned(mean) ||
+      misaligned(bias_eff))
+    return fail(HQ_ERR_INVALID_ARG,
+                "X, mean, bias_eff, workspace and prepared must be 16-byte aligned");
   const Workspace w = workspace_of(desc, T);
   if (workspace_bytes < w.total)
     return fail(HQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, w.total);
@@ -610,6 +620,9 @@ int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, in
   if (T == 0) return HQ_OK;
   if (!prepared || !X || !codes || !s_x || !mu || (desc->rank && !U))
     return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (misaligned(X) || misaligned(codes) || misaligned(prepared) || misaligned(s_x) ||
+      misaligned(mu) || misaligned(U))
+    return fail(HQ_ERR_INVALID_ARG, "X, codes, s_x, mu, U and prepared must be 16-byte aligned");
   const bool chan = desc->center == HQ_CENTER_CHANNEL;
   return run_act(desc, prepared, X, T, codes, s_x, chan ? nullptr : mu, chan ? mu : nullptr, U,
                  static_cast<hipStream_t>(stream));
@@ -623,6 +636,8 @@ int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, i
   if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0");
   if (T == 0) return HQ_OK;
   if (!prepared || !X || !Xt || !mu) return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (misaligned(X) || misaligned(Xt) || misaligned(prepared) || misaligned(mu))
+    return fail(HQ_ERR_INVALID_ARG, "X, Xt, mu and prepared must be 16-byte aligned");
   hq_prepared_layout L;
   layout_of(desc, &L);
   hq::RowArgs a = {};
@@ -651,6 +666,8 @@ int hq_gemm_i32(const hq_desc* desc, const void* a_codes, const void* w_codes, i
   if (T < 0 || N <= 0 || N % 8) return fail(HQ_ERR_INVALID_ARG, "need T >= 0 and N a positive multiple of 8");
   if (T == 0) return HQ_OK;
   if (!a_codes || !w_codes || !acc) return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (misaligned(a_codes) || misaligned(w_codes) || misaligned(acc))
+    return fail(HQ_ERR_INVALID_ARG, "a_codes, w_codes and acc must be 16-byte aligned");
   hipError_t e = launch_codes_gemm(desc, a_codes, T, w_codes, N, acc, N, nullptr,
                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? HQ_OK : hip_fail(e, "GEMM kernel launch");
@@ -666,8 +683,9 @@ int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes
   if (T == 0) return HQ_OK;
   if (!prepared || !codes || !s_x || !mu || !Y || (desc->rank && !U))
     return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (misaligned(Y) || misaligned(codes) || misaligned(prepared))
-    return fail(HQ_ERR_INVALID_ARG, "Y, codes and prepared must be 16-byte aligned");
+  if (misaligned(Y) || misaligned(codes) || misaligned(prepared) || misaligned(s_x) ||
+      misaligned(mu) || misaligned(U))
+    return fail(HQ_ERR_INVALID_ARG, "Y, codes, s_x, mu, U and prepared must be 16-byte aligned");
   return run_gemm_dequant(desc, prepared, codes, s_x, mu, U, T, Y,
                           static_cast<hipStream_t>(stream));
 }
@@ -713,7 +731,8 @@ int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bia
   if (!(s_x > 0.0f) || !(s_y > 0.0f) || !std::isfinite(s_x) || !std::isfinite(s_y))
     return fail(HQ_ERR_INVALID_ARG, "s_x and s_y must be positive and finite (got %g, %g)",
                 double(s_x), double(s_y));
-  if (misaligned(prepared)) return fail(HQ_ERR_INVALID_ARG, "prepared must be 16-byte aligned");
+  if (misaligned(prepared) || misaligned(weight) || misaligned(bias))
+    return fail(HQ_ERR_INVALID_ARG, "weight, bias and prepared must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hq_int_layout L;
   int_layout_of(desc, &L);

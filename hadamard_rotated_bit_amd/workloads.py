@@ -22,7 +22,8 @@ not available here:
                    log-uniformly in [20, 100]; block-diagonal 128-point rotation.
 * ``square4k``  -- 8192 x 4096 -> 4096 bf16, Student-t(3) activations plus
                    per-channel means ~ N(0, 2^2); one 4096-point rotation;
-                   run with and without centring.
+                   run with and without centring (``square4k_nc`` is the
+                   same layer and the same numbers with centring off).
 * ``lic_dh``    -- 12288 x 256 -> 256 fp32, a learned-image-coding 1x1 conv
                    (8 latents of 32 x 48 positions, channels last, token
                    index (n*32 + h)*48 + w); Laplace(0,1) with 8 channels x30;
@@ -91,6 +92,9 @@ WORKLOADS = {
                         "normal", 12, 20.0, 100.0, 0.02),
     "square4k": Workload(3, "square4k", 8192, 4096, 4096, "bf16", 4096, None, 1, 4, 4, 0,
                          "student_t3_means", 0, 1.0, 1.0, 0.015, mean_std=2.0),
+    # the same workload id (so the same X, weight and bias) with centring off
+    "square4k_nc": Workload(3, "square4k_nc", 8192, 4096, 4096, "bf16", 4096, None, 0, 4, 4, 0,
+                            "student_t3_means", 0, 1.0, 1.0, 0.015, mean_std=2.0),
     "lic_dh": Workload(4, "lic_dh", 12288, 256, 256, "f32", 256, None, 0, 8, 8, 0,
                        "laplace", 8, 30.0, 30.0, 0.05),
     "flux_proj": Workload(5, "flux_proj", 4608, 3072, 12288, "bf16", 1024, 0.5, 1, 4, 4, 32,
@@ -101,6 +105,8 @@ WORKLOADS = {
                        "laplace", 8, 30.0, 30.0, 0.05),
 }
 ORDER = ["tiny", "dit_fc1", "square4k", "lic_dh", "flux_proj"]
+# the five plus the square projection's second run (centring off)
+PARITY_ORDER = ORDER[:3] + ["square4k_nc"] + ORDER[3:]
 GROUP_ORDER = ["flux_g64"]
 WH_ORDER = ["lic_wh"]
 

@@ -54,8 +54,11 @@
  *    except where stated.
  *  - The caller allocates and owns every buffer. The library allocates no
  *    device memory and keeps no state besides a thread-local error string.
- *  - X, Y, prepared, workspace and code buffers must be 16-byte aligned
- *    (checked; any allocator's base pointer is).
+ *  - Every device array argument (X, Y, weight, bias, sigma, L1, L2,
+ *    prepared, workspace, code buffers, scales, means, accumulators) must be
+ *    16-byte aligned: the kernels read and write them with 16-byte vector
+ *    accesses and direct-to-LDS loads. Checked on the host (any allocator's
+ *    base pointer is aligned).
  *  - All arguments are validated on the host before anything is enqueued; on
  *    error nothing is launched, outputs are untouched, a negative hq_status
  *    is returned and hq_last_error() describes the problem. No C++
@@ -159,34 +162,40 @@ typedef struct {
   int64_t d_out_pad;   /* d_out rounded up to the GEMM column tile              */
 } hq_prepared_layout;
 
-/* Library ABI version (HQ_ABI_VERSION of the build). */
+/* Bookkeeping (no step of the method): library ABI version (HQ_ABI_VERSION). */
 int hq_abi_version(void);
 
-/* Text of the last error on the calling thread ("" if none). Never NULL. */
+/* Bookkeeping: text of the last error on the calling thread ("" if none).
+ * Never NULL. */
 const char* hq_last_error(void);
 
-/* Static name of a status code. */
+/* Bookkeeping: static name of a status code. */
 const char* hq_status_str(int status);
 
-/* Host-only check of a descriptor (host pointer). Returns HQ_OK or the error. */
+/* Bookkeeping, host-only: check a descriptor (host pointer). Returns HQ_OK
+ * or the error. */
 int hq_validate(const hq_desc* desc);
 
-/* Host-only: size in bytes of the prepared-weight blob for ``desc``;
- * 0 if the descriptor is invalid (see hq_last_error). */
+/* Bookkeeping, host-only: size in bytes of the prepared-weight blob for
+ * ``desc``; 0 if the descriptor is invalid (see hq_last_error). */
 size_t hq_prepared_bytes(const hq_desc* desc);
 
-/* Host-only: layout of the prepared blob (host pointers). */
+/* Bookkeeping, host-only: layout of the prepared blob (host pointers). With
+ * it a caller reads the arrays of a blob in place (weight codes, s_w, c, b,
+ * 1/sigma, the split low-rank factors), so no separate unpacking call exists. */
 int hq_prepared_layout_of(const hq_desc* desc, hq_prepared_layout* out);
 
-/* Host-only: workspace bytes hq_quant_linear needs for T tokens; 0 if invalid. */
+/* Bookkeeping, host-only: workspace bytes hq_quant_linear needs for T
+ * tokens; 0 if invalid. The stage entry points take their buffers as
+ * separate arguments, so no view into a workspace is exported. */
 size_t hq_workspace_bytes(const hq_desc* desc, int64_t T);
 
-/* Host-only: the code format of ``desc`` (hq_code_format_t), or a negative
- * hq_status if the descriptor is invalid. */
+/* Bookkeeping, host-only: the code format of ``desc`` (hq_code_format_t), or
+ * a negative hq_status if the descriptor is invalid. */
 int hq_code_format(const hq_desc* desc);
 
-/* Host-only: bytes of a code matrix of ``rows`` rows for ``desc`` (see Code
- * formats); 0 if the descriptor is invalid or rows < 0. */
+/* Bookkeeping, host-only: bytes of a code matrix of ``rows`` rows for
+ * ``desc`` (see Code formats); 0 if the descriptor is invalid or rows < 0. */
 size_t hq_code_bytes(const hq_desc* desc, int64_t rows);
 
 /* Calibration statistic for the smoothing scale (HadaNorm Eq. (3)):
@@ -217,11 +226,16 @@ int hq_prepare_weights(const hq_desc* desc, const void* weight, const float* bia
                        const float* sigma, const void* L1, const void* L2, void* prepared,
                        void* stream);
 
-/* Host-synchronising check that ``prepared`` was written by
+/* Bookkeeping: host-synchronising check that ``prepared`` was written by
  * hq_prepare_weights for this descriptor (reads its 256-byte header). */
 int hq_check_prepared(const hq_desc* desc, const void* prepared, void* stream);
 
-/* The hot path: Y = quantised layer(X) for T tokens.
+/* The hot path: Y = quantised layer(X) for T tokens, i.e. X~ W~ + b~ of
+ * HadaNorm Eq. (1) ("What carries the argument") with X~ quantised per token
+ * by HaTQ Sec. III-A Eq. (3), the integer product of HaTQ Sec. III-B Eq. (4),
+ * the accumulator scale s_x s_w of HaTQ Eq. (18), the bias correction mu W~,
+ * and (rank > 0) the 16-bit branch of the data-free int4 blog ("Hadamard
+ * rotation: the int4 improvement", steps 3-4).
  *  X [T, d_in] x_dtype, row-major;  Y [T, d_out] y_dtype, row-major.
  *  workspace: device buffer of at least hq_workspace_bytes(desc, T) bytes,
  *  not shared with a concurrent call. T = 0 is a no-op. */
@@ -230,7 +244,9 @@ int hq_quant_linear(const hq_desc* desc, const void* prepared, const void* X, in
 
 /* ---- Stage entry points (the same kernels, for testing and profiling) ---- */
 
-/* Per-channel centring statistics (center = 2 only; T >= 1): over the T rows
+/* Per-channel centring statistics (center = 2 only; T >= 1), the per-channel
+ * reading of mu in HadaNorm Eq. (1) (Fig. 2 caption: mu in R^d; "one added
+ * token"): over the T rows
  * of X, mean f32 [d_in] = mean_t X (the activation stage subtracts it from
  * every token before the channel scaling and the rotation, which yields the
  * same X~ as subtracting mu after them) and bias_eff f32 [d_out_pad] =
@@ -240,7 +256,10 @@ int hq_channel_center(const hq_desc* desc, const void* prepared, const void* X, 
                       float* mean, float* bias_eff, void* workspace, size_t workspace_bytes,
                       void* stream);
 
-/* Activation stage alone: codes of T rows in the descriptor's code format
+/* Activation stage alone: X~ = X diag(1/sigma) H - mu of HadaNorm Eq. (1),
+ * quantised per token (or per token and 64-channel group) by HaTQ Sec. III-A
+ * Eq. (3), plus U = x' L1 of the blog's step 3. Outputs: codes of T rows in
+ * the descriptor's code format
  * (hq_code_bytes(desc, T) bytes, natural channel order), s_x f32 [T]
  * (dequant scale of the normalised X~ row; [d_in / 64, T] with group = 64,
  * one per token and group), mu f32 [T], U f32 [T, rank]
@@ -249,20 +268,24 @@ int hq_channel_center(const hq_desc* desc, const void* prepared, const void* X, 
 int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
                     void* codes, float* s_x, float* mu, float* U, void* stream);
 
-/* Debug export of the float transform before quantisation:
- * Xt f32 [T, d_in] = X~ (normalised H, centred if desc->center), mu f32 [T].
+/* Debug export of the float transform before quantisation, X~ of HadaNorm
+ * Eq. (1) (H normalised as in HaTQ Eq. (7)):
+ * Xt f32 [T, d_in] = X~ (centred if desc->center), mu f32 [T].
  * For center = 2, mu is an INPUT: the mean [d_in] of hq_channel_center. */
 int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
                      float* Xt, float* mu, void* stream);
 
-/* Integer GEMM alone: acc int32 [T, N] = a_codes [T, d_in] . w_codes [N, d_in]^T,
+/* Integer GEMM alone, HaTQ Sec. III-B Eq. (4) with zero points 0:
+ * acc int32 [T, N] = a_codes [T, d_in] . w_codes [N, d_in]^T,
  * both in the descriptor's code format (T and N rows); N a multiple of 8.
  * With group = 64 this is still the product over all d_in channels (the sum
  * of the unscaled per-group products). */
 int hq_gemm_i32(const hq_desc* desc, const void* a_codes, const void* w_codes, int64_t T,
                 int64_t N, int32_t* acc, void* stream);
 
-/* GEMM + dequant epilogue alone, from activation-stage outputs (layouts as in
+/* GEMM + dequant epilogue alone (HaTQ Eq. (4) and the accumulator scale of
+ * Eq. (18); the bias correction b + mu W~ of HadaNorm Eq. (1); the blog's
+ * low-rank step 4), from activation-stage outputs (layouts as in
  * hq_act_quantize; U NULL when rank = 0). Y [T, d_out] y_dtype. For
  * center = 2, mu is the bias_eff [d_out_pad] of hq_channel_center. */
 int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes,
@@ -323,28 +346,32 @@ typedef struct {
   int64_t d_out_pad;
 } hq_int_layout;
 
-/* Host-only: validation, blob size and layout, workspace of hq_int_linear
- * (int32 products [T, d_out]). */
+/* Bookkeeping, host-only: validation, blob size and layout, workspace of
+ * hq_int_linear (int32 products [T, d_out]). */
 int hq_int_validate(const hq_int_desc* desc);
 size_t hq_int_prepared_bytes(const hq_int_desc* desc);
 int hq_int_prepared_layout_of(const hq_int_desc* desc, hq_int_layout* out);
 size_t hq_int_workspace_bytes(const hq_int_desc* desc, int64_t T);
 
-/* Offline: weight [d_out, d_in] (w_dtype) and bias f32 [d_out] (or NULL) into
+/* Offline half of an integer-only layer (HaTQ Sec. IV-B Eq. (13)-(19),
+ * supplement Eq. (40)-(44)): weight [d_out, d_in] (w_dtype) and bias f32
+ * [d_out] (or NULL) into
  * the blob (hq_int_prepared_bytes): W-bar, its int8 codes and scales, the bias
  * codes, the multipliers and the shift. s_x > 0 is the scale of the int8
  * input, s_y > 0 that of the int8 output. */
 int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bias, float s_x,
                    float s_y, void* prepared, void* stream);
 
-/* The hot path: y_codes int8 [T, d_out] from x_codes int8 [T, d_in] (codes in
+/* The integer-only hot path (HaTQ Eq. (4), then the requantisation of
+ * Eq. (19)-(22)): y_codes int8 [T, d_out] from x_codes int8 [T, d_in] (codes in
  * [-127, 127], row-major, in the layer's input basis): the int8 MFMA product
  * into the workspace, then hq_int_requant's kernel. T = 0 is a no-op. */
 int hq_int_linear(const hq_int_desc* desc, const void* prepared, const int8_t* x_codes,
                   int64_t T, int8_t* y_codes, void* workspace, size_t workspace_bytes,
                   void* stream);
 
-/* Requantisation alone: y_codes int8 [T, d_out] from the int32 products
+/* Requantisation alone (HaTQ Eq. (19)-(22) with the identity activation):
+ * y_codes int8 [T, d_out] from the int32 products
  * acc [T, d_out] (x_int . w-bar_int^T, WITHOUT the bias codes, which this
  * stage adds). |acc| <= 2^27 (as every product of int8 codes over d_in <= 8192
  * is); larger values are outside the exact range of the kernel. */

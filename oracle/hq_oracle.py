@@ -46,12 +46,13 @@ Readings taken where the pages leave a step open:
   contiguous block of ``block`` channels.
 * Activations get one scale per token, weights one scale per output
   channel; codes are symmetric in [-qmax, qmax], qmax = 2^(bits-1) - 1.
-* The rounding decision round(v / s) is taken on float32 operands as
-  rint_half_even(f32(v) * f32(qmax / f32(max|v|))), the product formed
-  exactly and rounded once to the integer grid: the same real number as
-  v / s, rounded a single time as "round" reads, in the precision the GPU
-  kernel uses, so both sides decide each code in the same arithmetic.
-  Scales, means and outputs stay float64.
+* The rounding decision is round(v / s) of HaTQ Eq. (3) as written: the
+  quotient of the float64 value and the float64 scale, rounded once, half
+  to even. The pages state no precision for it, so the oracle takes the
+  equation's own (real) arithmetic as closely as float64 gives it. A float32
+  evaluation of the same decision can differ only where v / s lies within
+  its float32 error of a half-integer; comparisons attribute every such
+  difference to a near-tie.
 * A row whose maximum is 0 gets scale 0 and all-zero codes.
 * The bias correction uses c = 1^T W~ from the unquantised W~.
 * The low-rank branch sees x' = x / sigma (smoothed, not rotated, not
@@ -174,20 +175,17 @@ def quantize_rows(v: np.ndarray, bits: int):
     """Symmetric per-row quantiser of HaTQ Sec. III-A Eq. (3).
 
     s = ||v||_inf / qmax with qmax = 2^(bits-1) - 1, and
-    q = clamp(round(v / s), -qmax, qmax). The division v / s is formed as
-    v * (qmax / ||v||_inf) on float32 operands and rounded once, half-to-even
-    (see the module header). Returns (codes int16 [rows, n], s float64 [rows]).
+    q = clamp(round(v / s), -qmax, qmax), round = half to even, all in
+    float64. A row whose maximum is 0 gets s = 0 and zero codes.
+    Returns (codes int16 [rows, n], s float64 [rows]).
     """
     qmax = 2 ** (bits - 1) - 1
     v = np.asarray(v, dtype=np.float64)
     amax = np.abs(v).max(axis=1) if v.shape[1] else np.zeros(v.shape[0])
     s = amax / qmax
-    a32 = amax.astype(np.float32)
-    nz = a32 > 0
-    r32 = np.zeros_like(a32)
-    r32[nz] = np.float32(qmax) / a32[nz]
-    # exact product of two float32 values (48 significant bits fit a float64)
-    t = v.astype(np.float32).astype(np.float64) * r32.astype(np.float64)[:, None]
+    t = np.zeros_like(v)
+    nz = s > 0
+    t[nz] = v[nz] / s[nz][:, None]
     q = np.clip(np.rint(t), -qmax, qmax).astype(np.int16)
     return q, s
 

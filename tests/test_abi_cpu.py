@@ -278,3 +278,66 @@ def test_int_entry_points_reject_before_launch():
     assert lib.hq_int_linear(d, None, p, 16, p, p, 1 << 30, None) == -1
     assert lib.hq_int_requant(d, p, None, 16, p, None) == -1
     assert lib.hq_int_requant(d, p, ctypes.c_void_p(0x1001), 16, p, None) == -1   # misaligned
+
+
+def test_entry_points_reject_misaligned_pointers():
+    # every entry point that launches kernels rejects a pointer that is not
+    # 16-byte aligned on the host, before anything is enqueued (each call
+    # below has exactly one misaligned pointer, so none reaches a launch)
+    d = ctypes.byref(_d())
+    d_ns = ctypes.byref(_d(smooth=False))
+    p = ctypes.c_void_p(0x1000)
+    q = ctypes.c_void_p(0x1008)
+    f = ctypes.c_float
+
+    def bad(st):
+        assert st == -1
+        assert b"aligned" in lib.hq_last_error()
+
+    bad(lib.hq_channel_absmax(d, q, 8, p, None))
+    bad(lib.hq_channel_absmax(d, p, 8, q, None))
+    bad(lib.hq_sigma(d, p, q, f(0.5), p, None))
+    bad(lib.hq_prepare_weights(d, q, None, p, None, None, p, None))
+    bad(lib.hq_prepare_weights(d, p, None, p, None, None, q, None))
+    bad(lib.hq_prepare_weights(d_ns, p, q, None, None, None, p, None))
+    bad(lib.hq_quant_linear(d, p, q, 16, p, p, 1 << 30, None))
+    bad(lib.hq_quant_linear(d, p, p, 16, q, p, 1 << 30, None))
+    bad(lib.hq_act_quantize(d, p, q, 4, p, p, p, None, None))
+    bad(lib.hq_act_quantize(d, p, p, 4, q, p, p, None, None))
+    bad(lib.hq_act_quantize(d, q, p, 4, p, p, p, None, None))
+    bad(lib.hq_act_transform(d, p, q, 4, p, p, None))
+    bad(lib.hq_act_transform(d, p, p, 4, q, p, None))
+    bad(lib.hq_gemm_i32(d, q, p, 16, 16, p, None))
+    bad(lib.hq_gemm_i32(d, p, q, 16, 16, p, None))
+    bad(lib.hq_gemm_i32(d, p, p, 16, 16, q, None))
+    bad(lib.hq_gemm_dequant(d, p, q, p, p, None, 16, p, None))
+    bad(lib.hq_gemm_dequant(d, p, p, p, p, None, 16, q, None))
+    c = ctypes.byref(_d(center=2))
+    bad(lib.hq_channel_center(c, p, q, 4, p, p, p, 1 << 30, None))
+    wi = _il()._ref
+    bad(lib.hq_int_prepare(wi, q, None, f(1.0), f(1.0), p, None))
+    bad(lib.hq_int_linear(wi, p, q, 16, p, p, 1 << 30, None))
+
+
+def test_every_declaration_cites_its_passage():
+    # each function declared in include/hq.h is preceded by a comment that
+    # cites the passage defining its operation (an equation, section, figure
+    # or step of the pages), or says that it is bookkeeping of the interface
+    # with no step of the method, or names the callers it exists for
+    import re
+    with open(_lib.HEADER) as f:
+        text = f.read()
+    cite = re.compile(r"Eq\. \(\d+\)|Sec\. [IVX]+|Fig\. \d|steps? \d|Bookkeeping|cannot allocate")
+    decl = re.compile(r"^(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(hq_[a-z0-9_]+)\s*\(", re.M)
+    seen = 0
+    for m in decl.finditer(text):
+        head = text[:m.start()]
+        comment = head[head.rfind("/*"):]
+        assert "*/" in comment, m.group(1)
+        # only declarations (and blank lines) may stand between the comment and this one
+        between = comment[comment.rfind("*/") + 2:]
+        assert all(re.match(r"^\s*$|^(?:const\s+)?(?:int|size_t|char|void)\b.*|^\s+\S.*[,;]$", ln)
+                   for ln in between.splitlines()), (m.group(1), between)
+        assert cite.search(comment), f"{m.group(1)}: no citation in {comment!r}"
+        seen += 1
+    assert seen == len(_lib.header_functions())

@@ -25,7 +25,7 @@ def sample_rows(T, n=64, seed=7):
     return np.unique(np.concatenate([np.arange(8), mid, np.arange(T - 8, T)]))
 
 
-@pytest.mark.parametrize("name", WL.ORDER)
+@pytest.mark.parametrize("name", WL.PARITY_ORDER)
 def test_full_size_sampled(name):
     w = WL.WORKLOADS[name]
     print(f"\n[case] full-size {name} T={w.T}", flush=True)

@@ -15,7 +15,7 @@ from parity import (ENGINE_CASES, MAX_FLIP_FRAC, XT_TOL, Y_TOL, case_id, check_c
                     codes_np, rel_fro, small_case, tdev, to_np)
 
 pytestmark = pytest.mark.gpu
-NAMES = WL.ORDER
+NAMES = WL.PARITY_ORDER
 
 
 @pytest.mark.parametrize("name", [n for n in NAMES if WL.WORKLOADS[n].alpha is not None])

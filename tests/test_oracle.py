@@ -371,8 +371,8 @@ def test_quantizer_properties(bits):
     # the row maximum maps to +-qmax with its sign
     am = np.abs(v).argmax(axis=1)
     np.testing.assert_array_equal(q[np.arange(64), am], np.sign(v[np.arange(64), am]) * qmax)
-    # reconstruction error at most half a step (plus float32 rounding of the decision)
-    assert np.all(np.abs(v - s[:, None] * q) <= s[:, None] * (0.5 + 1e-6))
+    # reconstruction error at most half a step (plus float64 rounding)
+    assert np.all(np.abs(v - s[:, None] * q) <= s[:, None] * (0.5 + 1e-12))
     # re-quantising the dequantised values returns the same codes
     q2, s2 = O.quantize_rows(s[:, None] * q, bits)
     np.testing.assert_array_equal(q2, q)
@@ -391,6 +391,43 @@ def test_quantizer_zero_row_and_ties():
     assert s[0] == 0
     # 0.5 / 1 -> tie between 0 and 1 -> 0 (even); -0.5 -> 0
     np.testing.assert_array_equal(q[1], [1, 0, 0])
+
+
+def test_quantizer_decides_in_float64():
+    # a quotient 3.5 - 2^-40 lies below the half-integer by far less than any
+    # float32 step at 3.5 (2^-22): the float64 decision of Eq. (3) rounds it
+    # down, a float32 product of the rounded operands would land on the tie
+    # and round to even (4)
+    qmax = 7
+    v = np.array([[7.0, 3.5 - 2.0 ** -40, 3.5 + 2.0 ** -40, -(3.5 - 2.0 ** -40)]])
+    q, s = O.quantize_rows(v, 4)
+    assert s[0] == 1.0
+    np.testing.assert_array_equal(q[0], [7, 3, 4, -3])
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantize_static_brute_force(bits):
+    # Per-tensor quantiser with a given scale: each code is the integer of
+    # [-qmax, qmax] nearest to x / s (ties to the even one), found by
+    # enumerating the grid; values beyond the range clamp to +-qmax.
+    qmax = 2 ** (bits - 1) - 1
+    s = 0.25
+    half = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5, qmax - 0.5, -(qmax - 0.5)]
+    vals = np.array(half + [0.0, 0.26, -0.74, 3.49, -3.51, qmax + 0.49, qmax + 40.0,
+                            -(qmax + 0.51), -1e6, 1e6]) * s
+    q = O.quantize_static(vals, s, bits)
+    grid = np.arange(-qmax, qmax + 1)
+    for x, c in zip(vals, q):
+        t = x / s
+        d = np.abs(grid - t)
+        best = grid[d == d.min()]
+        want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+        assert c == want, (x, c, want)
+    # the half-integers above go to their even neighbours
+    np.testing.assert_array_equal(q[:6], [0, 2, 2, 0, -2, -2])
+    assert q[6] == (qmax - 1 if (qmax - 1) % 2 == 0 else qmax)
+    assert np.abs(q).max() == qmax
+    assert q.dtype == np.int16
 
 
 # ---------------------------------------------------------------- integer GEMM
