@@ -199,6 +199,26 @@ def quant_linear(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
     return out
 
 
+NOALLOC_SCRATCH_BYTES = 32 << 20   # HQ_NOALLOC_SCRATCH_BYTES of include/hq.h
+
+
+def quant_linear_noalloc(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """quant_linear with the library's static per-GPU scratch array as the
+    workspace (hq_quant_linear_noalloc): the call allocates nothing on the
+    device besides ``out`` when it is not given. Calls that overlap on one
+    GPU share that array and must not run concurrently."""
+    T = X.shape[0]
+    _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
+    if out is None:
+        out = torch.empty(T, desc.d_out, dtype=_TORCH[desc.y_dtype], device=X.device)
+    else:
+        _need(out, "out", _TORCH[desc.y_dtype], (T, desc.d_out))
+    check(load().hq_quant_linear_noalloc(desc._ref, _ptr(prepared), _ptr(X), T, _ptr(out),
+                                         _stream()))
+    return out
+
+
 def _channel(desc: Desc) -> bool:
     return int(desc.center) == HQ_CENTER_CHANNEL
 

@@ -61,6 +61,7 @@ _SIGS = {
     "hq_prepare_weights": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P]),
     "hq_check_prepared": (ctypes.c_int, [_D, _P, _P]),
     "hq_quant_linear": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "hq_quant_linear_noalloc": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P]),
     "hq_channel_center": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "hq_act_quantize": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, _P, _P, _P]),
     "hq_act_transform": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, _P]),

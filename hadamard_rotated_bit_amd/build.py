@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhq.so")
 SOURCES = ["hq_act.hip", "hq_rowfast.hip", "hq_center.hip", "hq_gemm.hip", "hq_gemm6.hip", "hq_gemm6g.hip", "hq_int.hip",
-           "hq_abi.cpp"]
+           "hq_noalloc.hip", "hq_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU forms.

@@ -352,6 +352,8 @@ int run_int_requant(const hq_int_desc* d, const void* prepared, const int32_t* a
 
 }  // namespace
 
+int hq::set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
 extern "C" {
 
 int hq_abi_version(void) { return HQ_ABI_VERSION; }

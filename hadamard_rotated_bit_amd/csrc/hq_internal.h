@@ -10,6 +10,10 @@
 
 namespace hq {
 
+// Sets the calling thread's error text (what hq_last_error returns) and
+// returns `code`; for entry points defined outside hq_abi.cpp.
+int set_error(int code, const char* msg);
+
 // GEMM macro tile sizes; d_out is padded to a multiple of GEMM_BN in the
 // prepared blob and T to a multiple of GEMM_BM in the workspace.
 constexpr int GEMM_BM = 256;

@@ -242,6 +242,25 @@ int hq_check_prepared(const hq_desc* desc, const void* prepared, void* stream);
 int hq_quant_linear(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
                     void* Y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the static scratch array of hq_quant_linear_noalloc (per GPU). */
+#define HQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, hosts that forbid allocation): the same
+ * computation and kernels as hq_quant_linear, with the workspace in a static
+ * device array of HQ_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * each GPU it runs on until the process ends (its address is looked up on the
+ * first call on each device, with that device current). No allocation of any
+ * kind happens in the call. Returns HQ_ERR_WORKSPACE, launching nothing, when
+ * hq_workspace_bytes(desc, T) exceeds the array. Every call on one GPU shares
+ * that GPU's array, so calls that overlap on a GPU (other streams, other host
+ * threads) race: the caller serialises them. The array keeps the last call's
+ * contents; nothing in it needs clearing (every byte read is first written by
+ * the same call). Arguments and errors otherwise as hq_quant_linear;
+ * ``stream`` must belong to the current device. */
+int hq_quant_linear_noalloc(const hq_desc* desc, const void* prepared, const void* X,
+                            int64_t T, void* Y, void* stream);
+
 /* ---- Stage entry points (the same kernels, for testing and profiling) ---- */
 
 /* Per-channel centring statistics (center = 2 only; T >= 1), the per-channel

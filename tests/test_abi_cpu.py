@@ -341,3 +341,18 @@ def test_every_declaration_cites_its_passage():
         assert cite.search(comment), f"{m.group(1)}: no citation in {comment!r}"
         seen += 1
     assert seen == len(_lib.header_functions())
+
+
+def test_noalloc_rejects_before_launch():
+    # host-side checks of hq_quant_linear_noalloc: invalid descriptor, T < 0,
+    # and a workspace beyond the static array, all refused before any launch
+    d = ctypes.byref(_d())
+    p = ctypes.c_void_p(0x1000)
+    assert lib.hq_quant_linear_noalloc(ctypes.byref(_d(a_bits=3)), p, p, 16, p, None) == -2
+    assert lib.hq_quant_linear_noalloc(d, p, p, -1, p, None) == -1
+    assert lib.hq_quant_linear_noalloc(d, p, p, 0, None, None) == 0
+    big = ctypes.byref(_d(d_in=4096, block=4096))
+    T = 12000   # 12000 x 3072 bytes of codes alone exceed the 32 MiB array
+    assert lib.hq_workspace_bytes(big, T) > (32 << 20)
+    assert lib.hq_quant_linear_noalloc(big, p, p, T, p, None) == -3
+    assert b"static scratch" in lib.hq_last_error()
