@@ -264,6 +264,8 @@ int run_gemm_dequant(const hq_desc* d, const void* prepared, const void* codes,
   ep.U = U;
   ep.l2_hi = at<uint16_t>(prepared, L.l2_hi);
   ep.l2_lo = at<uint16_t>(prepared, L.l2_lo);
+  // L2 given in bf16 is exactly its bf16 hi part: the lo part is all zero
+  ep.l2_lo_zero = d->w_dtype == HQ_BF16;
   ep.rank = d->rank;
   ep.Y = Y;
   ep.y_bf16 = d->y_dtype == HQ_BF16;

@@ -579,7 +579,8 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
               const int64_t nr = nb + erow < N ? nb + erow : N - 1;
               const int64_t off = nr * ep.rank + k0 + 8 * ehalf;
               wh1[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
-              wl1[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
+              wl1[j][h] = ep.l2_lo_zero ? wh1[j][h]
+                                        : *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
             }
           }
           load_u(0, un);
@@ -611,7 +612,8 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
 #pragma unroll
               for (int j = 0; j < TN; ++j) {
                 lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh1[j][h], uh, lr[j], 0, 0, 0);
-                lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl1[j][h], uh, lr[j], 0, 0, 0);
+                if (!ep.l2_lo_zero)
+                  lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl1[j][h], uh, lr[j], 0, 0, 0);
                 lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh1[j][h], ul, lr[j], 0, 0, 0);
               }
             }
@@ -630,7 +632,8 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
                 const int64_t nr = nb + erow < N ? nb + erow : N - 1;
                 const int64_t off = nr * ep.rank + k0 + 8 * ehalf;
                 wh[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
-                wl[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
+                wl[j][h] = ep.l2_lo_zero ? wh[j][h]
+                                         : *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
               }
             }
 #pragma unroll
@@ -640,7 +643,8 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
 #pragma unroll
               for (int j = 0; j < TN; ++j) {
                 lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[j][h], uh, lr[j], 0, 0, 0);
-                lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl[j][h], uh, lr[j], 0, 0, 0);
+                if (!ep.l2_lo_zero)
+                  lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl[j][h], uh, lr[j], 0, 0, 0);
                 lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[j][h], ul, lr[j], 0, 0, 0);
               }
             }

@@ -115,9 +115,11 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[TM][TN], uint8_t* smem
           const int64_t nr = nb + lrow < N ? nb + lrow : N - 1;
           const int64_t off = nr * ep.rank + k0 + 8 * lhalf;
           const v8bf wh = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
-          const v8bf wl = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
           lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, uh, lr, 0, 0, 0);
-          lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, uh, lr, 0, 0, 0);
+          if (!ep.l2_lo_zero) {
+            const v8bf wl = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
+            lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, uh, lr, 0, 0, 0);
+          }
           lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, ul, lr, 0, 0, 0);
         }
 #pragma unroll
@@ -199,7 +201,7 @@ __device__ __forceinline__ void gemm_epilogue_bf16_staged(AccT (&acc)[TM][TN], u
           const int k0 = (h == 0 || two) ? kc + 16 * h : kc;
           const int64_t off = nr * ep.rank + k0 + 8 * lhalf;
           wh[h] = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
-          wl[h] = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
+          wl[h] = ep.l2_lo_zero ? wh[h] : *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
             const int64_t m = m0 + wm0 + i * 32 + lrow;
@@ -214,7 +216,8 @@ __device__ __forceinline__ void gemm_epilogue_bf16_staged(AccT (&acc)[TM][TN], u
           for (int i = 0; i < TM; ++i) {
             const v8bf uh = pack_bf16x8(uf[i][h], false), ul = pack_bf16x8(uf[i][h], true);
             lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[h], uh, lr[i], 0, 0, 0);
-            lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl[h], uh, lr[i], 0, 0, 0);
+            if (!ep.l2_lo_zero)
+              lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl[h], uh, lr[i], 0, 0, 0);
             lr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[h], ul, lr[i], 0, 0, 0);
           }
         }

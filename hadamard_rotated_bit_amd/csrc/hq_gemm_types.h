@@ -22,6 +22,8 @@ struct GemmEpi {
   const float* U;         // [M, rank] or NULL
   const uint16_t* l2_hi;  // [N, rank]
   const uint16_t* l2_lo;
+  int l2_lo_zero;         // l2_lo is all zero (L2 given in bf16 is its own hi
+                          // part): its products are skipped
   int rank;
   void* Y;                // [M, ldy]
   int y_bf16;
