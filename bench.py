@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="measure the headline workload only (both engines), e.g. for clean "
                          "profiles: no other configs, group-wise, integer-layer or centring objects")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="host only: turn the FETCH_SIZE / WRITE_SIZE counter runs in DIR "
@@ -77,38 +77,37 @@ def sha256_arrays(**arrays) -> dict:
 
 
 def cpu_baseline(w, x, weight, bias, sigma, l1, l2, Y_gpu, target_s):
-    """The CPU oracle's online half (transform, centre, quantise, integer GEMM,
-    dequantise; weight preparation done once beforehand and not timed) on a
-    bounded prefix of the workload's tokens, with NumPy's BLAS on every host
-    core. The same rows of the GPU output are compared with the oracle's
-    (relative Frobenius error) as the run's parity statistic."""
-    from oracle import hq_oracle as O
-    import threadpoolctl
+    """The C++ CPU oracle's online half (transform, centre, quantise, integer
+    GEMM, dequantise; weight preparation done once beforehand and not timed)
+    on a bounded prefix of the workload's tokens, std::thread over tokens on
+    every host core. The same rows of the GPU output are compared with the
+    oracle's (relative Frobenius error) as the run's parity statistic."""
+    from oracle import cpp as C
     cores = host_cores()
-    with threadpoolctl.threadpool_limits(limits=cores):
-        sig = np.ones(w.d_in) if sigma is None else sigma.astype(np.float64)
-        prep = O.prepare_weights(weight, sig, w.block, w.w_bits)
-        rows = min(w.T, 128)
+    sig = np.ones(w.d_in) if sigma is None else sigma.astype(np.float64)
+    t0 = time.perf_counter()
+    prep = C.prepare_weights(weight, sig, w.block, w.w_bits, threads=cores)
+    prep_s = time.perf_counter() - t0
 
-        def run(n):
-            t0 = time.perf_counter()
-            r = O.quant_linear(x[:n], prep, bias, sig, block=w.block, a_bits=w.a_bits,
-                               center=int(w.center), l1=None if l1 is None else l1,
-                               l2=l2, out_dtype=w.out_dtype)
-            return r, time.perf_counter() - t0
+    def run(n):
+        t0 = time.perf_counter()
+        r = C.quant_linear(x[:n], prep, bias, sig, block=w.block, a_bits=w.a_bits,
+                           center=int(w.center), l1=l1, l2=l2, out_dtype=w.out_dtype,
+                           want_acc=False, threads=cores)
+        return r, time.perf_counter() - t0
 
+    rows = min(w.T, 256)
+    r, dt = run(rows)
+    if dt < target_s and rows < w.T:
+        rows = int(min(w.T, max(rows, rows * target_s / max(dt, 1e-3))))
         r, dt = run(rows)
-        if dt < target_s and rows < w.T:
-            rows = int(min(w.T, max(rows, rows * target_s / max(dt, 1e-3))))
-            r, dt = run(rows)
-        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
     y = Y_gpu[:rows].float().cpu().numpy().astype(np.float64)
     ref = r["y_out"]
     err = float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
-    return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "blas_threads": int(threads),
-            "sample": f"first {rows} of {w.T} tokens of {w.name}, float64 NumPy oracle "
-                      f"(online half, prepared weights reused), {dt:.2f} s",
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle-c++",
+            "sample": f"first {rows} of {w.T} tokens of {w.name}, float64 C++17 oracle "
+                      f"(online half, std::thread on {cores} host cores, prepared weights "
+                      f"reused), {dt:.2f} s; weight preparation {prep_s:.2f} s, not timed",
             "parity_rel_fro_vs_gpu": err, "parity_rows": rows}
 
 
