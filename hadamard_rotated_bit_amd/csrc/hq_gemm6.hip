@@ -27,7 +27,7 @@ static hipError_t launch_f6_cfg(const uint8_t* A, int64_t M, const uint8_t* B, i
 // Persistent 256 x 192 kernel for bf16 outputs (K >= 384): one block per CU
 // (at most one per tile) walks its tiles with the stage pipeline running
 // across tile boundaries.
-template <bool LR>
+template <int LR>
 static hipError_t launch_f6_persist(const uint8_t* A, int64_t M, const uint8_t* B, int64_t N,
                                     int K, const GemmEpi& ep, int cus, hipStream_t s) {
   const int64_t ntiles = ((M + 255) / 256) * ((N + 191) / 192);
@@ -57,8 +57,9 @@ hipError_t launch_gemm_f6(const uint8_t* A, int64_t M, const uint8_t* B, int64_t
     if (cu_cache[dev] > 0) cus = cu_cache[dev];
   }
   if (epi && epi->y_bf16 && K >= 384)
-    return epi->rank ? launch_f6_persist<true>(A, M, B, N, K, *epi, cus, s)
-                     : launch_f6_persist<false>(A, M, B, N, K, *epi, cus, s);
+    return !epi->rank         ? launch_f6_persist<0>(A, M, B, N, K, *epi, cus, s)
+           : epi->l2_lo_zero ? launch_f6_persist<1>(A, M, B, N, K, *epi, cus, s)
+                             : launch_f6_persist<2>(A, M, B, N, K, *epi, cus, s);
   const int64_t tm = (M + 255) / 256;
   const int64_t rounds256 = (tm * ((N + 255) / 256) + cus - 1) / cus;
   const int64_t rounds192 = (tm * ((N + 191) / 192) + cus - 1) / cus;

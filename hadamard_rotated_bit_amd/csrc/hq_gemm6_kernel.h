@@ -358,7 +358,7 @@ __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_f6_kernel(
 // iteration earlier (LPW). The prologue issues NST stores that move no
 // memory so that the first tile has the same sequence. A tile's parameters
 // are retired by its k-step 2 (K >= 384: three stages per tile).
-template <int BM, int BN, int WM, int WN, int GM, int RG, bool LR>
+template <int BM, int BN, int WM, int WN, int GM, int RG, int LR>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
     const uint8_t* __restrict__ A, int64_t M, const uint8_t* __restrict__ B, int64_t N, int K,
@@ -554,10 +554,12 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
       const int ypitch = int(ep.ldy * 2);
       // Rank <= 32 (one 32-rank chunk): the wave's L2 operands are the same
       // for every slice, so they are loaded once per tile, and U of slice
-      // i + 1 is loaded while slice i is computed.
-      const bool lr_one = LR && ep.rank <= 32;
-      const bool lr_two = LR && ep.rank > 16;
-      v8bf wh1[LR ? TN : 1][2], wl1[LR ? TN : 1][2];
+      // i + 1 is loaded while slice i is computed. LR == 1: L2 was given in
+      // bf16, so its low half is zero and takes neither registers nor
+      // products; LR == 2: L2 is carried as bf16 hi + lo.
+      const bool lr_one = LR != 0 && ep.rank <= 32;
+      const bool lr_two = LR != 0 && ep.rank > 16;
+      v8bf wh1[LR ? TN : 1][2], wl1[LR == 2 ? TN : 1][2];
       float un[2][8];
       auto load_u = [&](int i_, float (&dst)[2][8]) {
         const int64_t m = mw + i_ * 32 + erow;
@@ -568,7 +570,7 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
           load8(ep.U + mc * ep.rank + k0 + 8 * ehalf, dst[h]);
         }
       };
-      if constexpr (LR) {
+      if constexpr (LR != 0) {
         if (lr_one) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
@@ -579,8 +581,7 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
               const int64_t nr = nb + erow < N ? nb + erow : N - 1;
               const int64_t off = nr * ep.rank + k0 + 8 * ehalf;
               wh1[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
-              wl1[j][h] = ep.l2_lo_zero ? wh1[j][h]
-                                        : *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
+              if constexpr (LR == 2) wl1[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
             }
           }
           load_u(0, un);
@@ -593,7 +594,7 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
         // Low-rank term of slice i (all strips): one 32-rank chunk of U and
         // L2 operands loaded before any product (see the tiled epilogue).
         v16f lr[LR ? TN : 1];
-        if constexpr (LR) {
+        if constexpr (LR != 0) {
           const int64_t m = mw + i * 32 + erow;
           const int64_t mc = m < M ? m : M - 1;
 #pragma unroll
@@ -612,7 +613,7 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
 #pragma unroll
               for (int j = 0; j < TN; ++j) {
                 lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh1[j][h], uh, lr[j], 0, 0, 0);
-                if (!ep.l2_lo_zero)
+                if constexpr (LR == 2)
                   lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl1[j][h], uh, lr[j], 0, 0, 0);
                 lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh1[j][h], ul, lr[j], 0, 0, 0);
               }
@@ -621,7 +622,7 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
           for (int kc = 0; !lr_one && kc < ep.rank; kc += 32) {
             const bool two = kc + 16 < ep.rank;
             float uf[2][8];
-            v8bf wh[TN][2], wl[TN][2];
+            v8bf wh[TN][2], wl[LR == 2 ? TN : 1][2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const int k0 = (h == 0 || two) ? kc + 16 * h : kc;
@@ -632,8 +633,7 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
                 const int64_t nr = nb + erow < N ? nb + erow : N - 1;
                 const int64_t off = nr * ep.rank + k0 + 8 * ehalf;
                 wh[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_hi + off);
-                wl[j][h] = ep.l2_lo_zero ? wh[j][h]
-                                         : *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
+                if constexpr (LR == 2) wl[j][h] = *reinterpret_cast<const v8bf*>(ep.l2_lo + off);
               }
             }
 #pragma unroll
@@ -643,7 +643,7 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
 #pragma unroll
               for (int j = 0; j < TN; ++j) {
                 lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[j][h], uh, lr[j], 0, 0, 0);
-                if (!ep.l2_lo_zero)
+                if constexpr (LR == 2)
                   lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl[j][h], uh, lr[j], 0, 0, 0);
                 lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[j][h], ul, lr[j], 0, 0, 0);
               }
@@ -666,7 +666,7 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
             float y1 = fmaf(a[4 * g + 1], sx * sw.y, fmaf(mu, cb.y, bb.y));
             float y2 = fmaf(a[4 * g + 2], sx * sw.z, fmaf(mu, cb.z, bb.z));
             float y3 = fmaf(a[4 * g + 3], sx * sw.w, fmaf(mu, cb.w, bb.w));
-            if constexpr (LR) {
+            if constexpr (LR != 0) {
               y0 += lr[j][4 * g + 0];
               y1 += lr[j][4 * g + 1];
               y2 += lr[j][4 * g + 2];
