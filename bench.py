@@ -186,10 +186,8 @@ class Layer:
 
 def measure(hq, torch, L, desc, steps, warmup):
     """Times `steps` quant_linear calls after `warmup` (the step), then each
-    stage alone as a replayed graph: the GEMM + epilogue (hq_gemm_dequant)
-    and the activation stage (hq_act_quantize; with a low-rank branch, whose
-    stage entry point runs a different down-projection kernel than
-    quant_linear's split one, the whole quant_linear call minus the GEMM)."""
+    stage alone as a replayed graph: the activation stage as quant_linear
+    runs it (hq_act_quantize_ws) and the GEMM + epilogue (hq_gemm_dequant)."""
     w, dev = L.w, L.dev
     prep = hq.prepare(desc, L.W, L.B, L.S, L.L1, L.L2)
     ws = torch.empty(hq.workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
@@ -211,24 +209,16 @@ def measure(hq, torch, L, desc, steps, warmup):
 
         def act(i):
             hq.channel_center_into(desc, prep, L.Xs[i % nbuf], mean, bias_eff, ws)
-            hq.act_quantize(desc, prep, L.Xs[i % nbuf], out=(codes, s_x, mu, U), mean=mean)
+            hq.act_quantize(desc, prep, L.Xs[i % nbuf], out=(codes, s_x, mu, U), mean=mean,
+                            workspace=ws)
         k1 = graph_time(torch, act, n)
         k2 = graph_time(torch, lambda i: hq.gemm_dequant(desc, prep, codes, s_x, bias_eff, U,
                                                          out=L.Ys[i % nbuf]), n)
     else:
-        hq.act_quantize(desc, prep, L.Xs[0], out=(codes, s_x, mu, U))
+        k1 = graph_time(torch, lambda i: hq.act_quantize(desc, prep, L.Xs[i % nbuf],
+                                                         out=(codes, s_x, mu, U), workspace=ws), n)
         k2 = graph_time(torch, lambda i: hq.gemm_dequant(desc, prep, codes, s_x, mu, U,
                                                          out=L.Ys[i % nbuf]), n)
-        if w.rank:
-            # the activation stage as quant_linear runs it (row kernel, then the
-            # split low-rank projection into its workspace): the whole call
-            # minus the GEMM stage, both as replayed graphs on one stream
-            kq = graph_time(torch, lambda i: hq.quant_linear(desc, prep, L.Xs[i % nbuf],
-                                                             out=L.Ys[i % nbuf], workspace=ws), n)
-            k1 = kq - k2
-        else:
-            k1 = graph_time(torch, lambda i: hq.act_quantize(desc, prep, L.Xs[i % nbuf],
-                                                             out=(codes, s_x, mu, U)), n)
     return {"ms": ms, "wall": wall, "k1": k1, "k2": k2, "prep": prep}
 
 

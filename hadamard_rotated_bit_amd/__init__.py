@@ -254,14 +254,18 @@ def channel_center_into(desc: Desc, prepared: torch.Tensor, X: torch.Tensor,
                                    _stream()))
 
 
-def act_quantize(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, out=None, mean=None):
+def act_quantize(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, out=None, mean=None,
+                 workspace: Optional[torch.Tensor] = None):
     """Activation stage alone: (codes, s_x, mu [T], U [T, rank] or None); s_x
     has desc.sx_shape(T) ([T], or [d_in / 64, T] with group-wise scales).
 
     ``codes`` is a uint8 buffer of code_bytes(desc, T) bytes in the
     descriptor's code format. ``out`` may supply that tuple preallocated.
     For center = 2 the third entry is the per-channel mean [d_in] that was
-    subtracted (``mean`` if given, else channel_center's)."""
+    subtracted (``mean`` if given, else channel_center's). With ``workspace``
+    (workspace_bytes(desc, T) bytes) the stage runs exactly as inside
+    quant_linear (hq_act_quantize_ws: the two-pass low-rank projection);
+    without it, hq_act_quantize (one pass, the same bits)."""
     T = X.shape[0]
     _need(X, "X", _TORCH[desc.x_dtype], (T, desc.d_in))
     dev = X.device
@@ -282,8 +286,13 @@ def act_quantize(desc: Desc, prepared: torch.Tensor, X: torch.Tensor, out=None, 
         if desc.rank:
             _need(U, "U", torch.float32, (T, desc.rank))
     _need(mu, "mu", torch.float32, (desc.d_in,) if chan else (T,))
-    check(load().hq_act_quantize(desc._ref, _ptr(prepared), _ptr(X), T, _ptr(codes),
-                                 _ptr(s_x), _ptr(mu), _ptr(U), _stream()))
+    if workspace is None:
+        check(load().hq_act_quantize(desc._ref, _ptr(prepared), _ptr(X), T, _ptr(codes),
+                                     _ptr(s_x), _ptr(mu), _ptr(U), _stream()))
+    else:
+        check(load().hq_act_quantize_ws(desc._ref, _ptr(prepared), _ptr(X), T, _ptr(codes),
+                                        _ptr(s_x), _ptr(mu), _ptr(U), _ptr(workspace),
+                                        workspace.numel(), _stream()))
     return codes, s_x, mu, U
 
 

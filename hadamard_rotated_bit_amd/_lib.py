@@ -64,6 +64,8 @@ _SIGS = {
     "hq_quant_linear_noalloc": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P]),
     "hq_channel_center": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "hq_act_quantize": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, _P, _P, _P]),
+    "hq_act_quantize_ws": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
     "hq_act_transform": (ctypes.c_int, [_D, _P, _P, _I64, _P, _P, _P]),
     "hq_gemm_i32": (ctypes.c_int, [_D, _P, _P, _I64, _I64, _P, _P]),
     "hq_gemm_dequant": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _I64, _P, _P]),

@@ -632,6 +632,29 @@ int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, in
                  static_cast<hipStream_t>(stream));
 }
 
+int hq_act_quantize_ws(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
+                       void* codes, float* s_x, float* mu, float* U, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int st = check_desc(desc);
+  if (st != HQ_OK) return st;
+  if (T < 0) return fail(HQ_ERR_INVALID_ARG, "T must be >= 0");
+  if (T == 0) return HQ_OK;
+  if (!prepared || !X || !codes || !s_x || !mu || (desc->rank && !U) || !workspace)
+    return fail(HQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (misaligned(X) || misaligned(codes) || misaligned(prepared) || misaligned(s_x) ||
+      misaligned(mu) || misaligned(U) || misaligned(workspace))
+    return fail(HQ_ERR_INVALID_ARG,
+                "X, codes, s_x, mu, U, workspace and prepared must be 16-byte aligned");
+  const Workspace w = workspace_of(desc, T);
+  if (workspace_bytes < w.total)
+    return fail(HQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, w.total);
+  float* lr_part = w.lr_part ? at<float>(workspace, w.lr_part) : nullptr;
+  const bool chan = desc->center == HQ_CENTER_CHANNEL;
+  return run_act(desc, prepared, X, T, codes, s_x, chan ? nullptr : mu, chan ? mu : nullptr, U,
+                 static_cast<hipStream_t>(stream), lr_part);
+}
+
 int hq_act_transform(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
                      float* Xt, float* mu, void* stream) {
   g_err.clear();

@@ -287,6 +287,18 @@ int hq_channel_center(const hq_desc* desc, const void* prepared, const void* X, 
 int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
                     void* codes, float* s_x, float* mu, float* U, void* stream);
 
+/* The activation stage exactly as hq_quant_linear runs it (HadaNorm Eq. (1),
+ * HaTQ Sec. III-A Eq. (3), blog steps 3-4): the same outputs as
+ * hq_act_quantize, bit for bit, but for rank > 0 the down projection U = x' L1
+ * takes the two-pass form that keeps its per-slice products in the workspace
+ * (hq_act_quantize, which has no workspace, makes one pass with every block
+ * reading all of L1). workspace: at least hq_workspace_bytes(desc, T) bytes
+ * (only its slice-product region is written); caller-owned, contents
+ * undefined on entry and exit. Returns HQ_ERR_WORKSPACE if too small. */
+int hq_act_quantize_ws(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
+                       void* codes, float* s_x, float* mu, float* U, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Debug export of the float transform before quantisation, X~ of HadaNorm
  * Eq. (1) (H normalised as in HaTQ Eq. (7)):
  * Xt f32 [T, d_in] = X~ (centred if desc->center), mu f32 [T].

@@ -305,6 +305,8 @@ def test_entry_points_reject_misaligned_pointers():
     bad(lib.hq_act_quantize(d, p, q, 4, p, p, p, None, None))
     bad(lib.hq_act_quantize(d, p, p, 4, q, p, p, None, None))
     bad(lib.hq_act_quantize(d, q, p, 4, p, p, p, None, None))
+    bad(lib.hq_act_quantize_ws(d, p, p, 4, p, p, p, None, q, 1 << 30, None))
+    bad(lib.hq_act_quantize_ws(d, p, q, 4, p, p, p, None, p, 1 << 30, None))
     bad(lib.hq_act_transform(d, p, q, 4, p, p, None))
     bad(lib.hq_act_transform(d, p, p, 4, q, p, None))
     bad(lib.hq_gemm_i32(d, q, p, 16, 16, p, None))

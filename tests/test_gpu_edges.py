@@ -139,6 +139,15 @@ def test_low_rank_split_matches_one_pass(T, d_in, rank, xd):
     err = np.linalg.norm(to_np(U) - ora["u"], axis=1) / np.linalg.norm(ora["u"], axis=1)
     assert err.max() <= 1e-4, err.max()
     assert torch.equal(Y, hq.gemm_dequant(desc, prep, codes, s_x, mu, U))
+    # the stage entry point with a workspace runs the two-pass form itself:
+    # the same bits as the one-pass stage
+    ws = torch.empty(hq.workspace_bytes(desc, T), dtype=torch.uint8, device=X.device)
+    c2, s2, m2, U2 = hq.act_quantize(desc, prep, X, workspace=ws)
+    np.testing.assert_array_equal(codes_np(desc, c2, T), codes_np(desc, codes, T))
+    assert torch.equal(s2, s_x) and torch.equal(m2, mu) and torch.equal(U2, U)
+    small = torch.empty(hq.workspace_bytes(desc, T) - 256, dtype=torch.uint8, device=X.device)
+    with pytest.raises(hq.HqError):
+        hq.act_quantize(desc, prep, X, workspace=small)
 
 
 def test_heavy_outliers_and_no_centring():
