@@ -15,7 +15,10 @@
 //   128 x 192 (4 waves, 2 blocks / CU)  K <= 2048 with d_out % 192 == 0, where
 //                                       the 192-wide tiles fill whole waves of CUs;
 //   128 x 128 (4 waves)                 narrow outputs (d_out <= 512).
-#include "hq_gemm_kernel.h"
+// bf16 outputs of larger problems take the persistent kernel instead
+// (gemm_i8_persist, hq_gemm6_kernel.h: one block per CU walking 256 x 192
+// tiles with the stage pipeline running across tile boundaries).
+#include "hq_gemm6_kernel.h"
 #include "hq_internal.h"
 
 namespace hq {
@@ -39,9 +42,39 @@ static hipError_t launch_cfg(const int8_t* A, int64_t M, const int8_t* B, int64_
   return hipGetLastError();
 }
 
+template <int LR>
+static hipError_t launch_i8_persist(const int8_t* A, int64_t M, const int8_t* B, int64_t N, int K,
+                                    const GemmEpi& ep, int cus, hipStream_t s) {
+  const int64_t ntiles = ((M + 255) / 256) * ((N + 191) / 192);
+  const unsigned grid = unsigned(ntiles < cus ? ntiles : cus);
+  hipLaunchKernelGGL((gemm_i8_persist<256, 192, 128, 96, 4, LR>), dim3(grid), dim3(256), 0, s,
+                     reinterpret_cast<const uint8_t*>(A), M, reinterpret_cast<const uint8_t*>(B),
+                     N, K, ep);
+  return hipGetLastError();
+}
+
+static int cu_count() {
+  // CU count per device, queried once (racing writers store the same value).
+  static int cu_cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cu_cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cu_cache[dev] = n;
+  }
+  return cu_cache[dev] > 0 ? cu_cache[dev] : 256;
+}
+
 hipError_t launch_gemm(const int8_t* A, int64_t M, const int8_t* B, int64_t N, int K,
                        int32_t* acc_out, int64_t ldc, const GemmEpi* epi, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (epi && epi->y_bf16 && K % 64 == 0 && K >= 192 && M > 512 && N > 512) {
+    const int cus = cu_count();
+    return !epi->rank         ? launch_i8_persist<0>(A, M, B, N, K, *epi, cus, s)
+           : epi->l2_lo_zero ? launch_i8_persist<1>(A, M, B, N, K, *epi, cus, s)
+                             : launch_i8_persist<2>(A, M, B, N, K, *epi, cus, s);
+  }
   if (N <= 512 || M <= 512)
     return launch_cfg<128, 128, 128, 64, 64, 3, 8, 1>(A, M, B, N, K, acc_out, ldc, epi, s);
   if (K <= 2048 && N % 192 == 0)

@@ -35,6 +35,8 @@
 // the MFMAs of stage kt. Each stage load has two iterations to land.
 #pragma once
 
+#include <type_traits>
+
 #include "hq_gemm_kernel.h"
 
 namespace hq {
@@ -358,18 +360,30 @@ __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_f6_kernel(
 // iteration earlier (LPW). The prologue issues NST stores that move no
 // memory so that the first tile has the same sequence. A tile's parameters
 // are retired by its k-step 2 (K >= 384: three stages per tile).
-template <int BM, int BN, int WM, int WN, int GM, int RG, int LR>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
-    const uint8_t* __restrict__ A, int64_t M, const uint8_t* __restrict__ B, int64_t N, int K,
-    GemmEpi ep) {
+//
+// The same body serves int8 codes (I8; gemm_i8_persist): a stage is then 64
+// codes, i.e. 64-byte rows stored with the int8 kernel's chunk swizzle
+// (chunk c of row r in slot c ^ ((r >> 2) & 3): the 16 lanes of a
+// ds_read_b128 phase hit 16 distinct 16-byte positions), one 1-KB DMA unit
+// holds 16 rows, and each 32-code half of a stage is one
+// v_mfma_i32_32x32x32_i8 per 32 x 32 output (int32 accumulators, converted
+// to float in the epilogue). K >= 192, K % 64 == 0.
+struct Frag8 {
+  v4i c[2];
+};
+template <bool I8, int BM, int BN, int WM, int WN, int GM, int RG, int LR>
+__device__ __forceinline__ void persist_body(const uint8_t* __restrict__ A, int64_t M,
+                                             const uint8_t* __restrict__ B, int64_t N, int K,
+                                             GemmEpi ep) {
   constexpr int S = 3;
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int WAVES_N = BN / WN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int STAGE = 96 * (BM + BN);
-  constexpr int UA = 3 * BM / 32;
-  constexpr int UNITS = 3 * (BM + BN) / 32;
+  constexpr int RB = I8 ? 64 : 96;             // bytes of a row per stage
+  constexpr int KS = I8 ? 64 : 128;            // codes per stage
+  constexpr int STAGE = RB * (BM + BN);
+  constexpr int UA = I8 ? BM / 16 : 3 * BM / 32;
+  constexpr int UNITS = I8 ? (BM + BN) / 16 : 3 * (BM + BN) / 32;
   constexpr int LPW = (UNITS + NW - 1) / NW;
   constexpr int QA = UA / NW;
   constexpr int NP = 3 * BN + 2 * BM;          // floats per parameter buffer
@@ -394,23 +408,31 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint8_t* const stg = lds + 2 * 4 * NP + wv * 32 * SP;
   const int wm0 = (wv / WAVES_N) * WM, wn0 = (wv % WAVES_N) * WN;
-  const int KT = K / 128;
-  const int64_t lda = f6_row_bytes(K);
+  const int KT = K / KS;
+  const int64_t lda = I8 ? int64_t(K) : f6_row_bytes(K);
   const int ntiles = int((M + BM - 1) / BM) * int((N + BN - 1) / BN);
   const int G = int(gridDim.x);
 
   // Three 1-KB units cover 32 rows exactly (192 chunks of 16 B), so the
   // global offset of unit 3t + r is that of unit r plus 32 t rows: each
   // lane keeps the offsets of units 0, 1 and 2 only.
-  static_assert(UA % 3 == 0 && 32 % RG == 0, "unit triples are whole row groups");
+  // (int8: every unit holds 16 whole rows and lane l always fetches row
+  // l / 4 of it, global chunk (l % 4) ^ ((l / 16) % 4): one offset, vb[0].)
+  static_assert(I8 || (UA % 3 == 0 && 32 % RG == 0), "unit triples are whole row groups");
+  static_assert(UA % NW == 0, "A units split evenly over the waves");
   uint32_t vb[3];
+  if constexpr (I8) {
+    vb[0] = uint32_t((lane >> 2) * lda + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+    vb[1] = vb[2] = vb[0];
+  } else {
 #pragma unroll
-  for (int r = 0; r < 3; ++r) {
-    const int c = 64 * r + lane;
-    const int row = c / 6, slot = c - 6 * (c / 6);
-    const int h = (slot >= 3 ? 1 : 0) ^ ((row >> 3) & 1);
-    vb[r] = uint32_t((row / RG) * RG * lda + (row % RG) * 96 + 48 * h +
-                     16 * (slot - 3 * (slot >= 3 ? 1 : 0)));
+    for (int r = 0; r < 3; ++r) {
+      const int c = 64 * r + lane;
+      const int row = c / 6, slot = c - 6 * (c / 6);
+      const int h = (slot >= 3 ? 1 : 0) ^ ((row >> 3) & 1);
+      vb[r] = uint32_t((row / RG) * RG * lda + (row % RG) * 96 + 48 * h +
+                       16 * (slot - 3 * (slot >= 3 ? 1 : 0)));
+    }
   }
 
   // Source rows of a tile: base pointers and descriptor sizes (0 past the end).
@@ -452,31 +474,61 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
       int u_ = q * NW + wv;                                                               \
       if (u_ > UNITS - 1) u_ = UNITS - 1;                                                 \
       const int ul_ = q < QA ? u_ : u_ - UA;                                              \
-      const int t_ = ul_ / 3, r_ = ul_ - 3 * t_;                                          \
-      const uint32_t vo_ = (r_ == 0 ? vb[0] : (r_ == 1 ? vb[1] : vb[2])) +                \
-                           uint32_t(t_) * uint32_t(32 * lda);                             \
-      lds_dma16_buf(q < QA ? ra_ : rb_, vo_, uint32_t(ks_) * (96u * RG), base_ + u_ * 1024); \
+      if constexpr (I8) {                                                                 \
+        lds_dma16_buf(q < QA ? ra_ : rb_, vb[0],                                          \
+                      uint32_t(ks_) * 64u + uint32_t(ul_) * uint32_t(16 * lda),           \
+                      base_ + u_ * 1024);                                                 \
+      } else {                                                                            \
+        const int t_ = ul_ / 3, r_ = ul_ - 3 * t_;                                        \
+        const uint32_t vo_ = (r_ == 0 ? vb[0] : (r_ == 1 ? vb[1] : vb[2])) +              \
+                             uint32_t(t_) * uint32_t(32 * lda);                           \
+        lds_dma16_buf(q < QA ? ra_ : rb_, vo_, uint32_t(ks_) * (96u * RG),                \
+                      base_ + u_ * 1024);                                                 \
+      }                                                                                   \
     }                                                                                     \
   } while (0)
 
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int loff = lrow * 96 + 48 * (lhalf ^ ((lrow >> 3) & 1));
+  // FP6: the lane's 48 bytes of its row (halves swapped on rows with bit 3);
+  // int8: chunk p (0, 1) of the lane's 32-code half h is global chunk
+  // 2 p + h, stored in slot (2 p + h) ^ ((row >> 2) & 3) (every 32-row block
+  // starts on a multiple of 4 rows, so the slot depends on lrow only).
+  const int loff = I8 ? lrow * 64 : lrow * 96 + 48 * (lhalf ^ ((lrow >> 3) & 1));
+  const int lsl0 = 16 * ((0 + lhalf) ^ ((lrow >> 2) & 3));
+  const int lsl1 = 16 * ((2 + lhalf) ^ ((lrow >> 2) & 3));
 #define HP_READ(SET_, BUF_)                                                               \
   do {                                                                                    \
     const uint8_t* cur_ = smem + (BUF_) * STAGE + loff;                                   \
-    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                        \
-      _Pragma("unroll") for (int p = 0; p < 3; ++p) af[SET_][i].c[p] =                    \
-          *reinterpret_cast<const v4i*>(cur_ + (wm0 + 32 * i) * 96 + 16 * p);             \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
-      _Pragma("unroll") for (int p = 0; p < 3; ++p) bf[SET_][j].c[p] =                    \
-          *reinterpret_cast<const v4i*>(cur_ + (BM + wn0 + 32 * j) * 96 + 16 * p);        \
+    if constexpr (I8) {                                                                   \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                    \
+        af[SET_][i].c[0] = *reinterpret_cast<const v4i*>(cur_ + (wm0 + 32 * i) * 64 + lsl0); \
+        af[SET_][i].c[1] = *reinterpret_cast<const v4i*>(cur_ + (wm0 + 32 * i) * 64 + lsl1); \
+      }                                                                                   \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                    \
+        bf[SET_][j].c[0] = *reinterpret_cast<const v4i*>(cur_ + (BM + wn0 + 32 * j) * 64 + lsl0); \
+        bf[SET_][j].c[1] = *reinterpret_cast<const v4i*>(cur_ + (BM + wn0 + 32 * j) * 64 + lsl1); \
+      }                                                                                   \
+    } else {                                                                              \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                      \
+        _Pragma("unroll") for (int p = 0; p < 3; ++p) af[SET_][i].c[p] =                  \
+            *reinterpret_cast<const v4i*>(cur_ + (wm0 + 32 * i) * 96 + 16 * p);           \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                      \
+        _Pragma("unroll") for (int p = 0; p < 3; ++p) bf[SET_][j].c[p] =                  \
+            *reinterpret_cast<const v4i*>(cur_ + (BM + wn0 + 32 * j) * 96 + 16 * p);      \
+    }                                                                                     \
   } while (0)
 #define HP_MFMA(SET_)                                                                     \
   do {                                                                                    \
     _Pragma("unroll") for (int i = 0; i < TM; ++i)                                        \
       _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                    \
-        acc[i][j] = mfma_f6(f6_op0(bf[SET_][j]), f6_op0(af[SET_][i]), acc[i][j]);         \
-        acc[i][j] = mfma_f6(f6_op1(bf[SET_][j]), f6_op1(af[SET_][i]), acc[i][j]);         \
+        if constexpr (I8) {                                                               \
+          _Pragma("unroll") for (int p = 0; p < 2; ++p) acc[i][j] =                       \
+              __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[SET_][j].c[p], af[SET_][i].c[p],   \
+                                                    acc[i][j], 0, 0, 0);                  \
+        } else {                                                                          \
+          acc[i][j] = mfma_f6(f6_op0(bf[SET_][j]), f6_op0(af[SET_][i]), acc[i][j]);       \
+          acc[i][j] = mfma_f6(f6_op1(bf[SET_][j]), f6_op1(af[SET_][i]), acc[i][j]);       \
+        }                                                                                 \
       }                                                                                   \
   } while (0)
   // One iteration on k-step KT_ of the current tile (fragments in SET_):
@@ -493,18 +545,20 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
     HP_ISSUE((KT_) + 3, bufc);                                                            \
     HP_READ(1 - (SET_), bn_);                                                             \
     HP_MFMA(SET_);                                                                        \
-    mfma_interleave<0, 2 * TM * TN, 3 * (TM + TN), LPW>();                                \
+    mfma_interleave<0, 2 * TM * TN, (I8 ? 2 : 3) * (TM + TN), LPW>();                     \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     bufc = bn_;                                                                           \
   } while (0)
 
-  v16f acc[TM][TN];
-  Frag6 af[2][TM], bf[2][TN];
+  using Acc = std::conditional_t<I8, v16i, v16f>;
+  using Frag = std::conditional_t<I8, Frag8, Frag6>;
+  Acc acc[TM][TN];
+  Frag af[2][TM], bf[2][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      acc[i][j] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      acc[i][j] = Acc{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
   HP_ISSUE(0, 0);
   HP_ISSUE(1, 1);
@@ -661,11 +715,11 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
             const float4 sw = make_float4(Pf[nl], Pf[nl+1], Pf[nl+2], Pf[nl+3]);
             const float4 cb = make_float4(Pf[BN+nl], Pf[BN+nl+1], Pf[BN+nl+2], Pf[BN+nl+3]);
             const float4 bb = make_float4(Pf[2*BN+nl], Pf[2*BN+nl+1], Pf[2*BN+nl+2], Pf[2*BN+nl+3]);
-            const v16f& a = acc[i][j];
-            float y0 = fmaf(a[4 * g + 0], sx * sw.x, fmaf(mu, cb.x, bb.x));
-            float y1 = fmaf(a[4 * g + 1], sx * sw.y, fmaf(mu, cb.y, bb.y));
-            float y2 = fmaf(a[4 * g + 2], sx * sw.z, fmaf(mu, cb.z, bb.z));
-            float y3 = fmaf(a[4 * g + 3], sx * sw.w, fmaf(mu, cb.w, bb.w));
+            const Acc& a = acc[i][j];
+            float y0 = fmaf(float(a[4 * g + 0]), sx * sw.x, fmaf(mu, cb.x, bb.x));
+            float y1 = fmaf(float(a[4 * g + 1]), sx * sw.y, fmaf(mu, cb.y, bb.y));
+            float y2 = fmaf(float(a[4 * g + 2]), sx * sw.z, fmaf(mu, cb.z, bb.z));
+            float y3 = fmaf(float(a[4 * g + 3]), sx * sw.w, fmaf(mu, cb.w, bb.w));
             if constexpr (LR != 0) {
               y0 += lr[j][4 * g + 0];
               y1 += lr[j][4 * g + 1];
@@ -722,13 +776,29 @@ __attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        acc[i][j] = Acc{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   }
   wait_vm_lgkm0<0>();  // no LDS write may land after the block ends
 #undef HP_STEP
 #undef HP_MFMA
 #undef HP_READ
 #undef HP_ISSUE
+}
+
+template <int BM, int BN, int WM, int WN, int GM, int RG, int LR>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(1))) void gemm_f6_persist(
+    const uint8_t* __restrict__ A, int64_t M, const uint8_t* __restrict__ B, int64_t N, int K,
+    GemmEpi ep) {
+  persist_body<false, BM, BN, WM, WN, GM, RG, LR>(A, M, B, N, K, ep);
+}
+
+template <int BM, int BN, int WM, int WN, int GM, int LR>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(1))) void gemm_i8_persist(
+    const uint8_t* __restrict__ A, int64_t M, const uint8_t* __restrict__ B, int64_t N, int K,
+    GemmEpi ep) {
+  persist_body<true, BM, BN, WM, WN, GM, 1, LR>(A, M, B, N, K, ep);
 }
 
 }  // namespace hq
