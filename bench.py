@@ -104,7 +104,25 @@ def cpu_baseline(w, x, weight, bias, sigma, l1, l2, Y_gpu, target_s):
     y = Y_gpu[:rows].float().cpu().numpy().astype(np.float64)
     ref = r["y_out"]
     err = float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
+    # one thread on the two small workloads (the tiny layer and the
+    # learned-image-coding 1x1 convolution), a prefix of up to 2048 tokens
+    from oracle import hq_oracle as O
+    from hadamard_rotated_bit_amd import workloads as WL
+    single = {}
+    for name in ("tiny", "lic_dh"):
+        wc = WL.WORKLOADS[name]
+        xc, wt, bc = WL.gen_x(wc), WL.gen_weight(wc), WL.gen_bias(wc)
+        sg = (O.smoothing_scales(xc, wt, wc.alpha) if wc.alpha is not None
+              else np.ones(wc.d_in))
+        pc = C.prepare_weights(wt, sg, wc.block, wc.w_bits, threads=1)
+        n = min(wc.T, 2048)
+        t0 = time.perf_counter()
+        C.quant_linear(xc[:n], pc, bc, sg, block=wc.block, a_bits=wc.a_bits,
+                       center=int(wc.center), out_dtype=wc.out_dtype, want_acc=False, threads=1)
+        single[name] = {"value": n / (time.perf_counter() - t0), "unit": "tokens/s",
+                        "cores": 1, "sample": f"first {n} of {wc.T} tokens"}
     return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle-c++",
+            "single_thread": single,
             "sample": f"first {rows} of {w.T} tokens of {w.name}, float64 C++17 oracle "
                       f"(online half, std::thread on {cores} host cores, prepared weights "
                       f"reused), {dt:.2f} s; weight preparation {prep_s:.2f} s, not timed",
@@ -123,6 +141,20 @@ def timed_steps(torch, fn, nbuf, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+
+
+def step_percentiles(torch, fn, nbuf, steps, start):
+    """p10 / p50 / p90 of `steps` individually event-timed calls fn(i) issued
+    back to back (ms), after the bracketed run."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        fn((start + i) % nbuf)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    pick = lambda q: round(d[int(round(q * (len(d) - 1)))], 5)
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
 
 
 def graph_time(torch, fn, n):
@@ -201,6 +233,7 @@ def measure(hq, torch, L, desc, steps, warmup):
         hq.quant_linear(desc, prep, L.Xs[i], out=L.Ys[i], workspace=ws)
 
     ms, wall = timed_steps(torch, step, nbuf, steps, warmup)
+    pct = step_percentiles(torch, step, nbuf, steps, warmup + steps)
     n = max(1, min(steps, 20))
     if int(desc.center) == hq.HQ_CENTER_CHANNEL:
         # per-channel centring: the statistics stage (column means and the
@@ -219,7 +252,7 @@ def measure(hq, torch, L, desc, steps, warmup):
                                                          out=(codes, s_x, mu, U), workspace=ws), n)
         k2 = graph_time(torch, lambda i: hq.gemm_dequant(desc, prep, codes, s_x, mu, U,
                                                          out=L.Ys[i % nbuf]), n)
-    return {"ms": ms, "wall": wall, "k1": k1, "k2": k2, "prep": prep}
+    return {"ms": ms, "wall": wall, "k1": k1, "k2": k2, "prep": prep, "pct": pct}
 
 
 def kernel_figures(hq, desc, w, r):
@@ -249,6 +282,7 @@ def kernel_figures(hq, desc, w, r):
         "engine": "e2m3 fp6 mfma" if fp6 else "int8 mfma",
         "value": round(w.T / (r["ms"] * 1e-3), 1), "unit": "tokens/s",
         "ms_per_step": round(r["ms"], 5),
+        "ms_per_step_percentiles": r["pct"],
         "effective_TOPS_step": round(k2_ops / (r["ms"] * 1e-3) / 1e12, 2),
         "k1": {"ms": round(r["k1"], 5), "bytes": int(k1_bytes), "GBs": round(k1_gbs, 1),
                "hbm_frac": round(k1_gbs / HBM_PEAK_GBS, 4),
