@@ -77,6 +77,23 @@ def test_ragged_outputs_large_tiles(T, d_out, gemm):
     check_all(r[3], r[4], r[5], r[8], r[0])
 
 
+@pytest.mark.parametrize("gemm", ENGINES)
+@pytest.mark.parametrize("rank,wd", [(0, "bf16"), (32, "bf16"), (32, "f32"), (64, "bf16")])
+def test_persistent_gemm_ragged(rank, wd, gemm):
+    # bf16 output with K >= 384 and M, N > 512 takes the persistent GEMM of
+    # either engine: 777 tokens (three full 256-row tiles and 9 rows) by 1160
+    # outputs (six 192-column tiles and 8 columns), every low-rank epilogue
+    # instance (none; bf16 L2, which has no low half; fp32 L2, hi + lo; rank
+    # 64, taken in 32-rank chunks)
+    r = run_case(777, 1024, 1160, block=256, rank=rank, x_dtype="bf16", w_dtype=wd,
+                 y_dtype="bf16", gemm=gemm)
+    desc, prep, X, Y, codes, s_x, mu, U, ora = r
+    check_all(Y, codes, s_x, ora, desc)
+    if rank:
+        err = np.linalg.norm(to_np(U) - ora["u"], axis=1) / np.linalg.norm(ora["u"], axis=1)
+        assert err.max() <= 1e-4, err.max()
+
+
 def test_zero_and_degenerate_rows():
     d = 128
     rng = np.random.default_rng(5)
