@@ -69,7 +69,7 @@ static int cu_count() {
 hipError_t launch_gemm(const int8_t* A, int64_t M, const int8_t* B, int64_t N, int K,
                        int32_t* acc_out, int64_t ldc, const GemmEpi* epi, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (epi && epi->y_bf16 && K % 64 == 0 && K >= 192 && M > 512 && N > 512) {
+  if (epi && epi->y_bf16 && K % 64 == 0 && K >= 256 && M > 512 && N > 512) {
     const int cus = cu_count();
     return !epi->rank         ? launch_i8_persist<0>(A, M, B, N, K, *epi, cus, s)
            : epi->l2_lo_zero ? launch_i8_persist<1>(A, M, B, N, K, *epi, cus, s)

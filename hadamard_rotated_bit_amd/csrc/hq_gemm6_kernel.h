@@ -344,8 +344,9 @@ __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_f6_kernel(
 // most one block per CU): the block walks the tiles blockIdx.x,
 // blockIdx.x + gridDim.x, ... with a single stage pipeline across tile
 // boundaries. Global stage g (tile g / KT, k-step g % KT) lives in buffer
-// g mod 3, so the last iterations of a tile already load the first three
-// stages of the next one and those loads overlap the epilogue.
+// g mod S (S = 3 stage buffers for FP6 codes, 4 for int8), so the last S
+// iterations of a tile already load the first S stages of the next one and
+// those loads overlap the epilogue.
 //
 // The epilogue does not touch the stage buffers: each wave stages its
 // 32-row slices in a private LDS area and writes them back with 16-byte
@@ -354,12 +355,13 @@ __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_f6_kernel(
 // parameters are loaded into the other of two parameter buffers. Every wave
 // thus issues, per tile, KT stage loads of LPW instructions, NST stores and
 // PPW parameter loads, in a fixed order, and the waits count them (vector
-// memory operations retire in issue order): k-steps 0 and 1 may leave the
+// memory operations retire in issue order): k-steps 0 .. S - 2 may leave the
 // previous epilogue's stores and parameter loads in flight
-// (LPW + NST + PPW outstanding), later k-steps only the stage loaded one
-// iteration earlier (LPW). The prologue issues NST stores that move no
-// memory so that the first tile has the same sequence. A tile's parameters
-// are retired by its k-step 2 (K >= 384: three stages per tile).
+// ((S - 2) LPW + NST + PPW outstanding), later k-steps only the S - 2 stages
+// loaded after the one they need ((S - 2) LPW). The prologue issues NST
+// stores that move no memory so that the first tile has the same sequence.
+// A tile's parameters are retired by its k-step S - 1 (at least S stages per
+// tile: K >= 384 for FP6 codes).
 //
 // The same body serves int8 codes (I8; gemm_i8_persist): a stage is then 64
 // codes, i.e. 64-byte rows stored with the int8 kernel's chunk swizzle
@@ -367,7 +369,9 @@ __attribute__((amdgpu_waves_per_eu(OCC))) void gemm_f6_kernel(
 // ds_read_b128 phase hit 16 distinct 16-byte positions), one 1-KB DMA unit
 // holds 16 rows, and each 32-code half of a stage is one
 // v_mfma_i32_32x32x32_i8 per 32 x 32 output (int32 accumulators, converted
-// to float in the epilogue). K >= 192, K % 64 == 0.
+// to float in the epilogue). Four stage buffers (28 KB each) fit beside the
+// staging and parameter areas, so each stage load has three iterations to
+// land. K >= 256, K % 64 == 0.
 struct Frag8 {
   v4i c[2];
 };
@@ -375,7 +379,8 @@ template <bool I8, int BM, int BN, int WM, int WN, int GM, int RG, int LR>
 __device__ __forceinline__ void persist_body(const uint8_t* __restrict__ A, int64_t M,
                                              const uint8_t* __restrict__ B, int64_t N, int K,
                                              GemmEpi ep) {
-  constexpr int S = 3;
+  // stage buffers: three 43-KB FP6 stages, four 28-KB int8 stages
+  constexpr int S = I8 ? 4 : 3;
   constexpr int NW = (BM / WM) * (BN / WN);
   constexpr int WAVES_N = BN / WN;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -392,10 +397,14 @@ __device__ __forceinline__ void persist_body(const uint8_t* __restrict__ A, int6
   constexpr int SP = 2 * WN + 8;               // staging pitch (bytes)
   constexpr int SPS = 32 * CPR / 64;           // stores per slice
   constexpr int NST = TM * SPS;                // stores per wave and tile
-  constexpr int WBIG = LPW + NST + PPW;
+  // outstanding vector-memory operations a k-step's wait allows: the S - 2
+  // stages loaded after the one it needs, plus, in the first S - 1 k-steps
+  // of a tile, the previous epilogue's stores and parameter loads
+  constexpr int WSTEP = (S - 2) * LPW;
+  constexpr int WBIG = WSTEP + NST + PPW;
   static_assert(UA % NW == 0 && BM % 32 == 0 && BN % 32 == 0, "whole 1-KB units per tile");
   static_assert((32 * CPR) % 64 == 0, "whole store instructions per slice");
-  static_assert(2 * LPW + NST + PPW <= 63, "outstanding count fits vmcnt");
+  static_assert((S - 1) * LPW + NST + PPW <= 63, "outstanding count fits vmcnt");
   static_assert((((SP / 4) % 64) & 3) == 2, "staging pitch = 2 x odd dwords mod 64 banks");
   // LDS: two parameter buffers, the waves' staging areas, the stage buffers
   // (the epilogue's accesses keep small constant offsets).
@@ -533,16 +542,16 @@ __device__ __forceinline__ void persist_body(const uint8_t* __restrict__ A, int6
   } while (0)
   // One iteration on k-step KT_ of the current tile (fragments in SET_):
   // wait for the next global stage, join the block, refill the current
-  // buffer with the stage three ahead, prefetch the fragments of the next
+  // buffer with the stage S ahead, prefetch the fragments of the next
   // global stage (at the tile's last k-step: the next tile's first), run the
   // MFMAs.
 #define HP_STEP(SET_, KT_)                                                                \
   do {                                                                                    \
-    if ((KT_) < 2) wait_vm_lgkm0<WBIG>(); else wait_vm_lgkm0<LPW>();                      \
+    if ((KT_) < S - 1) wait_vm_lgkm0<WBIG>(); else wait_vm_lgkm0<WSTEP>();                \
     __builtin_amdgcn_s_barrier();                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     const int bn_ = bufc == S - 1 ? 0 : bufc + 1;                                         \
-    HP_ISSUE((KT_) + 3, bufc);                                                            \
+    HP_ISSUE((KT_) + S, bufc);                                                            \
     HP_READ(1 - (SET_), bn_);                                                             \
     HP_MFMA(SET_);                                                                        \
     mfma_interleave<0, 2 * TM * TN, (I8 ? 2 : 3) * (TM + TN), LPW>();                     \
@@ -563,6 +572,7 @@ __device__ __forceinline__ void persist_body(const uint8_t* __restrict__ A, int6
   HP_ISSUE(0, 0);
   HP_ISSUE(1, 1);
   HP_ISSUE(2, 2);
+  if constexpr (S == 4) HP_ISSUE(3, 3);
   {
     const __amdgpu_buffer_rsrc_t none = make_rsrc(ep.Y, 0);
     const v4i z = v4i{0, 0, 0, 0};
@@ -570,7 +580,7 @@ __device__ __forceinline__ void persist_body(const uint8_t* __restrict__ A, int6
     for (int q = 0; q < NST; ++q) __builtin_amdgcn_raw_buffer_store_b128(z, none, 16 * q, 0, 0);
   }
   params_dma_fixed<BM, BN, NW>(lds, wv, lane, cur.m0, cur.n0, M, N, ep);
-  wait_vm_lgkm0<2 * LPW + NST + PPW>();
+  wait_vm_lgkm0<(S - 1) * LPW + NST + PPW>();
   __builtin_amdgcn_s_barrier();
   HP_READ(0, 0);
   for (;;) {
