@@ -360,15 +360,39 @@ def run(x, weight, bias, *, block: int, a_bits: int, w_bits: int, center,
 # channels with gamma = sqrt(m), which for a WH layer followed by a WH layer
 # restores the original basis (Table I, WH-to-WH), for a DH layer followed by
 # a DH layer produces the next layer's H_in basis (DH-to-DH), and with m = 1
-# is no transform (DH-to-WH). Readings taken where the pages leave a step
-# open:
+# is no transform (DH-to-WH).
+#
+# With an activation phi between the layers (Table I, Eq. (20)-(22); supplement
+# Sec. VIII-C Eq. (45)-(49)) the transition has two transforms: ``block`` (the
+# output-side H_out of a WH layer, before phi) and ``post_block`` (the next
+# layer's input-side H_in when that layer is DH, after phi); WH-to-DH uses
+# both. For phi = identity or ReLU (positively homogeneous) one multiplier per
+# channel and one shift carry the whole transition:
+#   y = clamp(round(H~_post(phi(H~_block(M . a))) / 2^n)),
+#   rho_c = s_A,c / (sqrt(block post_block) s_y).
+# For SiLU and GELU (not homogeneous) the pre-activation goes onto its own int8
+# grid s_z first, phi runs as a 255-entry integer lookup table, and a second
+# multiplier-shift pair moves the result onto the next layer's grid:
+#   z = clamp(round(H~_block(M_out . a) / 2^n_out)),  M_out ~ 2^n_out s_A / (sqrt(block) s_z)
+#   u = LUT[z] = clamp(round(phi(s_z z) / s_u))
+#   y = clamp(round(H~_post(M_in u) / 2^n_in)),        M_in ~ 2^n_in s_u / (sqrt(post_block) s_y)
+# Readings taken where the pages leave a step open:
 # * H is the normalised Sylvester matrix of the stated order (a power of two
 #   dividing the channel count), block-diagonal over contiguous blocks; the
-#   full order is the pages' transform. WH-to-DH (two transforms around the
-#   activation) and padded or Paley orders are not built.
+#   full order is the pages' transform. Padded or Paley orders are not built.
 # * M_c = round(2^n rho_c) with one shared shift n: the largest n in [0, 48]
-#   for which every M_c fits a positive 16-bit integer (<= 32767), the
-#   multiplier-precision constraint of Eq. (19); n = 0 when every rho_c is 0.
+#   for which every M_c fits the multiplier bound, the multiplier-precision
+#   and overflow constraints of Eq. (19); n = 0 when every rho_c is 0. The
+#   bound is 32767 (a positive 16-bit integer) unless the transforms' growth
+#   needs less: with block * post_block = 2^L the bound is
+#   min(32767, 2^(24 - L) - 1), so that |H~ H~ (M a)| stays below 2^52
+#   (two order-256 transforms: M <= 255).
+# * A DH layer has no output-side transform (Table I: H_out = I for DH): with
+#   an activation its next-layer transform goes in ``post_block`` and
+#   ``block`` must be 1. Without one (phi = identity) the two positions give
+#   the same integers.
+# * GELU is x Phi(x) with the Gaussian CDF (the erf form), SiLU x / (1 + e^-x);
+#   the table is built in float64 and rounded half to even.
 # * Bias codes saturate at +-2^27: with |a| <= 127^2 d_in <= 2^27 and M <= 32767,
 #   every intermediate of the requantisation then stays below 2^51 in magnitude.
 # * round() is round half to even throughout, on exact rationals.
@@ -391,16 +415,49 @@ def round_half_even_shift(v, n: int) -> np.ndarray:
     return q + up.astype(np.int64)
 
 
-def requant_shift(rho) -> int:
+def requant_shift(rho, mult_max: int = RQ_MULT_MAX) -> int:
     """The shared right shift n of Eq. (19) (see the reading above)."""
     rho = np.asarray(rho, dtype=np.float64)
     top = float(rho.max()) if rho.size else 0.0
     if top <= 0.0:
         return 0
     n = 0
-    while n < RQ_SHIFT_MAX and np.rint(top * 2.0 ** (n + 1)) <= RQ_MULT_MAX:
+    while n < RQ_SHIFT_MAX and np.rint(top * 2.0 ** (n + 1)) <= mult_max:
         n += 1
     return n
+
+
+def mult_bound(orders: int) -> int:
+    """Multiplier bound for transforms whose orders multiply to ``orders``:
+    |a + b_int| < 2^28, so M < 2^(24 - log2(orders)) keeps every output of the
+    unnormalised transforms below 2^52 (see the reading above)."""
+    lg = int(orders).bit_length() - 1
+    return min(RQ_MULT_MAX, 2 ** (24 - lg) - 1)
+
+
+ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU = 0, 1, 2, 3
+
+
+def silu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def gelu(x):
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+PHI = {ACT_SILU: silu, ACT_GELU: gelu}
+
+
+def act_table(phi, s_z: float, s_u: float, bits: int = 8) -> np.ndarray:
+    """The integer activation of Eq. (47) as a table over the int8 grid:
+    entry z + qmax = clamp(round(phi(s_z z) / s_u), +-qmax) for |z| <= qmax."""
+    qmax = 2 ** (bits - 1) - 1
+    z = np.arange(-qmax, qmax + 1, dtype=np.float64)
+    return np.clip(np.rint(phi(float(s_z) * z) / float(s_u)), -qmax, qmax).astype(np.int64)
 
 
 def unnormalised_transform(u, block: int) -> np.ndarray:
@@ -417,21 +474,36 @@ SIDE_WH, SIDE_DH = 0, 1
 
 
 def int_prepare(weight, bias, s_x: float, s_y: float, block: int, side: int = SIDE_WH,
-                in_block: int = 1, w_bits: int = 8):
+                in_block: int = 1, w_bits: int = 8, act: int = ACT_NONE, post_block: int = 1,
+                s_z: float = 0.0, s_u: float = 0.0, phi=None):
     """Offline half of an integer-only layer (HaTQ Eq. (13)-(19), supplement
-    Eq. (40)-(44)).
+    Eq. (40)-(49)).
 
     weight [d_out, d_in] (row c = output channel c), bias [d_out], s_x the
     static scale of the int8 input, s_y the scale of the int8 output (the
     next layer's input scale), block = m, the order of the output-side
     integer transform (for WH also the order of H_out on the weight), side
     SIDE_WH or SIDE_DH, in_block the order of H_in on a DH weight.
+    act: ACT_NONE, ACT_RELU, ACT_SILU or ACT_GELU (``phi``, a float64
+    function, overrides the SiLU/GELU table's function); post_block: the
+    order of the transform after the activation (the next layer's H_in);
+    s_z, s_u: the int8 grids before and after a SiLU/GELU table.
     Returns W-bar, b-bar, the weight codes and scales, the bias codes
-    b_int = round(b-bar / (s_x s_w)), rho, the shift n and the multipliers M."""
+    b_int = round(b-bar / (s_x s_w)), rho, the shift n and the multipliers M
+    (for SiLU/GELU: M_out and n_out, plus the table, M_in and n_in)."""
     weight = np.asarray(weight, dtype=np.float64)
     d_out, d_in = weight.shape
     if d_out % block:
         raise ValueError("block must divide d_out")
+    if post_block < 1 or post_block & (post_block - 1) or d_out % post_block:
+        raise ValueError("post_block must be a power of two dividing d_out")
+    if act not in (ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU):
+        raise ValueError(f"unknown activation {act}")
+    if side == SIDE_DH and act != ACT_NONE and block != 1:
+        raise ValueError("a DH layer has no output-side transform: use post_block")
+    general = act in (ACT_SILU, ACT_GELU)
+    if general and not (s_z > 0 and s_u > 0):
+        raise ValueError("SiLU/GELU need the grids s_z > 0 and s_u > 0")
     bias = np.asarray(bias, dtype=np.float64)
     if side == SIDE_WH:
         # H_out acts on the output-channel index: column-wise on weight, row-wise on b
@@ -449,36 +521,74 @@ def int_prepare(weight, bias, s_x: float, s_y: float, block: int, side: int = SI
     b_int = np.zeros(d_out, dtype=np.int64)
     nz = s_a > 0
     b_int[nz] = np.clip(np.rint(bbar[nz] / s_a[nz]), -RQ_BIAS_MAX, RQ_BIAS_MAX).astype(np.int64)
-    rho = s_a / (np.sqrt(block) * float(s_y))
-    n = requant_shift(rho)
-    m_c = np.rint(rho * 2.0 ** n).astype(np.int64)
-    return {"wbar": wbar, "bbar": bbar, "qw": qw, "s_w": s_w, "b_int": b_int, "rho": rho,
-            "shift": n, "mult": m_c, "block": block, "side": side, "in_block": in_block,
-            "s_x": float(s_x), "s_y": float(s_y)}
+    out = {"wbar": wbar, "bbar": bbar, "qw": qw, "s_w": s_w, "b_int": b_int, "block": block,
+           "side": side, "in_block": in_block, "s_x": float(s_x), "s_y": float(s_y), "act": act,
+           "post_block": post_block}
+    if not general:
+        # Eq. (19): one multiplier per channel and one shift for the whole
+        # transition (ReLU commutes with the common factor 2^-n, Eq. (20)-(22))
+        rho = s_a / (np.sqrt(block * post_block) * float(s_y))
+        n = requant_shift(rho, mult_bound(block * post_block))
+        out.update(rho=rho, shift=n, mult=np.rint(rho * 2.0 ** n).astype(np.int64))
+        return out
+    # Eq. (45): onto the pre-activation grid s_z, before the output-side transform
+    rho = s_a / (np.sqrt(block) * float(s_z))
+    n = requant_shift(rho, mult_bound(block))
+    # Eq. (47): the integer activation; Eq. (48): onto the next layer's grid
+    rho_in = float(s_u) / (np.sqrt(post_block) * float(s_y))
+    n_in = requant_shift(np.array([rho_in]))
+    out.update(rho=rho, shift=n, mult=np.rint(rho * 2.0 ** n).astype(np.int64),
+               lut=act_table(phi or PHI[act], s_z, s_u), rho_in=rho_in, shift_in=n_in,
+               mult_in=int(np.rint(rho_in * 2.0 ** n_in)), s_z=float(s_z), s_u=float(s_u))
+    return out
 
 
 def int_forward(x_int, prep, bits: int = 8) -> dict:
     """Online integer path: a = x_int w-bar_int^T + b_int (Eq. (4)),
-    v = H~_m (M . a) (Eq. (20), Eq. (22)'s transform for DH-to-DH),
-    y_int = clamp(round(v / 2^n), +-qmax) (Eq. (22), identity activation).
+    v = H~_block (M . a) (Eq. (20); Eq. (46) with M_out),
+    then the activation and the transform after it:
+    identity / ReLU (Eq. (21)-(22)): y = clamp(round(H~_post(phi(v)) / 2^n));
+    SiLU / GELU (Eq. (46)-(49)): z = clamp(round(v / 2^n_out)), u = LUT[z],
+    y = clamp(round(H~_post(M_in u) / 2^n_in)).
     x_int is the int8 input in the layer's own basis (the original one for
     WH, the H_in basis for DH)."""
     qmax = 2 ** (bits - 1) - 1
     a = int_gemm(x_int, prep["qw"]) + prep["b_int"][None, :]
     u = a * prep["mult"][None, :]
     v = unnormalised_transform(u, prep["block"])
-    y = np.clip(round_half_even_shift(v, prep["shift"]), -qmax, qmax)
-    return {"acc": a, "u": u, "v": v, "y_int": y.astype(np.int16)}
+    out = {"acc": a, "u": u, "v": v}
+    act = prep.get("act", ACT_NONE)
+    post = prep.get("post_block", 1)
+    if act in (ACT_NONE, ACT_RELU):
+        pv = np.maximum(v, 0) if act == ACT_RELU else v
+        w = unnormalised_transform(pv, post)
+        y = np.clip(round_half_even_shift(w, prep["shift"]), -qmax, qmax)
+    else:
+        z = np.clip(round_half_even_shift(v, prep["shift"]), -qmax, qmax)
+        ua = prep["lut"][z + qmax]
+        w = unnormalised_transform(ua * prep["mult_in"], post)
+        y = np.clip(round_half_even_shift(w, prep["shift_in"]), -qmax, qmax)
+        out.update(z=z, u_act=ua)
+    out.update(w=w, y_int=y.astype(np.int16))
+    return out
 
 
-def int_dequant_reference(x_int, prep) -> np.ndarray:
-    """The dequantised output with the bias codes, moved by the normalised
-    output-side transform and in units of s_y: (s_A . a) H_m / s_y (float64).
-    For WH this is Eq. (17) in the original basis; for DH the output of
-    Eq. (14) in the next layer's H_in basis."""
+def _relu(v):
+    return np.maximum(v, 0.0)
+
+
+def int_dequant_reference(x_int, prep, phi=None) -> np.ndarray:
+    """The dequantised output with the bias codes through the normalised
+    transforms and the activation, in units of s_y (float64):
+    phi((s_A . a) H_block) H_post / s_y. For WH this is Eq. (17) in the
+    original basis; for DH the output of Eq. (14) in the next layer's H_in
+    basis. No intermediate grid (s_z, s_u) is applied."""
+    act = prep.get("act", ACT_NONE)
+    if phi is None:
+        phi = {ACT_NONE: (lambda v: v), ACT_RELU: _relu}.get(act) or PHI[act]
     a = int_gemm(x_int, prep["qw"]) + prep["b_int"][None, :]
     ya = a.astype(np.float64) * (prep["s_x"] * prep["s_w"])[None, :]
-    return rotate(ya, prep["block"]) / prep["s_y"]
+    return rotate(phi(rotate(ya, prep["block"])), prep.get("post_block", 1)) / prep["s_y"]
 
 
 def quantize_static(x, s: float, bits: int = 8) -> np.ndarray:

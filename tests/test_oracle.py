@@ -705,3 +705,148 @@ def test_int_prepare_rejects_bad_side_and_block():
         O.int_prepare(weight, bias, s_x, s_y, 1, side=2)
     with pytest.raises(ValueError):
         O.int_prepare(weight, bias, s_x, s_y, 1, side=O.SIDE_DH, in_block=64)   # 96 % 64
+
+
+# --- Activations between integer layers (HaTQ Table I, Eq. (20)-(22);
+# supplement Sec. VIII-C Eq. (45)-(49)) ---
+
+def _blocksum(v, m):
+    """Sum of each block of m consecutive channels, repeated over the block."""
+    t, d = v.shape
+    return v.reshape(t, d // m, m).sum(axis=2).repeat(m, axis=1)
+
+
+@pytest.mark.parametrize("m", [1, 8, 64])
+def test_int_identity_transition_is_order_free(m):
+    # with phi = identity the transform before and after it give the same
+    # integers (a DH-to-DH transition written either way)
+    x, weight, bias, _, _ = _wh_inputs()
+    s_x = np.abs(x).max() / 127
+    s_y = np.abs(O.rotate(x @ weight.T + bias, m)).max() / 127
+    xi = O.quantize_static(x, s_x)
+    pa = O.int_prepare(weight, bias, s_x, s_y, m, side=O.SIDE_DH)
+    pb = O.int_prepare(weight, bias, s_x, s_y, 1, side=O.SIDE_DH, post_block=m)
+    assert pa["shift"] == pb["shift"] and np.array_equal(pa["mult"], pb["mult"])
+    assert np.array_equal(O.int_forward(xi, pa)["y_int"], O.int_forward(xi, pb)["y_int"])
+
+
+@pytest.mark.parametrize("m", [2, 16, 64])
+def test_int_two_transforms_compose_to_m_identity(m):
+    # WH-to-DH with phi = identity and equal orders: H~ H~ = m I (Eq. (7)), so
+    # the integers are clamp(round(m M a / 2^n)) with no transform at all
+    x, weight, bias, s_x, s_y = _wh_inputs()
+    p = O.int_prepare(weight, bias, s_x, s_y, m, side=O.SIDE_WH, post_block=m)
+    assert np.all(p["mult"] <= O.mult_bound(m * m))
+    r = O.int_forward(O.quantize_static(x, s_x), p)
+    direct = np.clip(O.round_half_even_shift(m * r["u"], p["shift"]), -127, 127)
+    assert np.array_equal(r["y_int"], direct)
+
+
+def test_mult_bound_keeps_two_transforms_exact():
+    assert O.mult_bound(1) == O.RQ_MULT_MAX and O.mult_bound(256) == O.RQ_MULT_MAX
+    assert O.mult_bound(256 * 256) == 255
+    # the largest possible output of two order-256 transforms stays below 2^52
+    assert (2 ** 28) * O.mult_bound(256 * 256) * 256 * 256 < 2 ** 52
+
+
+@pytest.mark.parametrize("side,m,post", [(0, 16, 1), (0, 16, 32), (1, 1, 32), (1, 1, 1)])
+def test_int_relu_within_its_rounding_bound(side, m, post):
+    # y = clamp(round(H~_post(relu(H~_m(M . a))) / 2^n)) against the float
+    # relu((s_A a) H_m) H_post / s_y: the multiplier rounding |M - 2^n rho| <= 1/2
+    # moves each output by at most the block sums of |a| / 2^(n+1) through both
+    # transforms (relu is 1-Lipschitz), plus the final rounding 1/2
+    x, weight, bias, _, _ = _wh_inputs()
+    xs = x if side == O.SIDE_WH else O.rotate(x, 32)
+    s_x = np.abs(xs).max() / 127
+    y = x @ weight.T + bias
+    s_y = np.abs(O.rotate(np.maximum(y, 0), post)).max() / 127
+    p = O.int_prepare(weight, bias, s_x, s_y, m, side=side, in_block=32 if side else 1,
+                      act=O.ACT_RELU, post_block=post)
+    xi = O.quantize_static(xs, s_x)
+    r = O.int_forward(xi, p)
+    ref = O.int_dequant_reference(xi, p)
+    e = _blocksum(_blocksum(0.5 * np.abs(r["acc"]).astype(np.float64), m), post) / 2.0 ** p["shift"]
+    assert np.all(np.abs(r["y_int"] - np.clip(ref, -127, 127)) <= 0.5 + e + 1e-9)
+    # the codes stand for relu(layer) in the next layer's basis
+    assert O.sqnr_db(O.rotate(np.maximum(y, 0), post) / s_y, r["y_int"].astype(np.float64)) > 25
+
+
+@pytest.mark.parametrize("act", [2, 3])
+def test_act_table_brute_force(act):
+    # each entry recomputed with the math module and Python's round (half to
+    # even), independently of the vectorised table
+    import math
+
+    def silu(v):
+        return v / (1.0 + math.exp(-v))
+
+    def gelu(v):
+        return 0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0)))
+
+    phi = silu if act == O.ACT_SILU else gelu
+    for s_z, s_u in [(0.05, 0.05), (0.031, 0.017), (0.2, 0.09)]:
+        lut = O.act_table(O.PHI[act], s_z, s_u)
+        ref = [max(-127, min(127, round(phi(s_z * z) / s_u))) for z in range(-127, 128)]
+        assert lut.tolist() == ref
+        assert lut[127] == 0                       # phi(0) = 0
+        assert lut[-1] == min(127, round(phi(127 * s_z) / s_u))
+
+
+@pytest.mark.parametrize("act", [2, 3])
+def test_int_general_path_brute_force(act):
+    # Eq. (46)-(49) on a tiny layer, recomputed with Python integers and
+    # fractions: a = x w^T + b_int; z = clamp(round(H~_2(M_out a) / 2^n_out));
+    # u = LUT[z]; y = clamp(round(H~_4(M_in u) / 2^n_in))
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    weight = rng.normal(0.0, 0.3, (4, 8))
+    bias = rng.normal(0.0, 0.1, 4)
+    x = rng.normal(0.0, 1.0, (5, 8))
+    s_x = np.abs(x).max() / 127
+    pre = O.rotate(x @ weight.T + bias, 2)
+    s_z = np.abs(pre).max() / 127
+    s_u = np.abs(O.PHI[act](pre)).max() / 127
+    s_y = 2 * s_u
+    p = O.int_prepare(weight, bias, s_x, s_y, 2, act=act, post_block=4, s_z=s_z, s_u=s_u)
+    xi = O.quantize_static(x, s_x)
+    r = O.int_forward(xi, p)
+    h2 = [[1, 1], [1, -1]]
+    h4 = [[1 if bin(i & j).count("1") % 2 == 0 else -1 for j in range(4)] for i in range(4)]
+    for t in range(5):
+        a = [sum(int(xi[t, i]) * int(p["qw"][c, i]) for i in range(8)) + int(p["b_int"][c])
+             for c in range(4)]
+        u = [a[c] * int(p["mult"][c]) for c in range(4)]
+        v = [sum(h2[c % 2][k] * u[2 * (c // 2) + k] for k in range(2)) for c in range(4)]
+        z = [max(-127, min(127, round(Fraction(vc, 2 ** p["shift"])))) for vc in v]
+        ua = [int(p["lut"][zc + 127]) * p["mult_in"] for zc in z]
+        w = [sum(h4[c][k] * ua[k] for k in range(4)) for c in range(4)]
+        y = [max(-127, min(127, round(Fraction(wc, 2 ** p["shift_in"])))) for wc in w]
+        assert r["y_int"][t].tolist() == y
+        assert r["z"][t].tolist() == z
+
+
+@pytest.mark.parametrize("act", [2, 3])
+def test_int_general_layer_reproduces_phi(act):
+    # WH-to-DH with SiLU / GELU between (Table I: H_out before phi, H_in after):
+    # the int8 codes stand for phi(layer) in the next layer's H_in basis
+    x, weight, bias, s_x, _ = _wh_inputs()
+    y = x @ weight.T + bias
+    s_z = np.abs(y).max() / 127
+    fy = O.PHI[act](y)
+    s_u = np.abs(fy).max() / 127
+    s_y = np.abs(O.rotate(fy, 32)).max() / 127
+    p = O.int_prepare(weight, bias, s_x, s_y, 16, act=act, post_block=32, s_z=s_z, s_u=s_u)
+    r = O.int_forward(O.quantize_static(x, s_x), p)
+    assert O.sqnr_db(O.rotate(fy, 32) / s_y, r["y_int"].astype(np.float64)) > 25
+
+
+def test_int_prepare_rejects_bad_activation_setups():
+    x, weight, bias, s_x, s_y = _wh_inputs()
+    with pytest.raises(ValueError):   # DH has no output-side transform before phi
+        O.int_prepare(weight, bias, s_x, s_y, 16, side=O.SIDE_DH, act=O.ACT_RELU)
+    with pytest.raises(ValueError):
+        O.int_prepare(weight, bias, s_x, s_y, 1, post_block=3)
+    with pytest.raises(ValueError):   # the table needs its grids
+        O.int_prepare(weight, bias, s_x, s_y, 1, act=O.ACT_GELU)
+    with pytest.raises(ValueError):
+        O.int_prepare(weight, bias, s_x, s_y, 1, act=7)
