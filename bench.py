@@ -407,35 +407,45 @@ def group_wise(hq, torch, WL, steps, warmup, dev):
             "sqnr_db": {k: v["method"] for k, v in sq.items()}}
 
 
-def integer_layer(hq, torch, WL, steps, warmup, dev, side):
+def integer_layer(hq, torch, WL, steps, warmup, dev, side, gelu=False):
     """lic_wh as an integer-only layer with integer requantisation (int8
     codes in, int8 codes out): the weight-only Hadamard layer (H_256 on the
-    output channels, output in the original basis) or the double-Hadamard
+    output channels, output in the original basis), the double-Hadamard
     layer (input in the H_256 basis of the previous DH layer, output moved to
-    the next one's H_256 basis). Time per call and the output SQNR of the int8
-    codes against the float32 layer in the same basis. The input codes are
-    the workload's X (rotated for DH) on a per-tensor grid (synthetic input)."""
+    the next one's H_256 basis), or (gelu) a WH layer followed by GELU and
+    handing over to a DH layer (H_out before the activation, the integer
+    GELU table on its own int8 grids, the next layer's H_256 after it). Time
+    per call and the output SQNR of the int8 codes against the float32 layer
+    (and activation) in the same basis. The input codes are the workload's X
+    (rotated for DH) on a per-tensor grid (synthetic input)."""
     w = WL.WORKLOADS["lic_wh"]
     X = torch.from_numpy(WL.gen_x(w)).to(dev)
     W = torch.from_numpy(WL.gen_weight(w)).to(dev)
     B = torch.from_numpy(WL.gen_bias(w)).to(dev)
     ref = torch.addmm(B, X, W.t())
     wh = side == hq.HQ_INT_WH
-    if not wh:
-        # orthonormal Sylvester H_256: the DH input and output bases
-        H = torch.ones(1, 1, dtype=torch.float64)
-        while H.shape[0] < w.block:
-            H = torch.cat([torch.cat([H, H], 1), torch.cat([H, -H], 1)], 0)
-        H = (H / math.sqrt(w.block)).to(dev)
+    # orthonormal Sylvester H_256: the DH input and output bases
+    H = torch.ones(1, 1, dtype=torch.float64)
+    while H.shape[0] < w.block:
+        H = torch.cat([torch.cat([H, H], 1), torch.cat([H, -H], 1)], 0)
+    H = (H / math.sqrt(w.block)).to(dev)
 
-        def rot(a):
-            return (a.double().reshape(a.shape[0], -1, w.block) @ H).reshape(a.shape).float()
+    def rot(a):
+        return (a.double().reshape(a.shape[0], -1, w.block) @ H).reshape(a.shape).float()
+    if not wh:
         X, ref = rot(X), rot(ref)
+    s_z = s_u = 0.0
+    if gelu:
+        act = torch.nn.functional.gelu(ref.double())
+        s_z = float(ref.abs().max().item() / 127.0)
+        s_u = float(act.abs().max().item() / 127.0)
+        ref = rot(act)
     s_x = float(X.abs().max().item() / 127.0)
     s_y = float(ref.abs().max().item() / 127.0)
     X0 = torch.clamp(torch.round(X / s_x), -127, 127).to(torch.int8)
-    desc = hq.IntDesc(w.d_in, w.d_out, w.block, hq.F32, side, 1 if wh else w.block)
-    prep = hq.int_prepare(desc, W, B, s_x, s_y)
+    desc = hq.IntDesc(w.d_in, w.d_out, w.block, hq.F32, side, 1 if wh else w.block,
+                      hq.HQ_INT_ACT_GELU if gelu else hq.HQ_INT_ACT_NONE, w.block if gelu else 1)
+    prep = hq.int_prepare(desc, W, B, s_x, s_y, s_z, s_u)
     nbuf = max(2, math.ceil(512e6 / X0.numel()))
     Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
     Ys = [torch.empty(w.T, w.d_out, dtype=torch.int8, device=dev) for _ in range(nbuf)]
@@ -447,7 +457,8 @@ def integer_layer(hq, torch, WL, steps, warmup, dev, side):
     del Xs, Ys
     # bytes that must move: int8 codes in and out, weight codes, constants
     algo = w.T * (w.d_in + w.d_out) + w.d_out * (w.d_in + 12)
-    return {"workload": w.name, "layer": "WH" if wh else "DH-to-DH", "tokens": w.T,
+    return {"workload": w.name,
+            "layer": "WH-to-DH with GELU" if gelu else ("WH" if wh else "DH-to-DH"), "tokens": w.T,
             "d_in": w.d_in, "d_out": w.d_out, "block": w.block, "bits": "W8A8 int8 -> int8",
             "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_step": round(ms, 5), "algorithmic_GBs": round(algo / (ms * 1e-3) / 1e9, 1),
@@ -620,7 +631,8 @@ def main():
         out["configs"] = cfgs
         out["group_wise"] = group_wise(hq, torch, WL, es, ew, dev)
         out["integer_layers"] = [integer_layer(hq, torch, WL, es, ew, dev, side)
-                                 for side in (hq.HQ_INT_WH, hq.HQ_INT_DH)]
+                                 for side in (hq.HQ_INT_WH, hq.HQ_INT_DH)] + [
+            integer_layer(hq, torch, WL, es, ew, dev, hq.HQ_INT_WH, gelu=True)]
     print(json.dumps(out), flush=True)
 
 

@@ -21,7 +21,8 @@ import torch
 
 from . import _lib
 from ._lib import (HQ_CENTER_CHANNEL, HQ_CENTER_NONE, HQ_CENTER_TOKEN, HQ_CODES_E2M3,
-                   HQ_CODES_I8, HQ_GEMM_AUTO, HQ_GEMM_I8, HQ_INT_DH, HQ_INT_WH, HqDesc, HqError,
+                   HQ_CODES_I8, HQ_GEMM_AUTO, HQ_GEMM_I8, HQ_INT_ACT_GELU, HQ_INT_ACT_NONE,
+                   HQ_INT_ACT_RELU, HQ_INT_ACT_SILU, HQ_INT_DH, HQ_INT_WH, HqDesc, HqError,
                    HqLayout, check, load)
 
 F32, BF16 = 0, 1
@@ -374,17 +375,21 @@ class IntDesc:
     """Descriptor of an integer-only layer; mirrors hq_int_desc. ``side``
     HQ_INT_WH (weight transformed along its outputs by H of order ``block``)
     or HQ_INT_DH (along its inputs by H of order ``in_block``); ``block`` is
-    the order of the output-side integer transform."""
+    the order of the output-side integer transform (before the activation),
+    ``act`` the activation to the next layer (HQ_INT_ACT_*), ``post_block``
+    the order of the transform after it (the next layer's H_in)."""
     d_in: int
     d_out: int
     block: int
     w_dtype: int = F32
     side: int = _lib.HQ_INT_WH
     in_block: int = 1
+    act: int = _lib.HQ_INT_ACT_NONE
+    post_block: int = 1
 
     def __post_init__(self):
         raw = _lib.HqIntDesc(self.d_in, self.d_out, self.block, self.w_dtype, self.side,
-                             self.in_block)
+                             self.in_block, self.act, self.post_block)
         object.__setattr__(self, "_raw", raw)
         object.__setattr__(self, "_ref", ctypes.byref(raw))
 
@@ -405,8 +410,9 @@ def int_workspace_bytes(desc: IntDesc, T: int) -> int:
 
 
 def int_prepare(desc: IntDesc, weight: torch.Tensor, bias: Optional[torch.Tensor], s_x: float,
-                s_y: float) -> torch.Tensor:
-    """Offline transform of an integer-only layer; returns the prepared blob."""
+                s_y: float, s_z: float = 0.0, s_u: float = 0.0) -> torch.Tensor:
+    """Offline transform of an integer-only layer; returns the prepared blob.
+    s_z, s_u: the int8 grids around a SiLU/GELU table (ignored otherwise)."""
     _need(weight, "weight", _TORCH[desc.w_dtype], (desc.d_out, desc.d_in))
     if bias is not None:
         _need(bias, "bias", torch.float32, (desc.d_out,))
@@ -415,7 +421,8 @@ def int_prepare(desc: IntDesc, weight: torch.Tensor, bias: Optional[torch.Tensor
         check(load().hq_int_validate(desc._ref))
     blob = torch.empty(n, dtype=torch.uint8, device=weight.device)
     check(load().hq_int_prepare(desc._ref, _ptr(weight), _ptr(bias), ctypes.c_float(s_x),
-                                ctypes.c_float(s_y), _ptr(blob), _stream()))
+                                ctypes.c_float(s_y), ctypes.c_float(s_z), ctypes.c_float(s_u),
+                                _ptr(blob), _stream()))
     return blob
 
 
@@ -461,4 +468,7 @@ def int_views(desc: IntDesc, prepared: torch.Tensor) -> dict:
         "mult": view(L.mult, npad, torch.int32, (npad,))[:desc.d_out],
         "shift": view(L.shift, 1, torch.int32, (1,)),
         "wbar": view(L.wbar, desc.d_out * d, torch.float32, (desc.d_out, d)),
+        "lut": view(L.lut, 256, torch.int8, (256,)),
+        "mult_in": view(L.mult_in, 1, torch.int32, (1,)),
+        "shift_in": view(L.shift_in, 1, torch.int32, (1,)),
     }

@@ -25,19 +25,21 @@ class HqLayout(ctypes.Structure):
 
 class HqIntDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ["d_in", "d_out", "block", "w_dtype", "side", "in_block"]]
+                ["d_in", "d_out", "block", "w_dtype", "side", "in_block", "act", "post_block"]]
 
 
 class HqIntLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ["total", "w_codes", "w_scale", "b_int", "mult", "shift", "wbar"]] + [
-        ("d_out_pad", ctypes.c_int64)]
+        ("d_out_pad", ctypes.c_int64)] + [
+        (n, ctypes.c_size_t) for n in ["lut", "mult_in", "shift_in"]]
 
 
 HQ_CODES_I8, HQ_CODES_E2M3 = 0, 1
 HQ_GEMM_AUTO, HQ_GEMM_I8 = 0, 1
 HQ_CENTER_NONE, HQ_CENTER_TOKEN, HQ_CENTER_CHANNEL = 0, 1, 2
 HQ_INT_WH, HQ_INT_DH = 0, 1
+HQ_INT_ACT_NONE, HQ_INT_ACT_RELU, HQ_INT_ACT_SILU, HQ_INT_ACT_GELU = 0, 1, 2, 3
 
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_BAD_PREPARED, \
     HQ_ERR_HIP = 0, -1, -2, -3, -4, -5
@@ -73,7 +75,8 @@ _SIGS = {
     "hq_int_prepared_bytes": (ctypes.c_size_t, [_W]),
     "hq_int_prepared_layout_of": (ctypes.c_int, [_W, ctypes.POINTER(HqIntLayout)]),
     "hq_int_workspace_bytes": (ctypes.c_size_t, [_W, _I64]),
-    "hq_int_prepare": (ctypes.c_int, [_W, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P]),
+    "hq_int_prepare": (ctypes.c_int, [_W, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                      ctypes.c_float, _P, _P]),
     "hq_int_linear": (ctypes.c_int, [_W, _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "hq_int_requant": (ctypes.c_int, [_W, _P, _P, _I64, _P, _P]),
 }

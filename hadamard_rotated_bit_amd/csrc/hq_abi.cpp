@@ -290,7 +290,7 @@ struct IntHeader {
   hq_int_desc desc;
   int64_t d_out_pad;
   uint64_t total;
-  float s_x, s_y;
+  float s_x, s_y, s_z, s_u;
 };
 static_assert(sizeof(IntHeader) <= 256, "header fits in 256 bytes");
 
@@ -319,6 +319,15 @@ int check_int_desc(const hq_int_desc* d) {
   if (d->side == HQ_INT_DH && (!is_pow2(d->in_block) || d->d_in % d->in_block))
     return fail(HQ_ERR_UNSUPPORTED, "in_block %d must be a power of two dividing d_in %d",
                 d->in_block, d->d_in);
+  if (d->act < HQ_INT_ACT_NONE || d->act > HQ_INT_ACT_GELU)
+    return fail(HQ_ERR_INVALID_ARG, "act %d is not an hq_int_act", d->act);
+  if (!is_pow2(d->post_block) || d->post_block > hq::WH_MAX_BLOCK || d->d_out % d->post_block)
+    return fail(HQ_ERR_UNSUPPORTED, "post_block %d must be a power of two <= %d dividing d_out %d",
+                d->post_block, hq::WH_MAX_BLOCK, d->d_out);
+  if (d->side == HQ_INT_DH && d->act != HQ_INT_ACT_NONE && d->block != 1)
+    return fail(HQ_ERR_UNSUPPORTED,
+                "a DH layer has no output-side transform before its activation: put the next "
+                "layer's H_in order in post_block and use block = 1 (got block %d)", d->block);
   return HQ_OK;
 }
 
@@ -335,20 +344,37 @@ void int_layout_of(const hq_int_desc* d, hq_int_layout* L) {
   L->mult = off;
   off += align256(4 * size_t(np));
   L->shift = off;
+  L->mult_in = off + 4;
+  L->shift_in = off + 8;
+  off += 256;
+  L->lut = off;
   off += 256;
   L->wbar = off;
   off += align256(4 * size_t(d->d_out) * d->d_in);
   L->total = off;
 }
 
-int run_int_requant(const hq_int_desc* d, const void* prepared, const int32_t* acc, int64_t T,
-                    int8_t* y, hipStream_t s) {
+// The transition's constants inside a prepared blob.
+hq::IntTransition transition_of(const hq_int_desc* d, const void* prepared) {
   hq_int_layout L;
   int_layout_of(d, &L);
-  hipError_t e = hq::launch_int_requant(acc, d->d_out, T, d->d_out, d->block,
-                                        at<int32_t>(prepared, L.b_int),
-                                        at<int32_t>(prepared, L.mult),
-                                        at<int32_t>(prepared, L.shift), y, d->d_out, s);
+  hq::IntTransition tr = {};
+  tr.m = d->block;
+  tr.post = d->post_block;
+  tr.act = d->act == HQ_INT_ACT_SILU || d->act == HQ_INT_ACT_GELU ? 2 : d->act;
+  tr.b_int = at<int32_t>(prepared, L.b_int);
+  tr.mult = at<int32_t>(prepared, L.mult);
+  tr.shift = at<int32_t>(prepared, L.shift);
+  tr.lut = at<int8_t>(prepared, L.lut);
+  tr.mult_in = at<int32_t>(prepared, L.mult_in);
+  tr.shift_in = at<int32_t>(prepared, L.shift_in);
+  return tr;
+}
+
+int run_int_requant(const hq_int_desc* d, const void* prepared, const int32_t* acc, int64_t T,
+                    int8_t* y, hipStream_t s) {
+  hipError_t e = hq::launch_int_requant(acc, d->d_out, T, d->d_out, transition_of(d, prepared),
+                                        y, d->d_out, s);
   return e == hipSuccess ? HQ_OK : hip_fail(e, "requantisation kernel launch");
 }
 
@@ -750,7 +776,7 @@ size_t hq_int_workspace_bytes(const hq_int_desc* desc, int64_t T) {
 }
 
 int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bias, float s_x,
-                   float s_y, void* prepared, void* stream) {
+                   float s_y, float s_z, float s_u, void* prepared, void* stream) {
   g_err.clear();
   int st = check_int_desc(desc);
   if (st != HQ_OK) return st;
@@ -758,6 +784,11 @@ int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bia
   if (!(s_x > 0.0f) || !(s_y > 0.0f) || !std::isfinite(s_x) || !std::isfinite(s_y))
     return fail(HQ_ERR_INVALID_ARG, "s_x and s_y must be positive and finite (got %g, %g)",
                 double(s_x), double(s_y));
+  const bool table = desc->act == HQ_INT_ACT_SILU || desc->act == HQ_INT_ACT_GELU;
+  if (table && (!(s_z > 0.0f) || !(s_u > 0.0f) || !std::isfinite(s_z) || !std::isfinite(s_u)))
+    return fail(HQ_ERR_INVALID_ARG,
+                "SiLU/GELU need s_z and s_u positive and finite (got %g, %g)", double(s_z),
+                double(s_u));
   if (misaligned(prepared) || misaligned(weight) || misaligned(bias))
     return fail(HQ_ERR_INVALID_ARG, "weight, bias and prepared must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -807,9 +838,12 @@ int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bia
   }
   if (e == hipSuccess)
     e = hq::launch_int_constants(bias, at<float>(prepared, L.w_scale), int(dout), int(np),
-                                 desc->block, wh ? desc->block : 1, s_x, s_y,
-                                 at<int32_t>(prepared, L.b_int), at<int32_t>(prepared, L.mult),
-                                 at<int32_t>(prepared, L.shift), s);
+                                 desc->block, desc->post_block, desc->act,
+                                 wh ? desc->block : 1, s_x, s_y, table ? s_z : 0.0f,
+                                 table ? s_u : 0.0f, at<int32_t>(prepared, L.b_int),
+                                 at<int32_t>(prepared, L.mult), at<int32_t>(prepared, L.shift),
+                                 at<int8_t>(prepared, L.lut), at<int32_t>(prepared, L.mult_in),
+                                 at<int32_t>(prepared, L.shift_in), s);
   if (e == hipSuccess) {
     IntHeader h = {};
     h.magic = kMagicInt;
@@ -819,6 +853,8 @@ int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bia
     h.total = L.total;
     h.s_x = s_x;
     h.s_y = s_y;
+    h.s_z = table ? s_z : 0.0f;
+    h.s_u = table ? s_u : 0.0f;
     e = hq::launch_write_header(&h, sizeof(h), prepared, s);
   }
   return e == hipSuccess ? HQ_OK : hip_fail(e, "integer-layer prepare kernel launch");
@@ -845,10 +881,9 @@ int hq_int_linear(const hq_int_desc* desc, const void* prepared, const int8_t* x
   if (desc->d_out % 256 == 0) {
     // whole 256-channel units: GEMM and requantisation in one kernel (the
     // same integers as the two-kernel path below)
-    const hipError_t e = hq::launch_int_fused(
-        x_codes, T, desc->d_in, at<int8_t>(prepared, L.w_codes), desc->d_out, desc->block,
-        at<int32_t>(prepared, L.b_int), at<int32_t>(prepared, L.mult),
-        at<int32_t>(prepared, L.shift), y_codes, s);
+    const hipError_t e =
+        hq::launch_int_fused(x_codes, T, desc->d_in, at<int8_t>(prepared, L.w_codes),
+                             desc->d_out, transition_of(desc, prepared), y_codes, s);
     return e == hipSuccess ? HQ_OK : hip_fail(e, "integer-layer kernel launch");
   }
   int32_t* acc = static_cast<int32_t*>(workspace);

@@ -13,7 +13,13 @@
 //   y = clamp(round(H~_m (M . a) / 2^n), -127, 127)
 //
 // with per-channel 16-bit multipliers M and one shared shift n (the Hadamard
-// normalisation 1/sqrt(m) folded into M).
+// normalisation 1/sqrt(m) folded into M). With an activation between the
+// layers (Table I, Eq. (20)-(22); supplement Eq. (45)-(49)) a second
+// transform H~_p (the next layer's H_in) follows it: ReLU keeps the single
+// multiplier-shift pair (y = clamp(round(H~_p relu(H~_m (M . a)) / 2^n))),
+// SiLU and GELU run on their own int8 grid through a 255-entry table:
+// z = clamp(round(H~_m (M_out . a) / 2^n_out)), u = LUT[z],
+// y = clamp(round(H~_p (M_in u) / 2^n_in)).
 #include "hq_device.h"
 #include "hq_internal.h"
 
@@ -53,24 +59,51 @@ __global__ __launch_bounds__(256) void wh_weight_kernel(const TW* __restrict__ w
     for (int r = tr; r < m; r += 8) wbar[(row0 + r) * d_in + col] = tile[r * LD + tc] * inv_sqrt_m;
 }
 
+// Multiplier bound for transforms whose orders multiply to `orders` (a power
+// of two): |a + b_int| < 2^28, so M < 2^(24 - log2 orders) keeps every
+// integer below 2^52 through the unnormalised transforms.
+__device__ __forceinline__ double int_mult_bound(int orders) {
+  const int lg = 31 - __clz(orders);
+  const double b = ldexp(1.0, 24 - lg) - 1.0;
+  return b < double(WH_MULT_MAX) ? b : double(WH_MULT_MAX);
+}
+
+// The largest shift n <= WH_SHIFT_MAX with round(2^n top) <= bound (0 when
+// top is 0).
+__device__ __forceinline__ int int_shift_for(double top, double bound) {
+  int n = 0;
+  if (top > 0.0)
+    while (n < WH_SHIFT_MAX && rint(ldexp(top, n + 1)) <= bound) ++n;
+  return n;
+}
+
+// The activations of the table (float64).
+__device__ __forceinline__ double int_phi(int act, double x) {
+  if (act == 2) return x / (1.0 + exp(-x));                 // SiLU
+  return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));              // GELU, x Phi(x)
+}
+
 // Offline constants (one block, float64): b-bar = b H_bb (bb = m for WH, 1
-// for DH), s_A = s_x s_w,
-// b_int = round(b-bar / s_A) (saturated at +-2^27, see the requantisation
-// kernel), rho = s_A / (sqrt(m) s_y), the shared shift n (largest n <= 48 with
-// every round(2^n rho) <= 32767) and M = round(2^n rho). Rows past d_out get
+// for DH), s_A = s_x s_w, b_int = round(b-bar / s_A) (saturated at +-2^27,
+// see the requantisation kernel), rho, the shared shift n (largest n <= 48
+// with every round(2^n rho) within the multiplier bound) and M = round(2^n
+// rho). Identity / ReLU: rho = s_A / (sqrt(m post) s_y), bound for m post.
+// SiLU / GELU: rho = s_A / (sqrt(m) s_z), bound for m; then the table over
+// z = -127 .. 127 (lut[z + 127] = clamp(round(phi(s_z z) / s_u)), lut[255] =
+// 0) and M_in = round(2^n_in s_u / (sqrt(post) s_y)). Rows past d_out get
 // zeros.
-__global__ __launch_bounds__(256) void int_constants_kernel(const float* __restrict__ bias,
-                                                           const float* __restrict__ s_w,
-                                                           int d_out, int d_out_pad, int m,
-                                                           int bb_order, double s_x, double s_y,
-                                                           int32_t* __restrict__ b_int,
-                                                           int32_t* __restrict__ mult,
-                                                           int32_t* __restrict__ shift) {
+__global__ __launch_bounds__(256) void int_constants_kernel(
+    const float* __restrict__ bias, const float* __restrict__ s_w, int d_out, int d_out_pad,
+    int m, int post, int act, int bb_order, double s_x, double s_y, double s_z, double s_u,
+    int32_t* __restrict__ b_int, int32_t* __restrict__ mult, int32_t* __restrict__ shift,
+    int8_t* __restrict__ lut, int32_t* __restrict__ mult_in, int32_t* __restrict__ shift_in) {
   __shared__ double red[256];
-  const double sqm = sqrt(double(m));
+  const bool general = act >= 2;
+  const double sqm = sqrt(double(general ? m : m * post));
+  const double s_den = general ? s_z : s_y;
   double top = 0.0;
   for (int c = threadIdx.x; c < d_out; c += 256) {
-    const double rho = s_x * double(s_w[c]) / (sqm * s_y);
+    const double rho = s_x * double(s_w[c]) / (sqm * s_den);
     top = rho > top ? rho : top;
   }
   red[threadIdx.x] = top;
@@ -82,15 +115,32 @@ __global__ __launch_bounds__(256) void int_constants_kernel(const float* __restr
     __syncthreads();
   }
   top = red[0];
-  int n = 0;
-  if (top > 0.0)
-    while (n < WH_SHIFT_MAX && rint(ldexp(top, n + 1)) <= double(WH_MULT_MAX)) ++n;
-  if (threadIdx.x == 0) *shift = n;
+  const int n = int_shift_for(top, int_mult_bound(general ? m : m * post));
+  if (threadIdx.x == 0) {
+    *shift = n;
+    int32_t mi = 0, ni = 0;
+    if (general) {
+      const double rho_in = s_u / (sqrt(double(post)) * s_y);
+      ni = int_shift_for(rho_in, double(WH_MULT_MAX));
+      mi = int32_t(rint(ldexp(rho_in, ni)));
+    }
+    *mult_in = mi;
+    *shift_in = ni;
+  }
+  {
+    const int t = threadIdx.x;   // one table entry per thread
+    double q = 0.0;
+    if (general && t < 255) {
+      q = rint(int_phi(act, s_z * double(t - 127)) / s_u);
+      q = q > 127.0 ? 127.0 : (q < -127.0 ? -127.0 : q);
+    }
+    lut[t] = int8_t(int(q));
+  }
   for (int c = threadIdx.x; c < d_out_pad; c += 256) {
     int32_t bi = 0, mc = 0;
     if (c < d_out) {
       const double s_a = s_x * double(s_w[c]);
-      const double rho = s_a / (sqm * s_y);
+      const double rho = s_a / (sqm * s_den);
       mc = int32_t(rint(ldexp(rho, n)));
       if (bias && s_a > 0.0) {
         const int base = (c / bb_order) * bb_order, ci = c - base;
@@ -111,9 +161,10 @@ __global__ __launch_bounds__(256) void int_constants_kernel(const float* __restr
 }
 
 // The requantisation carries its integers in float64 registers: with
-// |a + b_int| < 2^28 (|a| <= 127^2 d_in <= 2^27, |b_int| <= 2^27), M < 2^15
-// and at most 256 terms per butterfly output, every intermediate is an
-// integer below 2^51 in magnitude, so float64 additions, products, the scaling
+// |a + b_int| < 2^28 (|a| <= 127^2 d_in <= 2^27, |b_int| <= 2^27) and M below
+// the bound for the transforms' orders (2^(24 - log2(m post))), every
+// intermediate is an integer below 2^52 in magnitude (after a table, |M_in u|
+// <= 127 * 32767 and 256 terms), so float64 additions, products, the scaling
 // by 2^-n and round-to-nearest-even are exact and give the integer results
 // bit for bit, at a quarter of the instructions 64-bit integer arithmetic
 // needs on the VALU.
@@ -186,6 +237,30 @@ __device__ __forceinline__ uint4 int_unit_codes(const double (&u)[16], double sc
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// The transition on one unit, u = M . (acc + b_int) on entry: H~_m, the
+// activation, H~_post, then the final rounding as 16 int8 codes. ACT 0:
+// identity, 1: ReLU (both with the one shift), 2: the table (SiLU, GELU):
+// z = clamp(round(v / 2^n_out)), u = M_in lut[z + 127], final shift n_in.
+template <int ACT>
+__device__ __forceinline__ uint4 int_unit_transition(double (&u)[16], int lane,
+                                                     const IntTransition& tr) {
+  const double s1 = ldexp(1.0, -*tr.shift);
+  int_unit_transform(u, lane, tr.m);
+  if constexpr (ACT == 1) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) u[k] = fmax(u[k], 0.0);
+  } else if constexpr (ACT == 2) {
+    const double m_in = double(*tr.mult_in);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const double z = fmin(fmax(rint(u[k] * s1), -127.0), 127.0);
+      u[k] = double(tr.lut[int(z) + 127]) * m_in;
+    }
+  }
+  int_unit_transform(u, lane, tr.post);
+  return int_unit_codes(u, ACT == 2 ? ldexp(1.0, -*tr.shift_in) : s1);
+}
+
 // Requantisation of int32 products acc [T, ldc] (without bias). Each group of
 // 16 lanes takes one (token, 256-channel chunk) unit, lane l of the group
 // holding channels 16 l .. 16 l + 15 of the chunk. u = M (acc + b_int), the
@@ -194,10 +269,10 @@ __device__ __forceinline__ uint4 int_unit_codes(const double (&u)[16], double sc
 // round(u / 2^n) with ties to even and clamping to +-127. Every lane of a
 // group runs the butterflies (invalid channels hold 0; blocks never mix valid
 // and invalid channels, m dividing d_out).
+template <int ACT>
 __global__ __launch_bounds__(256) void int_requant_kernel(
-    const int32_t* __restrict__ acc, int64_t ldc, int64_t T, int d_out, int chunks, int m,
-    const int32_t* __restrict__ b_int, const int32_t* __restrict__ mult,
-    const int32_t* __restrict__ shift, int8_t* __restrict__ y, int64_t ldy) {
+    const int32_t* __restrict__ acc, int64_t ldc, int64_t T, int d_out, int chunks,
+    IntTransition tr, int8_t* __restrict__ y, int64_t ldy) {
   const int lane = threadIdx.x & 15;
   const int64_t unit = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const bool live = unit < T * chunks;
@@ -210,8 +285,8 @@ __global__ __launch_bounds__(256) void int_requant_kernel(
     const int c = c0 + 4 * q;
     if (c < d_out) {   // d_out % 8 == 0: whole runs of 4 are in or out
       const int4 a = *reinterpret_cast<const int4*>(acc + row * ldc + c);
-      const int4 b = *reinterpret_cast<const int4*>(b_int + c);
-      const int4 mm = *reinterpret_cast<const int4*>(mult + c);
+      const int4 b = *reinterpret_cast<const int4*>(tr.b_int + c);
+      const int4 mm = *reinterpret_cast<const int4*>(tr.mult + c);
       u[4 * q + 0] = double(a.x + b.x) * double(mm.x);
       u[4 * q + 1] = double(a.y + b.y) * double(mm.y);
       u[4 * q + 2] = double(a.z + b.z) * double(mm.z);
@@ -220,9 +295,8 @@ __global__ __launch_bounds__(256) void int_requant_kernel(
       u[4 * q + 0] = u[4 * q + 1] = u[4 * q + 2] = u[4 * q + 3] = 0.0;
     }
   }
-  int_unit_transform(u, lane, m);
+  const uint4 w = int_unit_transition<ACT>(u, lane, tr);
   if (!live || c0 >= d_out) return;
-  const uint4 w = int_unit_codes(u, ldexp(1.0, -*shift));
   int8_t* dst = y + row * ldy + c0;
   if (c0 + 16 <= d_out) {
     *reinterpret_cast<uint4*>(dst) = w;
@@ -242,10 +316,10 @@ typedef int iv4 __attribute__((ext_vector_type(4)));
 typedef int iv16 __attribute__((ext_vector_type(16)));
 constexpr int IF_ROWS = 32;
 constexpr int IF_PITCH = 256 + 4;   // int32 per LDS row (16-B aligned, rows 4 banks apart)
+template <int ACT>
 __global__ __launch_bounds__(512) void int_fused_kernel(
     const int8_t* __restrict__ x, int64_t T, int d_in, const int8_t* __restrict__ w, int d_out,
-    int m, const int32_t* __restrict__ b_int, const int32_t* __restrict__ mult,
-    const int32_t* __restrict__ shift, int8_t* __restrict__ y) {
+    IntTransition tr, int8_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) int32_t tile[IF_ROWS * IF_PITCH];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t row0 = int64_t(blockIdx.x) * IF_ROWS;
@@ -280,7 +354,6 @@ __global__ __launch_bounds__(512) void int_fused_kernel(
         iv4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
   __syncthreads();
   const int l16 = tid & 15, cl = 16 * l16;
-  const double scale = ldexp(1.0, -*shift);
   {
     const int r = tid >> 4;   // 32 units, one per 16 lanes
     double u[16];
@@ -288,16 +361,15 @@ __global__ __launch_bounds__(512) void int_fused_kernel(
     for (int q = 0; q < 4; ++q) {
       const int c = c_blk + cl + 4 * q;
       const int4 av = *reinterpret_cast<const int4*>(tile + r * IF_PITCH + cl + 4 * q);
-      const int4 bv = *reinterpret_cast<const int4*>(b_int + c);
-      const int4 mv = *reinterpret_cast<const int4*>(mult + c);
+      const int4 bv = *reinterpret_cast<const int4*>(tr.b_int + c);
+      const int4 mv = *reinterpret_cast<const int4*>(tr.mult + c);
       u[4 * q + 0] = double(av.x + bv.x) * double(mv.x);
       u[4 * q + 1] = double(av.y + bv.y) * double(mv.y);
       u[4 * q + 2] = double(av.z + bv.z) * double(mv.z);
       u[4 * q + 3] = double(av.w + bv.w) * double(mv.w);
     }
-    int_unit_transform(u, l16, m);
-    if (row0 + r < T)
-      *reinterpret_cast<uint4*>(y + (row0 + r) * d_out + c_blk + cl) = int_unit_codes(u, scale);
+    const uint4 codes = int_unit_transition<ACT>(u, l16, tr);
+    if (row0 + r < T) *reinterpret_cast<uint4*>(y + (row0 + r) * d_out + c_blk + cl) = codes;
   }
 }
 
@@ -316,37 +388,55 @@ hipError_t launch_wh_weight(const void* w, int w_bf16, int d_out, int d_in, int 
 }
 
 hipError_t launch_int_constants(const float* bias, const float* s_w, int d_out, int d_out_pad,
-                                int m, int bias_block, float s_x, float s_y, int32_t* b_int,
-                                int32_t* mult, int32_t* shift, hipStream_t s) {
-  if (bias_block < 1 || (bias_block & (bias_block - 1)) || d_out % bias_block)
+                                int m, int post, int act, int bias_block, float s_x, float s_y,
+                                float s_z, float s_u, int32_t* b_int, int32_t* mult,
+                                int32_t* shift, int8_t* lut, int32_t* mult_in,
+                                int32_t* shift_in, hipStream_t s) {
+  if (bias_block < 1 || (bias_block & (bias_block - 1)) || d_out % bias_block || act < 0 ||
+      act > 3 || post < 1 || (post & (post - 1)) || post > WH_MAX_BLOCK)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(int_constants_kernel, dim3(1), dim3(256), 0, s, bias, s_w, d_out, d_out_pad,
-                     m, bias_block, double(s_x), double(s_y), b_int, mult, shift);
+                     m, post, act, bias_block, double(s_x), double(s_y), double(s_z),
+                     double(s_u), b_int, mult, shift, lut, mult_in, shift_in);
   return hipGetLastError();
+}
+
+static bool transition_ok(const IntTransition& tr, int d_out) {
+  auto pow2 = [](int v) { return v >= 1 && v <= WH_MAX_BLOCK && !(v & (v - 1)); };
+  return pow2(tr.m) && pow2(tr.post) && d_out % tr.m == 0 && d_out % tr.post == 0 &&
+         tr.act >= 0 && tr.act <= 3;
 }
 
 hipError_t launch_int_fused(const int8_t* x, int64_t T, int d_in, const int8_t* w, int d_out,
-                            int m, const int32_t* b_int, const int32_t* mult,
-                            const int32_t* shift, int8_t* y, hipStream_t s) {
+                            const IntTransition& tr, int8_t* y, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (d_out % 256 || d_in % 32 || m < 1 || m > WH_MAX_BLOCK || (m & (m - 1)))
-    return hipErrorInvalidValue;
+  if (d_out % 256 || d_in % 32 || !transition_ok(tr, d_out)) return hipErrorInvalidValue;
   const dim3 grid{unsigned((T + IF_ROWS - 1) / IF_ROWS), unsigned(d_out / 256)};
-  hipLaunchKernelGGL(int_fused_kernel, grid, dim3(512), 0, s, x, T, d_in, w, d_out, m, b_int,
-                     mult, shift, y);
+  if (tr.act == 0)
+    hipLaunchKernelGGL(int_fused_kernel<0>, grid, dim3(512), 0, s, x, T, d_in, w, d_out, tr, y);
+  else if (tr.act == 1)
+    hipLaunchKernelGGL(int_fused_kernel<1>, grid, dim3(512), 0, s, x, T, d_in, w, d_out, tr, y);
+  else
+    hipLaunchKernelGGL(int_fused_kernel<2>, grid, dim3(512), 0, s, x, T, d_in, w, d_out, tr, y);
   return hipGetLastError();
 }
 
-hipError_t launch_int_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_out, int m,
-                             const int32_t* b_int, const int32_t* mult, const int32_t* shift,
-                             int8_t* y, int64_t ldy, hipStream_t s) {
+hipError_t launch_int_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_out,
+                              const IntTransition& tr, int8_t* y, int64_t ldy, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (m < 1 || m > WH_MAX_BLOCK || (m & (m - 1)) || d_out % m || d_out % 8)
-    return hipErrorInvalidValue;
+  if (d_out % 8 || !transition_ok(tr, d_out)) return hipErrorInvalidValue;
   const int chunks = (d_out + 255) / 256;
   const int64_t units = T * chunks;   // 16 lanes each, 16 per block
-  hipLaunchKernelGGL(int_requant_kernel, dim3(unsigned((units + 15) / 16)), dim3(256), 0, s, acc,
-                     ldc, T, d_out, chunks, m, b_int, mult, shift, y, ldy);
+  const dim3 grid{unsigned((units + 15) / 16)};
+  if (tr.act == 0)
+    hipLaunchKernelGGL(int_requant_kernel<0>, grid, dim3(256), 0, s, acc, ldc, T, d_out, chunks,
+                       tr, y, ldy);
+  else if (tr.act == 1)
+    hipLaunchKernelGGL(int_requant_kernel<1>, grid, dim3(256), 0, s, acc, ldc, T, d_out, chunks,
+                       tr, y, ldy);
+  else
+    hipLaunchKernelGGL(int_requant_kernel<2>, grid, dim3(256), 0, s, acc, ldc, T, d_out, chunks,
+                       tr, y, ldy);
   return hipGetLastError();
 }
 

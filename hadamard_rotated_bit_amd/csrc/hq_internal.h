@@ -137,20 +137,37 @@ constexpr int WH_BIAS_MAX = 1 << 27;    // bias codes saturate here (exact float
 // wbar [d_out, d_in] f32 = H_m (blocks of m output channels) . weight.
 hipError_t launch_wh_weight(const void* w, int w_bf16, int d_out, int d_in, int m, float* wbar,
                             hipStream_t s);
+// The transition after an integer layer: the transform before the
+// activation (m), the activation (hq_int_act), the transform after it (post),
+// and the prepared constants (bias codes, per-channel multipliers, the shift;
+// for SiLU/GELU also the table over z + 127, M_in and n_in).
+struct IntTransition {
+  int m, post, act;
+  const int32_t* b_int;
+  const int32_t* mult;
+  const int32_t* shift;
+  const int8_t* lut;
+  const int32_t* mult_in;
+  const int32_t* shift_in;
+};
 // b_int, mult [d_out_pad] and shift [1] from bias [d_out] (or NULL; b-bar =
-// b H over blocks of bias_block channels) and s_w [d_out]; rho uses sqrt(m).
+// b H over blocks of bias_block channels) and s_w [d_out]. Identity / ReLU:
+// rho = s_x s_w / (sqrt(m post) s_y). SiLU / GELU: rho = s_x s_w / (sqrt(m)
+// s_z), the table lut [256] (entry z + 127 = clamp(round(phi(s_z z) / s_u));
+// entry 255 = 0), M_in and n_in from s_u / (sqrt(post) s_y).
 hipError_t launch_int_constants(const float* bias, const float* s_w, int d_out, int d_out_pad,
-                                int m, int bias_block, float s_x, float s_y, int32_t* b_int,
-                                int32_t* mult, int32_t* shift, hipStream_t s);
-// The integer GEMM and that requantisation in one kernel (d_out % 256 == 0):
-// y [T, d_out] from x [T, d_in] int8 and w [>= d_out, d_in] int8; the int32
-// products stay on the chip.
+                                int m, int post, int act, int bias_block, float s_x, float s_y,
+                                float s_z, float s_u, int32_t* b_int, int32_t* mult,
+                                int32_t* shift, int8_t* lut, int32_t* mult_in,
+                                int32_t* shift_in, hipStream_t s);
+// The integer GEMM and the transition's requantisation in one kernel
+// (d_out % 256 == 0): y [T, d_out] from x [T, d_in] int8 and w [>= d_out,
+// d_in] int8; the int32 products stay on the chip.
 hipError_t launch_int_fused(const int8_t* x, int64_t T, int d_in, const int8_t* w, int d_out,
-                            int m, const int32_t* b_int, const int32_t* mult,
-                            const int32_t* shift, int8_t* y, hipStream_t s);
-// y [T, ldy] int8 = clamp(round(H~_m (mult . (acc + b_int)) / 2^shift), +-127).
-hipError_t launch_int_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_out, int m,
-                              const int32_t* b_int, const int32_t* mult, const int32_t* shift,
-                              int8_t* y, int64_t ldy, hipStream_t s);
+                            const IntTransition& tr, int8_t* y, hipStream_t s);
+// y [T, ldy] int8 from acc [T, ldc] (without the bias codes): the
+// transition's requantisation.
+hipError_t launch_int_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_out,
+                              const IntTransition& tr, int8_t* y, int64_t ldy, hipStream_t s);
 
 }  // namespace hq

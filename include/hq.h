@@ -94,7 +94,7 @@
 extern "C" {
 #endif
 
-#define HQ_ABI_VERSION 7
+#define HQ_ABI_VERSION 8
 
 typedef enum {
   HQ_OK = 0,
@@ -339,6 +339,27 @@ int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes
  *     y   = clamp(round(H~_m (M . a) / 2^n), -127, 127)
  *     M_c = round(2^n rho_c),  rho_c = s_x s_w,c / (sqrt(m) s_y)
  *
+ * With an activation phi between this layer and the next (Table I; Eq. (20)-
+ * (22); supplement Sec. VIII-C Eq. (45)-(49)), the transition runs H~_m
+ * before phi and H~_p after it (p = post_block: the next layer's H_in order
+ * when that layer is DH; WH-to-DH uses both). ReLU is positively homogeneous,
+ * so one multiplier per channel and one shift carry the whole transition:
+ *
+ *     y   = clamp(round(H~_p (relu(H~_m (M . a))) / 2^n), -127, 127)
+ *     rho_c = s_x s_w,c / (sqrt(m p) s_y)        (also for phi = identity)
+ *
+ * SiLU and GELU go through their own int8 grids s_z (before phi) and s_u
+ * (after it), phi realised as a 255-entry integer table:
+ *
+ *     z   = clamp(round(H~_m (M_out . a) / 2^n_out)),  M_out,c ~ 2^n_out s_x s_w,c / (sqrt(m) s_z)
+ *     u   = LUT[z] = clamp(round(phi(s_z z) / s_u))
+ *     y   = clamp(round(H~_p (M_in u) / 2^n_in)),     M_in ~ 2^n_in s_u / (sqrt(p) s_y)
+ *
+ * (GELU: x Phi(x) with the Gaussian CDF; SiLU: x / (1 + e^-x).) A DH layer
+ * has no output-side transform of its own, so with an activation its m must
+ * be 1 and the next layer's H_in goes in p; with phi = identity the two
+ * positions give the same integers.
+ *
  * H~_m: the +-1 Sylvester matrix of order m, block-diagonal over d_out / m
  * blocks of output channels (additions and subtractions only). It is Table
  * I's output-side conversion: for a WH layer followed by a WH layer it
@@ -348,12 +369,21 @@ int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes
  * H_out) is the normalised Sylvester matrix over contiguous blocks. s_w,c:
  * per-output-channel scale of W-bar (8-bit symmetric codes); s_y: the scale
  * of the output codes (the next layer's input scale). n: the largest shift
- * <= 48 with every M_c <= 32767. round() is round half to even; bias codes
- * saturate at +-2^27, so every intermediate stays below 2^51 in magnitude.
- * Every online step is exact integer arithmetic (int32 products; after M the
- * kernel carries the integers in float64 registers, exact in that range).
+ * <= 48 with every M_c within the multiplier bound, min(32767, 2^(24 - L) - 1)
+ * for transforms whose orders multiply to 2^L (32767 for one transform of
+ * order <= 256; 255 for two of order 256). round() is round half to even;
+ * bias codes saturate at +-2^27, so every intermediate stays below 2^52 in
+ * magnitude. Every online step is exact integer arithmetic (int32 products;
+ * after M the kernel carries the integers in float64 registers, exact in
+ * that range).
  */
 typedef enum { HQ_INT_WH = 0, HQ_INT_DH = 1 } hq_int_side;
+typedef enum {
+  HQ_INT_ACT_NONE = 0,  /* identity                                   */
+  HQ_INT_ACT_RELU = 1,  /* max(x, 0), on the common scale             */
+  HQ_INT_ACT_SILU = 2,  /* x / (1 + e^-x), integer table on s_z, s_u  */
+  HQ_INT_ACT_GELU = 3   /* x Phi(x), integer table on s_z, s_u        */
+} hq_int_act;
 
 typedef struct {
   int32_t d_in;     /* input channels: same rule as hq_desc.d_in                  */
@@ -363,6 +393,9 @@ typedef struct {
   int32_t w_dtype;  /* hq_dtype of weight                                         */
   int32_t side;     /* hq_int_side                                                */
   int32_t in_block; /* DH: order of H_in, a power of two dividing d_in; WH: 1     */
+  int32_t act;      /* hq_int_act between this layer and the next                 */
+  int32_t post_block; /* p: transform after the activation (the next layer's H_in
+                       order), power of two <= 256 dividing d_out; 1 = none       */
 } hq_int_desc;
 
 /* Byte offsets of the arrays in an integer-layer prepared blob (256-byte aligned). */
@@ -375,6 +408,9 @@ typedef struct {
   size_t shift;     /* int32 [1]                shared shift n                  */
   size_t wbar;      /* f32   [d_out, d_in]      W-bar (written by the prepare)  */
   int64_t d_out_pad;
+  size_t lut;       /* int8  [256]              SiLU/GELU table, entry z + 127  */
+  size_t mult_in;   /* int32 [1]                M_in (SiLU/GELU)                */
+  size_t shift_in;  /* int32 [1]                n_in (SiLU/GELU)                */
 } hq_int_layout;
 
 /* Bookkeeping, host-only: validation, blob size and layout, workspace of
@@ -385,23 +421,26 @@ int hq_int_prepared_layout_of(const hq_int_desc* desc, hq_int_layout* out);
 size_t hq_int_workspace_bytes(const hq_int_desc* desc, int64_t T);
 
 /* Offline half of an integer-only layer (HaTQ Sec. IV-B Eq. (13)-(19),
- * supplement Eq. (40)-(44)): weight [d_out, d_in] (w_dtype) and bias f32
+ * supplement Eq. (40)-(49)): weight [d_out, d_in] (w_dtype) and bias f32
  * [d_out] (or NULL) into
  * the blob (hq_int_prepared_bytes): W-bar, its int8 codes and scales, the bias
- * codes, the multipliers and the shift. s_x > 0 is the scale of the int8
- * input, s_y > 0 that of the int8 output. */
+ * codes, the multipliers and the shift (SiLU/GELU: also the table, M_in and
+ * n_in). s_x > 0 is the scale of the int8 input, s_y > 0 that of the int8
+ * output; s_z, s_u > 0 are the grids around a SiLU/GELU table (ignored for
+ * the other activations). */
 int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bias, float s_x,
-                   float s_y, void* prepared, void* stream);
+                   float s_y, float s_z, float s_u, void* prepared, void* stream);
 
 /* The integer-only hot path (HaTQ Eq. (4), then the requantisation of
- * Eq. (19)-(22)): y_codes int8 [T, d_out] from x_codes int8 [T, d_in] (codes in
+ * Eq. (19)-(22), or of supplement Eq. (45)-(49) for SiLU/GELU): y_codes int8
+ * [T, d_out] from x_codes int8 [T, d_in] (codes in
  * [-127, 127], row-major, in the layer's input basis): the int8 MFMA product
  * into the workspace, then hq_int_requant's kernel. T = 0 is a no-op. */
 int hq_int_linear(const hq_int_desc* desc, const void* prepared, const int8_t* x_codes,
                   int64_t T, int8_t* y_codes, void* workspace, size_t workspace_bytes,
                   void* stream);
 
-/* Requantisation alone (HaTQ Eq. (19)-(22) with the identity activation):
+/* Requantisation alone (HaTQ Eq. (19)-(22); supplement Eq. (45)-(49)):
  * y_codes int8 [T, d_out] from the int32 products
  * acc [T, d_out] (x_int . w-bar_int^T, WITHOUT the bias codes, which this
  * stage adds). |acc| <= 2^27 (as every product of int8 codes over d_in <= 8192

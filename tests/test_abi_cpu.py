@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lib.hq_abi_version() == 7
+    assert lib.hq_abi_version() == 8
     assert lib.hq_status_str(0) == b"HQ_OK"
     assert lib.hq_status_str(-3) == b"HQ_ERR_WORKSPACE"
     assert lib.hq_status_str(99) == b"HQ_ERR_UNKNOWN"
@@ -235,6 +235,9 @@ def _il(**kw):
     (dict(block=128, d_out=200), -2), (dict(block=0), -2), (dict(side=2), -1),
     (dict(side=-1), -1), (dict(in_block=2), -2), (dict(side=1, in_block=3), -2),
     (dict(side=1, in_block=512), -2), (dict(side=1, in_block=0), -2),
+    (dict(act=4), -1), (dict(act=-1), -1), (dict(post_block=3), -2), (dict(post_block=0), -2),
+    (dict(post_block=512, d_out=512), -2), (dict(post_block=64, d_out=96, block=1), -2),
+    (dict(side=1, in_block=256, act=1, block=16), -2),
 ])
 def test_int_validation_rejects(kw, status):
     d = _il(**kw)
@@ -245,7 +248,9 @@ def test_int_validation_rejects(kw, status):
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(side=1, in_block=256), dict(side=1, in_block=1, block=1),
-                                dict(side=1, in_block=32, block=8, d_out=136)])
+                                dict(side=1, in_block=32, block=8, d_out=136),
+                                dict(act=1, post_block=256), dict(act=3, post_block=8, block=16),
+                                dict(side=1, in_block=256, act=2, block=1, post_block=64)])
 def test_int_validation_accepts(kw):
     assert lib.hq_int_validate(_il(**kw)._ref) == 0
 
@@ -256,8 +261,9 @@ def test_int_layout_and_workspace():
     L = _lib.HqIntLayout()
     assert lib.hq_int_prepared_layout_of(d._ref, ctypes.byref(L)) == 0
     assert L.d_out_pad == 256
-    offs = [L.w_codes, L.w_scale, L.b_int, L.mult, L.shift, L.wbar, L.total]
+    offs = [L.w_codes, L.w_scale, L.b_int, L.mult, L.shift, L.lut, L.wbar, L.total]
     assert all(o % 256 == 0 for o in offs[:-1]) and offs == sorted(offs)
+    assert (L.mult_in, L.shift_in) == (L.shift + 4, L.shift + 8) and L.wbar - L.lut >= 256
     assert L.w_scale - L.w_codes >= 256 * 384 and L.total - L.wbar >= 4 * 136 * 384
     assert L.b_int - L.w_scale >= 4 * 256 and L.mult - L.b_int >= 4 * 256
     assert lib.hq_int_prepared_bytes(d._ref) == L.total
@@ -268,9 +274,15 @@ def test_int_layout_and_workspace():
 def test_int_entry_points_reject_before_launch():
     d = _il()._ref
     p = ctypes.c_void_p(0x1000)   # never dereferenced: every call fails validation first
-    assert lib.hq_int_prepare(d, None, None, ctypes.c_float(1.0), ctypes.c_float(1.0), p, None) == -1
-    assert lib.hq_int_prepare(d, p, None, ctypes.c_float(0.0), ctypes.c_float(1.0), p, None) == -1
-    assert lib.hq_int_prepare(d, p, None, ctypes.c_float(1.0), ctypes.c_float(float("nan")), p,
+    f = ctypes.c_float
+    assert lib.hq_int_prepare(d, None, None, f(1.0), f(1.0), f(0.0), f(0.0), p, None) == -1
+    assert lib.hq_int_prepare(d, p, None, f(0.0), f(1.0), f(0.0), f(0.0), p, None) == -1
+    assert lib.hq_int_prepare(d, p, None, f(1.0), f(float("nan")), f(0.0), f(0.0), p,
+                              None) == -1
+    # a SiLU / GELU table needs both of its grids
+    g = _il(act=3, post_block=8)._ref
+    assert lib.hq_int_prepare(g, p, None, f(1.0), f(1.0), f(0.0), f(1.0), p, None) == -1
+    assert lib.hq_int_prepare(g, p, None, f(1.0), f(1.0), f(1.0), f(float("inf")), p,
                               None) == -1
     assert lib.hq_int_linear(d, p, p, -1, p, p, 1 << 30, None) == -1
     assert lib.hq_int_linear(d, p, p, 16, p, p, 10, None) == -3
@@ -317,7 +329,7 @@ def test_entry_points_reject_misaligned_pointers():
     c = ctypes.byref(_d(center=2))
     bad(lib.hq_channel_center(c, p, q, 4, p, p, p, 1 << 30, None))
     wi = _il()._ref
-    bad(lib.hq_int_prepare(wi, q, None, f(1.0), f(1.0), p, None))
+    bad(lib.hq_int_prepare(wi, q, None, f(1.0), f(1.0), f(0.0), f(0.0), p, None))
     bad(lib.hq_int_linear(wi, p, q, 16, p, p, 1 << 30, None))
 
 
