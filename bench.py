@@ -501,7 +501,7 @@ def write_traffic(d, workload):
     """Per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of the GEMM from two counter
     runs of this benchmark on `workload`, each scaled by what the counter reads
     for the run's plain copy kernel of known size (a clone of X), into
-    profiles/gemm_f6_<workload>_traffic.json with the hash of the GEMM sources."""
+    profiles/gemm_f6_dequant_<workload>_traffic.json with the hash of the GEMM sources."""
     import csv
     from collections import defaultdict
     from hadamard_rotated_bit_amd import workloads as WL
