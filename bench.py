@@ -12,9 +12,12 @@ double-Hadamard W8A8 layer) get one object each in the same JSON line.
 
 Inputs rotate through enough distinct X / Y buffers (> 512 MB) that a step's
 activations are not served from the 256 MB Infinity Cache left over from the
-previous visit. Per-kernel times come from HIP events around back-to-back
-launches of each stage entry point (captured in a HIP graph, replayed on the
-stream the events are recorded on). Prints one JSON line.
+previous visit. Each workload first makes untimed calls for SPIN_UP_S seconds
+(the GPU leaves the idle clock state host-side data generation leaves it in),
+then W warmup steps, then the K timed steps. Per-kernel times come from HIP
+events around back-to-back launches of each stage entry point (captured in a
+HIP graph, replayed on the stream the events are recorded on; median of five
+replays). Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flux_proj]
 """
@@ -36,6 +39,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Hadamard-quantized linear tokens/s + effective TOPS (% int8 MFMA/HBM roofline)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+SPIN_UP_S = 0.2                # untimed calls before each workload's timings (s)
+GRAPH_REPS = 5                 # timed replays per stage graph (median taken)
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POP/s)
 FP6_PEAK_TOPS = 10100.0        # MI355X dense fp6 / fp4 MFMA (10.1 PFLOP/s)
 # Non-packed fp32 VALU lane operations per second: 256 CUs x 4 SIMDs x 16
@@ -129,6 +134,17 @@ def cpu_baseline(w, x, weight, bias, sigma, l1, l2, Y_gpu, target_s):
             "parity_rel_fro_vs_gpu": err, "parity_rows": rows}
 
 
+def spin_up(torch, fn, nbuf, seconds=SPIN_UP_S):
+    """Untimed calls of fn for at least `seconds` of wall time, so that the
+    GPU leaves its idle clock state (data generation on the host keeps it
+    idle before each workload) before anything is timed."""
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        fn(i % nbuf)
+        i += 1
+    torch.cuda.synchronize()
+
+
 def timed_steps(torch, fn, nbuf, steps, warmup):
     for i in range(warmup):
         fn(i % nbuf)
@@ -157,9 +173,11 @@ def step_percentiles(torch, fn, nbuf, steps, start):
     return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
 
 
-def graph_time(torch, fn, n):
-    """Average time of fn(i), i < n, captured back to back in one HIP graph
-    and replayed on the current stream, timed with HIP events on that stream."""
+def graph_time(torch, fn, n, reps=GRAPH_REPS):
+    """Time of fn(i), i < n, captured back to back in one HIP graph and
+    replayed on the current stream, timed with HIP events on that stream:
+    the median over `reps` timed replays (after one untimed replay) of the
+    replay time divided by n."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -172,13 +190,15 @@ def graph_time(torch, fn, n):
             fn(i)
     g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for k in range(reps):
+        g.replay()
+        ev[k + 1].record()
     torch.cuda.synchronize()
     del g
-    return e0.elapsed_time(e1) / n
+    t = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(reps))
+    return t[reps // 2] / n
 
 
 class Layer:
@@ -232,6 +252,7 @@ def measure(hq, torch, L, desc, steps, warmup):
     def step(i):
         hq.quant_linear(desc, prep, L.Xs[i], out=L.Ys[i], workspace=ws)
 
+    spin_up(torch, step, nbuf)
     ms, wall = timed_steps(torch, step, nbuf, steps, warmup)
     pct = step_percentiles(torch, step, nbuf, steps, warmup + steps)
     n = max(1, min(steps, 20))
@@ -450,6 +471,7 @@ def integer_layer(hq, torch, WL, steps, warmup, dev, side, gelu=False):
     Xs = [X0] + [X0.clone() for _ in range(nbuf - 1)]
     Ys = [torch.empty(w.T, w.d_out, dtype=torch.int8, device=dev) for _ in range(nbuf)]
     ws = torch.empty(hq.int_workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
+    spin_up(torch, lambda i: hq.int_linear(desc, prep, Xs[i], out=Ys[i], workspace=ws), nbuf)
     ms, _ = timed_steps(torch, lambda i: hq.int_linear(desc, prep, Xs[i], out=Ys[i], workspace=ws),
                         nbuf, steps, warmup)
     y = Ys[(warmup + steps - 1) % nbuf].float() * s_y
@@ -595,7 +617,8 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": k1["hbm_frac"], "traffic": None}
     out = {
         "metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": warmup, "ms_per_step": head["ms_per_step"],
+        "steps": steps, "warmup": warmup, "spin_up_s": SPIN_UP_S,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "e2m3" if fp6 else "int8", "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.T, "d_in": w.d_in, "d_out": w.d_out,
