@@ -393,6 +393,17 @@ def run(x, weight, bias, *, block: int, a_bits: int, w_bits: int, center,
 #   the same integers.
 # * GELU is x Phi(x) with the Gaussian CDF (the erf form), SiLU x / (1 + e^-x);
 #   the table is built in float64 and rounded half to even.
+# * Padded orders (supplement Sec. VII-B Eq. (35)-(41)), Sylvester orders
+#   only: a transform order m larger than the channel count C pads the
+#   channels with zeros, T = P_C H_m with P_C = [I_C 0]. A WH layer with
+#   ``block`` m > d_out holds W-bar = H_m [W; 0] and b-bar = [b 0] H_m (m
+#   accumulator channels) and keeps the first d_out channels after H~_m (the
+#   projection P_C); a DH layer with ``in_block`` m > d_in holds W-bar =
+#   [W 0] H_m and takes m-channel input codes (the previous layer's padded
+#   output); ``post_block`` m > d_out pads the activation's d_out channels
+#   with zeros before H~_post, so the output has m channels. Eq. (35) picks
+#   the smallest supported m >= 4 ceil(C / 4); any larger power of two
+#   gives the same identities and is accepted.
 # * Bias codes saturate at +-2^27: with |a| <= 127^2 d_in <= 2^27 and M <= 32767,
 #   every intermediate of the requantisation then stays below 2^51 in magnitude.
 # * round() is round half to even throughout, on exact rationals.
@@ -493,10 +504,14 @@ def int_prepare(weight, bias, s_x: float, s_y: float, block: int, side: int = SI
     (for SiLU/GELU: M_out and n_out, plus the table, M_in and n_in)."""
     weight = np.asarray(weight, dtype=np.float64)
     d_out, d_in = weight.shape
-    if d_out % block:
-        raise ValueError("block must divide d_out")
-    if post_block < 1 or post_block & (post_block - 1) or d_out % post_block:
-        raise ValueError("post_block must be a power of two dividing d_out")
+
+    def order_ok(m, c):
+        # a power of two dividing c (block-diagonal) or above it (one padded block)
+        return m >= 1 and not (m & (m - 1)) and (c % m == 0 or m > c)
+    if not order_ok(block, d_out) or (side == SIDE_DH and block > d_out):
+        raise ValueError("block must be a power of two dividing d_out (WH: or above it)")
+    if not order_ok(post_block, d_out):
+        raise ValueError("post_block must be a power of two dividing d_out or above it")
     if act not in (ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU):
         raise ValueError(f"unknown activation {act}")
     if side == SIDE_DH and act != ACT_NONE and block != 1:
@@ -506,24 +521,33 @@ def int_prepare(weight, bias, s_x: float, s_y: float, block: int, side: int = SI
         raise ValueError("SiLU/GELU need the grids s_z > 0 and s_u > 0")
     bias = np.asarray(bias, dtype=np.float64)
     if side == SIDE_WH:
-        # H_out acts on the output-channel index: column-wise on weight, row-wise on b
-        wbar = rotate(weight.T, block).T
-        bbar = rotate(bias[None, :], block)[0]
+        # H_out acts on the output-channel index: column-wise on weight, row-wise on b;
+        # a padded order first appends zero output channels (Eq. (40) with T_out = P H_m)
+        acc = max(block, d_out)
+        wpad = np.zeros((acc, d_in))
+        wpad[:d_out] = weight
+        bpad = np.zeros(acc)
+        bpad[:d_out] = bias
+        wbar = rotate(wpad.T, block).T
+        bbar = rotate(bpad[None, :], block)[0]
     elif side == SIDE_DH:
-        if d_in % in_block:
-            raise ValueError("in_block must divide d_in")
-        wbar = rotate(weight, in_block)
+        if not order_ok(in_block, d_in):
+            raise ValueError("in_block must be a power of two dividing d_in or above it")
+        # Eq. (39): the input channels padded to in_block, then H_in along them
+        wpad = np.zeros((d_out, max(in_block, d_in)))
+        wpad[:, :d_in] = weight
+        wbar = rotate(wpad, in_block)
         bbar = bias.copy()
     else:
         raise ValueError(f"side must be SIDE_WH or SIDE_DH, got {side}")
     qw, s_w = quantize_rows(wbar, w_bits)
     s_a = float(s_x) * s_w
-    b_int = np.zeros(d_out, dtype=np.int64)
+    b_int = np.zeros(wbar.shape[0], dtype=np.int64)
     nz = s_a > 0
     b_int[nz] = np.clip(np.rint(bbar[nz] / s_a[nz]), -RQ_BIAS_MAX, RQ_BIAS_MAX).astype(np.int64)
     out = {"wbar": wbar, "bbar": bbar, "qw": qw, "s_w": s_w, "b_int": b_int, "block": block,
            "side": side, "in_block": in_block, "s_x": float(s_x), "s_y": float(s_y), "act": act,
-           "post_block": post_block}
+           "post_block": post_block, "d_out": d_out}
     if not general:
         # Eq. (19): one multiplier per channel and one shift for the whole
         # transition (ReLU commutes with the common factor 2^-n, Eq. (20)-(22))
@@ -556,17 +580,25 @@ def int_forward(x_int, prep, bits: int = 8) -> dict:
     a = int_gemm(x_int, prep["qw"]) + prep["b_int"][None, :]
     u = a * prep["mult"][None, :]
     v = unnormalised_transform(u, prep["block"])
+    d_out = prep.get("d_out", v.shape[1])
+    v = v[:, :d_out]   # a padded WH order keeps the first d_out channels (P_C)
     out = {"acc": a, "u": u, "v": v}
     act = prep.get("act", ACT_NONE)
     post = prep.get("post_block", 1)
+
+    def pad(t):
+        # a padded post order appends zero channels up to post_block
+        if post <= t.shape[1]:
+            return t
+        return np.concatenate([t, np.zeros((t.shape[0], post - t.shape[1]), t.dtype)], axis=1)
     if act in (ACT_NONE, ACT_RELU):
         pv = np.maximum(v, 0) if act == ACT_RELU else v
-        w = unnormalised_transform(pv, post)
+        w = unnormalised_transform(pad(pv), post)
         y = np.clip(round_half_even_shift(w, prep["shift"]), -qmax, qmax)
     else:
         z = np.clip(round_half_even_shift(v, prep["shift"]), -qmax, qmax)
         ua = prep["lut"][z + qmax]
-        w = unnormalised_transform(ua * prep["mult_in"], post)
+        w = unnormalised_transform(pad(ua * prep["mult_in"]), post)
         y = np.clip(round_half_even_shift(w, prep["shift_in"]), -qmax, qmax)
         out.update(z=z, u_act=ua)
     out.update(w=w, y_int=y.astype(np.int16))
@@ -588,7 +620,11 @@ def int_dequant_reference(x_int, prep, phi=None) -> np.ndarray:
         phi = {ACT_NONE: (lambda v: v), ACT_RELU: _relu}.get(act) or PHI[act]
     a = int_gemm(x_int, prep["qw"]) + prep["b_int"][None, :]
     ya = a.astype(np.float64) * (prep["s_x"] * prep["s_w"])[None, :]
-    return rotate(phi(rotate(ya, prep["block"])), prep.get("post_block", 1)) / prep["s_y"]
+    v = phi(rotate(ya, prep["block"])[:, :prep.get("d_out", ya.shape[1])])
+    post = prep.get("post_block", 1)
+    if post > v.shape[1]:
+        v = np.concatenate([v, np.zeros((v.shape[0], post - v.shape[1]))], axis=1)
+    return rotate(v, post) / prep["s_y"]
 
 
 def quantize_static(x, s: float, bits: int = 8) -> np.ndarray:

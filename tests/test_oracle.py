@@ -623,7 +623,9 @@ def test_wh_rejects_bad_block():
     with pytest.raises(ValueError):
         O.int_prepare(weight, bias, s_x, s_y, 3)
     with pytest.raises(ValueError):
-        O.int_prepare(weight, bias, s_x, s_y, 128)
+        O.int_prepare(weight, bias, s_x, s_y, 48)
+    with pytest.raises(ValueError):   # a DH layer pads through post_block, not block
+        O.int_prepare(weight, bias, s_x, s_y, 128, side=O.SIDE_DH)
 
 
 @pytest.mark.parametrize("k", [1, 4, 32])
@@ -850,3 +852,98 @@ def test_int_prepare_rejects_bad_activation_setups():
         O.int_prepare(weight, bias, s_x, s_y, 1, act=O.ACT_GELU)
     with pytest.raises(ValueError):
         O.int_prepare(weight, bias, s_x, s_y, 1, act=7)
+
+
+# --- Padded orders (supplement Sec. VII-B Eq. (35)-(41)), Sylvester orders ---
+
+def _pad_inputs(seed=31, T=24, d_in=80, d_out=48):
+    rng = np.random.default_rng(seed)
+    x = rng.laplace(0.0, 1.0, (T, d_in))
+    x[:, 3] *= 20.0
+    weight = rng.normal(0.0, 0.05, (d_out, d_in))
+    bias = rng.normal(0.0, 0.05, d_out)
+    return x, weight, bias
+
+
+@pytest.mark.parametrize("m", [64, 128])
+def test_wh_padded_identity(m):
+    # T_out = P_C H_m^T (C x m, scipy-built H): W-bar = T_out^T W, b-bar = b T_out
+    # (Eq. (40)); orthonormal rows (Eq. (37)); the WH identity (Eq. (41)); the
+    # padded channels of (X W-bar^T + b-bar) H_m are zero, so keeping the first
+    # C (P_C) loses nothing
+    x, weight, bias = _pad_inputs()
+    c = weight.shape[0]
+    t_out = np.eye(c, m) @ (scipy.linalg.hadamard(m) / np.sqrt(m)).T
+    np.testing.assert_allclose(t_out @ t_out.T, np.eye(c), atol=1e-14)
+    p = O.int_prepare(weight, bias, 1.0, 1.0, m)
+    np.testing.assert_allclose(p["wbar"], t_out.T @ weight, atol=1e-14)
+    np.testing.assert_allclose(p["bbar"], bias @ t_out, atol=1e-14)
+    z = x @ p["wbar"].T + p["bbar"]
+    np.testing.assert_allclose(z @ t_out.T, x @ weight.T + bias, atol=1e-12)
+    assert np.abs(O.rotate(z, m)[:, c:]).max() < 1e-12
+
+
+@pytest.mark.parametrize("m", [128, 256])
+def test_dh_padded_identity(m):
+    # T_in = P_C H_m: W-bar = W T_in and (X T_in)(W T_in)^T + b = X W^T + b (Eq. (39))
+    x, weight, bias = _pad_inputs()
+    c = weight.shape[1]
+    t_in = np.eye(c, m) @ (scipy.linalg.hadamard(m) / np.sqrt(m))
+    p = O.int_prepare(weight, bias, 1.0, 1.0, 1, side=O.SIDE_DH, in_block=m)
+    np.testing.assert_allclose(p["wbar"], weight @ t_in, atol=1e-14)
+    np.testing.assert_allclose((x @ t_in) @ p["wbar"].T + bias, x @ weight.T + bias, atol=1e-12)
+
+
+@pytest.mark.parametrize("act,post", [(0, 1), (1, 64), (3, 64)])
+def test_wh_padded_integer_path(act, post):
+    # WH with a padded output order (48 channels, H_64) and a padded next-layer
+    # order: the integer codes against the dequantised reference through the
+    # same projections (identity / ReLU: within the rounding bound of the
+    # multiplier and the final shift), and the codes stand for phi(layer) in
+    # the next basis
+    x, weight, bias = _pad_inputs()
+    y = x @ weight.T + bias
+    phi = {0: (lambda v: v), 1: (lambda v: np.maximum(v, 0.0)), 3: O.gelu}[act]
+    fy = phi(y)
+    fpad = np.concatenate([fy, np.zeros((fy.shape[0], max(post, 48) - 48))], axis=1)
+    out = O.rotate(fpad, post)
+    s_x, s_y = np.abs(x).max() / 127, np.abs(out).max() / 127
+    kw = dict(act=act, post_block=post)
+    if act == 3:
+        kw.update(s_z=np.abs(y).max() / 127, s_u=np.abs(fy).max() / 127)
+    p = O.int_prepare(weight, bias, s_x, s_y, 64, **kw)
+    assert p["qw"].shape == (64, 80) and p["b_int"].shape == (64,)
+    xi = O.quantize_static(x, s_x)
+    r = O.int_forward(xi, p)
+    assert r["y_int"].shape == (24, max(post, 48))
+    if act != 3:
+        ref = O.int_dequant_reference(xi, p)
+        a = np.abs(r["acc"]).astype(np.float64)
+        e = _blocksum(0.5 * a, 64)[:, :48]
+        e = np.concatenate([e, np.zeros((24, max(post, 48) - 48))], axis=1)
+        e = _blocksum(e, post) / 2.0 ** p["shift"]
+        assert np.all(np.abs(r["y_int"] - np.clip(ref, -127, 127)) <= 0.5 + e + 1e-9)
+    assert O.sqnr_db(out / s_y, r["y_int"].astype(np.float64)) > 20
+
+
+def test_padded_wh_to_dh_chain():
+    # Table I, WH-to-DH across padded orders: a WH layer (48 outputs, H_out of
+    # order 64) with ReLU hands 64 codes in the next layer's padded H_64 basis to
+    # a DH layer whose 48 input channels are padded to 64 (Eq. (39))
+    x, w1, b1 = _pad_inputs()
+    rng = np.random.default_rng(32)
+    w2 = rng.normal(0.0, 0.1, (40, 48))
+    b2 = rng.normal(0.0, 0.05, 40)
+    h1 = np.maximum(x @ w1.T + b1, 0.0)
+    y2 = h1 @ w2.T + b2
+    s0 = np.abs(x).max() / 127
+    h1p = O.rotate(np.concatenate([h1, np.zeros((24, 16))], axis=1), 64)
+    s1 = np.abs(h1p).max() / 127
+    s2 = np.abs(y2).max() / 127
+    p1 = O.int_prepare(w1, b1, s0, s1, 64, act=O.ACT_RELU, post_block=64)
+    p2 = O.int_prepare(w2, b2, s1, s2, 1, side=O.SIDE_DH, in_block=64)
+    q1 = O.int_forward(O.quantize_static(x, s0), p1)["y_int"]
+    assert q1.shape == (24, 64)
+    q2 = O.int_forward(q1, p2)["y_int"]
+    assert O.sqnr_db(h1p / s1, q1.astype(np.float64)) > 25
+    assert O.sqnr_db(y2 / s2, q2.astype(np.float64)) > 20
