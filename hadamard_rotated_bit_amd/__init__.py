@@ -387,6 +387,23 @@ class IntDesc:
     act: int = _lib.HQ_INT_ACT_NONE
     post_block: int = 1
 
+    @property
+    def x_width(self) -> int:
+        """Input codes per token (a padded DH input order takes in_block)."""
+        pad = self.side == _lib.HQ_INT_DH and self.in_block > self.d_in
+        return self.in_block if pad else self.d_in
+
+    @property
+    def acc_width(self) -> int:
+        """Accumulator channels (a padded WH output order has block of them)."""
+        pad = self.side == _lib.HQ_INT_WH and self.block > self.d_out
+        return self.block if pad else self.d_out
+
+    @property
+    def out_width(self) -> int:
+        """Output codes per token (a padded post order writes post_block)."""
+        return self.post_block if self.post_block > self.d_out else self.d_out
+
     def __post_init__(self):
         raw = _lib.HqIntDesc(self.d_in, self.d_out, self.block, self.w_dtype, self.side,
                              self.in_block, self.act, self.post_block)
@@ -429,12 +446,13 @@ def int_prepare(desc: IntDesc, weight: torch.Tensor, bias: Optional[torch.Tensor
 def int_linear(desc: IntDesc, prepared: torch.Tensor, x_codes: torch.Tensor,
                out: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """int8 output codes [T, d_out] of the layer for int8 input codes [T, d_in]."""
+    """int8 output codes [T, out_width] of the layer for int8 input codes
+    [T, x_width]."""
     T = x_codes.shape[0]
-    _need(x_codes, "x_codes", torch.int8, (T, desc.d_in))
-    y = out if out is not None else torch.empty(T, desc.d_out, dtype=torch.int8,
+    _need(x_codes, "x_codes", torch.int8, (T, desc.x_width))
+    y = out if out is not None else torch.empty(T, desc.out_width, dtype=torch.int8,
                                                 device=x_codes.device)
-    _need(y, "out", torch.int8, (T, desc.d_out))
+    _need(y, "out", torch.int8, (T, desc.out_width))
     nws = int_workspace_bytes(desc, T)
     ws = workspace if workspace is not None else torch.empty(
         max(nws, 1), dtype=torch.uint8, device=x_codes.device)
@@ -444,10 +462,11 @@ def int_linear(desc: IntDesc, prepared: torch.Tensor, x_codes: torch.Tensor,
 
 
 def int_requant(desc: IntDesc, prepared: torch.Tensor, acc: torch.Tensor) -> torch.Tensor:
-    """Requantisation alone: int8 [T, d_out] from int32 products [T, d_out] (no bias)."""
+    """Requantisation alone: int8 [T, out_width] from int32 products
+    [T, acc_width] (no bias)."""
     T = acc.shape[0]
-    _need(acc, "acc", torch.int32, (T, desc.d_out))
-    y = torch.empty(T, desc.d_out, dtype=torch.int8, device=acc.device)
+    _need(acc, "acc", torch.int32, (T, desc.acc_width))
+    y = torch.empty(T, desc.out_width, dtype=torch.int8, device=acc.device)
     check(load().hq_int_requant(desc._ref, _ptr(prepared), _ptr(acc), T, _ptr(y), _stream()))
     return y
 
@@ -455,19 +474,19 @@ def int_requant(desc: IntDesc, prepared: torch.Tensor, acc: torch.Tensor) -> tor
 def int_views(desc: IntDesc, prepared: torch.Tensor) -> dict:
     """Views of the arrays inside an integer-layer prepared blob (for tests)."""
     L = int_layout(desc)
-    npad, d = L.d_out_pad, desc.d_in
+    npad, d, a = L.d_out_pad, desc.x_width, desc.acc_width
 
     def view(off, n, dtype, shape):
         nbytes = n * torch.empty(0, dtype=dtype).element_size()
         return prepared[off:off + nbytes].view(dtype).view(*shape)
 
     return {
-        "w_codes": view(L.w_codes, npad * d, torch.int8, (npad, d))[:desc.d_out],
-        "s_w": view(L.w_scale, npad, torch.float32, (npad,))[:desc.d_out],
-        "b_int": view(L.b_int, npad, torch.int32, (npad,))[:desc.d_out],
-        "mult": view(L.mult, npad, torch.int32, (npad,))[:desc.d_out],
+        "w_codes": view(L.w_codes, npad * d, torch.int8, (npad, d))[:a],
+        "s_w": view(L.w_scale, npad, torch.float32, (npad,))[:a],
+        "b_int": view(L.b_int, npad, torch.int32, (npad,))[:a],
+        "mult": view(L.mult, npad, torch.int32, (npad,))[:a],
         "shift": view(L.shift, 1, torch.int32, (1,)),
-        "wbar": view(L.wbar, desc.d_out * d, torch.float32, (desc.d_out, d)),
+        "wbar": view(L.wbar, a * d, torch.float32, (a, d)),
         "lut": view(L.lut, 256, torch.int8, (256,)),
         "mult_in": view(L.mult_in, 1, torch.int32, (1,)),
         "shift_in": view(L.shift_in, 1, torch.int32, (1,)),

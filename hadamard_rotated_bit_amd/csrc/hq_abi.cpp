@@ -294,6 +294,20 @@ struct IntHeader {
 };
 static_assert(sizeof(IntHeader) <= 256, "header fits in 256 bytes");
 
+// Widths of an integer layer (padded orders, supplement Sec. VII-B): the
+// input codes (a DH layer with in_block above d_in takes in_block of them),
+// the accumulator channels (a WH layer with block above d_out has block of
+// them) and the output codes (post_block above d_out: post_block of them).
+int int_x_width(const hq_int_desc* d) {
+  return d->side == HQ_INT_DH && d->in_block > d->d_in ? d->in_block : d->d_in;
+}
+int int_acc_width(const hq_int_desc* d) {
+  return d->side == HQ_INT_WH && d->block > d->d_out ? d->block : d->d_out;
+}
+int int_out_width(const hq_int_desc* d) {
+  return d->post_block > d->d_out ? d->post_block : d->d_out;
+}
+
 int check_int_desc(const hq_int_desc* d) {
   if (!d) return fail(HQ_ERR_INVALID_ARG, "desc is NULL");
   if (d->d_in <= 0 || d->d_out <= 0)
@@ -303,26 +317,34 @@ int check_int_desc(const hq_int_desc* d) {
     return fail(HQ_ERR_INVALID_ARG, "w_dtype %d is not an hq_dtype", d->w_dtype);
   if (d->side != HQ_INT_WH && d->side != HQ_INT_DH)
     return fail(HQ_ERR_INVALID_ARG, "side must be HQ_INT_WH or HQ_INT_DH (got %d)", d->side);
-  hq::RowGeom g;
-  if (d->d_in % 128 || !hq::row_geometry(d->d_in, &g))
-    return fail(HQ_ERR_UNSUPPORTED,
-                "d_in %d unsupported: need a multiple of 128 up to 2048, of 256 up to 4096, or "
-                "of 512 up to 8192",
-                d->d_in);
-  if (d->d_out % 8)
-    return fail(HQ_ERR_UNSUPPORTED, "d_out must be a multiple of 8 (got %d)", d->d_out);
-  if (!is_pow2(d->block) || d->block > hq::WH_MAX_BLOCK || d->d_out % d->block)
-    return fail(HQ_ERR_UNSUPPORTED, "block %d must be a power of two <= %d dividing d_out %d",
-                d->block, hq::WH_MAX_BLOCK, d->d_out);
   if (d->side == HQ_INT_WH && d->in_block != 1)
     return fail(HQ_ERR_UNSUPPORTED, "a WH layer takes in_block = 1 (got %d)", d->in_block);
-  if (d->side == HQ_INT_DH && (!is_pow2(d->in_block) || d->d_in % d->in_block))
-    return fail(HQ_ERR_UNSUPPORTED, "in_block %d must be a power of two dividing d_in %d",
+  if (d->side == HQ_INT_DH &&
+      (!is_pow2(d->in_block) || (d->d_in % d->in_block && d->in_block < d->d_in)))
+    return fail(HQ_ERR_UNSUPPORTED,
+                "in_block %d must be a power of two dividing d_in %d or above it (padded)",
                 d->in_block, d->d_in);
+  const int xw = int_x_width(d);
+  hq::RowGeom g;
+  if (xw % 128 || !hq::row_geometry(xw, &g))
+    return fail(HQ_ERR_UNSUPPORTED,
+                "input width %d unsupported: need a multiple of 128 up to 2048, of 256 up to "
+                "4096, or of 512 up to 8192",
+                xw);
+  if (d->d_out % 8)
+    return fail(HQ_ERR_UNSUPPORTED, "d_out must be a multiple of 8 (got %d)", d->d_out);
+  if (!is_pow2(d->block) || d->block > hq::WH_MAX_BLOCK ||
+      (d->d_out % d->block && (d->side == HQ_INT_DH || d->block < d->d_out)))
+    return fail(HQ_ERR_UNSUPPORTED,
+                "block %d must be a power of two <= %d dividing d_out %d (or above it for a "
+                "padded WH order)",
+                d->block, hq::WH_MAX_BLOCK, d->d_out);
   if (d->act < HQ_INT_ACT_NONE || d->act > HQ_INT_ACT_GELU)
     return fail(HQ_ERR_INVALID_ARG, "act %d is not an hq_int_act", d->act);
-  if (!is_pow2(d->post_block) || d->post_block > hq::WH_MAX_BLOCK || d->d_out % d->post_block)
-    return fail(HQ_ERR_UNSUPPORTED, "post_block %d must be a power of two <= %d dividing d_out %d",
+  if (!is_pow2(d->post_block) || d->post_block > hq::WH_MAX_BLOCK ||
+      (d->d_out % d->post_block && d->post_block < d->d_out))
+    return fail(HQ_ERR_UNSUPPORTED,
+                "post_block %d must be a power of two <= %d dividing d_out %d or above it",
                 d->post_block, hq::WH_MAX_BLOCK, d->d_out);
   if (d->side == HQ_INT_DH && d->act != HQ_INT_ACT_NONE && d->block != 1)
     return fail(HQ_ERR_UNSUPPORTED,
@@ -332,11 +354,12 @@ int check_int_desc(const hq_int_desc* d) {
 }
 
 void int_layout_of(const hq_int_desc* d, hq_int_layout* L) {
-  const int64_t np = round_up(d->d_out, hq::GEMM_BN);
+  const int64_t np = round_up(int_acc_width(d), hq::GEMM_BN);
+  const size_t xw = size_t(int_x_width(d));
   size_t off = 256;
   L->d_out_pad = np;
   L->w_codes = off;
-  off += align256(size_t(np) * d->d_in);
+  off += align256(size_t(np) * xw);
   L->w_scale = off;
   off += align256(4 * size_t(np));
   L->b_int = off;
@@ -350,7 +373,7 @@ void int_layout_of(const hq_int_desc* d, hq_int_layout* L) {
   L->lut = off;
   off += 256;
   L->wbar = off;
-  off += align256(4 * size_t(d->d_out) * d->d_in);
+  off += align256(4 * size_t(int_acc_width(d)) * xw);
   L->total = off;
 }
 
@@ -361,6 +384,7 @@ hq::IntTransition transition_of(const hq_int_desc* d, const void* prepared) {
   hq::IntTransition tr = {};
   tr.m = d->block;
   tr.post = d->post_block;
+  tr.keep = d->d_out;
   tr.act = d->act == HQ_INT_ACT_SILU || d->act == HQ_INT_ACT_GELU ? 2 : d->act;
   tr.b_int = at<int32_t>(prepared, L.b_int);
   tr.mult = at<int32_t>(prepared, L.mult);
@@ -373,8 +397,8 @@ hq::IntTransition transition_of(const hq_int_desc* d, const void* prepared) {
 
 int run_int_requant(const hq_int_desc* d, const void* prepared, const int32_t* acc, int64_t T,
                     int8_t* y, hipStream_t s) {
-  hipError_t e = hq::launch_int_requant(acc, d->d_out, T, d->d_out, transition_of(d, prepared),
-                                        y, d->d_out, s);
+  const int aw = int_acc_width(d), ow = int_out_width(d);
+  hipError_t e = hq::launch_int_requant(acc, aw, T, aw, ow, transition_of(d, prepared), y, ow, s);
   return e == hipSuccess ? HQ_OK : hip_fail(e, "requantisation kernel launch");
 }
 
@@ -772,7 +796,7 @@ size_t hq_int_workspace_bytes(const hq_int_desc* desc, int64_t T) {
     fail(HQ_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
     return 0;
   }
-  return align256(4 * size_t(T) * desc->d_out);
+  return align256(4 * size_t(T) * int_acc_width(desc));
 }
 
 int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bias, float s_x,
@@ -795,30 +819,40 @@ int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bia
   hq_int_layout L;
   int_layout_of(desc, &L);
   const int64_t np = L.d_out_pad, dout = desc->d_out, din = desc->d_in;
+  const int64_t aw = int_acc_width(desc), xw = int_x_width(desc);
   const bool wh = desc->side == HQ_INT_WH;
   hipError_t e = hipSuccess;
-  if (np > dout)
-    e = hq::launch_fill_u8(at<uint8_t>(prepared, L.w_codes + size_t(dout) * din), 0,
-                           size_t(np - dout) * din, s);
+  if (np > aw)
+    e = hq::launch_fill_u8(at<uint8_t>(prepared, L.w_codes + size_t(aw) * xw), 0,
+                           size_t(np - aw) * xw, s);
   if (e == hipSuccess)
     e = hq::launch_fill_u32(at<uint32_t>(prepared, L.w_scale), 0u, size_t(np), s);
   if (e == hipSuccess) {
     if (wh) {
-      // W-bar = H_out W: butterflies over the output-channel index
-      e = hq::launch_wh_weight(weight, desc->w_dtype == HQ_BF16, int(dout), int(din),
+      // W-bar = H_out [W; 0]: butterflies over the output-channel index
+      e = hq::launch_wh_weight(weight, desc->w_dtype == HQ_BF16, int(dout), int(aw), int(din),
                                desc->block, at<float>(prepared, L.wbar), s);
     } else {
-      // W-bar = W H_in: the row transform along d_in, exported as float
+      // W-bar = [W 0] H_in: the row transform along the (padded) input
+      // channels, exported as float; a padded order first writes [W 0] into
+      // W-bar's place and transforms it there (each row is read whole before
+      // any of it is written)
       hq::RowArgs a = {};
       a.in = weight;
       a.in_bf16 = desc->w_dtype == HQ_BF16;
+      if (xw > din) {
+        e = hq::launch_pad_rows(weight, desc->w_dtype == HQ_BF16, dout, int(din), int(xw),
+                                at<float>(prepared, L.wbar), s);
+        a.in = at<float>(prepared, L.wbar);
+        a.in_bf16 = 0;
+      }
       a.rows = dout;
-      a.d = int(din);
+      a.d = int(xw);
       a.log2b = log2i(desc->in_block);
       a.qmax = 127.0f;
       a.out_xt = at<float>(prepared, L.wbar);
       a.mode = hq::ROW_EXPORT;
-      e = hq::launch_row_transform(a, s);
+      if (e == hipSuccess) e = hq::launch_row_transform(a, s);
     }
   }
   if (e == hipSuccess) {
@@ -826,8 +860,8 @@ int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bia
     hq::RowArgs a = {};
     a.in = at<float>(prepared, L.wbar);
     a.in_bf16 = 0;
-    a.rows = dout;
-    a.d = int(din);
+    a.rows = aw;
+    a.d = int(xw);
     a.log2b = 0;
     a.qmax = 127.0f;
     a.codes = at<uint8_t>(prepared, L.w_codes);
@@ -837,8 +871,8 @@ int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bia
     e = hq::launch_row_transform(a, s);
   }
   if (e == hipSuccess)
-    e = hq::launch_int_constants(bias, at<float>(prepared, L.w_scale), int(dout), int(np),
-                                 desc->block, desc->post_block, desc->act,
+    e = hq::launch_int_constants(bias, int(dout), at<float>(prepared, L.w_scale), int(aw),
+                                 int(np), desc->block, desc->post_block, desc->act,
                                  wh ? desc->block : 1, s_x, s_y, table ? s_z : 0.0f,
                                  table ? s_u : 0.0f, at<int32_t>(prepared, L.b_int),
                                  at<int32_t>(prepared, L.mult), at<int32_t>(prepared, L.shift),
@@ -872,23 +906,24 @@ int hq_int_linear(const hq_int_desc* desc, const void* prepared, const int8_t* x
     return fail(HQ_ERR_INVALID_ARG, "prepared, x_codes, y_codes and workspace must be non-NULL");
   if (misaligned(x_codes) || misaligned(y_codes) || misaligned(workspace) || misaligned(prepared))
     return fail(HQ_ERR_INVALID_ARG, "x_codes, y_codes, workspace and prepared must be 16-byte aligned");
-  const size_t need = align256(4 * size_t(T) * desc->d_out);
+  const int aw = int_acc_width(desc), xw = int_x_width(desc), ow = int_out_width(desc);
+  const size_t need = align256(4 * size_t(T) * aw);
   if (workspace_bytes < need)
     return fail(HQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hq_int_layout L;
   int_layout_of(desc, &L);
-  if (desc->d_out % 256 == 0) {
+  if (desc->d_out % 256 == 0 && aw == desc->d_out && ow == desc->d_out) {
     // whole 256-channel units: GEMM and requantisation in one kernel (the
     // same integers as the two-kernel path below)
     const hipError_t e =
-        hq::launch_int_fused(x_codes, T, desc->d_in, at<int8_t>(prepared, L.w_codes),
+        hq::launch_int_fused(x_codes, T, xw, at<int8_t>(prepared, L.w_codes),
                              desc->d_out, transition_of(desc, prepared), y_codes, s);
     return e == hipSuccess ? HQ_OK : hip_fail(e, "integer-layer kernel launch");
   }
   int32_t* acc = static_cast<int32_t*>(workspace);
-  hipError_t e = hq::launch_gemm(x_codes, T, at<int8_t>(prepared, L.w_codes), desc->d_out,
-                                 desc->d_in, acc, desc->d_out, nullptr, s);
+  hipError_t e = hq::launch_gemm(x_codes, T, at<int8_t>(prepared, L.w_codes), aw, xw, acc, aw,
+                                 nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "GEMM kernel launch");
   return run_int_requant(desc, prepared, acc, T, y_codes, s);
 }

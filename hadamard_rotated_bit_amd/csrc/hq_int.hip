@@ -31,10 +31,11 @@ __device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
 // W-bar = H_m W over blocks of m output channels: block (x, y) of the grid
 // takes columns [32 x, 32 x + 32) of rows [m y, m y + m) into LDS, runs the
 // log2(m) butterfly stages over the row index and writes the rows times
-// 1/sqrt(m) as float32.
+// 1/sqrt(m) as float32. Rows at or past `rows` read as zeros (a padded
+// order: W-bar = H_m [W; 0], supplement Eq. (40) with T_out = P H_m).
 template <typename TW>
-__global__ __launch_bounds__(256) void wh_weight_kernel(const TW* __restrict__ w, int d_in,
-                                                        int m, float inv_sqrt_m,
+__global__ __launch_bounds__(256) void wh_weight_kernel(const TW* __restrict__ w, int rows,
+                                                        int d_in, int m, float inv_sqrt_m,
                                                         float* __restrict__ wbar) {
   constexpr int CW = 32, LD = CW + 1;
   __shared__ float tile[WH_MAX_BLOCK * LD];
@@ -43,7 +44,8 @@ __global__ __launch_bounds__(256) void wh_weight_kernel(const TW* __restrict__ w
   const int tc = threadIdx.x & (CW - 1), tr = threadIdx.x / CW;   // 8 row lanes
   const int col = col0 + tc;
   for (int r = tr; r < m; r += 8)
-    tile[r * LD + tc] = col < d_in ? to_f32(w[(row0 + r) * d_in + col]) : 0.0f;
+    tile[r * LD + tc] =
+        (col < d_in && row0 + r < rows) ? to_f32(w[(row0 + r) * d_in + col]) : 0.0f;
   __syncthreads();
   for (int h = 1; h < m; h <<= 1) {
     // m / 2 butterflies per column, (i, i + h) with bit h of i clear
@@ -57,6 +59,20 @@ __global__ __launch_bounds__(256) void wh_weight_kernel(const TW* __restrict__ w
   }
   if (col < d_in)
     for (int r = tr; r < m; r += 8) wbar[(row0 + r) * d_in + col] = tile[r * LD + tc] * inv_sqrt_m;
+}
+
+// out [rows, width] f32 = [w 0]: each row's d_in weights, then zeros up to
+// width (a padded input order: W-bar = [W 0] H_m, supplement Eq. (39)).
+template <typename TW>
+__global__ __launch_bounds__(256) void pad_rows_kernel(const TW* __restrict__ w, int64_t rows,
+                                                       int d_in, int width,
+                                                       float* __restrict__ out) {
+  const int64_t n = rows * width;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / width;
+    const int c = int(i - r * width);
+    out[i] = c < d_in ? to_f32(w[r * d_in + c]) : 0.0f;
+  }
 }
 
 // Multiplier bound for transforms whose orders multiply to `orders` (a power
@@ -90,11 +106,13 @@ __device__ __forceinline__ double int_phi(int act, double x) {
 // rho). Identity / ReLU: rho = s_A / (sqrt(m post) s_y), bound for m post.
 // SiLU / GELU: rho = s_A / (sqrt(m) s_z), bound for m; then the table over
 // z = -127 .. 127 (lut[z + 127] = clamp(round(phi(s_z z) / s_u)), lut[255] =
-// 0) and M_in = round(2^n_in s_u / (sqrt(post) s_y)). Rows past d_out get
-// zeros.
+// 0) and M_in = round(2^n_in s_u / (sqrt(post) s_y)). d_out counts the
+// accumulator channels (a padded WH order: m of them), n_bias the bias
+// entries (the bias reads as zero past them); rows past d_out get zeros.
 __global__ __launch_bounds__(256) void int_constants_kernel(
-    const float* __restrict__ bias, const float* __restrict__ s_w, int d_out, int d_out_pad,
-    int m, int post, int act, int bb_order, double s_x, double s_y, double s_z, double s_u,
+    const float* __restrict__ bias, int n_bias, const float* __restrict__ s_w, int d_out,
+    int d_out_pad, int m, int post, int act, int bb_order, double s_x, double s_y, double s_z,
+    double s_u,
     int32_t* __restrict__ b_int, int32_t* __restrict__ mult, int32_t* __restrict__ shift,
     int8_t* __restrict__ lut, int32_t* __restrict__ mult_in, int32_t* __restrict__ shift_in) {
   __shared__ double red[256];
@@ -145,7 +163,7 @@ __global__ __launch_bounds__(256) void int_constants_kernel(
       if (bias && s_a > 0.0) {
         const int base = (c / bb_order) * bb_order, ci = c - base;
         double bb = 0.0;
-        for (int k = 0; k < bb_order; ++k) {
+        for (int k = 0; k < bb_order && base + k < n_bias; ++k) {
           const double v = double(bias[base + k]);
           bb += (__popc(ci & k) & 1) ? -v : v;
         }
@@ -237,15 +255,21 @@ __device__ __forceinline__ uint4 int_unit_codes(const double (&u)[16], double sc
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// The transition on one unit, u = M . (acc + b_int) on entry: H~_m, the
-// activation, H~_post, then the final rounding as 16 int8 codes. ACT 0:
+// The transition on one unit, u = M . (acc + b_int) on entry (channels c0 ..
+// c0 + 15 of the lane): H~_m, the projection onto the first `keep` channels,
+// the activation, H~_post (channels past `keep` are the zero padding of a
+// padded post order), then the final rounding as 16 int8 codes. ACT 0:
 // identity, 1: ReLU (both with the one shift), 2: the table (SiLU, GELU):
 // z = clamp(round(v / 2^n_out)), u = M_in lut[z + 127], final shift n_in.
 template <int ACT>
-__device__ __forceinline__ uint4 int_unit_transition(double (&u)[16], int lane,
+__device__ __forceinline__ uint4 int_unit_transition(double (&u)[16], int lane, int c0,
                                                      const IntTransition& tr) {
   const double s1 = ldexp(1.0, -*tr.shift);
   int_unit_transform(u, lane, tr.m);
+  // a padded WH order keeps its first `keep` channels (the projection P)
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (c0 + k >= tr.keep) u[k] = 0.0;
   if constexpr (ACT == 1) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) u[k] = fmax(u[k], 0.0);
@@ -254,14 +278,15 @@ __device__ __forceinline__ uint4 int_unit_transition(double (&u)[16], int lane,
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const double z = fmin(fmax(rint(u[k] * s1), -127.0), 127.0);
-      u[k] = double(tr.lut[int(z) + 127]) * m_in;
+      u[k] = c0 + k < tr.keep ? double(tr.lut[int(z) + 127]) * m_in : 0.0;
     }
   }
   int_unit_transform(u, lane, tr.post);
   return int_unit_codes(u, ACT == 2 ? ldexp(1.0, -*tr.shift_in) : s1);
 }
 
-// Requantisation of int32 products acc [T, ldc] (without bias). Each group of
+// Requantisation of int32 products acc [T, ldc] (acc_w channels, without
+// bias) into y [T, ldy] (out_w channels). Each group of
 // 16 lanes takes one (token, 256-channel chunk) unit, lane l of the group
 // holding channels 16 l .. 16 l + 15 of the chunk. u = M (acc + b_int), the
 // unnormalised Sylvester butterflies over blocks of m channels (channel bits
@@ -271,7 +296,7 @@ __device__ __forceinline__ uint4 int_unit_transition(double (&u)[16], int lane,
 // and invalid channels, m dividing d_out).
 template <int ACT>
 __global__ __launch_bounds__(256) void int_requant_kernel(
-    const int32_t* __restrict__ acc, int64_t ldc, int64_t T, int d_out, int chunks,
+    const int32_t* __restrict__ acc, int64_t ldc, int64_t T, int acc_w, int out_w, int chunks,
     IntTransition tr, int8_t* __restrict__ y, int64_t ldy) {
   const int lane = threadIdx.x & 15;
   const int64_t unit = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
@@ -283,7 +308,7 @@ __global__ __launch_bounds__(256) void int_requant_kernel(
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int c = c0 + 4 * q;
-    if (c < d_out) {   // d_out % 8 == 0: whole runs of 4 are in or out
+    if (c < acc_w) {   // acc_w % 8 == 0: whole runs of 4 are in or out
       const int4 a = *reinterpret_cast<const int4*>(acc + row * ldc + c);
       const int4 b = *reinterpret_cast<const int4*>(tr.b_int + c);
       const int4 mm = *reinterpret_cast<const int4*>(tr.mult + c);
@@ -295,12 +320,12 @@ __global__ __launch_bounds__(256) void int_requant_kernel(
       u[4 * q + 0] = u[4 * q + 1] = u[4 * q + 2] = u[4 * q + 3] = 0.0;
     }
   }
-  const uint4 w = int_unit_transition<ACT>(u, lane, tr);
-  if (!live || c0 >= d_out) return;
+  const uint4 w = int_unit_transition<ACT>(u, lane, c0, tr);
+  if (!live || c0 >= out_w) return;
   int8_t* dst = y + row * ldy + c0;
-  if (c0 + 16 <= d_out) {
+  if (c0 + 16 <= out_w) {
     *reinterpret_cast<uint4*>(dst) = w;
-  } else {   // the last 8 channels of d_out
+  } else {   // the last 8 channels of out_w
     *reinterpret_cast<uint2*>(dst) = make_uint2(w.x, w.y);
   }
 }
@@ -368,49 +393,70 @@ __global__ __launch_bounds__(512) void int_fused_kernel(
       u[4 * q + 2] = double(av.z + bv.z) * double(mv.z);
       u[4 * q + 3] = double(av.w + bv.w) * double(mv.w);
     }
-    const uint4 codes = int_unit_transition<ACT>(u, l16, tr);
+    const uint4 codes = int_unit_transition<ACT>(u, l16, c_blk + cl, tr);
     if (row0 + r < T) *reinterpret_cast<uint4*>(y + (row0 + r) * d_out + c_blk + cl) = codes;
   }
 }
 
-hipError_t launch_wh_weight(const void* w, int w_bf16, int d_out, int d_in, int m, float* wbar,
-                            hipStream_t s) {
-  if (m < 1 || m > WH_MAX_BLOCK || (m & (m - 1)) || d_out % m) return hipErrorInvalidValue;
-  dim3 grid{unsigned((d_in + 31) / 32), unsigned(d_out / m)};
+hipError_t launch_wh_weight(const void* w, int w_bf16, int d_out, int acc_rows, int d_in, int m,
+                            float* wbar, hipStream_t s) {
+  if (m < 1 || m > WH_MAX_BLOCK || (m & (m - 1)) || acc_rows % m || acc_rows < d_out)
+    return hipErrorInvalidValue;
+  dim3 grid{unsigned((d_in + 31) / 32), unsigned(acc_rows / m)};
   const float ism = 1.0f / sqrtf(float(m));
   if (w_bf16)
     hipLaunchKernelGGL(wh_weight_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(w), d_in, m, ism, wbar);
+                       static_cast<const uint16_t*>(w), d_out, d_in, m, ism, wbar);
   else
     hipLaunchKernelGGL(wh_weight_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(w), d_in, m, ism, wbar);
+                       static_cast<const float*>(w), d_out, d_in, m, ism, wbar);
   return hipGetLastError();
 }
 
-hipError_t launch_int_constants(const float* bias, const float* s_w, int d_out, int d_out_pad,
-                                int m, int post, int act, int bias_block, float s_x, float s_y,
-                                float s_z, float s_u, int32_t* b_int, int32_t* mult,
-                                int32_t* shift, int8_t* lut, int32_t* mult_in,
+hipError_t launch_pad_rows(const void* w, int w_bf16, int64_t rows, int d_in, int width,
+                           float* out, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (width < d_in) return hipErrorInvalidValue;
+  const int64_t n = rows * width;
+  const unsigned blocks = unsigned(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
+  if (w_bf16)
+    hipLaunchKernelGGL(pad_rows_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(w), rows, d_in, width, out);
+  else
+    hipLaunchKernelGGL(pad_rows_kernel<float>, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const float*>(w), rows, d_in, width, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_int_constants(const float* bias, int n_bias, const float* s_w, int acc_w,
+                                int d_out_pad, int m, int post, int act, int bias_block,
+                                float s_x, float s_y, float s_z, float s_u, int32_t* b_int,
+                                int32_t* mult, int32_t* shift, int8_t* lut, int32_t* mult_in,
                                 int32_t* shift_in, hipStream_t s) {
-  if (bias_block < 1 || (bias_block & (bias_block - 1)) || d_out % bias_block || act < 0 ||
-      act > 3 || post < 1 || (post & (post - 1)) || post > WH_MAX_BLOCK)
+  if (bias_block < 1 || (bias_block & (bias_block - 1)) || acc_w % bias_block || act < 0 ||
+      act > 3 || post < 1 || (post & (post - 1)) || post > WH_MAX_BLOCK || n_bias > acc_w)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(int_constants_kernel, dim3(1), dim3(256), 0, s, bias, s_w, d_out, d_out_pad,
-                     m, post, act, bias_block, double(s_x), double(s_y), double(s_z),
+  hipLaunchKernelGGL(int_constants_kernel, dim3(1), dim3(256), 0, s, bias, n_bias, s_w, acc_w,
+                     d_out_pad, m, post, act, bias_block, double(s_x), double(s_y), double(s_z),
                      double(s_u), b_int, mult, shift, lut, mult_in, shift_in);
   return hipGetLastError();
 }
 
-static bool transition_ok(const IntTransition& tr, int d_out) {
+// acc_w accumulator channels (whole blocks of m), keep <= acc_w of them
+// after the projection, out_w output channels (whole blocks of post, at least
+// keep); every width a multiple of 8.
+static bool transition_ok(const IntTransition& tr, int acc_w, int out_w) {
   auto pow2 = [](int v) { return v >= 1 && v <= WH_MAX_BLOCK && !(v & (v - 1)); };
-  return pow2(tr.m) && pow2(tr.post) && d_out % tr.m == 0 && d_out % tr.post == 0 &&
-         tr.act >= 0 && tr.act <= 3;
+  return pow2(tr.m) && pow2(tr.post) && acc_w % tr.m == 0 && out_w % tr.post == 0 &&
+         tr.keep >= 1 && tr.keep <= acc_w && tr.keep <= out_w && acc_w % 8 == 0 &&
+         out_w % 8 == 0 && tr.act >= 0 && tr.act <= 3;
 }
 
 hipError_t launch_int_fused(const int8_t* x, int64_t T, int d_in, const int8_t* w, int d_out,
                             const IntTransition& tr, int8_t* y, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (d_out % 256 || d_in % 32 || !transition_ok(tr, d_out)) return hipErrorInvalidValue;
+  if (d_out % 256 || d_in % 32 || tr.keep != d_out || !transition_ok(tr, d_out, d_out))
+    return hipErrorInvalidValue;
   const dim3 grid{unsigned((T + IF_ROWS - 1) / IF_ROWS), unsigned(d_out / 256)};
   if (tr.act == 0)
     hipLaunchKernelGGL(int_fused_kernel<0>, grid, dim3(512), 0, s, x, T, d_in, w, d_out, tr, y);
@@ -421,22 +467,22 @@ hipError_t launch_int_fused(const int8_t* x, int64_t T, int d_in, const int8_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_int_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_out,
+hipError_t launch_int_requant(const int32_t* acc, int64_t ldc, int64_t T, int acc_w, int out_w,
                               const IntTransition& tr, int8_t* y, int64_t ldy, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (d_out % 8 || !transition_ok(tr, d_out)) return hipErrorInvalidValue;
-  const int chunks = (d_out + 255) / 256;
+  if (!transition_ok(tr, acc_w, out_w) || ldc < acc_w || ldy < out_w) return hipErrorInvalidValue;
+  const int chunks = ((acc_w > out_w ? acc_w : out_w) + 255) / 256;
   const int64_t units = T * chunks;   // 16 lanes each, 16 per block
   const dim3 grid{unsigned((units + 15) / 16)};
   if (tr.act == 0)
-    hipLaunchKernelGGL(int_requant_kernel<0>, grid, dim3(256), 0, s, acc, ldc, T, d_out, chunks,
-                       tr, y, ldy);
+    hipLaunchKernelGGL(int_requant_kernel<0>, grid, dim3(256), 0, s, acc, ldc, T, acc_w, out_w,
+                       chunks, tr, y, ldy);
   else if (tr.act == 1)
-    hipLaunchKernelGGL(int_requant_kernel<1>, grid, dim3(256), 0, s, acc, ldc, T, d_out, chunks,
-                       tr, y, ldy);
+    hipLaunchKernelGGL(int_requant_kernel<1>, grid, dim3(256), 0, s, acc, ldc, T, acc_w, out_w,
+                       chunks, tr, y, ldy);
   else
-    hipLaunchKernelGGL(int_requant_kernel<2>, grid, dim3(256), 0, s, acc, ldc, T, d_out, chunks,
-                       tr, y, ldy);
+    hipLaunchKernelGGL(int_requant_kernel<2>, grid, dim3(256), 0, s, acc, ldc, T, acc_w, out_w,
+                       chunks, tr, y, ldy);
   return hipGetLastError();
 }
 

@@ -134,15 +134,20 @@ constexpr int WH_MAX_BLOCK = 256;       // largest output-side Hadamard order
 constexpr int WH_SHIFT_MAX = 48;        // largest shared requantisation shift
 constexpr int WH_MULT_MAX = 32767;      // multipliers fit a positive 16-bit integer
 constexpr int WH_BIAS_MAX = 1 << 27;    // bias codes saturate here (exact float64 requant)
-// wbar [d_out, d_in] f32 = H_m (blocks of m output channels) . weight.
-hipError_t launch_wh_weight(const void* w, int w_bf16, int d_out, int d_in, int m, float* wbar,
-                            hipStream_t s);
+// wbar [acc_rows, d_in] f32 = H_m (blocks of m output channels) . [weight; 0]
+// (weight [d_out, d_in]; rows d_out .. acc_rows - 1 of a padded order are zero).
+hipError_t launch_wh_weight(const void* w, int w_bf16, int d_out, int acc_rows, int d_in, int m,
+                            float* wbar, hipStream_t s);
+// out [rows, width] f32 = [w 0] (w [rows, d_in], zeros in columns d_in ..).
+hipError_t launch_pad_rows(const void* w, int w_bf16, int64_t rows, int d_in, int width,
+                           float* out, hipStream_t s);
 // The transition after an integer layer: the transform before the
 // activation (m), the activation (hq_int_act), the transform after it (post),
 // and the prepared constants (bias codes, per-channel multipliers, the shift;
 // for SiLU/GELU also the table over z + 127, M_in and n_in).
 struct IntTransition {
   int m, post, act;
+  int keep;   // channels kept after H~_m (the layer's d_out)
   const int32_t* b_int;
   const int32_t* mult;
   const int32_t* shift;
@@ -155,19 +160,19 @@ struct IntTransition {
 // rho = s_x s_w / (sqrt(m post) s_y). SiLU / GELU: rho = s_x s_w / (sqrt(m)
 // s_z), the table lut [256] (entry z + 127 = clamp(round(phi(s_z z) / s_u));
 // entry 255 = 0), M_in and n_in from s_u / (sqrt(post) s_y).
-hipError_t launch_int_constants(const float* bias, const float* s_w, int d_out, int d_out_pad,
-                                int m, int post, int act, int bias_block, float s_x, float s_y,
-                                float s_z, float s_u, int32_t* b_int, int32_t* mult,
-                                int32_t* shift, int8_t* lut, int32_t* mult_in,
+hipError_t launch_int_constants(const float* bias, int n_bias, const float* s_w, int acc_w,
+                                int d_out_pad, int m, int post, int act, int bias_block,
+                                float s_x, float s_y, float s_z, float s_u, int32_t* b_int,
+                                int32_t* mult, int32_t* shift, int8_t* lut, int32_t* mult_in,
                                 int32_t* shift_in, hipStream_t s);
 // The integer GEMM and the transition's requantisation in one kernel
 // (d_out % 256 == 0): y [T, d_out] from x [T, d_in] int8 and w [>= d_out,
 // d_in] int8; the int32 products stay on the chip.
 hipError_t launch_int_fused(const int8_t* x, int64_t T, int d_in, const int8_t* w, int d_out,
                             const IntTransition& tr, int8_t* y, hipStream_t s);
-// y [T, ldy] int8 from acc [T, ldc] (without the bias codes): the
-// transition's requantisation.
-hipError_t launch_int_requant(const int32_t* acc, int64_t ldc, int64_t T, int d_out,
+// y [T, ldy] int8 (out_w channels) from acc [T, ldc] (acc_w channels, without
+// the bias codes): the transition's requantisation.
+hipError_t launch_int_requant(const int32_t* acc, int64_t ldc, int64_t T, int acc_w, int out_w,
                               const IntTransition& tr, int8_t* y, int64_t ldy, hipStream_t s);
 
 }  // namespace hq

@@ -360,6 +360,18 @@ int hq_gemm_dequant(const hq_desc* desc, const void* prepared, const void* codes
  * be 1 and the next layer's H_in goes in p; with phi = identity the two
  * positions give the same integers.
  *
+ * Padded orders (supplement Sec. VII-B Eq. (35)-(41); Sylvester orders only):
+ * an order above the channel count pads those channels with zeros, T = P H
+ * with P = [I 0]. A WH layer with block m > d_out holds W-bar = H_m [W; 0]
+ * and b-bar = [b 0] H_m (m accumulator channels) and keeps the first d_out
+ * channels after H~_m; a DH layer with in_block > d_in holds W-bar =
+ * [W 0] H_in and takes in_block input codes per token (the previous layer's
+ * padded output); post_block p > d_out pads the activation's d_out channels
+ * to p before H~_p, so the layer writes p output codes per token. Widths:
+ * input codes x_w = in_block if DH and in_block > d_in, else d_in;
+ * accumulators a_w = block if WH and block > d_out, else d_out; output codes
+ * o_w = post_block if post_block > d_out, else d_out.
+ *
  * H~_m: the +-1 Sylvester matrix of order m, block-diagonal over d_out / m
  * blocks of output channels (additions and subtractions only). It is Table
  * I's output-side conversion: for a WH layer followed by a WH layer it
@@ -386,35 +398,39 @@ typedef enum {
 } hq_int_act;
 
 typedef struct {
-  int32_t d_in;     /* input channels: same rule as hq_desc.d_in                  */
+  int32_t d_in;     /* input channels of the weight; the input width x_w follows
+                       hq_desc.d_in's rule                                        */
   int32_t d_out;    /* output channels: multiple of 8                             */
   int32_t block;    /* m: output-side transform order, power of two <= 256
-                       dividing d_out (for WH also the order of H_out)            */
+                       dividing d_out (for WH also the order of H_out, which may
+                       exceed d_out: a padded order)                              */
   int32_t w_dtype;  /* hq_dtype of weight                                         */
   int32_t side;     /* hq_int_side                                                */
-  int32_t in_block; /* DH: order of H_in, a power of two dividing d_in; WH: 1     */
+  int32_t in_block; /* DH: order of H_in, a power of two dividing d_in or above it
+                       (padded); WH: 1                                            */
   int32_t act;      /* hq_int_act between this layer and the next                 */
   int32_t post_block; /* p: transform after the activation (the next layer's H_in
-                       order), power of two <= 256 dividing d_out; 1 = none       */
+                       order), power of two <= 256 dividing d_out or above it
+                       (padded); 1 = none                                         */
 } hq_int_desc;
 
 /* Byte offsets of the arrays in an integer-layer prepared blob (256-byte aligned). */
 typedef struct {
   size_t total;
-  size_t w_codes;   /* int8  [d_out_pad, d_in]  codes of W-bar (padding rows 0)  */
+  size_t w_codes;   /* int8  [d_out_pad, x_w]   codes of W-bar (padding rows 0)  */
   size_t w_scale;   /* f32   [d_out_pad]        s_w                             */
   size_t b_int;     /* int32 [d_out_pad]        bias codes                      */
   size_t mult;      /* int32 [d_out_pad]        multipliers M                   */
   size_t shift;     /* int32 [1]                shared shift n                  */
-  size_t wbar;      /* f32   [d_out, d_in]      W-bar (written by the prepare)  */
-  int64_t d_out_pad;
+  size_t wbar;      /* f32   [a_w, x_w]         W-bar (written by the prepare)  */
+  int64_t d_out_pad; /* a_w rounded up to the GEMM tile                         */
   size_t lut;       /* int8  [256]              SiLU/GELU table, entry z + 127  */
   size_t mult_in;   /* int32 [1]                M_in (SiLU/GELU)                */
   size_t shift_in;  /* int32 [1]                n_in (SiLU/GELU)                */
 } hq_int_layout;
 
 /* Bookkeeping, host-only: validation, blob size and layout, workspace of
- * hq_int_linear (int32 products [T, d_out]). */
+ * hq_int_linear (int32 products [T, a_w]). */
 int hq_int_validate(const hq_int_desc* desc);
 size_t hq_int_prepared_bytes(const hq_int_desc* desc);
 int hq_int_prepared_layout_of(const hq_int_desc* desc, hq_int_layout* out);
@@ -433,7 +449,7 @@ int hq_int_prepare(const hq_int_desc* desc, const void* weight, const float* bia
 
 /* The integer-only hot path (HaTQ Eq. (4), then the requantisation of
  * Eq. (19)-(22), or of supplement Eq. (45)-(49) for SiLU/GELU): y_codes int8
- * [T, d_out] from x_codes int8 [T, d_in] (codes in
+ * [T, o_w] from x_codes int8 [T, x_w] (codes in
  * [-127, 127], row-major, in the layer's input basis): the int8 MFMA product
  * into the workspace, then hq_int_requant's kernel. T = 0 is a no-op. */
 int hq_int_linear(const hq_int_desc* desc, const void* prepared, const int8_t* x_codes,
@@ -441,8 +457,8 @@ int hq_int_linear(const hq_int_desc* desc, const void* prepared, const int8_t* x
                   void* stream);
 
 /* Requantisation alone (HaTQ Eq. (19)-(22); supplement Eq. (45)-(49)):
- * y_codes int8 [T, d_out] from the int32 products
- * acc [T, d_out] (x_int . w-bar_int^T, WITHOUT the bias codes, which this
+ * y_codes int8 [T, o_w] from the int32 products
+ * acc [T, a_w] (x_int . w-bar_int^T, WITHOUT the bias codes, which this
  * stage adds). |acc| <= 2^27 (as every product of int8 codes over d_in <= 8192
  * is); larger values are outside the exact range of the kernel. */
 int hq_int_requant(const hq_int_desc* desc, const void* prepared, const int32_t* acc, int64_t T,

@@ -234,7 +234,9 @@ def _il(**kw):
     (dict(d_out=260), -2), (dict(block=3), -2), (dict(block=512, d_out=512), -2),
     (dict(block=128, d_out=200), -2), (dict(block=0), -2), (dict(side=2), -1),
     (dict(side=-1), -1), (dict(in_block=2), -2), (dict(side=1, in_block=3), -2),
-    (dict(side=1, in_block=512), -2), (dict(side=1, in_block=0), -2),
+    (dict(side=1, in_block=16384), -2), (dict(side=1, in_block=0), -2),
+    (dict(side=1, in_block=256, block=512, d_out=200), -2),   # DH pads through post_block
+    (dict(block=512, d_out=200), -2), (dict(side=1, d_in=100, in_block=64), -2),
     (dict(act=4), -1), (dict(act=-1), -1), (dict(post_block=3), -2), (dict(post_block=0), -2),
     (dict(post_block=512, d_out=512), -2), (dict(post_block=64, d_out=96, block=1), -2),
     (dict(side=1, in_block=256, act=1, block=16), -2),
@@ -250,9 +252,30 @@ def test_int_validation_rejects(kw, status):
 @pytest.mark.parametrize("kw", [dict(), dict(side=1, in_block=256), dict(side=1, in_block=1, block=1),
                                 dict(side=1, in_block=32, block=8, d_out=136),
                                 dict(act=1, post_block=256), dict(act=3, post_block=8, block=16),
-                                dict(side=1, in_block=256, act=2, block=1, post_block=64)])
+                                dict(side=1, in_block=256, act=2, block=1, post_block=64),
+                                dict(side=1, in_block=512), dict(side=1, d_in=200, in_block=256),
+                                dict(block=256, d_out=200), dict(post_block=256, d_out=200),
+                                dict(block=256, d_out=200, act=3, post_block=256)])
 def test_int_validation_accepts(kw):
     assert lib.hq_int_validate(_il(**kw)._ref) == 0
+
+
+def test_int_padded_layout_and_workspace():
+    # a WH layer with a padded output order (200 channels, H_256) holds 256
+    # accumulator rows; a DH layer with a padded input order (200 -> 256)
+    # takes 256 input codes per token
+    d = _il(d_in=384, d_out=200, block=256)
+    L = _lib.HqIntLayout()
+    assert lib.hq_int_prepared_layout_of(d._ref, ctypes.byref(L)) == 0
+    assert L.d_out_pad == 256 and L.w_scale - L.w_codes >= 256 * 384
+    assert L.total - L.wbar >= 4 * 256 * 384
+    assert lib.hq_int_workspace_bytes(d._ref, 10) == 4 * 10 * 256 + (256 - (4 * 10 * 256) % 256) % 256
+    p = _il(d_in=200, d_out=64, block=1, side=1, in_block=256)
+    assert lib.hq_int_prepared_layout_of(p._ref, ctypes.byref(L)) == 0
+    assert L.w_scale - L.w_codes >= 256 * L.d_out_pad
+    assert (p.x_width, p.acc_width, p.out_width) == (256, 64, 64)
+    q = _il(d_out=200, block=256, post_block=256, act=1)
+    assert (q.x_width, q.acc_width, q.out_width) == (256, 256, 256)
 
 
 def test_int_layout_and_workspace():

@@ -53,11 +53,15 @@ class IntCase:
         # output in the basis the int8 output codes stand for: the activation
         # of the layer's output (in the original basis; a DH layer without an
         # activation may put the next layer's H_in in m), then H_post
-        self.x_in = self.x if side == hq.HQ_INT_WH else O.rotate(self.x, in_block)
+        # (padded orders: a DH input of in_block > d_in channels is [X 0] H_in,
+        # and a post order above d_out pads the activation with zeros)
+        self.desc = hq.IntDesc(w.d_in, w.d_out, m, DT[w.dtype], side, in_block, act, post)
+        xw = self.desc.x_width
+        self.x_in = self.x if side == hq.HQ_INT_WH else O.rotate(_pad_cols(self.x, xw), in_block)
         y = np.asarray(self.x, dtype=np.float64) @ np.asarray(self.weight, dtype=np.float64).T + \
             self.bias
         y_pre = y if side == hq.HQ_INT_WH else O.rotate(y, m)
-        self.y_ref = O.rotate(PHI[act](y_pre), post)
+        self.y_ref = O.rotate(_pad_cols(PHI[act](y_pre), self.desc.out_width), post)
         self.s_x = float(np.float32(np.abs(self.x_in).max() / 127.0)) if T else 1.0
         s_y = np.abs(self.y_ref).max() / 127.0 if T else 1.0
         self.s_y = float(np.float32(s_y * s_y_factor))
@@ -66,7 +70,6 @@ class IntCase:
         self.s_u = float(np.float32(np.abs(PHI[act](y_pre)).max() / 127.0)) if table and T else 0.0
         if table and not T:
             self.s_z = self.s_u = 1.0
-        self.desc = hq.IntDesc(w.d_in, w.d_out, m, DT[w.dtype], side, in_block, act, post)
         self.xi = O.quantize_static(self.x_in, self.s_x)
         self.ora = O.int_prepare(self.weight, self.bias, self.s_x, self.s_y, m, side=side,
                                  in_block=in_block, act=act, post_block=post, s_z=self.s_z,
@@ -83,7 +86,16 @@ class IntCase:
                 "block": self.m, "s_w": to_np(v["s_w"]).astype(np.float64),
                 "wbar": to_np(v["wbar"]).astype(np.float64), "act": self.act,
                 "post_block": self.post, "lut": to_np(v["lut"]).astype(np.int64),
-                "mult_in": int(to_np(v["mult_in"])[0]), "shift_in": int(to_np(v["shift_in"])[0])}
+                "mult_in": int(to_np(v["mult_in"])[0]), "shift_in": int(to_np(v["shift_in"])[0]),
+                "d_out": self.w.d_out}
+
+
+def _pad_cols(a, width):
+    """a with zero columns appended up to `width` (a padded order's P^T)."""
+    a = np.asarray(a, dtype=np.float64)
+    if a.shape[1] >= width:
+        return a
+    return np.concatenate([a, np.zeros((a.shape[0], width - a.shape[1]))], axis=1)
 
 
 def _half_integer_ties(t, d, rel=4e-6):
@@ -416,4 +428,81 @@ def test_wh_gelu_dh_two_layer_chain():
     assert np.array_equal(y2, q2)
     sq = O.sqnr_db(y2f / s2, y2.astype(np.float64))
     print(f"two-layer integer MLP (WH + GELU -> DH): output SQNR {sq:.2f} dB")
+    assert sq > 12
+
+
+# ---- padded orders (supplement Sec. VII-B Eq. (35)-(41), Sylvester orders)
+
+@pytest.mark.parametrize("act,post", [(NONE, 1), (RELU, 256), (GELU, 256), (SILU, 1)])
+def test_padded_wh_output(act, post):
+    # 200 outputs under H_256: 256 accumulator channels, the first 200 kept
+    w = WL.custom(970, 130, 256, 200, dtype="bf16", x_dist="laplace", n_outliers=3,
+                  outlier=20.0, w_std=0.05)
+    c = IntCase(w, 130, 256, act=act, post=post)
+    assert c.desc.acc_width == 256 and c.desc.out_width == max(post, 200)
+    check_constants(c)
+    y = check_outputs(c, hq.int_linear(c.desc, c.prep, c.X))
+    assert y.shape == (130, c.desc.out_width)
+    assert O.sqnr_db(c.y_ref / c.s_y, y.astype(np.float64)) > 12
+
+
+@pytest.mark.parametrize("d_in,k,d_out,act,post", [(200, 256, 64, NONE, 1), (200, 256, 120, RELU, 128),
+                                                  (640, 1024, 256, GELU, 1)])
+def test_padded_dh_input(d_in, k, d_out, act, post):
+    # the DH input of d_in channels padded to H_k (the previous layer's padded
+    # output); the second case also pads its own output for the next DH layer,
+    # the third runs the fused kernel (d_out 256) on a padded input
+    w = WL.custom(980 + d_in, 77, d_in, d_out, dtype="f32", x_dist="laplace", n_outliers=3,
+                  outlier=20.0, w_std=0.05)
+    c = IntCase(w, 77, 1, side=DH, in_block=k, act=act, post=post)
+    assert c.desc.x_width == k
+    check_constants(c)
+    y = check_outputs(c, hq.int_linear(c.desc, c.prep, c.X))
+    assert y.shape == (77, c.desc.out_width)
+
+
+def test_padded_requant_stage_bit_exact():
+    c = IntCase(WL.custom(990, 4, 256, 200, dtype="f32", x_dist="laplace"), 4, 256, act=RELU,
+                post=256)
+    g = c.gpu_constants()
+    rng = np.random.default_rng(29)
+    acc = rng.integers(-2 ** 27, 2 ** 27, (129, 256), dtype=np.int64)
+    acc[:2] = 0
+    y = to_np(hq.int_requant(c.desc, c.prep, torch.from_numpy(acc.astype(np.int32)).cuda()))
+    u = (acc + g["b_int"][None, :]) * g["mult"][None, :]
+    v = np.maximum(O.unnormalised_transform(u, 256)[:, :200], 0)
+    v = np.concatenate([v, np.zeros((129, 56), np.int64)], axis=1)
+    ref = np.clip(O.round_half_even_shift(O.unnormalised_transform(v, 256), g["shift"]), -127, 127)
+    assert y.shape == (129, 256) and np.array_equal(y.astype(np.int64), ref)
+
+
+def test_padded_wh_relu_dh_chain():
+    # Table I, WH-to-DH across padded orders: a WH layer (200 outputs under
+    # H_256) with ReLU hands 256 codes in the next layer's padded H_256 basis
+    # to a DH layer whose 200 input channels are padded to 256; the GPU chain
+    # equals the oracle's chain on the GPU's constants, code for code
+    w1 = WL.custom(995, 120, 256, 200, dtype="f32", x_dist="laplace", n_outliers=3, outlier=20.0,
+                   w_std=0.05)
+    c1 = IntCase(w1, 120, 256, act=RELU, post=256)
+    y1 = hq.int_linear(c1.desc, c1.prep, c1.X)
+    assert tuple(y1.shape) == (120, 256)
+    rng = np.random.default_rng(7)
+    w2 = rng.normal(0, 0.05, (136, 200)).astype(np.float32)
+    b2 = rng.normal(0, 0.01, 136).astype(np.float32)
+    h1 = np.maximum(np.asarray(c1.x, np.float64) @ np.asarray(c1.weight, np.float64).T + c1.bias, 0)
+    y2f = h1 @ w2.astype(np.float64).T + b2
+    s2 = float(np.float32(np.abs(y2f).max() / 127.0))
+    d2 = hq.IntDesc(200, 136, 1, hq.F32, DH, 256)
+    p2 = hq.int_prepare(d2, torch.from_numpy(w2).cuda(), torch.from_numpy(b2).cuda(), c1.s_y, s2)
+    y2 = to_np(hq.int_linear(d2, p2, y1)).astype(np.int64)
+    v2 = hq.int_views(d2, p2)
+    g2 = {"qw": to_np(v2["w_codes"]).astype(np.int64), "b_int": to_np(v2["b_int"]).astype(np.int64),
+          "mult": to_np(v2["mult"]).astype(np.int64), "shift": int(to_np(v2["shift"])[0]),
+          "block": 1, "d_out": 136}
+    q1 = O.int_forward(c1.xi, c1.gpu_constants())["y_int"]
+    assert np.array_equal(to_np(y1).astype(np.int64), q1.astype(np.int64))
+    q2 = O.int_forward(q1, g2)["y_int"].astype(np.int64)
+    assert np.array_equal(y2, q2)
+    sq = O.sqnr_db(y2f / s2, y2.astype(np.float64))
+    print(f"padded integer MLP (WH 200 under H_256 + ReLU -> DH 200 padded to 256): SQNR {sq:.2f} dB")
     assert sq > 12
