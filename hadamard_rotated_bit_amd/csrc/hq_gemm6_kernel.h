@@ -61,12 +61,6 @@ __device__ __forceinline__ v16f mfma_f6(const v8i& a, const v8i& b, const v16f& 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, 0, 0, 0);
 }
 
-// Raw buffer descriptor over `bytes` bytes at `base` (stride 0; gfx9 data
-// format word): loads at offsets >= bytes return without touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
 // 16 bytes per lane from a buffer into LDS (buffer_load_dwordx4 ... lds):
 // lane l's bytes land at lds + 16 l.
 __device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff,
@@ -765,12 +759,12 @@ __device__ __forceinline__ void persist_body(const uint8_t* __restrict__ A, int6
             : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "=&v"(d4), "=&v"(d5)
             : "v"(la[0]), "v"(la[1]), "v"(la[2]), "v"(la[3]), "v"(la[4]), "v"(la[5])
             : "memory");
-        __builtin_amdgcn_raw_buffer_store_b128(d0, yr, off[0], 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(d1, yr, off[1], 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(d2, yr, off[2], 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(d3, yr, off[3], 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(d4, yr, off[4], 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(d5, yr, off[5], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(d0, yr, off[0], 0, Y_STORE_CPOL);
+        __builtin_amdgcn_raw_buffer_store_b128(d1, yr, off[1], 0, Y_STORE_CPOL);
+        __builtin_amdgcn_raw_buffer_store_b128(d2, yr, off[2], 0, Y_STORE_CPOL);
+        __builtin_amdgcn_raw_buffer_store_b128(d3, yr, off[3], 0, Y_STORE_CPOL);
+        __builtin_amdgcn_raw_buffer_store_b128(d4, yr, off[4], 0, Y_STORE_CPOL);
+        __builtin_amdgcn_raw_buffer_store_b128(d5, yr, off[5], 0, Y_STORE_CPOL);
       }
     }
     // The next tile's parameters go to the other buffer (nobody reads it:

@@ -21,6 +21,19 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * BK + ((chunk ^ ((row >> SH) & (NC - 1))) << 4);
 }
 
+// Raw buffer descriptor over `bytes` bytes at `base` (stride 0; gfx9 data
+// format word): loads at offsets >= bytes return without touching memory, stores there are
+// dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Cache policy of the output stores (sc0 sc1: system scope). Y is written
+// once and never read back by the kernel, so its lines are written through
+// to memory instead of being kept in L2, where they would evict the operand
+// lines the other tiles of the XCD still read.
+constexpr int Y_STORE_CPOL = 17;
+
 // s_waitcnt with vmcnt = N (vector-memory ops still allowed in flight) and
 // lgkmcnt = 0 (every LDS read issued by this wave has returned).
 template <int N>
@@ -250,7 +263,10 @@ __device__ __forceinline__ void gemm_epilogue_bf16_staged(AccT (&acc)[TM][TN], u
   }
   __syncthreads();
   constexpr int CPR = BN / 8;  // 16-byte pieces per tile row
-  uint16_t* Y = static_cast<uint16_t*>(ep.Y);
+  // the tile's rows of Y (m0 < M for every launched tile)
+  const int64_t rows_v = M - m0 < BM ? M - m0 : BM;
+  const __amdgpu_buffer_rsrc_t yr =
+      make_rsrc(static_cast<uint16_t*>(ep.Y) + m0 * ep.ldy, int(rows_v * ep.ldy * 2));
 #pragma unroll 8
   for (int q = tid; q < BM * CPR; q += NW * 64) {
     const int row = q / CPR, ch = q - row * CPR;
@@ -259,7 +275,8 @@ __device__ __forceinline__ void gemm_epilogue_bf16_staged(AccT (&acc)[TM][TN], u
       const uint8_t* src = tile + row * PITCH + ch * 16;
       const uint2 lo = *reinterpret_cast<const uint2*>(src);
       const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
-      *reinterpret_cast<uint4*>(Y + m * ep.ldy + n) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      __builtin_amdgcn_raw_buffer_store_b128(v4i{int(lo.x), int(lo.y), int(hi.x), int(hi.y)}, yr,
+                                             uint32_t((row * ep.ldy + n) * 2), 0, Y_STORE_CPOL);
     }
   }
 }
