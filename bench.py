@@ -15,9 +15,16 @@ activations are not served from the 256 MB Infinity Cache left over from the
 previous visit. Each workload first makes untimed calls for SPIN_UP_S seconds
 (the GPU leaves the idle clock state host-side data generation leaves it in),
 then W warmup steps, then the K timed steps. Per-kernel times come from HIP
-events around back-to-back launches of each stage entry point (captured in a
-HIP graph, replayed on the stream the events are recorded on; median of five
-replays). Prints one JSON line.
+events recorded after each stage inside a run of steps (the two stage entry
+points called in turn, as quant_linear issues them, on the stream the events
+are recorded on; median over the steps). The same stages launched back to
+back in a replayed HIP graph (median of five replays) are reported beside
+them as `graph_ms`: a run of GEMMs with no activation stage between them
+holds the chip at a higher power and a lower clock than the step does. Where
+the two in-step stage times add up to more than 1.1x the step (launch-bound
+layers, whose GPU then waits for the host between the stages), the graph
+times take their place (`stage_timing`: "graph" instead of "steps").
+Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flux_proj]
 """
@@ -173,6 +180,23 @@ def step_percentiles(torch, fn, nbuf, steps, start):
     return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
 
 
+def staged_steps(torch, act, gemm, nbuf, steps, start):
+    """Per-stage times inside a run of steps: act(i) then gemm(i) for `steps`
+    consecutive i, a HIP event recorded after each call on the stream both
+    run on; the median over the steps of each stage's time (ms)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        act((start + i) % nbuf)
+        ev[2 * i + 1].record()
+        gemm((start + i) % nbuf)
+        ev[2 * i + 2].record()
+    torch.cuda.synchronize()
+    k1 = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))
+    k2 = sorted(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(steps))
+    return k1[steps // 2], k2[steps // 2]
+
+
 def graph_time(torch, fn, n, reps=GRAPH_REPS):
     """Time of fn(i), i < n, captured back to back in one HIP graph and
     replayed on the current stream, timed with HIP events on that stream:
@@ -237,9 +261,10 @@ class Layer:
 
 
 def measure(hq, torch, L, desc, steps, warmup):
-    """Times `steps` quant_linear calls after `warmup` (the step), then each
-    stage alone as a replayed graph: the activation stage as quant_linear
-    runs it (hq_act_quantize_ws) and the GEMM + epilogue (hq_gemm_dequant)."""
+    """Times `steps` quant_linear calls after `warmup` (the step), then the
+    two stages inside a run of steps and each stage alone as a replayed
+    graph: the activation stage as quant_linear runs it (hq_act_quantize_ws)
+    and the GEMM + epilogue (hq_gemm_dequant)."""
     w, dev = L.w, L.dev
     prep = hq.prepare(desc, L.W, L.B, L.S, L.L1, L.L2)
     ws = torch.empty(hq.workspace_bytes(desc, w.T), dtype=torch.uint8, device=dev)
@@ -265,15 +290,24 @@ def measure(hq, torch, L, desc, steps, warmup):
             hq.channel_center_into(desc, prep, L.Xs[i % nbuf], mean, bias_eff, ws)
             hq.act_quantize(desc, prep, L.Xs[i % nbuf], out=(codes, s_x, mu, U), mean=mean,
                             workspace=ws)
-        k1 = graph_time(torch, act, n)
-        k2 = graph_time(torch, lambda i: hq.gemm_dequant(desc, prep, codes, s_x, bias_eff, U,
-                                                         out=L.Ys[i % nbuf]), n)
+
+        def gemm(i):
+            hq.gemm_dequant(desc, prep, codes, s_x, bias_eff, U, out=L.Ys[i % nbuf])
     else:
-        k1 = graph_time(torch, lambda i: hq.act_quantize(desc, prep, L.Xs[i % nbuf],
-                                                         out=(codes, s_x, mu, U), workspace=ws), n)
-        k2 = graph_time(torch, lambda i: hq.gemm_dequant(desc, prep, codes, s_x, mu, U,
-                                                         out=L.Ys[i % nbuf]), n)
-    return {"ms": ms, "wall": wall, "k1": k1, "k2": k2, "prep": prep, "pct": pct}
+        def act(i):
+            hq.act_quantize(desc, prep, L.Xs[i % nbuf], out=(codes, s_x, mu, U), workspace=ws)
+
+        def gemm(i):
+            hq.gemm_dequant(desc, prep, codes, s_x, mu, U, out=L.Ys[i % nbuf])
+    k1, k2 = staged_steps(torch, act, gemm, nbuf, max(steps, 20), warmup + 2 * steps)
+    k1g, k2g = graph_time(torch, act, n), graph_time(torch, gemm, n)
+    timing = "steps"
+    if k1 + k2 > 1.1 * ms:
+        # launch-bound layer: the events between the stages keep the GPU
+        # waiting for the host, so the in-step split is not the kernels' time
+        k1, k2, timing = k1g, k2g, "graph"
+    return {"ms": ms, "wall": wall, "k1": k1, "k2": k2, "k1_graph": k1g, "k2_graph": k2g,
+            "timing": timing, "prep": prep, "pct": pct}
 
 
 def kernel_figures(hq, desc, w, r):
@@ -304,12 +338,15 @@ def kernel_figures(hq, desc, w, r):
         "value": round(w.T / (r["ms"] * 1e-3), 1), "unit": "tokens/s",
         "ms_per_step": round(r["ms"], 5),
         "ms_per_step_percentiles": r["pct"],
+        "stage_timing": r["timing"],
         "effective_TOPS_step": round(k2_ops / (r["ms"] * 1e-3) / 1e12, 2),
-        "k1": {"ms": round(r["k1"], 5), "bytes": int(k1_bytes), "GBs": round(k1_gbs, 1),
+        "k1": {"ms": round(r["k1"], 5), "graph_ms": round(r["k1_graph"], 5),
+               "bytes": int(k1_bytes), "GBs": round(k1_gbs, 1),
                "hbm_frac": round(k1_gbs / HBM_PEAK_GBS, 4),
                "bytes_4bit_min": int(k1_min),
                "hbm_frac_4bit_min": round(k1_min / (r["k1"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "k2": {"ms": round(r["k2"], 5), "ops": k2_ops, "TOPS": round(k2_tops, 2),
+        "k2": {"ms": round(r["k2"], 5), "graph_ms": round(r["k2_graph"], 5),
+               "ops": k2_ops, "TOPS": round(k2_tops, 2),
                "peak_TOPS": peak, "mfma_frac": round(k2_tops / peak, 4),
                "bytes": int(k2_bytes), "GBs": round(k2_gbs, 1),
                "hbm_frac": round(k2_gbs / HBM_PEAK_GBS, 4)},
