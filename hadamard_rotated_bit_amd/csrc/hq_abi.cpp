@@ -151,7 +151,7 @@ Workspace workspace_of(const hq_desc* d, int64_t T) {
   off += align256(4 * size_t(T));
   w.U = off;
   off += align256(4 * size_t(T) * d->rank);
-  const int ks = d->rank ? hq::lowrank_slices(d->d_in, d->rank) : 0;
+  const int ks = d->rank ? hq::lowrank_slices(d->d_in, d->rank, T) : 0;
   w.lr_part = ks ? off : 0;
   off += align256(4 * size_t(ks) * size_t(T) * d->rank);
   if (d->center == HQ_CENTER_CHANNEL) {

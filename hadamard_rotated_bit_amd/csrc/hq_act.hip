@@ -676,22 +676,39 @@ __global__ void lowrank_sum_kernel(const float* __restrict__ part, int64_t n,
   U[i] = s;
 }
 
-// Waves (one-pass kernel) = slices (split form) per width d.
+// Waves of the one-pass kernel where the split form does not apply.
 static int lowrank_waves(int d) { return d % 256 == 0 && d >= 1024 ? 8 : 4; }
 
-int lowrank_slices(int d, int r) {
+constexpr int LR_LDS_MAX = 81920;   // LDS of one split-form block (two fit on a CU)
+constexpr int LR_CUS = 256;         // compute units the split form is balanced for
+
+int lowrank_slices(int d, int r, int64_t rows) {
   if (d % 128 || (r != 16 && r != 32 && r != 48 && r != 64)) return 0;
-  const int ks = lowrank_waves(d), kw = d / ks;
-  if (kw / 32 > LR_MAX_STEPS || 2 * r * (kw / 8) > LR_FILL * 512) return 0;
-  if (2 * r * (kw / 8 + 1) * 16 > 65536) return 0;   // the slice in at most 64 KB of LDS
-  return ks;
+  // Among 4, 6 and 8 slices of whole 32-channel steps that the block's
+  // registers and LDS hold, the one with the least work per slice times
+  // rounds of blocks over the compute units (ties: fewer slices).
+  const int64_t row_blocks = (rows + 127) / 128;
+  int best = 0;
+  int64_t best_cost = 0;
+  for (int ks : {4, 6, 8}) {
+    const int kw = d / ks;
+    if ((d / 32) % ks || kw / 32 > LR_MAX_STEPS || 2 * r * (kw / 8) > LR_FILL * 512 ||
+        2 * r * (kw / 8 + 1) * 16 > LR_LDS_MAX)
+      continue;
+    const int64_t cost = (row_blocks * ks + LR_CUS - 1) / LR_CUS * kw;
+    if (!best || cost < best_cost) {
+      best = ks;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_lowrank_split(const void* x, int x_bf16, int64_t rows, int d, int r,
                                 const uint16_t* l1_hi, const uint16_t* l1_lo, float* part,
                                 float* U, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  const int ks = lowrank_slices(d, r);
+  const int ks = lowrank_slices(d, r, rows);
   if (!ks) return hipErrorInvalidValue;
   const int kw = d / ks;
   const size_t lds = size_t(2) * r * (kw / 8 + 1) * 16;
@@ -717,6 +734,8 @@ hipError_t launch_lowrank_split(const void* x, int x_bf16, int64_t rows, int d, 
   const dim3 sg{unsigned((n + 255) / 256)};
   if (ks == 8)
     hipLaunchKernelGGL(lowrank_sum_kernel<8>, sg, dim3(256), 0, s, part, n, U);
+  else if (ks == 6)
+    hipLaunchKernelGGL(lowrank_sum_kernel<6>, sg, dim3(256), 0, s, part, n, U);
   else
     hipLaunchKernelGGL(lowrank_sum_kernel<4>, sg, dim3(256), 0, s, part, n, U);
   return hipGetLastError();
@@ -727,8 +746,11 @@ hipError_t launch_lowrank_down(const void* x, int x_bf16, int64_t rows, int d, i
                                hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (d % 128) return hipErrorInvalidValue;
-  // eight waves per 16 rows when every wave still gets whole 32-channel steps
-  const bool wide = lowrank_waves(d) == 8;
+  // one wave per slice of the split form (the same partition, so the same
+  // bits), else eight waves per 16 rows when every wave still gets whole
+  // 32-channel steps, else four
+  const int ks = lowrank_slices(d, r, rows);
+  const int waves = ks ? ks : lowrank_waves(d);
   dim3 grid{unsigned((rows + 15) / 16)};
 #define HQ_LR_LAUNCH(RR, WW)                                                                    \
   if (x_bf16)                                                                                   \
@@ -739,7 +761,9 @@ hipError_t launch_lowrank_down(const void* x, int x_bf16, int64_t rows, int d, i
                        static_cast<const float*>(x), rows, d, l1_hi, l1_lo, U);
 #define HQ_LR_CASE(RR)                                                                          \
   case RR:                                                                                      \
-    if (wide) { HQ_LR_LAUNCH(RR, 8) } else { HQ_LR_LAUNCH(RR, 4) }                              \
+    if (waves == 8) { HQ_LR_LAUNCH(RR, 8) }                                                    \
+    else if (waves == 6) { HQ_LR_LAUNCH(RR, 6) }                                               \
+    else { HQ_LR_LAUNCH(RR, 4) }                                                               \
     break;
   switch (r) {
     HQ_LR_CASE(16) HQ_LR_CASE(32) HQ_LR_CASE(48) HQ_LR_CASE(64)

@@ -93,10 +93,11 @@ hipError_t launch_lowrank_down(const void* x, int x_bf16, int64_t rows, int d, i
                                hipStream_t s);
 // The same U in two passes: per slice of d, products for 128 rows per block
 // with the slice of l1 shared in LDS, into part [slices, rows, r]; then the
-// slices summed in order. lowrank_slices(d, r) is the slice count (the
-// partition the one-pass kernel gives its waves, so U is bit-identical), or
-// 0 where the split form does not apply.
-int lowrank_slices(int d, int r);
+// slices summed in order. lowrank_slices(d, r, rows) is the slice count
+// (4, 6 or 8, chosen for the row count; the partition the one-pass kernel
+// gives its waves, so U is bit-identical), or 0 where the split form does
+// not apply.
+int lowrank_slices(int d, int r, int64_t rows);
 hipError_t launch_lowrank_split(const void* x, int x_bf16, int64_t rows, int d, int r,
                                 const uint16_t* l1_hi, const uint16_t* l1_lo, float* part,
                                 float* U, hipStream_t s);

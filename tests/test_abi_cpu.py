@@ -126,6 +126,28 @@ def test_e2m3_row_group_placement():
     np.testing.assert_array_equal(codefmt.decode(codefmt.E2M3, buf, rows, d), q)
 
 
+@pytest.mark.parametrize("d_in,rank,T,slices", [
+    (3072, 32, 300, 8), (3072, 32, 4200, 6), (3072, 32, 4608, 6), (3072, 32, 65536, 6),
+    (3072, 16, 4500, 6), (3072, 48, 4608, 0), (2048, 32, 128, 8), (2048, 32, 8192, 4),
+    (1152, 16, 8192, 4), (4096, 32, 4608, 8)])
+def test_low_rank_slice_count(d_in, rank, T, slices):
+    # The workspace holds U [T, rank] and the slice products [slices, T, rank]
+    # of the two-pass down projection. The slice count is the one of 4, 6
+    # and 8 (whole 32-channel steps, at most 16 steps per slice, the slice of
+    # L1 within one block's registers and LDS) with the least channels per
+    # slice times rounds of 128-row blocks over 256 compute units, fewer
+    # slices on a tie: d_in 3072 takes 8 slices of 384 at 300 rows (one
+    # round either way) and 6 slices of 512 from 33 blocks of rows up; rank
+    # 48 at 3072 fits no slicing (one-pass form, no slice products).
+    with_r = _d(d_in=d_in, block=128, rank=rank)
+    without = _d(d_in=d_in, block=128, rank=0)
+    assert lib.hq_validate(ctypes.byref(with_r)) == 0
+    al = lambda n: (n + 255) // 256 * 256
+    extra = lib.hq_workspace_bytes(ctypes.byref(with_r), T) - \
+        lib.hq_workspace_bytes(ctypes.byref(without), T)
+    assert extra == al(4 * T * rank) + al(4 * slices * T * rank)
+
+
 @pytest.mark.parametrize("w_dtype,esize", [(BF16, 2), (F32, 4)])
 def test_channel_centring_layout(w_dtype, esize):
     # center = 2 keeps a copy of the weight in the blob and needs partial sums,

@@ -144,12 +144,16 @@ def test_low_rank(rank, xd, gemm):
 
 @pytest.mark.parametrize("T,d_in,rank,xd", [(130, 2048, 32, "bf16"), (300, 3072, 32, "bf16"),
                                          (77, 1152, 16, "f32"), (129, 1024, 64, "f32"),
-                                         (1, 512, 48, "bf16"), (200, 1024, 16, "bf16")])
+                                         (1, 512, 48, "bf16"), (200, 1024, 16, "bf16"),
+                                         (4200, 3072, 32, "bf16"), (4500, 3072, 16, "f32")])
 def test_low_rank_split_matches_one_pass(T, d_in, rank, xd):
     # quant_linear forms U in two passes over slices of d_in (workspace for the
     # slice products); act_quantize has no workspace and runs the one-pass
     # kernel. The slices are the one-pass kernel's wave partition summed in
-    # the same order, so U and therefore Y are bit-identical.
+    # the same order, so U and therefore Y are bit-identical. The slice count
+    # follows the row count: 8 slices of 384 channels for d_in 3072 at 300
+    # rows, 6 of 512 at 4200 and 4500 rows (33-36 blocks of 128 rows, so 6
+    # slices fill the compute units in one round and 8 would not).
     r = run_case(T, d_in, 264, block=128, rank=rank, x_dtype=xd, w_dtype=xd, y_dtype=xd)
     desc, prep, X, Y, codes, s_x, mu, U, ora = r
     check_all(Y, codes, s_x, ora, desc)
