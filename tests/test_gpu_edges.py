@@ -9,7 +9,7 @@ import torch
 import hadamard_rotated_bit_amd as hq
 from hadamard_rotated_bit_amd import workloads as WL
 from oracle import hq_oracle as O
-from parity import MAX_FLIP_FRAC, Y_TOL, check_codes, codes_np, rel_fro, tdev, to_np
+from parity import MAX_FLIP_FRAC, XT_TOL, Y_TOL, check_codes, codes_np, rel_fro, tdev, to_np
 
 pytestmark = pytest.mark.gpu
 DT = {"f32": hq.F32, "bf16": hq.BF16}
@@ -169,6 +169,35 @@ def test_low_rank_split_matches_one_pass(T, d_in, rank, xd):
     small = torch.empty(hq.workspace_bytes(desc, T) - 256, dtype=torch.uint8, device=X.device)
     with pytest.raises(hq.HqError):
         hq.act_quantize(desc, prep, X, workspace=small)
+
+
+@pytest.mark.parametrize("T,d_in,block,rank,alpha,center", [
+    (300, 3072, 1024, 32, 0.5, True), (1, 3072, 512, 16, 0.5, True),
+    (17, 2560, 512, 32, None, False), (64, 2560, 512, 16, 0.5, True),
+    (4100, 3072, 1024, 32, None, True)])
+def test_low_rank_wide_rows(T, d_in, block, rank, alpha, center):
+    # bf16 input with d_in 2560 or 3072 (64 lanes per row in the row kernel),
+    # blocks of >= 512 channels and rank 16 or 32, with and without smoothing
+    # and centring: the flux_proj geometry at ragged row counts (1, 17, 300,
+    # 4100 rows: partial 128-row blocks of the down projection). quant_linear
+    # and act_quantize with a workspace run the two-pass projection,
+    # act_quantize without one the one-pass kernel, which adds the same
+    # slices in the same order: U, and therefore Y, are the same bits
+    # through all three.
+    r = run_case(T, d_in, 520, block=block, rank=rank, alpha=alpha, center=center,
+                 x_dtype="bf16", w_dtype="bf16", y_dtype="bf16")
+    desc, prep, X, Y, codes, s_x, mu, U, ora = r
+    check_all(Y, codes, s_x, ora, desc)
+    err = np.linalg.norm(to_np(U) - ora["u"], axis=1) / np.linalg.norm(ora["u"], axis=1)
+    print(f"U: max row error {err.max():.2e}")
+    assert err.max() <= 1e-4, err.max()
+    rms = np.sqrt(np.mean(ora["y"] ** 2, axis=1))
+    assert np.all(np.abs(to_np(mu) - ora["mu"]) <= XT_TOL * rms)
+    assert torch.equal(Y, hq.gemm_dequant(desc, prep, codes, s_x, mu, U))
+    ws = torch.empty(hq.workspace_bytes(desc, T), dtype=torch.uint8, device=X.device)
+    c2, s2, m2, U2 = hq.act_quantize(desc, prep, X, workspace=ws)
+    np.testing.assert_array_equal(codes_np(desc, c2, T), codes_np(desc, codes, T))
+    assert torch.equal(s2, s_x) and torch.equal(m2, mu) and torch.equal(U2, U)
 
 
 def test_heavy_outliers_and_no_centring():
