@@ -218,6 +218,13 @@ int run_act(const hq_desc* d, const void* prepared, const void* X, int64_t T, vo
   a.s_ld = T;
   a.out_aux = mu;
   a.mode = hq::ROW_ACT;
+  hq::RowGeom g;
+  if (d->rank && hq::row_geometry(d->d_in, &g) && hq::act_lr_applies(a, g, d->rank)) {
+    // row transform and low-rank projection in one launch
+    const hipError_t e = hq::launch_act_lr(a, g, d->rank, at<uint16_t>(prepared, L.l1_hi),
+                                           at<uint16_t>(prepared, L.l1_lo), U, s);
+    return e == hipSuccess ? HQ_OK : hip_fail(e, "activation kernel launch");
+  }
   hipError_t e = hq::launch_row_transform(a, s);
   if (e != hipSuccess) return hip_fail(e, "activation kernel launch");
   if (d->rank) {

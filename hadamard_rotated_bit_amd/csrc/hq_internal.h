@@ -64,6 +64,14 @@ hipError_t launch_row_transform(const RowArgs& a, hipStream_t s);
 // The fast kernel for blocks of at least 8 G channels; hipErrorNotSupported
 // when the geometry has no instance (the general kernel then runs).
 hipError_t launch_row_fast(const RowArgs& a, const RowGeom& g, hipStream_t s);
+// The fast row transform (activation mode) and the rank-r down projection
+// U [rows, r] = in . (l1_hi + l1_lo)^T in one launch; act_lr_applies says
+// whether the geometry has this form (bf16 input, G = 64 with C = 5 or 6,
+// r = 16 or 32, blocks of >= 512 channels, no per-channel means or groups),
+// launch_act_lr returns hipErrorNotSupported where it has not.
+bool act_lr_applies(const RowArgs& a, const RowGeom& g, int r);
+hipError_t launch_act_lr(const RowArgs& a, const RowGeom& g, int r, const uint16_t* l1_hi,
+                         const uint16_t* l1_lo, float* U, hipStream_t s);
 
 // absmax[i] = max over rows of |in[r, i]| ; absmax zeroed by the launcher.
 hipError_t launch_col_absmax(const void* in, int in_bf16, int64_t rows, int d, float* absmax,

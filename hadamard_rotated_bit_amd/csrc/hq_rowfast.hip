@@ -100,54 +100,17 @@ __device__ __forceinline__ void store_piece48(uint8_t* p, uint32_t w0, uint32_t 
   *reinterpret_cast<uint16_t*>(p + (odd ? 0 : 4)) = uint16_t(odd ? w0 : w1);
 }
 
-template <typename TIn, int G, int C, int NX, int P>
-__global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt_b) {
-  constexpr int LOG2G = (G == 16) ? 4 : (G == 32) ? 5 : 6;
+// Everything after a row's loads: means and multipliers, the butterflies,
+// the centring and the quantiser, for the row `row` whose lane-t chunks are
+// in v. lpar holds the block's multipliers (P >= 1) and, from float4 MO on,
+// its means (P = 2).
+template <int G, int C, int NX, int P, int MO>
+__device__ __forceinline__ void row_fast_body(const RowArgs& a, float inv_sqrt_b, int t,
+                                              int64_t row, bool valid, float* v,
+                                              const float4* lpar) {
   constexpr int E = 8 * C;
-  constexpr int RPW = 64 / G;
   constexpr int NEG = (G >= 32) ? 31 : 15;  // lane bits done in negating form
-  static_assert((C >> NX) << NX == C, "chunk stages pair whole chunks");
-  const int lane = threadIdx.x & 63;
-  const int t = lane & (G - 1);
-  const int64_t row = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW + lane / G;
-  const bool valid = row < a.rows;
-  const int64_t r = valid ? row : a.rows - 1;
   const int d = a.d;
-  const TIn* src = static_cast<const TIn*>(a.in) + r * d + t * 8;
-
-  // The channel multipliers (P >= 1) and means (P = 2) are the same for
-  // every row: the block stages them once in LDS and each lane reads its 8
-  // per chunk there, so they hold no per-lane registers across the row and
-  // take no slots in the vector memory queue behind the row. Their loads go
-  // first (loads retire in issue order, so issued after the row they would
-  // wait for the whole row); lanes past the end repeat the last float4, so
-  // no load or store is conditional.
-  constexpr int NV4 = 2 * C * G;                // float4 per vector (d / 4)
-  constexpr int PV = (NV4 + 255) / 256;         // per thread
-  constexpr int NP = P == 2 ? 2 : 1;
-  __shared__ float4 lpar[P == 0 ? 1 : NP * PV * 256];
-  float v[E];
-  if constexpr (P > 0) {
-    const int tid = threadIdx.x;
-    float4 pv[NP][PV];
-#pragma unroll
-    for (int k = 0; k < PV; ++k) {
-      const int i = k * 256 + tid < NV4 ? k * 256 + tid : NV4 - 1;
-      pv[0][k] = reinterpret_cast<const float4*>(a.scale)[i];
-      if constexpr (P == 2) pv[1][k] = reinterpret_cast<const float4*>(a.chan_mean)[i];
-    }
-#pragma unroll
-    for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
-#pragma unroll
-    for (int q = 0; q < NP; ++q)
-#pragma unroll
-      for (int k = 0; k < PV; ++k) lpar[q * PV * 256 + k * 256 + tid] = pv[q][k];
-    __syncthreads();
-  } else {
-#pragma unroll
-    for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
-  }
-
   const float g1 = (t & 1) ? -1.0f : 1.0f, g2 = (t & 2) ? -1.0f : 1.0f;
   const float g4 = (t & 4) ? -1.0f : 1.0f, g8 = (t & 8) ? -1.0f : 1.0f;
   const float g16 = (t & 16) ? -1.0f : 1.0f, g32 = (t & 32) ? -1.0f : 1.0f;
@@ -165,7 +128,7 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
   for (int c = 0; c < C; ++c) {
     float* vc = &v[c * 8];
     if constexpr (P == 2) {
-      const float4 m0 = lpar[PV * 256 + c * 2 * G + 2 * t], m1 = lpar[PV * 256 + c * 2 * G + 2 * t + 1];
+      const float4 m0 = lpar[MO + c * 2 * G + 2 * t], m1 = lpar[MO + c * 2 * G + 2 * t + 1];
       vc[0] -= m0.x; vc[1] -= m0.y; vc[2] -= m0.z; vc[3] -= m0.w;
       vc[4] -= m1.x; vc[5] -= m1.y; vc[6] -= m1.z; vc[7] -= m1.w;
     }
@@ -286,6 +249,57 @@ __global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt
   }
 }
 
+
+template <typename TIn, int G, int C, int NX, int P>
+__global__ __launch_bounds__(256) void row_fast_kernel(RowArgs a, float inv_sqrt_b) {
+  constexpr int LOG2G = (G == 16) ? 4 : (G == 32) ? 5 : 6;
+  constexpr int E = 8 * C;
+  constexpr int RPW = 64 / G;
+  static_assert((C >> NX) << NX == C, "chunk stages pair whole chunks");
+  const int lane = threadIdx.x & 63;
+  const int t = lane & (G - 1);
+  const int64_t row = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW + lane / G;
+  const bool valid = row < a.rows;
+  const int64_t r = valid ? row : a.rows - 1;
+  const int d = a.d;
+  const TIn* src = static_cast<const TIn*>(a.in) + r * d + t * 8;
+
+  // The channel multipliers (P >= 1) and means (P = 2) are the same for
+  // every row: the block stages them once in LDS and each lane reads its 8
+  // per chunk there, so they hold no per-lane registers across the row and
+  // take no slots in the vector memory queue behind the row. Their loads go
+  // first (loads retire in issue order, so issued after the row they would
+  // wait for the whole row); lanes past the end repeat the last float4, so
+  // no load or store is conditional.
+  constexpr int NV4 = 2 * C * G;                // float4 per vector (d / 4)
+  constexpr int PV = (NV4 + 255) / 256;         // per thread
+  constexpr int NP = P == 2 ? 2 : 1;
+  __shared__ float4 lpar[P == 0 ? 1 : NP * PV * 256];
+  float v[E];
+  if constexpr (P > 0) {
+    const int tid = threadIdx.x;
+    float4 pv[NP][PV];
+#pragma unroll
+    for (int k = 0; k < PV; ++k) {
+      const int i = k * 256 + tid < NV4 ? k * 256 + tid : NV4 - 1;
+      pv[0][k] = reinterpret_cast<const float4*>(a.scale)[i];
+      if constexpr (P == 2) pv[1][k] = reinterpret_cast<const float4*>(a.chan_mean)[i];
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int k = 0; k < PV; ++k) lpar[q * PV * 256 + k * 256 + tid] = pv[q][k];
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
+  }
+
+  row_fast_body<G, C, NX, P, PV * 256>(a, inv_sqrt_b, t, row, valid, v, lpar);
+}
+
 // Instantiated geometries: the (G, C) pairs row_geometry picks for the
 // supported widths, each with every chunk-stage count its block sizes need.
 template <typename TIn, int G, int C>
@@ -352,6 +366,223 @@ hipError_t launch_row_fast(const RowArgs& a, const RowGeom& g, hipStream_t s) {
   if (g.G == 16) return launch_fast_g<float, 16>(a, g.C, nx, s);
   if (g.G == 32) return launch_fast_g<float, 32>(a, g.C, nx, s);
   return launch_fast_g<float, 64>(a, g.C, nx, s);
+}
+
+// The activation stage with the rank-r down projection in one launch, for
+// bf16 input with 64 lanes per row: U = X (diag(1/sigma) L1) of the data-free
+// int4 blog's low-rank branch ("Hadamard rotation: the int4 improvement",
+// steps 3-4; "How it is applied here": the branch takes the smoothed input
+// inside the activation pass) beside the row transform. sigma is folded into
+// the prepared L1 (bf16 hi + lo, rank-major), so the branch multiplies the
+// bf16 input itself, exact as an MFMA operand.
+//
+// Blocks below npb are projection blocks: 64 rows of U each, complete (no
+// slice products to add afterwards, so no second launch). Wave w takes rows
+// 16 (w % 4) .. + 15 and one half of d (w / 4); the halves advance in 12
+// (d = 3072) or 10 (d = 2560) phases of 128 channels. A phase's L1 slices
+// (both halves, hi and lo: 32 KB for rank 32) go straight from L2 into one
+// of two LDS buffers by global_load_lds_dwordx4, one phase ahead, with the
+// chunks of rank row n rotated by n mod 16 (the 16 lanes of an operand read
+// hit 16 distinct bank positions); the X operands go into registers two
+// phases ahead. Each 32-channel step is two v_mfma_f32_16x16x32_bf16 per 16
+// ranks (hi, then lo), and the two halves are added in a fixed order at the
+// end. The other blocks run the row transform, eight rows per block.
+// Projection blocks have the lowest indices, so they start first and run
+// beside the row blocks, which are bound by their butterflies rather than
+// by memory; both kinds fit two blocks per CU (at most 64 KB of LDS and
+// 128 VGPRs). The projection blocks' chain of 12 latency-bound phases is
+// the longer of the two on flux_proj's shape.
+constexpr int AL_ROWS = 64;   // rows of U per projection block
+constexpr int AL_PH = 128;    // channels per phase and half of d
+
+template <int C, int NX, int P, int NT>
+__global__ __launch_bounds__(512) void act_lr_kernel(RowArgs a, float inv_sqrt_b,
+                                                        const uint16_t* __restrict__ l1hi,
+                                                        const uint16_t* __restrict__ l1lo,
+                                                        float* __restrict__ U, int npb) {
+  constexpr int G = 64, E = 8 * C, R = 16 * NT;
+  constexpr int D = 8 * G * C;              // channels of a row
+  constexpr int DH = D / 2;                 // channels per half
+  constexpr int NPH = DH / AL_PH;           // phases
+  constexpr int CH = AL_PH / 8;             // 16-byte chunks of a rank row per phase
+  constexpr int NV4 = 2 * C * G;            // float4 of multipliers
+  constexpr int PV = (NV4 + 511) / 512;
+  constexpr int LDS_LR = 2 * 4 * R * CH;    // uint4 of two buffers of slices
+  constexpr int LDS_ROW = P == 0 ? 1 : PV * 512;
+  static_assert(NPH * AL_PH == DH && R % 8 == 0, "whole phases and fills");
+  static_assert((C >> NX) << NX == C, "chunk stages pair whole chunks");
+  __shared__ uint4 lds[LDS_LR > LDS_ROW ? LDS_LR : LDS_ROW];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  if (int(blockIdx.x) < npb) {
+    const int rg = w & 3, kh = w >> 2;
+    const int kq = 8 * (lane >> 4), nl = lane & 15;
+    const int64_t rbase = int64_t(blockIdx.x) * AL_ROWS + 16 * rg;
+    const int64_t xrow = rbase + nl < a.rows ? rbase + nl : a.rows - 1;
+    const uint16_t* const xp = static_cast<const uint16_t*>(a.in) + xrow * D + kh * DH + kq;
+    // A phase's slices go straight to LDS (global_load_lds_dwordx4, 1 KB
+    // per wave instruction): slot s of a buffer holds chunk (s % 16) ^ (n % 16)
+    // of rank row n = (s / 16) % R of slice s / (16 R) = 2 half + (0 hi, 1 lo),
+    // so the 16 lanes of an operand read (16 rank rows, one chunk) hit 16
+    // distinct bank positions. Wave w fills units w UW .. w UW + UW - 1.
+    constexpr int UW = R / 8;                 // 64-slot units per wave and phase
+    constexpr int BUF = 4 * R * CH;           // slots (uint4) per buffer
+    const uint16_t* dsrc[UW];
+#pragma unroll
+    for (int i = 0; i < UW; ++i) {
+      const int sl = 64 * (w * UW + i) + lane, q = sl / (16 * R), n = (sl >> 4) % R;
+      const int c = (sl & 15) ^ (n & 15);
+      dsrc[i] = ((q & 1) ? l1lo : l1hi) + int64_t(n) * D + (q >> 1) * DH + 8 * c;
+    }
+    // X operands XD - 1 phases ahead in a ring of XD register sets, the
+    // slices one phase ahead in two LDS buffers. Phase P issues the slices
+    // of P + 1, then the X operands of P + XD - 1; so when phase P > 0
+    // starts, only the X operands issued in phase P - 1 came after the
+    // slices it needs, and its wait leaves those in flight (vector memory
+    // operations retire in issue order). Phase 0 waits for the slices and
+    // X operands of phase 0 only.
+    constexpr int XS = AL_PH / 32;            // X operands per phase
+    constexpr int XD = 3;                     // X register sets
+    v8bf xa[XD][XS];
+    v4f acc[NT];
+#pragma unroll
+    for (int g = 0; g < NT; ++g) acc[g] = v4f{0, 0, 0, 0};
+#define HQ_AL_DMA(P_)                                                                       \
+  do {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < UW; ++i)                                          \
+      lds_dma16(dsrc[i] + (P_) * AL_PH, &lds[((P_) & 1) * BUF + 64 * (w * UW + i)]);        \
+    __builtin_amdgcn_sched_barrier(0);                                                      \
+  } while (0)
+#define HQ_AL_X(P_)                                                                         \
+  if constexpr ((P_) < NPH) {                                                               \
+    _Pragma("unroll") for (int st = 0; st < XS; ++st)                                       \
+      xa[(P_) % XD][st] = *reinterpret_cast<const v8bf*>(xp + (P_) * AL_PH + 32 * st);      \
+    __builtin_amdgcn_sched_barrier(0);                                                      \
+  }
+    // loads phase P may leave in flight (see above)
+    constexpr auto al_pending = [](int ph) {
+      if (ph == 0) return ((XD - 2) < (NPH - 1) ? (XD - 2) : (NPH - 1)) * XS;
+      return ph + XD - 2 < NPH ? XS : 0;
+    };
+#define HQ_AL_PHASE(P_)                                                                     \
+  if constexpr ((P_) < NPH) {                                                               \
+    /* vmcnt(al_pending(P_)) lgkmcnt(0) */                                                  \
+    __builtin_amdgcn_s_waitcnt((al_pending(P_) & 0xF) | ((al_pending(P_) >> 4) << 14) |     \
+                               0x70);                                                       \
+    __syncthreads();                                                                        \
+    if constexpr ((P_) + 1 < NPH) HQ_AL_DMA((P_) + 1);                                      \
+    HQ_AL_X((P_) + XD - 1)                                                                  \
+    const uint4* const bq = &lds[((P_) & 1) * BUF];                                         \
+    _Pragma("unroll") for (int st = 0; st < XS; ++st)                                       \
+      _Pragma("unroll") for (int g = 0; g < NT; ++g) {                                      \
+        const int ci = (g * 16 + nl) * 16 + ((4 * st + (lane >> 4)) ^ nl);                 \
+        const v8bf bh = *reinterpret_cast<const v8bf*>(&bq[(2 * kh) * R * 16 + ci]);        \
+        const v8bf bl = *reinterpret_cast<const v8bf*>(&bq[(2 * kh + 1) * R * 16 + ci]);    \
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[(P_) % XD][st], bh, acc[g], 0, 0, 0); \
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[(P_) % XD][st], bl, acc[g], 0, 0, 0); \
+      }                                                                                     \
+  }
+    static_assert(CH == 16 && NPH >= 2 && NPH <= 12 && (XD - 2) * XS < 64, "phase schedule");
+    HQ_AL_DMA(0);
+    // the prologue loads the X operands of phases 0 .. XD - 2
+    static_assert(XD >= 2 && XD <= 5, "prologue length");
+    HQ_AL_X(0)
+    if constexpr (XD > 2) { HQ_AL_X(1) }
+    if constexpr (XD > 3) { HQ_AL_X(2) }
+    if constexpr (XD > 4) { HQ_AL_X(3) }
+    HQ_AL_PHASE(0) HQ_AL_PHASE(1) HQ_AL_PHASE(2) HQ_AL_PHASE(3) HQ_AL_PHASE(4) HQ_AL_PHASE(5)
+    HQ_AL_PHASE(6) HQ_AL_PHASE(7) HQ_AL_PHASE(8) HQ_AL_PHASE(9) HQ_AL_PHASE(10) HQ_AL_PHASE(11)
+#undef HQ_AL_PHASE
+#undef HQ_AL_X
+#undef HQ_AL_DMA
+    // the halves: the second writes its products, the first adds them
+    // (16x16 output layout: lane l, register j -> row 4 (l / 16) + j, rank l % 16)
+    __syncthreads();
+    float* const red = reinterpret_cast<float*>(lds);
+    if (kh == 1) {
+#pragma unroll
+      for (int g = 0; g < NT; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[(rg * 16 + 4 * (lane >> 4) + j) * R + g * 16 + nl] = acc[g][j];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int g = 0; g < NT; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t m = rbase + 4 * (lane >> 4) + j;
+          if (m < a.rows)
+            U[m * R + g * 16 + nl] = acc[g][j] + red[(rg * 16 + 4 * (lane >> 4) + j) * R + g * 16 + nl];
+        }
+    }
+    return;
+  }
+
+  // row transform of rows 8 (blockIdx.x - npb) + w (the row kernel's body)
+  const int t = lane;
+  const int64_t row = int64_t(int(blockIdx.x) - npb) * 8 + w;
+  const bool valid = row < a.rows;
+  const int64_t r = valid ? row : a.rows - 1;
+  const uint16_t* src = static_cast<const uint16_t*>(a.in) + r * D + t * 8;
+  float4* const lpar = reinterpret_cast<float4*>(lds);
+  float v[E];
+  if constexpr (P > 0) {
+    float4 pv[PV];
+#pragma unroll
+    for (int k = 0; k < PV; ++k) {
+      const int i = k * 512 + tid < NV4 ? k * 512 + tid : NV4 - 1;
+      pv[k] = reinterpret_cast<const float4*>(a.scale)[i];
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
+#pragma unroll
+    for (int k = 0; k < PV; ++k) lpar[k * 512 + tid] = pv[k];
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int c = 0; c < C; ++c) load8(src + c * 8 * G, &v[c * 8]);
+  }
+  row_fast_body<G, C, NX, P, 0>(a, inv_sqrt_b, t, row, valid, v, lpar);
+}
+
+bool act_lr_applies(const RowArgs& a, const RowGeom& g, int r) {
+  const int nx = a.log2b - 9;
+  return a.in_bf16 && a.mode == ROW_ACT && !a.group && !a.chan_mean && g.G == 64 &&
+         (g.C == 5 || g.C == 6) && (r == 16 || r == 32) && nx >= 0 && (1 << nx) <= g.C &&
+         g.C % (1 << nx) == 0;
+}
+
+template <int C, int NX, int NT>
+static void launch_al_p(const RowArgs& a, dim3 grid, float isb, const uint16_t* hi,
+                        const uint16_t* lo, float* U, int npb, hipStream_t s) {
+  if (a.scale)
+    hipLaunchKernelGGL((act_lr_kernel<C, NX, 1, NT>), grid, dim3(512), 0, s, a, isb, hi, lo, U, npb);
+  else
+    hipLaunchKernelGGL((act_lr_kernel<C, NX, 0, NT>), grid, dim3(512), 0, s, a, isb, hi, lo, U, npb);
+}
+
+template <int NT>
+static hipError_t launch_al_nt(const RowArgs& a, const RowGeom& g, dim3 grid, float isb,
+                               const uint16_t* hi, const uint16_t* lo, float* U, int npb,
+                               hipStream_t s) {
+  const int nx = a.log2b - 9;
+  if (g.C == 5 && nx == 0) launch_al_p<5, 0, NT>(a, grid, isb, hi, lo, U, npb, s);
+  else if (g.C == 6 && nx == 0) launch_al_p<6, 0, NT>(a, grid, isb, hi, lo, U, npb, s);
+  else if (g.C == 6 && nx == 1) launch_al_p<6, 1, NT>(a, grid, isb, hi, lo, U, npb, s);
+  else return hipErrorNotSupported;
+  return hipGetLastError();
+}
+
+hipError_t launch_act_lr(const RowArgs& a, const RowGeom& g, int r, const uint16_t* l1_hi,
+                         const uint16_t* l1_lo, float* U, hipStream_t s) {
+  if (!act_lr_applies(a, g, r)) return hipErrorNotSupported;
+  if (a.rows <= 0) return hipSuccess;
+  const int64_t npb = (a.rows + AL_ROWS - 1) / AL_ROWS;
+  const dim3 grid{unsigned(npb + (a.rows + 7) / 8)};
+  const float isb = 1.0f / sqrtf(float(1 << a.log2b));
+  if (r == 16) return launch_al_nt<1>(a, g, grid, isb, l1_hi, l1_lo, U, int(npb), s);
+  return launch_al_nt<2>(a, g, grid, isb, l1_hi, l1_lo, U, int(npb), s);
 }
 
 }  // namespace hq

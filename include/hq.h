@@ -292,9 +292,12 @@ int hq_act_quantize(const hq_desc* desc, const void* prepared, const void* X, in
  * hq_act_quantize, bit for bit, but for rank > 0 the down projection U = x' L1
  * takes the two-pass form that keeps its per-slice products in the workspace
  * (hq_act_quantize, which has no workspace, makes one pass with every block
- * reading all of L1). workspace: at least hq_workspace_bytes(desc, T) bytes
- * (only its slice-product region is written); caller-owned, contents
- * undefined on entry and exit. Returns HQ_ERR_WORKSPACE if too small. */
+ * reading all of L1). Where the row transform and the projection run as one
+ * launch (bf16 X, d_in 2560 or 3072, block >= 512, rank 16 or 32, center
+ * 0 or 1, no groups) both entry points run that launch and the workspace is
+ * not written. workspace: at least hq_workspace_bytes(desc, T) bytes (only
+ * its slice-product region is written); caller-owned, contents undefined on
+ * entry and exit. Returns HQ_ERR_WORKSPACE if too small. */
 int hq_act_quantize_ws(const hq_desc* desc, const void* prepared, const void* X, int64_t T,
                        void* codes, float* s_x, float* mu, float* U, void* workspace,
                        size_t workspace_bytes, void* stream);

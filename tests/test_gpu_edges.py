@@ -179,11 +179,11 @@ def test_low_rank_wide_rows(T, d_in, block, rank, alpha, center):
     # bf16 input with d_in 2560 or 3072 (64 lanes per row in the row kernel),
     # blocks of >= 512 channels and rank 16 or 32, with and without smoothing
     # and centring: the flux_proj geometry at ragged row counts (1, 17, 300,
-    # 4100 rows: partial 128-row blocks of the down projection). quant_linear
-    # and act_quantize with a workspace run the two-pass projection,
-    # act_quantize without one the one-pass kernel, which adds the same
-    # slices in the same order: U, and therefore Y, are the same bits
-    # through all three.
+    # 4100 rows: partial 64-row projection blocks and 8-row transform
+    # blocks). These geometries run the row transform and the down
+    # projection in one launch through every entry point (quant_linear,
+    # act_quantize with and without a workspace), so U, and therefore Y, are
+    # the same bits through all three.
     r = run_case(T, d_in, 520, block=block, rank=rank, alpha=alpha, center=center,
                  x_dtype="bf16", w_dtype="bf16", y_dtype="bf16")
     desc, prep, X, Y, codes, s_x, mu, U, ora = r
