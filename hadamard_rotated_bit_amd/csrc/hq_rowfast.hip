@@ -368,6 +368,23 @@ hipError_t launch_row_fast(const RowArgs& a, const RowGeom& g, hipStream_t s) {
   return launch_fast_g<float, 64>(a, g.C, nx, s);
 }
 
+// Two 16-byte LDS reads that wait for their own results. Written as inline
+// asm so that the compiler, which cannot tell these addresses from the
+// targets of the LDS DMA still in flight, does not put a vmcnt(0) in front
+// of them (that would drain the loads issued for the next phases).
+__device__ __forceinline__ void lds_read2_b128(const uint4* p0, const uint4* p1, v4i& d0,
+                                               v4i& d1) {
+  const uint32_t a0 = uint32_t(reinterpret_cast<uintptr_t>(p0));
+  const uint32_t a1 = uint32_t(reinterpret_cast<uintptr_t>(p1));
+  asm volatile(
+      "ds_read_b128 %0, %2\n"
+      "ds_read_b128 %1, %3\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d0), "=&v"(d1)
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+
 // The activation stage with the rank-r down projection in one launch, for
 // bf16 input with 64 lanes per row: U = X (diag(1/sigma) L1) of the data-free
 // int4 blog's low-rank branch ("Hadamard rotation: the int4 improvement",
@@ -378,22 +395,24 @@ hipError_t launch_row_fast(const RowArgs& a, const RowGeom& g, hipStream_t s) {
 //
 // Blocks below npb are projection blocks: 64 rows of U each, complete (no
 // slice products to add afterwards, so no second launch). Wave w takes rows
-// 16 (w % 4) .. + 15 and one half of d (w / 4); the halves advance in 12
-// (d = 3072) or 10 (d = 2560) phases of 128 channels. A phase's L1 slices
-// (both halves, hi and lo: 32 KB for rank 32) go straight from L2 into one
-// of two LDS buffers by global_load_lds_dwordx4, one phase ahead, with the
-// chunks of rank row n rotated by n mod 16 (the 16 lanes of an operand read
-// hit 16 distinct bank positions); the X operands go into registers two
-// phases ahead. Each 32-channel step is two v_mfma_f32_16x16x32_bf16 per 16
-// ranks (hi, then lo), and the two halves are added in a fixed order at the
-// end. The other blocks run the row transform, eight rows per block.
-// Projection blocks have the lowest indices, so they start first and run
-// beside the row blocks, which are bound by their butterflies rather than
-// by memory; both kinds fit two blocks per CU (at most 64 KB of LDS and
-// 128 VGPRs). The projection blocks' chain of 12 latency-bound phases is
-// the longer of the two on flux_proj's shape.
+// 16 (w % 4) .. + 15 and one half of d (w / 4); the halves advance in 24
+// (d = 3072) or 20 (d = 2560) phases of 64 channels. Every load runs three
+// phases ahead: a phase's L1 slices (both halves, hi and lo: 16 KB for rank
+// 32) go straight from L2 into one of four LDS buffers by
+// global_load_lds_dwordx4, with the chunks of rank row n rotated by
+// (n / 2) mod 8 (the 16 lanes of an operand read hit 16 distinct bank
+// positions), and its X operands into one of four register sets. A phase
+// waits for its own loads only (an explicit vmcnt that leaves the next two
+// phases' loads in flight) and meets the other waves at a bare s_barrier.
+// Each 32-channel step is two v_mfma_f32_16x16x32_bf16 per 16 ranks (hi,
+// then lo), and the two halves are added in a fixed order at the end. The
+// other blocks run the row transform, eight rows per block. Projection
+// blocks have the lowest indices, so they start first and run beside the
+// row blocks, which are bound by their butterflies rather than by memory;
+// both kinds fit two blocks per CU (at most 64 KB of LDS and 128 VGPRs).
 constexpr int AL_ROWS = 64;   // rows of U per projection block
-constexpr int AL_PH = 128;    // channels per phase and half of d
+constexpr int AL_PH = 64;     // channels per phase and half of d
+constexpr int AL_NB = 4;      // LDS buffers and X register sets (loads NB - 1 phases ahead)
 
 template <int C, int NX, int P, int NT>
 __global__ __launch_bounds__(512) void act_lr_kernel(RowArgs a, float inv_sqrt_b,
@@ -407,7 +426,7 @@ __global__ __launch_bounds__(512) void act_lr_kernel(RowArgs a, float inv_sqrt_b
   constexpr int CH = AL_PH / 8;             // 16-byte chunks of a rank row per phase
   constexpr int NV4 = 2 * C * G;            // float4 of multipliers
   constexpr int PV = (NV4 + 511) / 512;
-  constexpr int LDS_LR = 2 * 4 * R * CH;    // uint4 of two buffers of slices
+  constexpr int LDS_LR = AL_NB * 4 * R * CH; // uint4 of the slice buffers
   constexpr int LDS_ROW = P == 0 ? 1 : PV * 512;
   static_assert(NPH * AL_PH == DH && R % 8 == 0, "whole phases and fills");
   static_assert((C >> NX) << NX == C, "chunk stages pair whole chunks");
@@ -420,81 +439,81 @@ __global__ __launch_bounds__(512) void act_lr_kernel(RowArgs a, float inv_sqrt_b
     const int64_t rbase = int64_t(blockIdx.x) * AL_ROWS + 16 * rg;
     const int64_t xrow = rbase + nl < a.rows ? rbase + nl : a.rows - 1;
     const uint16_t* const xp = static_cast<const uint16_t*>(a.in) + xrow * D + kh * DH + kq;
-    // A phase's slices go straight to LDS (global_load_lds_dwordx4, 1 KB
-    // per wave instruction): slot s of a buffer holds chunk (s % 16) ^ (n % 16)
-    // of rank row n = (s / 16) % R of slice s / (16 R) = 2 half + (0 hi, 1 lo),
-    // so the 16 lanes of an operand read (16 rank rows, one chunk) hit 16
-    // distinct bank positions. Wave w fills units w UW .. w UW + UW - 1.
-    constexpr int UW = R / 8;                 // 64-slot units per wave and phase
+    // Every load runs NB - 1 phases ahead: a phase's slices go straight to
+    // one of NB LDS buffers (global_load_lds_dwordx4, 1 KB per wave
+    // instruction), its X operands into one of NB register sets. Slot s of
+    // a buffer holds chunk (s % CH) ^ ((n / 2) % CH) of rank row
+    // n = (s / CH) % R of slice s / (CH R) = 2 half + (0 hi, 1 lo), so the
+    // 16 lanes of an operand read (16 rank rows, one chunk) hit 16 distinct
+    // bank positions. Wave w fills units w UW .. w UW + UW - 1.
+    static_assert(CH == 8, "rotation over 8 chunks per rank row");
+    constexpr int UW = R * CH / 128;          // 64-slot units per wave and phase
     constexpr int BUF = 4 * R * CH;           // slots (uint4) per buffer
+    constexpr int XS = AL_PH / 32;            // X operands per phase
     const uint16_t* dsrc[UW];
 #pragma unroll
     for (int i = 0; i < UW; ++i) {
-      const int sl = 64 * (w * UW + i) + lane, q = sl / (16 * R), n = (sl >> 4) % R;
-      const int c = (sl & 15) ^ (n & 15);
+      const int sl = 64 * (w * UW + i) + lane, q = sl / (CH * R), n = (sl / CH) % R;
+      const int c = (sl % CH) ^ ((n >> 1) % CH);
       dsrc[i] = ((q & 1) ? l1lo : l1hi) + int64_t(n) * D + (q >> 1) * DH + 8 * c;
     }
-    // X operands XD - 1 phases ahead in a ring of XD register sets, the
-    // slices one phase ahead in two LDS buffers. Phase P issues the slices
-    // of P + 1, then the X operands of P + XD - 1; so when phase P > 0
-    // starts, only the X operands issued in phase P - 1 came after the
-    // slices it needs, and its wait leaves those in flight (vector memory
-    // operations retire in issue order). Phase 0 waits for the slices and
-    // X operands of phase 0 only.
-    constexpr int XS = AL_PH / 32;            // X operands per phase
-    constexpr int XD = 3;                     // X register sets
-    v8bf xa[XD][XS];
+    v8bf xa[AL_NB][XS];
     v4f acc[NT];
 #pragma unroll
     for (int g = 0; g < NT; ++g) acc[g] = v4f{0, 0, 0, 0};
-#define HQ_AL_DMA(P_)                                                                       \
-  do {                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < UW; ++i)                                          \
-      lds_dma16(dsrc[i] + (P_) * AL_PH, &lds[((P_) & 1) * BUF + 64 * (w * UW + i)]);        \
-    __builtin_amdgcn_sched_barrier(0);                                                      \
-  } while (0)
-#define HQ_AL_X(P_)                                                                         \
+    // Issue order: the prologue loads phases 0 .. NB - 2 (slices, then X, per
+    // phase); phase Q issues the loads of phase Q + NB - 1. Vector memory
+    // operations retire in issue order, so the wait at the start of phase P
+    // may leave in flight exactly the operations issued after the X
+    // operands of P.
+    constexpr auto al_pending = [](int ph) {
+      int after = 0;
+      for (int j = ph + 1; j <= AL_NB - 2 && j < NPH; ++j) after += UW + XS;   // prologue
+      for (int q = 0; q < ph; ++q)                                             // phases before
+        if (q + AL_NB - 1 < NPH && q + AL_NB - 1 > ph) after += UW + XS;
+      return after;
+    };
+#define HQ_AL_LOAD(P_)                                                                      \
   if constexpr ((P_) < NPH) {                                                               \
+    _Pragma("unroll") for (int i = 0; i < UW; ++i)                                          \
+      lds_dma16(dsrc[i] + (P_) * AL_PH, &lds[((P_) % AL_NB) * BUF + 64 * (w * UW + i)]);    \
     _Pragma("unroll") for (int st = 0; st < XS; ++st)                                       \
-      xa[(P_) % XD][st] = *reinterpret_cast<const v8bf*>(xp + (P_) * AL_PH + 32 * st);      \
+      xa[(P_) % AL_NB][st] = *reinterpret_cast<const v8bf*>(xp + (P_) * AL_PH + 32 * st);   \
     __builtin_amdgcn_sched_barrier(0);                                                      \
   }
-    // loads phase P may leave in flight (see above)
-    constexpr auto al_pending = [](int ph) {
-      if (ph == 0) return ((XD - 2) < (NPH - 1) ? (XD - 2) : (NPH - 1)) * XS;
-      return ph + XD - 2 < NPH ? XS : 0;
-    };
 #define HQ_AL_PHASE(P_)                                                                     \
   if constexpr ((P_) < NPH) {                                                               \
     /* vmcnt(al_pending(P_)) lgkmcnt(0) */                                                  \
     __builtin_amdgcn_s_waitcnt((al_pending(P_) & 0xF) | ((al_pending(P_) >> 4) << 14) |     \
                                0x70);                                                       \
-    __syncthreads();                                                                        \
-    if constexpr ((P_) + 1 < NPH) HQ_AL_DMA((P_) + 1);                                      \
-    HQ_AL_X((P_) + XD - 1)                                                                  \
-    const uint4* const bq = &lds[((P_) & 1) * BUF];                                         \
+    /* every wave's slices of P_ are in LDS and buffer (P_ - 1) % NB is read; a */            \
+    /* bare barrier: __syncthreads' release fence would wait for the DMA of the */           \
+    /* later phases too */                                                                   \
+    asm volatile("" ::: "memory");                                                          \
+    __builtin_amdgcn_s_barrier();                                                           \
+    asm volatile("" ::: "memory");                                                          \
+    HQ_AL_LOAD((P_) + AL_NB - 1)                                                            \
+    const uint4* const bq = &lds[((P_) % AL_NB) * BUF];                                     \
     _Pragma("unroll") for (int st = 0; st < XS; ++st)                                       \
       _Pragma("unroll") for (int g = 0; g < NT; ++g) {                                      \
-        const int ci = (g * 16 + nl) * 16 + ((4 * st + (lane >> 4)) ^ nl);                 \
-        const v8bf bh = *reinterpret_cast<const v8bf*>(&bq[(2 * kh) * R * 16 + ci]);        \
-        const v8bf bl = *reinterpret_cast<const v8bf*>(&bq[(2 * kh + 1) * R * 16 + ci]);    \
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[(P_) % XD][st], bh, acc[g], 0, 0, 0); \
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[(P_) % XD][st], bl, acc[g], 0, 0, 0); \
+        const int n = g * 16 + nl, ci = n * CH + ((4 * st + (lane >> 4)) ^ ((n >> 1) % CH)); \
+        v4i bh, bl;                                                                         \
+        lds_read2_b128(&bq[(2 * kh) * R * CH + ci], &bq[(2 * kh + 1) * R * CH + ci], bh, bl); \
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[(P_) % AL_NB][st],              \
+                                                         __builtin_bit_cast(v8bf, bh), acc[g], 0, 0, 0); \
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[(P_) % AL_NB][st],              \
+                                                         __builtin_bit_cast(v8bf, bl), acc[g], 0, 0, 0); \
       }                                                                                     \
   }
-    static_assert(CH == 16 && NPH >= 2 && NPH <= 12 && (XD - 2) * XS < 64, "phase schedule");
-    HQ_AL_DMA(0);
-    // the prologue loads the X operands of phases 0 .. XD - 2
-    static_assert(XD >= 2 && XD <= 5, "prologue length");
-    HQ_AL_X(0)
-    if constexpr (XD > 2) { HQ_AL_X(1) }
-    if constexpr (XD > 3) { HQ_AL_X(2) }
-    if constexpr (XD > 4) { HQ_AL_X(3) }
+    static_assert(NPH <= 24 && AL_NB == 4, "phase sequence below");
+    HQ_AL_LOAD(0) HQ_AL_LOAD(1) HQ_AL_LOAD(2)
     HQ_AL_PHASE(0) HQ_AL_PHASE(1) HQ_AL_PHASE(2) HQ_AL_PHASE(3) HQ_AL_PHASE(4) HQ_AL_PHASE(5)
     HQ_AL_PHASE(6) HQ_AL_PHASE(7) HQ_AL_PHASE(8) HQ_AL_PHASE(9) HQ_AL_PHASE(10) HQ_AL_PHASE(11)
+    HQ_AL_PHASE(12) HQ_AL_PHASE(13) HQ_AL_PHASE(14) HQ_AL_PHASE(15) HQ_AL_PHASE(16)
+    HQ_AL_PHASE(17) HQ_AL_PHASE(18) HQ_AL_PHASE(19) HQ_AL_PHASE(20) HQ_AL_PHASE(21)
+    HQ_AL_PHASE(22) HQ_AL_PHASE(23)
 #undef HQ_AL_PHASE
-#undef HQ_AL_X
-#undef HQ_AL_DMA
+#undef HQ_AL_LOAD
     // the halves: the second writes its products, the first adds them
     // (16x16 output layout: lane l, register j -> row 4 (l / 16) + j, rank l % 16)
     __syncthreads();
