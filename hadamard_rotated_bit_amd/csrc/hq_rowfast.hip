@@ -415,10 +415,9 @@ constexpr int AL_PH = 64;     // channels per phase and half of d
 constexpr int AL_NB = 4;      // LDS buffers and X register sets (loads NB - 1 phases ahead)
 
 template <int C, int NX, int P, int NT>
-__global__ __launch_bounds__(512) void act_lr_kernel(RowArgs a, float inv_sqrt_b,
-                                                        const uint16_t* __restrict__ l1hi,
-                                                        const uint16_t* __restrict__ l1lo,
-                                                        float* __restrict__ U, int npb) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void act_lr_kernel(
+    RowArgs a, float inv_sqrt_b, const uint16_t* __restrict__ l1hi,
+    const uint16_t* __restrict__ l1lo, float* __restrict__ U, int npb) {
   constexpr int G = 64, E = 8 * C, R = 16 * NT;
   constexpr int D = 8 * G * C;              // channels of a row
   constexpr int DH = D / 2;                 // channels per half
