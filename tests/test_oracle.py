@@ -589,6 +589,31 @@ def test_wh_integer_path_within_its_rounding_bound(m):
     assert O.sqnr_db((x @ weight.T + bias) / s_y, r["y_int"].astype(np.float64)) > 25
 
 
+@pytest.mark.parametrize("m,act", [(1, "none"), (16, "none"), (64, "none"), (16, "relu")])
+def test_int_dequant_reference_on_one_hot_inputs(m, act):
+    # A one-hot int8 input v e_k selects column k of the weight codes, so the
+    # dequantised WH output (Eq. (17), in units of s_y) is
+    # phi((v qw[:, k] + b_int) s_x s_w) H_out / s_y, written here with the
+    # dense block-diagonal H from scipy and explicit column indexing instead
+    # of the oracle's GEMM and transform.
+    x, weight, bias, s_x, s_y = _wh_inputs()
+    code = O.ACT_NONE if act == "none" else O.ACT_RELU
+    p = O.int_prepare(weight, bias, s_x, s_y, m, act=code)
+    d_out, d_in = weight.shape
+    hd = scipy.linalg.block_diag(*([scipy.linalg.hadamard(m) / np.sqrt(m)] * (d_out // m)))
+    for k, v in [(0, 1), (5, -7), (d_in - 1, 127)]:
+        xi = np.zeros((1, d_in), dtype=np.int16)
+        xi[0, k] = v
+        a = v * p["qw"][:, k].astype(np.float64) + p["b_int"]
+        ya = a * s_x * p["s_w"]
+        pre = ya @ hd
+        if act == "relu":
+            pre = np.maximum(pre, 0.0)
+        expect = pre / s_y
+        got = O.int_dequant_reference(xi, p)[0]
+        np.testing.assert_allclose(got, expect, rtol=1e-12, atol=1e-12 * np.abs(expect).max())
+
+
 def test_wh_bias_only_passes_back_to_original_basis():
     # x = 0: a = b_int, and the restored output is b / s_y up to the bias and
     # multiplier roundings (the bias is transformed with the weight, Eq. (40),
