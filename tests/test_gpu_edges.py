@@ -171,11 +171,15 @@ def test_low_rank_split_matches_one_pass(T, d_in, rank, xd):
         hq.act_quantize(desc, prep, X, workspace=small)
 
 
-@pytest.mark.parametrize("T,d_in,block,rank,alpha,center", [
-    (300, 3072, 1024, 32, 0.5, True), (1, 3072, 512, 16, 0.5, True),
-    (17, 2560, 512, 32, None, False), (64, 2560, 512, 16, 0.5, True),
-    (4100, 3072, 1024, 32, None, True)])
-def test_low_rank_wide_rows(T, d_in, block, rank, alpha, center):
+@pytest.mark.parametrize("T,d_in,block,rank,alpha,center,bits,gemm", [
+    (300, 3072, 1024, 32, 0.5, True, 4, hq.HQ_GEMM_AUTO),
+    (1, 3072, 512, 16, 0.5, True, 4, hq.HQ_GEMM_AUTO),
+    (17, 2560, 512, 32, None, False, 4, hq.HQ_GEMM_AUTO),
+    (64, 2560, 512, 16, 0.5, True, 4, hq.HQ_GEMM_AUTO),
+    (4100, 3072, 1024, 32, None, True, 4, hq.HQ_GEMM_AUTO),
+    (300, 3072, 1024, 32, 0.5, True, 4, hq.HQ_GEMM_I8),
+    (129, 2560, 512, 16, 0.5, True, 8, hq.HQ_GEMM_AUTO)])
+def test_low_rank_wide_rows(T, d_in, block, rank, alpha, center, bits, gemm):
     # bf16 input with d_in 2560 or 3072 (64 lanes per row in the row kernel),
     # blocks of >= 512 channels and rank 16 or 32, with and without smoothing
     # and centring: the flux_proj geometry at ragged row counts (1, 17, 300,
@@ -183,9 +187,11 @@ def test_low_rank_wide_rows(T, d_in, block, rank, alpha, center):
     # blocks). These geometries run the row transform and the down
     # projection in one launch through every entry point (quant_linear,
     # act_quantize with and without a workspace), so U, and therefore Y, are
-    # the same bits through all three.
+    # the same bits through all three. The int8 engine and 8-bit codes take
+    # the transform role's int8 code writer.
     r = run_case(T, d_in, 520, block=block, rank=rank, alpha=alpha, center=center,
-                 x_dtype="bf16", w_dtype="bf16", y_dtype="bf16")
+                 a_bits=bits, w_bits=bits, x_dtype="bf16", w_dtype="bf16", y_dtype="bf16",
+                 gemm=gemm)
     desc, prep, X, Y, codes, s_x, mu, U, ora = r
     check_all(Y, codes, s_x, ora, desc)
     err = np.linalg.norm(to_np(U) - ora["u"], axis=1) / np.linalg.norm(ora["u"], axis=1)
