@@ -206,6 +206,35 @@ def test_low_rank_wide_rows(T, d_in, block, rank, alpha, center, bits, gemm):
     assert torch.equal(s2, s_x) and torch.equal(m2, mu) and torch.equal(U2, U)
 
 
+def test_one_launch_activation_matches_separate_kernels():
+    # The same bf16 values given as bf16 X (the one-launch activation kernel)
+    # and as float32 X (the row kernel, then the two-pass down projection):
+    # the transforms run the same float32 arithmetic, so codes, scales and
+    # means are bit-identical; U is summed in a different order and agrees to
+    # float32 rounding.
+    T, d_in, d_out, rank = 300, 3072, 520, 32
+    print(f"\n[case] one launch vs separate kernels T={T} {d_in}->{d_out} rank={rank}", flush=True)
+    w = WL.custom(321, T, d_in, d_out, dtype="bf16", block=1024, alpha=0.5, center=1, rank=rank)
+    x, weight, bias = WL.gen_x(w), WL.gen_weight(w), WL.gen_bias(w)
+    l1, l2 = WL.gen_lowrank(w)
+    sig = torch.from_numpy(O.smoothing_scales(x, weight, 0.5).astype(np.float32)).cuda()
+    xb = tdev(x, "bf16")
+    outs = []
+    for xd, X in ((hq.BF16, xb), (hq.F32, xb.float())):
+        desc = hq.Desc(d_in, d_out, 1024, 4, 4, True, True, rank, xd, hq.BF16, hq.BF16)
+        prep = hq.prepare(desc, tdev(weight, "bf16"), torch.from_numpy(bias).cuda(), sig,
+                          tdev(l1, "bf16"), tdev(l2, "bf16"))
+        ws = torch.empty(hq.workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+        c, s_x, mu, U = hq.act_quantize(desc, prep, X, workspace=ws)
+        outs.append((codes_np(desc, c, T), s_x, mu, U))
+    (cb, sb, mb, ub), (cf, sf, mf, uf) = outs
+    np.testing.assert_array_equal(cb, cf)
+    assert torch.equal(sb, sf) and torch.equal(mb, mf)
+    err = (torch.linalg.norm(ub - uf, dim=1) / torch.linalg.norm(uf, dim=1)).max().item()
+    print(f"U: largest row difference {err:.2e}")
+    assert err <= 1e-6, err
+
+
 def test_heavy_outliers_and_no_centring():
     r = run_case(400, 2048, 512, block=2048, center=False, alpha=None, n_outliers=16,
                  outlier=1000.0)
